@@ -1,0 +1,58 @@
+"""Build libkda.so in-tree with hipcc for gfx950.
+
+    python -m gated_delta_rule_40_amd.build
+
+Every HIP source is compiled with packed-fp32 instruction selection turned
+off (the compiler otherwise forms v_pk_* fp32 ops on its own).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "lib", "libkda.so")
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip"]
+ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+CFLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", INCLUDE, "-I", CSRC]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, "--offload-arch=" + ARCH, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, res.stdout, res.stderr))
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile all sources and link ``gated_delta_rule_40_amd/lib/libkda.so``."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    os.makedirs(os.path.dirname(LIB), exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (res.stdout, res.stderr))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

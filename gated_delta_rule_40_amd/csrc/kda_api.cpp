@@ -1,0 +1,130 @@
+// kda_api.cpp -- host side of the libkda C ABI (declared in include/kda.h).
+//
+// Validates every argument before touching HIP, picks the kernel tiling and
+// launches on the caller's stream.  No device memory is allocated, no stream
+// is synchronised and no mutable state is shared between calls.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda.h"
+
+extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, const void *q,
+                                         const void *k, const void *v, const float *g,
+                                         const float *beta, const float *init, const int32_t *cu,
+                                         int32_t N, int32_t T_tot, int32_t H, int32_t dv,
+                                         void *out, float *fin, hipStream_t stream);
+extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
+                                        const float *g, const float *beta, float *state,
+                                        int32_t N, int32_t H, void *out, hipStream_t stream);
+
+namespace {
+
+constexpr int32_t kHeadDim = 128;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kda_status check_common(const void *q, const void *k, const void *v, const float *g,
+                        const float *beta, const void *out, int32_t dk, int32_t dv,
+                        kda_dtype dtype)
+{
+    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_INVALID_ARG;
+    if (dk <= 0 || dv <= 0) return KDA_ERR_INVALID_ARG;
+    // 16-byte vector accesses on q, k, v, out and g rows
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(g, 16) ||
+        !aligned(beta, 4))
+        return KDA_ERR_INVALID_ARG;
+    if (dk != kHeadDim || dv != kHeadDim) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+// Value-column block per workgroup: the largest block that still gives at
+// least one workgroup per compute unit (more blocks = more parallel state
+// chains, at the cost of repeating the state-independent chunk work).
+int auto_dv_block(int64_t units, int dv)
+{
+    int cus = 256;
+    int dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) cus = n;
+    }
+    int bv = dv;
+    while (bv > 16 && units * (dv / bv) < cus) bv /= 2;
+    return bv;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                          int32_t dv, kda_dtype dtype, void *out, float *final_state,
+                          int32_t chunk, int32_t dv_block, kda_stream_t stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, out, dk, dv, dtype);
+    if (st == KDA_ERR_INVALID_ARG) return st;
+    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return KDA_ERR_INVALID_ARG;
+    if (st != KDA_OK) return st;
+    const bool bf16 = dtype == KDA_BF16;
+    if (chunk == 0) chunk = bf16 ? 64 : 32;
+    const bool chunk_ok = bf16 ? (chunk == 32 || chunk == 64) : (chunk == 16 || chunk == 32);
+    if (!chunk_ok) return KDA_ERR_UNSUPPORTED;
+    if (dv_block != 0 && dv_block != 16 && dv_block != 32 && dv_block != 64 && dv_block != 128)
+        return KDA_ERR_UNSUPPORTED;
+    if (dv_block > dv) return KDA_ERR_UNSUPPORTED;
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    if (units == 0) return KDA_OK;
+    if (units * (dv / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;   // grid size
+    if (dv_block == 0) dv_block = auto_dv_block(units, dv);
+    hipError_t e = kda_launch_prefill(bf16 ? 1 : 0, chunk, dv_block, q, k, v, g, beta, initial_state,
+                                      cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
+                                      final_state, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_prefill(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                       int32_t dv, kda_dtype dtype, void *out, float *final_state,
+                       kda_stream_t stream)
+{
+    return kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens,
+                          num_heads, dk, dv, dtype, out, final_state, 0, 0, stream);
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state_inout, int32_t num_seqs,
+                           int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype, void *out,
+                           kda_stream_t stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, out, dk, dv, dtype);
+    if (st == KDA_ERR_INVALID_ARG) return st;
+    if (!state_inout || !aligned(state_inout, 16) || num_seqs < 0 || num_heads <= 0)
+        return KDA_ERR_INVALID_ARG;
+    if (st != KDA_OK) return st;
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    if (units == 0) return KDA_OK;
+    if (units > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda_launch_decode(dtype == KDA_BF16 ? 1 : 0, q, k, v, g, beta, state_inout,
+                                     num_seqs, num_heads, out, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+const char *kda_status_string(kda_status status)
+{
+    switch (status) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument (null, negative, misaligned or bad dtype)";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid but unsupported configuration (v1: dk = dv = 128)";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: HIP kernel launch failed";
+    }
+    return "unknown kda_status";
+}
+
+int32_t kda_version(void) { return 100; }
+
+}  // extern "C"

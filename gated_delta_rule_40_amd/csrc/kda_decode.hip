@@ -1,0 +1,114 @@
+// kda_decode.hip -- one KDA decode step (one new token per sequence and head).
+//
+// The step (page ailearn.mscapital.top/kimi-k3.html, card "KDA 单头递归"),
+// with Sbar = Diag(exp(g)) S:
+//     a = Sbar^T k,  b = Sbar^T q,  u = v - a,
+//     S' = Sbar + beta k u^T,  o = S'^T q = b + beta (q.k) u,
+// so one pass over the state yields both dk-reductions, and the state is read
+// once and written once.  The kernel is bound by HBM traffic: 128 KiB of the
+// 132.6 KB moved per (sequence, head) is the fp32 state.
+//
+// One workgroup (256 threads) per (sequence, head).  Thread t owns value
+// columns 4*(t%32)..+3 and key rows (t/32) + 8*i, i = 0..15: every state row
+// is read and written as 512 contiguous bytes (32 lanes x float4).  Partial
+// reductions are combined across the 8 row groups through LDS.
+#include "kda_device.hpp"
+
+namespace kda {
+
+constexpr int D = 128;          // dk = dv
+constexpr int DEC_THREADS = 256;
+constexpr int ROWG = DEC_THREADS / 32;   // row groups
+constexpr int RPT = D / ROWG;            // rows per thread
+
+template <typename T>
+__global__ __launch_bounds__(DEC_THREADS) void kda_decode_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
+    T *__restrict__ out)
+{
+    __shared__ float sk[D], sq[D], sa[D];
+    __shared__ f32x4 red_a[ROWG][D / 4], red_b[ROWG][D / 4];
+    __shared__ float su[D];
+    __shared__ float sqk;
+
+    const int64_t u = blockIdx.x;
+    const int t = threadIdx.x;
+    const int cg = t & 31, rg = t >> 5;
+
+    // state loads first: they are the bulk of the traffic
+    f32x4 s[RPT];
+    const f32x4 *S4 = reinterpret_cast<const f32x4 *>(state + u * (int64_t)D * D);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S4[(rg + ROWG * i) * (D / 4) + cg]);
+
+    if (t < D) {
+        sk[t] = to_f(k[u * D + t]);
+        sq[t] = to_f(q[u * D + t]);
+        sa[t] = __expf(g[u * D + t]);
+    }
+    __syncthreads();
+    if (t < 64) {   // q.k by one wave
+        float p = sk[t] * sq[t] + sk[t + 64] * sq[t + 64];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+        if (t == 0) sqk = p;
+    }
+
+    f32x4 pa = zero4(), pb = zero4();
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + ROWG * i;
+        s[i] *= sa[r];
+        pa += s[i] * sk[r];
+        pb += s[i] * sq[r];
+    }
+    red_a[rg][cg] = pa;
+    red_b[rg][cg] = pb;
+    __syncthreads();
+
+    const float bt = beta[u];
+    if (t < D) {
+        const int c4 = t >> 2, e = t & 3;
+        float A = 0.f, B = 0.f;
+#pragma unroll
+        for (int r = 0; r < ROWG; ++r) {
+            A += red_a[r][c4][e];
+            B += red_b[r][c4][e];
+        }
+        const float uu = to_f(v[u * D + t]) - A;
+        su[t] = uu;
+        out[u * D + t] = from_f<T>(B + bt * sqk * uu);
+    }
+    __syncthreads();
+
+    const f32x4 uu = reinterpret_cast<const f32x4 *>(su)[cg];
+    f32x4 *W4 = reinterpret_cast<f32x4 *>(state + u * (int64_t)D * D);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + ROWG * i;
+        const f32x4 x = s[i] + (bt * sk[r]) * uu;
+        __builtin_nontemporal_store(x, &W4[r * (D / 4) + cg]);
+    }
+}
+
+}  // namespace kda
+
+extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
+                                        const float *g, const float *beta, float *state,
+                                        int32_t N, int32_t H, void *out, hipStream_t stream)
+{
+    using namespace kda;
+    const int64_t units = (int64_t)N * H;
+    if (units <= 0) return hipSuccess;
+    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (bf16)
+        hipLaunchKernelGGL(kda_decode_kernel<bf16_t>, dim3((unsigned)units), dim3(DEC_THREADS), 0, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
+                           static_cast<const bf16_t *>(v), g, beta, state, static_cast<bf16_t *>(out));
+    else
+        hipLaunchKernelGGL(kda_decode_kernel<float>, dim3((unsigned)units), dim3(DEC_THREADS), 0, stream,
+                           static_cast<const float *>(q), static_cast<const float *>(k),
+                           static_cast<const float *>(v), g, beta, state, static_cast<float *>(out));
+    return hipGetLastError();
+}

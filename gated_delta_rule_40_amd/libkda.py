@@ -1,0 +1,141 @@
+"""ctypes binding over libkda.so (C ABI declared in include/kda.h).
+
+Argument marshalling only: shapes and dtypes are read off torch tensors,
+device pointers and the current HIP stream are passed to the C entry points,
+and every step of the computation runs in libkda's HIP kernels.  There is no
+fallback: if the library is missing the calls raise.
+
+    kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    kda_prefill_ex(..., chunk=0, dv_block=0)
+    kda_decode_step(q, k, v, g, beta, state_inout, out)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
+KDA_F32, KDA_BF16 = 0, 1
+
+EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_decode_step", "kda_status_string", "kda_version")
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libkda.so (built by ``python -m gated_delta_rule_40_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError("libkda.so not built at %s; run python -m gated_delta_rule_40_amd.build" % p)
+    lib = ctypes.CDLL(p)
+    vp, fp, ip, i32 = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32
+    lib.kda_prefill.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp, vp]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
+                                   i32, i32, vp]
+    lib.kda_prefill_ex.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, vp, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_int32
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().kda_status_string(status).decode()
+
+
+def _check(status: int) -> None:
+    if status != KDA_OK:
+        raise KdaError(status, status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                   chunk: int = 0, dv_block: int = 0, stream=None) -> None:
+    """Packed varlen prefill.  q, k, g: [T, H, dk]; v, out: [T, H, dv];
+    beta: [T, H] fp32; initial_state/final_state: [N, H, dk, dv] fp32 or None;
+    cu_seqlens: [N+1] int32 on the device."""
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.shape[0] - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out)):
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens must be int32 on the device")
+    _require(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be float32")
+    _require(k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (T, H) and out.shape == v.shape,
+             "shape mismatch")
+    _require(tuple(beta.shape) == (T, H), "beta must be [T, H]")
+    _require(k.dtype == q.dtype and v.dtype == q.dtype and out.dtype == q.dtype, "q/k/v/out dtypes differ")
+    for name, s in (("initial_state", initial_state), ("final_state", final_state)):
+        if s is not None:
+            _require(s.dtype == torch.float32 and s.is_contiguous() and tuple(s.shape) == (N, H, dk, dv),
+                     "%s must be contiguous float32 [N, H, dk, dv]" % name)
+    lib = load()
+    _check(lib.kda_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                              _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
+                              _ptr(final_state), int(chunk), int(dv_block), _stream(stream)))
+
+
+def kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, stream=None) -> None:
+    """kda_prefill with the library's default tiling."""
+    kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, 0, 0, stream)
+
+
+def kda_decode_step(q, k, v, g, beta, state_inout, out, stream=None) -> None:
+    """One decode step, state updated in place.  q, k, g: [N, H, dk];
+    v, out: [N, H, dv]; beta: [N, H]; state_inout: [N, H, dk, dv] fp32."""
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state_inout),
+                    ("out", out)):
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _require(k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (N, H) and out.shape == v.shape,
+             "shape mismatch")
+    _require(tuple(beta.shape) == (N, H) and tuple(state_inout.shape) == (N, H, dk, dv), "shape mismatch")
+    _require(state_inout.dtype == torch.float32 and g.dtype == torch.float32 and beta.dtype == torch.float32,
+             "g, beta and state must be float32")
+    lib = load()
+    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_inout), N, H, dk,
+                               dv, _dtype_code(q), _ptr(out), _stream(stream)))

@@ -1,0 +1,129 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * The operation (page "Kimi K3 把 3T 级模型、百万上下文和 Agent 训练接成一套系统",
+ * ailearn.mscapital.top/kimi-k3.html, card "KDA 单头递归"), per sequence n and
+ * head h, for tokens t in order:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                  (the query reads the updated state)
+ *
+ * with alpha_t = exp(g_t) per key channel.  S is dk x dv (row = key channel,
+ * column = value channel), fixed in size whatever the sequence length (same
+ * page, section "百万上下文的关键，不是让所有层都保存百万份 KV").  Nothing else
+ * is applied: no query scaling, key normalisation, output gate or short
+ * convolution.  Results are guaranteed for g in [-5, 0] (card "g ∈ (-5, 0)"):
+ * outside that range the intermediate decay factors may overflow and the
+ * result is unspecified.  beta may be any finite value.
+ *
+ * Conventions for every call:
+ *   - Device pointers are on the current HIP device, dense and row-major as
+ *     documented; the caller owns every buffer.  The library allocates no
+ *     device memory and keeps no mutable global state (thread-safe).
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and never
+ *     synchronise.  Argument errors are returned before any HIP call; a
+ *     launch failure returns KDA_ERR_LAUNCH; device faults surface at the
+ *     caller's next synchronisation of `stream`.
+ *   - v1 supports dk = dv = 128 only (other sizes: KDA_ERR_UNSUPPORTED).
+ *   - Arithmetic: q/k/v/out in `dtype`; g, beta and states fp32; all
+ *     accumulation and the carried state are fp32.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *kda_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad dtype, overflowing sizes */
+    KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. dk != 128) */
+    KDA_ERR_LAUNCH = 3       /* the HIP launch itself failed */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,  /* q, k, v, out are fp32 */
+    KDA_BF16 = 1  /* q, k, v, out are bf16 (round-to-nearest-even on output) */
+} kda_dtype;
+
+/*
+ * kda_prefill -- run the recurrence over packed variable-length sequences.
+ *
+ *   q, k          [total_tokens, num_heads, dk]   dtype
+ *   v             [total_tokens, num_heads, dv]   dtype
+ *   g             [total_tokens, num_heads, dk]   fp32, log-decay (alpha = exp(g))
+ *   beta          [total_tokens, num_heads]       fp32, write strength
+ *   initial_state [num_seqs, num_heads, dk, dv]   fp32, or NULL for zeros
+ *   cu_seqlens    [num_seqs + 1]                  int32, DEVICE memory:
+ *                 cu[0] = 0, non-decreasing, cu[num_seqs] <= total_tokens.
+ *                 Sequence n owns tokens [cu[n], cu[n+1]).  It is not read on
+ *                 the host; entries outside [0, total_tokens] are clamped on
+ *                 the device (memory-safe, result for that sequence unspecified).
+ *   out           [total_tokens, num_heads, dv]   dtype; rows of tokens owned
+ *                 by a sequence are written, other rows are left untouched.
+ *   final_state   [num_seqs, num_heads, dk, dv]   fp32, or NULL (not written).
+ *                 final_state == initial_state is allowed (in-place update of
+ *                 the carried state); any other overlap is undefined.
+ *
+ * An empty sequence writes no output and final_state[n] = initial_state[n]
+ * (zeros if NULL).  Continuation: passing one call's final_state as the next
+ * call's initial_state over the following tokens equals one call over all of
+ * them, which is how a state is restored at a token boundary (page section
+ * "目标模型太大，缓存和草稿都必须理解 KDA").
+ */
+kda_status kda_prefill(const void *q, const void *k, const void *v,
+                       const float *g, const float *beta,
+                       const float *initial_state, const int32_t *cu_seqlens,
+                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                       int32_t dk, int32_t dv, kda_dtype dtype,
+                       void *out, float *final_state, kda_stream_t stream);
+
+/*
+ * kda_prefill_ex -- kda_prefill with explicit kernel tiling (tests, tuning).
+ *   chunk    tokens per chunk: 32 or 64 for bf16, 16 or 32 for fp32; 0 = default
+ *   dv_block value columns per workgroup: 16, 32, 64 or 128; 0 = automatic
+ * Any tiling gives the same result up to fp32 rounding order.  Other values
+ * return KDA_ERR_UNSUPPORTED.
+ */
+kda_status kda_prefill_ex(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                          int32_t dk, int32_t dv, kda_dtype dtype,
+                          void *out, float *final_state,
+                          int32_t chunk, int32_t dv_block, kda_stream_t stream);
+
+/*
+ * kda_decode_step -- one new token per (sequence, head), state updated in place
+ * (the same recurrence step; page card "KDA 单头递归").
+ *
+ *   q, k          [num_seqs, num_heads, dk]       dtype
+ *   v             [num_seqs, num_heads, dv]       dtype
+ *   g             [num_seqs, num_heads, dk]       fp32
+ *   beta          [num_seqs, num_heads]           fp32
+ *   state_inout   [num_seqs, num_heads, dk, dv]   fp32, read then overwritten
+ *   out           [num_seqs, num_heads, dv]       dtype
+ * Each (sequence, head) state is read once and written once.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta, float *state_inout,
+                           int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv,
+                           kda_dtype dtype, void *out, kda_stream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *kda_status_string(kda_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

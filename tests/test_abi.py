@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+that include/kda.h declares, and rejects bad arguments with the documented
+status codes before making any HIP call (so these run on a CPU-only host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_40_amd import libkda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from gated_delta_rule_40_amd import build
+        build.build()
+    return K.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kda_prefill", "kda_decode_step", "kda_status_string"):
+        assert required in names
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_version() >= 100
+    for code in range(4):
+        s = lib.kda_status_string(code)
+        assert s and s.decode().startswith(("KDA_OK", "KDA_ERR"))
+    assert lib.kda_status_string(99) is not None
+
+
+# fake but 16-byte aligned, non-null device pointers: never dereferenced,
+# because every call below fails validation before any HIP call
+P = ctypes.c_void_p(0x10000)
+NULL = None
+
+
+def prefill(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, init=NULL, cu=P, N=1, T=16, H=1, dk=128, dv=128,
+             dtype=K.KDA_BF16, out=P, fin=NULL, chunk=0, dvb=0)
+    a.update(kw)
+    return lib.kda_prefill_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["init"], a["cu"], a["N"],
+                              a["T"], a["H"], a["dk"], a["dv"], a["dtype"], a["out"], a["fin"],
+                              a["chunk"], a["dvb"], None)
+
+
+def decode(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, state=P, N=1, H=1, dk=128, dv=128, dtype=K.KDA_BF16, out=P)
+    a.update(kw)
+    return lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state"], a["N"], a["H"],
+                               a["dk"], a["dv"], a["dtype"], a["out"], None)
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "beta", "cu", "out"])
+def test_prefill_null_pointer(lib, field):
+    assert prefill(lib, dk=64, **{field: NULL}) == K.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), K.KDA_ERR_INVALID_ARG),
+    (dict(T=-5), K.KDA_ERR_INVALID_ARG),
+    (dict(H=0), K.KDA_ERR_INVALID_ARG),
+    (dict(dk=0), K.KDA_ERR_INVALID_ARG),
+    (dict(dtype=7), K.KDA_ERR_INVALID_ARG),
+    (dict(q=ctypes.c_void_p(0x10008)), K.KDA_ERR_INVALID_ARG),   # misaligned
+    (dict(dk=64), K.KDA_ERR_UNSUPPORTED),
+    (dict(dv=256), K.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=48), K.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=16), K.KDA_ERR_UNSUPPORTED),                    # bf16 supports 32 / 64
+    (dict(dtype=K.KDA_F32, chunk=64), K.KDA_ERR_UNSUPPORTED),   # fp32 supports 16 / 32
+    (dict(dvb=24), K.KDA_ERR_UNSUPPORTED),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill(lib, **kw) == code
+
+
+def test_prefill_empty_batch_is_a_no_op(lib):
+    # no sequences: nothing to launch, success without touching the device
+    assert prefill(lib, N=0, T=0) == K.KDA_OK
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "beta", "state", "out"])
+def test_decode_null_pointer(lib, field):
+    assert decode(lib, **{field: NULL}) == K.KDA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-2), K.KDA_ERR_INVALID_ARG),
+    (dict(H=-1), K.KDA_ERR_INVALID_ARG),
+    (dict(dtype=3), K.KDA_ERR_INVALID_ARG),
+    (dict(state=ctypes.c_void_p(0x10004)), K.KDA_ERR_INVALID_ARG),
+    (dict(dk=96), K.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_rejects(lib, kw, code):
+    assert decode(lib, **kw) == code
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert decode(lib, N=0) == K.KDA_OK
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        K.load(str(tmp_path / "missing.so"))
