@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * kda_prefill over the long-context varlen batch (8 sequences, lengths drawn
+    log-uniform over [1K, 256K] and rescaled to 1,048,576 tokens, 16 heads,
+    dk = dv = 128, bf16 q/k/v, fp32 g/beta/state, zero initial state), then
+  * 64 consecutive in-place kda_decode_step calls on the decode batch
+    (512 sequences x 32 heads, 1 GiB fp32 state).
+Inputs are generated on the device before timing (resident in HBM).
+
+Prints ONE JSON line.  `value` is prefill tokens/s (sequence tokens, all 16
+heads each); the decode figures sit under "decode".  Kernel durations come from
+HIP events recorded on the stream the kernels run on, inside the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + % bf16 MFMA peak; decode tokens/s + % HBM peak (1 GPU)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA, TFLOP/s
+DK = DV = 128
+# algorithmic bytes per head-token of prefill: q, k, v, out (bf16) + g (fp32) + beta (fp32)
+PREFILL_BYTES_PER_HT = 3 * 2 * DK + 4 * DK + 4 + 2 * DV
+# reference chunk-form flops per head-token (three dk x dv contractions + chunk terms at C = 64)
+PREFILL_FREF_PER_HT = 6 * DK * DV + 2 * 64 * (DK + DV)
+# decode bytes per (sequence, head): state read + write, q/k/v/out bf16, g fp32, beta fp32
+DECODE_BYTES_PER_UNIT = 2 * DK * DV * 4 + 3 * 2 * DK + 4 * DK + 4 + 2 * DV
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_traffic.json")
+PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_prefill.hip")
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_traffic():
+    """HBM bytes per prefill launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            d = json.load(f)
+        if d.get("kernel_source_sha256_16") != source_hash(PREFILL_SRC):
+            return None
+        return float(d["hbm_bytes_per_launch"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(pre, H, target_s=15.0):
+    """Time the fp64 oracle (as it stands) on host cores on a bounded sample:
+    the first Ls tokens of every sequence of the same prefill inputs, all heads."""
+    import numpy as np
+    import torch
+    from oracle import kda_oracle as O
+
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = max(1, min(cores, 16))
+    cu = pre["cu_seqlens"].cpu().tolist()
+    N = len(cu) - 1
+
+    def run(Ls):
+        rows = [torch.arange(cu[n], cu[n] + min(Ls, cu[n + 1] - cu[n])) for n in range(N)]
+        lens = [len(r) for r in rows]
+        idx = torch.cat(rows).to(pre["q"].device)
+        sub = {k_: pre[k_].index_select(0, idx).float().cpu().numpy() for k_ in ("q", "k", "v", "g", "beta")}
+        scu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        t0 = time.perf_counter()
+        O.prefill(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], None, scu, num_threads=cores)
+        return time.perf_counter() - t0, sum(lens)
+
+    O.build()
+    t, tok = run(64)                       # calibration
+    rate = tok / max(t, 1e-6)
+    Ls = int(max(64, min(rate * target_s / N, max(cu[n + 1] - cu[n] for n in range(N)))))
+    t, tok = run(Ls)
+    return {"value": tok / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "first %d tokens of each of the %d sequences x %d heads of the same prefill inputs "
+                      "(%d tokens, %d head-tokens, %.1f s, fp64 token loop, OpenMP over (sequence, head))"
+                      % (Ls, N, H, tok, tok * H, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the KDA path on a single MI355X "
+              "(heads and sequences shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gated_delta_rule_40_amd import inputs as I
+    from gated_delta_rule_40_amd import libkda as K
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    K.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl_p = I.WORKLOADS["prefill_varlen_1m_h16"]
+    wl_d = I.WORKLOADS["decode_512x32"]
+    pre = I.make_prefill(wl_p, device=dev)
+    dec = I.make_decode(wl_d, device=dev, steps=args.decode_steps)
+    T, H = pre["q"].shape[0], pre["q"].shape[1]
+    N = pre["cu_seqlens"].shape[0] - 1
+    out = torch.empty(T, H, DV, dtype=torch.bfloat16, device=dev)
+    fin = torch.empty(N, H, DK, DV, dtype=torch.float32, device=dev)
+    Nd, Hd = wl_d.num_seqs, wl_d.heads
+    state = dec["state"]
+    dout = torch.empty(args.decode_steps, Nd, Hd, DV, dtype=torch.bfloat16, device=dev)
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        K.kda_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, pre["cu_seqlens"], out, fin)
+        if ev is not None:
+            ev[1].record(stream)
+        for s in range(args.decode_steps):
+            K.kda_decode_step(dec["q"][s], dec["k"][s], dec["v"][s], dec["g"][s], dec["beta"][s], state, dout[s])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    head_tokens = T * H
+    pre_bytes = head_tokens * PREFILL_BYTES_PER_HT + N * H * DK * DV * 4      # + final state write
+    pre_gbs = pre_bytes / (pre_avg * 1e-3) / 1e9
+    pre_tflops = head_tokens * PREFILL_FREF_PER_HT / (pre_avg * 1e-3) / 1e12
+    dec_step_ms = dec_avg / args.decode_steps
+    dec_bytes = Nd * Hd * DECODE_BYTES_PER_UNIT
+    dec_gbs = dec_bytes / (dec_step_ms * 1e-3) / 1e9
+    traffic = pmc_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": T / (pre_avg * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill_varlen_1m_h16 + decode_512x32",
+            "prefill": {"num_seqs": N, "lengths": pre["lengths"], "total_tokens": T, "heads": H,
+                        "dk": DK, "dv": DV, "io": "bf16 q/k/v/out, fp32 g/beta/state",
+                        "initial_state": "zero", "ms": pre_avg, "head_tokens_per_s": head_tokens / (pre_avg * 1e-3),
+                        "fref_tflops": pre_tflops, "mfma_frac_fref": pre_tflops / BF16_PEAK_TFLOPS,
+                        "compute": "fp16 MFMA operands (exact power-of-two column scaling), fp32 accumulate and state"},
+            "decode": {"num_seqs": Nd, "heads": Hd, "steps": args.decode_steps, "state_bytes": Nd * Hd * DK * DV * 4},
+        },
+        "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": pre_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": "kda_prefill_kernel<bf16, 64, NW>", "algorithmic_bytes_per_launch": pre_bytes,
+                     "avg_launch_ms": pre_avg},
+        "decode": {"tokens_per_s": Nd / (dec_step_ms * 1e-3), "ms_per_decode_step": dec_step_ms,
+                   "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": dec_gbs / HBM_PEAK_GBS, "kernel": "kda_decode_kernel<bf16>",
+                                "algorithmic_bytes_per_launch": dec_bytes}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pre, H)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,16 +70,22 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const flo
     if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return KDA_ERR_INVALID_ARG;
     if (st != KDA_OK) return st;
     const bool bf16 = dtype == KDA_BF16;
-    if (chunk == 0) chunk = bf16 ? 64 : 32;
+    if (chunk == 0) chunk = 32;
     const bool chunk_ok = bf16 ? (chunk == 32 || chunk == 64) : (chunk == 16 || chunk == 32);
     if (!chunk_ok) return KDA_ERR_UNSUPPORTED;
     if (dv_block != 0 && dv_block != 16 && dv_block != 32 && dv_block != 64 && dv_block != 128)
         return KDA_ERR_UNSUPPORTED;
     if (dv_block > dv) return KDA_ERR_UNSUPPORTED;
+    // 64-token bf16 chunks need at least two waves (value block >= 32)
+    const int min_block = (bf16 && chunk == 64) ? 32 : 16;
+    if (dv_block != 0 && dv_block < min_block) return KDA_ERR_UNSUPPORTED;
     const int64_t units = (int64_t)num_seqs * num_heads;
     if (units == 0) return KDA_OK;
     if (units * (dv / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;   // grid size
-    if (dv_block == 0) dv_block = auto_dv_block(units, dv);
+    if (dv_block == 0) {
+        dv_block = auto_dv_block(units, dv);
+        if (dv_block < min_block) dv_block = min_block;
+    }
     hipError_t e = kda_launch_prefill(bf16 ? 1 : 0, chunk, dv_block, q, k, v, g, beta, initial_state,
                                       cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                                       final_state, reinterpret_cast<hipStream_t>(stream));

@@ -7,30 +7,31 @@
 // Chunked form evaluated here (derived from that recurrence; C tokens per
 // chunk, entering state S0, Gamma_r = sum_{i<=r} g_i, all per key channel):
 //     X   = Diag(b) (V - K+ S0)                           K+ = K (.) e^Gamma
-//     (I + Diag(b) A) W = X,  A_ri = sum_c k_rc k_ic e^(Gamma_rc - Gamma_ic), i < r
+//     W   = (I + N)^-1 X,     N = Diag(b) A,  A_ri = sum_c k_rc k_ic e^(Gamma_rc - Gamma_ic), i < r
 //     O   = Q+ S0 + P W,      P_ri = sum_c q_rc k_ic e^(Gamma_rc - Gamma_ic), i <= r
 //     S_C = Diag(e^Gamma_C) S0 + K^T W                    K^ = K (.) e^(Gamma_C - Gamma)
-// A and P ("Gram" tiles) are built per 16-token sub-tile pair with decay
-// factors referenced to sub-tile boundaries (card "g ∈ (-5, 0)": inside a
-// 16-token tile the cumulative scaling stays within bf16 range), so every
-// factor is <= 1 except the diagonal sub-tile's column factor (<= e^80 for
-// g >= -5).  W comes from block forward substitution over the sub-tiles with
-// the 16x16 diagonal blocks inverted once per chunk.
+// A and P ("Gram" tiles) factor each decay e^(Gamma_r - Gamma_i) into a row and
+// a column factor.  When every channel decays by at most e^-11 over the chunk
+// (always true for gates of a few tenths), the chunk start is the reference:
+// rows use K+ / Q+ and columns K (.) e^-Gamma <= e^11, so A and P are plain
+// dense products of the operands the chain uses anyway.  Otherwise the factors
+// are referenced to 16-token sub-tile boundaries (card "g ∈ (-5, 0)": inside a
+// 16-token tile the cumulative scaling stays within bf16 range) and the Gram
+// runs on fp32 MFMA, so g anywhere in [-5, 0] stays exact.
 //
-// Precision (bf16 q/k/v): all state-dependent contractions run on fp16 MFMA
-// operands with fp32 accumulation; the fp32 state, X and W are converted with
-// exact per-column power-of-two scales, so their range is unrestricted.  The
-// Gram tiles use fp16 operands when every sub-tile's decay span is <= 8
-// (column factors <= e^8) and fp32 MFMA otherwise (chosen per chunk).  fp32
-// q/k/v use fp32 MFMA throughout.
+// Precision (bf16 q/k/v): every MFMA operand is fp16 with fp32 accumulation;
+// the fp32 state, X and W are converted with exact per-column power-of-two
+// scales, so their range is unrestricted; (I + N)^-1 is kept per 16x16 block
+// with a power-of-two scale.  fp32 q/k/v use fp32 MFMA throughout.
 //
 // Work decomposition: one workgroup per (sequence, head, block of BV value
 // columns), NW = BV/16 waves.  Each wave owns 16 columns of the fp32 state,
 // kept in MFMA accumulator registers for the whole sequence.  Per chunk:
-//   1. decay prep (all threads): sub-tile gate sums, per-token cumulative
-//      products, decayed operands written to LDS;
+//   1. decay prep from registers loaded one chunk ahead: sub-tile gate sums,
+//      per-token decay products, decayed operands to LDS;
 //   2. Gram tiles A, P on MFMA (jobs spread over the waves);
-//   3. 16x16 diagonal inverses (VALU forward substitution), value tile load;
+//   3. (I + N)^-1: 16x16 diagonal blocks by VALU forward substitution, then
+//      off-diagonal blocks by block recursion on MFMA;
 //   4. state-dependent chain per wave: X, W, O and the state update on MFMA;
 //   5. coalesced store of the output tile.
 // Ragged chunks are zero-padded (k = q = v = 0, g = 0, b = 0), which leaves
@@ -43,16 +44,11 @@ namespace kda {
 
 constexpr int DK = 128;
 constexpr int SUB = 16;
-constexpr float SPAN_FAST = 8.f;   // max sub-tile decay span for fp16 Gram operands
-// fp16 Gram operands: row operands are stored x2^5 and column factors x2^-5
-// (exact, cancelling) so that row values keep clear of fp16 subnormals while
-// column values (up to |k| e^8) stay below the fp16 maximum.
-constexpr float GRAM16_ROW = 32.f;
 
 template <typename TIn, int C, int NW>
 struct PrefillCfg {
     static constexpr bool kIn16 = !std::is_same<TIn, float>::value;
-    typedef typename std::conditional<kIn16, f16_t, float>::type OpT;   // chain operands
+    typedef typename std::conditional<kIn16, f16_t, float>::type OpT;   // MFMA operands
     static constexpr int BV = 16 * NW;
     static constexpr int NT = 64 * NW;
     static constexpr int NSUB = C / SUB;
@@ -60,48 +56,67 @@ struct PrefillCfg {
     static constexpr int KB = Mma<OpT>::KB;
     static_assert(C % KB == 0, "chunk must be a multiple of the MFMA K-block");
     static_assert(NSUB >= 1 && NSUB <= 4, "chunk of 16..64 tokens");
+    // Decay products are built from fixed 4-token groups, always combined in
+    // the same order, so every tiling computes bit-identical decay factors.
+    static constexpr int GRP = 4;
+    static constexpr int NGRP = C / GRP;
+    // fast decay prep: thread -> (segment of SEG tokens, channel pair), from
+    // registers loaded one chunk ahead (ITEMS items per thread)
+    static constexpr int SEG0 = C * 64 / NT;
+    static constexpr int SEG = SEG0 < GRP ? GRP : (SEG0 > 16 ? 16 : SEG0);
+    static constexpr int NSEG = C / SEG;
+    static constexpr int ITEMS = (NSEG * 64 + NT - 1) / NT;
+    static_assert(SEG % GRP == 0 && SUB % SEG == 0, "prep mapping");
+    // slow decay prep: thread -> (sub-tile, CPT consecutive channels)
+    static constexpr int CPT = (DK * NSUB >= NT) ? DK * NSUB / NT : 1;
+    static constexpr int NPREP = DK * NSUB / CPT;                      // slow prep threads
+    static_assert(CPT == 1 || CPT == 2 || CPT == 4, "channels per prep thread");
+    // chunk-start reference allowed when no channel decays by more than this
+    // over the chunk (11 for fp16 operands, 60 for fp32)
+    static constexpr float SPAN_CHUNK = kIn16 ? 11.f : 60.f;
+    // exact power-of-two rebalance of fp16 operands: row operands x GS, column /GS
+    static constexpr float GS = kIn16 ? 32.f : 1.f;
 
-    // row strides (elements), each row padded by 16 bytes against bank conflicts
-    static constexpr int LDK = DK + 16 / (int)sizeof(OpT);     // [C][DK] OpT tiles
-    static constexpr int LDC = C + 16 / (int)sizeof(OpT);      // [*][C] OpT tiles
-    static constexpr int LDK32 = DK + 4;                       // [C][DK] fp32 tiles
+    // row strides (elements), rows padded by 16 bytes against bank conflicts
+    static constexpr int LDK = DK + 16 / (int)sizeof(OpT);     // [C][DK] operand tiles
+    static constexpr int LDC = C + 16 / (int)sizeof(OpT);      // [*][C] operand tiles
+    static constexpr int LDK32 = DK + 4;                       // [C][DK] fp32 Gram inputs
     static constexpr int LDV = BV + 16 / (int)sizeof(TIn);     // value / output tiles
-    static constexpr int LDI = SUB + 16 / (int)sizeof(OpT);    // diagonal inverses
 
     static constexpr size_t tileK = sizeof(OpT) * C * LDK;
-    static constexpr size_t tileK32 = sizeof(float) * C * LDK32;
-    // Region G/B: Gram inputs [Kr][Qr][KD] (OpT) then chain operands
-    // [-K+][Q+][K^T] (OpT).  For bf16 input the fp32 Gram inputs of a
-    // strong-decay chunk [Kr32][Qr32][KD32] overlay the whole region.
-    static constexpr size_t offKr = 0;
-    static constexpr size_t offQr = offKr + tileK;
-    static constexpr size_t offKD = offQr + tileK;
-    static constexpr size_t offNKp = offKD + tileK;
-    static constexpr size_t offQp = offNKp + tileK;
-    static constexpr size_t offKhT = offQp + tileK;
-    static constexpr size_t endGB = offKhT + sizeof(OpT) * DK * LDC;
+    // region 0: chain operands and staging; the fp32 sub-tile Gram inputs of a
+    // strong-decay chunk overlay it (everything but Kc is rewritten afterwards)
+    static constexpr size_t offNKp = 0;                                    // -GS K+   [C][LDK]
+    static constexpr size_t offQp = offNKp + tileK;                        //  GS Q+   [C][LDK]
+    static constexpr size_t offKc = offQp + tileK;                         //  K e^-G / GS [C][LDK]
+    static constexpr size_t offKhT = offKc + tileK;                        //  GS K^T  [DK][LDC]
+    static constexpr size_t offV = offKhT + sizeof(OpT) * DK * LDC;        //  V       [C][LDV]
+    static constexpr size_t offO = offV + sizeof(TIn) * C * LDV;           //  O       [C][LDV]
+    static constexpr size_t endFast = offO + sizeof(TIn) * C * LDV;
     static constexpr size_t offKr32 = 0;
-    static constexpr size_t offQr32 = offKr32 + tileK32;
-    static constexpr size_t offKD32 = offQr32 + tileK32;
-    static_assert(!kIn16 || offKD32 + tileK32 <= endGB, "fp32 Gram inputs must fit the region");
-    // Region D (after the Gram step): value tile, output tile, inverses; inside [Kr][Qr][KD]
-    static constexpr size_t offV = 0;
-    static constexpr size_t offO = offV + sizeof(TIn) * C * LDV;
-    static constexpr size_t offInv = offO + sizeof(TIn) * C * LDV;
-    static_assert(offInv + sizeof(OpT) * NSUB * SUB * LDI <= offNKp, "region D must fit");
-    // Region C: Gram outputs
-    static constexpr size_t offAd = endGB;                                   // fp32 [NSUB*16][17]
-    static constexpr size_t offNs = offAd + sizeof(float) * NSUB * SUB * 17;  // OpT [C][LDC]
-    static constexpr size_t offP = offNs + sizeof(OpT) * C * LDC;            // OpT [C][LDC]
-    static constexpr size_t endC = offP + sizeof(OpT) * C * LDC;
+    static constexpr size_t offQr32 = offKr32 + sizeof(float) * C * LDK32;
+    static constexpr size_t offKD32 = offQr32 + sizeof(float) * C * LDK32;
+    static constexpr size_t endSlow = offKD32 + sizeof(float) * C * LDK32;
+    static constexpr size_t end0 = ((endFast > endSlow ? endFast : endSlow) + 15) / 16 * 16;
+    // region 1: Gram outputs and (I + N)^-1
+    static constexpr int LDAD = 20;                                          // 80-byte rows
+    static constexpr size_t offAd = end0;                                   // fp32 [NSUB][16][LDAD], N^T
+    static constexpr size_t offN = offAd + sizeof(float) * NSUB * SUB * LDAD; // OpT [C][LDC]
+    static constexpr size_t offT = offN + sizeof(OpT) * C * LDC;            // OpT [C][LDC]
+    static constexpr size_t offP = offT + sizeof(OpT) * C * LDC;            // OpT [C][LDC]
+    static constexpr size_t end1 = (offP + sizeof(OpT) * C * LDC + 15) / 16 * 16;
     // small fp32 tables
-    static constexpr size_t offF = (endC + 15) / 16 * 16;                    // [NSUB][DK]
-    static constexpr size_t offH = offF + sizeof(float) * NSUB * DK;         // [NPAIR][DK]
-    static constexpr size_t offGam = offH + sizeof(float) * NPAIR * DK;      // [DK]
-    static constexpr size_t offBeta = offGam + sizeof(float) * DK;           // [C]
-    static constexpr size_t offInvS = offBeta + sizeof(float) * C;           // [NSUB]
-    static constexpr size_t bytes = offInvS + sizeof(float) * NSUB;
+    static constexpr size_t offF = end1;                                    // [NGRP][DK]
+    static constexpr size_t offH = offF + sizeof(float) * NGRP * DK;        // [NPAIR][DK]
+    static constexpr size_t offGam = offH + sizeof(float) * NPAIR * DK;     // [DK]
+    static constexpr size_t offBeta = offGam + sizeof(float) * DK;          // [C]
+    static constexpr size_t offTs = offBeta + sizeof(float) * C;            // [NSUB][NSUB]
+    static constexpr size_t bytes = offTs + sizeof(float) * NSUB * NSUB;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    // workgroups per CU that the LDS allows (the register budget is set to match)
+    static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
+    // waves per SIMD the register budget is sized for (at most 2: 256 registers)
+    static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
 };
 
 // sub-tile pair p -> (a, b), b <= a
@@ -111,54 +126,128 @@ __device__ __forceinline__ void pair_of(int p, int &a, int &b) {
     b = p - a * (a + 1) / 2;
 }
 
-// Gram tiles A (strictly lower) and P (lower incl.) for every sub-tile pair,
-// operands of type GT in LDS with row stride ld; the column operand of pair
-// (a, b) is KD of sub-tile b scaled per channel by H(a, b).
+// Gram tiles A (strictly lower) and P (lower incl.), one job = one sub-tile
+// pair and one of the two products.  Operands of type GT with row stride ld;
+// if hs != nullptr the column operand of pair p is scaled per channel by
+// hs[p][.].  sign: +1 if the row operand of A is +K, -1 if it holds -K.
+// Output: N = Diag(beta) A (diagonal blocks fp32 to sAd, others to sN) and P.
 template <typename GT, typename OpT, int C, int NW>
-__device__ __forceinline__ void gram_tiles(const GT *sKr, const GT *sQr, const GT *sKD, int ld,
-                                           const float *sH, const float *sBeta, float *sAd,
-                                           OpT *sNs, OpT *sP, int ldc, int wave, int lj, int lm)
+__device__ __forceinline__ void gram_tiles(const GT *rowA_base, const GT *rowP_base, const GT *col_base,
+                                           int ld, const float *hs, float signA,
+                                           const float *sBeta, float *sAd, OpT *sN, OpT *sP, int ldc,
+                                           int wave, int lj, int lm)
 {
     typedef Mma<GT> G;
     constexpr int NSUB = C / SUB, NPAIR = NSUB * (NSUB + 1) / 2;
     constexpr int KBc = Mma<OpT>::KB;    // K-block of the P W contraction in the chain
-    for (int p = wave; p < NPAIR; p += NW) {
+    for (int job = wave; job < 2 * NPAIR; job += NW) {
+        const int p = job >> 1;
+        const bool isP = job & 1;
         int a, b;
         pair_of(p, a, b);
-        f32x4 accA = zero4(), accP = zero4();
-        const GT *rowKr = sKr + (a * SUB + lm) * ld;
-        const GT *rowQr = sQr + (a * SUB + lm) * ld;
-        const GT *rowKD = sKD + (b * SUB + lm) * ld;
-        const float *hs = sH + p * DK;
+        f32x4 acc = zero4();
+        const GT *rowR = (isP ? rowP_base : rowA_base) + (a * SUB + lm) * ld;
+        const GT *rowC = col_base + (b * SUB + lm) * ld;
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += G::KB) {
-            const typename G::frag bf = G::load_scaled(rowKD, hs, k0, lj);
-            accA = G::mma(G::load(rowKr, k0, lj), bf, accA);
-            accP = G::mma(G::load(rowQr, k0, lj), bf, accP);
+            const typename G::frag bf = hs ? G::load_scaled(rowC, hs + p * DK, k0, lj) : G::load(rowC, k0, lj);
+            acc = G::mma(G::load(rowR, k0, lj), bf, acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 4 * lj + i;                 // row within sub-tile a
             const int r = a * SUB + rl, cc = b * SUB + lm;
-            float av = accA[i], pv = accP[i];
-            if (a == b) {
-                if (lm >= rl) av = 0.f;
-                if (lm > rl) pv = 0.f;
+            if (isP) {
+                const float pv = (a == b && lm > rl) ? 0.f : acc[i];
+                sP[r * ldc + cc] = from_f<OpT>(pv);
+                if (KBc == 32 && a == b && (a & 1) == 0 && a + 1 < NSUB)
+                    sP[r * ldc + cc + SUB] = from_f<OpT>(0.f);  // a K-block pairs sub-tiles a, a+1
+            } else if (a != b) {
+                sN[r * ldc + cc] = from_f<OpT>(sBeta[r] * signA * acc[i]);   // N = Diag(beta) A
             }
-            const float nv = sBeta[r] * av;            // N = Diag(beta) A
-            if (a == b)
-                sAd[(a * SUB + rl) * 17 + lm] = nv;
-            else
-                sNs[r * ldc + cc] = from_f<OpT>(-nv);
-            sP[r * ldc + cc] = from_f<OpT>(pv);
-            if (KBc == 32 && a == b && (a & 1) == 0 && a + 1 < NSUB)
-                sP[r * ldc + cc + SUB] = from_f<OpT>(0.f);  // a K-block pairs sub-tiles a, a+1
+        }
+        if (!isP && a == b) {
+            // diagonal block, strictly lower, stored transposed: sAd[a][col][row]
+            f32x4 nt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rl = 4 * lj + i;
+                nt[i] = (lm >= rl) ? 0.f : sBeta[a * SUB + rl] * signA * acc[i];
+            }
+            *reinterpret_cast<f32x4 *>(sAd + (a * SUB + lm) * 20 + 4 * lj) = nt;
+        }
+    }
+}
+
+// B operand of a 16-wide contraction read from a row-major OpT tile:
+// B[k][n] = tile[k][n], lane (n + 16 j) takes rows 4j..4j+3 of column n.
+template <typename OpT>
+__device__ __forceinline__ typename Mma<OpT>::frag16 load16_col(const OpT *tile, int ld, int lj, int lm) {
+    typename Mma<OpT>::frag16 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = tile[(4 * lj + e) * ld + lm];
+    return r;
+}
+
+// Decayed operands of a strong-decay chunk, with 16-token sub-tile references,
+// reading the chunk from global memory (it is not staged for this path).
+// gram_inputs: fp32 Gram inputs K (.) R, Q (.) R, K (.) D with R, D the decay
+// products inside the sub-tile up to / after each token; otherwise the chain
+// operands -GS K+, GS Q+, GS K^T.  Written as plain loops that hold few values
+// at a time, so that this rarely used path adds little register pressure.
+template <typename TIn, int C, int NW>
+__device__ __forceinline__ void prep_slow(
+    bool gram_inputs, const TIn *__restrict__ q, const TIn *__restrict__ k, const float *__restrict__ g,
+    int c0, int L, int64_t rowK, int64_t hK, int tid, const float *sF, float *sKr32, float *sQr32,
+    float *sKD32, typename PrefillCfg<TIn, C, NW>::OpT *sNKp, typename PrefillCfg<TIn, C, NW>::OpT *sQp,
+    typename PrefillCfg<TIn, C, NW>::OpT *sKhT)
+{
+    typedef PrefillCfg<TIn, C, NW> P;
+    typedef typename P::OpT OpT;
+    constexpr int CPT = P::CPT, NGRP = P::NGRP, GPS = SUB / P::GRP;
+    constexpr int LDK = P::LDK, LDC = P::LDC, LDK32 = P::LDK32;
+    constexpr float GS = P::GS;
+    if (tid >= P::NPREP) return;
+    const int pa = tid / (DK / CPT), pc = (tid % (DK / CPT)) * CPT;
+#pragma unroll 1
+    for (int e = 0; e < CPT; ++e) {
+        const int c = pc + e;
+        float erho = 1.f, suff = 1.f;
+        for (int s = 0; s < pa * GPS; ++s) erho *= sF[s * DK + c];
+        for (int s = (pa + 1) * GPS; s < NGRP; ++s) suff *= sF[s * DK + c];
+        float D = 1.f;                      // prod of alpha after r within the sub-tile
+#pragma unroll 1
+        for (int rr = SUB - 1; rr >= 0; --rr) {
+            const int r = pa * SUB + rr;
+            const bool ok = r < L;
+            const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowK + hK + c;
+            const float kv = ok ? to_f(k[off]) : 0.f;
+            if (gram_inputs) sKD32[r * LDK32 + c] = kv * D;
+            else sKhT[c * LDC + r] = from_f<OpT>(GS * kv * D * suff);
+            D *= ok ? __expf(g[off]) : 1.f;
+        }
+        float R = 1.f;                      // prod of alpha up to r within the sub-tile
+#pragma unroll 1
+        for (int rr = 0; rr < SUB; ++rr) {
+            const int r = pa * SUB + rr;
+            const bool ok = r < L;
+            const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowK + hK + c;
+            const float kv = ok ? to_f(k[off]) : 0.f, qv = ok ? to_f(q[off]) : 0.f;
+            R *= ok ? __expf(g[off]) : 1.f;
+            if (gram_inputs) {
+                sKr32[r * LDK32 + c] = kv * R;
+                sQr32[r * LDK32 + c] = qv * R;
+            } else {
+                sNKp[r * LDK + c] = from_f<OpT>(-GS * kv * R * erho);
+                sQp[r * LDK + c] = from_f<OpT>(GS * qv * R * erho);
+            }
         }
     }
 }
 
 template <typename TIn, int C, int NW>
-__global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PrefillCfg<TIn, C, NW>::WAVES_PER_EU)))
+void kda_prefill_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *initial_state, const int32_t *__restrict__ cu_seqlens,
@@ -169,30 +258,30 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
     typedef typename P::OpT OpT;
     typedef Mma<OpT> M;
     constexpr bool kIn16 = P::kIn16;
-    constexpr int NSUB = P::NSUB, BV = P::BV, NT = P::NT, KB = P::KB;
-    constexpr int LDK = P::LDK, LDC = P::LDC, LDK32 = P::LDK32, LDV = P::LDV, LDI = P::LDI;
+    constexpr int NSUB = P::NSUB, BV = P::BV, NT = P::NT, KB = P::KB, CPT = P::CPT;
+    constexpr int SEG = P::SEG, NSEG = P::NSEG, ITEMS = P::ITEMS, GRP = P::GRP, NGRP = P::NGRP;
+    constexpr int LDK = P::LDK, LDC = P::LDC, LDK32 = P::LDK32, LDV = P::LDV;
+    constexpr float GS = P::GS;
 
     extern __shared__ __align__(16) unsigned char smem[];
-    OpT *sKr = reinterpret_cast<OpT *>(smem + P::offKr);
-    OpT *sQr = reinterpret_cast<OpT *>(smem + P::offQr);
-    OpT *sKD = reinterpret_cast<OpT *>(smem + P::offKD);
-    float *sKr32 = reinterpret_cast<float *>(smem + P::offKr32);
-    float *sQr32 = reinterpret_cast<float *>(smem + P::offQr32);
-    float *sKD32 = reinterpret_cast<float *>(smem + P::offKD32);
     OpT *sNKp = reinterpret_cast<OpT *>(smem + P::offNKp);
     OpT *sQp = reinterpret_cast<OpT *>(smem + P::offQp);
+    OpT *sKc = reinterpret_cast<OpT *>(smem + P::offKc);
     OpT *sKhT = reinterpret_cast<OpT *>(smem + P::offKhT);
     TIn *sV = reinterpret_cast<TIn *>(smem + P::offV);
     TIn *sO = reinterpret_cast<TIn *>(smem + P::offO);
-    OpT *sInv = reinterpret_cast<OpT *>(smem + P::offInv);
+    float *sKr32 = reinterpret_cast<float *>(smem + P::offKr32);
+    float *sQr32 = reinterpret_cast<float *>(smem + P::offQr32);
+    float *sKD32 = reinterpret_cast<float *>(smem + P::offKD32);
     float *sAd = reinterpret_cast<float *>(smem + P::offAd);
-    OpT *sNs = reinterpret_cast<OpT *>(smem + P::offNs);
+    OpT *sN = reinterpret_cast<OpT *>(smem + P::offN);
+    OpT *sT = reinterpret_cast<OpT *>(smem + P::offT);
     OpT *sP = reinterpret_cast<OpT *>(smem + P::offP);
     float *sF = reinterpret_cast<float *>(smem + P::offF);
     float *sH = reinterpret_cast<float *>(smem + P::offH);
     float *sGam = reinterpret_cast<float *>(smem + P::offGam);
     float *sBeta = reinterpret_cast<float *>(smem + P::offBeta);
-    float *sInvS = reinterpret_cast<float *>(smem + P::offInvS);
+    float *sTs = reinterpret_cast<float *>(smem + P::offTs);
 
     // ---- workgroup -> (sequence, head, value block); blocks of one unit share an XCD
     const int nblk = dv / BV;
@@ -216,153 +305,218 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
     const int64_t rowV = (int64_t)H * dv;      // token stride of v, out
     const int64_t hK = (int64_t)h * DK;
 
+    // slow-prep item of this thread: sub-tile pa, channels pc .. pc + CPT - 1
+    const bool prep = tid < P::NPREP;
+    const int pa = prep ? tid / (DK / CPT) : 0;
+    const int pc = prep ? (tid % (DK / CPT)) * CPT : 0;
+
     // ---- state slice of this wave: rows 16r + 4*lj + i, column dv0 + 16*wave + lm
     f32x4 S[DK / 16];
     const int col = dv0 + 16 * wave + lm;
     const int64_t sbase = unit * (int64_t)DK * dv;
+    if (initial_state) {
 #pragma unroll
-    for (int r = 0; r < DK / 16; ++r)
+        for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[r][i] = initial_state ? initial_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] : 0.f;
+            for (int i = 0; i < 4; ++i) S[r][i] = initial_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col];
+    } else {
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) S[r] = zero4();
+    }
+
+    // ---- raw chunk data staged in registers, loaded one chunk ahead: item it
+    //      of this thread is segment (tid + it NT) / 64, channels 2 ((tid + it NT) % 64) + {0, 1}.
+    //      Rows past the end of the sequence read the last valid row (in bounds)
+    //      and are masked where they are used, so every load is unconditional.
+    constexpr int VEC = 16 / (int)sizeof(TIn);            // elements per 16-byte vector
+    constexpr int VPR = BV / VEC;                         // vectors per token row
+    constexpr int VITEMS = (C * VPR + NT - 1) / NT;
+    typedef typename Pair<TIn>::type PairT;
+    f32x2 rg[ITEMS][SEG];
+    PairT rk[ITEMS][SEG], rq[ITEMS][SEG];
+    f32x4 rv[VITEMS];
+    float rb = 0.f;
+    auto load_chunk = [&](int cc0) {
+        const int LL = min(C, t_end - cc0);
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = min(tid + it * NT, NSEG * 64 - 1), sg = item / 64, c = 2 * (item % 64);
+#pragma unroll
+            for (int rr = 0; rr < SEG; ++rr) {
+                const int rc = min(sg * SEG + rr, LL - 1);
+                const int64_t off = (int64_t)(cc0 + rc) * rowK + hK + c;
+                rg[it][rr] = *reinterpret_cast<const f32x2 *>(g + off);
+                rk[it][rr] = *reinterpret_cast<const PairT *>(k + off);
+                rq[it][rr] = *reinterpret_cast<const PairT *>(q + off);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VITEMS; ++it) {
+            const int e = tid + it * NT;
+            if (e < C * VPR) {
+                const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
+                rv[it] = *reinterpret_cast<const f32x4 *>(v + (int64_t)(cc0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
+            }
+        }
+        if (tid < C) rb = beta[(int64_t)(cc0 + min(tid, LL - 1)) * H + h];
+    };
+    const int c_last = t_start + ((t_end - t_start - 1) / C) * C;   // start of the last chunk
+    if (t_start < t_end) load_chunk(t_start);
+
+    // product of the group decays over groups [g0, g1) of channel c, in order
+    auto grp_prod = [&](int g0, int g1, int c) {
+        float p = 1.f;
+        for (int s = g0; s < g1; ++s) p *= sF[s * DK + c];
+        return p;
+    };
+    constexpr int GPS = SUB / GRP;                        // groups per sub-tile
 
     for (int c0 = t_start; c0 < t_end; c0 += C) {
         const int L = min(C, t_end - c0);        // valid tokens in this chunk
         __syncthreads();                          // previous chunk done with all LDS
 
-        // ---- 1a. sub-tile gate sums -> F_a = exp(sum); beta; strong-decay test
-        int strong = 0;
-        for (int item = tid; item < NSUB * (DK / 2); item += NT) {
-            const int a = item / (DK / 2), c = 2 * (item % (DK / 2));
-            float s0 = 0.f, s1 = 0.f;
-            for (int rr = 0; rr < SUB; ++rr) {
-                const int r = a * SUB + rr;
-                if (r < L) {
-                    const f32x2 gg = *reinterpret_cast<const f32x2 *>(g + (int64_t)(c0 + r) * rowK + hK + c);
-                    s0 += gg[0];
-                    s1 += gg[1];
+        // ---- 1a. group gate sums -> F = exp(sum); beta
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+            const int item = tid + it * NT, sg = item / 64, c = 2 * (item % 64);
+            if (item < NSEG * 64) {
+#pragma unroll
+                for (int gi = 0; gi < SEG / GRP; ++gi) {
+                    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                    for (int rr = gi * GRP; rr < (gi + 1) * GRP; ++rr) {
+                        const bool ok = sg * SEG + rr < L;
+                        s0 += ok ? rg[it][rr][0] : 0.f;
+                        s1 += ok ? rg[it][rr][1] : 0.f;
+                    }
+                    const int G = (sg * SEG) / GRP + gi;
+                    sF[G * DK + c] = __expf(s0);
+                    sF[G * DK + c + 1] = __expf(s1);
                 }
             }
-            strong |= (s0 < -SPAN_FAST) | (s1 < -SPAN_FAST);
-            sF[a * DK + c] = __expf(s0);
-            sF[a * DK + c + 1] = __expf(s1);
         }
-        for (int r = tid; r < C; r += NT)
-            sBeta[r] = (r < L) ? beta[(int64_t)(c0 + r) * H + h] : 0.f;
-        // fp16 Gram operands need every column factor <= e^8; fp32 input always uses fp32
-        const bool gram32 = !kIn16 || __syncthreads_or(strong);
-        if (!kIn16) __syncthreads();
+        if (tid < C) sBeta[tid] = tid < L ? rb : 0.f;
+        __syncthreads();
 
-        // ---- 1b. tables: H(a,b) = prod_{b<s<a} F_s (b < a), 1/F_a (b = a); gamma = prod F
-        for (int e = tid; e < (P::NPAIR + 1) * DK; e += NT) {
-            const int p = e / DK, c = e % DK;
-            if (p == P::NPAIR) {
-                float gm = 1.f;
-                for (int s = 0; s < NSUB; ++s) gm *= sF[s * DK + c];
-                sGam[c] = gm;
-            } else {
+        // ---- 1b. gamma = prod of all group decays; decay-span test; sub-tile
+        //          tables H(a,b) for the strong-decay Gram
+        int strong = 0;
+        for (int c = tid; c < DK; c += NT) {
+            const float gm = grp_prod(0, NGRP, c);
+            sGam[c] = gm;
+            strong |= gm < __expf(-P::SPAN_CHUNK);
+        }
+        const bool slow = __syncthreads_or(strong);
+        if (slow) {
+            for (int e = tid; e < P::NPAIR * DK; e += NT) {
+                const int p = e / DK, c = e % DK;
                 int a, b;
                 pair_of(p, a, b);
-                float hv;
-                if (b == a) {
-                    hv = 1.f / sF[a * DK + c];
-                } else {
-                    hv = 1.f;
-                    for (int s = b + 1; s < a; ++s) hv *= sF[s * DK + c];
-                }
-                sH[p * DK + c] = gram32 ? hv : hv * (1.f / GRAM16_ROW);
+                sH[p * DK + c] = (b == a) ? 1.f / grp_prod(a * GPS, (a + 1) * GPS, c)
+                                          : grp_prod((b + 1) * GPS, a * GPS, c);
             }
         }
 
-        // ---- 1c. per-token decayed operands (Gram inputs; chain operands unless
-        //          the Gram inputs are fp32 and overlay them)
-        auto decay_prep = [&](bool gram_inputs, bool chain_ops, bool as32) {
-            for (int item = tid; item < NSUB * (DK / 2); item += NT) {
-                const int a = item / (DK / 2), c = 2 * (item % (DK / 2));
-                f32x2 erho = {1.f, 1.f}, suff = {1.f, 1.f};
-                for (int s = 0; s < a; ++s) { erho[0] *= sF[s * DK + c]; erho[1] *= sF[s * DK + c + 1]; }
-                for (int s = a + 1; s < NSUB; ++s) { suff[0] *= sF[s * DK + c]; suff[1] *= sF[s * DK + c + 1]; }
-                f32x2 al[SUB], kk[SUB];
+        // ---- 1c. decayed operands
+        // fast: from the staged registers, chunk-start reference R_r = e^Gamma_r,
+        //       written once for both the Gram and the chain
+        auto prep_fast = [&]() {
 #pragma unroll
-                for (int rr = 0; rr < SUB; ++rr) {
-                    const int r = a * SUB + rr;
-                    if (r < L) {
-                        const int64_t off = (int64_t)(c0 + r) * rowK + hK + c;
-                        const f32x2 gg = *reinterpret_cast<const f32x2 *>(g + off);
-                        al[rr][0] = __expf(gg[0]);
-                        al[rr][1] = __expf(gg[1]);
-                        kk[rr] = load_pair(k + off);
-                    } else {
-                        al[rr] = f32x2{1.f, 1.f};
-                        kk[rr] = f32x2{0.f, 0.f};
-                    }
-                }
-                // backward products: D_r = prod_{s > r in sub-tile} alpha_s
-                f32x2 D = {1.f, 1.f};
+            for (int it = 0; it < ITEMS; ++it) {
+                const int item = tid + it * NT, sg = item / 64, c = 2 * (item % 64);
+                if (item >= NSEG * 64) continue;
+                const int G0 = (sg * SEG) / GRP;
+                f32x2 pre, gm;                          // prefix over earlier groups; all groups
+                pre[0] = grp_prod(0, G0, c);
+                pre[1] = grp_prod(0, G0, c + 1);
+                gm[0] = sGam[c];
+                gm[1] = sGam[c + 1];
+                OpT kh0[SEG], kh1[SEG];
+                f32x2 R;
 #pragma unroll
-                for (int rr = SUB - 1; rr >= 0; --rr) {
-                    const int r = a * SUB + rr;
-                    const float kd0 = kk[rr][0] * D[0], kd1 = kk[rr][1] * D[1];
-                    if (gram_inputs) {
-                        if (as32) store_pair(sKD32 + r * LDK32 + c, kd0, kd1);
-                        else store_pair(sKD + r * LDK + c, kd0, kd1);
-                    }
-                    if (chain_ops) {
-                        sKhT[c * LDC + r] = from_f<OpT>(kd0 * suff[0]);
-                        sKhT[(c + 1) * LDC + r] = from_f<OpT>(kd1 * suff[1]);
-                    }
-                    D = D * al[rr];
-                }
-                // forward products: R_r = prod_{s <= r in sub-tile} alpha_s
-                f32x2 R = {1.f, 1.f};
-#pragma unroll
-                for (int rr = 0; rr < SUB; ++rr) {
-                    const int r = a * SUB + rr;
-                    f32x2 qq = {0.f, 0.f};
-                    if (r < L) qq = load_pair(q + (int64_t)(c0 + r) * rowK + hK + c);
-                    R = R * al[rr];
-                    const float kr0 = kk[rr][0] * R[0], kr1 = kk[rr][1] * R[1];
-                    const float qr0 = qq[0] * R[0], qr1 = qq[1] * R[1];
-                    if (gram_inputs) {
-                        if (as32) {
-                            store_pair(sKr32 + r * LDK32 + c, kr0, kr1);
-                            store_pair(sQr32 + r * LDK32 + c, qr0, qr1);
-                        } else {
-                            store_pair(sKr + r * LDK + c, kr0 * GRAM16_ROW, kr1 * GRAM16_ROW);
-                            store_pair(sQr + r * LDK + c, qr0 * GRAM16_ROW, qr1 * GRAM16_ROW);
+                for (int rr = 0; rr < SEG; ++rr) {
+                    const int r = sg * SEG + rr;
+                    const bool ok = r < L;
+                    if (rr % GRP == 0) {
+                        if (rr > 0) {
+                            pre[0] *= sF[(G0 + rr / GRP - 1) * DK + c];
+                            pre[1] *= sF[(G0 + rr / GRP - 1) * DK + c + 1];
                         }
+                        R = f32x2{1.f, 1.f};
                     }
-                    if (chain_ops) {
-                        store_pair(sNKp + r * LDK + c, -kr0 * erho[0], -kr1 * erho[1]);
-                        store_pair(sQp + r * LDK + c, qr0 * erho[0], qr1 * erho[1]);
-                    }
+                    const float k0 = ok ? to_f(rk[it][rr][0]) : 0.f, k1 = ok ? to_f(rk[it][rr][1]) : 0.f;
+                    const float q0 = ok ? to_f(rq[it][rr][0]) : 0.f, q1 = ok ? to_f(rq[it][rr][1]) : 0.f;
+                    R[0] *= ok ? __expf(rg[it][rr][0]) : 1.f;      // decay inside the group
+                    R[1] *= ok ? __expf(rg[it][rr][1]) : 1.f;
+                    const float e0 = pre[0] * R[0], e1 = pre[1] * R[1];   // e^Gamma_r
+                    const float i0 = __builtin_amdgcn_rcpf(e0), i1 = __builtin_amdgcn_rcpf(e1);
+                    store_pair(sNKp + r * LDK + c, -GS * k0 * e0, -GS * k1 * e1);
+                    store_pair(sQp + r * LDK + c, GS * q0 * e0, GS * q1 * e1);
+                    store_pair(sKc + r * LDK + c, k0 * i0 * (1.f / GS), k1 * i1 * (1.f / GS));
+                    kh0[rr] = from_f<OpT>(GS * k0 * (gm[0] * i0));
+                    kh1[rr] = from_f<OpT>(GS * k1 * (gm[1] * i1));
+                }
+                // K^ transposed: SEG consecutive tokens of channels c, c+1
+                typedef OpT V4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+                for (int rr = 0; rr < SEG; rr += 4) {
+                    V4 w0, w1;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) { w0[x] = kh0[rr + x]; w1[x] = kh1[rr + x]; }
+                    *reinterpret_cast<V4 *>(sKhT + c * LDC + sg * SEG + rr) = w0;
+                    *reinterpret_cast<V4 *>(sKhT + (c + 1) * LDC + sg * SEG + rr) = w1;
                 }
             }
         };
-        const bool overlay = kIn16 && gram32;     // fp32 Gram inputs overlay the chain operands
-        decay_prep(true, !overlay, gram32);
+        if (slow)
+            prep_slow<TIn, C, NW>(true, q, k, g, c0, L, rowK, hK, tid, sF, sKr32, sQr32, sKD32, sNKp, sQp, sKhT);
+        else
+            prep_fast();
         __syncthreads();
 
         // ---- 2. Gram tiles
-        if (gram32)
-            gram_tiles<float, OpT, C, NW>(sKr32, sQr32, sKD32, LDK32, sH, sBeta, sAd, sNs, sP, LDC, wave, lj, lm);
-        else
-            gram_tiles<OpT, OpT, C, NW>(sKr, sQr, sKD, LDK, sH, sBeta, sAd, sNs, sP, LDC, wave, lj, lm);
+        if (slow)
+            gram_tiles<float, OpT, C, NW>(sKr32, sQr32, sKD32, LDK32, sH, 1.f, sBeta, sAd, sN, sP, LDC,
+                                          wave, lj, lm);
+        else   // rows hold -GS K+ and GS Q+, columns K e^-Gamma / GS
+            gram_tiles<OpT, OpT, C, NW>(sNKp, sQp, sKc, LDK, nullptr, -1.f, sBeta, sAd, sN, sP, LDC,
+                                        wave, lj, lm);
         __syncthreads();
 
-        // ---- 3. chain operands after an fp32 Gram; diagonal inverses; value tile
-        if (overlay) decay_prep(false, true, false);
-        for (int e = tid; e < NSUB * SUB; e += NT) {
-            const int a = e / SUB, nc = e % SUB;
-            const float *Nb = sAd + a * SUB * 17;
+        // ---- 3. chain operands after a slow Gram; value tile; next chunk's
+        //         loads (they overlap the rest of this chunk); diagonal blocks of
+        //         (I + N)^-1 by forward substitution, lane = column
+        if (slow)
+            prep_slow<TIn, C, NW>(false, q, k, g, c0, L, rowK, hK, tid, sF, sKr32, sQr32, sKD32, sNKp, sQp, sKhT);
+#pragma unroll
+        for (int it = 0; it < VITEMS; ++it) {
+            const int e = tid + it * NT;
+            if (e < C * VPR) {
+                const int r = e / VPR, cv = (e % VPR) * VEC;
+                *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < L ? rv[it] : zero4();
+            }
+        }
+        // unconditional (the last chunk re-reads itself): a conditional load
+        // would make the compiler wait for it right away
+        load_chunk(min(c0 + C, c_last));
+        if (tid < NSUB * SUB) {
+            const int a = tid / SUB, nc = tid % SUB;
+            const float *NT = sAd + a * SUB * P::LDAD;     // NT[s][r] = N[r][s]
             float x[SUB];
 #pragma unroll
             for (int r = 0; r < SUB; ++r) x[r] = (r == nc) ? 1.f : 0.f;
 #pragma unroll
-            for (int s = 0; s < SUB; ++s)
+            for (int s = 0; s < SUB - 1; ++s) {
+                float col[SUB];
 #pragma unroll
-                for (int r = s + 1; r < SUB; ++r) x[r] -= Nb[r * 17 + s] * x[s];
-            // keep fp16 operands in range: scale the block down if it exceeds 2^14
+                for (int q4 = 0; q4 < SUB; q4 += 4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(NT + s * P::LDAD + q4);
+                    col[q4] = t[0]; col[q4 + 1] = t[1]; col[q4 + 2] = t[2]; col[q4 + 3] = t[3];
+                }
+#pragma unroll
+                for (int r = s + 1; r < SUB; ++r) x[r] -= col[r] * x[s];
+            }
+            // fp16 range: scale the block down by a power of two if it exceeds 2^14
             float sc = 1.f;
             if (kIn16) {
                 float m = 0.f;
@@ -373,44 +527,63 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
                 m = fmaxf(m, __shfl_xor(m, 4));
                 m = fmaxf(m, __shfl_xor(m, 8));
                 if (m > 16384.f) sc = pow2_scale(m);
-                if (nc == 0) sInvS[a] = pow2_inv(sc);
-            } else if (nc == 0) {
-                sInvS[a] = 1.f;
             }
+            if (nc == 0) sTs[a * NSUB + a] = pow2_inv(sc);
 #pragma unroll
-            for (int r = 0; r < SUB; ++r) sInv[(a * SUB + r) * LDI + nc] = from_f<OpT>(x[r] * sc);
-        }
-        {
-            constexpr int VEC = 16 / sizeof(TIn);          // elements per 16-byte vector
-            constexpr int VPR = BV / VEC;                  // vectors per token row
-            for (int e = tid; e < C * VPR; e += NT) {
-                const int r = e / VPR, cv = (e % VPR) * VEC;
-                f32x4 val = zero4();
-                if (r < L)
-                    val = *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + cv);
-                *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = val;
-            }
+            for (int r = 0; r < SUB; ++r) sT[(a * SUB + r) * LDC + a * SUB + nc] = from_f<OpT>(x[r] * sc);
         }
         __syncthreads();
+
+        // ---- 3b. off-diagonal blocks: T_ab = -T_aa sum_{b<=s<a} N_as T_sb, by distance a-b
+#pragma unroll
+        for (int d = 1; d < NSUB; ++d) {
+            for (int b = wave; b + d < NSUB; b += NW) {
+                const int a = b + d;
+                f32x4 y = zero4();
+                const OpT *rowN = sN + (a * SUB + lm) * LDC;
+                for (int s = b; s < a; ++s) {
+                    const f32x4 t = M::mma16(M::load16(rowN, s * SUB, lj),
+                                             load16_col(sT + (s * SUB) * LDC + b * SUB, LDC, lj, lm), zero4());
+                    y += t * sTs[s * NSUB + b];
+                }
+                float sy = 1.f;
+                if (kIn16) sy = pow2_scale(colmax(absmax4(y)));
+                f32x4 t = M::mma16(M::load16(sT + (a * SUB + lm) * LDC, a * SUB, lj), M::from_acc16(y, sy), zero4());
+                t *= -(sTs[a * NSUB + a] * pow2_inv(sy));
+                float sc = 1.f;
+                if (kIn16) {
+                    float m = absmax4(t);
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+                    if (m > 16384.f) sc = pow2_scale(m);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sT[(a * SUB + 4 * lj + i) * LDC + b * SUB + lm] = from_f<OpT>(t[i] * sc);
+                if (lane == 0) sTs[a * NSUB + b] = pow2_inv(sc);
+            }
+            __syncthreads();
+        }
 
         // ---- 4. state-dependent chain (this wave's 16 columns)
         {
             const int vc = 16 * wave + lm;                 // column within the value block
             // state operand, scaled per column into fp16 range
-            float sS = 1.f, isS = 1.f;
+            float sS = 1.f;
             if (kIn16) {
                 float m = 0.f;
 #pragma unroll
                 for (int r = 0; r < DK / 16; ++r) m = fmaxf(m, absmax4(S[r]));
                 sS = pow2_scale(colmax(m));
-                isS = pow2_inv(sS);
             }
+            const float isS = pow2_inv(sS) * (1.f / GS);   // also undoes the GS on K+ / Q+
             typename M::frag Sf[DK / KB];
 #pragma unroll
             for (int kb = 0; kb < DK / KB; ++kb) Sf[kb] = M::from_acc(&S[kb * (KB / 16)], sS);
 
-            // X = Diag(beta) (V - K+ S0)
+            // X = Diag(beta) (V - K+ S0)       (rows of sNKp hold -GS K+)
             f32x4 X[NSUB];
+            float xmax = 0.f;
 #pragma unroll
             for (int mt = 0; mt < NSUB; ++mt) {
                 f32x4 t = zero4();
@@ -422,41 +595,37 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
                     const int r = mt * SUB + 4 * lj + i;
                     X[mt][i] = sBeta[r] * (to_f(sV[r * LDV + vc]) + t[i] * isS);
                 }
+                xmax = fmaxf(xmax, absmax4(X[mt]));
             }
-            // W by forward substitution over sub-tiles (fp16 operands, per-tile column scales)
+            // W = (I + N)^-1 X, block lower triangular, per-block scales
+            float sX = 1.f;
+            if (kIn16) sX = pow2_scale(colmax(xmax));
+            const float isX = pow2_inv(sX);
+            typename M::frag16 X16[NSUB];
+#pragma unroll
+            for (int b = 0; b < NSUB; ++b) X16[b] = M::from_acc16(X[b], sX);
             f32x4 W[NSUB];
-            typename M::frag16 W16[NSUB];
-            float iW[NSUB];
             float wmax = 0.f;
 #pragma unroll
             for (int a = 0; a < NSUB; ++a) {
-                f32x4 acc = X[a];
-                const OpT *rowN = sNs + (a * SUB + lm) * LDC;
+                f32x4 w = zero4();
+                const OpT *rowT = sT + (a * SUB + lm) * LDC;
 #pragma unroll
-                for (int b = 0; b < a; ++b) {
-                    const f32x4 t = M::mma16(M::load16(rowN, b * SUB, lj), W16[b], zero4());
-                    acc += t * iW[b];
+                for (int b = 0; b <= a; ++b) {
+                    const f32x4 t = M::mma16(M::load16(rowT, b * SUB, lj), X16[b], zero4());
+                    w += t * (sTs[a * NSUB + b] * isX);
                 }
-                float sR = 1.f, isR = 1.f;
-                if (kIn16) { sR = pow2_scale(colmax(absmax4(acc))); isR = pow2_inv(sR); }
-                const f32x4 t = M::mma16(M::load16(sInv + (a * SUB + lm) * LDI, 0, lj), M::from_acc16(acc, sR), zero4());
-                W[a] = t * (isR * sInvS[a]);
-                float sW = 1.f;
-                if (kIn16) {
-                    const float m = colmax(absmax4(W[a]));
-                    wmax = fmaxf(wmax, m);
-                    sW = pow2_scale(m);
-                }
-                iW[a] = pow2_inv(sW);
-                W16[a] = M::from_acc16(W[a], sW);
+                W[a] = w;
+                wmax = fmaxf(wmax, absmax4(w));
             }
-            float sWc = 1.f, isWc = 1.f;
-            if (kIn16) { sWc = pow2_scale(wmax); isWc = pow2_inv(sWc); }
+            float sW = 1.f;
+            if (kIn16) sW = pow2_scale(colmax(wmax));
+            const float isW = pow2_inv(sW);
             typename M::frag Wf[C / KB];
 #pragma unroll
-            for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sWc);
+            for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sW);
 
-            // O = Q+ S0 + P W
+            // O = Q+ S0 + P W       (rows of sQp hold GS Q+)
 #pragma unroll
             for (int mt = 0; mt < NSUB; ++mt) {
                 f32x4 o1 = zero4(), o2 = zero4();
@@ -467,11 +636,12 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
 #pragma unroll
                 for (int kb = 0; kb < C / KB; ++kb)
                     if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load(rowP, kb * KB, lj), Wf[kb], o2);
-                const f32x4 o = o1 * isS + o2 * isWc;
+                const f32x4 o = o1 * isS + o2 * isW;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * LDV + vc] = from_f<TIn>(o[i]);
             }
-            // S = Diag(gamma) S0 + K^T W
+            // S = Diag(gamma) S0 + K^T W       (rows of sKhT hold GS K^ per channel)
+            const float isWk = isW * (1.f / GS);
 #pragma unroll
             for (int r = 0; r < DK / 16; ++r) {
                 f32x4 t = zero4();
@@ -479,21 +649,17 @@ __global__ __launch_bounds__(64 * NW) void kda_prefill_kernel(
 #pragma unroll
                 for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load(rowK, kb * KB, lj), Wf[kb], t);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[r][i] = S[r][i] * sGam[16 * r + 4 * lj + i] + t[i] * isWc;
+                for (int i = 0; i < 4; ++i) S[r][i] = S[r][i] * sGam[16 * r + 4 * lj + i] + t[i] * isWk;
             }
         }
         __syncthreads();
 
         // ---- 5. output tile -> global (valid tokens only)
-        {
-            constexpr int VEC = 16 / sizeof(TIn);
-            constexpr int VPR = BV / VEC;
-            for (int e = tid; e < C * VPR; e += NT) {
-                const int r = e / VPR, cv = (e % VPR) * VEC;
-                if (r < L)
-                    *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + cv) =
-                        *reinterpret_cast<const f32x4 *>(sO + r * LDV + cv);
-            }
+        for (int e = tid; e < C * VPR; e += NT) {
+            const int r = e / VPR, cv = (e % VPR) * VEC;
+            if (r < L)
+                *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + cv) =
+                    *reinterpret_cast<const f32x4 *>(sO + r * LDV + cv);
         }
     }
 
@@ -549,8 +715,8 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
     if (chunk == CC && dv_block == 16 * NWW)                                                       \
         return launch_prefill_t<TT, CC, NWW>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, stream);
     if (bf16) {
-        KDA_CASE(bf16_t, 64, 1) KDA_CASE(bf16_t, 64, 2) KDA_CASE(bf16_t, 64, 4) KDA_CASE(bf16_t, 64, 8)
         KDA_CASE(bf16_t, 32, 1) KDA_CASE(bf16_t, 32, 2) KDA_CASE(bf16_t, 32, 4) KDA_CASE(bf16_t, 32, 8)
+        KDA_CASE(bf16_t, 64, 2) KDA_CASE(bf16_t, 64, 4) KDA_CASE(bf16_t, 64, 8)
     } else {
         KDA_CASE(float, 32, 1) KDA_CASE(float, 32, 2) KDA_CASE(float, 32, 4) KDA_CASE(float, 32, 8)
         KDA_CASE(float, 16, 1) KDA_CASE(float, 16, 2) KDA_CASE(float, 16, 4) KDA_CASE(float, 16, 8)

@@ -86,8 +86,9 @@ kda_status kda_prefill(const void *q, const void *k, const void *v,
 
 /*
  * kda_prefill_ex -- kda_prefill with explicit kernel tiling (tests, tuning).
- *   chunk    tokens per chunk: 32 or 64 for bf16, 16 or 32 for fp32; 0 = default
- *   dv_block value columns per workgroup: 16, 32, 64 or 128; 0 = automatic
+ *   chunk    tokens per chunk: 32 or 64 for bf16, 16 or 32 for fp32; 0 = 32
+ *   dv_block value columns per workgroup: 16, 32, 64 or 128 (at least 32 for
+ *            64-token bf16 chunks); 0 = automatic
  * Any tiling gives the same result up to fp32 rounding order.  Other values
  * return KDA_ERR_UNSUPPORTED.
  */

@@ -87,6 +87,7 @@ def test_prefill_null_pointer(lib, field):
     (dict(chunk=16), K.KDA_ERR_UNSUPPORTED),                    # bf16 supports 32 / 64
     (dict(dtype=K.KDA_F32, chunk=64), K.KDA_ERR_UNSUPPORTED),   # fp32 supports 16 / 32
     (dict(dvb=24), K.KDA_ERR_UNSUPPORTED),
+    (dict(chunk=64, dvb=16), K.KDA_ERR_UNSUPPORTED),             # 64-token bf16 chunks need >= 2 waves
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill(lib, **kw) == code
