@@ -2,9 +2,10 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  * kda_prefill over the long-context varlen batch (8 sequences, lengths drawn
-    log-uniform over [1K, 256K] and rescaled to 1,048,576 tokens, 16 heads,
-    dk = dv = 128, bf16 q/k/v, fp32 g/beta/state, zero initial state), then
+  * kda_prefill_cp over the long-context varlen batch (8 sequences, lengths
+    drawn log-uniform over [1K, 256K] and rescaled to 1,048,576 tokens, 16
+    heads, dk = dv = 128, bf16 q/k/v, fp32 g/beta/state, zero initial state;
+    sequences split into segments that run side by side), then
   * 64 consecutive in-place kda_decode_step calls on the decode batch
     (512 sequences x 32 heads, 1 GiB fp32 state).
 Inputs are generated on the device before timing (resident in HBM).
@@ -14,6 +15,7 @@ heads each); the decode figures sit under "decode".  Kernel durations come from
 HIP events recorded on the stream the kernels run on, inside the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--prefill cp|plain] [--seg-len L]
 """
 import argparse
 import hashlib
@@ -97,6 +99,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", choices=("cp", "plain"), default="cp",
+                    help="cp: kda_prefill_cp (segments side by side); plain: kda_prefill")
+    ap.add_argument("--seg-len", type=int, default=0, help="kda_prefill_cp segment length (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -134,11 +139,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     stream = torch.cuda.current_stream()
+    ws = None
+    if args.prefill == "cp":
+        ws_bytes = K.kda_prefill_cp_workspace_size(N, T, H, DK, DV, args.seg_len)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def prefill():
+        if args.prefill == "cp":
+            K.kda_prefill_cp(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, pre["cu_seqlens"], out,
+                             fin, seg_len=args.seg_len, workspace=ws)
+        else:
+            K.kda_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, pre["cu_seqlens"], out, fin)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        K.kda_prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, pre["cu_seqlens"], out, fin)
+        prefill()
         if ev is not None:
             ev[1].record(stream)
         for s in range(args.decode_steps):

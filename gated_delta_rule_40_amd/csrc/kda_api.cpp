@@ -13,7 +13,14 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          const void *k, const void *v, const float *g,
                                          const float *beta, const float *init, const int32_t *cu,
                                          int32_t N, int32_t T_tot, int32_t H, int32_t dv,
-                                         void *out, float *fin, hipStream_t stream);
+                                         void *out, float *fin, const int32_t *plan, int32_t num_segs,
+                                         int32_t mode, const float *seg_init, float *seg_out,
+                                         hipStream_t stream);
+extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
+                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, hipStream_t stream);
+extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
+                                            const int32_t *seq_seg, const float *seg_out, float *seg_init,
+                                            hipStream_t stream);
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, float *state,
                                         int32_t N, int32_t H, void *out, hipStream_t stream);
@@ -88,7 +95,8 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const flo
     }
     hipError_t e = kda_launch_prefill(bf16 ? 1 : 0, chunk, dv_block, q, k, v, g, beta, initial_state,
                                       cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                                      final_state, reinterpret_cast<hipStream_t>(stream));
+                                      final_state, nullptr, 0, 0, nullptr, nullptr,
+                                      reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -100,6 +108,98 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const float 
 {
     return kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens,
                           num_heads, dk, dv, dtype, out, final_state, 0, 0, stream);
+}
+
+// ---------------------------------------------------------------- context parallel
+namespace {
+
+constexpr int32_t kCpChunk = 32;     // chunk size of the segmented runs
+constexpr int32_t kCpBlock = 64;     // value columns per workgroup of the segmented runs
+
+struct CpLayout {
+    size_t plan, seq_seg, seg_out, seg_init, total;
+    int32_t max_segs;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace sections: plan [max_segs][4] int32, per-sequence first segment
+// [N + 1] int32, summaries [max_segs][H][dk][dv + dk] fp32, entering states
+// [max_segs][H][dk][dv] fp32.  max_segs bounds the segment count: every
+// sequence of length L takes max(1, ceil(L / seg_len)) segments.
+bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t seg_len, CpLayout *lay)
+{
+    const int64_t segs = (int64_t)T / seg_len + 1 + N;
+    if (segs > INT32_MAX / 4) return false;
+    lay->max_segs = (int32_t)segs;
+    lay->plan = 0;
+    lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
+    lay->seg_out = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->seg_init = align256(lay->seg_out + sizeof(float) * (size_t)segs * H * dk * (dv + dk));
+    lay->total = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * dk * dv);
+    return true;
+}
+
+// Default segment length: long enough that the extra segment-summary work
+// stays a fraction of the total, short enough that a long sequence splits
+// into several segments that run side by side.
+int32_t cp_default_seg_len(int32_t T, int32_t H)
+{
+    int64_t len = (int64_t)T * H / 512;
+    len = len < 4096 ? 4096 : (len > 65536 ? 65536 : len);
+    return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
+}
+
+}  // namespace
+
+size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                     int32_t dk, int32_t dv, int32_t seg_len)
+{
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || dk != kHeadDim || dv != kHeadDim) return 0;
+    if (seg_len == 0) seg_len = cp_default_seg_len(total_tokens, num_heads);
+    if (seg_len < kCpChunk || seg_len % kCpChunk) return 0;
+    CpLayout lay;
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, seg_len, &lay)) return 0;
+    return lay.total;
+}
+
+kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                          int32_t dv, kda_dtype dtype, void *out, float *final_state, int32_t seg_len,
+                          void *workspace, size_t workspace_bytes, kda_stream_t stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, out, dk, dv, dtype);
+    if (st == KDA_ERR_INVALID_ARG) return st;
+    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || seg_len < 0)
+        return KDA_ERR_INVALID_ARG;
+    if (st != KDA_OK) return st;
+    if (seg_len == 0) seg_len = cp_default_seg_len(total_tokens, num_heads);
+    if (seg_len < kCpChunk || seg_len % kCpChunk) return KDA_ERR_UNSUPPORTED;
+    CpLayout lay;
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, seg_len, &lay)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)lay.max_segs * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return KDA_OK;
+    const int bf16 = dtype == KDA_BF16 ? 1 : 0;
+    char *ws = static_cast<char *>(workspace);
+    int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
+    int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
+    float *seg_out = reinterpret_cast<float *>(ws + lay.seg_out);
+    float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg, s);
+    if (e == hipSuccess)   // segment summaries (segments with a successor)
+        e = kda_launch_prefill(bf16, kCpChunk, kCpBlock, q, k, v, g, beta, nullptr, cu_seqlens, num_seqs,
+                               total_tokens, num_heads, dv, out, nullptr, plan, lay.max_segs, 1, nullptr,
+                               seg_out, s);
+    if (e == hipSuccess)   // entering state of every segment
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, s);
+    if (e == hipSuccess)   // outputs and final states
+        e = kda_launch_prefill(bf16, kCpChunk, kCpBlock, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs,
+                               total_tokens, num_heads, dv, out, final_state, plan, lay.max_segs, 0,
+                               seg_init, nullptr, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g,

@@ -119,6 +119,23 @@ struct PrefillCfg {
     static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
 };
 
+// Segmented (context-parallel) execution.  A plan lists segments of the
+// packed sequences as {sequence, first token, end token, flags}; entries with
+// sequence < 0 are unused.  SEG_SUMMARY runs each segment from a zero state
+// over dv value columns plus DK transition columns (V = 0, entering state I)
+// and writes [S_end | transition]; SEG_OUTPUT runs each segment from its
+// entering state (seg_init) and writes outputs and, for a last segment, the
+// final state.
+enum { SEG_OUTPUT = 0, SEG_SUMMARY = 1 };
+enum { SEG_FIRST = 1, SEG_LAST = 2 };
+struct SegArgs {
+    const int32_t *plan;     // [num_segs][4] or nullptr (one unit per sequence)
+    int32_t num_segs;
+    int32_t mode;            // SEG_OUTPUT or SEG_SUMMARY
+    const float *seg_init;   // [num_segs][H][DK][dv] entering states (SEG_OUTPUT)
+    float *seg_out;          // [num_segs][H][DK][dv + DK] summaries (SEG_SUMMARY)
+};
+
 // sub-tile pair p -> (a, b), b <= a
 __device__ __forceinline__ void pair_of(int p, int &a, int &b) {
     a = 0;
@@ -252,7 +269,7 @@ void kda_prefill_kernel(
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *initial_state, const int32_t *__restrict__ cu_seqlens,
     int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
-    TIn *__restrict__ out, float *final_state)
+    TIn *__restrict__ out, float *final_state, SegArgs seg)
 {
     typedef PrefillCfg<TIn, C, NW> P;
     typedef typename P::OpT OpT;
@@ -283,19 +300,34 @@ void kda_prefill_kernel(
     float *sBeta = reinterpret_cast<float *>(smem + P::offBeta);
     float *sTs = reinterpret_cast<float *>(smem + P::offTs);
 
-    // ---- workgroup -> (sequence, head, value block); blocks of one unit share an XCD
-    const int nblk = dv / BV;
+    // ---- workgroup -> (work unit, value block); blocks of one unit share an XCD.
+    //      A work unit is a (sequence, head) pair, or a (segment, head) pair when
+    //      a segment plan is given; summary mode adds DK transition columns.
+    const bool segmented = seg.plan != nullptr;
+    const bool summary = seg.mode == SEG_SUMMARY;
+    const int ncols = summary ? dv + DK : dv;
+    const int nblk = ncols / BV;
     const int wg = blockIdx.x;
     const int xcd = wg & 7, slot = wg >> 3;
     const int vb = slot % nblk;
     const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
-    if (unit >= (int64_t)num_seqs * num_heads) return;
-    const int n = (int)(unit / num_heads), h = (int)(unit % num_heads);
-    const int dv0 = vb * BV;
-
-    int t_start = cu_seqlens[n], t_end = cu_seqlens[n + 1];
+    if (unit >= (int64_t)(segmented ? seg.num_segs : num_seqs) * num_heads) return;
+    const int su = (int)(unit / num_heads), h = (int)(unit % num_heads);
+    int n = su, t_start, t_end, sflags = SEG_FIRST | SEG_LAST;
+    if (segmented) {
+        n = seg.plan[4 * su];
+        t_start = seg.plan[4 * su + 1];
+        t_end = seg.plan[4 * su + 2];
+        sflags = seg.plan[4 * su + 3];
+        if (n < 0 || (summary && (sflags & SEG_LAST))) return;   // unused entry / summary not needed
+    } else {
+        t_start = cu_seqlens[n];
+        t_end = cu_seqlens[n + 1];
+    }
     t_start = min(max(t_start, 0), total_tokens);
     t_end = min(max(t_end, t_start), total_tokens);
+    const int dv0 = vb * BV;
+    const bool trans_cols = summary && dv0 >= dv;   // transition columns: V = 0, entering state I
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -313,15 +345,31 @@ void kda_prefill_kernel(
     // ---- state slice of this wave: rows 16r + 4*lj + i, column dv0 + 16*wave + lm
     f32x4 S[DK / 16];
     const int col = dv0 + 16 * wave + lm;
-    const int64_t sbase = unit * (int64_t)DK * dv;
-    if (initial_state) {
+    const int64_t sbase = ((int64_t)n * num_heads + h) * DK * dv;   // this (sequence, head) in init/final
+    const float *S_in = nullptr;
+    int64_t S_in_base = 0;
+    if (summary) {
+        S_in = nullptr;                                   // zero (value columns) or identity
+    } else if (segmented) {
+        // every segment, a first one included, enters from seg_init: the
+        // initial state was copied there before this pass, so a last segment
+        // may overwrite it (final_state == initial_state) while others run
+        S_in = seg.seg_init;
+        S_in_base = ((int64_t)su * num_heads + h) * DK * dv;
+    } else if (initial_state) {
+        S_in = initial_state;
+        S_in_base = sbase;
+    }
+    if (S_in) {
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[r][i] = initial_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col];
+            for (int i = 0; i < 4; ++i) S[r][i] = S_in[S_in_base + (int64_t)(16 * r + 4 * lj + i) * dv + col];
     } else {
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r) S[r] = zero4();
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[r][i] = (trans_cols && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
     }
 
     // ---- raw chunk data staged in registers, loaded one chunk ahead: item it
@@ -355,7 +403,8 @@ void kda_prefill_kernel(
             const int e = tid + it * NT;
             if (e < C * VPR) {
                 const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
-                rv[it] = *reinterpret_cast<const f32x4 *>(v + (int64_t)(cc0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
+                rv[it] = trans_cols ? zero4()
+                                    : *reinterpret_cast<const f32x4 *>(v + (int64_t)(cc0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
             }
         }
         if (tid < C) rb = beta[(int64_t)(cc0 + min(tid, LL - 1)) * H + h];
@@ -625,9 +674,9 @@ void kda_prefill_kernel(
 #pragma unroll
             for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sW);
 
-            // O = Q+ S0 + P W       (rows of sQp hold GS Q+)
+            // O = Q+ S0 + P W       (rows of sQp hold GS Q+); not needed for a summary
 #pragma unroll
-            for (int mt = 0; mt < NSUB; ++mt) {
+            for (int mt = 0; mt < (summary ? 0 : NSUB); ++mt) {
                 f32x4 o1 = zero4(), o2 = zero4();
                 const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
 #pragma unroll
@@ -655,7 +704,7 @@ void kda_prefill_kernel(
         __syncthreads();
 
         // ---- 5. output tile -> global (valid tokens only)
-        for (int e = tid; e < C * VPR; e += NT) {
+        for (int e = tid; e < (summary ? 0 : C * VPR); e += NT) {
             const int r = e / VPR, cv = (e % VPR) * VEC;
             if (r < L)
                 *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + cv) =
@@ -663,7 +712,14 @@ void kda_prefill_kernel(
         }
     }
 
-    if (final_state) {
+    if (summary) {
+        // segment summary: [S_end from zero | segment transition], row stride dv + DK
+        float *dst = seg.seg_out + ((int64_t)su * num_heads + h) * DK * (dv + DK);
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i];
+    } else if (final_state && (sflags & SEG_LAST)) {
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -677,7 +733,7 @@ template <typename TIn, int C, int NW>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *init, const int32_t *cu,
                                    int32_t N, int32_t T_tot, int32_t H, int32_t dv, void *out,
-                                   float *fin, hipStream_t stream)
+                                   float *fin, SegArgs seg, hipStream_t stream)
 {
     typedef PrefillCfg<TIn, C, NW> P;
     auto kern = kda_prefill_kernel<TIn, C, NW>;
@@ -688,16 +744,119 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t units = (int64_t)N * H;
-    const int nblk = dv / P::BV;
+    const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
+    const int ncols = seg.mode == SEG_SUMMARY ? dv + DK : dv;
+    const int nblk = ncols / P::BV;
     const int64_t groups = (units + 7) / 8;
     const int64_t grid = groups * 8 * nblk;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(P::NT), P::bytes, stream,
                        static_cast<const TIn *>(q), static_cast<const TIn *>(k), static_cast<const TIn *>(v),
-                       g, beta, init, cu, N, T_tot, H, dv, static_cast<TIn *>(out), fin);
+                       g, beta, init, cu, N, T_tot, H, dv, static_cast<TIn *>(out), fin, seg);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------- segment planning
+// One workgroup: segments per sequence (at least one, so that empty sequences
+// still produce their final state), exclusive scan, plan entries.
+__global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restrict__ cu, int32_t N,
+                                                          int32_t T_tot, int32_t seg_len, int32_t max_segs,
+                                                          int32_t *__restrict__ plan,
+                                                          int32_t *__restrict__ seq_seg)
+{
+    __shared__ int64_t scan[256];
+    int64_t carry = 0;                                 // 64-bit: cu is not trusted
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + (int)threadIdx.x;
+        int32_t t0 = 0, t1 = 0, ns = 0;
+        if (n < N) {
+            t0 = min(max(cu[n], 0), T_tot);
+            t1 = min(max(cu[n + 1], t0), T_tot);
+            ns = max(1, (int32_t)(((int64_t)t1 - t0 + seg_len - 1) / seg_len));
+        }
+        scan[threadIdx.x] = ns;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {       // inclusive scan
+            const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            scan[threadIdx.x] += x;
+            __syncthreads();
+        }
+        const int64_t start = carry + scan[threadIdx.x] - ns;
+        if (n < N) {
+            // With non-decreasing cu the host bound on max_segs always holds;
+            // otherwise segments past it are dropped (memory-safe, result unspecified).
+            seq_seg[n] = (int32_t)min(start, (int64_t)max_segs);
+            for (int s = 0; s < ns && start + s < max_segs; ++s) {
+                const int gs = (int)(start + s);
+                plan[4 * gs] = n;
+                plan[4 * gs + 1] = t0 + s * seg_len;
+                plan[4 * gs + 2] = min(t0 + (s + 1) * seg_len, t1);
+                plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) | (s == ns - 1 ? SEG_LAST : 0);
+            }
+        }
+        carry += scan[255];
+        __syncthreads();
+    }
+    const int32_t used = (int32_t)min(carry, (int64_t)max_segs);
+    if (threadIdx.x == 0) seq_seg[N] = used;
+    for (int gs = used + (int)threadIdx.x; gs < max_segs; gs += 256) {
+        plan[4 * gs] = -1;
+        plan[4 * gs + 1] = 0;
+        plan[4 * gs + 2] = 0;
+        plan[4 * gs + 3] = 0;
+    }
+}
+
+// ------------------------------------------------------ segment combination
+// Per (sequence, head, 64 value columns): walk the segments in order,
+// S_in(first) = initial state, S_in(s+1) = M_s S_in(s) + S_s^0 on fp32 MFMA,
+// writing each segment's entering state.  The state slice lives in MFMA
+// accumulator registers (row tiles as in the prefill kernel); M is read
+// straight from global memory as A operands.
+__global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
+                                                             int32_t H, int32_t dv,
+                                                             const int32_t *__restrict__ seq_seg,
+                                                             const float *__restrict__ seg_out,
+                                                             float *__restrict__ seg_init)
+{
+    typedef Mma<float> M;
+    const int nblk = dv / 64;
+    const int64_t unit = blockIdx.x / nblk;
+    if (unit >= (int64_t)N * H) return;
+    const int n = (int)(unit / H), h = (int)(unit % H);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
+    const int col = (blockIdx.x % nblk) * 64 + 16 * wave + lm;
+    const int ld = dv + DK;
+    f32x4 S[DK / 16];
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[r][i] = init ? init[((int64_t)n * H + h) * DK * dv + (int64_t)(16 * r + 4 * lj + i) * dv + col] : 0.f;
+    const int s0 = seq_seg[n], s1 = seq_seg[n + 1];
+    for (int gs = s0; gs < s1; ++gs) {
+        float *dst = seg_init + ((int64_t)gs * H + h) * DK * dv;
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
+        if (gs == s1 - 1) break;
+        const float *src = seg_out + ((int64_t)gs * H + h) * DK * ld;
+        f32x4 Sn[DK / 16];
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sn[r][i] = src[(int64_t)(16 * r + 4 * lj + i) * ld + col];   // S^0
+            const float *mrow = src + (int64_t)(16 * r + lm) * ld + dv;                              // M row
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; ++kb)
+                Sn[r] = M::mma(*reinterpret_cast<const f32x4 *>(mrow + 16 * kb + 4 * lj), S[kb], Sn[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) S[r] = Sn[r];
+    }
 }
 
 }  // namespace kda
@@ -708,12 +867,15 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          const void *q, const void *k, const void *v,
                                          const float *g, const float *beta, const float *init,
                                          const int32_t *cu, int32_t N, int32_t T_tot, int32_t H,
-                                         int32_t dv, void *out, float *fin, hipStream_t stream)
+                                         int32_t dv, void *out, float *fin,
+                                         const int32_t *plan, int32_t num_segs, int32_t mode,
+                                         const float *seg_init, float *seg_out, hipStream_t stream)
 {
     using namespace kda;
+    const SegArgs seg = {plan, num_segs, mode, seg_init, seg_out};
 #define KDA_CASE(TT, CC, NWW)                                                                    \
     if (chunk == CC && dv_block == 16 * NWW)                                                       \
-        return launch_prefill_t<TT, CC, NWW>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, stream);
+        return launch_prefill_t<TT, CC, NWW>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (bf16) {
         KDA_CASE(bf16_t, 32, 1) KDA_CASE(bf16_t, 32, 2) KDA_CASE(bf16_t, 32, 4) KDA_CASE(bf16_t, 32, 8)
         KDA_CASE(bf16_t, 64, 2) KDA_CASE(bf16_t, 64, 4) KDA_CASE(bf16_t, 64, 8)
@@ -723,4 +885,24 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
     }
 #undef KDA_CASE
     return hipErrorInvalidValue;
+}
+
+extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
+                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_tot, seg_len, max_segs,
+                       plan, seq_seg);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
+                                            const int32_t *seq_seg, const float *seg_out, float *seg_init,
+                                            hipStream_t stream)
+{
+    const int64_t grid = (int64_t)N * H * (dv / 64);
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, init, N, H, dv,
+                       seq_seg, seg_out, seg_init);
+    return hipGetLastError();
 }

@@ -7,6 +7,8 @@ fallback: if the library is missing the calls raise.
 
     kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     kda_prefill_ex(..., chunk=0, dv_block=0)
+    kda_prefill_cp(..., seg_len=0, workspace=None)
+    kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len)
     kda_decode_step(q, k, v, g, beta, state_inout, out)
 """
 from __future__ import annotations
@@ -23,7 +25,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 
-EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_decode_step", "kda_status_string", "kda_version")
+EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_prefill_cp", "kda_prefill_cp_workspace_size",
+           "kda_decode_step", "kda_status_string", "kda_version")
 
 _lib = None
 
@@ -49,6 +52,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_prefill_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
                                    i32, i32, vp]
     lib.kda_prefill_ex.restype = ctypes.c_int
+    lib.kda_prefill_cp.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
+                                   i32, vp, ctypes.c_size_t, vp]
+    lib.kda_prefill_cp.restype = ctypes.c_int
+    lib.kda_prefill_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.kda_prefill_cp_workspace_size.restype = ctypes.c_size_t
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
@@ -92,11 +100,7 @@ def _require(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
-def kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                   chunk: int = 0, dv_block: int = 0, stream=None) -> None:
-    """Packed varlen prefill.  q, k, g: [T, H, dk]; v, out: [T, H, dv];
-    beta: [T, H] fp32; initial_state/final_state: [N, H, dk, dv] fp32 or None;
-    cu_seqlens: [N+1] int32 on the device."""
+def _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state):
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.shape[0] - 1
@@ -112,10 +116,43 @@ def kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state
         if s is not None:
             _require(s.dtype == torch.float32 and s.is_contiguous() and tuple(s.shape) == (N, H, dk, dv),
                      "%s must be contiguous float32 [N, H, dk, dv]" % name)
+    return N, T, H, dk, dv
+
+
+def kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                   chunk: int = 0, dv_block: int = 0, stream=None) -> None:
+    """Packed varlen prefill.  q, k, g: [T, H, dk]; v, out: [T, H, dv];
+    beta: [T, H] fp32; initial_state/final_state: [N, H, dk, dv] fp32 or None;
+    cu_seqlens: [N+1] int32 on the device."""
+    N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     lib = load()
     _check(lib.kda_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                               _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
                               _ptr(final_state), int(chunk), int(dv_block), _stream(stream)))
+
+
+def kda_prefill_cp_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                                  seg_len: int = 0) -> int:
+    """Bytes of device workspace kda_prefill_cp needs (0 = unsupported sizes)."""
+    return int(load().kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len))
+
+
+def kda_prefill_cp(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                   seg_len: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Context-parallel prefill (same arguments and result as kda_prefill):
+    sequences are split into seg_len-token segments that run side by side.
+    ``workspace`` is a uint8 device tensor of at least
+    kda_prefill_cp_workspace_size(...) bytes; if None, one is allocated."""
+    N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    need = kda_prefill_cp_workspace_size(N, T, H, dk, dv, seg_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    _check(lib.kda_prefill_cp(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                              _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
+                              _ptr(final_state), int(seg_len), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, stream=None) -> None:

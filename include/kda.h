@@ -101,6 +101,39 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v,
                           int32_t chunk, int32_t dv_block, kda_stream_t stream);
 
 /*
+ * kda_prefill_cp -- kda_prefill with context parallelism inside the device.
+ * Each sequence is split into segments of seg_len tokens that
+ * run side by side: every segment but a sequence's last is first run from a
+ * zero state to give its end state S^0 and its transition M (S_end = M S_in
+ * + S^0, the recurrence being affine in the entering state); the segments'
+ * entering states are then chained, S_in(s+1) = M_s S_in(s) + S^0_s; finally
+ * every segment is run from its entering state for the outputs.  This is the
+ * fixed-size-state-fragment scheme of page ailearn.mscapital.top/kimi-k3.html,
+ * card "传固定状态片段" (local cumulative transform and zero-state fragment,
+ * then a prefix combination), applied across the compute units of one GPU.
+ * Results equal kda_prefill up to fp32 rounding order.
+ *
+ *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
+ *   workspace  device memory of at least kda_prefill_cp_workspace_size(...)
+ *              bytes, 256-byte aligned, owned by the caller, contents
+ *              ignored on entry; calls that share one workspace must not
+ *              overlap in time.
+ * Other arguments, conventions and errors as kda_prefill (final_state ==
+ * initial_state is allowed).  KDA_ERR_INVALID_ARG if the workspace is
+ * missing, misaligned or too small.
+ */
+size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                     int32_t dk, int32_t dv, int32_t seg_len);
+
+kda_status kda_prefill_cp(const void *q, const void *k, const void *v,
+                          const float *g, const float *beta,
+                          const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                          int32_t dk, int32_t dv, kda_dtype dtype,
+                          void *out, float *final_state, int32_t seg_len,
+                          void *workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
  * kda_decode_step -- one new token per (sequence, head), state updated in place
  * (the same recurrence step; page card "KDA 单头递归").
  *

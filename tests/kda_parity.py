@@ -52,6 +52,22 @@ def run_prefill(inp, chunk=0, dv_block=0, final=True, out=None, fin=None, use_in
     return out, fin
 
 
+def run_prefill_cp(inp, seg_len=0, final=True, out=None, fin=None, use_init=True, workspace=None):
+    q = inp["q"]
+    T, H, dk = q.shape
+    dv = inp["v"].shape[-1]
+    N = inp["cu_seqlens"].shape[0] - 1
+    if out is None:
+        out = torch.empty(T, H, dv, dtype=q.dtype, device=q.device)
+    if final and fin is None:
+        fin = torch.empty(N, H, dk, dv, dtype=torch.float32, device=q.device)
+    init = inp["initial_state"] if use_init else None
+    K.kda_prefill_cp(q, inp["k"], inp["v"], inp["g"], inp["beta"], init, inp["cu_seqlens"], out,
+                     fin if final else None, seg_len=seg_len, workspace=workspace)
+    torch.cuda.synchronize()
+    return out, fin
+
+
 def oracle_prefill(inp, use_init=True, threads=0):
     init = inp["initial_state"] if use_init else None
     return O.prefill(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]), host(inp["beta"]),

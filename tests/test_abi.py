@@ -121,3 +121,44 @@ def test_decode_empty_batch_is_a_no_op(lib):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(FileNotFoundError):
         K.load(str(tmp_path / "missing.so"))
+
+
+def prefill_cp(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, init=NULL, cu=P, N=1, T=4096, H=1, dk=128, dv=128,
+             dtype=K.KDA_BF16, out=P, fin=NULL, seg=1024, ws=ctypes.c_void_p(0x100000), wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_prefill_cp(a["q"], a["k"], a["v"], a["g"], a["beta"], a["init"], a["cu"], a["N"], a["T"],
+                              a["H"], a["dk"], a["dv"], a["dtype"], a["out"], a["fin"], a["seg"], a["ws"],
+                              a["wsb"], None)
+
+
+def test_cp_workspace_size(lib):
+    ws = lib.kda_prefill_cp_workspace_size
+    small = ws(1, 4096, 1, 128, 128, 1024)
+    # at least: summaries (dk x (dv + dk)) and entering states (dk x dv) per segment
+    assert small >= 5 * 128 * (256 + 128) * 4
+    assert ws(1, 8192, 1, 128, 128, 1024) > small           # more segments
+    assert ws(1, 4096, 4, 128, 128, 1024) > small           # more heads
+    assert ws(1, 4096, 1, 128, 128, 0) > 0                  # automatic segment length
+    assert ws(1, 4096, 1, 64, 128, 1024) == 0               # unsupported head size
+    assert ws(1, 4096, 1, 128, 128, 48) == 0                # not a multiple of 32
+    assert ws(-1, 4096, 1, 128, 128, 1024) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(ws=ctypes.c_void_p(0x100010)), K.KDA_ERR_INVALID_ARG),   # workspace not 256-byte aligned
+    (dict(wsb=1024), K.KDA_ERR_INVALID_ARG),                       # workspace too small
+    (dict(seg=-32), K.KDA_ERR_INVALID_ARG),
+    (dict(cu=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(q=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(seg=48), K.KDA_ERR_UNSUPPORTED),
+    (dict(seg=16), K.KDA_ERR_UNSUPPORTED),
+    (dict(dk=64), K.KDA_ERR_UNSUPPORTED),
+])
+def test_prefill_cp_rejects(lib, kw, code):
+    assert prefill_cp(lib, **kw) == code
+
+
+def test_prefill_cp_empty_batch_is_a_no_op(lib):
+    assert prefill_cp(lib, N=0, T=0) == K.KDA_OK

@@ -14,7 +14,7 @@ import torch
 
 from gated_delta_rule_40_amd import inputs as I
 from gated_delta_rule_40_amd import libkda as K
-from kda_parity import TOL, assert_close, host, log, oracle_prefill, run_prefill, to_dev
+from kda_parity import TOL, assert_close, host, log, oracle_prefill, run_prefill, run_prefill_cp, to_dev
 from oracle import kda_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -199,9 +199,9 @@ def test_nonzero_stream():
 
 
 # ------------------------------------------------------------ full sizes, sampled
-def _sampled_units_check(inp, units, tol, label):
-    """Oracle on selected (sequence, head) units, packed into one H=1 problem."""
-    out, fin = run_prefill(inp)
+def _sampled_units_check(inp, units, tol, label, runners=(("prefill", run_prefill),)):
+    """Oracle on selected (sequence, head) units, packed into one H=1 problem;
+    every runner's outputs on those units are checked against it."""
     cu = inp["cu_seqlens"].cpu().tolist()
     sl = lambda key, n, h: inp[key][cu[n]:cu[n + 1], h:h + 1]
     sub = {key: torch.cat([sl(key, n, h) for n, h in units]).cpu() for key in ("q", "k", "v", "g", "beta")}
@@ -211,10 +211,14 @@ def _sampled_units_check(inp, units, tol, label):
     sub["initial_state"] = None if init is None else torch.stack([init[n, h:h + 1] for n, h in units])
     log("[oracle] %s: %d units, %d tokens" % (label, len(units), sum(lens)))
     ref_out, ref_fin = oracle_prefill(sub)
-    got_out = torch.cat([out[cu[n]:cu[n + 1], h] for n, h in units]).float().cpu().numpy()
-    got_fin = torch.stack([fin[n, h] for n, h in units]).cpu().numpy()
-    assert_close(got_out, ref_out[:, 0], tol, label + " out (sampled)", out.dtype)
-    assert_close(got_fin, ref_fin[:, 0], tol, label + " final (sampled)")
+    for name, run in runners:
+        log("[%s] %s" % (name, label))
+        out, fin = run(inp)
+        got_out = torch.cat([out[cu[n]:cu[n + 1], h] for n, h in units]).float().cpu().numpy()
+        got_fin = torch.stack([fin[n, h] for n, h in units]).cpu().numpy()
+        del out, fin
+        assert_close(got_out, ref_out[:, 0], tol, "%s %s out (sampled)" % (name, label), torch.bfloat16)
+        assert_close(got_fin, ref_fin[:, 0], tol, "%s %s final (sampled)" % (name, label))
 
 
 @pytest.mark.slow
@@ -231,7 +235,8 @@ def test_parity_varlen_1m_h16_sampled():
     inp = I.make_prefill(wl, device="cuda")
     log("[varlen_1m] lengths %s" % inp["lengths"])
     units = [(n, (5 * n) % 16) for n in range(8)]
-    _sampled_units_check(inp, units, TOL[torch.bfloat16], "varlen_1m_h16")
+    _sampled_units_check(inp, units, TOL[torch.bfloat16], "varlen_1m_h16",
+                         runners=(("prefill", run_prefill), ("prefill_cp", run_prefill_cp)))
 
 
 # ------------------------------------------------------------ decode
