@@ -37,6 +37,11 @@ PREFILL_BYTES_PER_HT = 3 * 2 * DK + 4 * DK + 4 + 2 * DV
 PREFILL_FREF_PER_HT = 6 * DK * DV + 2 * 64 * (DK + DV)
 # decode bytes per (sequence, head): state read + write, q/k/v/out bf16, g fp32, beta fp32
 DECODE_BYTES_PER_UNIT = 2 * DK * DV * 4 + 3 * 2 * DK + 4 * DK + 4 + 2 * DV
+PREFILL_KERNELS = {
+    "cp": "kda_prefill_cp call: kda_cp_plan_kernel, kda_prefill_kernel<bf16,32,4> (segment summaries), "
+          "kda_cp_combine_kernel, kda_prefill_kernel<bf16,32,4> (segment outputs)",
+    "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4>",
+}
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_traffic.json")
 PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_prefill.hip")
 
@@ -59,7 +64,47 @@ def pmc_traffic():
         return None
 
 
-def cpu_baseline(pre, H, target_s=15.0):
+def _pmc_rows(path):
+    """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3 counter CSV."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = r["Dispatch_Id"]
+            name, val = rows.get(d, (r["Kernel_Name"], 0.0))
+            rows[d] = (name, val + float(r["Counter_Value"]))
+    return rows
+
+
+def write_traffic(fetch_csv, write_csv):
+    """HBM bytes per kda_prefill_cp call from two rocprofv3 --pmc runs of
+    ``bench.py --copy-calibration`` (FETCH_SIZE, then WRITE_SIZE), each scaled
+    by what the same counter reads for the 1 GiB-in / 1 GiB-out negation."""
+    out = {"kernel_source_sha256_16": source_hash(PREFILL_SRC),
+           "commands": ["cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <dir> -o run "
+                        "-- python <repo>/bench.py --steps 1 --warmup 1 --decode-steps 2 --no-cpu-baseline "
+                        "--copy-calibration" % c for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                       + ["python bench.py --traffic-from <fetch dir>/run_counter_collection.csv "
+                          "<write dir>/run_counter_collection.csv"],
+           "unit": "bytes per kda_prefill_cp call (all four launches), counters scaled by the 1 GiB negation"}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _pmc_rows(path)
+        calib = max(v for n, v in rows.values() if "neg" in n.lower())
+        factor = float(1 << 30) / (calib * 1024.0)
+        kda = [(n, v) for n, v in rows.values() if "kda_prefill_kernel" in n or "kda_cp_" in n]
+        calls = sum(1 for n, _ in kda if "kda_cp_plan_kernel" in n) or sum(1 for n, _ in kda)
+        per_call = sum(v for _, v in kda) * 1024.0 / calls
+        out[counter] = {"calibration_kib": calib, "scale": factor, "calls": calls,
+                        "kib_per_call_raw": per_call / 1024.0, "bytes_per_call": per_call * factor}
+        total += per_call * factor
+    out["hbm_bytes_per_launch"] = total
+    with open(PMC_SUMMARY, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def cpu_baseline(pre, H, target_s=20.0):
     """Time the fp64 oracle (as it stands) on host cores on a bounded sample:
     the first Ls tokens of every sequence of the same prefill inputs, all heads."""
     import numpy as np
@@ -104,11 +149,16 @@ def main():
     ap.add_argument("--seg-len", type=int, default=0, help="kda_prefill_cp segment length (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit (no GPU)")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the KDA path on a single MI355X "
-              "(heads and sequences shard across GPUs with no exchange; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: libkda runs the KDA path on a single MI355X "
+              "(heads and sequences would shard across GPUs with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -132,10 +182,12 @@ def main():
     state = dec["state"]
     dout = torch.empty(args.decode_steps, Nd, Hd, DV, dtype=torch.bfloat16, device=dev)
     if args.copy_calibration:
+        # a plain streaming kernel of known size for the HBM counters: torch's
+        # elementwise negation reads 1 GiB and writes 1 GiB (kernel name holds "neg")
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     stream = torch.cuda.current_stream()
@@ -201,7 +253,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "prefill_varlen_1m_h16 + decode_512x32",
-            "prefill": {"num_seqs": N, "lengths": pre["lengths"], "total_tokens": T, "heads": H,
+            "prefill": {"entry": "kda_prefill_cp" if args.prefill == "cp" else "kda_prefill",
+                        "seg_len": args.seg_len if args.prefill == "cp" else None,
+                        "num_seqs": N, "lengths": pre["lengths"], "total_tokens": T, "heads": H,
                         "dk": DK, "dv": DV, "io": "bf16 q/k/v/out, fp32 g/beta/state",
                         "initial_state": "zero", "ms": pre_avg, "head_tokens_per_s": head_tokens / (pre_avg * 1e-3),
                         "fref_tflops": pre_tflops, "mfma_frac_fref": pre_tflops / BF16_PEAK_TFLOPS,
@@ -211,7 +265,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": pre_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": pre_gbs / HBM_PEAK_GBS,
                      "traffic": traffic,
-                     "kernel": "kda_prefill_kernel<bf16, 64, NW>", "algorithmic_bytes_per_launch": pre_bytes,
+                     "kernel": PREFILL_KERNELS[args.prefill], "algorithmic_bytes_per_launch": pre_bytes,
                      "avg_launch_ms": pre_avg},
         "decode": {"tokens_per_s": Nd / (dec_step_ms * 1e-3), "ms_per_decode_step": dec_step_ms,
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
