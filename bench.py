@@ -193,7 +193,7 @@ def main():
     stream = torch.cuda.current_stream()
     ws = None
     if args.prefill == "cp":
-        ws_bytes = K.kda_prefill_cp_workspace_size(N, T, H, DK, DV, args.seg_len)
+        ws_bytes = K.kda_prefill_cp_workspace_size(N, T, H, DK, DV, torch.bfloat16, args.seg_len)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def prefill():

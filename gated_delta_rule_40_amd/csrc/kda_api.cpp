@@ -17,7 +17,18 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          int32_t mode, const float *seg_init, float *seg_out,
                                          hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
-                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, hipStream_t stream);
+                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
+                                         int32_t max_chunks, int32_t *chunk_off, hipStream_t stream);
+extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
+                                            const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
+                                            int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
+                                            hipStream_t stream);
+extern "C" hipError_t kda_launch_chain(int bf16, const void *v, const float *init, const int32_t *cu, int32_t N,
+                                       int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
+                                       const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
+                                       float *seg_out, const int32_t *chunk_off, const void *img,
+                                       hipStream_t stream);
+extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             hipStream_t stream);
@@ -114,29 +125,34 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const float 
 namespace {
 
 constexpr int32_t kCpChunk = 32;     // chunk size of the segmented runs
-constexpr int32_t kCpBlock = 64;     // value columns per workgroup of the segmented runs
 
 struct CpLayout {
-    size_t plan, seq_seg, seg_out, seg_init, total;
-    int32_t max_segs;
+    size_t plan, seq_seg, chunk_off, seg_out, seg_init, img, total;
+    int32_t max_segs, max_chunks;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace sections: plan [max_segs][4] int32, per-sequence first segment
-// [N + 1] int32, summaries [max_segs][H][dk][dv + dk] fp32, entering states
-// [max_segs][H][dk][dv] fp32.  max_segs bounds the segment count: every
-// sequence of length L takes max(1, ceil(L / seg_len)) segments.
-bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int32_t seg_len, CpLayout *lay)
+// [N + 1] int32, per-sequence first chunk [N + 1] int32, summaries
+// [max_segs][H][dk][dv + dk] fp32, entering states [max_segs][H][dk][dv]
+// fp32, chunk-operand images [max_chunks][H][image].  Every sequence of
+// length L takes max(1, ceil(L / seg_len)) segments and ceil(L / 32) chunks,
+// which max_segs and max_chunks bound.
+bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16, int32_t seg_len, CpLayout *lay)
 {
     const int64_t segs = (int64_t)T / seg_len + 1 + N;
-    if (segs > INT32_MAX / 4) return false;
+    const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
+    if (segs > INT32_MAX / 4 || chunks > INT32_MAX / 4) return false;
     lay->max_segs = (int32_t)segs;
+    lay->max_chunks = (int32_t)chunks;
     lay->plan = 0;
     lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
-    lay->seg_out = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->seg_out = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
     lay->seg_init = align256(lay->seg_out + sizeof(float) * (size_t)segs * H * dk * (dv + dk));
-    lay->total = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * dk * dv);
+    lay->img = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * dk * dv);
+    lay->total = align256(lay->img + kda_chunk_image_bytes(bf16) * (size_t)chunks * H);
     return true;
 }
 
@@ -153,13 +169,14 @@ int32_t cp_default_seg_len(int32_t T, int32_t H)
 }  // namespace
 
 size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
-                                     int32_t dk, int32_t dv, int32_t seg_len)
+                                     int32_t dk, int32_t dv, kda_dtype dtype, int32_t seg_len)
 {
     if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || dk != kHeadDim || dv != kHeadDim) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     if (seg_len == 0) seg_len = cp_default_seg_len(total_tokens, num_heads);
     if (seg_len < kCpChunk || seg_len % kCpChunk) return 0;
     CpLayout lay;
-    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, seg_len, &lay)) return 0;
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_BF16, seg_len, &lay)) return 0;
     return lay.total;
 }
 
@@ -176,29 +193,34 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
     if (st != KDA_OK) return st;
     if (seg_len == 0) seg_len = cp_default_seg_len(total_tokens, num_heads);
     if (seg_len < kCpChunk || seg_len % kCpChunk) return KDA_ERR_UNSUPPORTED;
+    const int bf16 = dtype == KDA_BF16 ? 1 : 0;
     CpLayout lay;
-    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, seg_len, &lay)) return KDA_ERR_INVALID_ARG;
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, bf16, seg_len, &lay)) return KDA_ERR_INVALID_ARG;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
     if ((int64_t)lay.max_segs * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)lay.max_chunks * num_heads > INT32_MAX) return KDA_ERR_INVALID_ARG;
     if (num_seqs == 0) return KDA_OK;
-    const int bf16 = dtype == KDA_BF16 ? 1 : 0;
     char *ws = static_cast<char *>(workspace);
     int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
     int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
+    int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + lay.chunk_off);
     float *seg_out = reinterpret_cast<float *>(ws + lay.seg_out);
     float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
+    void *img = ws + lay.img;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg, s);
+    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
+                                      kCpChunk, lay.max_chunks, chunk_off, s);
+    if (e == hipSuccess)   // chunk operands of every (chunk, head)
+        e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
+                                  lay.max_chunks, img, s);
     if (e == hipSuccess)   // segment summaries (segments with a successor)
-        e = kda_launch_prefill(bf16, kCpChunk, kCpBlock, q, k, v, g, beta, nullptr, cu_seqlens, num_seqs,
-                               total_tokens, num_heads, dv, out, nullptr, plan, lay.max_segs, 1, nullptr,
-                               seg_out, s);
+        e = kda_launch_chain(bf16, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
+                             plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, s);
     if (e == hipSuccess)   // entering state of every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, s);
     if (e == hipSuccess)   // outputs and final states
-        e = kda_launch_prefill(bf16, kCpChunk, kCpBlock, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs,
-                               total_tokens, num_heads, dv, out, final_state, plan, lay.max_segs, 0,
-                               seg_init, nullptr, s);
+        e = kda_launch_chain(bf16, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
+                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -111,7 +111,7 @@ struct PrefillCfg {
     static constexpr size_t offGam = offH + sizeof(float) * NPAIR * DK;     // [DK]
     static constexpr size_t offBeta = offGam + sizeof(float) * DK;          // [C]
     static constexpr size_t offTs = offBeta + sizeof(float) * C;            // [NSUB][NSUB]
-    static constexpr size_t bytes = offTs + sizeof(float) * NSUB * NSUB;
+    static constexpr size_t bytes = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     // workgroups per CU that the LDS allows (the register budget is set to match)
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
@@ -134,6 +134,51 @@ struct SegArgs {
     int32_t mode;            // SEG_OUTPUT or SEG_SUMMARY
     const float *seg_init;   // [num_segs][H][DK][dv] entering states (SEG_OUTPUT)
     float *seg_out;          // [num_segs][H][DK][dv + DK] summaries (SEG_SUMMARY)
+    const int32_t *chunk_off;   // [N + 1] first chunk of each sequence (chunk-image passes)
+    f32x4 *img;                 // chunk-operand images (chunk-image passes)
+};
+
+enum { MODE_FUSED = 0, MODE_PREP = 1 };
+constexpr int PREP_GROUP = 8;    // consecutive chunks per workgroup of the chunk-operand pass
+
+// Chunk-operand image: everything the state chain of one (chunk, head) reads
+// besides V, as computed by the chunk-operand pass -- -GS K+, GS Q+, GS K^
+// transposed, the (I + N)^-1 blocks and P in the MFMA operand type, then the
+// fp32 chunk decay, beta and T-block scales.  Packed row-major without padding
+// as 16-byte vectors; lds_off maps vector v to its place in an LDS buffer that
+// uses the padded strides of PrefillCfg.  Chunks are numbered across the
+// packed sequences: sequence n owns chunks chunk_off[n] .. chunk_off[n+1]-1,
+// and the image of (chunk c, head h) is vector block c * H + h.
+template <typename TIn, int C>
+struct ChunkImage {
+    typedef PrefillCfg<TIn, C, 4> P;                   // strides (independent of NW)
+    typedef typename P::OpT OpT;
+    static constexpr int EPV = 16 / (int)sizeof(OpT);  // elements per vector
+    static constexpr int NSUB = C / SUB;
+    static constexpr int vNKp = C * DK / EPV, vQp = C * DK / EPV, vKhT = DK * C / EPV;
+    static constexpr int vT = C * C / EPV, vP = C * C / EPV;
+    static constexpr int vGam = DK / 4, vBeta = C / 4, vTs = (NSUB * NSUB + 3) / 4;
+    static constexpr int NVEC = vNKp + vQp + vKhT + vT + vP + vGam + vBeta + vTs;
+    static constexpr size_t BYTES = (size_t)NVEC * 16;
+    struct Offs { uint32_t nkp, qp, kht, t, p, gam, beta, ts; };   // byte offsets of the regions
+    __device__ static __forceinline__ uint32_t lds_off(int v, const Offs &o) {
+        constexpr int RK = DK / EPV, RC = C / EPV;                  // vectors per row
+        constexpr uint32_t E = sizeof(OpT);
+        if (v < vNKp) return o.nkp + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
+        v -= vNKp;
+        if (v < vQp) return o.qp + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
+        v -= vQp;
+        if (v < vKhT) return o.kht + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vKhT;
+        if (v < vT) return o.t + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vT;
+        if (v < vP) return o.p + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vP;
+        if (v < vGam) return o.gam + 16 * v;
+        v -= vGam;
+        if (v < vBeta) return o.beta + 16 * v;
+        return o.ts + 16 * (v - vBeta);
+    }
 };
 
 // sub-tile pair p -> (a, b), b <= a
@@ -262,7 +307,118 @@ __device__ __forceinline__ void prep_slow(
     }
 }
 
-template <typename TIn, int C, int NW>
+// State-dependent part of one chunk for the 16 value columns of this wave:
+//     X = Diag(b) (V - K+ S0),  W = (I + N)^-1 X,  O = Q+ S0 + P W,
+//     S = Diag(e^Gamma_C) S0 + K^T W,
+// reading the chunk operands from LDS (sNKp = -GS K+, sQp = GS Q+,
+// sKhT = GS K^ transposed, sT = (I + N)^-1 blocks with scales sTs, sP, the
+// chunk decay sGam and sBeta), V from sV[r * ldv + vc] and writing O to
+// sO[r * ldo + oc] unless `summary`.  S (this wave's 128 x 16 slice, MFMA
+// accumulator layout) is updated in place.
+template <typename TIn, int C, int ldv, int ldo>
+__device__ __forceinline__ void chain_chunk(
+    f32x4 (&S)[DK / 16], const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
+    const typename PrefillCfg<TIn, C, 4>::OpT *sQp, const typename PrefillCfg<TIn, C, 4>::OpT *sKhT,
+    const typename PrefillCfg<TIn, C, 4>::OpT *sT, const typename PrefillCfg<TIn, C, 4>::OpT *sP,
+    const float *sTs, const float *sGam, const float *sBeta, const TIn *sV, int vc, TIn *sO, int oc,
+    bool summary, int lj, int lm)
+{
+    typedef PrefillCfg<TIn, C, 4> P;
+    typedef typename P::OpT OpT;
+    typedef Mma<OpT> M;
+    constexpr bool kIn16 = P::kIn16;
+    constexpr int NSUB = P::NSUB, KB = P::KB, LDK = P::LDK, LDC = P::LDC;
+    constexpr float GS = P::GS;
+                // state operand, scaled per column into fp16 range
+        float sS = 1.f;
+        if (kIn16) {
+            float m = 0.f;
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) m = fmaxf(m, absmax4(S[r]));
+            sS = pow2_scale(colmax(m));
+        }
+        const float isS = pow2_inv(sS) * (1.f / GS);   // also undoes the GS on K+ / Q+
+        typename M::frag Sf[DK / KB];
+#pragma unroll
+        for (int kb = 0; kb < DK / KB; ++kb) Sf[kb] = M::from_acc(&S[kb * (KB / 16)], sS);
+
+        // X = Diag(beta) (V - K+ S0)       (rows of sNKp hold -GS K+)
+        f32x4 X[NSUB];
+        float xmax = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < NSUB; ++mt) {
+            f32x4 t = zero4();
+            const OpT *rowA = sNKp + (mt * SUB + lm) * LDK;
+#pragma unroll
+            for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load(rowA, kb * KB, lj), Sf[kb], t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = mt * SUB + 4 * lj + i;
+                X[mt][i] = sBeta[r] * (to_f(sV[r * ldv + vc]) + t[i] * isS);
+            }
+            xmax = fmaxf(xmax, absmax4(X[mt]));
+        }
+        // W = (I + N)^-1 X, block lower triangular, per-block scales
+        float sX = 1.f;
+        if (kIn16) sX = pow2_scale(colmax(xmax));
+        const float isX = pow2_inv(sX);
+        typename M::frag16 X16[NSUB];
+#pragma unroll
+        for (int b = 0; b < NSUB; ++b) X16[b] = M::from_acc16(X[b], sX);
+        f32x4 W[NSUB];
+        float wmax = 0.f;
+#pragma unroll
+        for (int a = 0; a < NSUB; ++a) {
+            f32x4 w = zero4();
+            const OpT *rowT = sT + (a * SUB + lm) * LDC;
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const f32x4 t = M::mma16(M::load16(rowT, b * SUB, lj), X16[b], zero4());
+                w += t * (sTs[a * NSUB + b] * isX);
+            }
+            W[a] = w;
+            wmax = fmaxf(wmax, absmax4(w));
+        }
+        float sW = 1.f;
+        if (kIn16) sW = pow2_scale(colmax(wmax));
+        const float isW = pow2_inv(sW);
+        typename M::frag Wf[C / KB];
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sW);
+
+        // O = Q+ S0 + P W       (rows of sQp hold GS Q+); not needed for a summary
+#pragma unroll
+        for (int mt = 0; mt < (summary ? 0 : NSUB); ++mt) {
+            f32x4 o1 = zero4(), o2 = zero4();
+            const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
+#pragma unroll
+            for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load(rowQ, kb * KB, lj), Sf[kb], o1);
+            const OpT *rowP = sP + (mt * SUB + lm) * LDC;
+#pragma unroll
+            for (int kb = 0; kb < C / KB; ++kb)
+                if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load(rowP, kb * KB, lj), Wf[kb], o2);
+            const f32x4 o = o1 * isS + o2 * isW;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc] = from_f<TIn>(o[i]);
+        }
+        // S = Diag(gamma) S0 + K^T W       (rows of sKhT hold GS K^ per channel)
+        const float isWk = isW * (1.f / GS);
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) {
+            f32x4 t = zero4();
+            const OpT *rowK = sKhT + (16 * r + lm) * LDC;
+#pragma unroll
+            for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load(rowK, kb * KB, lj), Wf[kb], t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[r][i] = S[r][i] * sGam[16 * r + 4 * lj + i] + t[i] * isWk;
+        }
+}
+
+// MODE_FUSED: the whole chunk loop per (unit, value block), as described at
+// the top.  MODE_PREP: the chunk-operand pass -- phases 1-3 only, for
+// PREP_GROUP consecutive chunks (numbered across sequences) of one head per
+// workgroup, each chunk's operands stored as its image (no state, no V).
+template <typename TIn, int C, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(PrefillCfg<TIn, C, NW>::WAVES_PER_EU)))
 void kda_prefill_kernel(
     const TIn *__restrict__ q, const TIn *__restrict__ k, const TIn *__restrict__ v,
@@ -303,29 +459,60 @@ void kda_prefill_kernel(
     // ---- workgroup -> (work unit, value block); blocks of one unit share an XCD.
     //      A work unit is a (sequence, head) pair, or a (segment, head) pair when
     //      a segment plan is given; summary mode adds DK transition columns.
-    const bool segmented = seg.plan != nullptr;
-    const bool summary = seg.mode == SEG_SUMMARY;
-    const int ncols = summary ? dv + DK : dv;
-    const int nblk = ncols / BV;
+    constexpr bool kPrep = MODE == MODE_PREP;
+    const bool segmented = !kPrep && seg.plan != nullptr;
+    const bool summary = !kPrep && seg.mode == SEG_SUMMARY;
     const int wg = blockIdx.x;
-    const int xcd = wg & 7, slot = wg >> 3;
-    const int vb = slot % nblk;
-    const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
-    if (unit >= (int64_t)(segmented ? seg.num_segs : num_seqs) * num_heads) return;
-    const int su = (int)(unit / num_heads), h = (int)(unit % num_heads);
-    int n = su, t_start, t_end, sflags = SEG_FIRST | SEG_LAST;
-    if (segmented) {
-        n = seg.plan[4 * su];
-        t_start = seg.plan[4 * su + 1];
-        t_end = seg.plan[4 * su + 2];
-        sflags = seg.plan[4 * su + 3];
-        if (n < 0 || (summary && (sflags & SEG_LAST))) return;   // unused entry / summary not needed
+    int su = 0, h = 0, n = 0, vb = 0, t_start = 0, t_end = 0, sflags = SEG_FIRST | SEG_LAST;
+    int gc_begin = 0, nch = 0;      // chunk-operand pass: first global chunk, chunk count
+    if constexpr (kPrep) {
+        h = wg % num_heads;
+        gc_begin = (wg / num_heads) * PREP_GROUP;
+        const int total_chunks = seg.chunk_off[num_seqs];
+        if (gc_begin >= total_chunks) return;
+        nch = min(PREP_GROUP, total_chunks - gc_begin);
     } else {
-        t_start = cu_seqlens[n];
-        t_end = cu_seqlens[n + 1];
+        const int nblk = (summary ? dv + DK : dv) / BV;
+        const int xcd = wg & 7, slot = wg >> 3;
+        vb = slot % nblk;
+        const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
+        if (unit >= (int64_t)(segmented ? seg.num_segs : num_seqs) * num_heads) return;
+        su = (int)(unit / num_heads);
+        h = (int)(unit % num_heads);
+        n = su;
+        if (segmented) {
+            n = seg.plan[4 * su];
+            t_start = seg.plan[4 * su + 1];
+            t_end = seg.plan[4 * su + 2];
+            sflags = seg.plan[4 * su + 3];
+            if (n < 0 || (summary && (sflags & SEG_LAST))) return;   // unused entry / summary not needed
+        } else {
+            t_start = cu_seqlens[n];
+            t_end = cu_seqlens[n + 1];
+        }
+        t_start = min(max(t_start, 0), total_tokens);
+        t_end = min(max(t_end, t_start), total_tokens);
+        nch = (t_end - t_start + C - 1) / C;
     }
-    t_start = min(max(t_start, 0), total_tokens);
-    t_end = min(max(t_end, t_start), total_tokens);
+    // chunk ci of this workgroup: tokens [c0, min(c0 + C, cend))
+    auto chunk_range = [&](int ci, int &c0, int &cend) {
+        if constexpr (kPrep) {
+            const int gc = gc_begin + ci;
+            int lo = 0, hi = num_seqs;                 // chunk_off[lo] <= gc < chunk_off[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (seg.chunk_off[mid] <= gc) lo = mid; else hi = mid;
+            }
+            const int s0 = min(max(cu_seqlens[lo], 0), total_tokens);
+            cend = min(max(cu_seqlens[lo + 1], s0), total_tokens);
+            // in range for any valid cu_seqlens; the clamp keeps every load in
+            // bounds for any other contents
+            c0 = min(s0 + (gc - seg.chunk_off[lo]) * C, total_tokens - 1);
+        } else {
+            c0 = t_start + ci * C;
+            cend = t_end;
+        }
+    };
     const int dv0 = vb * BV;
     const bool trans_cols = summary && dv0 >= dv;   // transition columns: V = 0, entering state I
 
@@ -384,8 +571,8 @@ void kda_prefill_kernel(
     PairT rk[ITEMS][SEG], rq[ITEMS][SEG];
     f32x4 rv[VITEMS];
     float rb = 0.f;
-    auto load_chunk = [&](int cc0) {
-        const int LL = min(C, t_end - cc0);
+    auto load_chunk = [&](int cc0, int cend) {
+        const int LL = max(1, min(C, cend - cc0));
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
             const int item = min(tid + it * NT, NSEG * 64 - 1), sg = item / 64, c = 2 * (item % 64);
@@ -399,7 +586,7 @@ void kda_prefill_kernel(
             }
         }
 #pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
+        for (int it = 0; it < (kPrep ? 0 : VITEMS); ++it) {
             const int e = tid + it * NT;
             if (e < C * VPR) {
                 const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
@@ -409,8 +596,11 @@ void kda_prefill_kernel(
         }
         if (tid < C) rb = beta[(int64_t)(cc0 + min(tid, LL - 1)) * H + h];
     };
-    const int c_last = t_start + ((t_end - t_start - 1) / C) * C;   // start of the last chunk
-    if (t_start < t_end) load_chunk(t_start);
+    if (nch > 0) {
+        int a0, a1;
+        chunk_range(0, a0, a1);
+        load_chunk(a0, a1);
+    }
 
     // product of the group decays over groups [g0, g1) of channel c, in order
     auto grp_prod = [&](int g0, int g1, int c) {
@@ -420,8 +610,10 @@ void kda_prefill_kernel(
     };
     constexpr int GPS = SUB / GRP;                        // groups per sub-tile
 
-    for (int c0 = t_start; c0 < t_end; c0 += C) {
-        const int L = min(C, t_end - c0);        // valid tokens in this chunk
+    for (int ci = 0; ci < nch; ++ci) {
+        int c0, cend;
+        chunk_range(ci, c0, cend);
+        const int L = min(C, cend - c0);         // valid tokens in this chunk
         __syncthreads();                          // previous chunk done with all LDS
 
         // ---- 1a. group gate sums -> F = exp(sum); beta
@@ -538,7 +730,7 @@ void kda_prefill_kernel(
         if (slow)
             prep_slow<TIn, C, NW>(false, q, k, g, c0, L, rowK, hK, tid, sF, sKr32, sQr32, sKD32, sNKp, sQp, sKhT);
 #pragma unroll
-        for (int it = 0; it < VITEMS; ++it) {
+        for (int it = 0; it < (kPrep ? 0 : VITEMS); ++it) {
             const int e = tid + it * NT;
             if (e < C * VPR) {
                 const int r = e / VPR, cv = (e % VPR) * VEC;
@@ -547,7 +739,11 @@ void kda_prefill_kernel(
         }
         // unconditional (the last chunk re-reads itself): a conditional load
         // would make the compiler wait for it right away
-        load_chunk(min(c0 + C, c_last));
+        {
+            int n0, n1;
+            chunk_range(min(ci + 1, nch - 1), n0, n1);
+            load_chunk(n0, n1);
+        }
         if (tid < NSUB * SUB) {
             const int a = tid / SUB, nc = tid % SUB;
             const float *NT = sAd + a * SUB * P::LDAD;     // NT[s][r] = N[r][s]
@@ -614,93 +810,20 @@ void kda_prefill_kernel(
             __syncthreads();
         }
 
-        // ---- 4. state-dependent chain (this wave's 16 columns)
-        {
-            const int vc = 16 * wave + lm;                 // column within the value block
-            // state operand, scaled per column into fp16 range
-            float sS = 1.f;
-            if (kIn16) {
-                float m = 0.f;
-#pragma unroll
-                for (int r = 0; r < DK / 16; ++r) m = fmaxf(m, absmax4(S[r]));
-                sS = pow2_scale(colmax(m));
-            }
-            const float isS = pow2_inv(sS) * (1.f / GS);   // also undoes the GS on K+ / Q+
-            typename M::frag Sf[DK / KB];
-#pragma unroll
-            for (int kb = 0; kb < DK / KB; ++kb) Sf[kb] = M::from_acc(&S[kb * (KB / 16)], sS);
-
-            // X = Diag(beta) (V - K+ S0)       (rows of sNKp hold -GS K+)
-            f32x4 X[NSUB];
-            float xmax = 0.f;
-#pragma unroll
-            for (int mt = 0; mt < NSUB; ++mt) {
-                f32x4 t = zero4();
-                const OpT *rowA = sNKp + (mt * SUB + lm) * LDK;
-#pragma unroll
-                for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load(rowA, kb * KB, lj), Sf[kb], t);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = mt * SUB + 4 * lj + i;
-                    X[mt][i] = sBeta[r] * (to_f(sV[r * LDV + vc]) + t[i] * isS);
-                }
-                xmax = fmaxf(xmax, absmax4(X[mt]));
-            }
-            // W = (I + N)^-1 X, block lower triangular, per-block scales
-            float sX = 1.f;
-            if (kIn16) sX = pow2_scale(colmax(xmax));
-            const float isX = pow2_inv(sX);
-            typename M::frag16 X16[NSUB];
-#pragma unroll
-            for (int b = 0; b < NSUB; ++b) X16[b] = M::from_acc16(X[b], sX);
-            f32x4 W[NSUB];
-            float wmax = 0.f;
-#pragma unroll
-            for (int a = 0; a < NSUB; ++a) {
-                f32x4 w = zero4();
-                const OpT *rowT = sT + (a * SUB + lm) * LDC;
-#pragma unroll
-                for (int b = 0; b <= a; ++b) {
-                    const f32x4 t = M::mma16(M::load16(rowT, b * SUB, lj), X16[b], zero4());
-                    w += t * (sTs[a * NSUB + b] * isX);
-                }
-                W[a] = w;
-                wmax = fmaxf(wmax, absmax4(w));
-            }
-            float sW = 1.f;
-            if (kIn16) sW = pow2_scale(colmax(wmax));
-            const float isW = pow2_inv(sW);
-            typename M::frag Wf[C / KB];
-#pragma unroll
-            for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sW);
-
-            // O = Q+ S0 + P W       (rows of sQp hold GS Q+); not needed for a summary
-#pragma unroll
-            for (int mt = 0; mt < (summary ? 0 : NSUB); ++mt) {
-                f32x4 o1 = zero4(), o2 = zero4();
-                const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
-#pragma unroll
-                for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load(rowQ, kb * KB, lj), Sf[kb], o1);
-                const OpT *rowP = sP + (mt * SUB + lm) * LDC;
-#pragma unroll
-                for (int kb = 0; kb < C / KB; ++kb)
-                    if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load(rowP, kb * KB, lj), Wf[kb], o2);
-                const f32x4 o = o1 * isS + o2 * isW;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * LDV + vc] = from_f<TIn>(o[i]);
-            }
-            // S = Diag(gamma) S0 + K^T W       (rows of sKhT hold GS K^ per channel)
-            const float isWk = isW * (1.f / GS);
-#pragma unroll
-            for (int r = 0; r < DK / 16; ++r) {
-                f32x4 t = zero4();
-                const OpT *rowK = sKhT + (16 * r + lm) * LDC;
-#pragma unroll
-                for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load(rowK, kb * KB, lj), Wf[kb], t);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[r][i] = S[r][i] * sGam[16 * r + 4 * lj + i] + t[i] * isWk;
-            }
+        if constexpr (kPrep) {
+            // ---- chunk-operand image of (chunk, head) -> global
+            typedef ChunkImage<TIn, C> Img;
+            const typename Img::Offs o = {(uint32_t)P::offNKp, (uint32_t)P::offQp, (uint32_t)P::offKhT,
+                                          (uint32_t)P::offT, (uint32_t)P::offP, (uint32_t)P::offGam,
+                                          (uint32_t)P::offBeta, (uint32_t)P::offTs};
+            f32x4 *dst = seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC;
+            for (int e = tid; e < Img::NVEC; e += NT)
+                dst[e] = *reinterpret_cast<const f32x4 *>(smem + Img::lds_off(e, o));
+            continue;
         }
+        // ---- 4. state-dependent chain (this wave's 16 columns)
+        chain_chunk<TIn, C, LDV, LDV>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
+                                      16 * wave + lm, summary, lj, lm);
         __syncthreads();
 
         // ---- 5. output tile -> global (valid tokens only)
@@ -736,7 +859,7 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
                                    float *fin, SegArgs seg, hipStream_t stream)
 {
     typedef PrefillCfg<TIn, C, NW> P;
-    auto kern = kda_prefill_kernel<TIn, C, NW>;
+    auto kern = kda_prefill_kernel<TIn, C, NW, MODE_FUSED>;
     static bool attr_set = false;   // idempotent; racing threads set the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -757,32 +880,284 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
     return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------ state chain
+// The state-dependent pass over chunk-operand images: one workgroup per
+// (unit, block of BV value columns) as in the fused kernel, walking the unit's
+// chunks in order.  Per chunk: one barrier; the next chunk's image and value
+// tile are loaded into registers, the chain runs on the current LDS buffer,
+// each wave stores its own output columns, and the registers are written to
+// the other LDS buffer.
+template <typename TIn, int C, int NW>
+struct ChainCfg {
+    typedef PrefillCfg<TIn, C, NW> P;
+    typedef typename P::OpT OpT;
+    typedef ChunkImage<TIn, C> Img;
+    static constexpr int NT = 64 * NW, BV = 16 * NW, NSUB = C / SUB;
+    static constexpr int LDK = P::LDK, LDC = P::LDC, LDV = P::LDV;
+    static constexpr uint32_t offNKp = 0;
+    static constexpr uint32_t offQp = offNKp + sizeof(OpT) * C * LDK;
+    static constexpr uint32_t offKhT = offQp + sizeof(OpT) * C * LDK;
+    static constexpr uint32_t offT = offKhT + sizeof(OpT) * DK * LDC;
+    static constexpr uint32_t offP = offT + sizeof(OpT) * C * LDC;
+    static constexpr uint32_t offGam = offP + sizeof(OpT) * C * LDC;
+    static constexpr uint32_t offBeta = offGam + sizeof(float) * DK;
+    static constexpr uint32_t offTs = offBeta + sizeof(float) * C;
+    static constexpr uint32_t offV = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
+    static constexpr uint32_t BUF = (offV + sizeof(TIn) * C * LDV + 15) / 16 * 16;   // one chunk buffer
+    static constexpr uint32_t offO = 2 * BUF;                                        // [NW][C][16] outputs
+    static constexpr uint32_t bytes = offO + sizeof(TIn) * NW * C * 16;
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
+    static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
+    static constexpr int IITEMS = (Img::NVEC + NT - 1) / NT;        // image vectors per thread
+    static constexpr int VEC = 16 / (int)sizeof(TIn);               // elements per 16-byte vector
+    static constexpr int VPR = BV / VEC;                            // vectors per value-tile row
+    static constexpr int VITEMS = (C * VPR + NT - 1) / NT;
+    static constexpr int OVEC = C * 16 / VEC;                       // vectors of one wave's output tile
+};
+
+template <typename TIn, int C, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW>::WAVES_PER_EU)))
+void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
+                      int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
+                      TIn *__restrict__ out, float *final_state, SegArgs seg)
+{
+    typedef ChainCfg<TIn, C, NW> Q;
+    typedef typename Q::OpT OpT;
+    typedef typename Q::Img Img;
+    constexpr int NT = Q::NT, BV = Q::BV, LDV = Q::LDV, VEC = Q::VEC, VPR = Q::VPR;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    // ---- workgroup -> (unit, value block): as in the fused kernel
+    const bool segmented = seg.plan != nullptr;
+    const bool summary = seg.mode == SEG_SUMMARY;
+    const int nblk = (summary ? dv + DK : dv) / BV;
+    const int wg = blockIdx.x;
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int vb = slot % nblk;
+    const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
+    if (unit >= (int64_t)(segmented ? seg.num_segs : num_seqs) * num_heads) return;
+    const int su = (int)(unit / num_heads), h = (int)(unit % num_heads);
+    int n = su, t_start, t_end, sflags = SEG_FIRST | SEG_LAST;
+    if (segmented) {
+        n = seg.plan[4 * su];
+        t_start = seg.plan[4 * su + 1];
+        t_end = seg.plan[4 * su + 2];
+        sflags = seg.plan[4 * su + 3];
+        if (n < 0 || (summary && (sflags & SEG_LAST))) return;
+    } else {
+        t_start = cu_seqlens[n];
+        t_end = cu_seqlens[n + 1];
+    }
+    const int seq_start = min(max(cu_seqlens[n], 0), total_tokens);
+    t_start = min(max(t_start, 0), total_tokens);
+    t_end = min(max(t_end, t_start), total_tokens);
+    const int64_t gc0 = seg.chunk_off[n] + (t_start - seq_start) / C;   // first global chunk
+    // the images cover chunks [0, chunk_off[N]); the bound only binds when
+    // cu_seqlens is not non-decreasing (result unspecified, memory safe)
+    const int nch = (int)max((int64_t)0, min((int64_t)(t_end - t_start + C - 1) / C,
+                                             (int64_t)seg.chunk_off[num_seqs] - gc0));
+    const int dv0 = vb * BV;
+    const bool trans_cols = summary && dv0 >= dv;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lj = lane >> 4, lm = lane & 15;
+    const int H = num_heads;
+    const int64_t rowV = (int64_t)H * dv;
+
+    // ---- entering state (as in the fused kernel)
+    f32x4 S[DK / 16];
+    const int col = dv0 + 16 * wave + lm;
+    const int64_t sbase = ((int64_t)n * num_heads + h) * DK * dv;
+    const float *S_in = nullptr;
+    int64_t S_in_base = 0;
+    if (summary) {
+        S_in = nullptr;
+    } else if (segmented) {
+        S_in = seg.seg_init;
+        S_in_base = ((int64_t)su * num_heads + h) * DK * dv;
+    } else if (initial_state) {
+        S_in = initial_state;
+        S_in_base = sbase;
+    }
+    if (S_in) {
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[r][i] = S_in[S_in_base + (int64_t)(16 * r + 4 * lj + i) * dv + col];
+    } else {
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[r][i] = (trans_cols && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
+    }
+
+    // ---- chunk staging: image + value tile of chunk ci in registers
+    f32x4 ri[Q::IITEMS], rv[Q::VITEMS];
+    auto load = [&](int ci) {
+        const f32x4 *src = seg.img + ((gc0 + ci) * H + h) * Img::NVEC;
+#pragma unroll
+        for (int it = 0; it < Q::IITEMS; ++it) ri[it] = src[min(tid + it * NT, Img::NVEC - 1)];
+        const int c0 = t_start + ci * C, LL = min(C, t_end - c0);
+#pragma unroll
+        for (int it = 0; it < Q::VITEMS; ++it) {
+            const int e = tid + it * NT;
+            if (e < C * VPR) {
+                const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
+                rv[it] = trans_cols ? zero4()
+                                    : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
+            }
+        }
+    };
+    const typename Img::Offs offs = {Q::offNKp, Q::offQp, Q::offKhT, Q::offT, Q::offP, Q::offGam, Q::offBeta, Q::offTs};
+    auto stage = [&](int ci, int b) {
+        unsigned char *base = smem + b * Q::BUF;
+#pragma unroll
+        for (int it = 0; it < Q::IITEMS; ++it) {
+            const int e = tid + it * NT;
+            if (e < Img::NVEC) *reinterpret_cast<f32x4 *>(base + Img::lds_off(e, offs)) = ri[it];
+        }
+        TIn *sV = reinterpret_cast<TIn *>(base + Q::offV);
+        const int LL = min(C, t_end - (t_start + ci * C));
+#pragma unroll
+        for (int it = 0; it < Q::VITEMS; ++it) {
+            const int e = tid + it * NT;
+            if (e < C * VPR) {
+                const int r = e / VPR, cv = (e % VPR) * VEC;
+                *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < LL ? rv[it] : zero4();
+            }
+        }
+    };
+    if (nch > 0) {
+        load(0);
+        stage(0, 0);
+    }
+    TIn *sOw = reinterpret_cast<TIn *>(smem + Q::offO) + wave * C * 16;    // this wave's output tile
+    for (int ci = 0; ci < nch; ++ci) {
+        __syncthreads();                          // buffer ci & 1 staged; ci - 1 done with the other
+        load(min(ci + 1, nch - 1));               // unconditional, see the fused kernel
+        const unsigned char *base = smem + (ci & 1) * Q::BUF;
+        chain_chunk<TIn, C, LDV, 16>(
+            S, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
+            reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
+            reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
+            reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
+            reinterpret_cast<const TIn *>(base + Q::offV), 16 * wave + lm, sOw, lm, summary, lj, lm);
+        if (!summary) {
+            // this wave's 16 output columns: rows of 16 * sizeof(TIn) bytes, one
+            // 16-byte vector per lane and step (LDS is in order within a wave)
+            __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int c0 = t_start + ci * C, L = min(C, t_end - c0);
+            constexpr int VPW = 16 / VEC;                              // vectors per row of the tile
+#pragma unroll
+            for (int e = lane; e < Q::OVEC; e += 64) {
+                const int r = e / VPW, cv = (e % VPW) * VEC;
+                if (r < L)
+                    *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + 16 * wave + cv) =
+                        *reinterpret_cast<const f32x4 *>(sOw + r * 16 + cv);
+            }
+            __asm__ volatile("" ::: "memory");
+        }
+        stage(min(ci + 1, nch - 1), (ci + 1) & 1);
+    }
+
+    if (summary) {
+        float *dst = seg.seg_out + ((int64_t)su * num_heads + h) * DK * (dv + DK);
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i];
+    } else if (final_state && (sflags & SEG_LAST)) {
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
+    }
+}
+
+template <typename TIn, int C>
+static hipError_t launch_prep_t(const void *q, const void *k, const float *g, const float *beta,
+                                const int32_t *cu, int32_t N, int32_t T_tot, int32_t H, int64_t max_chunks,
+                                SegArgs seg, hipStream_t stream)
+{
+    typedef PrefillCfg<TIn, C, 4> P;
+    auto kern = kda_prefill_kernel<TIn, C, 4, MODE_PREP>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)P::bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t grid = (max_chunks + PREP_GROUP - 1) / PREP_GROUP * H;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(P::NT), P::bytes, stream,
+                       static_cast<const TIn *>(q), static_cast<const TIn *>(k), static_cast<const TIn *>(nullptr),
+                       g, beta, nullptr, cu, N, T_tot, H, DK, static_cast<TIn *>(nullptr), nullptr, seg);
+    return hipGetLastError();
+}
+
+template <typename TIn, int C, int NW>
+static hipError_t launch_chain_t(const void *v, const float *init, const int32_t *cu, int32_t N, int32_t T_tot,
+                                 int32_t H, int32_t dv, void *out, float *fin, SegArgs seg, hipStream_t stream)
+{
+    typedef ChainCfg<TIn, C, NW> Q;
+    auto kern = kda_chain_kernel<TIn, C, NW>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::bytes);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
+    const int nblk = (seg.mode == SEG_SUMMARY ? dv + DK : dv) / Q::BV;
+    const int64_t grid = (units + 7) / 8 * 8 * nblk;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(v), init,
+                       cu, N, T_tot, H, dv, static_cast<TIn *>(out), fin, seg);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------- segment planning
 // One workgroup: segments per sequence (at least one, so that empty sequences
-// still produce their final state), exclusive scan, plan entries.
+// still produce their final state), exclusive scan, plan entries; and, if
+// chunk_off is given, the first chunk of each sequence in chunks of `chunk`
+// tokens (chunk_off[N] = total chunks, at most max_chunks).
 __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restrict__ cu, int32_t N,
                                                           int32_t T_tot, int32_t seg_len, int32_t max_segs,
                                                           int32_t *__restrict__ plan,
-                                                          int32_t *__restrict__ seq_seg)
+                                                          int32_t *__restrict__ seq_seg, int32_t chunk,
+                                                          int32_t max_chunks, int32_t *__restrict__ chunk_off)
 {
-    __shared__ int64_t scan[256];
-    int64_t carry = 0;                                 // 64-bit: cu is not trusted
+    __shared__ int64_t scan[256], cscan[256];
+    int64_t carry = 0, ccarry = 0;                     // 64-bit: cu is not trusted
     for (int base = 0; base < N; base += 256) {
         const int n = base + (int)threadIdx.x;
-        int32_t t0 = 0, t1 = 0, ns = 0;
+        int32_t t0 = 0, t1 = 0, ns = 0, nc = 0;
         if (n < N) {
             t0 = min(max(cu[n], 0), T_tot);
             t1 = min(max(cu[n + 1], t0), T_tot);
             ns = max(1, (int32_t)(((int64_t)t1 - t0 + seg_len - 1) / seg_len));
+            nc = (int32_t)(((int64_t)t1 - t0 + chunk - 1) / chunk);
         }
         scan[threadIdx.x] = ns;
+        cscan[threadIdx.x] = nc;
         __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {       // inclusive scan
+        for (int off = 1; off < 256; off <<= 1) {       // inclusive scans
             const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+            const int64_t y = threadIdx.x >= (unsigned)off ? cscan[threadIdx.x - off] : 0;
             __syncthreads();
             scan[threadIdx.x] += x;
+            cscan[threadIdx.x] += y;
             __syncthreads();
         }
+        if (chunk_off && n < N) chunk_off[n] = (int32_t)min(ccarry + cscan[threadIdx.x] - nc, (int64_t)max_chunks);
         const int64_t start = carry + scan[threadIdx.x] - ns;
         if (n < N) {
             // With non-decreasing cu the host bound on max_segs always holds;
@@ -797,10 +1172,12 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
             }
         }
         carry += scan[255];
+        ccarry += cscan[255];
         __syncthreads();
     }
     const int32_t used = (int32_t)min(carry, (int64_t)max_segs);
     if (threadIdx.x == 0) seq_seg[N] = used;
+    if (chunk_off && threadIdx.x == 0) chunk_off[N] = (int32_t)min(ccarry, (int64_t)max_chunks);
     for (int gs = used + (int)threadIdx.x; gs < max_segs; gs += 256) {
         plan[4 * gs] = -1;
         plan[4 * gs + 1] = 0;
@@ -872,7 +1249,7 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          const float *seg_init, float *seg_out, hipStream_t stream)
 {
     using namespace kda;
-    const SegArgs seg = {plan, num_segs, mode, seg_init, seg_out};
+    const SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, nullptr, nullptr};
 #define KDA_CASE(TT, CC, NWW)                                                                    \
     if (chunk == CC && dv_block == 16 * NWW)                                                       \
         return launch_prefill_t<TT, CC, NWW>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
@@ -888,11 +1265,44 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
 }
 
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
-                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, hipStream_t stream)
+                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
+                                         int32_t max_chunks, int32_t *chunk_off, hipStream_t stream)
 {
     hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_tot, seg_len, max_segs,
-                       plan, seq_seg);
+                       plan, seq_seg, chunk, max_chunks, chunk_off);
     return hipGetLastError();
+}
+
+// Chunk-operand pass: images of every (chunk, head), 32-token chunks.
+extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
+                                            const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
+                                            int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
+                                            hipStream_t stream)
+{
+    using namespace kda;
+    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img)};
+    if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
+    return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
+}
+
+// State-chain pass over the images (value blocks of 64 columns); plan, mode,
+// seg_init and seg_out as for kda_launch_prefill.
+extern "C" hipError_t kda_launch_chain(int bf16, const void *v, const float *init, const int32_t *cu, int32_t N,
+                                       int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
+                                       const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
+                                       float *seg_out, const int32_t *chunk_off, const void *img,
+                                       hipStream_t stream)
+{
+    using namespace kda;
+    SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
+                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img))};
+    if (bf16) return launch_chain_t<bf16_t, 32, 4>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    return launch_chain_t<float, 32, 4>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+}
+
+extern "C" size_t kda_chunk_image_bytes(int bf16)
+{
+    return bf16 ? kda::ChunkImage<kda::bf16_t, 32>::BYTES : kda::ChunkImage<float, 32>::BYTES;
 }
 
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,

@@ -55,7 +55,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_prefill_cp.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
                                    i32, vp, ctypes.c_size_t, vp]
     lib.kda_prefill_cp.restype = ctypes.c_int
-    lib.kda_prefill_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.kda_prefill_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.kda_prefill_cp_workspace_size.restype = ctypes.c_size_t
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -132,9 +132,11 @@ def kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state
 
 
 def kda_prefill_cp_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
-                                  seg_len: int = 0) -> int:
-    """Bytes of device workspace kda_prefill_cp needs (0 = unsupported sizes)."""
-    return int(load().kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len))
+                                  dtype=torch.bfloat16, seg_len: int = 0) -> int:
+    """Bytes of device workspace kda_prefill_cp needs (0 = unsupported sizes);
+    dtype is that of q/k/v (torch.bfloat16 or torch.float32)."""
+    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    return int(load().kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code, seg_len))
 
 
 def kda_prefill_cp(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
@@ -144,7 +146,7 @@ def kda_prefill_cp(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state
     ``workspace`` is a uint8 device tensor of at least
     kda_prefill_cp_workspace_size(...) bytes; if None, one is allocated."""
     N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
-    need = kda_prefill_cp_workspace_size(N, T, H, dk, dv, seg_len)
+    need = kda_prefill_cp_workspace_size(N, T, H, dk, dv, q.dtype, seg_len)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")

@@ -123,7 +123,7 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v,
  * missing, misaligned or too small.
  */
 size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
-                                     int32_t dk, int32_t dv, int32_t seg_len);
+                                     int32_t dk, int32_t dv, kda_dtype dtype, int32_t seg_len);
 
 kda_status kda_prefill_cp(const void *q, const void *k, const void *v,
                           const float *g, const float *beta,

@@ -134,15 +134,19 @@ def prefill_cp(lib, **kw):
 
 def test_cp_workspace_size(lib):
     ws = lib.kda_prefill_cp_workspace_size
-    small = ws(1, 4096, 1, 128, 128, 1024)
-    # at least: summaries (dk x (dv + dk)) and entering states (dk x dv) per segment
-    assert small >= 5 * 128 * (256 + 128) * 4
-    assert ws(1, 8192, 1, 128, 128, 1024) > small           # more segments
-    assert ws(1, 4096, 4, 128, 128, 1024) > small           # more heads
-    assert ws(1, 4096, 1, 128, 128, 0) > 0                  # automatic segment length
-    assert ws(1, 4096, 1, 64, 128, 1024) == 0               # unsupported head size
-    assert ws(1, 4096, 1, 128, 128, 48) == 0                # not a multiple of 32
-    assert ws(-1, 4096, 1, 128, 128, 1024) == 0
+    B = K.KDA_BF16
+    small = ws(1, 4096, 1, 128, 128, B, 1024)
+    # at least: summaries (dk x (dv + dk)) and entering states (dk x dv) per
+    # segment, and one chunk-operand image (> 24 KiB in bf16) per 32-token chunk
+    assert small >= 5 * 128 * (256 + 128) * 4 + 128 * 24 * 1024
+    assert ws(1, 4096, 1, 128, 128, K.KDA_F32, 1024) > small   # fp32 operand images are larger
+    assert ws(1, 8192, 1, 128, 128, B, 1024) > small           # more segments and chunks
+    assert ws(1, 4096, 4, 128, 128, B, 1024) > small           # more heads
+    assert ws(1, 4096, 1, 128, 128, B, 0) > 0                  # automatic segment length
+    assert ws(1, 4096, 1, 64, 128, B, 1024) == 0               # unsupported head size
+    assert ws(1, 4096, 1, 128, 128, B, 48) == 0                # not a multiple of 32
+    assert ws(1, 4096, 1, 128, 128, 7, 1024) == 0              # bad dtype
+    assert ws(-1, 4096, 1, 128, 128, B, 1024) == 0
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -106,8 +106,8 @@ def test_cp_final_state_may_alias_initial_state():
 def test_cp_workspace_contents_are_ignored_and_reusable():
     big = to_dev(I.random_prefill([700, 300], H=3, dtype=torch.bfloat16, seed=36))
     small = to_dev(I.random_prefill([90, 200, 31], H=3, dtype=torch.bfloat16, seed=37))
-    need = max(K.kda_prefill_cp_workspace_size(2, 1000, 3, 128, 128, 32),
-               K.kda_prefill_cp_workspace_size(3, 321, 3, 128, 128, 32))
+    need = max(K.kda_prefill_cp_workspace_size(2, 1000, 3, 128, 128, torch.bfloat16, 32),
+               K.kda_prefill_cp_workspace_size(3, 321, 3, 128, 128, torch.bfloat16, 32))
     ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device="cuda").view(torch.uint8)
     o_fresh, f_fresh = run_prefill_cp(small, seg_len=32)
     run_prefill_cp(big, seg_len=32, workspace=ws)
