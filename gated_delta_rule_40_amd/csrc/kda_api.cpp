@@ -23,7 +23,7 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
                                             const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
                                             int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
                                             hipStream_t stream);
-extern "C" hipError_t kda_launch_chain(int bf16, const void *v, const float *init, const int32_t *cu, int32_t N,
+extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
@@ -125,6 +125,7 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const float 
 namespace {
 
 constexpr int32_t kCpChunk = 32;     // chunk size of the segmented runs
+constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the state-chain passes
 
 struct CpLayout {
     size_t plan, seq_seg, chunk_off, seg_out, seg_init, img, total;
@@ -214,12 +215,12 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
     if (e == hipSuccess)   // segment summaries (segments with a successor)
-        e = kda_launch_chain(bf16, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
+        e = kda_launch_chain(bf16, kCpBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
                              plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, s);
     if (e == hipSuccess)   // entering state of every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, s);
     if (e == hipSuccess)   // outputs and final states
-        e = kda_launch_chain(bf16, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
+        e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }

@@ -55,7 +55,12 @@ template <typename H, typename V8, typename V4> struct Mma2 {
         const V4 hi = *reinterpret_cast<const V4 *>(row + k0 + 16 + 4 * j);
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    // Same, each value multiplied by s[k] (fp32 per-channel scale) before rounding.
+    // The same K-block from a row stored in the permuted order of kperm: the
+    // eight values of group j sit contiguously at 8j (one 16-byte read).
+    __device__ static __forceinline__ frag load_p(const H *row, int k0, int j) {
+        return *reinterpret_cast<const V8 *>(row + k0 + 8 * j);
+    }
+    // Same as load, each value multiplied by s[k] (fp32 per-channel scale) before rounding.
     __device__ static __forceinline__ frag load_scaled(const H *row, const float *s, int k0, int j) {
         const V4 lo = *reinterpret_cast<const V4 *>(row + k0 + 4 * j);
         const V4 hi = *reinterpret_cast<const V4 *>(row + k0 + 16 + 4 * j);
@@ -118,6 +123,7 @@ template <> struct Mma<float> {
     __device__ static __forceinline__ frag load(const float *row, int k0, int j) {
         return *reinterpret_cast<const f32x4 *>(row + k0 + 4 * j);
     }
+    __device__ static __forceinline__ frag load_p(const float *row, int k0, int j) { return load(row, k0, j); }
     __device__ static __forceinline__ frag load_scaled(const float *row, const float *s, int k0, int j) {
         const f32x4 x = *reinterpret_cast<const f32x4 *>(row + k0 + 4 * j);
         const f32x4 y = *reinterpret_cast<const f32x4 *>(s + k0 + 4 * j);
@@ -135,6 +141,16 @@ template <> struct Mma<float> {
     __device__ static __forceinline__ frag16 from_acc16(const f32x4 &t, float scale = 1.f) { return t * scale; }
     __device__ static __forceinline__ f32x4 mma16(const frag16 &a, const frag16 &b, f32x4 c) { return mma(a, b, c); }
 };
+
+// Storage position of contraction index k in a row read with load_p: for
+// 2-byte operands, inside each 32-block the indices of lane group j
+// ({4j..4j+3} and {16+4j..16+4j+3}) are stored contiguously at 8j..8j+7, so
+// 4-aligned runs of k stay contiguous; fp32 rows are stored in order.
+template <typename T>
+__device__ __forceinline__ int kperm(int k) {
+    if (sizeof(T) == 4) return k;
+    return (k & ~31) | (((k & 15) >> 2) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
 
 // ------------------------------------------------------------- small loads
 template <typename T> struct Pair;       // two adjacent elements of a row
@@ -175,11 +191,15 @@ __device__ __forceinline__ float pow2_inv(float s) {
     const uint32_t e = (__float_as_uint(s) >> 23) & 0xffu;
     return __uint_as_float((254u - e) << 23);
 }
-// Maximum over the four lane groups (j = lane/16) that share a column.
+// Maximum over the four lane groups (j = lane/16) that share a column, with
+// the gfx950 lane swaps (VALU, no LDS round trip): permlane16_swap(x, x)
+// returns rows {0,0,2,2} and {1,1,3,3} of x (a row = 16 lanes), and
+// permlane32_swap(x, x) the lower and the upper half-wave, each in both halves.
 __device__ __forceinline__ float colmax(float m) {
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
-    return m;
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float absmax4(const f32x4 &x) {
     return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));

@@ -83,6 +83,9 @@ struct PrefillCfg {
     static constexpr int LDK32 = DK + 4;                       // [C][DK] fp32 Gram inputs
     static constexpr int LDV = BV + 16 / (int)sizeof(TIn);     // value / output tiles
 
+    // Rows of the 2-byte MFMA row operands (NKp, Qp, Kc along channels; KhT, P
+    // along tokens) hold their contraction index in kperm order, so each lane
+    // reads a K-block fragment with one 16-byte load.
     static constexpr size_t tileK = sizeof(OpT) * C * LDK;
     // region 0: chain operands and staging; the fp32 sub-tile Gram inputs of a
     // strong-decay chunk overlay it (everything but Kc is rewritten afterwards)
@@ -212,8 +215,8 @@ __device__ __forceinline__ void gram_tiles(const GT *rowA_base, const GT *rowP_b
         const GT *rowC = col_base + (b * SUB + lm) * ld;
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += G::KB) {
-            const typename G::frag bf = hs ? G::load_scaled(rowC, hs + p * DK, k0, lj) : G::load(rowC, k0, lj);
-            acc = G::mma(G::load(rowR, k0, lj), bf, acc);
+            const typename G::frag bf = hs ? G::load_scaled(rowC, hs + p * DK, k0, lj) : G::load_p(rowC, k0, lj);
+            acc = G::mma(G::load_p(rowR, k0, lj), bf, acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -221,9 +224,9 @@ __device__ __forceinline__ void gram_tiles(const GT *rowA_base, const GT *rowP_b
             const int r = a * SUB + rl, cc = b * SUB + lm;
             if (isP) {
                 const float pv = (a == b && lm > rl) ? 0.f : acc[i];
-                sP[r * ldc + cc] = from_f<OpT>(pv);
+                sP[r * ldc + kperm<OpT>(cc)] = from_f<OpT>(pv);
                 if (KBc == 32 && a == b && (a & 1) == 0 && a + 1 < NSUB)
-                    sP[r * ldc + cc + SUB] = from_f<OpT>(0.f);  // a K-block pairs sub-tiles a, a+1
+                    sP[r * ldc + kperm<OpT>(cc + SUB)] = from_f<OpT>(0.f);  // a K-block pairs sub-tiles a, a+1
             } else if (a != b) {
                 sN[r * ldc + cc] = from_f<OpT>(sBeta[r] * signA * acc[i]);   // N = Diag(beta) A
             }
@@ -285,7 +288,7 @@ __device__ __forceinline__ void prep_slow(
             const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowK + hK + c;
             const float kv = ok ? to_f(k[off]) : 0.f;
             if (gram_inputs) sKD32[r * LDK32 + c] = kv * D;
-            else sKhT[c * LDC + r] = from_f<OpT>(GS * kv * D * suff);
+            else sKhT[c * LDC + kperm<OpT>(r)] = from_f<OpT>(GS * kv * D * suff);
             D *= ok ? __expf(g[off]) : 1.f;
         }
         float R = 1.f;                      // prod of alpha up to r within the sub-tile
@@ -300,8 +303,8 @@ __device__ __forceinline__ void prep_slow(
                 sKr32[r * LDK32 + c] = kv * R;
                 sQr32[r * LDK32 + c] = qv * R;
             } else {
-                sNKp[r * LDK + c] = from_f<OpT>(-GS * kv * R * erho);
-                sQp[r * LDK + c] = from_f<OpT>(GS * qv * R * erho);
+                sNKp[r * LDK + kperm<OpT>(c)] = from_f<OpT>(-GS * kv * R * erho);
+                sQp[r * LDK + kperm<OpT>(c)] = from_f<OpT>(GS * qv * R * erho);
             }
         }
     }
@@ -315,13 +318,13 @@ __device__ __forceinline__ void prep_slow(
 // chunk decay sGam and sBeta), V from sV[r * ldv + vc] and writing O to
 // sO[r * ldo + oc] unless `summary`.  S (this wave's 128 x 16 slice, MFMA
 // accumulator layout) is updated in place.
-template <typename TIn, int C, int ldv, int ldo>
+template <typename TIn, int C, int ldv, int ldo, bool SUMMARY>
 __device__ __forceinline__ void chain_chunk(
     f32x4 (&S)[DK / 16], const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
     const typename PrefillCfg<TIn, C, 4>::OpT *sQp, const typename PrefillCfg<TIn, C, 4>::OpT *sKhT,
     const typename PrefillCfg<TIn, C, 4>::OpT *sT, const typename PrefillCfg<TIn, C, 4>::OpT *sP,
     const float *sTs, const float *sGam, const float *sBeta, const TIn *sV, int vc, TIn *sO, int oc,
-    bool summary, int lj, int lm)
+    int lj, int lm)
 {
     typedef PrefillCfg<TIn, C, 4> P;
     typedef typename P::OpT OpT;
@@ -350,7 +353,7 @@ __device__ __forceinline__ void chain_chunk(
             f32x4 t = zero4();
             const OpT *rowA = sNKp + (mt * SUB + lm) * LDK;
 #pragma unroll
-            for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load(rowA, kb * KB, lj), Sf[kb], t);
+            for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load_p(rowA, kb * KB, lj), Sf[kb], t);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = mt * SUB + 4 * lj + i;
@@ -388,15 +391,15 @@ __device__ __forceinline__ void chain_chunk(
 
         // O = Q+ S0 + P W       (rows of sQp hold GS Q+); not needed for a summary
 #pragma unroll
-        for (int mt = 0; mt < (summary ? 0 : NSUB); ++mt) {
+        for (int mt = 0; mt < (SUMMARY ? 0 : NSUB); ++mt) {
             f32x4 o1 = zero4(), o2 = zero4();
             const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
 #pragma unroll
-            for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load(rowQ, kb * KB, lj), Sf[kb], o1);
+            for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load_p(rowQ, kb * KB, lj), Sf[kb], o1);
             const OpT *rowP = sP + (mt * SUB + lm) * LDC;
 #pragma unroll
             for (int kb = 0; kb < C / KB; ++kb)
-                if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load(rowP, kb * KB, lj), Wf[kb], o2);
+                if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load_p(rowP, kb * KB, lj), Wf[kb], o2);
             const f32x4 o = o1 * isS + o2 * isW;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc] = from_f<TIn>(o[i]);
@@ -408,7 +411,7 @@ __device__ __forceinline__ void chain_chunk(
             f32x4 t = zero4();
             const OpT *rowK = sKhT + (16 * r + lm) * LDC;
 #pragma unroll
-            for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load(rowK, kb * KB, lj), Wf[kb], t);
+            for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load_p(rowK, kb * KB, lj), Wf[kb], t);
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[r][i] = S[r][i] * sGam[16 * r + 4 * lj + i] + t[i] * isWk;
         }
@@ -691,9 +694,10 @@ void kda_prefill_kernel(
                     R[1] *= ok ? __expf(rg[it][rr][1]) : 1.f;
                     const float e0 = pre[0] * R[0], e1 = pre[1] * R[1];   // e^Gamma_r
                     const float i0 = __builtin_amdgcn_rcpf(e0), i1 = __builtin_amdgcn_rcpf(e1);
-                    store_pair(sNKp + r * LDK + c, -GS * k0 * e0, -GS * k1 * e1);
-                    store_pair(sQp + r * LDK + c, GS * q0 * e0, GS * q1 * e1);
-                    store_pair(sKc + r * LDK + c, k0 * i0 * (1.f / GS), k1 * i1 * (1.f / GS));
+                    const int pc2 = kperm<OpT>(c);          // c, c + 1 stay adjacent (c even)
+                    store_pair(sNKp + r * LDK + pc2, -GS * k0 * e0, -GS * k1 * e1);
+                    store_pair(sQp + r * LDK + pc2, GS * q0 * e0, GS * q1 * e1);
+                    store_pair(sKc + r * LDK + pc2, k0 * i0 * (1.f / GS), k1 * i1 * (1.f / GS));
                     kh0[rr] = from_f<OpT>(GS * k0 * (gm[0] * i0));
                     kh1[rr] = from_f<OpT>(GS * k1 * (gm[1] * i1));
                 }
@@ -704,8 +708,9 @@ void kda_prefill_kernel(
                     V4 w0, w1;
 #pragma unroll
                     for (int x = 0; x < 4; ++x) { w0[x] = kh0[rr + x]; w1[x] = kh1[rr + x]; }
-                    *reinterpret_cast<V4 *>(sKhT + c * LDC + sg * SEG + rr) = w0;
-                    *reinterpret_cast<V4 *>(sKhT + (c + 1) * LDC + sg * SEG + rr) = w1;
+                    const int pt = kperm<OpT>(sg * SEG + rr);   // 4 tokens stay contiguous
+                    *reinterpret_cast<V4 *>(sKhT + c * LDC + pt) = w0;
+                    *reinterpret_cast<V4 *>(sKhT + (c + 1) * LDC + pt) = w1;
                 }
             }
         };
@@ -822,8 +827,12 @@ void kda_prefill_kernel(
             continue;
         }
         // ---- 4. state-dependent chain (this wave's 16 columns)
-        chain_chunk<TIn, C, LDV, LDV>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
-                                      16 * wave + lm, summary, lj, lm);
+        if (summary)
+            chain_chunk<TIn, C, LDV, LDV, true>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm,
+                                                sO, 16 * wave + lm, lj, lm);
+        else
+            chain_chunk<TIn, C, LDV, LDV, false>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm,
+                                                 sO, 16 * wave + lm, lj, lm);
         __syncthreads();
 
         // ---- 5. output tile -> global (valid tokens only)
@@ -917,7 +926,7 @@ struct ChainCfg {
     static constexpr int OVEC = C * 16 / VEC;                       // vectors of one wave's output tile
 };
 
-template <typename TIn, int C, int NW>
+template <typename TIn, int C, int NW, bool SUMMARY>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
@@ -931,7 +940,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
 
     // ---- workgroup -> (unit, value block): as in the fused kernel
     const bool segmented = seg.plan != nullptr;
-    const bool summary = seg.mode == SEG_SUMMARY;
+    constexpr bool summary = SUMMARY;
     const int nblk = (summary ? dv + DK : dv) / BV;
     const int wg = blockIdx.x;
     const int xcd = wg & 7, slot = wg >> 3;
@@ -1003,31 +1012,31 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         const int c0 = t_start + ci * C, LL = min(C, t_end - c0);
 #pragma unroll
         for (int it = 0; it < Q::VITEMS; ++it) {
-            const int e = tid + it * NT;
-            if (e < C * VPR) {
-                const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
-                rv[it] = trans_cols ? zero4()
-                                    : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
-            }
+            const int e = min(tid + it * NT, C * VPR - 1);
+            const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
+            rv[it] = trans_cols ? zero4()
+                                : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
         }
     };
     const typename Img::Offs offs = {Q::offNKp, Q::offQp, Q::offKhT, Q::offT, Q::offP, Q::offGam, Q::offBeta, Q::offTs};
+    // Every staged register is written on every path (surplus items repeat
+    // the last vector, same value to the same place): a conditional consumer
+    // would leave the loads pending at the loop head for the compiler, which
+    // then waits there for all older memory operations, output stores included.
     auto stage = [&](int ci, int b) {
         unsigned char *base = smem + b * Q::BUF;
 #pragma unroll
         for (int it = 0; it < Q::IITEMS; ++it) {
-            const int e = tid + it * NT;
-            if (e < Img::NVEC) *reinterpret_cast<f32x4 *>(base + Img::lds_off(e, offs)) = ri[it];
+            const int e = min(tid + it * NT, Img::NVEC - 1);
+            *reinterpret_cast<f32x4 *>(base + Img::lds_off(e, offs)) = ri[it];
         }
         TIn *sV = reinterpret_cast<TIn *>(base + Q::offV);
         const int LL = min(C, t_end - (t_start + ci * C));
 #pragma unroll
         for (int it = 0; it < Q::VITEMS; ++it) {
-            const int e = tid + it * NT;
-            if (e < C * VPR) {
-                const int r = e / VPR, cv = (e % VPR) * VEC;
-                *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < LL ? rv[it] : zero4();
-            }
+            const int e = min(tid + it * NT, C * VPR - 1);
+            const int r = e / VPR, cv = (e % VPR) * VEC;
+            *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < LL ? rv[it] : zero4();
         }
     };
     if (nch > 0) {
@@ -1039,24 +1048,26 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         __syncthreads();                          // buffer ci & 1 staged; ci - 1 done with the other
         load(min(ci + 1, nch - 1));               // unconditional, see the fused kernel
         const unsigned char *base = smem + (ci & 1) * Q::BUF;
-        chain_chunk<TIn, C, LDV, 16>(
+        chain_chunk<TIn, C, LDV, 16, SUMMARY>(
             S, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
             reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
             reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
-            reinterpret_cast<const TIn *>(base + Q::offV), 16 * wave + lm, sOw, lm, summary, lj, lm);
-        if (!summary) {
+            reinterpret_cast<const TIn *>(base + Q::offV), 16 * wave + lm, sOw, lm, lj, lm);
+        if constexpr (!SUMMARY) {
             // this wave's 16 output columns: rows of 16 * sizeof(TIn) bytes, one
-            // 16-byte vector per lane and step (LDS is in order within a wave)
+            // 16-byte vector per lane and step (LDS is in order within a wave).
+            // Every lane stores on every path -- rows past the end of the
+            // sequence rewrite the last valid row with its own value -- so that
+            // the compiler can count the store and need not wait for it later.
             __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             const int c0 = t_start + ci * C, L = min(C, t_end - c0);
             constexpr int VPW = 16 / VEC;                              // vectors per row of the tile
 #pragma unroll
             for (int e = lane; e < Q::OVEC; e += 64) {
-                const int r = e / VPW, cv = (e % VPW) * VEC;
-                if (r < L)
-                    *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + 16 * wave + cv) =
-                        *reinterpret_cast<const f32x4 *>(sOw + r * 16 + cv);
+                const int r = min(e / VPW, L - 1), cv = (e % VPW) * VEC;
+                *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + 16 * wave + cv) =
+                    *reinterpret_cast<const f32x4 *>(sOw + r * 16 + cv);
             }
             __asm__ volatile("" ::: "memory");
         }
@@ -1106,16 +1117,17 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
                                  int32_t H, int32_t dv, void *out, float *fin, SegArgs seg, hipStream_t stream)
 {
     typedef ChainCfg<TIn, C, NW> Q;
-    auto kern = kda_chain_kernel<TIn, C, NW>;
-    static bool attr_set = false;
-    if (!attr_set) {
+    const bool summary = seg.mode == SEG_SUMMARY;
+    auto kern = summary ? kda_chain_kernel<TIn, C, NW, true> : kda_chain_kernel<TIn, C, NW, false>;
+    static bool attr_set[2] = {false, false};   // idempotent; racing threads set the same value
+    if (!attr_set[summary]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::bytes);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set[summary] = true;
     }
     const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
-    const int nblk = (seg.mode == SEG_SUMMARY ? dv + DK : dv) / Q::BV;
+    const int nblk = (summary ? dv + DK : dv) / Q::BV;
     const int64_t grid = (units + 7) / 8 * 8 * nblk;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -1285,9 +1297,9 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
 
-// State-chain pass over the images (value blocks of 64 columns); plan, mode,
-// seg_init and seg_out as for kda_launch_prefill.
-extern "C" hipError_t kda_launch_chain(int bf16, const void *v, const float *init, const int32_t *cu, int32_t N,
+// State-chain pass over the images, value blocks of dv_block (64 or 128)
+// columns; plan, mode, seg_init and seg_out as for kda_launch_prefill.
+extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
@@ -1296,6 +1308,9 @@ extern "C" hipError_t kda_launch_chain(int bf16, const void *v, const float *ini
     using namespace kda;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img))};
+    // fp32 images are twice as large: their buffers fit the LDS at 64 columns only
+    if (dv_block == 128 && bf16) return launch_chain_t<bf16_t, 32, 8>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    if (dv_block != 64 && dv_block != 128) return hipErrorInvalidValue;
     if (bf16) return launch_chain_t<bf16_t, 32, 4>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     return launch_chain_t<float, 32, 4>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
 }
