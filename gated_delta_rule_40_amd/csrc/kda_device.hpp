@@ -158,6 +158,11 @@ template <> struct Pair<bf16_t> { typedef bf16x2 type; };
 template <> struct Pair<f16_t> { typedef f16x2 type; };
 template <> struct Pair<float> { typedef f32x2 type; };
 
+template <typename T> struct Quad;       // four adjacent elements of a row
+template <> struct Quad<bf16_t> { typedef bf16x4 type; };
+template <> struct Quad<f16_t> { typedef f16x4 type; };
+template <> struct Quad<float> { typedef f32x4 type; };
+
 template <typename T>
 __device__ __forceinline__ f32x2 load_pair(const T *p) {
     const typename Pair<T>::type x = *reinterpret_cast<const typename Pair<T>::type *>(p);

@@ -60,12 +60,14 @@ struct PrefillCfg {
     // the same order, so every tiling computes bit-identical decay factors.
     static constexpr int GRP = 4;
     static constexpr int NGRP = C / GRP;
-    // fast decay prep: thread -> (segment of SEG tokens, channel pair), from
-    // registers loaded one chunk ahead (ITEMS items per thread)
-    static constexpr int SEG0 = C * 64 / NT;
+    // fast decay prep: thread -> (segment of SEG tokens, CPI consecutive
+    // channels), from registers loaded one chunk ahead (ITEMS items per thread)
+    static constexpr int CPI = 4;
+    static constexpr int IPR = DK / CPI;                               // items per token row
+    static constexpr int SEG0 = C * IPR / NT;
     static constexpr int SEG = SEG0 < GRP ? GRP : (SEG0 > 16 ? 16 : SEG0);
     static constexpr int NSEG = C / SEG;
-    static constexpr int ITEMS = (NSEG * 64 + NT - 1) / NT;
+    static constexpr int ITEMS = (NSEG * IPR + NT - 1) / NT;
     static_assert(SEG % GRP == 0 && SUB % SEG == 0, "prep mapping");
     // slow decay prep: thread -> (sub-tile, CPT consecutive channels)
     static constexpr int CPT = (DK * NSUB >= NT) ? DK * NSUB / NT : 1;
@@ -114,7 +116,8 @@ struct PrefillCfg {
     static constexpr size_t offGam = offH + sizeof(float) * NPAIR * DK;     // [DK]
     static constexpr size_t offBeta = offGam + sizeof(float) * DK;          // [C]
     static constexpr size_t offTs = offBeta + sizeof(float) * C;            // [NSUB][NSUB]
-    static constexpr size_t bytes = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
+    static constexpr size_t offPre = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;   // [NGRP + 1][DK]
+    static constexpr size_t bytes = offPre + sizeof(float) * (NGRP + 1) * DK;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     // workgroups per CU that the LDS allows (the register budget is set to match)
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
@@ -436,6 +439,7 @@ void kda_prefill_kernel(
     constexpr bool kIn16 = P::kIn16;
     constexpr int NSUB = P::NSUB, BV = P::BV, NT = P::NT, KB = P::KB, CPT = P::CPT;
     constexpr int SEG = P::SEG, NSEG = P::NSEG, ITEMS = P::ITEMS, GRP = P::GRP, NGRP = P::NGRP;
+    constexpr int CPI = P::CPI, IPR = P::IPR;
     constexpr int LDK = P::LDK, LDC = P::LDC, LDK32 = P::LDK32, LDV = P::LDV;
     constexpr float GS = P::GS;
 
@@ -456,6 +460,7 @@ void kda_prefill_kernel(
     float *sF = reinterpret_cast<float *>(smem + P::offF);
     float *sH = reinterpret_cast<float *>(smem + P::offH);
     float *sGam = reinterpret_cast<float *>(smem + P::offGam);
+    float *sPre = reinterpret_cast<float *>(smem + P::offPre);   // prefix products of group decays
     float *sBeta = reinterpret_cast<float *>(smem + P::offBeta);
     float *sTs = reinterpret_cast<float *>(smem + P::offTs);
 
@@ -569,23 +574,23 @@ void kda_prefill_kernel(
     constexpr int VEC = 16 / (int)sizeof(TIn);            // elements per 16-byte vector
     constexpr int VPR = BV / VEC;                         // vectors per token row
     constexpr int VITEMS = (C * VPR + NT - 1) / NT;
-    typedef typename Pair<TIn>::type PairT;
-    f32x2 rg[ITEMS][SEG];
-    PairT rk[ITEMS][SEG], rq[ITEMS][SEG];
+    typedef typename Quad<TIn>::type QuadT;
+    f32x4 rg[ITEMS][SEG];
+    QuadT rk[ITEMS][SEG], rq[ITEMS][SEG];
     f32x4 rv[VITEMS];
     float rb = 0.f;
     auto load_chunk = [&](int cc0, int cend) {
         const int LL = max(1, min(C, cend - cc0));
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int item = min(tid + it * NT, NSEG * 64 - 1), sg = item / 64, c = 2 * (item % 64);
+            const int item = min(tid + it * NT, NSEG * IPR - 1), sg = item / IPR, c = CPI * (item % IPR);
 #pragma unroll
             for (int rr = 0; rr < SEG; ++rr) {
                 const int rc = min(sg * SEG + rr, LL - 1);
                 const int64_t off = (int64_t)(cc0 + rc) * rowK + hK + c;
-                rg[it][rr] = *reinterpret_cast<const f32x2 *>(g + off);
-                rk[it][rr] = *reinterpret_cast<const PairT *>(k + off);
-                rq[it][rr] = *reinterpret_cast<const PairT *>(q + off);
+                rg[it][rr] = *reinterpret_cast<const f32x4 *>(g + off);
+                rk[it][rr] = *reinterpret_cast<const QuadT *>(k + off);
+                rq[it][rr] = *reinterpret_cast<const QuadT *>(q + off);
             }
         }
 #pragma unroll
@@ -622,20 +627,22 @@ void kda_prefill_kernel(
         // ---- 1a. group gate sums -> F = exp(sum); beta
 #pragma unroll
         for (int it = 0; it < ITEMS; ++it) {
-            const int item = tid + it * NT, sg = item / 64, c = 2 * (item % 64);
-            if (item < NSEG * 64) {
+            const int item = tid + it * NT, sg = item / IPR, c = CPI * (item % IPR);
+            if (item < NSEG * IPR) {
 #pragma unroll
                 for (int gi = 0; gi < SEG / GRP; ++gi) {
-                    float s0 = 0.f, s1 = 0.f;
+                    f32x4 sum = zero4();
 #pragma unroll
                     for (int rr = gi * GRP; rr < (gi + 1) * GRP; ++rr) {
                         const bool ok = sg * SEG + rr < L;
-                        s0 += ok ? rg[it][rr][0] : 0.f;
-                        s1 += ok ? rg[it][rr][1] : 0.f;
+#pragma unroll
+                        for (int x = 0; x < CPI; ++x) sum[x] += ok ? rg[it][rr][x] : 0.f;
                     }
                     const int G = (sg * SEG) / GRP + gi;
-                    sF[G * DK + c] = __expf(s0);
-                    sF[G * DK + c + 1] = __expf(s1);
+                    f32x4 f;
+#pragma unroll
+                    for (int x = 0; x < CPI; ++x) f[x] = __expf(sum[x]);
+                    *reinterpret_cast<f32x4 *>(sF + G * DK + c) = f;
                 }
             }
         }
@@ -646,7 +653,12 @@ void kda_prefill_kernel(
         //          tables H(a,b) for the strong-decay Gram
         int strong = 0;
         for (int c = tid; c < DK; c += NT) {
-            const float gm = grp_prod(0, NGRP, c);
+            float gm = 1.f;                         // same order as grp_prod(0, G, c)
+            sPre[c] = gm;
+            for (int G = 0; G < NGRP; ++G) {
+                gm *= sF[G * DK + c];
+                sPre[(G + 1) * DK + c] = gm;
+            }
             sGam[c] = gm;
             strong |= gm < __expf(-P::SPAN_CHUNK);
         }
@@ -665,52 +677,52 @@ void kda_prefill_kernel(
         // fast: from the staged registers, chunk-start reference R_r = e^Gamma_r,
         //       written once for both the Gram and the chain
         auto prep_fast = [&]() {
+            typedef OpT V4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int it = 0; it < ITEMS; ++it) {
-                const int item = tid + it * NT, sg = item / 64, c = 2 * (item % 64);
-                if (item >= NSEG * 64) continue;
+                const int item = tid + it * NT, sg = item / IPR, c = CPI * (item % IPR);
+                if (item >= NSEG * IPR) continue;
                 const int G0 = (sg * SEG) / GRP;
-                f32x2 pre, gm;                          // prefix over earlier groups; all groups
-                pre[0] = grp_prod(0, G0, c);
-                pre[1] = grp_prod(0, G0, c + 1);
-                gm[0] = sGam[c];
-                gm[1] = sGam[c + 1];
-                OpT kh0[SEG], kh1[SEG];
-                f32x2 R;
+                const int pc4 = kperm<OpT>(c);              // channels c .. c + 3 stay contiguous
+                f32x4 pre = *reinterpret_cast<const f32x4 *>(sPre + G0 * DK + c);   // prefix over earlier groups
+                const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + c);        // all groups
+                OpT kh[CPI][SEG];
+                f32x4 R;
 #pragma unroll
                 for (int rr = 0; rr < SEG; ++rr) {
                     const int r = sg * SEG + rr;
                     const bool ok = r < L;
                     if (rr % GRP == 0) {
-                        if (rr > 0) {
-                            pre[0] *= sF[(G0 + rr / GRP - 1) * DK + c];
-                            pre[1] *= sF[(G0 + rr / GRP - 1) * DK + c + 1];
-                        }
-                        R = f32x2{1.f, 1.f};
+                        if (rr > 0) pre = *reinterpret_cast<const f32x4 *>(sPre + (G0 + rr / GRP) * DK + c);
+                        R = f32x4{1.f, 1.f, 1.f, 1.f};
                     }
-                    const float k0 = ok ? to_f(rk[it][rr][0]) : 0.f, k1 = ok ? to_f(rk[it][rr][1]) : 0.f;
-                    const float q0 = ok ? to_f(rq[it][rr][0]) : 0.f, q1 = ok ? to_f(rq[it][rr][1]) : 0.f;
-                    R[0] *= ok ? __expf(rg[it][rr][0]) : 1.f;      // decay inside the group
-                    R[1] *= ok ? __expf(rg[it][rr][1]) : 1.f;
-                    const float e0 = pre[0] * R[0], e1 = pre[1] * R[1];   // e^Gamma_r
-                    const float i0 = __builtin_amdgcn_rcpf(e0), i1 = __builtin_amdgcn_rcpf(e1);
-                    const int pc2 = kperm<OpT>(c);          // c, c + 1 stay adjacent (c even)
-                    store_pair(sNKp + r * LDK + pc2, -GS * k0 * e0, -GS * k1 * e1);
-                    store_pair(sQp + r * LDK + pc2, GS * q0 * e0, GS * q1 * e1);
-                    store_pair(sKc + r * LDK + pc2, k0 * i0 * (1.f / GS), k1 * i1 * (1.f / GS));
-                    kh0[rr] = from_f<OpT>(GS * k0 * (gm[0] * i0));
-                    kh1[rr] = from_f<OpT>(GS * k1 * (gm[1] * i1));
+                    V4 nk, qq, kc;
+#pragma unroll
+                    for (int x = 0; x < CPI; ++x) {
+                        const float kx = ok ? to_f(rk[it][rr][x]) : 0.f, qx = ok ? to_f(rq[it][rr][x]) : 0.f;
+                        R[x] *= ok ? __expf(rg[it][rr][x]) : 1.f;     // decay inside the group
+                        const float e = pre[x] * R[x];                 // e^Gamma_r
+                        const float ie = __builtin_amdgcn_rcpf(e);
+                        nk[x] = from_f<OpT>(-GS * kx * e);
+                        qq[x] = from_f<OpT>(GS * qx * e);
+                        kc[x] = from_f<OpT>(kx * ie * (1.f / GS));
+                        kh[x][rr] = from_f<OpT>(GS * kx * (gm[x] * ie));
+                    }
+                    *reinterpret_cast<V4 *>(sNKp + r * LDK + pc4) = nk;
+                    *reinterpret_cast<V4 *>(sQp + r * LDK + pc4) = qq;
+                    *reinterpret_cast<V4 *>(sKc + r * LDK + pc4) = kc;
                 }
-                // K^ transposed: SEG consecutive tokens of channels c, c+1
-                typedef OpT V4 __attribute__((ext_vector_type(4)));
+                // K^ transposed: SEG consecutive tokens of channels c .. c + 3
 #pragma unroll
                 for (int rr = 0; rr < SEG; rr += 4) {
-                    V4 w0, w1;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) { w0[x] = kh0[rr + x]; w1[x] = kh1[rr + x]; }
                     const int pt = kperm<OpT>(sg * SEG + rr);   // 4 tokens stay contiguous
-                    *reinterpret_cast<V4 *>(sKhT + c * LDC + pt) = w0;
-                    *reinterpret_cast<V4 *>(sKhT + (c + 1) * LDC + pt) = w1;
+#pragma unroll
+                    for (int x = 0; x < CPI; ++x) {
+                        V4 w;
+#pragma unroll
+                        for (int y = 0; y < 4; ++y) w[y] = kh[x][rr + y];
+                        *reinterpret_cast<V4 *>(sKhT + (c + x) * LDC + pt) = w;
+                    }
                 }
             }
         };
@@ -822,8 +834,15 @@ void kda_prefill_kernel(
                                           (uint32_t)P::offT, (uint32_t)P::offP, (uint32_t)P::offGam,
                                           (uint32_t)P::offBeta, (uint32_t)P::offTs};
             f32x4 *dst = seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC;
-            for (int e = tid; e < Img::NVEC; e += NT)
-                dst[e] = *reinterpret_cast<const f32x4 *>(smem + Img::lds_off(e, o));
+            // all LDS reads first, then the stores; surplus items repeat the last
+            // vector (same value, same place) so that every store is issued
+            constexpr int SITEMS = (Img::NVEC + NT - 1) / NT;
+            f32x4 tv[SITEMS];
+#pragma unroll
+            for (int it = 0; it < SITEMS; ++it)
+                tv[it] = *reinterpret_cast<const f32x4 *>(smem + Img::lds_off(min(tid + it * NT, Img::NVEC - 1), o));
+#pragma unroll
+            for (int it = 0; it < SITEMS; ++it) dst[min(tid + it * NT, Img::NVEC - 1)] = tv[it];
             continue;
         }
         // ---- 4. state-dependent chain (this wave's 16 columns)
