@@ -206,6 +206,22 @@ __device__ __forceinline__ float colmax(float m) {
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Lane movement inside each 16-lane row by DPP (VALU, no LDS round trip):
+// quad_perm(1,0,3,2) = 0xB1 and quad_perm(2,3,0,1) = 0x4E swap neighbours at
+// distance 1 and 2, row_ror:4 = 0x124 and row_ror:8 = 0x128 rotate the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Maximum over the 16 lanes of each row.
+__device__ __forceinline__ float rowmax16(float m) {
+    m = fmaxf(m, dpp_mov<0xB1>(m));
+    m = fmaxf(m, dpp_mov<0x4E>(m));
+    m = fmaxf(m, dpp_mov<0x124>(m));
+    return fmaxf(m, dpp_mov<0x128>(m));
+}
+// Maximum over the whole wave.
+__device__ __forceinline__ float wavemax(float m) { return colmax(rowmax16(m)); }
 __device__ __forceinline__ float absmax4(const f32x4 &x) {
     return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
 }

@@ -769,14 +769,14 @@ void kda_prefill_kernel(
             for (int r = 0; r < SUB; ++r) x[r] = (r == nc) ? 1.f : 0.f;
 #pragma unroll
             for (int s = 0; s < SUB - 1; ++s) {
-                float col[SUB];
+                // the 4-aligned tail of column s below the diagonal
 #pragma unroll
-                for (int q4 = 0; q4 < SUB; q4 += 4) {
+                for (int q4 = (s + 1) & ~3; q4 < SUB; q4 += 4) {
                     const f32x4 t = *reinterpret_cast<const f32x4 *>(NT + s * P::LDAD + q4);
-                    col[q4] = t[0]; col[q4 + 1] = t[1]; col[q4 + 2] = t[2]; col[q4 + 3] = t[3];
-                }
 #pragma unroll
-                for (int r = s + 1; r < SUB; ++r) x[r] -= col[r] * x[s];
+                    for (int e = 0; e < 4; ++e)
+                        if (q4 + e > s) x[q4 + e] -= t[e] * x[s];
+                }
             }
             // fp16 range: scale the block down by a power of two if it exceeds 2^14
             float sc = 1.f;
@@ -784,10 +784,7 @@ void kda_prefill_kernel(
                 float m = 0.f;
 #pragma unroll
                 for (int r = 0; r < SUB; ++r) m = fmaxf(m, fabsf(x[r]));
-                m = fmaxf(m, __shfl_xor(m, 1));
-                m = fmaxf(m, __shfl_xor(m, 2));
-                m = fmaxf(m, __shfl_xor(m, 4));
-                m = fmaxf(m, __shfl_xor(m, 8));
+                m = rowmax16(m);                         // the 16 lanes of block a
                 if (m > 16384.f) sc = pow2_scale(m);
             }
             if (nc == 0) sTs[a * NSUB + a] = pow2_inv(sc);
@@ -814,9 +811,7 @@ void kda_prefill_kernel(
                 t *= -(sTs[a * NSUB + a] * pow2_inv(sy));
                 float sc = 1.f;
                 if (kIn16) {
-                    float m = absmax4(t);
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+                    const float m = wavemax(absmax4(t));
                     if (m > 16384.f) sc = pow2_scale(m);
                 }
 #pragma unroll
