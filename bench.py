@@ -38,9 +38,9 @@ PREFILL_FREF_PER_HT = 6 * DK * DV + 2 * 64 * (DK + DV)
 # decode bytes per (sequence, head): state read + write, q/k/v/out bf16, g fp32, beta fp32
 DECODE_BYTES_PER_UNIT = 2 * DK * DV * 4 + 3 * 2 * DK + 4 * DK + 4 + 2 * DV
 PREFILL_KERNELS = {
-    "cp": "kda_prefill_cp call: kda_cp_plan_kernel, kda_prefill_kernel<bf16,32,4> (segment summaries), "
-          "kda_cp_combine_kernel, kda_prefill_kernel<bf16,32,4> (segment outputs)",
-    "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4>",
+    "cp": "kda_prefill_cp call: kda_cp_plan_kernel, kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
+          "kda_chain_kernel<bf16,32,8,summary>, kda_cp_combine_kernel, kda_chain_kernel<bf16,32,8,output>",
+    "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
 }
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_traffic.json")
 PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_prefill.hip")
@@ -127,9 +127,9 @@ def cpu_baseline(pre, H, target_s=20.0):
         return time.perf_counter() - t0, sum(lens)
 
     O.build()
-    t, tok = run(64)                       # calibration
+    t, tok = run(2048)                     # calibration (long enough that setup does not dominate)
     rate = tok / max(t, 1e-6)
-    Ls = int(max(64, min(rate * target_s / N, max(cu[n + 1] - cu[n] for n in range(N)))))
+    Ls = int(max(2048, min(rate * target_s / N, max(cu[n + 1] - cu[n] for n in range(N)))))
     t, tok = run(Ls)
     return {"value": tok / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "first %d tokens of each of the %d sequences x %d heads of the same prefill inputs "
