@@ -13,9 +13,7 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          const void *k, const void *v, const float *g,
                                          const float *beta, const float *init, const int32_t *cu,
                                          int32_t N, int32_t T_tot, int32_t H, int32_t dv,
-                                         void *out, float *fin, const int32_t *plan, int32_t num_segs,
-                                         int32_t mode, const float *seg_init, float *seg_out,
-                                         hipStream_t stream);
+                                         void *out, float *fin, hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, hipStream_t stream);
@@ -106,8 +104,7 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const flo
     }
     hipError_t e = kda_launch_prefill(bf16 ? 1 : 0, chunk, dv_block, q, k, v, g, beta, initial_state,
                                       cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                                      final_state, nullptr, 0, 0, nullptr, nullptr,
-                                      reinterpret_cast<hipStream_t>(stream));
+                                      final_state, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -36,6 +36,14 @@
 //   5. coalesced store of the output tile.
 // Ragged chunks are zero-padded (k = q = v = 0, g = 0, b = 0), which leaves
 // the result exact.
+//
+// Two-stage form (context-parallel entry): phases 1-3 do not depend on the
+// state, so a chunk-parallel pass (MODE_PREP) runs them once per (chunk,
+// head) and stores the chain operands as a chunk image; kda_chain_kernel then
+// runs phase 4 alone per (segment, head, value block), reading the images.
+// Segments are combined through their end state from zero and transition
+// (page card "传固定状态片段": local cumulative transform plus zero-state
+// fragment, then a prefix combination).
 #include <type_traits>
 
 #include "kda_device.hpp"
@@ -420,8 +428,8 @@ __device__ __forceinline__ void chain_chunk(
         }
 }
 
-// MODE_FUSED: the whole chunk loop per (unit, value block), as described at
-// the top.  MODE_PREP: the chunk-operand pass -- phases 1-3 only, for
+// MODE_FUSED: the whole chunk loop per (sequence, head, value block), as
+// described at the top.  MODE_PREP: the chunk-operand pass -- phases 1-3 only, for
 // PREP_GROUP consecutive chunks (numbered across sequences) of one head per
 // workgroup, each chunk's operands stored as its image (no state, no V).
 template <typename TIn, int C, int NW, int MODE>
@@ -468,8 +476,9 @@ void kda_prefill_kernel(
     //      A work unit is a (sequence, head) pair, or a (segment, head) pair when
     //      a segment plan is given; summary mode adds DK transition columns.
     constexpr bool kPrep = MODE == MODE_PREP;
-    const bool segmented = !kPrep && seg.plan != nullptr;
-    const bool summary = !kPrep && seg.mode == SEG_SUMMARY;
+    // the fused kernel runs whole sequences; segments run in kda_chain_kernel
+    constexpr bool segmented = false;
+    constexpr bool summary = false;
     const int wg = blockIdx.x;
     int su = 0, h = 0, n = 0, vb = 0, t_start = 0, t_end = 0, sflags = SEG_FIRST | SEG_LAST;
     int gc_begin = 0, nch = 0;      // chunk-operand pass: first global chunk, chunk count
@@ -841,12 +850,8 @@ void kda_prefill_kernel(
             continue;
         }
         // ---- 4. state-dependent chain (this wave's 16 columns)
-        if (summary)
-            chain_chunk<TIn, C, LDV, LDV, true>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm,
-                                                sO, 16 * wave + lm, lj, lm);
-        else
-            chain_chunk<TIn, C, LDV, LDV, false>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm,
-                                                 sO, 16 * wave + lm, lj, lm);
+        chain_chunk<TIn, C, LDV, LDV, false>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
+                                             16 * wave + lm, lj, lm);
         __syncthreads();
 
         // ---- 5. output tile -> global (valid tokens only)
@@ -890,9 +895,8 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
-    const int ncols = seg.mode == SEG_SUMMARY ? dv + DK : dv;
-    const int nblk = ncols / P::BV;
+    const int64_t units = (int64_t)N * H;
+    const int nblk = dv / P::BV;
     const int64_t groups = (units + 7) / 8;
     const int64_t grid = groups * 8 * nblk;
     if (grid <= 0) return hipSuccess;
@@ -1270,12 +1274,10 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          const void *q, const void *k, const void *v,
                                          const float *g, const float *beta, const float *init,
                                          const int32_t *cu, int32_t N, int32_t T_tot, int32_t H,
-                                         int32_t dv, void *out, float *fin,
-                                         const int32_t *plan, int32_t num_segs, int32_t mode,
-                                         const float *seg_init, float *seg_out, hipStream_t stream)
+                                         int32_t dv, void *out, float *fin, hipStream_t stream)
 {
     using namespace kda;
-    const SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, nullptr, nullptr};
+    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, nullptr, nullptr};
 #define KDA_CASE(TT, CC, NWW)                                                                    \
     if (chunk == CC && dv_block == 16 * NWW)                                                       \
         return launch_prefill_t<TT, CC, NWW>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
