@@ -27,6 +27,11 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        float *seg_out, const int32_t *chunk_off, const void *img,
                                        hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
+extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const void *k, const void *v,
+                                               const float *g, const float *beta, const int32_t *cu,
+                                               const int32_t *num_tokens, const float *state_in,
+                                               float *state_out, int32_t N, int32_t T_tot, int32_t H, void *out,
+                                               hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             hipStream_t stream);
@@ -237,6 +242,28 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
     if (units > INT32_MAX) return KDA_ERR_INVALID_ARG;
     hipError_t e = kda_launch_decode(dtype == KDA_BF16 ? 1 : 0, q, k, v, g, beta, state_inout,
                                      num_seqs, num_heads, out, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, const int32_t *cu_seqlens, const int32_t *num_tokens,
+                             const float *state_in, float *state_out, int32_t num_seqs,
+                             int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                             kda_dtype dtype, void *out, kda_stream_t stream)
+{
+    // out may be NULL (replay only): validate it only when given
+    kda_status st = check_common(q, k, v, g, beta, out ? out : q, dk, dv, dtype);
+    if (st == KDA_ERR_INVALID_ARG) return st;
+    if (!cu_seqlens || !state_in || !aligned(state_in, 16) || (state_out && !aligned(state_out, 16)) ||
+        num_seqs < 0 || total_tokens < 0 || num_heads <= 0)
+        return KDA_ERR_INVALID_ARG;
+    if (st != KDA_OK) return st;
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    if (units == 0) return KDA_OK;
+    if (units > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    hipError_t e = kda_launch_decode_tokens(dtype == KDA_BF16 ? 1 : 0, q, k, v, g, beta, cu_seqlens, num_tokens,
+                                           state_in, state_out, num_seqs, total_tokens, num_heads, out,
+                                           reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

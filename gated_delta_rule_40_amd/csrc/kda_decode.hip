@@ -92,6 +92,96 @@ __global__ __launch_bounds__(DEC_THREADS) void kda_decode_kernel(
     }
 }
 
+
+// Several consecutive tokens per (sequence, head) with the state kept in
+// registers: it is read once and written at most once, whatever the number
+// of tokens.  This serves speculative decoding (page section "目标模型太大，缓存
+// 和草稿都必须理解 KDA": the projected inputs of draft tokens are cached, the
+// accepted ones are replayed on chip, and a rejected draft is rolled back by
+// not committing its state): verify a draft with state_out = NULL (outputs
+// for every draft token, state untouched), then replay the accepted prefix
+// with num_tokens = the accepted counts (state committed, out may be NULL).
+// Per token the arithmetic is exactly that of kda_decode_kernel.
+template <typename T>
+__global__ __launch_bounds__(DEC_THREADS) void kda_decode_tokens_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ num_tokens, const float *state_in, float *state_out,
+    int32_t H, int32_t T_tot, T *__restrict__ out)
+{
+    __shared__ float sk[D], sq[D], sa[D];
+    __shared__ f32x4 red_a[ROWG][D / 4], red_b[ROWG][D / 4];
+    __shared__ float su[D];
+    __shared__ float sqk;
+
+    const int64_t u = blockIdx.x;                 // (sequence, head)
+    const int n = (int)(u / H), h = (int)(u % H);
+    const int t = threadIdx.x;
+    const int cg = t & 31, rg = t >> 5;
+    const int t0 = min(max(cu[n], 0), T_tot);
+    int len = min(max(cu[n + 1], t0), T_tot) - t0;
+    if (num_tokens) len = min(len, max(num_tokens[n], 0));
+
+    f32x4 s[RPT];
+    const f32x4 *S4 = reinterpret_cast<const f32x4 *>(state_in + u * (int64_t)D * D);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&S4[(rg + ROWG * i) * (D / 4) + cg]);
+
+    for (int j = 0; j < len; ++j) {
+        const int64_t row = (int64_t)(t0 + j) * H + h;    // this token of this head
+        __syncthreads();                                 // previous token done with the LDS vectors
+        if (t < D) {
+            sk[t] = to_f(k[row * D + t]);
+            sq[t] = to_f(q[row * D + t]);
+            sa[t] = __expf(g[row * D + t]);
+        }
+        __syncthreads();
+        if (t < 64) {   // q.k by one wave
+            float p = sk[t] * sq[t] + sk[t + 64] * sq[t + 64];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
+            if (t == 0) sqk = p;
+        }
+        f32x4 pa = zero4(), pb = zero4();
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + ROWG * i;
+            s[i] *= sa[r];
+            pa += s[i] * sk[r];
+            pb += s[i] * sq[r];
+        }
+        red_a[rg][cg] = pa;
+        red_b[rg][cg] = pb;
+        __syncthreads();
+        const float bt = beta[row];
+        if (t < D) {
+            const int c4 = t >> 2, e = t & 3;
+            float A = 0.f, B = 0.f;
+#pragma unroll
+            for (int r = 0; r < ROWG; ++r) {
+                A += red_a[r][c4][e];
+                B += red_b[r][c4][e];
+            }
+            const float uu = to_f(v[row * D + t]) - A;
+            su[t] = uu;
+            if (out) out[row * D + t] = from_f<T>(B + bt * sqk * uu);
+        }
+        __syncthreads();
+        const f32x4 uu = reinterpret_cast<const f32x4 *>(su)[cg];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + ROWG * i;
+            s[i] = s[i] + (bt * sk[r]) * uu;
+        }
+    }
+
+    if (state_out) {
+        f32x4 *W4 = reinterpret_cast<f32x4 *>(state_out + u * (int64_t)D * D);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(s[i], &W4[(rg + ROWG * i) * (D / 4) + cg]);
+    }
+}
+
 }  // namespace kda
 
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
@@ -110,5 +200,28 @@ extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, 
         hipLaunchKernelGGL(kda_decode_kernel<float>, dim3((unsigned)units), dim3(DEC_THREADS), 0, stream,
                            static_cast<const float *>(q), static_cast<const float *>(k),
                            static_cast<const float *>(v), g, beta, state, static_cast<float *>(out));
+    return hipGetLastError();
+}
+
+extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const void *k, const void *v,
+                                               const float *g, const float *beta, const int32_t *cu,
+                                               const int32_t *num_tokens, const float *state_in,
+                                               float *state_out, int32_t N, int32_t T_tot, int32_t H, void *out,
+                                               hipStream_t stream)
+{
+    using namespace kda;
+    const int64_t units = (int64_t)N * H;
+    if (units <= 0) return hipSuccess;
+    if (units > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (bf16)
+        hipLaunchKernelGGL(kda_decode_tokens_kernel<bf16_t>, dim3((unsigned)units), dim3(DEC_THREADS), 0, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
+                           static_cast<const bf16_t *>(v), g, beta, cu, num_tokens, state_in, state_out, H, T_tot,
+                           static_cast<bf16_t *>(out));
+    else
+        hipLaunchKernelGGL(kda_decode_tokens_kernel<float>, dim3((unsigned)units), dim3(DEC_THREADS), 0, stream,
+                           static_cast<const float *>(q), static_cast<const float *>(k),
+                           static_cast<const float *>(v), g, beta, cu, num_tokens, state_in, state_out, H, T_tot,
+                           static_cast<float *>(out));
     return hipGetLastError();
 }

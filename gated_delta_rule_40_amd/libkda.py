@@ -10,6 +10,7 @@ fallback: if the library is missing the calls raise.
     kda_prefill_cp(..., seg_len=0, workspace=None)
     kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len)
     kda_decode_step(q, k, v, g, beta, state_inout, out)
+    kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, num_tokens=None)
 """
 from __future__ import annotations
 
@@ -26,7 +27,7 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 
 EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_prefill_cp", "kda_prefill_cp_workspace_size",
-           "kda_decode_step", "kda_status_string", "kda_version")
+           "kda_decode_step", "kda_decode_tokens", "kda_status_string", "kda_version")
 
 _lib = None
 
@@ -59,6 +60,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_prefill_cp_workspace_size.restype = ctypes.c_size_t
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_tokens.argtypes = [vp, vp, vp, fp, fp, ip, ip, fp, fp, i32, i32, i32, i32, i32, ctypes.c_int,
+                                      vp, vp]
+    lib.kda_decode_tokens.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -178,3 +182,33 @@ def kda_decode_step(q, k, v, g, beta, state_inout, out, stream=None) -> None:
     lib = load()
     _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_inout), N, H, dk,
                                dv, _dtype_code(q), _ptr(out), _stream(stream)))
+
+
+def kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, num_tokens=None,
+                      stream=None) -> None:
+    """A few consecutive tokens per (sequence, head), state kept on chip.
+    q, k, g: [T, H, dk]; v, out: [T, H, dv]; beta: [T, H]; cu_seqlens: [N+1]
+    int32 on the device; num_tokens: [N] int32 on the device or None;
+    state_in / state_out: [N, H, dk, dv] fp32 (state_out None: not written)."""
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = cu_seqlens.shape[0] - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_in", state_in)):
+        _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens must be int32 on the device")
+    _require(k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (T, H) and tuple(beta.shape) == (T, H),
+             "shape mismatch")
+    _require(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be float32")
+    for name, st in (("state_in", state_in), ("state_out", state_out)):
+        if st is not None:
+            _require(st.dtype == torch.float32 and st.is_contiguous() and tuple(st.shape) == (N, H, dk, dv),
+                     "%s must be contiguous float32 [N, H, dk, dv]" % name)
+    if out is not None:
+        _require(out.is_contiguous() and out.shape == v.shape and out.dtype == q.dtype, "out must match v")
+    if num_tokens is not None:
+        _require(num_tokens.dtype == torch.int32 and num_tokens.is_cuda and tuple(num_tokens.shape) == (N,),
+                 "num_tokens must be int32 [N] on the device")
+    lib = load()
+    _check(lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                 _ptr(num_tokens), _ptr(state_in), _ptr(state_out), N, T, H, dk, dv,
+                                 _dtype_code(q), _ptr(out), _stream(stream)))

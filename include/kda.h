@@ -150,6 +150,42 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv,
                            kda_dtype dtype, void *out, kda_stream_t stream);
 
+/*
+ * kda_decode_tokens -- a few consecutive tokens per (sequence, head) with the
+ * state held on chip: it is read once and written at most once, so k tokens
+ * cost about one state round trip instead of k.  This is the speculative
+ * decoding path of page ailearn.mscapital.top/kimi-k3.html, section
+ * "目标模型太大，缓存和草稿都必须理解 KDA": the projected inputs of the draft
+ * tokens are cached, the accepted ones are replayed on chip, and a rejected
+ * draft is rolled back by not committing its state.  Typical use:
+ *   verify:  state_out = NULL, num_tokens = NULL  -> out for every draft token,
+ *            the committed state is untouched;
+ *   replay:  num_tokens = accepted counts, state_out = state_in, out = NULL
+ *            -> the state advanced over the accepted prefix only.
+ *
+ *   q, k, g       [total_tokens, num_heads, dk]   dtype / fp32
+ *   v             [total_tokens, num_heads, dv]   dtype
+ *   beta          [total_tokens, num_heads]       fp32
+ *   cu_seqlens    [num_seqs + 1]  int32, DEVICE: sequence n owns tokens
+ *                 [cu[n], cu[n+1]) (clamped as for kda_prefill)
+ *   num_tokens    [num_seqs]      int32, DEVICE, or NULL: process only the
+ *                 first min(max(num_tokens[n], 0), cu[n+1] - cu[n]) tokens
+ *   state_in      [num_seqs, num_heads, dk, dv]   fp32
+ *   state_out     same shape, or NULL (not written); may equal state_in
+ *   out           [total_tokens, num_heads, dv]   dtype, or NULL; rows of the
+ *                 processed tokens are written, other rows are left untouched
+ * Per token the arithmetic is that of kda_decode_step (bitwise identical to
+ * applying kda_decode_step token by token).  Intended for a few tokens per
+ * sequence; long runs belong to kda_prefill.
+ */
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             const int32_t *cu_seqlens, const int32_t *num_tokens,
+                             const float *state_in, float *state_out,
+                             int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                             int32_t dk, int32_t dv, kda_dtype dtype,
+                             void *out, kda_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *kda_status_string(kda_status status);
 

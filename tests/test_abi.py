@@ -166,3 +166,30 @@ def test_prefill_cp_rejects(lib, kw, code):
 
 def test_prefill_cp_empty_batch_is_a_no_op(lib):
     assert prefill_cp(lib, N=0, T=0) == K.KDA_OK
+
+
+def decode_tokens(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, cu=P, nt=NULL, sin=P, sout=NULL, N=1, T=4, H=1, dk=128, dv=128,
+             dtype=K.KDA_BF16, out=NULL)
+    a.update(kw)
+    return lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"], a["nt"], a["sin"], a["sout"],
+                                 a["N"], a["T"], a["H"], a["dk"], a["dv"], a["dtype"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(cu=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(sin=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(sin=ctypes.c_void_p(0x10004)), K.KDA_ERR_INVALID_ARG),
+    (dict(sout=ctypes.c_void_p(0x10008)), K.KDA_ERR_INVALID_ARG),
+    (dict(out=ctypes.c_void_p(0x10002)), K.KDA_ERR_INVALID_ARG),
+    (dict(N=-1), K.KDA_ERR_INVALID_ARG),
+    (dict(dtype=5), K.KDA_ERR_INVALID_ARG),
+    (dict(dk=64), K.KDA_ERR_UNSUPPORTED),
+])
+def test_decode_tokens_rejects(lib, kw, code):
+    assert decode_tokens(lib, **kw) == code
+
+
+def test_decode_tokens_empty_batch_is_a_no_op(lib):
+    assert decode_tokens(lib, N=0, T=0) == K.KDA_OK
