@@ -238,6 +238,30 @@ def main():
     dec_gbs = dec_bytes / (dec_step_ms * 1e-3) / 1e9
     traffic = pmc_traffic()
 
+    # speculative-decoding replay: 4 draft tokens per (sequence, head) of the
+    # decode batch, outputs for all of them and the state committed, one call
+    # (its own measurement, outside the timed steps)
+    RT = 4
+    perm = lambda x: x[:RT].transpose(0, 1).reshape(Nd * RT, *x.shape[2:]).contiguous()
+    rq, rk, rv, rg, rb = (perm(dec[key]) for key in ("q", "k", "v", "g", "beta"))
+    rcu = torch.arange(Nd + 1, dtype=torch.int32, device=dev) * RT
+    rout = torch.empty(Nd * RT, Hd, DV, dtype=torch.bfloat16, device=dev)
+
+    def replay():
+        K.kda_decode_tokens(rq, rk, rv, rg, rb, rcu, state, state_out=state, out=rout)
+
+    for _ in range(2):
+        replay()
+    r_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    r_ev[0].record(stream)
+    for _ in range(5):
+        replay()
+    r_ev[1].record(stream)
+    torch.cuda.synchronize()
+    rep_ms = r_ev[0].elapsed_time(r_ev[1]) / 5
+    rep_bytes = Nd * Hd * (2 * DK * DV * 4 + RT * (DECODE_BYTES_PER_UNIT - 2 * DK * DV * 4))
+    rep_gbs = rep_bytes / (rep_ms * 1e-3) / 1e9
+
     result = {
         "metric": METRIC,
         "value": T / (pre_avg * 1e-3),
@@ -271,6 +295,10 @@ def main():
                    "roofline": {"bound": "hbm", "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": dec_gbs / HBM_PEAK_GBS, "kernel": "kda_decode_kernel<bf16>",
                                 "algorithmic_bytes_per_launch": dec_bytes}},
+        "decode_tokens": {"draft_tokens": RT, "ms_per_call": rep_ms, "tokens_per_s": Nd * RT / (rep_ms * 1e-3),
+                          "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": rep_gbs / HBM_PEAK_GBS, "kernel": "kda_decode_tokens_kernel<bf16>",
+                                       "algorithmic_bytes_per_launch": rep_bytes}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

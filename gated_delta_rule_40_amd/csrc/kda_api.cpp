@@ -13,7 +13,8 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          const void *k, const void *v, const float *g,
                                          const float *beta, const float *init, const int32_t *cu,
                                          int32_t N, int32_t T_tot, int32_t H, int32_t dv,
-                                         void *out, float *fin, hipStream_t stream);
+                                         void *out, float *fin, float *snap, int32_t snap_every,
+                                         int32_t max_snaps, hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, hipStream_t stream);
@@ -80,11 +81,12 @@ int auto_dv_block(int64_t units, int dv)
 
 extern "C" {
 
-kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
-                          int32_t dv, kda_dtype dtype, void *out, float *final_state,
-                          int32_t chunk, int32_t dv_block, kda_stream_t stream)
+static kda_status prefill_impl(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                               int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                               int32_t dv, kda_dtype dtype, void *out, float *final_state,
+                               int32_t chunk, int32_t dv_block, float *snap, int32_t snap_every,
+                               int32_t max_snaps, kda_stream_t stream)
 {
     kda_status st = check_common(q, k, v, g, beta, out, dk, dv, dtype);
     if (st == KDA_ERR_INVALID_ARG) return st;
@@ -100,6 +102,10 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const flo
     // 64-token bf16 chunks need at least two waves (value block >= 32)
     const int min_block = (bf16 && chunk == 64) ? 32 : 16;
     if (dv_block != 0 && dv_block < min_block) return KDA_ERR_UNSUPPORTED;
+    if (snap) {
+        if (snap_every <= 0 || max_snaps <= 0 || !aligned(snap, 4)) return KDA_ERR_INVALID_ARG;
+        if (snap_every % chunk) return KDA_ERR_UNSUPPORTED;
+    }
     const int64_t units = (int64_t)num_seqs * num_heads;
     if (units == 0) return KDA_OK;
     if (units * (dv / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;   // grid size
@@ -109,8 +115,30 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const flo
     }
     hipError_t e = kda_launch_prefill(bf16 ? 1 : 0, chunk, dv_block, q, k, v, g, beta, initial_state,
                                       cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                                      final_state, reinterpret_cast<hipStream_t>(stream));
+                                      final_state, snap, snap_every, max_snaps,
+                                      reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status kda_prefill_ex(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                          int32_t dv, kda_dtype dtype, void *out, float *final_state,
+                          int32_t chunk, int32_t dv_block, kda_stream_t stream)
+{
+    return prefill_impl(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
+                        dtype, out, final_state, chunk, dv_block, nullptr, 0, 0, stream);
+}
+
+kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                                 int32_t dv, kda_dtype dtype, void *out, float *final_state,
+                                 int32_t snap_every, int32_t max_snaps, float *snapshots, kda_stream_t stream)
+{
+    if (!snapshots) return KDA_ERR_INVALID_ARG;
+    return prefill_impl(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv,
+                        dtype, out, final_state, 32, 64, snapshots, snap_every, max_snaps, stream);
 }
 
 kda_status kda_prefill(const void *q, const void *k, const void *v, const float *g,

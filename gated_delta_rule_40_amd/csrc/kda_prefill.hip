@@ -150,9 +150,12 @@ struct SegArgs {
     float *seg_out;          // [num_segs][H][DK][dv + DK] summaries (SEG_SUMMARY)
     const int32_t *chunk_off;   // [N + 1] first chunk of each sequence (chunk-image passes)
     f32x4 *img;                 // chunk-operand images (chunk-image passes)
+    float *snap;                // [N][max_snaps][H][DK][dv] state snapshots, or nullptr (fused kernel)
+    int32_t snap_every;         // tokens between snapshots, a multiple of the chunk
+    int32_t max_snaps;
 };
 
-enum { MODE_FUSED = 0, MODE_PREP = 1 };
+enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2 };   // MODE_SNAP: fused + state snapshots
 constexpr int PREP_GROUP = 8;    // consecutive chunks per workgroup of the chunk-operand pass
 
 // Chunk-operand image: everything the state chain of one (chunk, head) reads
@@ -861,6 +864,18 @@ void kda_prefill_kernel(
                 *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + cv) =
                     *reinterpret_cast<const f32x4 *>(sO + r * LDV + cv);
         }
+        // ---- state snapshot when this chunk ends (snap_every)-aligned tokens
+        //      into the sequence (prefix caching)
+        if (MODE == MODE_SNAP && L == C && ((ci + 1) * C) % seg.snap_every == 0) {
+            const int j = (ci + 1) * C / seg.snap_every - 1;
+            if (j < seg.max_snaps) {
+                float *dst = seg.snap + (((int64_t)n * seg.max_snaps + j) * num_heads + h) * DK * dv;
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
+            }
+        }
     }
 
     if (summary) {
@@ -880,14 +895,14 @@ void kda_prefill_kernel(
 }
 
 // ------------------------------------------------------------------ launch
-template <typename TIn, int C, int NW>
+template <typename TIn, int C, int NW, int MODE>
 static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, const float *g,
                                    const float *beta, const float *init, const int32_t *cu,
                                    int32_t N, int32_t T_tot, int32_t H, int32_t dv, void *out,
                                    float *fin, SegArgs seg, hipStream_t stream)
 {
     typedef PrefillCfg<TIn, C, NW> P;
-    auto kern = kda_prefill_kernel<TIn, C, NW, MODE_FUSED>;
+    auto kern = kda_prefill_kernel<TIn, C, NW, MODE>;
     static bool attr_set = false;   // idempotent; racing threads set the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1274,13 +1289,19 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          const void *q, const void *k, const void *v,
                                          const float *g, const float *beta, const float *init,
                                          const int32_t *cu, int32_t N, int32_t T_tot, int32_t H,
-                                         int32_t dv, void *out, float *fin, hipStream_t stream)
+                                         int32_t dv, void *out, float *fin, float *snap, int32_t snap_every,
+                                         int32_t max_snaps, hipStream_t stream)
 {
     using namespace kda;
-    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, nullptr, nullptr};
+    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, nullptr, nullptr, snap, snap_every, max_snaps};
+    if (snap) {   // snapshots: 32-token chunks, 64-column value blocks
+        if (chunk != 32 || dv_block != 64) return hipErrorInvalidValue;
+        if (bf16) return launch_prefill_t<bf16_t, 32, 4, MODE_SNAP>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+        return launch_prefill_t<float, 32, 4, MODE_SNAP>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    }
 #define KDA_CASE(TT, CC, NWW)                                                                    \
     if (chunk == CC && dv_block == 16 * NWW)                                                       \
-        return launch_prefill_t<TT, CC, NWW>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+        return launch_prefill_t<TT, CC, NWW, MODE_FUSED>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (bf16) {
         KDA_CASE(bf16_t, 32, 1) KDA_CASE(bf16_t, 32, 2) KDA_CASE(bf16_t, 32, 4) KDA_CASE(bf16_t, 32, 8)
         KDA_CASE(bf16_t, 64, 2) KDA_CASE(bf16_t, 64, 4) KDA_CASE(bf16_t, 64, 8)
@@ -1308,7 +1329,7 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
                                             hipStream_t stream)
 {
     using namespace kda;
-    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img)};
+    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0};
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
@@ -1323,7 +1344,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
 {
     using namespace kda;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
-                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img))};
+                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), nullptr, 0, 0};
     // fp32 images are twice as large: their buffers fit the LDS at 64 columns only
     if (dv_block == 128 && bf16) return launch_chain_t<bf16_t, 32, 8>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (dv_block != 64 && dv_block != 128) return hipErrorInvalidValue;

@@ -7,6 +7,7 @@ fallback: if the library is missing the calls raise.
 
     kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
     kda_prefill_ex(..., chunk=0, dv_block=0)
+    kda_prefill_snapshots(..., snapshots, snap_every)
     kda_prefill_cp(..., seg_len=0, workspace=None)
     kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len)
     kda_decode_step(q, k, v, g, beta, state_inout, out)
@@ -26,8 +27,9 @@ LIB_PATH = os.path.join(_HERE, "lib", "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 
-EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_prefill_cp", "kda_prefill_cp_workspace_size",
-           "kda_decode_step", "kda_decode_tokens", "kda_status_string", "kda_version")
+EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_prefill_snapshots", "kda_prefill_cp",
+           "kda_prefill_cp_workspace_size", "kda_decode_step", "kda_decode_tokens", "kda_status_string",
+           "kda_version")
 
 _lib = None
 
@@ -53,6 +55,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_prefill_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
                                    i32, i32, vp]
     lib.kda_prefill_ex.restype = ctypes.c_int
+    lib.kda_prefill_snapshots.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp,
+                                          fp, i32, i32, fp, vp]
+    lib.kda_prefill_snapshots.restype = ctypes.c_int
     lib.kda_prefill_cp.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
                                    i32, vp, ctypes.c_size_t, vp]
     lib.kda_prefill_cp.restype = ctypes.c_int
@@ -133,6 +138,21 @@ def kda_prefill_ex(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state
     _check(lib.kda_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                               _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
                               _ptr(final_state), int(chunk), int(dv_block), _stream(stream)))
+
+
+def kda_prefill_snapshots(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, snapshots,
+                          snap_every: int, stream=None) -> None:
+    """kda_prefill plus the state after every snap_every tokens of each
+    sequence: snapshots [N, max_snaps, H, dk, dv] fp32 (max_snaps from its shape)."""
+    N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    _require(snapshots.dtype == torch.float32 and snapshots.is_contiguous() and snapshots.dim() == 5 and
+             snapshots.shape[0] == N and tuple(snapshots.shape[2:]) == (H, dk, dv),
+             "snapshots must be contiguous float32 [N, max_snaps, H, dk, dv]")
+    lib = load()
+    _check(lib.kda_prefill_snapshots(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                     _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
+                                     _ptr(final_state), int(snap_every), int(snapshots.shape[1]),
+                                     _ptr(snapshots), _stream(stream)))
 
 
 def kda_prefill_cp_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,

@@ -101,6 +101,32 @@ kda_status kda_prefill_ex(const void *q, const void *k, const void *v,
                           int32_t chunk, int32_t dv_block, kda_stream_t stream);
 
 /*
+ * kda_prefill_snapshots -- kda_prefill that also keeps copies of the state
+ * at regular token boundaries, so that a prefix cache can restore the KDA
+ * state of any of those prefixes (page ailearn.mscapital.top/kimi-k3.html,
+ * section "目标模型太大，缓存和草稿都必须理解 KDA": the prefix cache restores the
+ * recurrent state at a token boundary).
+ *   snap_every  tokens between snapshots, a positive multiple of 32 (the
+ *               chunk); other multiples return KDA_ERR_UNSUPPORTED
+ *   max_snaps   snapshots kept per sequence (> 0)
+ *   snapshots   [num_seqs, max_snaps, num_heads, dk, dv] fp32, DEVICE:
+ *               snapshots[n][j] = the state after the first (j + 1) *
+ *               snap_every tokens of sequence n, for every j < max_snaps with
+ *               (j + 1) * snap_every <= its length; other entries are left
+ *               untouched.
+ * Other arguments and conventions as kda_prefill; snapshot j equals, bit for
+ * bit, the final state of kda_prefill over that prefix alone.
+ */
+kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 const float *initial_state, const int32_t *cu_seqlens,
+                                 int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                 int32_t dk, int32_t dv, kda_dtype dtype,
+                                 void *out, float *final_state,
+                                 int32_t snap_every, int32_t max_snaps, float *snapshots,
+                                 kda_stream_t stream);
+
+/*
  * kda_prefill_cp -- kda_prefill with context parallelism inside the device.
  * Each sequence is split into segments of seg_len tokens that
  * run side by side: every segment but a sequence's last is first run from a

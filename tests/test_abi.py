@@ -193,3 +193,28 @@ def test_decode_tokens_rejects(lib, kw, code):
 
 def test_decode_tokens_empty_batch_is_a_no_op(lib):
     assert decode_tokens(lib, N=0, T=0) == K.KDA_OK
+
+
+def prefill_snap(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, init=NULL, cu=P, N=1, T=64, H=1, dk=128, dv=128,
+             dtype=K.KDA_BF16, out=P, fin=NULL, every=64, maxs=2, snaps=P)
+    a.update(kw)
+    return lib.kda_prefill_snapshots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["init"], a["cu"], a["N"], a["T"],
+                                     a["H"], a["dk"], a["dv"], a["dtype"], a["out"], a["fin"], a["every"],
+                                     a["maxs"], a["snaps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(snaps=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(every=0), K.KDA_ERR_INVALID_ARG),
+    (dict(maxs=0), K.KDA_ERR_INVALID_ARG),
+    (dict(every=48), K.KDA_ERR_UNSUPPORTED),
+    (dict(every=48, N=0, T=0), K.KDA_ERR_UNSUPPORTED),          # checked before the empty-batch exit
+    (dict(dk=64), K.KDA_ERR_UNSUPPORTED),
+])
+def test_prefill_snapshots_rejects(lib, kw, code):
+    assert prefill_snap(lib, **kw) == code
+
+
+def test_prefill_snapshots_empty_batch_is_a_no_op(lib):
+    assert prefill_snap(lib, N=0, T=0) == K.KDA_OK

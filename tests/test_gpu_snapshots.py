@@ -1,0 +1,70 @@
+"""GPU parity of kda_prefill_snapshots (the state kept every snap_every tokens,
+for a prefix cache) against the fp64 oracle run on each prefix, through the
+C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_40_amd import inputs as I
+from gated_delta_rule_40_amd import libkda as K
+from kda_parity import TOL, assert_close, host, log, oracle_prefill, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    K.load()
+
+
+def _prefix(inp, n, length):
+    cu = inp["cu_seqlens"].cpu().tolist()
+    sub = {key: inp[key][cu[n]:cu[n] + length].contiguous() for key in ("q", "k", "v", "g", "beta")}
+    sub["initial_state"] = inp["initial_state"][n:n + 1].contiguous()
+    sub["cu_seqlens"] = torch.tensor([0, length], dtype=torch.int32, device=inp["q"].device)
+    return sub
+
+
+@pytest.mark.parametrize("dtype,every", [(torch.bfloat16, 64), (torch.float32, 32)])
+def test_snapshots_vs_oracle(dtype, every):
+    lengths = [0, 31, 32, 100, 257, 320]
+    H, max_snaps = 2, 4
+    inp = I.random_prefill(lengths, H=H, dtype=dtype, seed=50, device="cuda")
+    T = sum(lengths)
+    out = torch.empty(T, H, 128, dtype=dtype, device="cuda")
+    fin = torch.empty(len(lengths), H, 128, 128, device="cuda")
+    snaps = torch.full((len(lengths), max_snaps, H, 128, 128), float("nan"), device="cuda")
+    K.kda_prefill_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                            inp["cu_seqlens"], out, fin, snaps, every)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle_prefill(inp)
+    assert_close(host(out), ref_out, TOL[dtype], "snapshots out", dtype)
+    assert_close(host(fin), ref_fin, TOL[dtype], "snapshots final_state")
+    for n, L in enumerate(lengths):
+        for j in range(max_snaps):
+            got = host(snaps[n, j])
+            if (j + 1) * every > L:
+                assert np.isnan(got).all(), (n, j)
+                continue
+            log("[snapshot] sequence %d prefix %d" % (n, (j + 1) * every))
+            _, ref = oracle_prefill(_prefix(inp, n, (j + 1) * every))
+            assert_close(got, ref[0], TOL[dtype], "snapshot n=%d j=%d" % (n, j))
+
+
+def test_snapshot_equals_prefill_of_prefix_bitwise():
+    lengths = [200, 130]
+    inp = I.random_prefill(lengths, H=3, dtype=torch.bfloat16, seed=51, device="cuda", g_lo=-5.0)
+    snaps = torch.empty(2, 3, 3, 128, 128, device="cuda")
+    out = torch.empty(sum(lengths), 3, 128, dtype=torch.bfloat16, device="cuda")
+    K.kda_prefill_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                            inp["cu_seqlens"], out, None, snaps, 64)
+    torch.cuda.synchronize()
+    for n, L in enumerate(lengths):
+        for j in range(L // 64):
+            _, f = run_prefill(_prefix(inp, n, (j + 1) * 64), chunk=32, dv_block=64)
+            assert torch.equal(f[0], snaps[n, j]), (n, j)
+    # outputs equal the plain kda_prefill at the same tiling
+    o_ref, _ = run_prefill(inp, chunk=32, dv_block=64)
+    assert torch.equal(o_ref, out)
