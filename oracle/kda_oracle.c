@@ -195,3 +195,132 @@ int kda_oracle_decode_step(const float *q, const float *k, const float *v,
     }
     return failed ? 2 : 0;
 }
+
+/*
+ * Backward pass (gradients of a scalar loss through the recurrence), by the
+ * chain rule applied to the token step in reverse order.  With Sp = S_{t-1},
+ * Sbar = Diag(alpha) Sp, u = v - Sbar^T k, S = Sbar + beta k u^T, o = S^T q,
+ * and dS the loss gradient with respect to S_t (from later tokens and, at the
+ * end, d(final_state)):
+ *     dS   += q do^T;                      dq = S do
+ *     du    = beta dS^T k;                 dbeta = k^T dS u;   dk = beta dS u
+ *     dv    = du;   dSbar = dS - k du^T;   dk -= Sbar du
+ *     dalpha = rowsum(dSbar (.) Sp);       dg = alpha (.) dalpha
+ *     dS_{t-1} = Diag(alpha) dSbar
+ * and d(initial_state) = dS after the first token.  Each unit keeps all its
+ * states S_0 .. S_T (fp64), so this is meant for test-sized inputs.
+ *   dout: [T_tot, H, dv] fp64;  dfinal: [N, H, dk, dv] fp64 or NULL (zero)
+ *   dq, dk, dg: [T_tot, H, dk] fp64;  dv: [T_tot, H, dv] fp64;
+ *   dbeta: [T_tot, H] fp64;  dinit: [N, H, dk, dv] fp64 or NULL
+ * Returns 0 on success, 1 on invalid arguments, 2 on allocation failure.
+ */
+int kda_oracle_backward(const float *q, const float *k, const float *v,
+                        const float *g, const float *beta,
+                        const double *initial_state, const int32_t *cu_seqlens,
+                        int32_t num_seqs, int32_t num_heads, int32_t dk, int32_t dv,
+                        const double *dout, const double *dfinal,
+                        double *dq, double *dk_out, double *dv_out, double *dg, double *dbeta,
+                        double *dinit, int32_t num_threads)
+{
+    if (!q || !k || !v || !g || !beta || !cu_seqlens || !dout) return 1;
+    if (!dq || !dk_out || !dv_out || !dg || !dbeta) return 1;
+    if (num_seqs < 0 || num_heads <= 0 || dk <= 0 || dv <= 0) return 1;
+    if (cu_seqlens[0] != 0) return 1;
+    for (int32_t n = 0; n < num_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n]) return 1;
+    const int64_t nunits = (int64_t)num_seqs * num_heads;
+    const size_t SS = (size_t)dk * dv;
+    int failed = 0;
+#ifdef _OPENMP
+    if (num_threads > 0) omp_set_num_threads(num_threads);
+#else
+    (void)num_threads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < nunits; ++i) {
+        const int32_t n = (int32_t)(i / num_heads), h = (int32_t)(i % num_heads);
+        const int32_t t0 = cu_seqlens[n], len = cu_seqlens[n + 1] - cu_seqlens[n];
+        const size_t sidx = ((size_t)n * num_heads + h) * SS;
+        double *S = (double *)malloc(sizeof(double) * SS * ((size_t)len + 1));
+        double *dS = (double *)malloc(sizeof(double) * SS);
+        double *Sbar = (double *)malloc(sizeof(double) * SS);
+        double *u = (double *)malloc(sizeof(double) * dv);
+        double *o = (double *)malloc(sizeof(double) * dv);
+        double *du = (double *)malloc(sizeof(double) * dv);
+        if (!S || !dS || !Sbar || !u || !o || !du) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            /* forward, keeping every state */
+            if (initial_state) memcpy(S, initial_state + sidx, sizeof(double) * SS);
+            else memset(S, 0, sizeof(double) * SS);
+            for (int32_t t = 0; t < len; ++t) {
+                const size_t th = (size_t)(t0 + t) * num_heads + h;
+                memcpy(S + (size_t)(t + 1) * SS, S + (size_t)t * SS, sizeof(double) * SS);
+                kda_token_step(S + (size_t)(t + 1) * SS, dk, dv, q + th * dk, k + th * dk, v + th * dv,
+                               g + th * dk, (double)beta[th], u, o);
+            }
+            /* reverse */
+            if (dfinal) memcpy(dS, dfinal + sidx, sizeof(double) * SS);
+            else memset(dS, 0, sizeof(double) * SS);
+            for (int32_t t = len - 1; t >= 0; --t) {
+                const size_t th = (size_t)(t0 + t) * num_heads + h;
+                const float *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *gt = g + th * dk;
+                const double bt = (double)beta[th];
+                const double *Sp = S + (size_t)t * SS, *Sn = S + (size_t)(t + 1) * SS;
+                const double *dot = dout + th * dv;
+                /* recompute Sbar and u of this token */
+                for (int c = 0; c < dk; ++c) {
+                    const double a = exp((double)gt[c]);
+                    for (int j = 0; j < dv; ++j) Sbar[(size_t)c * dv + j] = a * Sp[(size_t)c * dv + j];
+                }
+                for (int j = 0; j < dv; ++j) {
+                    double s = (double)vt[j];
+                    for (int c = 0; c < dk; ++c) s -= Sbar[(size_t)c * dv + j] * (double)kt[c];
+                    u[j] = s;
+                }
+                /* o = S^T q */
+                for (int c = 0; c < dk; ++c) {
+                    double s = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        dS[(size_t)c * dv + j] += (double)qt[c] * dot[j];
+                        s += Sn[(size_t)c * dv + j] * dot[j];
+                    }
+                    dq[th * dk + c] = s;
+                }
+                /* S = Sbar + beta k u^T */
+                double db = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    double s = 0.0;
+                    for (int c = 0; c < dk; ++c) s += dS[(size_t)c * dv + j] * (double)kt[c];
+                    du[j] = bt * s;
+                    db += s * u[j];
+                }
+                dbeta[th] = db;
+                for (int c = 0; c < dk; ++c) {
+                    double s = 0.0, r = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        s += dS[(size_t)c * dv + j] * u[j];
+                        r += Sbar[(size_t)c * dv + j] * du[j];
+                    }
+                    dk_out[th * dk + c] = bt * s - r;   /* write term, then u = v - Sbar^T k */
+                }
+                for (int j = 0; j < dv; ++j) dv_out[th * dv + j] = du[j];
+                /* dSbar = dS - k du^T, then Sbar = Diag(alpha) Sp */
+                for (int c = 0; c < dk; ++c) {
+                    const double a = exp((double)gt[c]);
+                    double da = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        const double dsb = dS[(size_t)c * dv + j] - (double)kt[c] * du[j];
+                        da += dsb * Sp[(size_t)c * dv + j];
+                        dS[(size_t)c * dv + j] = a * dsb;
+                    }
+                    dg[th * dk + c] = a * da;
+                }
+            }
+            if (dinit) memcpy(dinit + sidx, dS, sizeof(double) * SS);
+        }
+        free(S); free(dS); free(Sbar); free(u); free(o); free(du);
+    }
+    return failed ? 2 : 0;
+}

@@ -18,6 +18,11 @@ Two independent implementations live here:
 * ``numpy_prefill``: a numpy fp64 token loop written in the page's grouping
   (apply ``I - beta k k^T`` to the decayed state, then add ``beta k v^T``).
 
+``backward`` gives fp64 gradients through the recurrence (pinned in
+``tests/test_oracle_backward.py`` against torch fp64 autograd of a token loop
+written from the page's product form, central finite differences, and closed
+forms).
+
 Parity status: pinned by the tests in ``tests/test_oracle.py`` (hand-worked
 example, the page's product form with explicit matrices, beta = 0 and
 alpha = 1 closed forms, continuation, varlen, linearity, contraction, and the
@@ -63,6 +68,9 @@ def _load():
         lib.kda_oracle_prefill.restype = ctypes.c_int
         lib.kda_oracle_decode_step.argtypes = [fp, fp, fp, fp, fp, dp, i32, i32, i32, i32, dp, i32]
         lib.kda_oracle_decode_step.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [fp, fp, fp, fp, fp, dp, ip, i32, i32, i32, i32, dp, dp,
+                                            dp, dp, dp, dp, dp, dp, i32]
+        lib.kda_oracle_backward.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -133,6 +141,38 @@ def decode_step(q, k, v, g, beta, state, num_threads: int = 0):
     if rc != 0:
         raise ValueError("kda_oracle_decode_step failed with code %d" % rc)
     return out, S
+
+
+def backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None, num_threads: int = 0):
+    """fp64 gradients of a scalar loss through the recurrence (C implementation):
+    given dL/d(out) ``dout`` [T, H, dv] and dL/d(final_state) ``dfinal``
+    [N, H, dk, dv] (None = zero), returns a dict with dq, dk, dv, dg [T, H, *],
+    dbeta [T, H] and dinit [N, H, dk, dv], all fp64.  Keeps every state of a
+    sequence in memory: test-sized inputs."""
+    lib = _load()
+    q, k, v, g, beta = (_f32(x) for x in (q, k, v, g, beta))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int32)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    init = None if initial_state is None else _f64(initial_state)
+    dout = _f64(dout)
+    assert dout.shape == (T, H, dv)
+    dfin = None if dfinal is None else _f64(dfinal)
+    if dfin is not None:
+        assert dfin.shape == (N, H, dk, dv)
+    res = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+           "dg": np.zeros((T, H, dk)), "dbeta": np.zeros((T, H)), "dinit": np.zeros((N, H, dk, dv))}
+    d = lambda key: _ptr(res[key], ctypes.c_double)
+    rc = lib.kda_oracle_backward(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(g, ctypes.c_float), _ptr(beta, ctypes.c_float),
+        None if init is None else _ptr(init, ctypes.c_double), _ptr(cu, ctypes.c_int32),
+        N, H, dk, dv, _ptr(dout, ctypes.c_double), None if dfin is None else _ptr(dfin, ctypes.c_double),
+        d("dq"), d("dk"), d("dv"), d("dg"), d("dbeta"), d("dinit"), int(num_threads))
+    if rc != 0:
+        raise ValueError("kda_oracle_backward failed with code %d" % rc)
+    return res
 
 
 def numpy_prefill(q, k, v, g, beta, initial_state, cu_seqlens):
