@@ -14,7 +14,7 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          const float *beta, const float *init, const int32_t *cu,
                                          int32_t N, int32_t T_tot, int32_t H, int32_t dv,
                                          void *out, float *fin, float *snap, int32_t snap_every,
-                                         int32_t max_snaps, hipStream_t stream);
+                                         int32_t max_snaps, const int32_t *snap_chunk_off, hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, hipStream_t stream);
@@ -28,6 +28,14 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        float *seg_out, const int32_t *chunk_off, const void *img,
                                        hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
+extern "C" size_t kda_backward_scratch_floats_per_unit();
+extern "C" int32_t kda_backward_num_blocks();
+extern "C" hipError_t kda_launch_backward(int bf16, const void *q, const void *k, const void *v, const float *g,
+                                          const float *beta, const float *init, const int32_t *cu,
+                                          const int32_t *chunk_off, const float *snaps, const void *dout,
+                                          const float *dfinal, int32_t N, int32_t T_tot, int32_t H, float *scratch,
+                                          float *part_vec, float *part_beta, float *dq, float *dk, float *dv,
+                                          float *dg, float *dbeta, float *dinit, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const void *k, const void *v,
                                                const float *g, const float *beta, const int32_t *cu,
                                                const int32_t *num_tokens, const float *state_in,
@@ -115,7 +123,7 @@ static kda_status prefill_impl(const void *q, const void *k, const void *v, cons
     }
     hipError_t e = kda_launch_prefill(bf16 ? 1 : 0, chunk, dv_block, q, k, v, g, beta, initial_state,
                                       cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                                      final_state, snap, snap_every, max_snaps,
+                                      final_state, snap, snap_every, max_snaps, nullptr,
                                       reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
@@ -292,6 +300,88 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
     hipError_t e = kda_launch_decode_tokens(dtype == KDA_BF16 ? 1 : 0, q, k, v, g, beta, cu_seqlens, num_tokens,
                                            state_in, state_out, num_seqs, total_tokens, num_heads, out,
                                            reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------- backward
+namespace {
+
+struct BwdLayout {
+    size_t plan, seq_seg, chunk_off, snaps, scratch, part_vec, part_beta, total;
+    int32_t max_chunks;
+};
+
+bool bwd_layout(int32_t N, int32_t T, int32_t H, BwdLayout *lay)
+{
+    const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
+    if (chunks > INT32_MAX / 4 || (int64_t)N + 1 > INT32_MAX / 4) return false;
+    const size_t S = (size_t)kHeadDim * kHeadDim;
+    const size_t rows = (size_t)T * H;
+    const size_t nblk = (size_t)kda_backward_num_blocks();
+    lay->max_chunks = (int32_t)chunks;
+    lay->plan = 0;
+    lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * ((size_t)N + 1));
+    lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->snaps = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
+    lay->scratch = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
+    lay->part_vec = align256(lay->scratch + sizeof(float) * (size_t)N * H * kda_backward_scratch_floats_per_unit());
+    lay->part_beta = align256(lay->part_vec + sizeof(float) * nblk * 3 * rows * kHeadDim);
+    lay->total = align256(lay->part_beta + sizeof(float) * nblk * rows);
+    return true;
+}
+
+}  // namespace
+
+size_t kda_backward_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv)
+{
+    if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || dk != kHeadDim || dv != kHeadDim) return 0;
+    BwdLayout lay;
+    if (!bwd_layout(num_seqs, total_tokens, num_heads, &lay)) return 0;
+    return lay.total;
+}
+
+kda_status kda_backward(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                        const float *initial_state, const int32_t *cu_seqlens, int32_t num_seqs,
+                        int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv, kda_dtype dtype,
+                        const void *dout, const float *dfinal, float *dq, float *dk_out, float *dv_out,
+                        float *dg, float *dbeta, float *dinit, void *workspace, size_t workspace_bytes,
+                        kda_stream_t stream)
+{
+    kda_status st = check_common(q, k, v, g, beta, dout, dk, dv, dtype);
+    if (st == KDA_ERR_INVALID_ARG) return st;
+    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return KDA_ERR_INVALID_ARG;
+    if (!dq || !dk_out || !dv_out || !dg || !dbeta) return KDA_ERR_INVALID_ARG;
+    if (!aligned(dq, 16) || !aligned(dk_out, 16) || !aligned(dv_out, 16) || !aligned(dg, 16) ||
+        !aligned(dbeta, 4) || (dfinal && !aligned(dfinal, 16)) || (dinit && !aligned(dinit, 16)) ||
+        (initial_state && !aligned(initial_state, 16)))
+        return KDA_ERR_INVALID_ARG;
+    if (st != KDA_OK) return st;
+    BwdLayout lay;
+    if (!bwd_layout(num_seqs, total_tokens, num_heads, &lay)) return KDA_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
+    const int64_t units = (int64_t)num_seqs * num_heads;
+    if (units == 0) return KDA_OK;
+    if (units * kda_backward_num_blocks() > INT32_MAX || (int64_t)lay.max_chunks * num_heads > INT32_MAX)
+        return KDA_ERR_INVALID_ARG;
+    const int bf16 = dtype == KDA_BF16 ? 1 : 0;
+    char *ws = static_cast<char *>(workspace);
+    int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
+    int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
+    int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + lay.chunk_off);
+    float *snaps = reinterpret_cast<float *>(ws + lay.snaps);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // chunk numbering (one segment per sequence: only chunk_off is used)
+    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, 1 << 30, num_seqs + 1, plan, seq_seg,
+                                      kCpChunk, lay.max_chunks, chunk_off, s);
+    if (e == hipSuccess)   // forward: the state at every chunk start
+        e = kda_launch_prefill(bf16, kCpChunk, 64, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs,
+                               total_tokens, num_heads, dv, nullptr, nullptr, snaps, kCpChunk, 0, chunk_off, s);
+    if (e == hipSuccess)
+        e = kda_launch_backward(bf16, q, k, v, g, beta, initial_state, cu_seqlens, chunk_off, snaps, dout, dfinal,
+                                num_seqs, total_tokens, num_heads, reinterpret_cast<float *>(ws + lay.scratch),
+                                reinterpret_cast<float *>(ws + lay.part_vec),
+                                reinterpret_cast<float *>(ws + lay.part_beta), dq, dk_out, dv_out, dg, dbeta, dinit,
+                                s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

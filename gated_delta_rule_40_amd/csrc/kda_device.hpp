@@ -222,6 +222,24 @@ __device__ __forceinline__ float rowmax16(float m) {
 }
 // Maximum over the whole wave.
 __device__ __forceinline__ float wavemax(float m) { return colmax(rowmax16(m)); }
+// Sum over each aligned group of 8 lanes, in every lane of the group
+// (row_half_mirror = 0x141 pairs lane l with 7 - l).
+__device__ __forceinline__ float sum8(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    return x + dpp_mov<0x141>(x);
+}
+// Sum over the whole wave, in every lane.
+__device__ __forceinline__ float wavesum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x128>(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ float absmax4(const f32x4 &x) {
     return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
 }

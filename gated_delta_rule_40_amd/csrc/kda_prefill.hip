@@ -858,7 +858,7 @@ void kda_prefill_kernel(
         __syncthreads();
 
         // ---- 5. output tile -> global (valid tokens only)
-        for (int e = tid; e < (summary ? 0 : C * VPR); e += NT) {
+        for (int e = tid; e < (summary || !out ? 0 : C * VPR); e += NT) {   // out: NULL only when snapshotting
             const int r = e / VPR, cv = (e % VPR) * VEC;
             if (r < L)
                 *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + cv) =
@@ -866,10 +866,14 @@ void kda_prefill_kernel(
         }
         // ---- state snapshot when this chunk ends (snap_every)-aligned tokens
         //      into the sequence (prefix caching)
-        if (MODE == MODE_SNAP && L == C && ((ci + 1) * C) % seg.snap_every == 0) {
-            const int j = (ci + 1) * C / seg.snap_every - 1;
-            if (j < seg.max_snaps) {
-                float *dst = seg.snap + (((int64_t)n * seg.max_snaps + j) * num_heads + h) * DK * dv;
+        //      Packed form (chunk_off given): the state at the start of every
+        //      chunk but a sequence's first, at its global chunk index.
+        if (MODE == MODE_SNAP && L == C &&
+            (seg.chunk_off ? ci + 1 < nch : ((ci + 1) * C) % seg.snap_every == 0)) {
+            const int j = seg.chunk_off ? seg.chunk_off[n] + ci + 1 : (ci + 1) * C / seg.snap_every - 1;
+            if (seg.chunk_off || j < seg.max_snaps) {
+                float *dst = seg.snap + ((seg.chunk_off ? (int64_t)j : (int64_t)n * seg.max_snaps + j) * num_heads + h) *
+                                            DK * dv;
 #pragma unroll
                 for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -1290,10 +1294,10 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          const float *g, const float *beta, const float *init,
                                          const int32_t *cu, int32_t N, int32_t T_tot, int32_t H,
                                          int32_t dv, void *out, float *fin, float *snap, int32_t snap_every,
-                                         int32_t max_snaps, hipStream_t stream)
+                                         int32_t max_snaps, const int32_t *snap_chunk_off, hipStream_t stream)
 {
     using namespace kda;
-    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, nullptr, nullptr, snap, snap_every, max_snaps};
+    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, snap_chunk_off, nullptr, snap, snap_every, max_snaps};
     if (snap) {   // snapshots: 32-token chunks, 64-column value blocks
         if (chunk != 32 || dv_block != 64) return hipErrorInvalidValue;
         if (bf16) return launch_prefill_t<bf16_t, 32, 4, MODE_SNAP>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);

@@ -12,6 +12,7 @@ fallback: if the library is missing the calls raise.
     kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len)
     kda_decode_step(q, k, v, g, beta, state_inout, out)
     kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, num_tokens=None)
+    kda_backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None, ...) -> gradients
 """
 from __future__ import annotations
 
@@ -28,8 +29,8 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
 KDA_F32, KDA_BF16 = 0, 1
 
 EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_prefill_snapshots", "kda_prefill_cp",
-           "kda_prefill_cp_workspace_size", "kda_decode_step", "kda_decode_tokens", "kda_status_string",
-           "kda_version")
+           "kda_prefill_cp_workspace_size", "kda_decode_step", "kda_decode_tokens", "kda_backward",
+           "kda_backward_workspace_size", "kda_status_string", "kda_version")
 
 _lib = None
 
@@ -68,6 +69,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_tokens.argtypes = [vp, vp, vp, fp, fp, ip, ip, fp, fp, i32, i32, i32, i32, i32, ctypes.c_int,
                                       vp, vp]
     lib.kda_decode_tokens.restype = ctypes.c_int
+    lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
+                                 fp, fp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    lib.kda_backward.restype = ctypes.c_int
+    lib.kda_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.kda_backward_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -232,3 +238,34 @@ def kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, ou
     _check(lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                                  _ptr(num_tokens), _ptr(state_in), _ptr(state_out), N, T, H, dk, dv,
                                  _dtype_code(q), _ptr(out), _stream(stream)))
+
+
+def kda_backward_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int) -> int:
+    return int(load().kda_backward_workspace_size(num_seqs, total_tokens, num_heads, dk, dv))
+
+
+def kda_backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None, grads=None, want_dinit=True,
+                 workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of a scalar loss given dout = dL/d(out) [T, H, dv] (q's dtype)
+    and dfinal = dL/d(final_state) [N, H, dk, dv] fp32 or None.  Returns a dict
+    of fp32 tensors dq, dk, dv, dg [T, H, *], dbeta [T, H] and dinit
+    [N, H, dk, dv] (None unless want_dinit); ``grads`` may supply them."""
+    N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, dout, None)
+    if dfinal is not None:
+        _require(dfinal.dtype == torch.float32 and dfinal.is_contiguous() and tuple(dfinal.shape) == (N, H, dk, dv),
+                 "dfinal must be contiguous float32 [N, H, dk, dv]")
+    dev = q.device
+    if grads is None:
+        f = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)
+        grads = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
+                 "dinit": f(N, H, dk, dv) if want_dinit else None}
+    need = kda_backward_workspace_size(N, T, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    lib = load()
+    _check(lib.kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),
+                            N, T, H, dk, dv, _dtype_code(q), _ptr(dout), _ptr(dfinal), _ptr(grads["dq"]),
+                            _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbeta"]),
+                            _ptr(grads.get("dinit")), _ptr(workspace), nbytes, _stream(stream)))
+    return grads

@@ -212,6 +212,40 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              int32_t dk, int32_t dv, kda_dtype dtype,
                              void *out, kda_stream_t stream);
 
+/*
+ * kda_backward -- gradients for training: given dL/d(out) and dL/d(final
+ * state) of a scalar loss L, the gradients with respect to q, k, v, g, beta
+ * and the initial state, by the chain rule through the recurrence of card
+ * "KDA 单头递归" (page ailearn.mscapital.top/kimi-k3.html) in reverse token order.
+ *
+ *   q, k, v, g, beta, initial_state, cu_seqlens, dtype: as kda_prefill
+ *   dout          [total_tokens, num_heads, dv]   dtype
+ *   dfinal        [num_seqs, num_heads, dk, dv]   fp32, or NULL (zero)
+ *   dq, dk, dg    [total_tokens, num_heads, dk]   fp32, written
+ *   dv            [total_tokens, num_heads, dv]   fp32, written
+ *   dbeta         [total_tokens, num_heads]       fp32, written
+ *   dinit         [num_seqs, num_heads, dk, dv]   fp32, or NULL (not written)
+ *   workspace     device memory of at least kda_backward_workspace_size(...)
+ *                 bytes, 256-byte aligned, owned by the caller (the forward
+ *                 states at every 32-token chunk start, per-workgroup scratch
+ *                 and partial sums); calls sharing it must not overlap
+ * Rows of tokens owned by a sequence are written; others are left untouched.
+ * Gradients are fp32 whatever the input dtype.  Deterministic (fixed
+ * summation order).
+ */
+size_t kda_backward_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                   int32_t dk, int32_t dv);
+
+kda_status kda_backward(const void *q, const void *k, const void *v,
+                        const float *g, const float *beta,
+                        const float *initial_state, const int32_t *cu_seqlens,
+                        int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                        int32_t dk, int32_t dv, kda_dtype dtype,
+                        const void *dout, const float *dfinal,
+                        float *dq, float *dk_out, float *dv_out, float *dg, float *dbeta,
+                        float *dinit, void *workspace, size_t workspace_bytes,
+                        kda_stream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *kda_status_string(kda_status status);
 

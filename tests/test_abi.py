@@ -218,3 +218,41 @@ def test_prefill_snapshots_rejects(lib, kw, code):
 
 def test_prefill_snapshots_empty_batch_is_a_no_op(lib):
     assert prefill_snap(lib, N=0, T=0) == K.KDA_OK
+
+
+def backward(lib, **kw):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, init=NULL, cu=P, N=1, T=64, H=1, dk=128, dv=128, dtype=K.KDA_BF16,
+             dout=P, dfin=NULL, dq=P, dk_=P, dv_=P, dg=P, db=P, dinit=NULL, ws=ctypes.c_void_p(0x100000),
+             wsb=1 << 40)
+    a.update(kw)
+    return lib.kda_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["init"], a["cu"], a["N"], a["T"], a["H"],
+                            a["dk"], a["dv"], a["dtype"], a["dout"], a["dfin"], a["dq"], a["dk_"], a["dv_"], a["dg"],
+                            a["db"], a["dinit"], a["ws"], a["wsb"], None)
+
+
+def test_backward_workspace_size(lib):
+    ws = lib.kda_backward_workspace_size
+    small = ws(1, 4096, 2, 128, 128)
+    # at least the chunk-start states: (4096 / 32 + 2) chunks x 2 heads x 64 KiB
+    assert small >= 130 * 2 * 65536
+    assert ws(1, 8192, 2, 128, 128) > small and ws(2, 4096, 2, 128, 128) > small
+    assert ws(1, 4096, 2, 64, 128) == 0 and ws(-1, 4096, 2, 128, 128) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dout=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(dq=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(db=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(dg=ctypes.c_void_p(0x10004)), K.KDA_ERR_INVALID_ARG),
+    (dict(dinit=ctypes.c_void_p(0x10008)), K.KDA_ERR_INVALID_ARG),
+    (dict(ws=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(wsb=4096), K.KDA_ERR_INVALID_ARG),
+    (dict(cu=NULL), K.KDA_ERR_INVALID_ARG),
+    (dict(dk=64), K.KDA_ERR_UNSUPPORTED),
+])
+def test_backward_rejects(lib, kw, code):
+    assert backward(lib, **kw) == code
+
+
+def test_backward_empty_batch_is_a_no_op(lib):
+    assert backward(lib, N=0, T=0) == K.KDA_OK

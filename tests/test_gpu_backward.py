@@ -1,0 +1,81 @@
+"""GPU parity of kda_backward (gradients through the recurrence) against the
+fp64 oracle backward (itself pinned by torch autograd of the page's product
+form, finite differences and a closed form in tests/test_oracle_backward.py),
+through the C ABI.  Loss L = <dout, out> + <dfinal, final_state>; every
+gradient is compared with the rule of tests/kda_parity.py (tol * RMS of that
+gradient + half an fp32 ulp)."""
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_40_amd import inputs as I
+from gated_delta_rule_40_amd import libkda as K
+from kda_parity import TOL, assert_close, host, log
+from oracle import kda_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    K.load()
+
+
+def _case(lengths, H, dtype, seed, g_lo=-5 / 16, init="normal", with_dfinal=True):
+    inp = I.random_prefill(lengths, H=H, dtype=dtype, seed=seed, device="cuda", init=init, g_lo=g_lo)
+    gen = torch.Generator(device="cuda").manual_seed(seed + 1)
+    T, N = sum(lengths), len(lengths)
+    inp["dout"] = torch.randn(T, H, 128, generator=gen, device="cuda").to(dtype)
+    inp["dfinal"] = torch.randn(N, H, 128, 128, generator=gen, device="cuda") * 0.1 if with_dfinal else None
+    return inp
+
+
+def _check(inp, dtype, label):
+    log("[backward] %s T=%d H=%d N=%d dtype=%s" % (label, inp["q"].shape[0], inp["q"].shape[1],
+                                                 inp["cu_seqlens"].shape[0] - 1, dtype))
+    gr = K.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                        inp["cu_seqlens"], inp["dout"], inp["dfinal"])
+    torch.cuda.synchronize()
+    init = inp["initial_state"]
+    ref = O.backward(host(inp["q"]), host(inp["k"]), host(inp["v"]), host(inp["g"]), host(inp["beta"]),
+                     None if init is None else init.double().cpu().numpy(), inp["cu_seqlens"].cpu().numpy(),
+                     inp["dout"].double().cpu().numpy(),
+                     None if inp["dfinal"] is None else inp["dfinal"].double().cpu().numpy())
+    cu = inp["cu_seqlens"].cpu().numpy()
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(cu) - 1)]).astype(np.int64)
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert_close(host(gr[key])[rows], ref[key][rows], TOL[dtype], "%s %s" % (label, key))
+    assert_close(host(gr["dinit"]), ref["dinit"], TOL[dtype], "%s dinit" % label)
+    return gr
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_ragged_vs_oracle(dtype):
+    _check(_case([1, 17, 64, 0, 100, 63, 33], H=2, dtype=dtype, seed=60), dtype, "ragged")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_page_gate_range(dtype):
+    _check(_case([96, 41], H=2, dtype=dtype, seed=61, g_lo=-5.0), dtype, "g_in_(-5,0)")
+
+
+def test_backward_null_initial_state_and_dfinal():
+    _check(_case([70, 128], H=3, dtype=torch.bfloat16, seed=62, init="zero", with_dfinal=False),
+           torch.bfloat16, "zero_init_no_dfinal")
+
+
+def test_backward_t512_h4():
+    _check(_case([512], H=4, dtype=torch.bfloat16, seed=63), torch.bfloat16, "t512_h4")
+
+
+def test_backward_bitwise_deterministic():
+    inp = _case([200, 77], H=2, dtype=torch.bfloat16, seed=64)
+    a = K.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                       inp["cu_seqlens"], inp["dout"], inp["dfinal"])
+    b = K.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                       inp["cu_seqlens"], inp["dout"], inp["dfinal"])
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
