@@ -262,6 +262,30 @@ def main():
     rep_bytes = Nd * Hd * (2 * DK * DV * 4 + RT * (DECODE_BYTES_PER_UNIT - 2 * DK * DV * 4))
     rep_gbs = rep_bytes / (rep_ms * 1e-3) / 1e9
 
+    # backward (training) on the 4,096-token, 8-head workload: its own
+    # measurement, outside the timed steps
+    wl_b = I.WORKLOADS["prefill_t4096_h8"]
+    bwd = I.make_prefill(wl_b, device=dev)
+    Tb, Hb = bwd["q"].shape[0], bwd["q"].shape[1]
+    gen = torch.Generator(device=dev).manual_seed(7)
+    b_dout = torch.randn(Tb, Hb, DV, generator=gen, device=dev).to(torch.bfloat16)
+    b_ws = torch.empty(K.kda_backward_workspace_size(1, Tb, Hb, DK, DV), dtype=torch.uint8, device=dev)
+    b_grads = None
+
+    def backward():
+        return K.kda_backward(bwd["q"], bwd["k"], bwd["v"], bwd["g"], bwd["beta"], bwd["initial_state"],
+                              bwd["cu_seqlens"], b_dout, None, grads=b_grads, workspace=b_ws)
+
+    b_grads = backward()
+    torch.cuda.synchronize()
+    b_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    b_ev[0].record(stream)
+    for _ in range(3):
+        backward()
+    b_ev[1].record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = b_ev[0].elapsed_time(b_ev[1]) / 3
+
     result = {
         "metric": METRIC,
         "value": T / (pre_avg * 1e-3),
@@ -299,6 +323,9 @@ def main():
                           "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": rep_gbs / HBM_PEAK_GBS, "kernel": "kda_decode_tokens_kernel<bf16>",
                                        "algorithmic_bytes_per_launch": rep_bytes}},
+        "backward": {"workload": "prefill_t4096_h8", "ms_per_call": bwd_ms, "tokens_per_s": Tb / (bwd_ms * 1e-3),
+                     "head_tokens_per_s": Tb * Hb / (bwd_ms * 1e-3),
+                     "kernels": "forward with chunk-start states, kda_backward_kernel<bf16>, kda_backward_reduce_kernel"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
