@@ -240,6 +240,11 @@ __device__ __forceinline__ float wavesum(float x) {
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// m folded with |x| elementwise, as two three-input maxima (v_max3 with |.|).
+__device__ __forceinline__ float absmax_acc(float m, const f32x4 &x) {
+    m = fmaxf(fmaxf(m, fabsf(x[0])), fabsf(x[1]));
+    return fmaxf(fmaxf(m, fabsf(x[2])), fabsf(x[3]));
+}
 __device__ __forceinline__ float absmax4(const f32x4 &x) {
     return fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
 }

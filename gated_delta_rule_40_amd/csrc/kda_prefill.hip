@@ -324,17 +324,27 @@ __device__ __forceinline__ void prep_slow(
     }
 }
 
+// Largest per-column state scale (2^64; see chain_chunk).
+constexpr float kScaleCap = 18446744073709551616.f;
+
 // State-dependent part of one chunk for the 16 value columns of this wave:
 //     X = Diag(b) (V - K+ S0),  W = (I + N)^-1 X,  O = Q+ S0 + P W,
 //     S = Diag(e^Gamma_C) S0 + K^T W,
 // reading the chunk operands from LDS (sNKp = -GS K+, sQp = GS Q+,
 // sKhT = GS K^ transposed, sT = (I + N)^-1 blocks with scales sTs, sP, the
 // chunk decay sGam and sBeta), V from sV[r * ldv + vc] and writing O to
-// sO[r * ldo + oc] unless `summary`.  S (this wave's 128 x 16 slice, MFMA
-// accumulator layout) is updated in place.
+// sO[r * ldo + oc] unless SUMMARY.
+//
+// S (this wave's 128 x 16 slice, MFMA accumulator layout) holds the state
+// scaled per column, S~ = S * sS, with sS an exact power of two per lane's
+// column (always 1 for fp32 operands).  S~ then feeds the fp16 MFMA operand
+// with no per-chunk multiply, and the update runs as the MFMA accumulator:
+// W is rounded as W sS / GS, so (GS K^)^T (W sS / GS) = K^T W sS lands in the
+// same scaled units.  sS changes (by exact powers of two) only when a column
+// leaves [2^-8, 2^15), or when W sS / GS would leave the fp16 range.
 template <typename TIn, int C, int ldv, int ldo, bool SUMMARY>
 __device__ __forceinline__ void chain_chunk(
-    f32x4 (&S)[DK / 16], const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
+    f32x4 (&S)[DK / 16], float &sS, const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
     const typename PrefillCfg<TIn, C, 4>::OpT *sQp, const typename PrefillCfg<TIn, C, 4>::OpT *sKhT,
     const typename PrefillCfg<TIn, C, 4>::OpT *sT, const typename PrefillCfg<TIn, C, 4>::OpT *sP,
     const float *sTs, const float *sGam, const float *sBeta, const TIn *sV, int vc, TIn *sO, int oc,
@@ -346,89 +356,108 @@ __device__ __forceinline__ void chain_chunk(
     constexpr bool kIn16 = P::kIn16;
     constexpr int NSUB = P::NSUB, KB = P::KB, LDK = P::LDK, LDC = P::LDC;
     constexpr float GS = P::GS;
-                // state operand, scaled per column into fp16 range
-        float sS = 1.f;
-        if (kIn16) {
-            float m = 0.f;
-#pragma unroll
-            for (int r = 0; r < DK / 16; ++r) m = fmaxf(m, absmax4(S[r]));
-            sS = pow2_scale(colmax(m));
-        }
-        const float isS = pow2_inv(sS) * (1.f / GS);   // also undoes the GS on K+ / Q+
-        typename M::frag Sf[DK / KB];
-#pragma unroll
-        for (int kb = 0; kb < DK / KB; ++kb) Sf[kb] = M::from_acc(&S[kb * (KB / 16)], sS);
 
-        // X = Diag(beta) (V - K+ S0)       (rows of sNKp hold -GS K+)
-        f32x4 X[NSUB];
-        float xmax = 0.f;
+    const float isS = pow2_inv(sS) * (1.f / GS);   // undoes the state scale and the GS on K+ / Q+
+    typename M::frag Sf[DK / KB];
 #pragma unroll
-        for (int mt = 0; mt < NSUB; ++mt) {
-            f32x4 t = zero4();
-            const OpT *rowA = sNKp + (mt * SUB + lm) * LDK;
-#pragma unroll
-            for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load_p(rowA, kb * KB, lj), Sf[kb], t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = mt * SUB + 4 * lj + i;
-                X[mt][i] = sBeta[r] * (to_f(sV[r * ldv + vc]) + t[i] * isS);
-            }
-            xmax = fmaxf(xmax, absmax4(X[mt]));
-        }
-        // W = (I + N)^-1 X, block lower triangular, per-block scales
-        float sX = 1.f;
-        if (kIn16) sX = pow2_scale(colmax(xmax));
-        const float isX = pow2_inv(sX);
-        typename M::frag16 X16[NSUB];
-#pragma unroll
-        for (int b = 0; b < NSUB; ++b) X16[b] = M::from_acc16(X[b], sX);
-        f32x4 W[NSUB];
-        float wmax = 0.f;
-#pragma unroll
-        for (int a = 0; a < NSUB; ++a) {
-            f32x4 w = zero4();
-            const OpT *rowT = sT + (a * SUB + lm) * LDC;
-#pragma unroll
-            for (int b = 0; b <= a; ++b) {
-                const f32x4 t = M::mma16(M::load16(rowT, b * SUB, lj), X16[b], zero4());
-                w += t * (sTs[a * NSUB + b] * isX);
-            }
-            W[a] = w;
-            wmax = fmaxf(wmax, absmax4(w));
-        }
-        float sW = 1.f;
-        if (kIn16) sW = pow2_scale(colmax(wmax));
-        const float isW = pow2_inv(sW);
-        typename M::frag Wf[C / KB];
-#pragma unroll
-        for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sW);
+    for (int kb = 0; kb < DK / KB; ++kb) Sf[kb] = M::from_acc(&S[kb * (KB / 16)]);
 
-        // O = Q+ S0 + P W       (rows of sQp hold GS Q+); not needed for a summary
+    // X = Diag(beta) (V - K+ S0)       (rows of sNKp hold -GS K+)
+    f32x4 X[NSUB];
+    float xmax = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < (SUMMARY ? 0 : NSUB); ++mt) {
-            f32x4 o1 = zero4(), o2 = zero4();
-            const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
+    for (int mt = 0; mt < NSUB; ++mt) {
+        f32x4 t = zero4();
+        const OpT *rowA = sNKp + (mt * SUB + lm) * LDK;
 #pragma unroll
-            for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load_p(rowQ, kb * KB, lj), Sf[kb], o1);
-            const OpT *rowP = sP + (mt * SUB + lm) * LDC;
+        for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load_p(rowA, kb * KB, lj), Sf[kb], t);
 #pragma unroll
-            for (int kb = 0; kb < C / KB; ++kb)
-                if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load_p(rowP, kb * KB, lj), Wf[kb], o2);
-            const f32x4 o = o1 * isS + o2 * isW;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc] = from_f<TIn>(o[i]);
+        for (int i = 0; i < 4; ++i) {
+            const int r = mt * SUB + 4 * lj + i;
+            X[mt][i] = sBeta[r] * (to_f(sV[r * ldv + vc]) + t[i] * isS);
         }
-        // S = Diag(gamma) S0 + K^T W       (rows of sKhT hold GS K^ per channel)
-        const float isWk = isW * (1.f / GS);
+        xmax = absmax_acc(xmax, X[mt]);
+    }
+    // W = (I + N)^-1 X, block lower triangular, per-block scales
+    float sX = 1.f;
+    if (kIn16) sX = pow2_scale(colmax(xmax));
+    const float isX = pow2_inv(sX);
+    typename M::frag16 X16[NSUB];
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r) {
-            f32x4 t = zero4();
-            const OpT *rowK = sKhT + (16 * r + lm) * LDC;
+    for (int b = 0; b < NSUB; ++b) X16[b] = M::from_acc16(X[b], sX);
+    f32x4 W[NSUB];
+    float wmax = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load_p(rowK, kb * KB, lj), Wf[kb], t);
+    for (int a = 0; a < NSUB; ++a) {
+        f32x4 w = zero4();
+        const OpT *rowT = sT + (a * SUB + lm) * LDC;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[r][i] = S[r][i] * sGam[16 * r + 4 * lj + i] + t[i] * isWk;
+        for (int b = 0; b <= a; ++b) {
+            const f32x4 t = M::mma16(M::load16(rowT, b * SUB, lj), X16[b], zero4());
+            w += t * (sTs[a * NSUB + b] * isX);
         }
+        W[a] = w;
+        wmax = absmax_acc(wmax, w);
+    }
+    // W enters in the state's units; if W sS / GS would not fit fp16, the
+    // state scale comes down first (wave-uniform branch, rarely taken)
+    float sWt = sS * (1.f / GS);
+    if (kIn16) {
+        const float wm = colmax(wmax) * sWt;
+        const float p = wm >= 32768.f ? pow2_scale(wm) : 1.f;
+        if (__ballot(p != 1.f)) {
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) S[r] *= p;
+            sS *= p;
+            sWt *= p;
+        }
+    }
+    typename M::frag Wf[C / KB];
+#pragma unroll
+    for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sWt);
+
+    // O = Q+ S0 + P W       (rows of sQp hold GS Q+; Sf carries the entry scale)
+    const float isWt = pow2_inv(sWt);
+#pragma unroll
+    for (int mt = 0; mt < (SUMMARY ? 0 : NSUB); ++mt) {
+        f32x4 o1 = zero4(), o2 = zero4();
+        const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
+#pragma unroll
+        for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load_p(rowQ, kb * KB, lj), Sf[kb], o1);
+        const OpT *rowP = sP + (mt * SUB + lm) * LDC;
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb)
+            if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load_p(rowP, kb * KB, lj), Wf[kb], o2);
+        const f32x4 o = o1 * isS + o2 * isWt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc] = from_f<TIn>(o[i]);
+    }
+    // S~ = Diag(gamma) S~ + (GS K^)^T Wf, the decayed state as the accumulator
+    float smax = 0.f;
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r) {
+        f32x4 t = S[r] * *reinterpret_cast<const f32x4 *>(sGam + 16 * r + 4 * lj);
+        const OpT *rowK = sKhT + (16 * r + lm) * LDC;
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load_p(rowK, kb * KB, lj), Wf[kb], t);
+        S[r] = t;
+        if (kIn16) smax = absmax_acc(smax, t);
+    }
+    // keep every column inside [2^-8, 2^15) (fp16 normal range with margin);
+    // the scale never grows past 2^64: a column decaying towards zero (the
+    // transition columns of a strongly decaying segment) is then left to
+    // shrink, its values being negligible at that point
+    if (kIn16) {
+        const float m = colmax(smax);
+        float q = 1.f;
+        if (m >= 32768.f) q = pow2_scale(m);
+        else if (m > 0.f && m < 0.00390625f) q = fmaxf(1.f, fminf(pow2_scale(m), kScaleCap * pow2_inv(sS)));
+        if (__ballot(q != 1.f)) {
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) S[r] *= q;
+            sS *= q;
+        }
+    }
 }
 
 // MODE_FUSED: the whole chunk loop per (sequence, head, value block), as
@@ -577,6 +606,16 @@ void kda_prefill_kernel(
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[r][i] = (trans_cols && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
+    }
+    // the state is carried scaled per column by a power of two (see chain_chunk)
+    float sS = 1.f;
+    if (kIn16) {
+        float m = 0.f;
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, S[r]);
+        sS = fminf(pow2_scale(colmax(m)), kScaleCap);
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) S[r] *= sS;
     }
 
     // ---- raw chunk data staged in registers, loaded one chunk ahead: item it
@@ -853,7 +892,7 @@ void kda_prefill_kernel(
             continue;
         }
         // ---- 4. state-dependent chain (this wave's 16 columns)
-        chain_chunk<TIn, C, LDV, LDV, false>(S, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
+        chain_chunk<TIn, C, LDV, LDV, false>(S, sS, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
                                              16 * wave + lm, lj, lm);
         __syncthreads();
 
@@ -877,7 +916,8 @@ void kda_prefill_kernel(
 #pragma unroll
                 for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
+                    for (int i = 0; i < 4; ++i)
+                        dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i] * pow2_inv(sS);
             }
         }
     }
@@ -888,13 +928,13 @@ void kda_prefill_kernel(
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i];
+            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i] * pow2_inv(sS);
     } else if (final_state && (sflags & SEG_LAST)) {
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
+                final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i] * pow2_inv(sS);
     }
 }
 
@@ -1039,6 +1079,16 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
 #pragma unroll
             for (int i = 0; i < 4; ++i) S[r][i] = (trans_cols && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
     }
+    // the state is carried scaled per column by a power of two (see chain_chunk)
+    float sS = 1.f;
+    if (Q::P::kIn16) {
+        float m = 0.f;
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, S[r]);
+        sS = fminf(pow2_scale(colmax(m)), kScaleCap);
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) S[r] *= sS;
+    }
 
     // ---- chunk staging: image + value tile of chunk ci in registers
     f32x4 ri[Q::IITEMS], rv[Q::VITEMS];
@@ -1086,7 +1136,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         load(min(ci + 1, nch - 1));               // unconditional, see the fused kernel
         const unsigned char *base = smem + (ci & 1) * Q::BUF;
         chain_chunk<TIn, C, LDV, 16, SUMMARY>(
-            S, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
+            S, sS, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
             reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
             reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
@@ -1116,13 +1166,13 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i];
+            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i] * pow2_inv(sS);
     } else if (final_state && (sflags & SEG_LAST)) {
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
+                final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i] * pow2_inv(sS);
     }
 }
 
