@@ -163,7 +163,8 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const float 
 namespace {
 
 constexpr int32_t kCpChunk = 32;     // chunk size of the segmented runs
-constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the state-chain passes
+constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the segment-output pass
+constexpr int32_t kCpSumBlock = 256; // value + transition columns per workgroup of the summary pass
 
 struct CpLayout {
     size_t plan, seq_seg, chunk_off, seg_out, seg_init, img, total;
@@ -253,7 +254,7 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
     if (e == hipSuccess)   // segment summaries (segments with a successor)
-        e = kda_launch_chain(bf16, kCpBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
+        e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
                              plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, s);
     if (e == hipSuccess)   // entering state of every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, s);

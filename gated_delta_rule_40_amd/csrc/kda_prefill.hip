@@ -342,14 +342,16 @@ constexpr float kScaleCap = 18446744073709551616.f;
 // W is rounded as W sS / GS, so (GS K^)^T (W sS / GS) = K^T W sS lands in the
 // same scaled units.  sS changes (by exact powers of two) only when a column
 // leaves [2^-8, 2^15), or when W sS / GS would leave the fp16 range.
-template <typename TIn, int C, int ldv, int ldo, bool SUMMARY>
+template <typename TIn, int C, int ldv, int ldo, bool SUMMARY, int NCT = 1>
 __device__ __forceinline__ void chain_chunk(
-    f32x4 (&S)[DK / 16], float &sS, const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
+    f32x4 (&S)[NCT][DK / 16], float (&sS)[NCT], const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
     const typename PrefillCfg<TIn, C, 4>::OpT *sQp, const typename PrefillCfg<TIn, C, 4>::OpT *sKhT,
     const typename PrefillCfg<TIn, C, 4>::OpT *sT, const typename PrefillCfg<TIn, C, 4>::OpT *sP,
     const float *sTs, const float *sGam, const float *sBeta, const TIn *sV, int vc, TIn *sO, int oc,
     int lj, int lm)
 {
+    // NCT column tiles of 16 per wave (tile ct: value column vc + 16 ct, output column oc + 16 ct):
+    // every operand fragment read from LDS serves all of them
     typedef PrefillCfg<TIn, C, 4> P;
     typedef typename P::OpT OpT;
     typedef Mma<OpT> M;
@@ -357,105 +359,166 @@ __device__ __forceinline__ void chain_chunk(
     constexpr int NSUB = P::NSUB, KB = P::KB, LDK = P::LDK, LDC = P::LDC;
     constexpr float GS = P::GS;
 
-    const float isS = pow2_inv(sS) * (1.f / GS);   // undoes the state scale and the GS on K+ / Q+
-    typename M::frag Sf[DK / KB];
+    float isS[NCT];
+    typename M::frag Sf[NCT][DK / KB];
 #pragma unroll
-    for (int kb = 0; kb < DK / KB; ++kb) Sf[kb] = M::from_acc(&S[kb * (KB / 16)]);
+    for (int ct = 0; ct < NCT; ++ct) {
+        isS[ct] = pow2_inv(sS[ct]) * (1.f / GS);   // undoes the state scale and the GS on K+ / Q+
+#pragma unroll
+        for (int kb = 0; kb < DK / KB; ++kb) Sf[ct][kb] = M::from_acc(&S[ct][kb * (KB / 16)]);
+    }
 
     // X = Diag(beta) (V - K+ S0)       (rows of sNKp hold -GS K+)
-    f32x4 X[NSUB];
-    float xmax = 0.f;
+    f32x4 X[NCT][NSUB];
+    float xmax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) xmax[ct] = 0.f;
 #pragma unroll
     for (int mt = 0; mt < NSUB; ++mt) {
-        f32x4 t = zero4();
+        f32x4 t[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) t[ct] = zero4();
         const OpT *rowA = sNKp + (mt * SUB + lm) * LDK;
 #pragma unroll
-        for (int kb = 0; kb < DK / KB; ++kb) t = M::mma(M::load_p(rowA, kb * KB, lj), Sf[kb], t);
+        for (int kb = 0; kb < DK / KB; ++kb) {
+            const typename M::frag af = M::load_p(rowA, kb * KB, lj);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) t[ct] = M::mma(af, Sf[ct][kb], t[ct]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = mt * SUB + 4 * lj + i;
-            X[mt][i] = sBeta[r] * (to_f(sV[r * ldv + vc]) + t[i] * isS);
+            const float br = sBeta[r];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                X[ct][mt][i] = br * (to_f(sV[r * ldv + vc + 16 * ct]) + t[ct][i] * isS[ct]);
         }
-        xmax = absmax_acc(xmax, X[mt]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) xmax[ct] = absmax_acc(xmax[ct], X[ct][mt]);
     }
     // W = (I + N)^-1 X, block lower triangular, per-block scales
-    float sX = 1.f;
-    if (kIn16) sX = pow2_scale(colmax(xmax));
-    const float isX = pow2_inv(sX);
-    typename M::frag16 X16[NSUB];
+    typename M::frag16 X16[NCT][NSUB];
+    float isX[NCT];
 #pragma unroll
-    for (int b = 0; b < NSUB; ++b) X16[b] = M::from_acc16(X[b], sX);
-    f32x4 W[NSUB];
-    float wmax = 0.f;
+    for (int ct = 0; ct < NCT; ++ct) {
+        float sX = 1.f;
+        if (kIn16) sX = pow2_scale(colmax(xmax[ct]));
+        isX[ct] = pow2_inv(sX);
+#pragma unroll
+        for (int b = 0; b < NSUB; ++b) X16[ct][b] = M::from_acc16(X[ct][b], sX);
+    }
+    f32x4 W[NCT][NSUB];
+    float wmax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) wmax[ct] = 0.f;
 #pragma unroll
     for (int a = 0; a < NSUB; ++a) {
-        f32x4 w = zero4();
+        f32x4 w[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) w[ct] = zero4();
         const OpT *rowT = sT + (a * SUB + lm) * LDC;
 #pragma unroll
         for (int b = 0; b <= a; ++b) {
-            const f32x4 t = M::mma16(M::load16(rowT, b * SUB, lj), X16[b], zero4());
-            w += t * (sTs[a * NSUB + b] * isX);
+            const typename M::frag16 tf = M::load16(rowT, b * SUB, lj);
+            const float ts = sTs[a * NSUB + b];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) w[ct] += M::mma16(tf, X16[ct][b], zero4()) * (ts * isX[ct]);
         }
-        W[a] = w;
-        wmax = absmax_acc(wmax, w);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            W[ct][a] = w[ct];
+            wmax[ct] = absmax_acc(wmax[ct], w[ct]);
+        }
     }
     // W enters in the state's units; if W sS / GS would not fit fp16, the
     // state scale comes down first (wave-uniform branch, rarely taken)
-    float sWt = sS * (1.f / GS);
-    if (kIn16) {
-        const float wm = colmax(wmax) * sWt;
-        const float p = wm >= 32768.f ? pow2_scale(wm) : 1.f;
-        if (__ballot(p != 1.f)) {
+    typename M::frag Wf[NCT][C / KB];
+    float isWt[NCT];
 #pragma unroll
-            for (int r = 0; r < DK / 16; ++r) S[r] *= p;
-            sS *= p;
-            sWt *= p;
+    for (int ct = 0; ct < NCT; ++ct) {
+        float sWt = sS[ct] * (1.f / GS);
+        if (kIn16) {
+            const float wm = colmax(wmax[ct]) * sWt;
+            const float p = wm >= 32768.f ? pow2_scale(wm) : 1.f;
+            if (__ballot(p != 1.f)) {
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r) S[ct][r] *= p;
+                sS[ct] *= p;
+                sWt *= p;
+            }
         }
-    }
-    typename M::frag Wf[C / KB];
+        isWt[ct] = pow2_inv(sWt);
 #pragma unroll
-    for (int kb = 0; kb < C / KB; ++kb) Wf[kb] = M::from_acc(&W[kb * (KB / 16)], sWt);
+        for (int kb = 0; kb < C / KB; ++kb) Wf[ct][kb] = M::from_acc(&W[ct][kb * (KB / 16)], sWt);
+    }
 
     // O = Q+ S0 + P W       (rows of sQp hold GS Q+; Sf carries the entry scale)
-    const float isWt = pow2_inv(sWt);
 #pragma unroll
     for (int mt = 0; mt < (SUMMARY ? 0 : NSUB); ++mt) {
-        f32x4 o1 = zero4(), o2 = zero4();
+        f32x4 o1[NCT], o2[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) o1[ct] = o2[ct] = zero4();
         const OpT *rowQ = sQp + (mt * SUB + lm) * LDK;
 #pragma unroll
-        for (int kb = 0; kb < DK / KB; ++kb) o1 = M::mma(M::load_p(rowQ, kb * KB, lj), Sf[kb], o1);
+        for (int kb = 0; kb < DK / KB; ++kb) {
+            const typename M::frag qf = M::load_p(rowQ, kb * KB, lj);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) o1[ct] = M::mma(qf, Sf[ct][kb], o1[ct]);
+        }
         const OpT *rowP = sP + (mt * SUB + lm) * LDC;
 #pragma unroll
         for (int kb = 0; kb < C / KB; ++kb)
-            if (kb * KB <= mt * SUB + SUB - 1) o2 = M::mma(M::load_p(rowP, kb * KB, lj), Wf[kb], o2);
-        const f32x4 o = o1 * isS + o2 * isWt;
+            if (kb * KB <= mt * SUB + SUB - 1) {
+                const typename M::frag pf = M::load_p(rowP, kb * KB, lj);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc] = from_f<TIn>(o[i]);
+                for (int ct = 0; ct < NCT; ++ct) o2[ct] = M::mma(pf, Wf[ct][kb], o2[ct]);
+            }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const f32x4 o = o1[ct] * isS[ct] + o2[ct] * isWt[ct];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc + 16 * ct] = from_f<TIn>(o[i]);
+        }
     }
     // S~ = Diag(gamma) S~ + (GS K^)^T Wf, the decayed state as the accumulator
-    float smax = 0.f;
+    float smax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) smax[ct] = 0.f;
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r) {
-        f32x4 t = S[r] * *reinterpret_cast<const f32x4 *>(sGam + 16 * r + 4 * lj);
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * r + 4 * lj);
+        f32x4 t[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) t[ct] = S[ct][r] * gm;
         const OpT *rowK = sKhT + (16 * r + lm) * LDC;
 #pragma unroll
-        for (int kb = 0; kb < C / KB; ++kb) t = M::mma(M::load_p(rowK, kb * KB, lj), Wf[kb], t);
-        S[r] = t;
-        if (kIn16) smax = absmax_acc(smax, t);
+        for (int kb = 0; kb < C / KB; ++kb) {
+            const typename M::frag kf = M::load_p(rowK, kb * KB, lj);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) t[ct] = M::mma(kf, Wf[ct][kb], t[ct]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            S[ct][r] = t[ct];
+            if (kIn16) smax[ct] = absmax_acc(smax[ct], t[ct]);
+        }
     }
     // keep every column inside [2^-8, 2^15) (fp16 normal range with margin);
     // the scale never grows past 2^64: a column decaying towards zero (the
     // transition columns of a strongly decaying segment) is then left to
     // shrink, its values being negligible at that point
     if (kIn16) {
-        const float m = colmax(smax);
-        float q = 1.f;
-        if (m >= 32768.f) q = pow2_scale(m);
-        else if (m > 0.f && m < 0.00390625f) q = fmaxf(1.f, fminf(pow2_scale(m), kScaleCap * pow2_inv(sS)));
-        if (__ballot(q != 1.f)) {
 #pragma unroll
-            for (int r = 0; r < DK / 16; ++r) S[r] *= q;
-            sS *= q;
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float m = colmax(smax[ct]);
+            float q = 1.f;
+            if (m >= 32768.f) q = pow2_scale(m);
+            else if (m > 0.f && m < 0.00390625f) q = fmaxf(1.f, fminf(pow2_scale(m), kScaleCap * pow2_inv(sS[ct])));
+            if (__ballot(q != 1.f)) {
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r) S[ct][r] *= q;
+                sS[ct] *= q;
+            }
         }
     }
 }
@@ -579,7 +642,8 @@ void kda_prefill_kernel(
     const int pc = prep ? (tid % (DK / CPT)) * CPT : 0;
 
     // ---- state slice of this wave: rows 16r + 4*lj + i, column dv0 + 16*wave + lm
-    f32x4 S[DK / 16];
+    f32x4 Sarr[1][DK / 16];
+    f32x4 (&S)[DK / 16] = Sarr[0];
     const int col = dv0 + 16 * wave + lm;
     const int64_t sbase = ((int64_t)n * num_heads + h) * DK * dv;   // this (sequence, head) in init/final
     const float *S_in = nullptr;
@@ -608,7 +672,8 @@ void kda_prefill_kernel(
             for (int i = 0; i < 4; ++i) S[r][i] = (trans_cols && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
     }
     // the state is carried scaled per column by a power of two (see chain_chunk)
-    float sS = 1.f;
+    float sSarr[1] = {1.f};
+    float &sS = sSarr[0];
     if (kIn16) {
         float m = 0.f;
 #pragma unroll
@@ -669,6 +734,17 @@ void kda_prefill_kernel(
     };
     constexpr int GPS = SUB / GRP;                        // groups per sub-tile
 
+    // chunk-operand pass: LDS byte offsets of this thread's image vectors (fixed)
+    typedef ChunkImage<TIn, C> Img;
+    constexpr int SITEMS = kPrep ? (Img::NVEC + NT - 1) / NT : 1;
+    uint32_t img_off[SITEMS];
+    if constexpr (kPrep) {
+        const typename Img::Offs o = {(uint32_t)P::offNKp, (uint32_t)P::offQp, (uint32_t)P::offKhT,
+                                      (uint32_t)P::offT, (uint32_t)P::offP, (uint32_t)P::offGam,
+                                      (uint32_t)P::offBeta, (uint32_t)P::offTs};
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) img_off[it] = Img::lds_off(min(tid + it * NT, Img::NVEC - 1), o);
+    }
     for (int ci = 0; ci < nch; ++ci) {
         int c0, cend;
         chunk_range(ci, c0, cend);
@@ -727,7 +803,9 @@ void kda_prefill_kernel(
         // ---- 1c. decayed operands
         // fast: from the staged registers, chunk-start reference R_r = e^Gamma_r,
         //       written once for both the Gram and the chain
-        auto prep_fast = [&]() {
+        // FULL: every row of the chunk is a token (no masking needed)
+        auto prep_fast = [&](auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
             typedef OpT V4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int it = 0; it < ITEMS; ++it) {
@@ -742,7 +820,7 @@ void kda_prefill_kernel(
 #pragma unroll
                 for (int rr = 0; rr < SEG; ++rr) {
                     const int r = sg * SEG + rr;
-                    const bool ok = r < L;
+                    const bool ok = FULL || r < L;
                     if (rr % GRP == 0) {
                         if (rr > 0) pre = *reinterpret_cast<const f32x4 *>(sPre + (G0 + rr / GRP) * DK + c);
                         R = f32x4{1.f, 1.f, 1.f, 1.f};
@@ -779,8 +857,10 @@ void kda_prefill_kernel(
         };
         if (slow)
             prep_slow<TIn, C, NW>(true, q, k, g, c0, L, rowK, hK, tid, sF, sKr32, sQr32, sKD32, sNKp, sQp, sKhT);
+        else if (L == C)
+            prep_fast(std::true_type());
         else
-            prep_fast();
+            prep_fast(std::false_type());
         __syncthreads();
 
         // ---- 2. Gram tiles
@@ -875,24 +955,18 @@ void kda_prefill_kernel(
 
         if constexpr (kPrep) {
             // ---- chunk-operand image of (chunk, head) -> global
-            typedef ChunkImage<TIn, C> Img;
-            const typename Img::Offs o = {(uint32_t)P::offNKp, (uint32_t)P::offQp, (uint32_t)P::offKhT,
-                                          (uint32_t)P::offT, (uint32_t)P::offP, (uint32_t)P::offGam,
-                                          (uint32_t)P::offBeta, (uint32_t)P::offTs};
             f32x4 *dst = seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC;
             // all LDS reads first, then the stores; surplus items repeat the last
             // vector (same value, same place) so that every store is issued
-            constexpr int SITEMS = (Img::NVEC + NT - 1) / NT;
             f32x4 tv[SITEMS];
 #pragma unroll
-            for (int it = 0; it < SITEMS; ++it)
-                tv[it] = *reinterpret_cast<const f32x4 *>(smem + Img::lds_off(min(tid + it * NT, Img::NVEC - 1), o));
+            for (int it = 0; it < SITEMS; ++it) tv[it] = *reinterpret_cast<const f32x4 *>(smem + img_off[it]);
 #pragma unroll
             for (int it = 0; it < SITEMS; ++it) dst[min(tid + it * NT, Img::NVEC - 1)] = tv[it];
             continue;
         }
         // ---- 4. state-dependent chain (this wave's 16 columns)
-        chain_chunk<TIn, C, LDV, LDV, false>(S, sS, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
+        chain_chunk<TIn, C, LDV, LDV, false>(Sarr, sSarr, sNKp, sQp, sKhT, sT, sP, sTs, sGam, sBeta, sV, 16 * wave + lm, sO,
                                              16 * wave + lm, lj, lm);
         __syncthreads();
 
@@ -974,13 +1048,13 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 // tile are loaded into registers, the chain runs on the current LDS buffer,
 // each wave stores its own output columns, and the registers are written to
 // the other LDS buffer.
-template <typename TIn, int C, int NW>
+template <typename TIn, int C, int NW, int NCT>
 struct ChainCfg {
     typedef PrefillCfg<TIn, C, NW> P;
     typedef typename P::OpT OpT;
     typedef ChunkImage<TIn, C> Img;
-    static constexpr int NT = 64 * NW, BV = 16 * NW, NSUB = C / SUB;
-    static constexpr int LDK = P::LDK, LDC = P::LDC, LDV = P::LDV;
+    static constexpr int NT = 64 * NW, BV = 16 * NW * NCT, NSUB = C / SUB;   // NCT 16-column tiles per wave
+    static constexpr int LDK = P::LDK, LDC = P::LDC, LDV = BV + 16 / (int)sizeof(TIn);
     static constexpr uint32_t offNKp = 0;
     static constexpr uint32_t offQp = offNKp + sizeof(OpT) * C * LDK;
     static constexpr uint32_t offKhT = offQp + sizeof(OpT) * C * LDK;
@@ -991,8 +1065,8 @@ struct ChainCfg {
     static constexpr uint32_t offTs = offBeta + sizeof(float) * C;
     static constexpr uint32_t offV = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
     static constexpr uint32_t BUF = (offV + sizeof(TIn) * C * LDV + 15) / 16 * 16;   // one chunk buffer
-    static constexpr uint32_t offO = 2 * BUF;                                        // [NW][C][16] outputs
-    static constexpr uint32_t bytes = offO + sizeof(TIn) * NW * C * 16;
+    static constexpr uint32_t offO = 2 * BUF;                                  // [NW][C][16 NCT] outputs
+    static constexpr uint32_t bytes = offO + sizeof(TIn) * NW * C * 16 * NCT;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
     static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
@@ -1000,16 +1074,16 @@ struct ChainCfg {
     static constexpr int VEC = 16 / (int)sizeof(TIn);               // elements per 16-byte vector
     static constexpr int VPR = BV / VEC;                            // vectors per value-tile row
     static constexpr int VITEMS = (C * VPR + NT - 1) / NT;
-    static constexpr int OVEC = C * 16 / VEC;                       // vectors of one wave's output tile
+    static constexpr int OVEC = C * 16 * NCT / VEC;                 // vectors of one wave's output tile
 };
 
-template <typename TIn, int C, int NW, bool SUMMARY>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW>::WAVES_PER_EU)))
+template <typename TIn, int C, int NW, int NCT, bool SUMMARY>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
                       TIn *__restrict__ out, float *final_state, SegArgs seg)
 {
-    typedef ChainCfg<TIn, C, NW> Q;
+    typedef ChainCfg<TIn, C, NW, NCT> Q;
     typedef typename Q::OpT OpT;
     typedef typename Q::Img Img;
     constexpr int NT = Q::NT, BV = Q::BV, LDV = Q::LDV, VEC = Q::VEC, VPR = Q::VPR;
@@ -1044,8 +1118,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     // cu_seqlens is not non-decreasing (result unspecified, memory safe)
     const int nch = (int)max((int64_t)0, min((int64_t)(t_end - t_start + C - 1) / C,
                                              (int64_t)seg.chunk_off[num_seqs] - gc0));
-    const int dv0 = vb * BV;
-    const bool trans_cols = summary && dv0 >= dv;
+    const int dv0 = vb * BV;                 // summary blocks may span value and transition columns
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
@@ -1053,9 +1126,12 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     const int H = num_heads;
     const int64_t rowV = (int64_t)H * dv;
 
-    // ---- entering state (as in the fused kernel)
-    f32x4 S[DK / 16];
-    const int col = dv0 + 16 * wave + lm;
+    // ---- entering state: tile ct of this wave is column dv0 + 16 (NCT wave + ct) + lm
+    f32x4 S[NCT][DK / 16];
+    float sS[NCT];
+    int colc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) colc[ct] = dv0 + 16 * (NCT * wave + ct) + lm;
     const int64_t sbase = ((int64_t)n * num_heads + h) * DK * dv;
     const float *S_in = nullptr;
     int64_t S_in_base = 0;
@@ -1068,26 +1144,30 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         S_in = initial_state;
         S_in_base = sbase;
     }
-    if (S_in) {
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = colc[ct];
+        if (S_in) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[r][i] = S_in[S_in_base + (int64_t)(16 * r + 4 * lj + i) * dv + col];
-    } else {
+            for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
+                for (int i = 0; i < 4; ++i) S[ct][r][i] = S_in[S_in_base + (int64_t)(16 * r + 4 * lj + i) * dv + col];
+        } else {   // zero; a summary's transition columns start from the identity
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[r][i] = (trans_cols && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
-    }
-    // the state is carried scaled per column by a power of two (see chain_chunk)
-    float sS = 1.f;
-    if (Q::P::kIn16) {
-        float m = 0.f;
+            for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, S[r]);
-        sS = fminf(pow2_scale(colmax(m)), kScaleCap);
+                for (int i = 0; i < 4; ++i) S[ct][r][i] = (summary && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
+        }
+        // the state is carried scaled per column by a power of two (see chain_chunk)
+        sS[ct] = 1.f;
+        if (Q::P::kIn16) {
+            float m = 0.f;
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r) S[r] *= sS;
+            for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, S[ct][r]);
+            sS[ct] = fminf(pow2_scale(colmax(m)), kScaleCap);
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) S[ct][r] *= sS[ct];
+        }
     }
 
     // ---- chunk staging: image + value tile of chunk ci in registers
@@ -1101,11 +1181,14 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         for (int it = 0; it < Q::VITEMS; ++it) {
             const int e = min(tid + it * NT, C * VPR - 1);
             const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
-            rv[it] = trans_cols ? zero4()
-                                : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
+            rv[it] = dv0 + cv >= dv ? zero4()      // transition columns: V = 0
+                                    : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
         }
     };
     const typename Img::Offs offs = {Q::offNKp, Q::offQp, Q::offKhT, Q::offT, Q::offP, Q::offGam, Q::offBeta, Q::offTs};
+    uint32_t stage_off[Q::IITEMS];                        // LDS byte offsets of this thread's image vectors
+#pragma unroll
+    for (int it = 0; it < Q::IITEMS; ++it) stage_off[it] = Img::lds_off(min(tid + it * NT, Img::NVEC - 1), offs);
     // Every staged register is written on every path (surplus items repeat
     // the last vector, same value to the same place): a conditional consumer
     // would leave the loads pending at the loop head for the compiler, which
@@ -1113,10 +1196,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     auto stage = [&](int ci, int b) {
         unsigned char *base = smem + b * Q::BUF;
 #pragma unroll
-        for (int it = 0; it < Q::IITEMS; ++it) {
-            const int e = min(tid + it * NT, Img::NVEC - 1);
-            *reinterpret_cast<f32x4 *>(base + Img::lds_off(e, offs)) = ri[it];
-        }
+        for (int it = 0; it < Q::IITEMS; ++it) *reinterpret_cast<f32x4 *>(base + stage_off[it]) = ri[it];
         TIn *sV = reinterpret_cast<TIn *>(base + Q::offV);
         const int LL = min(C, t_end - (t_start + ci * C));
 #pragma unroll
@@ -1130,17 +1210,17 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         load(0);
         stage(0, 0);
     }
-    TIn *sOw = reinterpret_cast<TIn *>(smem + Q::offO) + wave * C * 16;    // this wave's output tile
+    TIn *sOw = reinterpret_cast<TIn *>(smem + Q::offO) + wave * C * 16 * NCT;   // this wave's output tile
     for (int ci = 0; ci < nch; ++ci) {
         __syncthreads();                          // buffer ci & 1 staged; ci - 1 done with the other
         load(min(ci + 1, nch - 1));               // unconditional, see the fused kernel
         const unsigned char *base = smem + (ci & 1) * Q::BUF;
-        chain_chunk<TIn, C, LDV, 16, SUMMARY>(
+        chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT>(
             S, sS, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
             reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
             reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
-            reinterpret_cast<const TIn *>(base + Q::offV), 16 * wave + lm, sOw, lm, lj, lm);
+            reinterpret_cast<const TIn *>(base + Q::offV), 16 * NCT * wave + lm, sOw, lm, lj, lm);
         if constexpr (!SUMMARY) {
             // this wave's 16 output columns: rows of 16 * sizeof(TIn) bytes, one
             // 16-byte vector per lane and step (LDS is in order within a wave).
@@ -1149,30 +1229,35 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
             // the compiler can count the store and need not wait for it later.
             __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             const int c0 = t_start + ci * C, L = min(C, t_end - c0);
-            constexpr int VPW = 16 / VEC;                              // vectors per row of the tile
+            constexpr int VPW = 16 * NCT / VEC;                        // vectors per row of the tile
 #pragma unroll
             for (int e = lane; e < Q::OVEC; e += 64) {
                 const int r = min(e / VPW, L - 1), cv = (e % VPW) * VEC;
-                *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + 16 * wave + cv) =
-                    *reinterpret_cast<const f32x4 *>(sOw + r * 16 + cv);
+                *reinterpret_cast<f32x4 *>(out + (int64_t)(c0 + r) * rowV + (int64_t)h * dv + dv0 + 16 * NCT * wave + cv) =
+                    *reinterpret_cast<const f32x4 *>(sOw + r * 16 * NCT + cv);
             }
             __asm__ volatile("" ::: "memory");
         }
         stage(min(ci + 1, nch - 1), (ci + 1) & 1);
     }
 
-    if (summary) {
-        float *dst = seg.seg_out + ((int64_t)su * num_heads + h) * DK * (dv + DK);
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = colc[ct];
+        const float inv = pow2_inv(sS[ct]);
+        if (summary) {
+            float *dst = seg.seg_out + ((int64_t)su * num_heads + h) * DK * (dv + DK);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[r][i] * pow2_inv(sS);
-    } else if (final_state && (sflags & SEG_LAST)) {
+            for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
+                for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * (dv + DK) + col] = S[ct][r][i] * inv;
+        } else if (final_state && (sflags & SEG_LAST)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i] * pow2_inv(sS);
+            for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[ct][r][i] * inv;
+        }
     }
 }
 
@@ -1199,13 +1284,13 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
     return hipGetLastError();
 }
 
-template <typename TIn, int C, int NW>
+template <typename TIn, int C, int NW, int NCT>
 static hipError_t launch_chain_t(const void *v, const float *init, const int32_t *cu, int32_t N, int32_t T_tot,
                                  int32_t H, int32_t dv, void *out, float *fin, SegArgs seg, hipStream_t stream)
 {
-    typedef ChainCfg<TIn, C, NW> Q;
+    typedef ChainCfg<TIn, C, NW, NCT> Q;
     const bool summary = seg.mode == SEG_SUMMARY;
-    auto kern = summary ? kda_chain_kernel<TIn, C, NW, true> : kda_chain_kernel<TIn, C, NW, false>;
+    auto kern = summary ? kda_chain_kernel<TIn, C, NW, NCT, true> : kda_chain_kernel<TIn, C, NW, NCT, false>;
     static bool attr_set[2] = {false, false};   // idempotent; racing threads set the same value
     if (!attr_set[summary]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1388,8 +1473,9 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
 
-// State-chain pass over the images, value blocks of dv_block (64 or 128)
-// columns; plan, mode, seg_init and seg_out as for kda_launch_prefill.
+// State-chain pass over the images, value blocks of dv_block columns (64,
+// 128, or 256 for a summary's value + transition columns in one block);
+// plan, mode, seg_init and seg_out as for kda_launch_prefill.
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
@@ -1399,11 +1485,15 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     using namespace kda;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), nullptr, 0, 0};
-    // fp32 images are twice as large: their buffers fit the LDS at 64 columns only
-    if (dv_block == 128 && bf16) return launch_chain_t<bf16_t, 32, 8>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
-    if (dv_block != 64 && dv_block != 128) return hipErrorInvalidValue;
-    if (bf16) return launch_chain_t<bf16_t, 32, 4>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
-    return launch_chain_t<float, 32, 4>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    // bf16: 128 columns as 8 waves x 1 tile, 256 as 8 waves x 2 tiles (two
+    // tiles per wave share every operand fragment, but four waves of two
+    // tiles hide latency worse than eight of one); fp32 images are twice as
+    // large and their buffers fit the LDS at 64 columns only
+    if (bf16 && dv_block == 256) return launch_chain_t<bf16_t, 32, 8, 2>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    if (bf16 && dv_block == 128) return launch_chain_t<bf16_t, 32, 8, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    if (dv_block != 64 && dv_block != 128 && dv_block != 256) return hipErrorInvalidValue;
+    if (bf16) return launch_chain_t<bf16_t, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    return launch_chain_t<float, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
 }
 
 extern "C" size_t kda_chunk_image_bytes(int bf16)
