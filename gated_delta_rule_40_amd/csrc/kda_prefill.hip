@@ -159,11 +159,12 @@ enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2 };   // MODE_SNAP: fused + s
 constexpr int PREP_GROUP = 8;    // consecutive chunks per workgroup of the chunk-operand pass
 
 // Chunk-operand image: everything the state chain of one (chunk, head) reads
-// besides V, as computed by the chunk-operand pass -- -GS K+, GS Q+, GS K^
-// transposed, the (I + N)^-1 blocks and P in the MFMA operand type, then the
-// fp32 chunk decay, beta and T-block scales.  Packed row-major without padding
-// as 16-byte vectors; lds_off maps vector v to its place in an LDS buffer that
-// uses the padded strides of PrefillCfg.  Chunks are numbered across the
+// besides V, as computed by the chunk-operand pass -- -GS K+, GS K^
+// transposed, the (I + N)^-1 blocks, the fp32 chunk decay, beta and T-block
+// scales (what a segment summary needs: the first NVEC_SUM vectors), then
+// GS Q+ and P (for the outputs).  Packed row-major without padding as 16-byte
+// vectors; lds_off maps vector v to its place in an LDS buffer that uses the
+// padded strides of PrefillCfg.  Chunks are numbered across the
 // packed sequences: sequence n owns chunks chunk_off[n] .. chunk_off[n+1]-1,
 // and the image of (chunk c, head h) is vector block c * H + h.
 template <typename TIn, int C>
@@ -175,7 +176,8 @@ struct ChunkImage {
     static constexpr int vNKp = C * DK / EPV, vQp = C * DK / EPV, vKhT = DK * C / EPV;
     static constexpr int vT = C * C / EPV, vP = C * C / EPV;
     static constexpr int vGam = DK / 4, vBeta = C / 4, vTs = (NSUB * NSUB + 3) / 4;
-    static constexpr int NVEC = vNKp + vQp + vKhT + vT + vP + vGam + vBeta + vTs;
+    static constexpr int NVEC_SUM = vNKp + vKhT + vT + vGam + vBeta + vTs;
+    static constexpr int NVEC = NVEC_SUM + vQp + vP;
     static constexpr size_t BYTES = (size_t)NVEC * 16;
     struct Offs { uint32_t nkp, qp, kht, t, p, gam, beta, ts; };   // byte offsets of the regions
     __device__ static __forceinline__ uint32_t lds_off(int v, const Offs &o) {
@@ -183,18 +185,18 @@ struct ChunkImage {
         constexpr uint32_t E = sizeof(OpT);
         if (v < vNKp) return o.nkp + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
         v -= vNKp;
-        if (v < vQp) return o.qp + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
-        v -= vQp;
         if (v < vKhT) return o.kht + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
         v -= vKhT;
         if (v < vT) return o.t + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
         v -= vT;
-        if (v < vP) return o.p + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
-        v -= vP;
         if (v < vGam) return o.gam + 16 * v;
         v -= vGam;
         if (v < vBeta) return o.beta + 16 * v;
-        return o.ts + 16 * (v - vBeta);
+        v -= vBeta;
+        if (v < vTs) return o.ts + 16 * v;
+        v -= vTs;
+        if (v < vQp) return o.qp + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
+        return o.p + (((v - vQp) / RC) * P::LDC + ((v - vQp) % RC) * EPV) * E;
     }
 };
 
@@ -1070,7 +1072,8 @@ struct ChainCfg {
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
     static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
-    static constexpr int IITEMS = (Img::NVEC + NT - 1) / NT;        // image vectors per thread
+    static constexpr int IITEMS = (Img::NVEC + NT - 1) / NT;        // image vectors per thread (outputs)
+    static constexpr int IITEMS_SUM = (Img::NVEC_SUM + NT - 1) / NT; // (summaries: no Q+, P)
     static constexpr int VEC = 16 / (int)sizeof(TIn);               // elements per 16-byte vector
     static constexpr int VPR = BV / VEC;                            // vectors per value-tile row
     static constexpr int VITEMS = (C * VPR + NT - 1) / NT;
@@ -1171,11 +1174,13 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     }
 
     // ---- chunk staging: image + value tile of chunk ci in registers
-    f32x4 ri[Q::IITEMS], rv[Q::VITEMS];
+    constexpr int IIT = SUMMARY ? Q::IITEMS_SUM : Q::IITEMS;       // image vectors this pass reads
+    constexpr int NV = SUMMARY ? Img::NVEC_SUM : Img::NVEC;
+    f32x4 ri[IIT], rv[Q::VITEMS];
     auto load = [&](int ci) {
         const f32x4 *src = seg.img + ((gc0 + ci) * H + h) * Img::NVEC;
 #pragma unroll
-        for (int it = 0; it < Q::IITEMS; ++it) ri[it] = src[min(tid + it * NT, Img::NVEC - 1)];
+        for (int it = 0; it < IIT; ++it) ri[it] = src[min(tid + it * NT, NV - 1)];
         const int c0 = t_start + ci * C, LL = min(C, t_end - c0);
 #pragma unroll
         for (int it = 0; it < Q::VITEMS; ++it) {
@@ -1186,9 +1191,9 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         }
     };
     const typename Img::Offs offs = {Q::offNKp, Q::offQp, Q::offKhT, Q::offT, Q::offP, Q::offGam, Q::offBeta, Q::offTs};
-    uint32_t stage_off[Q::IITEMS];                        // LDS byte offsets of this thread's image vectors
+    uint32_t stage_off[IIT];                              // LDS byte offsets of this thread's image vectors
 #pragma unroll
-    for (int it = 0; it < Q::IITEMS; ++it) stage_off[it] = Img::lds_off(min(tid + it * NT, Img::NVEC - 1), offs);
+    for (int it = 0; it < IIT; ++it) stage_off[it] = Img::lds_off(min(tid + it * NT, NV - 1), offs);
     // Every staged register is written on every path (surplus items repeat
     // the last vector, same value to the same place): a conditional consumer
     // would leave the loads pending at the loop head for the compiler, which
@@ -1196,7 +1201,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     auto stage = [&](int ci, int b) {
         unsigned char *base = smem + b * Q::BUF;
 #pragma unroll
-        for (int it = 0; it < Q::IITEMS; ++it) *reinterpret_cast<f32x4 *>(base + stage_off[it]) = ri[it];
+        for (int it = 0; it < IIT; ++it) *reinterpret_cast<f32x4 *>(base + stage_off[it]) = ri[it];
         TIn *sV = reinterpret_cast<TIn *>(base + Q::offV);
         const int LL = min(C, t_end - (t_start + ci * C));
 #pragma unroll
