@@ -39,7 +39,8 @@ PREFILL_FREF_PER_HT = 6 * DK * DV + 2 * 64 * (DK + DV)
 DECODE_BYTES_PER_UNIT = 2 * DK * DV * 4 + 3 * 2 * DK + 4 * DK + 4 + 2 * DV
 PREFILL_KERNELS = {
     "cp": "kda_prefill_cp call: kda_cp_plan_kernel, kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
-          "kda_chain_kernel<bf16,32,8,summary>, kda_cp_combine_kernel, kda_chain_kernel<bf16,32,8,output>",
+          "kda_chain_kernel<bf16,32,8 waves,2 tiles,summary>, kda_cp_combine_kernel, "
+          "kda_chain_kernel<bf16,32,4 waves,2 tiles,output,single buffer>",
     "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
 }
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_traffic.json")
@@ -86,16 +87,26 @@ def write_traffic(fetch_csv, write_csv):
                         "--copy-calibration" % c for c in ("FETCH_SIZE", "WRITE_SIZE")]
                        + ["python bench.py --traffic-from <fetch dir>/run_counter_collection.csv "
                           "<write dir>/run_counter_collection.csv"],
-           "unit": "bytes per kda_prefill_cp call (all four launches), counters scaled by the 1 GiB negation"}
+           "unit": "bytes per kda_prefill_cp call (all five launches), counters scaled by the 1 GiB negation"}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path)
         calib = max(v for n, v in rows.values() if "neg" in n.lower())
         factor = float(1 << 30) / (calib * 1024.0)
-        kda = [(n, v) for n, v in rows.values() if "kda_prefill_kernel" in n or "kda_cp_" in n]
-        calls = sum(1 for n, _ in kda if "kda_cp_plan_kernel" in n) or sum(1 for n, _ in kda)
-        per_call = sum(v for _, v in kda) * 1024.0 / calls
-        out[counter] = {"calibration_kib": calib, "scale": factor, "calls": calls,
+        # one kda_prefill_cp call = one launch of each kind below (the plan
+        # kernel also serves the backward, so each kind is averaged on its own)
+        kinds = {"plan": lambda n: "kda_cp_plan_kernel" in n,
+                 "chunk_operands": lambda n: "kda_prefill_kernel" in n and "Li1EEE" in n,
+                 "summaries": lambda n: "kda_chain_kernel" in n and "Lb1ELb" in n,
+                 "combine": lambda n: "kda_cp_combine_kernel" in n,
+                 "outputs": lambda n: "kda_chain_kernel" in n and "Lb0ELb" in n}
+        per_kind = {}
+        for kind, match in kinds.items():
+            vals = [v for n, v in rows.values() if match(n)]
+            per_kind[kind] = {"launches": len(vals), "kib_avg_raw": sum(vals) / max(len(vals), 1),
+                              "bytes_avg": sum(vals) / max(len(vals), 1) * 1024.0 * factor}
+        per_call = sum(k["kib_avg_raw"] for k in per_kind.values()) * 1024.0
+        out[counter] = {"calibration_kib": calib, "scale": factor, "per_kernel": per_kind,
                         "kib_per_call_raw": per_call / 1024.0, "bytes_per_call": per_call * factor}
         total += per_call * factor
     out["hbm_bytes_per_launch"] = total
@@ -241,7 +252,7 @@ def main():
     # speculative-decoding replay: 4 draft tokens per (sequence, head) of the
     # decode batch, outputs for all of them and the state committed, one call
     # (its own measurement, outside the timed steps)
-    RT = 4
+    RT = min(4, dec["q"].shape[0])
     perm = lambda x: x[:RT].transpose(0, 1).reshape(Nd * RT, *x.shape[2:]).contiguous()
     rq, rk, rv, rg, rb = (perm(dec[key]) for key in ("q", "k", "v", "g", "beta"))
     rcu = torch.arange(Nd + 1, dtype=torch.int32, device=dev) * RT

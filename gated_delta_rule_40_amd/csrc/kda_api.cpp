@@ -17,7 +17,8 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          int32_t max_snaps, const int32_t *snap_chunk_off, hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
-                                         int32_t max_chunks, int32_t *chunk_off, hipStream_t stream);
+                                         int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
+                                         hipStream_t stream);
 extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
                                             const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
                                             int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
@@ -26,7 +27,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       hipStream_t stream);
+                                       const int32_t *sched, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" size_t kda_backward_scratch_floats_per_unit();
 extern "C" int32_t kda_backward_num_blocks();
@@ -167,13 +168,14 @@ constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the segme
 constexpr int32_t kCpSumBlock = 256; // value + transition columns per workgroup of the summary pass
 
 struct CpLayout {
-    size_t plan, seq_seg, chunk_off, seg_out, seg_init, img, total;
+    size_t plan, sched, seq_seg, chunk_off, seg_out, seg_init, img, total;
     int32_t max_segs, max_chunks;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace sections: plan [max_segs][4] int32, per-sequence first segment
+// Workspace sections: plan [max_segs][4] int32, dispatch order [max_segs]
+// int32, per-sequence first segment
 // [N + 1] int32, per-sequence first chunk [N + 1] int32, summaries
 // [max_segs][H][dk][dv + dk] fp32, entering states [max_segs][H][dk][dv]
 // fp32, chunk-operand images [max_chunks][H][image].  Every sequence of
@@ -187,7 +189,8 @@ bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16
     lay->max_segs = (int32_t)segs;
     lay->max_chunks = (int32_t)chunks;
     lay->plan = 0;
-    lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
+    lay->sched = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
+    lay->seq_seg = align256(lay->sched + sizeof(int32_t) * (size_t)segs);
     lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
     lay->seg_out = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
     lay->seg_init = align256(lay->seg_out + sizeof(float) * (size_t)segs * H * dk * (dv + dk));
@@ -242,6 +245,7 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
     if (num_seqs == 0) return KDA_OK;
     char *ws = static_cast<char *>(workspace);
     int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
+    int32_t *sched = reinterpret_cast<int32_t *>(ws + lay.sched);
     int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + lay.chunk_off);
     float *seg_out = reinterpret_cast<float *>(ws + lay.seg_out);
@@ -249,18 +253,18 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
     void *img = ws + lay.img;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, s);
+                                      kCpChunk, lay.max_chunks, chunk_off, sched, s);
     if (e == hipSuccess)   // chunk operands of every (chunk, head)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
     if (e == hipSuccess)   // segment summaries (segments with a successor)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
-                             plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, s);
+                             plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, sched, s);
     if (e == hipSuccess)   // entering state of every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, s);
     if (e == hipSuccess)   // outputs and final states
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, s);
+                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -373,7 +377,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // chunk numbering (one segment per sequence: only chunk_off is used)
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, 1 << 30, num_seqs + 1, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, s);
+                                      kCpChunk, lay.max_chunks, chunk_off, nullptr, s);
     if (e == hipSuccess)   // forward: the state at every chunk start
         e = kda_launch_prefill(bf16, kCpChunk, 64, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs,
                                total_tokens, num_heads, dv, nullptr, nullptr, snaps, kCpChunk, 0, chunk_off, s);

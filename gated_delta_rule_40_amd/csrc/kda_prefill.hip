@@ -153,6 +153,7 @@ struct SegArgs {
     float *snap;                // [N][max_snaps][H][DK][dv] state snapshots, or nullptr (fused kernel)
     int32_t snap_every;         // tokens between snapshots, a multiple of the chunk
     int32_t max_snaps;
+    const int32_t *sched;       // [num_segs] plan index of each dispatch position, or nullptr (plan order)
 };
 
 enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2 };   // MODE_SNAP: fused + state snapshots
@@ -1046,11 +1047,14 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 // ------------------------------------------------------------ state chain
 // The state-dependent pass over chunk-operand images: one workgroup per
 // (unit, block of BV value columns) as in the fused kernel, walking the unit's
-// chunks in order.  Per chunk: one barrier; the next chunk's image and value
-// tile are loaded into registers, the chain runs on the current LDS buffer,
-// each wave stores its own output columns, and the registers are written to
-// the other LDS buffer.
-template <typename TIn, int C, int NW, int NCT>
+// chunks in order.  Per chunk: the next chunk's image and value tile are
+// loaded into registers, the chain runs on the current LDS buffer, each wave
+// stores its own output columns, and the registers are written to the LDS.
+// Double-buffered (SB = false): one barrier per chunk, the registers go to the
+// other buffer.  Single-buffered (SB = true): a second barrier before the
+// registers overwrite the one buffer; half the LDS, so that two workgroups
+// share a compute unit and one runs while the other waits.
+template <typename TIn, int C, int NW, int NCT, bool SB = false>
 struct ChainCfg {
     typedef PrefillCfg<TIn, C, NW> P;
     typedef typename P::OpT OpT;
@@ -1067,7 +1071,7 @@ struct ChainCfg {
     static constexpr uint32_t offTs = offBeta + sizeof(float) * C;
     static constexpr uint32_t offV = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
     static constexpr uint32_t BUF = (offV + sizeof(TIn) * C * LDV + 15) / 16 * 16;   // one chunk buffer
-    static constexpr uint32_t offO = 2 * BUF;                                  // [NW][C][16 NCT] outputs
+    static constexpr uint32_t offO = (SB ? 1 : 2) * BUF;                       // [NW][C][16 NCT] outputs
     static constexpr uint32_t bytes = offO + sizeof(TIn) * NW * C * 16 * NCT;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
@@ -1080,13 +1084,13 @@ struct ChainCfg {
     static constexpr int OVEC = C * 16 * NCT / VEC;                 // vectors of one wave's output tile
 };
 
-template <typename TIn, int C, int NW, int NCT, bool SUMMARY>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT>::WAVES_PER_EU)))
+template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
                       TIn *__restrict__ out, float *final_state, SegArgs seg)
 {
-    typedef ChainCfg<TIn, C, NW, NCT> Q;
+    typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
     typedef typename Q::OpT OpT;
     typedef typename Q::Img Img;
     constexpr int NT = Q::NT, BV = Q::BV, LDV = Q::LDV, VEC = Q::VEC, VPR = Q::VPR;
@@ -1101,9 +1105,11 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     const int vb = slot % nblk;
     const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
     if (unit >= (int64_t)(segmented ? seg.num_segs : num_seqs) * num_heads) return;
-    const int su = (int)(unit / num_heads), h = (int)(unit % num_heads);
+    int su = (int)(unit / num_heads);
+    const int h = (int)(unit % num_heads);
     int n = su, t_start, t_end, sflags = SEG_FIRST | SEG_LAST;
     if (segmented) {
+        if (seg.sched) su = min(max(seg.sched[su], 0), seg.num_segs - 1);
         n = seg.plan[4 * su];
         t_start = seg.plan[4 * su + 1];
         t_end = seg.plan[4 * su + 2];
@@ -1217,9 +1223,9 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     }
     TIn *sOw = reinterpret_cast<TIn *>(smem + Q::offO) + wave * C * 16 * NCT;   // this wave's output tile
     for (int ci = 0; ci < nch; ++ci) {
-        __syncthreads();                          // buffer ci & 1 staged; ci - 1 done with the other
+        __syncthreads();                          // chunk ci staged; (double buffer) ci - 1 done with the other
         load(min(ci + 1, nch - 1));               // unconditional, see the fused kernel
-        const unsigned char *base = smem + (ci & 1) * Q::BUF;
+        const unsigned char *base = smem + (SB ? 0 : (ci & 1) * Q::BUF);
         chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT>(
             S, sS, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
             reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
@@ -1243,7 +1249,8 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
             }
             __asm__ volatile("" ::: "memory");
         }
-        stage(min(ci + 1, nch - 1), (ci + 1) & 1);
+        if constexpr (SB) __syncthreads();       // every wave is done with the buffer
+        stage(min(ci + 1, nch - 1), SB ? 0 : (ci + 1) & 1);
     }
 
 #pragma unroll
@@ -1289,13 +1296,13 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
     return hipGetLastError();
 }
 
-template <typename TIn, int C, int NW, int NCT>
+template <typename TIn, int C, int NW, int NCT, bool SB = false>
 static hipError_t launch_chain_t(const void *v, const float *init, const int32_t *cu, int32_t N, int32_t T_tot,
                                  int32_t H, int32_t dv, void *out, float *fin, SegArgs seg, hipStream_t stream)
 {
-    typedef ChainCfg<TIn, C, NW, NCT> Q;
+    typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
     const bool summary = seg.mode == SEG_SUMMARY;
-    auto kern = summary ? kda_chain_kernel<TIn, C, NW, NCT, true> : kda_chain_kernel<TIn, C, NW, NCT, false>;
+    auto kern = summary ? kda_chain_kernel<TIn, C, NW, NCT, true, SB> : kda_chain_kernel<TIn, C, NW, NCT, false, SB>;
     static bool attr_set[2] = {false, false};   // idempotent; racing threads set the same value
     if (!attr_set[summary]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -1317,14 +1324,17 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
 // One workgroup: segments per sequence (at least one, so that empty sequences
 // still produce their final state), exclusive scan, plan entries; and, if
 // chunk_off is given, the first chunk of each sequence in chunks of `chunk`
-// tokens (chunk_off[N] = total chunks, at most max_chunks).
+// tokens (chunk_off[N] = total chunks, at most max_chunks); and, if sched is
+// given, a dispatch order of the max_segs plan entries (a permutation).
 __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restrict__ cu, int32_t N,
                                                           int32_t T_tot, int32_t seg_len, int32_t max_segs,
                                                           int32_t *__restrict__ plan,
                                                           int32_t *__restrict__ seq_seg, int32_t chunk,
-                                                          int32_t max_chunks, int32_t *__restrict__ chunk_off)
+                                                          int32_t max_chunks, int32_t *__restrict__ chunk_off,
+                                                          int32_t *__restrict__ sched)
 {
     __shared__ int64_t scan[256], cscan[256];
+    __shared__ int32_t hist[256];
     int64_t carry = 0, ccarry = 0;                     // 64-bit: cu is not trusted
     for (int base = 0; base < N; base += 256) {
         const int n = base + (int)threadIdx.x;
@@ -1372,6 +1382,35 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
         plan[4 * gs + 1] = 0;
         plan[4 * gs + 2] = 0;
         plan[4 * gs + 3] = 0;
+        if (sched) sched[gs] = gs;
+    }
+    if (!sched) return;
+    // Dispatch order, longest segment first: workgroups start in index order,
+    // so the short tail segments fill the gaps the full-length ones leave at
+    // the end of a pass.  Counting sort on 256 length buckets (bucket 0 = full
+    // length, 255 = empty); the order inside a bucket does not matter, since
+    // the segments of one pass are independent.
+    hist[threadIdx.x] = 0;
+    __syncthreads();   // also makes this workgroup's plan entries visible below
+    for (int gs = (int)threadIdx.x; gs < used; gs += 256) {
+        const int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
+        atomicAdd(&hist[(int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len)], 1);
+    }
+    __syncthreads();
+    const int32_t cnt = hist[threadIdx.x];
+    scan[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+        __syncthreads();
+        scan[threadIdx.x] += x;
+        __syncthreads();
+    }
+    hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - cnt);   // bucket start
+    __syncthreads();
+    for (int gs = (int)threadIdx.x; gs < used; gs += 256) {
+        const int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
+        sched[atomicAdd(&hist[(int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len)], 1)] = gs;
     }
 }
 
@@ -1437,7 +1476,7 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          int32_t max_snaps, const int32_t *snap_chunk_off, hipStream_t stream)
 {
     using namespace kda;
-    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, snap_chunk_off, nullptr, snap, snap_every, max_snaps};
+    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, snap_chunk_off, nullptr, snap, snap_every, max_snaps, nullptr};
     if (snap) {   // snapshots: 32-token chunks, 64-column value blocks
         if (chunk != 32 || dv_block != 64) return hipErrorInvalidValue;
         if (bf16) return launch_prefill_t<bf16_t, 32, 4, MODE_SNAP>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
@@ -1459,10 +1498,11 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
 
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
-                                         int32_t max_chunks, int32_t *chunk_off, hipStream_t stream)
+                                         int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
+                                         hipStream_t stream)
 {
     hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_tot, seg_len, max_segs,
-                       plan, seq_seg, chunk, max_chunks, chunk_off);
+                       plan, seq_seg, chunk, max_chunks, chunk_off, sched);
     return hipGetLastError();
 }
 
@@ -1473,7 +1513,7 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
                                             hipStream_t stream)
 {
     using namespace kda;
-    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0};
+    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr};
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
@@ -1485,17 +1525,18 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       hipStream_t stream)
+                                       const int32_t *sched, hipStream_t stream)
 {
     using namespace kda;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
-                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), nullptr, 0, 0};
-    // bf16: 128 columns as 8 waves x 1 tile, 256 as 8 waves x 2 tiles (two
-    // tiles per wave share every operand fragment, but four waves of two
-    // tiles hide latency worse than eight of one); fp32 images are twice as
-    // large and their buffers fit the LDS at 64 columns only
+                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), nullptr, 0, 0, sched};
+    // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
+    // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
+    // two workgroups per compute unit (two tiles per wave share every operand
+    // fragment; the second workgroup covers the waits of the first); fp32
+    // images are twice as large and their buffers fit the LDS at 64 columns only
     if (bf16 && dv_block == 256) return launch_chain_t<bf16_t, 32, 8, 2>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
-    if (bf16 && dv_block == 128) return launch_chain_t<bf16_t, 32, 8, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    if (bf16 && dv_block == 128) return launch_chain_t<bf16_t, 32, 4, 2, true>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (dv_block != 64 && dv_block != 128 && dv_block != 256) return hipErrorInvalidValue;
     if (bf16) return launch_chain_t<bf16_t, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     return launch_chain_t<float, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
