@@ -184,12 +184,12 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // Exact power-of-two scale that maps a magnitude m into [2^13, 2^14):
 // returns 2^(13 - floor(log2 m)) for finite normal m > 0, else 1.  Used to
 // keep fp16 MFMA operands in range without changing their relative rounding.
+// Branch-free: the exponent arithmetic runs on every lane and a select
+// picks 1 for the special cases.
 __device__ __forceinline__ float pow2_scale(float m) {
-    const uint32_t e = (__float_as_uint(m) >> 23) & 0xffu;
-    if (e == 0u || e == 0xffu) return 1.f;
-    int se = 13 - ((int)e - 127) + 127;
-    se = se < 1 ? 1 : (se > 254 ? 254 : se);
-    return __uint_as_float((uint32_t)se << 23);
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);
+    const int se = min(max(13 - (e - 127) + 127, 1), 254);
+    return __uint_as_float((uint32_t)((e == 0 || e == 0xff) ? 127 : se) << 23);
 }
 // 1/s for a scale s returned by pow2_scale (exact).
 __device__ __forceinline__ float pow2_inv(float s) {
@@ -200,11 +200,13 @@ __device__ __forceinline__ float pow2_inv(float s) {
 // the gfx950 lane swaps (VALU, no LDS round trip): permlane16_swap(x, x)
 // returns rows {0,0,2,2} and {1,1,3,3} of x (a row = 16 lanes), and
 // permlane32_swap(x, x) the lower and the upper half-wave, each in both halves.
+// For m >= 0 (magnitudes): non-negative floats order as their bit patterns, so
+// the maxima are integer maxima, which need no NaN canonicalisation.
 __device__ __forceinline__ float colmax(float m) {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    const uint32_t u = max(a[0], a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(max(b[0], b[1]));
 }
 // Lane movement inside each 16-lane row by DPP (VALU, no LDS round trip):
 // quad_perm(1,0,3,2) = 0xB1 and quad_perm(2,3,0,1) = 0x4E swap neighbours at
@@ -213,14 +215,19 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-// Maximum over the 16 lanes of each row.
-__device__ __forceinline__ float rowmax16(float m) {
-    m = fmaxf(m, dpp_mov<0xB1>(m));
-    m = fmaxf(m, dpp_mov<0x4E>(m));
-    m = fmaxf(m, dpp_mov<0x124>(m));
-    return fmaxf(m, dpp_mov<0x128>(m));
+// Maximum over the 16 lanes of each row, for m >= 0 (integer maxima as in colmax).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_movu(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
-// Maximum over the whole wave.
+__device__ __forceinline__ float rowmax16(float m) {
+    uint32_t u = __float_as_uint(m);
+    u = max(u, dpp_movu<0xB1>(u));
+    u = max(u, dpp_movu<0x4E>(u));
+    u = max(u, dpp_movu<0x124>(u));
+    return __uint_as_float(max(u, dpp_movu<0x128>(u)));
+}
+// Maximum over the whole wave, for m >= 0.
 __device__ __forceinline__ float wavemax(float m) { return colmax(rowmax16(m)); }
 // Sum over each aligned group of 8 lanes, in every lane of the group
 // (row_half_mirror = 0x141 pairs lane l with 7 - l).

@@ -201,6 +201,14 @@ struct ChunkImage {
     }
 };
 
+// 16-byte vectors of the 4-aligned tails below the diagonal of columns
+// s0 .. s1-1 of a 16 x 16 block (rows ((s + 1) & ~3) .. 15 of column s).
+constexpr int tail_vecs(int s0, int s1) {
+    int n = 0;
+    for (int s = s0; s < s1; ++s) n += (SUB - ((s + 1) & ~3)) / 4;
+    return n;
+}
+
 // sub-tile pair p -> (a, b), b <= a
 __device__ __forceinline__ void pair_of(int p, int &a, int &b) {
     a = 0;
@@ -898,20 +906,37 @@ void kda_prefill_kernel(
         if (tid < NSUB * SUB) {
             const int a = tid / SUB, nc = tid % SUB;
             const float *NT = sAd + a * SUB * P::LDAD;     // NT[s][r] = N[r][s]
+            // Forward substitution, lane = column.  The 4-aligned tails of the
+            // columns below the diagonal are read in batches ahead of the
+            // steps that use them: read one step at a time, every read's
+            // latency would sit on the dependent chain.
             float x[SUB];
 #pragma unroll
             for (int r = 0; r < SUB; ++r) x[r] = (r == nc) ? 1.f : 0.f;
+            auto solve = [&](auto s0_tag, auto s1_tag) {
+                constexpr int S0 = decltype(s0_tag)::value, S1 = decltype(s1_tag)::value;
+                f32x4 tv[tail_vecs(S0, S1)];
+                int v = 0;
 #pragma unroll
-            for (int s = 0; s < SUB - 1; ++s) {
-                // the 4-aligned tail of column s below the diagonal
+                for (int s = S0; s < S1; ++s)
 #pragma unroll
-                for (int q4 = (s + 1) & ~3; q4 < SUB; q4 += 4) {
-                    const f32x4 t = *reinterpret_cast<const f32x4 *>(NT + s * P::LDAD + q4);
+                    for (int q4 = (s + 1) & ~3; q4 < SUB; q4 += 4)
+                        tv[v++] = *reinterpret_cast<const f32x4 *>(NT + s * P::LDAD + q4);
+                v = 0;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (q4 + e > s) x[q4 + e] -= t[e] * x[s];
-                }
-            }
+                for (int s = S0; s < S1; ++s)
+#pragma unroll
+                    for (int q4 = (s + 1) & ~3; q4 < SUB; q4 += 4) {
+                        const f32x4 t = tv[v++];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (q4 + e > s) x[q4 + e] -= t[e] * x[s];
+                    }
+            };
+            solve(std::integral_constant<int, 0>(), std::integral_constant<int, 3>());
+            solve(std::integral_constant<int, 3>(), std::integral_constant<int, 7>());
+            solve(std::integral_constant<int, 7>(), std::integral_constant<int, 11>());
+            solve(std::integral_constant<int, 11>(), std::integral_constant<int, SUB - 1>());
             // fp16 range: scale the block down by a power of two if it exceeds 2^14
             float sc = 1.f;
             if (kIn16) {
