@@ -280,7 +280,7 @@ def main():
     Tb, Hb = bwd["q"].shape[0], bwd["q"].shape[1]
     gen = torch.Generator(device=dev).manual_seed(7)
     b_dout = torch.randn(Tb, Hb, DV, generator=gen, device=dev).to(torch.bfloat16)
-    b_ws = torch.empty(K.kda_backward_workspace_size(1, Tb, Hb, DK, DV), dtype=torch.uint8, device=dev)
+    b_ws = torch.empty(K.kda_backward_workspace_size(1, Tb, Hb, DK, DV, torch.bfloat16), dtype=torch.uint8, device=dev)
     b_grads = None
 
     def backward():

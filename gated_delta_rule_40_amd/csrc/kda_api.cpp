@@ -27,14 +27,20 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, hipStream_t stream);
+                                       const int32_t *sched, float *snap, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
-extern "C" size_t kda_backward_scratch_floats_per_unit();
+extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
+                                                  const float *beta, const void *dout, const int32_t *plan,
+                                                  int32_t num_segs, int32_t T_tot, int32_t H, float *seg_out,
+                                                  hipStream_t stream);
+extern "C" size_t kda_backward_scratch_floats_per_wg();
+extern "C" int32_t kda_backward_max_wgs();
 extern "C" int32_t kda_backward_num_blocks();
 extern "C" hipError_t kda_launch_backward(int bf16, const void *q, const void *k, const void *v, const float *g,
                                           const float *beta, const float *init, const int32_t *cu,
                                           const int32_t *chunk_off, const float *snaps, const void *dout,
-                                          const float *dfinal, int32_t N, int32_t T_tot, int32_t H, float *scratch,
+                                          const int32_t *plan, int32_t num_segs, const float *seg_dsend,
+                                          int32_t N, int32_t T_tot, int32_t H, float *scratch,
                                           float *part_vec, float *part_beta, float *dq, float *dk, float *dv,
                                           float *dg, float *dbeta, float *dinit, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const void *k, const void *v,
@@ -44,7 +50,7 @@ extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const vo
                                                hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
-                                            hipStream_t stream);
+                                            int32_t reverse, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, float *state,
                                         int32_t N, int32_t H, void *out, hipStream_t stream);
@@ -259,12 +265,12 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
                                   lay.max_chunks, img, s);
     if (e == hipSuccess)   // segment summaries (segments with a successor)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
-                             plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, sched, s);
+                             plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, sched, nullptr, s);
     if (e == hipSuccess)   // entering state of every segment
-        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, s);
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, 0, s);
     if (e == hipSuccess)   // outputs and final states
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, s);
+                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -312,24 +318,70 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
 namespace {
 
 struct BwdLayout {
-    size_t plan, seq_seg, chunk_off, snaps, scratch, part_vec, part_beta, total;
-    int32_t max_chunks;
+    size_t plan, seq_seg, chunk_off, fplan, fsched, fseq_seg, img, snaps, seg_sum, seg_dsend, scratch, part_vec,
+        part_beta, total;
+    int32_t max_chunks, max_segs, seg_len, fmax_segs, fseg_len;
 };
 
-bool bwd_layout(int32_t N, int32_t T, int32_t H, BwdLayout *lay)
+// Segment length of the backward passes: about 1,024 work items of (segment,
+// head, 32 columns) in total (two per workgroup of the main pass; shorter
+// segments lengthen the sequential combine), at least 64 tokens, a multiple
+// of the chunk.
+int32_t bwd_seg_len(int32_t T, int32_t H)
 {
+    int64_t len = (int64_t)T * H * kda_backward_num_blocks() / 1024;
+    len = len < 64 ? 64 : (len > 65536 ? 65536 : len);
+    return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
+}
+
+// Segment length of the forward pass that stores the chunk-start states (the
+// context-parallel pipeline with state stores): longer than the backward's.
+int32_t bwd_fwd_seg_len(int32_t T, int32_t H, int32_t bwd_len)
+{
+    int64_t len = (int64_t)T * H / 256;
+    len = len < 256 ? 256 : (len > 65536 ? 65536 : len);
+    len = (len + kCpChunk - 1) / kCpChunk * kCpChunk;
+    return (int32_t)(len < bwd_len ? bwd_len : len);
+}
+
+// Workspace sections: the backward's plan [max_segs][4] int32 with the first
+// segment [N+1] and first chunk [N+1] of each sequence; the forward's plan
+// [fmax_segs][4], dispatch order and first segments; the forward's chunk
+// images; forward states at chunk starts [max_chunks][H][dk][dv]; summaries
+// [max_segs][H][dk][dv + dk] and entering states / gradients
+// [max_segs][H][dk][dv] (used by the forward pass, then by the backward);
+// the main pass's per-workgroup scratch; the partial row sums of dq, dk, dg
+// and dbeta.
+bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
+{
+    const int32_t seg_len = bwd_seg_len(T, H);
+    const int32_t fseg_len = bwd_fwd_seg_len(T, H, seg_len);
     const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
-    if (chunks > INT32_MAX / 4 || (int64_t)N + 1 > INT32_MAX / 4) return false;
+    const int64_t segs = (int64_t)T / seg_len + 1 + N;
+    const int64_t fsegs = (int64_t)T / fseg_len + 1 + N;
+    if (chunks > INT32_MAX / 4 || segs > INT32_MAX / 4) return false;
     const size_t S = (size_t)kHeadDim * kHeadDim;
     const size_t rows = (size_t)T * H;
     const size_t nblk = (size_t)kda_backward_num_blocks();
+    const int64_t items = segs * H * (int64_t)nblk;
+    const size_t wgs = (size_t)(items < kda_backward_max_wgs() ? items : kda_backward_max_wgs());
+    lay->seg_len = seg_len;
+    lay->fseg_len = fseg_len;
     lay->max_chunks = (int32_t)chunks;
+    lay->max_segs = (int32_t)segs;
+    lay->fmax_segs = (int32_t)fsegs;
     lay->plan = 0;
-    lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * ((size_t)N + 1));
+    lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
     lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
-    lay->snaps = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
-    lay->scratch = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
-    lay->part_vec = align256(lay->scratch + sizeof(float) * (size_t)N * H * kda_backward_scratch_floats_per_unit());
+    lay->fplan = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
+    lay->fsched = align256(lay->fplan + sizeof(int32_t) * 4 * (size_t)fsegs);
+    lay->fseq_seg = align256(lay->fsched + sizeof(int32_t) * (size_t)fsegs);
+    lay->img = align256(lay->fseq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->snaps = align256(lay->img + kda_chunk_image_bytes(bf16) * (size_t)chunks * H);
+    lay->seg_sum = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
+    lay->seg_dsend = align256(lay->seg_sum + sizeof(float) * (size_t)segs * H * 2 * S);
+    lay->scratch = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
+    lay->part_vec = align256(lay->scratch + sizeof(float) * wgs * kda_backward_scratch_floats_per_wg());
     lay->part_beta = align256(lay->part_vec + sizeof(float) * nblk * 3 * rows * kHeadDim);
     lay->total = align256(lay->part_beta + sizeof(float) * nblk * rows);
     return true;
@@ -337,11 +389,13 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, BwdLayout *lay)
 
 }  // namespace
 
-size_t kda_backward_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv)
+size_t kda_backward_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk, int32_t dv,
+                                   kda_dtype dtype)
 {
     if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || dk != kHeadDim || dv != kHeadDim) return 0;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
     BwdLayout lay;
-    if (!bwd_layout(num_seqs, total_tokens, num_heads, &lay)) return 0;
+    if (!bwd_layout(num_seqs, total_tokens, num_heads, dtype == KDA_BF16, &lay)) return 0;
     return lay.total;
 }
 
@@ -362,11 +416,12 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
         return KDA_ERR_INVALID_ARG;
     if (st != KDA_OK) return st;
     BwdLayout lay;
-    if (!bwd_layout(num_seqs, total_tokens, num_heads, &lay)) return KDA_ERR_INVALID_ARG;
+    if (!bwd_layout(num_seqs, total_tokens, num_heads, dtype == KDA_BF16, &lay)) return KDA_ERR_INVALID_ARG;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
     const int64_t units = (int64_t)num_seqs * num_heads;
     if (units == 0) return KDA_OK;
-    if (units * kda_backward_num_blocks() > INT32_MAX || (int64_t)lay.max_chunks * num_heads > INT32_MAX)
+    if ((int64_t)lay.max_segs * num_heads * 2 * kda_backward_num_blocks() > INT32_MAX ||
+        (int64_t)lay.max_chunks * num_heads > INT32_MAX)
         return KDA_ERR_INVALID_ARG;
     const int bf16 = dtype == KDA_BF16 ? 1 : 0;
     char *ws = static_cast<char *>(workspace);
@@ -374,16 +429,43 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + lay.chunk_off);
     float *snaps = reinterpret_cast<float *>(ws + lay.snaps);
+    float *seg_sum = reinterpret_cast<float *>(ws + lay.seg_sum);
+    float *seg_dsend = reinterpret_cast<float *>(ws + lay.seg_dsend);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // chunk numbering (one segment per sequence: only chunk_off is used)
-    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, 1 << 30, num_seqs + 1, plan, seq_seg,
+    // segments and chunk numbering
+    int32_t *fplan = reinterpret_cast<int32_t *>(ws + lay.fplan);
+    int32_t *fsched = reinterpret_cast<int32_t *>(ws + lay.fsched);
+    int32_t *fseq_seg = reinterpret_cast<int32_t *>(ws + lay.fseq_seg);
+    void *img = ws + lay.img;
+    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
                                       kCpChunk, lay.max_chunks, chunk_off, nullptr, s);
-    if (e == hipSuccess)   // forward: the state at every chunk start
-        e = kda_launch_prefill(bf16, kCpChunk, 64, q, k, v, g, beta, initial_state, cu_seqlens, num_seqs,
-                               total_tokens, num_heads, dv, nullptr, nullptr, snaps, kCpChunk, 0, chunk_off, s);
+    // forward: the state at every chunk start, by the context-parallel
+    // pipeline (its own, longer segments) with state stores and no outputs
     if (e == hipSuccess)
-        e = kda_launch_backward(bf16, q, k, v, g, beta, initial_state, cu_seqlens, chunk_off, snaps, dout, dfinal,
-                                num_seqs, total_tokens, num_heads, reinterpret_cast<float *>(ws + lay.scratch),
+        e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.fseg_len, lay.fmax_segs, fplan, fseq_seg,
+                               kCpChunk, lay.max_chunks, chunk_off, fsched, s);
+    if (e == hipSuccess)
+        e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
+                                  lay.max_chunks, img, s);
+    if (e == hipSuccess)
+        e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
+                             nullptr, nullptr, fplan, lay.fmax_segs, 1, nullptr, seg_sum, chunk_off, img, fsched,
+                             nullptr, s);
+    if (e == hipSuccess)
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, fseq_seg, seg_sum, seg_dsend, 0, s);
+    if (e == hipSuccess)
+        e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
+                             nullptr, nullptr, fplan, lay.fmax_segs, 0, seg_dsend, nullptr, chunk_off, img, fsched,
+                             snaps, s);
+    if (e == hipSuccess)   // gradient summaries of every segment but a sequence's first
+        e = kda_launch_backward_summary(bf16, q, k, g, beta, dout, plan, lay.max_segs, total_tokens, num_heads,
+                                        seg_sum, s);
+    if (e == hipSuccess)   // the gradient entering every segment at its end
+        e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, seg_sum, seg_dsend, 1, s);
+    if (e == hipSuccess)
+        e = kda_launch_backward(bf16, q, k, v, g, beta, initial_state, cu_seqlens, chunk_off, snaps, dout, plan,
+                                lay.max_segs, seg_dsend, num_seqs, total_tokens, num_heads,
+                                reinterpret_cast<float *>(ws + lay.scratch),
                                 reinterpret_cast<float *>(ws + lay.part_vec),
                                 reinterpret_cast<float *>(ws + lay.part_beta), dq, dk_out, dv_out, dg, dbeta, dinit,
                                 s);

@@ -13,13 +13,23 @@
 //
 // Work decomposition.  The state and its gradient evolve column by column:
 // column c of S and dS needs only column c of v, do and du.  Only dq, dk, dg
-// and dbeta sum over columns.  So one workgroup owns a (sequence, head) and a
+// and dbeta sum over columns.  So one work item is a (segment, head) and a
 // block of BV = 32 value columns, with S and dS in registers; its row sums go
 // to per-block partial buffers that a second kernel adds in a fixed order
 // (deterministic).  The forward states are needed in reverse order: the
 // state at every 32-token chunk start comes from the forward prefill kernel
 // (snapshot mode), and inside a chunk the workgroup recomputes the 32 token
 // states into its own scratch area, then walks them backwards.
+//
+// Segments.  The gradient recurrence is linear in dS, as the forward one is
+// in S (dS_{t-1} = Diag(alpha) (I - beta k k^T) (dS_t + q do^T)), so the
+// sequences are cut into chunk-aligned segments that run side by side, as in
+// the context-parallel forward: a summary pass takes each segment but a
+// sequence's first from a zero gradient at its end to its start over 128
+// value columns plus 128 transition columns (identity at the end, do = 0),
+// giving [G^0 | R]; a reverse combine then gives the gradient entering every
+// segment at its end, G(last) = d(final_state), G(s-1) = R_s G(s) + G^0_s; and
+// the main pass runs every segment from there.
 #include "kda_device.hpp"
 
 namespace kda {
@@ -38,16 +48,104 @@ __device__ __forceinline__ float dot4(const f32x4 &a, const f32x4 &b) {
     return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-// part_vec: [NBLK][3][T_tot * H][BD] partial row sums (dq, dk, dg);
-// part_beta: [NBLK][T_tot * H]; scratch: [N * H * NBLK][BWD_C][BD][BWD_BV];
-// snaps: [chunks][H][BD][BD], the state at the start of global chunk
-// chunk_off[n] + c for c >= 1 (c = 0 is the initial state).
+// Segment summaries of the gradient recurrence: one workgroup per (segment,
+// head, block of 32 of the 128 + 128 columns), segments that are not a
+// sequence's first.  seg_out: [num_segs][H][BD][2 BD], [G^0 | R] per segment.
+template <typename T>
+__global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ plan,
+    int32_t num_segs, int32_t H, int32_t T_tot, float *__restrict__ seg_out)
+{
+    __shared__ float sq[BD], sk[BD], sa[BD];
+    __shared__ float sdo[BWD_BV], sx[BWD_BV];
+    __shared__ f32x4 red_x[BWD_RG][BWD_CPR];
+    constexpr int NB2 = 2 * BD / BWD_BV;
+    const int blk = blockIdx.x % NB2;
+    const int64_t unit = blockIdx.x / NB2;
+    if (unit >= (int64_t)num_segs * H) return;
+    const int su = (int)(unit / H), h = (int)(unit % H);
+    if (plan[4 * su] < 0 || (plan[4 * su + 3] & SEG_FIRST)) return;
+    const int ts = min(max(plan[4 * su + 1], 0), T_tot);
+    const int te = min(max(plan[4 * su + 2], ts), T_tot);
+    const int t = threadIdx.x;
+    const int cg = t % BWD_CPR, rg = t / BWD_CPR;
+    const bool trans = blk * BWD_BV >= BD;            // transition columns: identity at the end, do = 0
+    const int c4 = blk * BWD_BV + 4 * cg;             // column in [0, 2 BD)
+    f32x4 G[BWD_RPT];
+#pragma unroll
+    for (int i = 0; i < BWD_RPT; ++i) {
+        const int r = rg + BWD_RG * i;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) G[i][e] = (trans && r == c4 + e - BD) ? 1.f : 0.f;
+    }
+    // the next token's vectors are loaded one step ahead (clamped rows, so
+    // every load is issued on every path); tt >= ts >= 0 whenever the loop runs
+    float nk = 0.f, ng = 0.f, nq = 0.f, ndo = 0.f, nb = 0.f;
+    auto fetch = [&](int tt) {
+        const int64_t row = (int64_t)tt * H + h;
+        const int tc = min(t, BD - 1), vc = min(t, BWD_BV - 1);
+        nk = to_f(k[row * BD + tc]);
+        ng = g[row * BD + tc];
+        nq = to_f(q[row * BD + tc]);
+        ndo = to_f(dout[row * BD + blk % (BD / BWD_BV) * BWD_BV + vc]);
+        nb = beta[row];
+    };
+    if (te > ts) fetch(te - 1);
+    for (int tt = te - 1; tt >= ts; --tt) {
+        __syncthreads();                                   // token vectors free
+        if (t < BD) {
+            sk[t] = nk;
+            sa[t] = __expf(ng);
+            sq[t] = nq;
+        }
+        if (t < BWD_BV) sdo[t] = ndo;
+        const float bt = nb;
+        fetch(max(tt - 1, ts));
+        __syncthreads();
+        const f32x4 do4 = trans ? zero4() : *reinterpret_cast<const f32x4 *>(sdo + 4 * cg);
+        f32x4 px = zero4();
+#pragma unroll
+        for (int i = 0; i < BWD_RPT; ++i) {
+            const int r = rg + BWD_RG * i;
+            if (!trans) G[i] += sq[r] * do4;               // o = S^T q
+            px += G[i] * sk[r];                            // dS^T k
+        }
+        red_x[rg][cg] = px;
+        __syncthreads();
+        if (t < BWD_BV) {
+            float X = 0.f;
+            for (int r = 0; r < BWD_RG; ++r) X += red_x[r][t >> 2][t & 3];
+            sx[t] = X;
+        }
+        __syncthreads();
+        const f32x4 du4 = *reinterpret_cast<const f32x4 *>(sx + 4 * cg) * bt;
+#pragma unroll
+        for (int i = 0; i < BWD_RPT; ++i) {
+            const int r = rg + BWD_RG * i;
+            G[i] = (G[i] - sk[r] * du4) * sa[r];
+        }
+    }
+    float *dst = seg_out + ((int64_t)su * H + h) * BD * (2 * BD);
+#pragma unroll
+    for (int i = 0; i < BWD_RPT; ++i)
+        *reinterpret_cast<f32x4 *>(dst + (int64_t)(rg + BWD_RG * i) * (2 * BD) + c4) = G[i];
+}
+
+// Work items (segment su, head h, column block blk) in the order
+// item = (su H + h) NBLK + blk, walked with a stride of the grid (the scratch
+// area belongs to the workgroup, not the item).  seg_dsend: [num_segs][H][BD][BD],
+// the gradient entering each segment at its end.  part_vec: [NBLK][3][T_tot * H][BD]
+// partial row sums (dq, dk, dg); part_beta: [NBLK][T_tot * H]; scratch:
+// [gridDim.x][BWD_C][BD][BWD_BV]; snaps: [chunks][H][BD][BD], the state at the
+// start of global chunk chunk_off[n] + c for c >= 1 (c = 0 is the initial state).
 template <typename T>
 __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *initial_state,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, const float *__restrict__ snaps,
-    const T *__restrict__ dout, const float *dfinal, int32_t H, int32_t T_tot,
+    const T *__restrict__ dout, const int32_t *__restrict__ plan, int32_t num_segs,
+    const float *__restrict__ seg_dsend, int32_t H, int32_t T_tot,
     float *__restrict__ scratch, float *__restrict__ part_vec, float *__restrict__ part_beta,
     float *__restrict__ dv_out, float *dinit)
 {
@@ -55,30 +153,39 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     __shared__ float sv[BWD_BV], sdo[BWD_BV], su[BWD_BV], sx[BWD_BV];
     __shared__ f32x4 red_a[BWD_RG][BWD_CPR], red_x[BWD_RG][BWD_CPR];
 
-    const int blk = blockIdx.x % BWD_NBLK;
-    const int64_t unit = blockIdx.x / BWD_NBLK;
-    const int n = (int)(unit / H), h = (int)(unit % H);
     const int t = threadIdx.x;
     const int cg = t % BWD_CPR, rg = t / BWD_CPR;
-    const int dv0 = blk * BWD_BV, c4 = dv0 + 4 * cg;
-    const int t0 = min(max(cu[n], 0), T_tot);
-    const int t1 = min(max(cu[n + 1], t0), T_tot);
-    const int nch = (t1 - t0 + BWD_C - 1) / BWD_C;
-    const int64_t sbase = unit * BD * BD;              // this (sequence, head) in [N, H, BD, BD]
     const int64_t rows_all = (int64_t)T_tot * H;
-    float *scr = scratch + ((int64_t)unit * BWD_NBLK + blk) * BWD_C * BD * BWD_BV;
+    float *scr = scratch + (int64_t)blockIdx.x * BWD_C * BD * BWD_BV;
+    const int64_t items = (int64_t)num_segs * H * BWD_NBLK;
+
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int blk = (int)(item % BWD_NBLK);
+    const int64_t unit = item / BWD_NBLK;                 // (segment, head)
+    const int sg = (int)(unit / H), h = (int)(unit % H);
+    const int n = plan[4 * sg];
+    if (n < 0) continue;                                  // unused plan entry (uniform per workgroup)
+    const int flags = plan[4 * sg + 3];
+    const int dv0 = blk * BWD_BV, c4 = dv0 + 4 * cg;
+    const int t0 = min(max(cu[n], 0), T_tot);             // the sequence
+    const int ts = min(max(plan[4 * sg + 1], t0), T_tot); // the segment: [ts, te), chunk-aligned in the sequence
+    const int te = min(max(plan[4 * sg + 2], ts), T_tot);
+    const int nch = (te - ts + BWD_C - 1) / BWD_C;
+    const int64_t sbase = ((int64_t)n * H + h) * BD * BD;   // this (sequence, head) in [N, H, BD, BD]
+    const float *gin = seg_dsend + unit * BD * BD;
 
     f32x4 S[BWD_RPT], dS[BWD_RPT], Sp[BWD_RPT];
 #pragma unroll
     for (int i = 0; i < BWD_RPT; ++i) {
         const int r = rg + BWD_RG * i;
-        dS[i] = dfinal ? *reinterpret_cast<const f32x4 *>(dfinal + sbase + (int64_t)r * BD + c4) : zero4();
+        dS[i] = *reinterpret_cast<const f32x4 *>(gin + (int64_t)r * BD + c4);
     }
 
     for (int c = nch - 1; c >= 0; --c) {
-        const int c0 = t0 + c * BWD_C, Lc = min(BWD_C, t1 - c0);
-        const float *src = c ? snaps + ((int64_t)(chunk_off[n] + c) * H + h) * BD * BD
-                             : (initial_state ? initial_state + sbase : nullptr);
+        const int c0 = ts + c * BWD_C, Lc = min(BWD_C, te - c0);
+        const int cs = (c0 - t0) / BWD_C;                 // chunk index within the sequence
+        const float *src = cs ? snaps + ((int64_t)(chunk_off[n] + cs) * H + h) * BD * BD
+                              : (initial_state ? initial_state + sbase : nullptr);
 #pragma unroll
         for (int i = 0; i < BWD_RPT; ++i) {
             const int r = rg + BWD_RG * i;
@@ -86,19 +193,32 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
         }
 
         // ---- forward inside the chunk: scr[j] = state before token c0 + j
-        for (int j = 0; j < Lc; ++j) {
+        // token vectors one step ahead, clamped rows (loads on every path)
+        const int tc = min(t, BD - 1), vc = min(t, BWD_BV - 1);
+        float nk, ng, nq, nv, ndo, nb;
+        auto fetch = [&](int j) {
             const int64_t row = (int64_t)(c0 + j) * H + h;
+            nk = to_f(k[row * BD + tc]);
+            ng = g[row * BD + tc];
+            nq = to_f(q[row * BD + tc]);
+            nv = to_f(v[row * BD + dv0 + vc]);
+            ndo = to_f(dout[row * BD + dv0 + vc]);
+            nb = beta[row];
+        };
+        fetch(0);
+        for (int j = 0; j < Lc; ++j) {
 #pragma unroll
             for (int i = 0; i < BWD_RPT; ++i)
                 *reinterpret_cast<f32x4 *>(scr + ((int64_t)j * BD + rg + BWD_RG * i) * BWD_BV + 4 * cg) = S[i];
             __syncthreads();                                   // token vectors free
             if (t < BD) {
-                sk[t] = to_f(k[row * BD + t]);
-                sa[t] = __expf(g[row * BD + t]);
+                sk[t] = nk;
+                sa[t] = __expf(ng);
             }
-            if (t < BWD_BV) sv[t] = to_f(v[row * BD + dv0 + t]);
+            if (t < BWD_BV) sv[t] = nv;
+            const float bt = nb;
+            fetch(min(j + 1, Lc - 1));
             __syncthreads();
-            const float bt = beta[row];
             f32x4 pa = zero4();
 #pragma unroll
             for (int i = 0; i < BWD_RPT; ++i) {
@@ -120,23 +240,32 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
         }
 
         // ---- reverse over the chunk's tokens
+        fetch(Lc - 1);
+        f32x4 nSp[BWD_RPT];
+        auto fetch_sp = [&](int j) {
+#pragma unroll
+            for (int i = 0; i < BWD_RPT; ++i)
+                nSp[i] = *reinterpret_cast<const f32x4 *>(scr + ((int64_t)j * BD + rg + BWD_RG * i) * BWD_BV + 4 * cg);
+        };
+        fetch_sp(Lc - 1);                                      // this thread's own stores: in order
         for (int j = Lc - 1; j >= 0; --j) {
             const int64_t row = (int64_t)(c0 + j) * H + h;
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i)
-                Sp[i] = *reinterpret_cast<const f32x4 *>(scr + ((int64_t)j * BD + rg + BWD_RG * i) * BWD_BV + 4 * cg);
+            for (int i = 0; i < BWD_RPT; ++i) Sp[i] = nSp[i];
             __syncthreads();
             if (t < BD) {
-                sq[t] = to_f(q[row * BD + t]);
-                sk[t] = to_f(k[row * BD + t]);
-                sa[t] = __expf(g[row * BD + t]);
+                sq[t] = nq;
+                sk[t] = nk;
+                sa[t] = __expf(ng);
             }
             if (t < BWD_BV) {
-                sv[t] = to_f(v[row * BD + dv0 + t]);
-                sdo[t] = to_f(dout[row * BD + dv0 + t]);
+                sv[t] = nv;
+                sdo[t] = ndo;
             }
+            const float bt = nb;
+            fetch(max(j - 1, 0));
+            fetch_sp(max(j - 1, 0));
             __syncthreads();
-            const float bt = beta[row];
             const f32x4 do4 = *reinterpret_cast<const f32x4 *>(sdo + 4 * cg);
             f32x4 pa = zero4(), px = zero4();
 #pragma unroll
@@ -198,13 +327,15 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
         }
     }
 
-    if (dinit) {
+    if (dinit && (flags & SEG_FIRST)) {
 #pragma unroll
         for (int i = 0; i < BWD_RPT; ++i) {
             const int r = rg + BWD_RG * i;
             *reinterpret_cast<f32x4 *>(dinit + sbase + (int64_t)r * BD + c4) = dS[i];
         }
     }
+    __syncthreads();                                      // the next item reuses the token vectors
+  }
 }
 
 // Sum of the per-block partials in block order: dq, dk, dg [rows][BD], dbeta [rows].
@@ -244,32 +375,56 @@ __global__ __launch_bounds__(256) void kda_backward_reduce_kernel(
 
 }  // namespace kda
 
-extern "C" size_t kda_backward_scratch_floats_per_unit() { return (size_t)kda::BWD_NBLK * kda::BWD_C * kda::BD * kda::BWD_BV; }
+// Scratch floats per workgroup of the main pass, and the most workgroups it
+// launches (the item loop covers the rest): 512 x 512 KB of scratch at most.
+extern "C" size_t kda_backward_scratch_floats_per_wg() { return (size_t)kda::BWD_C * kda::BD * kda::BWD_BV; }
+extern "C" int32_t kda_backward_max_wgs() { return 512; }
 extern "C" int32_t kda_backward_num_blocks() { return kda::BWD_NBLK; }
+
+extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
+                                                  const float *beta, const void *dout, const int32_t *plan,
+                                                  int32_t num_segs, int32_t T_tot, int32_t H, float *seg_out,
+                                                  hipStream_t stream)
+{
+    using namespace kda;
+    const int64_t grid = (int64_t)num_segs * H * (2 * BD / BWD_BV);
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (bf16)
+        hipLaunchKernelGGL(kda_backward_summary_kernel<bf16_t>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), g, beta,
+                           static_cast<const bf16_t *>(dout), plan, num_segs, H, T_tot, seg_out);
+    else
+        hipLaunchKernelGGL(kda_backward_summary_kernel<float>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
+                           static_cast<const float *>(q), static_cast<const float *>(k), g, beta,
+                           static_cast<const float *>(dout), plan, num_segs, H, T_tot, seg_out);
+    return hipGetLastError();
+}
 
 extern "C" hipError_t kda_launch_backward(int bf16, const void *q, const void *k, const void *v, const float *g,
                                           const float *beta, const float *init, const int32_t *cu,
                                           const int32_t *chunk_off, const float *snaps, const void *dout,
-                                          const float *dfinal, int32_t N, int32_t T_tot, int32_t H, float *scratch,
+                                          const int32_t *plan, int32_t num_segs, const float *seg_dsend,
+                                          int32_t N, int32_t T_tot, int32_t H, float *scratch,
                                           float *part_vec, float *part_beta, float *dq, float *dk, float *dv,
                                           float *dg, float *dbeta, float *dinit, hipStream_t stream)
 {
     using namespace kda;
-    const int64_t grid = (int64_t)N * H * BWD_NBLK;
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const int64_t items = (int64_t)num_segs * H * BWD_NBLK;
+    if (items <= 0) return hipSuccess;
+    const int64_t grid = min(items, (int64_t)kda_backward_max_wgs());
     if (bf16)
         hipLaunchKernelGGL(kda_backward_kernel<bf16_t>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
                            static_cast<const bf16_t *>(v), g, beta, init, cu, chunk_off, snaps,
-                           static_cast<const bf16_t *>(dout), dfinal, H, T_tot, scratch, part_vec, part_beta, dv,
-                           dinit);
+                           static_cast<const bf16_t *>(dout), plan, num_segs, seg_dsend, H, T_tot, scratch,
+                           part_vec, part_beta, dv, dinit);
     else
         hipLaunchKernelGGL(kda_backward_kernel<float>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
                            static_cast<const float *>(q), static_cast<const float *>(k),
                            static_cast<const float *>(v), g, beta, init, cu, chunk_off, snaps,
-                           static_cast<const float *>(dout), dfinal, H, T_tot, scratch, part_vec, part_beta, dv,
-                           dinit);
+                           static_cast<const float *>(dout), plan, num_segs, seg_dsend, H, T_tot, scratch,
+                           part_vec, part_beta, dv, dinit);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t rows_all = (int64_t)T_tot * H;

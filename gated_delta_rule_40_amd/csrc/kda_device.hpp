@@ -181,6 +181,10 @@ __device__ __forceinline__ void store_pair(T *p, float a, float b) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Flags of a segment-plan entry {sequence, t0, t1, flags}: the sequence's
+// first and last segment.
+enum { SEG_FIRST = 1, SEG_LAST = 2 };
+
 // Exact power-of-two scale that maps a magnitude m into [2^13, 2^14):
 // returns 2^(13 - floor(log2 m)) for finite normal m > 0, else 1.  Used to
 // keep fp16 MFMA operands in range without changing their relative rounding.

@@ -141,7 +141,6 @@ struct PrefillCfg {
 // entering state (seg_init) and writes outputs and, for a last segment, the
 // final state.
 enum { SEG_OUTPUT = 0, SEG_SUMMARY = 1 };
-enum { SEG_FIRST = 1, SEG_LAST = 2 };
 struct SegArgs {
     const int32_t *plan;     // [num_segs][4] or nullptr (one unit per sequence)
     int32_t num_segs;
@@ -1109,7 +1108,10 @@ struct ChainCfg {
     static constexpr int OVEC = C * 16 * NCT / VEC;                 // vectors of one wave's output tile
 };
 
-template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB>
+// SNAP (outputs only): also store the state after every chunk that is not its
+// sequence's last, as the state at the start of the next chunk, at that
+// chunk's global index in seg.snap ([chunks][H][DK][dv]); out may be NULL.
+template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
@@ -1257,7 +1259,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
             reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
             reinterpret_cast<const TIn *>(base + Q::offV), 16 * NCT * wave + lm, sOw, lm, lj, lm);
-        if constexpr (!SUMMARY) {
+        if (!SUMMARY && (!SNAP || out)) {
             // this wave's 16 output columns: rows of 16 * sizeof(TIn) bytes, one
             // 16-byte vector per lane and step (LDS is in order within a wave).
             // Every lane stores on every path -- rows past the end of the
@@ -1273,6 +1275,21 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
                     *reinterpret_cast<const f32x4 *>(sOw + r * 16 * NCT + cv);
             }
             __asm__ volatile("" ::: "memory");
+        }
+        if constexpr (SNAP) {
+            const int64_t gc = gc0 + ci + 1;            // the sequence's next chunk
+            if (gc < (int64_t)seg.chunk_off[n + 1]) {
+                float *dst = seg.snap + (gc * num_heads + h) * DK * dv;
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const float inv = pow2_inv(sS[ct]);
+#pragma unroll
+                    for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            dst[(int64_t)(16 * r + 4 * lj + i) * dv + colc[ct]] = S[ct][r][i] * inv;
+                }
+            }
         }
         if constexpr (SB) __syncthreads();       // every wave is done with the buffer
         stage(min(ci + 1, nch - 1), SB ? 0 : (ci + 1) & 1);
@@ -1327,13 +1344,16 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
 {
     typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
     const bool summary = seg.mode == SEG_SUMMARY;
-    auto kern = summary ? kda_chain_kernel<TIn, C, NW, NCT, true, SB> : kda_chain_kernel<TIn, C, NW, NCT, false, SB>;
-    static bool attr_set[2] = {false, false};   // idempotent; racing threads set the same value
-    if (!attr_set[summary]) {
+    const int kind = summary ? 1 : (seg.snap ? 2 : 0);
+    auto kern = kind == 1 ? kda_chain_kernel<TIn, C, NW, NCT, true, SB>
+                          : (kind == 2 ? kda_chain_kernel<TIn, C, NW, NCT, false, SB, true>
+                                       : kda_chain_kernel<TIn, C, NW, NCT, false, SB>);
+    static bool attr_set[3] = {false, false, false};   // idempotent; racing threads set the same value
+    if (!attr_set[kind]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::bytes);
         if (e != hipSuccess) return e;
-        attr_set[summary] = true;
+        attr_set[kind] = true;
     }
     const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
     const int nblk = (summary ? dv + DK : dv) / Q::BV;
@@ -1444,12 +1464,14 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 // S_in(first) = initial state, S_in(s+1) = M_s S_in(s) + S_s^0 on fp32 MFMA,
 // writing each segment's entering state.  The state slice lives in MFMA
 // accumulator registers (row tiles as in the prefill kernel); M is read
-// straight from global memory as A operands.
+// straight from global memory as A operands.  reverse: the same combination
+// walked from the last segment to the first (gradients of the state, which
+// enter a segment at its end): G(last) = init, G(s-1) = R_s G(s) + G_s^0.
 __global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
                                                              int32_t H, int32_t dv,
                                                              const int32_t *__restrict__ seq_seg,
                                                              const float *__restrict__ seg_out,
-                                                             float *__restrict__ seg_init)
+                                                             float *__restrict__ seg_init, int32_t reverse)
 {
     typedef Mma<float> M;
     const int nblk = dv / 64;
@@ -1466,13 +1488,14 @@ __global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__rest
         for (int i = 0; i < 4; ++i)
             S[r][i] = init ? init[((int64_t)n * H + h) * DK * dv + (int64_t)(16 * r + 4 * lj + i) * dv + col] : 0.f;
     const int s0 = seq_seg[n], s1 = seq_seg[n + 1];
-    for (int gs = s0; gs < s1; ++gs) {
+    for (int it = 0; it < s1 - s0; ++it) {
+        const int gs = reverse ? s1 - 1 - it : s0 + it;
         float *dst = seg_init + ((int64_t)gs * H + h) * DK * dv;
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
-        if (gs == s1 - 1) break;
+        if (it == s1 - s0 - 1) break;
         const float *src = seg_out + ((int64_t)gs * H + h) * DK * ld;
         f32x4 Sn[DK / 16];
 #pragma unroll
@@ -1550,16 +1573,19 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, hipStream_t stream)
+                                       const int32_t *sched, float *snap, hipStream_t stream)
 {
     using namespace kda;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
-                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), nullptr, 0, 0, sched};
+                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), mode == SEG_SUMMARY ? nullptr : snap, 0, 0,
+                   sched};
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
     // fragment; the second workgroup covers the waits of the first); fp32
     // images are twice as large and their buffers fit the LDS at 64 columns only
+    // with state stores: 64 columns per workgroup (the two-tile form has no registers left for them)
+    if (bf16 && seg.snap) return launch_chain_t<bf16_t, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (bf16 && dv_block == 256) return launch_chain_t<bf16_t, 32, 8, 2>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (bf16 && dv_block == 128) return launch_chain_t<bf16_t, 32, 4, 2, true>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (dv_block != 64 && dv_block != 128 && dv_block != 256) return hipErrorInvalidValue;
@@ -1574,12 +1600,12 @@ extern "C" size_t kda_chunk_image_bytes(int bf16)
 
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
-                                            hipStream_t stream)
+                                            int32_t reverse, hipStream_t stream)
 {
     const int64_t grid = (int64_t)N * H * (dv / 64);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, init, N, H, dv,
-                       seq_seg, seg_out, seg_init);
+                       seq_seg, seg_out, seg_init, reverse);
     return hipGetLastError();
 }

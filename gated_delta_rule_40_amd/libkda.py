@@ -72,7 +72,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_backward.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
                                  fp, fp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
     lib.kda_backward.restype = ctypes.c_int
-    lib.kda_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.kda_backward_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int]
     lib.kda_backward_workspace_size.restype = ctypes.c_size_t
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -240,8 +240,12 @@ def kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, ou
                                  _dtype_code(q), _ptr(out), _stream(stream)))
 
 
-def kda_backward_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int) -> int:
-    return int(load().kda_backward_workspace_size(num_seqs, total_tokens, num_heads, dk, dv))
+def kda_backward_workspace_size(num_seqs: int, total_tokens: int, num_heads: int, dk: int, dv: int,
+                                dtype=torch.bfloat16) -> int:
+    code = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32}.get(dtype)
+    if code is None:
+        raise TypeError("dtype must be torch.bfloat16 or torch.float32, got %s" % dtype)
+    return int(load().kda_backward_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code))
 
 
 def kda_backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None, grads=None, want_dinit=True,
@@ -259,7 +263,7 @@ def kda_backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None,
         f = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)
         grads = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
                  "dinit": f(N, H, dk, dv) if want_dinit else None}
-    need = kda_backward_workspace_size(N, T, H, dk, dv)
+    need = kda_backward_workspace_size(N, T, H, dk, dv, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     nbytes = workspace.numel() * workspace.element_size()

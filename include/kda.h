@@ -217,6 +217,10 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  * state) of a scalar loss L, the gradients with respect to q, k, v, g, beta
  * and the initial state, by the chain rule through the recurrence of card
  * "KDA 单头递归" (page ailearn.mscapital.top/kimi-k3.html) in reverse token order.
+ * Sequences are cut into segments that run side by side, as in
+ * kda_prefill_cp (card "传固定状态片段"): the gradient recurrence is linear in
+ * the state's gradient, so each segment's gradient summary combines, in reverse
+ * segment order, into the gradient entering every segment.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, dtype: as kda_prefill
  *   dout          [total_tokens, num_heads, dv]   dtype
@@ -226,15 +230,17 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  *   dbeta         [total_tokens, num_heads]       fp32, written
  *   dinit         [num_seqs, num_heads, dk, dv]   fp32, or NULL (not written)
  *   workspace     device memory of at least kda_backward_workspace_size(...)
- *                 bytes, 256-byte aligned, owned by the caller (the forward
- *                 states at every 32-token chunk start, per-workgroup scratch
- *                 and partial sums); calls sharing it must not overlap
+ *                 bytes (for the same sizes and dtype), 256-byte aligned, owned
+ *                 by the caller (segment plans, chunk images and the forward
+ *                 states at every 32-token chunk start, segment summaries,
+ *                 per-workgroup scratch and partial sums); calls sharing it
+ *                 must not overlap
  * Rows of tokens owned by a sequence are written; others are left untouched.
  * Gradients are fp32 whatever the input dtype.  Deterministic (fixed
  * summation order).
  */
 size_t kda_backward_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
-                                   int32_t dk, int32_t dv);
+                                   int32_t dk, int32_t dv, kda_dtype dtype);
 
 kda_status kda_backward(const void *q, const void *k, const void *v,
                         const float *g, const float *beta,

@@ -232,11 +232,13 @@ def backward(lib, **kw):
 
 def test_backward_workspace_size(lib):
     ws = lib.kda_backward_workspace_size
-    small = ws(1, 4096, 2, 128, 128)
+    small = ws(1, 4096, 2, 128, 128, K.KDA_BF16)
     # at least the chunk-start states: (4096 / 32 + 2) chunks x 2 heads x 64 KiB
     assert small >= 130 * 2 * 65536
-    assert ws(1, 8192, 2, 128, 128) > small and ws(2, 4096, 2, 128, 128) > small
-    assert ws(1, 4096, 2, 64, 128) == 0 and ws(-1, 4096, 2, 128, 128) == 0
+    assert ws(1, 8192, 2, 128, 128, K.KDA_BF16) > small and ws(2, 4096, 2, 128, 128, K.KDA_BF16) > small
+    assert ws(1, 4096, 2, 128, 128, K.KDA_F32) > small      # fp32 chunk images are larger
+    assert ws(1, 4096, 2, 64, 128, K.KDA_BF16) == 0 and ws(-1, 4096, 2, 128, 128, K.KDA_BF16) == 0
+    assert ws(1, 4096, 2, 128, 128, 7) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
