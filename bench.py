@@ -37,6 +37,14 @@ PREFILL_BYTES_PER_HT = 3 * 2 * DK + 4 * DK + 4 + 2 * DV
 PREFILL_FREF_PER_HT = 6 * DK * DV + 2 * 64 * (DK + DV)
 # decode bytes per (sequence, head): state read + write, q/k/v/out bf16, g fp32, beta fp32
 DECODE_BYTES_PER_UNIT = 2 * DK * DV * 4 + 3 * 2 * DK + 4 * DK + 4 + 2 * DV
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
+# backward, per head-token: q, k, v, dout in bf16, g fp32, beta in; dq, dk, dg,
+# dv fp32 and dbeta out
+BWD_BYTES_PER_HT = 4 * 2 * DK + 4 * DK + 4 + 4 * (3 * DK + DV) + 4
+# backward token form, flops per state element and token: recompute
+# (decay 1, S^T k 2, rank-1 update 2) + reverse (decay 1, S^T k 2, q do^T 2,
+# dS^T k 2, S do with the update 4, dk 4, dSbar 2, dg 2, decay 1) = 25
+BWD_FLOP_PER_HT = 25 * DK * DV
 PREFILL_KERNELS = {
     "cp": "kda_prefill_cp call: kda_cp_plan_kernel, kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
           "kda_chain_kernel<bf16,32,8 waves,2 tiles,summary>, kda_cp_combine_kernel, "
@@ -296,6 +304,8 @@ def main():
     b_ev[1].record(stream)
     torch.cuda.synchronize()
     bwd_ms = b_ev[0].elapsed_time(b_ev[1]) / 3
+    bwd_tflops = Tb * Hb * BWD_FLOP_PER_HT / (bwd_ms * 1e-3) / 1e12
+    bwd_bytes = Tb * Hb * BWD_BYTES_PER_HT + 3 * Hb * DK * DV * 4      # + initial state, dfinal, dinit
 
     result = {
         "metric": METRIC,
@@ -336,7 +346,14 @@ def main():
                                        "algorithmic_bytes_per_launch": rep_bytes}},
         "backward": {"workload": "prefill_t4096_h8", "ms_per_call": bwd_ms, "tokens_per_s": Tb / (bwd_ms * 1e-3),
                      "head_tokens_per_s": Tb * Hb / (bwd_ms * 1e-3),
-                     "kernels": "forward with chunk-start states, kda_backward_kernel<bf16>, kda_backward_reduce_kernel"},
+                     "roofline": {"bound": "alu", "achieved": bwd_tflops, "peak": FP32_VALU_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": bwd_tflops / FP32_VALU_PEAK_TFLOPS,
+                                  "flop_per_head_token": BWD_FLOP_PER_HT,
+                                  "hbm_achieved_gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
+                                  "algorithmic_bytes_per_launch": bwd_bytes},
+                     "kernels": "kda_cp_plan_kernel x2, chunk operands, kda_chain_kernel summary and output with "
+                                "state stores, kda_cp_combine_kernel x2, kda_backward_summary_kernel<bf16>, "
+                                "kda_backward_kernel<bf16>, kda_backward_reduce_kernel"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
