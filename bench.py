@@ -74,15 +74,20 @@ def pmc_traffic():
 
 
 def _pmc_rows(path):
-    """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3 counter CSV."""
+    """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3 counter
+    CSV, for the timed steps only: the dispatches before the first replay
+    kernel (the replay and backward measurements, which follow the steps, reuse
+    some of the prefill kernels)."""
     import csv
     rows = {}
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
-            d = r["Dispatch_Id"]
+            d = int(r["Dispatch_Id"])
             name, val = rows.get(d, (r["Kernel_Name"], 0.0))
             rows[d] = (name, val + float(r["Counter_Value"]))
-    return rows
+    first_extra = min((d for d, (n, _) in rows.items() if "kda_decode_tokens_kernel" in n), default=None)
+    return {d: v for d, v in rows.items()
+            if first_extra is None or d < first_extra or "kda" not in v[0]}
 
 
 def write_traffic(fetch_csv, write_csv):
@@ -105,9 +110,10 @@ def write_traffic(fetch_csv, write_csv):
         # kernel also serves the backward, so each kind is averaged on its own)
         kinds = {"plan": lambda n: "kda_cp_plan_kernel" in n,
                  "chunk_operands": lambda n: "kda_prefill_kernel" in n and "Li1EEE" in n,
-                 "summaries": lambda n: "kda_chain_kernel" in n and "Lb1ELb" in n,
+                 # kda_chain_kernel<TIn, C, NW, NCT, SUMMARY, SB, SNAP>: the 5th argument
+                 "summaries": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "1",
                  "combine": lambda n: "kda_cp_combine_kernel" in n,
-                 "outputs": lambda n: "kda_chain_kernel" in n and "Lb0ELb" in n}
+                 "outputs": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "0"}
         per_kind = {}
         for kind, match in kinds.items():
             vals = [v for n, v in rows.values() if match(n)]
@@ -148,7 +154,18 @@ def cpu_baseline(pre, H, target_s=20.0):
     O.build()
     t, tok = run(2048)                     # calibration (long enough that setup does not dominate)
     rate = tok / max(t, 1e-6)
-    Ls = int(max(2048, min(rate * target_s / N, max(cu[n + 1] - cu[n] for n in range(N)))))
+    # the sample's tokens are sum_n min(Ls, L_n): the smallest Ls that reaches
+    # rate * target_s (or the whole input)
+    lens = [cu[n + 1] - cu[n] for n in range(N)]
+    want = rate * target_s
+    lo, hi = 2048, max(max(lens), 2048)
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if sum(min(mid, L) for L in lens) >= want:
+            hi = mid
+        else:
+            lo = mid + 1
+    Ls = lo
     t, tok = run(Ls)
     return {"value": tok / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": "first %d tokens of each of the %d sequences x %d heads of the same prefill inputs "
