@@ -871,6 +871,15 @@ void kda_prefill_kernel(
             prep_fast(std::true_type());
         else
             prep_fast(std::false_type());
+        // chunk-operand pass: the staged registers are free once the decayed
+        // operands are written, so the next chunk's loads go out here and
+        // stay in flight through the Gram, the inverse and the image store
+        // (the fused kernel still needs its value registers until phase 3)
+        if constexpr (kPrep) {
+            int n0, n1;
+            chunk_range(min(ci + 1, nch - 1), n0, n1);
+            load_chunk(n0, n1);
+        }
         __syncthreads();
 
         // ---- 2. Gram tiles
@@ -897,7 +906,7 @@ void kda_prefill_kernel(
         }
         // unconditional (the last chunk re-reads itself): a conditional load
         // would make the compiler wait for it right away
-        {
+        if constexpr (!kPrep) {
             int n0, n1;
             chunk_range(min(ci + 1, nch - 1), n0, n1);
             load_chunk(n0, n1);
