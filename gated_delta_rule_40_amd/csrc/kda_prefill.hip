@@ -1471,11 +1471,16 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 // ------------------------------------------------------ segment combination
 // Per (sequence, head, 64 value columns): walk the segments in order,
 // S_in(first) = initial state, S_in(s+1) = M_s S_in(s) + S_s^0 on fp32 MFMA,
-// writing each segment's entering state.  The state slice lives in MFMA
-// accumulator registers (row tiles as in the prefill kernel); M is read
-// straight from global memory as A operands.  reverse: the same combination
-// walked from the last segment to the first (gradients of the state, which
-// enter a segment at its end): G(last) = init, G(s-1) = R_s G(s) + G_s^0.
+// writing each segment's entering state.  One workgroup of four waves per
+// (sequence, head, 64 columns); the state slice lives in MFMA accumulator
+// registers (row tiles as in the prefill kernel).  Per step the workgroup
+// stages M in LDS (every wave reads all of it as A operands) and loads the
+// next step's M and S^0 into registers while it multiplies.  reverse: the
+// same combination walked from the last segment to the first (gradients of
+// the state, which enter a segment at its end): G(last) = init,
+// G(s-1) = R_s G(s) + G_s^0.
+constexpr int CMB_LDM = DK + 4;                            // padded LDS row of M (fp32)
+constexpr uint32_t CMB_BYTES = sizeof(float) * DK * CMB_LDM;
 __global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
                                                              int32_t H, int32_t dv,
                                                              const int32_t *__restrict__ seq_seg,
@@ -1483,6 +1488,8 @@ __global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__rest
                                                              float *__restrict__ seg_init, int32_t reverse)
 {
     typedef Mma<float> M;
+    extern __shared__ __align__(16) unsigned char smem[];
+    float *sM = reinterpret_cast<float *>(smem);
     const int nblk = dv / 64;
     const int64_t unit = blockIdx.x / nblk;
     if (unit >= (int64_t)N * H) return;
@@ -1496,22 +1503,44 @@ __global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__rest
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[r][i] = init ? init[((int64_t)n * H + h) * DK * dv + (int64_t)(16 * r + 4 * lj + i) * dv + col] : 0.f;
-    const int s0 = seq_seg[n], s1 = seq_seg[n + 1];
-    for (int it = 0; it < s1 - s0; ++it) {
-        const int gs = reverse ? s1 - 1 - it : s0 + it;
+    const int s0 = seq_seg[n], s1 = seq_seg[n + 1], ns = s1 - s0;
+    auto seg_of = [&](int it) { return reverse ? s1 - 1 - it : s0 + it; };
+
+    // register copies of one step's operands: M rows tid / 32 + 8 it, columns
+    // 4 (tid % 32) .. +3; S^0 in accumulator layout
+    constexpr int MIT = DK * DK / 4 / 256;
+    f32x4 rM[MIT], rS0[DK / 16];
+    auto fetch = [&](int gs) {
+        const float *src = seg_out + ((int64_t)gs * H + h) * DK * ld;
+#pragma unroll
+        for (int it = 0; it < MIT; ++it)
+            rM[it] = *reinterpret_cast<const f32x4 *>(src + (int64_t)(tid / 32 + 8 * it) * ld + dv + 4 * (tid % 32));
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rS0[r][i] = src[(int64_t)(16 * r + 4 * lj + i) * ld + col];
+    };
+    if (ns > 1) fetch(seg_of(0));
+    for (int it = 0; it < ns; ++it) {
+        const int gs = seg_of(it);
         float *dst = seg_init + ((int64_t)gs * H + h) * DK * dv;
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
-        if (it == s1 - s0 - 1) break;
-        const float *src = seg_out + ((int64_t)gs * H + h) * DK * ld;
+        if (it == ns - 1) break;
+        __syncthreads();                                   // the previous step's reads of sM are done
+#pragma unroll
+        for (int k = 0; k < MIT; ++k)
+            *reinterpret_cast<f32x4 *>(sM + (tid / 32 + 8 * k) * CMB_LDM + 4 * (tid % 32)) = rM[k];
         f32x4 Sn[DK / 16];
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r) {
+        for (int r = 0; r < DK / 16; ++r) Sn[r] = rS0[r];
+        __syncthreads();
+        fetch(seg_of(min(it + 1, ns - 2)));                // next step (the last step re-reads itself)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Sn[r][i] = src[(int64_t)(16 * r + 4 * lj + i) * ld + col];   // S^0
-            const float *mrow = src + (int64_t)(16 * r + lm) * ld + dv;                              // M row
+        for (int r = 0; r < DK / 16; ++r) {
+            const float *mrow = sM + (16 * r + lm) * CMB_LDM;
 #pragma unroll
             for (int kb = 0; kb < DK / 16; ++kb)
                 Sn[r] = M::mma(*reinterpret_cast<const f32x4 *>(mrow + 16 * kb + 4 * lj), S[kb], Sn[r]);
@@ -1614,7 +1643,14 @@ extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_
     const int64_t grid = (int64_t)N * H * (dv / 64);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, init, N, H, dv,
-                       seq_seg, seg_out, seg_init, reverse);
+    static bool attr_set = false;   // idempotent; racing threads set the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kda::kda_cp_combine_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kda::CMB_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(256), kda::CMB_BYTES, stream, init, N,
+                       H, dv, seq_seg, seg_out, seg_init, reverse);
     return hipGetLastError();
 }
