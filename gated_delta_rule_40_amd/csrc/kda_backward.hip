@@ -48,18 +48,37 @@ __device__ __forceinline__ float dot4(const f32x4 &a, const f32x4 &b) {
     return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
+// ---- wave-level layout.  A wave owns 8 columns: lane = rg + 16 cg holds rows
+// rg + 16 i (i = 0..7) of columns 2 cg, 2 cg + 1.  A sum over the 128 rows
+// is a sum over the 16 lanes of a DPP row (symmetric exchanges, so every lane
+// ends with the same value); a sum over the wave's columns is a sum over its
+// four DPP rows.  Token vectors go through a wave-private LDS area with
+// channel c at (c mod 16) 8 + c / 16, so that a lane's 8 rows are contiguous.
+__device__ __forceinline__ float sum16(float x) {       // over the 16 lanes of each DPP row
+    x += dpp_mov<0xB1>(x);                             // quad_perm(1,0,3,2): lane ^ 1
+    x += dpp_mov<0x4E>(x);                             // quad_perm(2,3,0,1): lane ^ 2
+    x += dpp_mov<0x141>(x);                            // row_half_mirror: lane ^ 7 within 8
+    return x + dpp_mov<0x140>(x);                      // row_mirror: lane ^ 15 within 16
+}
+__device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ int chan_pos(int c) { return (c & 15) * 8 + (c >> 4); }
+
 // Segment summaries of the gradient recurrence: one workgroup per (segment,
 // head, block of 32 of the 128 + 128 columns), segments that are not a
-// sequence's first.  seg_out: [num_segs][H][BD][2 BD], [G^0 | R] per segment.
+// sequence's first; each wave runs its 8 columns on its own (no barrier).
+// seg_out: [num_segs][H][BD][2 BD], [G^0 | R] per segment.
 template <typename T>
 __global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ plan,
     int32_t num_segs, int32_t H, int32_t T_tot, float *__restrict__ seg_out)
 {
-    __shared__ float sq[BD], sk[BD], sa[BD];
-    __shared__ float sdo[BWD_BV], sx[BWD_BV];
-    __shared__ f32x4 red_x[BWD_RG][BWD_CPR];
+    __shared__ __align__(16) float sv[BWD_THREADS / 64][3][BD];   // per wave: k, alpha, q
     constexpr int NB2 = 2 * BD / BWD_BV;
     const int blk = blockIdx.x % NB2;
     const int64_t unit = blockIdx.x / NB2;
@@ -68,68 +87,70 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
     if (plan[4 * su] < 0 || (plan[4 * su + 3] & SEG_FIRST)) return;
     const int ts = min(max(plan[4 * su + 1], 0), T_tot);
     const int te = min(max(plan[4 * su + 2], ts), T_tot);
-    const int t = threadIdx.x;
-    const int cg = t % BWD_CPR, rg = t / BWD_CPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rg = lane & 15, cg = lane >> 4;
+    const int c0 = blk * BWD_BV + 8 * wave + 2 * cg;   // this lane's columns c0, c0 + 1 in [0, 2 BD)
     const bool trans = blk * BWD_BV >= BD;            // transition columns: identity at the end, do = 0
-    const int c4 = blk * BWD_BV + 4 * cg;             // column in [0, 2 BD)
-    f32x4 G[BWD_RPT];
+    float (*w)[BD] = sv[wave];
+    f32x2 G[8];
 #pragma unroll
-    for (int i = 0; i < BWD_RPT; ++i) {
-        const int r = rg + BWD_RG * i;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) G[i][e] = (trans && r == c4 + e - BD) ? 1.f : 0.f;
+    for (int i = 0; i < 8; ++i) {
+        const int r = rg + 16 * i;
+        G[i][0] = (trans && r == c0 - BD) ? 1.f : 0.f;
+        G[i][1] = (trans && r == c0 + 1 - BD) ? 1.f : 0.f;
     }
-    // the next token's vectors are loaded one step ahead (clamped rows, so
-    // every load is issued on every path); tt >= ts >= 0 whenever the loop runs
-    float nk = 0.f, ng = 0.f, nq = 0.f, ndo = 0.f, nb = 0.f;
+    // the next token's vectors, one step ahead: channels 2 lane, 2 lane + 1 of
+    // k, g, q, and this lane's two columns of dout (clamped rows: loads on every path)
+    f32x2 nk, ng, nq, ndo;
+    float nb;
     auto fetch = [&](int tt) {
         const int64_t row = (int64_t)tt * H + h;
-        const int tc = min(t, BD - 1), vc = min(t, BWD_BV - 1);
-        nk = to_f(k[row * BD + tc]);
-        ng = g[row * BD + tc];
-        nq = to_f(q[row * BD + tc]);
-        ndo = to_f(dout[row * BD + blk % (BD / BWD_BV) * BWD_BV + vc]);
+        nk = load_pair(k + row * BD + 2 * lane);
+        ng = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
+        nq = load_pair(q + row * BD + 2 * lane);
+        ndo = load_pair(dout + row * BD + (c0 & (BD - 1)));
         nb = beta[row];
     };
     if (te > ts) fetch(te - 1);
     for (int tt = te - 1; tt >= ts; --tt) {
-        __syncthreads();                                   // token vectors free
-        if (t < BD) {
-            sk[t] = nk;
-            sa[t] = __expf(ng);
-            sq[t] = nq;
-        }
-        if (t < BWD_BV) sdo[t] = ndo;
+        const f32x2 kk = nk, gg = ng, qq = nq, dd = trans ? f32x2{0.f, 0.f} : ndo;
         const float bt = nb;
         fetch(max(tt - 1, ts));
-        __syncthreads();
-        const f32x4 do4 = trans ? zero4() : *reinterpret_cast<const f32x4 *>(sdo + 4 * cg);
-        f32x4 px = zero4();
+        // wave-private LDS: written and read by this wave only, in order
+        w[0][chan_pos(2 * lane)] = kk[0];
+        w[0][chan_pos(2 * lane + 1)] = kk[1];
+        w[1][chan_pos(2 * lane)] = __expf(gg[0]);
+        w[1][chan_pos(2 * lane + 1)] = __expf(gg[1]);
+        w[2][chan_pos(2 * lane)] = qq[0];
+        w[2][chan_pos(2 * lane + 1)] = qq[1];
+        __builtin_amdgcn_wave_barrier();
+        float kr[8], ar[8], qr[8];
+        *reinterpret_cast<f32x4 *>(kr) = *reinterpret_cast<const f32x4 *>(&w[0][8 * rg]);
+        *reinterpret_cast<f32x4 *>(kr + 4) = *reinterpret_cast<const f32x4 *>(&w[0][8 * rg + 4]);
+        *reinterpret_cast<f32x4 *>(ar) = *reinterpret_cast<const f32x4 *>(&w[1][8 * rg]);
+        *reinterpret_cast<f32x4 *>(ar + 4) = *reinterpret_cast<const f32x4 *>(&w[1][8 * rg + 4]);
+        *reinterpret_cast<f32x4 *>(qr) = *reinterpret_cast<const f32x4 *>(&w[2][8 * rg]);
+        *reinterpret_cast<f32x4 *>(qr + 4) = *reinterpret_cast<const f32x4 *>(&w[2][8 * rg + 4]);
+        __builtin_amdgcn_wave_barrier();
+        float px0 = 0.f, px1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < BWD_RPT; ++i) {
-            const int r = rg + BWD_RG * i;
-            if (!trans) G[i] += sq[r] * do4;               // o = S^T q
-            px += G[i] * sk[r];                            // dS^T k
+        for (int i = 0; i < 8; ++i) {
+            G[i][0] += qr[i] * dd[0];                   // o = S^T q
+            G[i][1] += qr[i] * dd[1];
+            px0 += G[i][0] * kr[i];                      // dS^T k
+            px1 += G[i][1] * kr[i];
         }
-        red_x[rg][cg] = px;
-        __syncthreads();
-        if (t < BWD_BV) {
-            float X = 0.f;
-            for (int r = 0; r < BWD_RG; ++r) X += red_x[r][t >> 2][t & 3];
-            sx[t] = X;
-        }
-        __syncthreads();
-        const f32x4 du4 = *reinterpret_cast<const f32x4 *>(sx + 4 * cg) * bt;
+        const float du0 = sum16(px0) * bt, du1 = sum16(px1) * bt;
 #pragma unroll
-        for (int i = 0; i < BWD_RPT; ++i) {
-            const int r = rg + BWD_RG * i;
-            G[i] = (G[i] - sk[r] * du4) * sa[r];
+        for (int i = 0; i < 8; ++i) {
+            G[i][0] = (G[i][0] - kr[i] * du0) * ar[i];
+            G[i][1] = (G[i][1] - kr[i] * du1) * ar[i];
         }
     }
     float *dst = seg_out + ((int64_t)su * H + h) * BD * (2 * BD);
 #pragma unroll
-    for (int i = 0; i < BWD_RPT; ++i)
-        *reinterpret_cast<f32x4 *>(dst + (int64_t)(rg + BWD_RG * i) * (2 * BD) + c4) = G[i];
+    for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<f32x2 *>(dst + (int64_t)(rg + 16 * i) * (2 * BD) + c0) = G[i];
 }
 
 // Work items (segment su, head h, column block blk) in the order
