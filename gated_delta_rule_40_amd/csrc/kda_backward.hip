@@ -158,8 +158,31 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
 // area belongs to the workgroup, not the item).  seg_dsend: [num_segs][H][BD][BD],
 // the gradient entering each segment at its end.  part_vec: [NBLK][3][T_tot * H][BD]
 // partial row sums (dq, dk, dg); part_beta: [NBLK][T_tot * H]; scratch:
-// [gridDim.x][BWD_C][BD][BWD_BV]; snaps: [chunks][H][BD][BD], the state at the
-// start of global chunk chunk_off[n] + c for c >= 1 (c = 0 is the initial state).
+// [gridDim.x][BWD_C / BWD_G][BD][BWD_BV] floats; snaps: [chunks][H][BD][BD], the
+// state at the start of global chunk chunk_off[n] + c for c >= 1 (c = 0 is the
+// initial state).
+//
+// Each wave runs its 8 columns on its own, in the wave-level layout above.  Per
+// chunk: a forward walk from the chunk's start state keeps u of every token (in
+// LDS) and the state before every 4th token (in the scratch area, each lane's own
+// values); then the chunk is walked backwards in groups of 4 tokens, whose 4
+// states are rebuilt in registers from the group's stored state and the kept u
+// (S = Diag(alpha) S + beta k u^T, no reduction).  A token's row sums (dq, dk, dg
+// over the wave's columns) are reduced across the wave's four DPP rows so that
+// each lane keeps 6 of the 3 x 128; after each group the four waves' sums meet in
+// LDS and the workgroup adds them in wave order and writes its partials.
+constexpr int BWD_G = 4;                  // tokens per reverse group (and per partial-sum batch)
+constexpr int BWD_RED = 3 * BD;           // row sums per token and wave
+
+__device__ __forceinline__ float perm32_sum(float a, float b) {   // lanes 0-31: a over lanes L, L+32; 32-63: b
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float perm16_sum(float a, float b) {   // even DPP rows: a over rows 2m, 2m+1; odd: b
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 template <typename T>
 __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
@@ -170,15 +193,34 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     float *__restrict__ scratch, float *__restrict__ part_vec, float *__restrict__ part_beta,
     float *__restrict__ dv_out, float *dinit)
 {
-    __shared__ float sq[BD], sk[BD], sa[BD];
-    __shared__ float sv[BWD_BV], sdo[BWD_BV], su[BWD_BV], sx[BWD_BV];
-    __shared__ f32x4 red_a[BWD_RG][BWD_CPR], red_x[BWD_RG][BWD_CPR];
+    typedef typename Pair<T>::type Raw2;
+    constexpr int NWV = BWD_THREADS / 64;
+    __shared__ __align__(16) float tv[NWV][BWD_G][3][BD];       // per wave: k, alpha, q of a group's tokens
+    __shared__ __align__(16) float su[NWV][BWD_C][8];            // per wave: u of the chunk's tokens
+    __shared__ __align__(16) float red[NWV][BWD_G * BWD_RED];   // per wave: row sums of a group
+    __shared__ float redb[NWV][BWD_G];                           // per wave: dbeta of a group
 
-    const int t = threadIdx.x;
-    const int cg = t % BWD_CPR, rg = t / BWD_CPR;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int rg = lane & 15, cg = lane >> 4;
     const int64_t rows_all = (int64_t)T_tot * H;
-    float *scr = scratch + (int64_t)blockIdx.x * BWD_C * BD * BWD_BV;
+    // scratch: [checkpoint][wave][4][lane] f32x4, rows rg + 16 i of the lane's two columns
+    f32x4 *scr = reinterpret_cast<f32x4 *>(scratch + (int64_t)blockIdx.x * (BWD_C / BWD_G) * BD * BWD_BV) +
+                 wave * 4 * 64 + lane;
+    constexpr int CK = NWV * 4 * 64;                             // f32x4 per checkpoint
     const int64_t items = (int64_t)num_segs * H * BWD_NBLK;
+    float *rw = red[wave];
+
+    // a token's channel vectors (channels 2 lane, 2 lane + 1) to the wave's LDS
+    // slot, read back as this lane's rows rg + 16 i (written and read by this
+    // wave only, in order)
+    auto put = [&](float *dst, float x0, float x1) {
+        dst[chan_pos(2 * lane)] = x0;
+        dst[chan_pos(2 * lane + 1)] = x1;
+    };
+    auto get = [&](const float *src, float r[8]) {
+        *reinterpret_cast<f32x4 *>(r) = *reinterpret_cast<const f32x4 *>(src + 8 * rg);
+        *reinterpret_cast<f32x4 *>(r + 4) = *reinterpret_cast<const f32x4 *>(src + 8 * rg + 4);
+    };
 
   for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
     const int blk = (int)(item % BWD_NBLK);
@@ -187,7 +229,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     const int n = plan[4 * sg];
     if (n < 0) continue;                                  // unused plan entry (uniform per workgroup)
     const int flags = plan[4 * sg + 3];
-    const int dv0 = blk * BWD_BV, c4 = dv0 + 4 * cg;
+    const int cb = blk * BWD_BV + 8 * wave + 2 * cg;      // this lane's value columns cb, cb + 1
     const int t0 = min(max(cu[n], 0), T_tot);             // the sequence
     const int ts = min(max(plan[4 * sg + 1], t0), T_tot); // the segment: [ts, te), chunk-aligned in the sequence
     const int te = min(max(plan[4 * sg + 2], ts), T_tot);
@@ -195,167 +237,205 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     const int64_t sbase = ((int64_t)n * H + h) * BD * BD;   // this (sequence, head) in [N, H, BD, BD]
     const float *gin = seg_dsend + unit * BD * BD;
 
-    f32x4 S[BWD_RPT], dS[BWD_RPT], Sp[BWD_RPT];
+    f32x2 dS[8];
 #pragma unroll
-    for (int i = 0; i < BWD_RPT; ++i) {
-        const int r = rg + BWD_RG * i;
-        dS[i] = *reinterpret_cast<const f32x4 *>(gin + (int64_t)r * BD + c4);
-    }
+    for (int i = 0; i < 8; ++i) dS[i] = *reinterpret_cast<const f32x2 *>(gin + (int64_t)(rg + 16 * i) * BD + cb);
 
     for (int c = nch - 1; c >= 0; --c) {
         const int c0 = ts + c * BWD_C, Lc = min(BWD_C, te - c0);
         const int cs = (c0 - t0) / BWD_C;                 // chunk index within the sequence
         const float *src = cs ? snaps + ((int64_t)(chunk_off[n] + cs) * H + h) * BD * BD
                               : (initial_state ? initial_state + sbase : nullptr);
+        f32x2 S[8];
 #pragma unroll
-        for (int i = 0; i < BWD_RPT; ++i) {
-            const int r = rg + BWD_RG * i;
-            S[i] = src ? *reinterpret_cast<const f32x4 *>(src + (int64_t)r * BD + c4) : zero4();
-        }
+        for (int i = 0; i < 8; ++i)
+            S[i] = src ? *reinterpret_cast<const f32x2 *>(src + (int64_t)(rg + 16 * i) * BD + cb) : f32x2{0.f, 0.f};
 
-        // ---- forward inside the chunk: scr[j] = state before token c0 + j
-        // token vectors one step ahead, clamped rows (loads on every path)
-        const int tc = min(t, BD - 1), vc = min(t, BWD_BV - 1);
-        float nk, ng, nq, nv, ndo, nb;
-        auto fetch = [&](int j) {
+        // ---- forward over the chunk: u of every token; the state before every 4th
+        // token to the scratch area.  Token vectors one step ahead (clamped rows).
+        Raw2 fk, fv;
+        f32x2 fg;
+        float fb;
+        auto fetch1 = [&](int j) {
             const int64_t row = (int64_t)(c0 + j) * H + h;
-            nk = to_f(k[row * BD + tc]);
-            ng = g[row * BD + tc];
-            nq = to_f(q[row * BD + tc]);
-            nv = to_f(v[row * BD + dv0 + vc]);
-            ndo = to_f(dout[row * BD + dv0 + vc]);
-            nb = beta[row];
+            fk = *reinterpret_cast<const Raw2 *>(k + row * BD + 2 * lane);
+            fg = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
+            fv = *reinterpret_cast<const Raw2 *>(v + row * BD + cb);
+            fb = beta[row];
         };
-        fetch(0);
+        fetch1(0);
         for (int j = 0; j < Lc; ++j) {
+            if ((j & (BWD_G - 1)) == 0) {
+                f32x4 *sj = scr + (j / BWD_G) * CK;
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i)
-                *reinterpret_cast<f32x4 *>(scr + ((int64_t)j * BD + rg + BWD_RG * i) * BWD_BV + 4 * cg) = S[i];
-            __syncthreads();                                   // token vectors free
-            if (t < BD) {
-                sk[t] = nk;
-                sa[t] = __expf(ng);
+                for (int p = 0; p < 4; ++p)
+                    sj[p * 64] = f32x4{S[2 * p][0], S[2 * p][1], S[2 * p + 1][0], S[2 * p + 1][1]};
             }
-            if (t < BWD_BV) sv[t] = nv;
-            const float bt = nb;
-            fetch(min(j + 1, Lc - 1));
-            __syncthreads();
-            f32x4 pa = zero4();
+            const Raw2 kk = fk, vv = fv;
+            const f32x2 gg = fg;
+            const float bt = fb;
+            fetch1(min(j + 1, Lc - 1));
+            float *w = tv[wave][0][0];
+            put(w, to_f(kk[0]), to_f(kk[1]));
+            put(w + BD, __expf(gg[0]), __expf(gg[1]));
+            __builtin_amdgcn_wave_barrier();
+            float kr[8], ar[8];
+            get(w, kr);
+            get(w + BD, ar);
+            __builtin_amdgcn_wave_barrier();
+            float pa0 = 0.f, pa1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i) {
-                const int r = rg + BWD_RG * i;
-                S[i] *= sa[r];
-                pa += S[i] * sk[r];
+            for (int i = 0; i < 8; ++i) {
+                S[i] *= ar[i];
+                pa0 += S[i][0] * kr[i];
+                pa1 += S[i][1] * kr[i];
             }
-            red_a[rg][cg] = pa;
-            __syncthreads();
-            if (t < BWD_BV) {
-                float A = 0.f;
-                for (int r = 0; r < BWD_RG; ++r) A += red_a[r][t >> 2][t & 3];
-                su[t] = sv[t] - A;
-            }
-            __syncthreads();
-            const f32x4 u4 = *reinterpret_cast<const f32x4 *>(su + 4 * cg);
+            const float u0 = to_f(vv[0]) - sum16(pa0), u1 = to_f(vv[1]) - sum16(pa1);
+            if (rg == 0) *reinterpret_cast<f32x2 *>(&su[wave][j][2 * cg]) = f32x2{u0, u1};
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i) S[i] += (bt * sk[rg + BWD_RG * i]) * u4;
+            for (int i = 0; i < 8; ++i) {
+                const float bk = bt * kr[i];
+                S[i][0] += bk * u0;
+                S[i][1] += bk * u1;
+            }
         }
+        __builtin_amdgcn_wave_barrier();
 
-        // ---- reverse over the chunk's tokens
-        fetch(Lc - 1);
-        f32x4 nSp[BWD_RPT];
-        auto fetch_sp = [&](int j) {
+        // ---- backwards in groups of BWD_G tokens; a group's vectors and stored
+        // state are loaded while the group before it is processed
+        Raw2 gk[BWD_G], gq[BWD_G], gd[BWD_G];
+        f32x2 gg_[BWD_G];
+        float gb[BWD_G];
+        f32x4 ck[4];
+        auto fetch_group = [&](int m) {
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i)
-                nSp[i] = *reinterpret_cast<const f32x4 *>(scr + ((int64_t)j * BD + rg + BWD_RG * i) * BWD_BV + 4 * cg);
+            for (int jj = 0; jj < BWD_G; ++jj) {
+                const int64_t row = (int64_t)(c0 + min(m * BWD_G + jj, Lc - 1)) * H + h;
+                gk[jj] = *reinterpret_cast<const Raw2 *>(k + row * BD + 2 * lane);
+                gg_[jj] = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
+                gq[jj] = *reinterpret_cast<const Raw2 *>(q + row * BD + 2 * lane);
+                gd[jj] = *reinterpret_cast<const Raw2 *>(dout + row * BD + cb);
+                gb[jj] = beta[row];
+            }
+            const f32x4 *sj = scr + m * CK;                  // this lane's own stores: in order
+#pragma unroll
+            for (int p = 0; p < 4; ++p) ck[p] = sj[p * 64];
         };
-        fetch_sp(Lc - 1);                                      // this thread's own stores: in order
-        for (int j = Lc - 1; j >= 0; --j) {
-            const int64_t row = (int64_t)(c0 + j) * H + h;
+        const int mtop = (Lc - 1) / BWD_G;
+        fetch_group(mtop);
+        for (int m = mtop; m >= 0; --m) {
+            const int jl = m * BWD_G, ng = min(BWD_G, Lc - jl);
+            f32x2 dd[BWD_G], Sp[BWD_G][8];
+            float bb[BWD_G];
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i) Sp[i] = nSp[i];
-            __syncthreads();
-            if (t < BD) {
-                sq[t] = nq;
-                sk[t] = nk;
-                sa[t] = __expf(ng);
-            }
-            if (t < BWD_BV) {
-                sv[t] = nv;
-                sdo[t] = ndo;
-            }
-            const float bt = nb;
-            fetch(max(j - 1, 0));
-            fetch_sp(max(j - 1, 0));
-            __syncthreads();
-            const f32x4 do4 = *reinterpret_cast<const f32x4 *>(sdo + 4 * cg);
-            f32x4 pa = zero4(), px = zero4();
-#pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i) {
-                const int r = rg + BWD_RG * i;
-                pa += (Sp[i] * sa[r]) * sk[r];                 // Sbar^T k
-                dS[i] += sq[r] * do4;                          // o = S^T q
-                px += dS[i] * sk[r];                           // dS^T k
-            }
-            red_a[rg][cg] = pa;
-            red_x[rg][cg] = px;
-            __syncthreads();
-            if (t < BWD_BV) {
-                float A = 0.f, X = 0.f;
-                for (int r = 0; r < BWD_RG; ++r) {
-                    A += red_a[r][t >> 2][t & 3];
-                    X += red_x[r][t >> 2][t & 3];
-                }
-                su[t] = sv[t] - A;
-                sx[t] = X;
-                dv_out[row * BD + dv0 + t] = bt * X;
-            }
-            __syncthreads();
-            const f32x4 u4 = *reinterpret_cast<const f32x4 *>(su + 4 * cg);
-            const f32x4 du4 = *reinterpret_cast<const f32x4 *>(sx + 4 * cg) * bt;
-            float pq[BWD_RPT], pk[BWD_RPT], pg[BWD_RPT];
-#pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i) {
-                const int r = rg + BWD_RG * i;
-                const float a = sa[r], kr = sk[r];
-                const f32x4 sb = Sp[i] * a;
-                const f32x4 sn = sb + (bt * kr) * u4;
-                pq[i] = dot4(sn, do4);
-                pk[i] = bt * dot4(dS[i], u4) - dot4(sb, du4);
-                const f32x4 dsb = dS[i] - kr * du4;
-                pg[i] = a * dot4(dsb, Sp[i]);
-                dS[i] = dsb * a;
+            for (int jj = 0; jj < BWD_G; ++jj) {
+                float *w = tv[wave][jj][0];
+                put(w, to_f(gk[jj][0]), to_f(gk[jj][1]));
+                put(w + BD, __expf(gg_[jj][0]), __expf(gg_[jj][1]));
+                put(w + 2 * BD, to_f(gq[jj][0]), to_f(gq[jj][1]));
+                dd[jj] = f32x2{to_f(gd[jj][0]), to_f(gd[jj][1])};
+                bb[jj] = gb[jj];
             }
 #pragma unroll
-            for (int i = 0; i < BWD_RPT; ++i) {
-                pq[i] = sum8(pq[i]);
-                pk[i] = sum8(pk[i]);
-                pg[i] = sum8(pg[i]);
+            for (int p = 0; p < 4; ++p) {
+                Sp[0][2 * p] = f32x2{ck[p][0], ck[p][1]};
+                Sp[0][2 * p + 1] = f32x2{ck[p][2], ck[p][3]};
             }
-            if (cg == 0) {
-                float *pv = part_vec + (int64_t)blk * 3 * rows_all * BD + row * BD;
+            fetch_group(max(m - 1, 0));
+            __builtin_amdgcn_wave_barrier();
+            // the group's states before each token, from the stored one and the kept u
 #pragma unroll
-                for (int i = 0; i < BWD_RPT; ++i) {
-                    const int r = rg + BWD_RG * i;
-                    pv[r] = pq[i];
-                    pv[rows_all * BD + r] = pk[i];
-                    pv[2 * rows_all * BD + r] = pg[i];
+            for (int jj = 1; jj < BWD_G; ++jj) {
+                if (jj < ng) {
+                    float kr[8], ar[8];
+                    get(tv[wave][jj - 1][0], kr);
+                    get(tv[wave][jj - 1][1], ar);
+                    const f32x2 u2 = *reinterpret_cast<const f32x2 *>(&su[wave][jl + jj - 1][2 * cg]);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float bk = bb[jj - 1] * kr[i];
+                        Sp[jj][i][0] = Sp[jj - 1][i][0] * ar[i] + bk * u2[0];
+                        Sp[jj][i][1] = Sp[jj - 1][i][1] * ar[i] + bk * u2[1];
+                    }
                 }
             }
-            if (t < 64) {   // dbeta over this block's columns (wave 0)
-                const float p = wavesum(t < BWD_BV ? sx[t] * su[t] : 0.f);
-                if (t == 0) part_beta[(int64_t)blk * rows_all + row] = p;
+#pragma unroll
+            for (int jj = BWD_G - 1; jj >= 0; --jj) {
+                if (jj < ng) {
+                    const int j = jl + jj;
+                    const int64_t row = (int64_t)(c0 + j) * H + h;
+                    float kr[8], ar[8], qr[8];
+                    get(tv[wave][jj][0], kr);
+                    get(tv[wave][jj][1], ar);
+                    get(tv[wave][jj][2], qr);
+                    const f32x2 u2 = *reinterpret_cast<const f32x2 *>(&su[wave][j][2 * cg]);
+                    const f32x2 d2 = dd[jj];
+                    const float bt = bb[jj];
+                    float px0 = 0.f, px1 = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        dS[i][0] += qr[i] * d2[0];                   // o = S^T q
+                        dS[i][1] += qr[i] * d2[1];
+                        px0 += dS[i][0] * kr[i];                     // dS^T k
+                        px1 += dS[i][1] * kr[i];
+                    }
+                    const float x0 = sum16(px0), x1 = sum16(px1);
+                    const float du0 = bt * x0, du1 = bt * x1;
+                    if (rg == 0) *reinterpret_cast<f32x2 *>(dv_out + row * BD + cb) = f32x2{du0, du1};
+                    float V[24];                                      // [dq | dk | dg] rows rg + 16 i, this lane's columns
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float a = ar[i], kr_ = kr[i], bk = bt * kr_;
+                        const f32x2 sp = Sp[jj][i];
+                        const f32x2 sb = sp * a;
+                        const f32x2 sn = sb + bk * u2;
+                        V[i] = sn[0] * d2[0] + sn[1] * d2[1];
+                        V[8 + i] = bt * (dS[i][0] * u2[0] + dS[i][1] * u2[1]) - (sb[0] * du0 + sb[1] * du1);
+                        const f32x2 dsb = f32x2{dS[i][0] - kr_ * du0, dS[i][1] - kr_ * du1};
+                        V[16 + i] = a * (dsb[0] * sp[0] + dsb[1] * sp[1]);
+                        dS[i] = dsb * a;
+                    }
+                    // sums over the wave's four DPP rows, scattered: lane cg keeps V[6 cg + e]
+                    float W[12], X[6];
+#pragma unroll
+                    for (int e = 0; e < 12; ++e) W[e] = perm32_sum(V[e], V[e + 12]);
+#pragma unroll
+                    for (int e = 0; e < 6; ++e) X[e] = perm16_sum(W[e], W[e + 6]);
+#pragma unroll
+                    for (int e = 0; e < 6; ++e) {
+                        const int ee = 6 * cg + e;                    // quantity ee / 8, row rg + 16 (ee % 8)
+                        rw[jj * BWD_RED + (ee >> 3) * BD + rg + 16 * (ee & 7)] = X[e];
+                    }
+                    const float db = sum_rows4(x0 * u2[0] + x1 * u2[1]);
+                    if (lane == 0) redb[wave][jj] = db;
+                }
             }
+            // the group's partial sums: the four waves added in order
+            __syncthreads();
+            for (int idx = threadIdx.x; idx < ng * BWD_RED; idx += BWD_THREADS) {
+                float s = red[0][idx];
+#pragma unroll
+                for (int wv = 1; wv < NWV; ++wv) s += red[wv][idx];
+                const int tok = idx / BWD_RED, rem = idx - tok * BWD_RED;
+                const int qn = rem / BD, r = rem - qn * BD;
+                const int64_t prow = (int64_t)(c0 + jl + tok) * H + h;
+                part_vec[(((int64_t)blk * 3 + qn) * rows_all + prow) * BD + r] = s;
+            }
+            if ((int)threadIdx.x < ng) {
+                float s = redb[0][threadIdx.x];
+#pragma unroll
+                for (int wv = 1; wv < NWV; ++wv) s += redb[wv][threadIdx.x];
+                part_beta[(int64_t)blk * rows_all + (int64_t)(c0 + jl + threadIdx.x) * H + h] = s;
+            }
+            __syncthreads();
         }
     }
 
     if (dinit && (flags & SEG_FIRST)) {
 #pragma unroll
-        for (int i = 0; i < BWD_RPT; ++i) {
-            const int r = rg + BWD_RG * i;
-            *reinterpret_cast<f32x4 *>(dinit + sbase + (int64_t)r * BD + c4) = dS[i];
-        }
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<f32x2 *>(dinit + sbase + (int64_t)(rg + 16 * i) * BD + cb) = dS[i];
     }
-    __syncthreads();                                      // the next item reuses the token vectors
   }
 }
 
@@ -397,8 +477,8 @@ __global__ __launch_bounds__(256) void kda_backward_reduce_kernel(
 }  // namespace kda
 
 // Scratch floats per workgroup of the main pass, and the most workgroups it
-// launches (the item loop covers the rest): 512 x 512 KB of scratch at most.
-extern "C" size_t kda_backward_scratch_floats_per_wg() { return (size_t)kda::BWD_C * kda::BD * kda::BWD_BV; }
+// launches (the item loop covers the rest): 512 x 128 KB of scratch at most.
+extern "C" size_t kda_backward_scratch_floats_per_wg() { return (size_t)(kda::BWD_C / kda::BWD_G) * kda::BD * kda::BWD_BV; }
 extern "C" int32_t kda_backward_max_wgs() { return 512; }
 extern "C" int32_t kda_backward_num_blocks() { return kda::BWD_NBLK; }
 
