@@ -1469,84 +1469,89 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 }
 
 // ------------------------------------------------------ segment combination
-// Per (sequence, head, 64 value columns): walk the segments in order,
+// Per (sequence, head, 16 value columns): walk the segments in order,
 // S_in(first) = initial state, S_in(s+1) = M_s S_in(s) + S_s^0 on fp32 MFMA,
-// writing each segment's entering state.  One workgroup of four waves per
-// (sequence, head, 64 columns); the state slice lives in MFMA accumulator
-// registers (row tiles as in the prefill kernel).  Per step the workgroup
-// stages M in LDS (every wave reads all of it as A operands) and loads the
-// next step's M and S^0 into registers while it multiplies.  reverse: the
-// same combination walked from the last segment to the first (gradients of
-// the state, which enter a segment at its end): G(last) = init,
-// G(s-1) = R_s G(s) + G_s^0.
-constexpr int CMB_LDM = DK + 4;                            // padded LDS row of M (fp32)
-constexpr uint32_t CMB_BYTES = sizeof(float) * DK * CMB_LDM;
-__global__ __launch_bounds__(256) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
-                                                             int32_t H, int32_t dv,
-                                                             const int32_t *__restrict__ seq_seg,
-                                                             const float *__restrict__ seg_out,
-                                                             float *__restrict__ seg_init, int32_t reverse)
+// writing each segment's entering state.  One workgroup of eight waves per
+// (sequence, head, 16 columns), so that a long sequence's chain of steps is
+// spread over many compute units: wave w computes row tile w of the next state
+// from its own rows of M and the whole current state slice, which every wave
+// holds in MFMA accumulator layout and which is exchanged through LDS after
+// each step.  A step's operands are loaded two steps ahead, into a ring of
+// three register sets.  reverse: the same combination walked from the last
+// segment to the first (gradients of the state, which enter a segment at its
+// end): G(last) = init, G(s-1) = R_s G(s) + G_s^0.
+constexpr int CMB_COLS = 16;
+constexpr int CMB_THREADS = 64 * (DK / 16);
+struct CmbOps {
+    f32x4 m[DK / 16];   // M rows 16 w + lm, columns 16 kb + 4 lj .. + 3 (the k order of Mma<float>)
+    f32x4 s0;           // S^0 rows 16 w + 4 lj + i, this lane's column
+};
+__global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
+                                                                     int32_t H, int32_t dv,
+                                                                     const int32_t *__restrict__ seq_seg,
+                                                                     const float *__restrict__ seg_out,
+                                                                     float *__restrict__ seg_init, int32_t reverse)
 {
     typedef Mma<float> M;
-    extern __shared__ __align__(16) unsigned char smem[];
-    float *sM = reinterpret_cast<float *>(smem);
-    const int nblk = dv / 64;
+    __shared__ __align__(16) f32x4 sS[DK / 16][64];         // the state slice, accumulator layout per row tile
+    const int nblk = dv / CMB_COLS;
     const int64_t unit = blockIdx.x / nblk;
     if (unit >= (int64_t)N * H) return;
     const int n = (int)(unit / H), h = (int)(unit % H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
-    const int col = (blockIdx.x % nblk) * 64 + 16 * wave + lm;
+    const int col = (blockIdx.x % nblk) * CMB_COLS + lm;
     const int ld = dv + DK;
-    f32x4 S[DK / 16];
+    // the state slice: every wave holds all of it (rows 16 r + 4 lj + i, column
+    // col) and its own row tile in own; both always come from LDS
+    f32x4 own, S[DK / 16];
 #pragma unroll
-    for (int r = 0; r < DK / 16; ++r)
+    for (int i = 0; i < 4; ++i)
+        own[i] = init ? init[((int64_t)n * H + h) * DK * dv + (int64_t)(16 * wave + 4 * lj + i) * dv + col] : 0.f;
+    sS[wave][lane] = own;
+    __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[r][i] = init ? init[((int64_t)n * H + h) * DK * dv + (int64_t)(16 * r + 4 * lj + i) * dv + col] : 0.f;
+    for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
+    own = sS[wave][lane];
     const int s0 = seq_seg[n], s1 = seq_seg[n + 1], ns = s1 - s0;
     auto seg_of = [&](int it) { return reverse ? s1 - 1 - it : s0 + it; };
-
-    // register copies of one step's operands: M rows tid / 32 + 8 it, columns
-    // 4 (tid % 32) .. +3; S^0 in accumulator layout
-    constexpr int MIT = DK * DK / 4 / 256;
-    f32x4 rM[MIT], rS0[DK / 16];
-    auto fetch = [&](int gs) {
-        const float *src = seg_out + ((int64_t)gs * H + h) * DK * ld;
+    auto fetch = [&](int it, CmbOps &o) {                  // step it's operands (clamped to the last step)
+        const float *src = seg_out + ((int64_t)seg_of(min(it, ns - 2)) * H + h) * DK * ld;
 #pragma unroll
-        for (int it = 0; it < MIT; ++it)
-            rM[it] = *reinterpret_cast<const f32x4 *>(src + (int64_t)(tid / 32 + 8 * it) * ld + dv + 4 * (tid % 32));
+        for (int kb = 0; kb < DK / 16; ++kb)
+            o.m[kb] = *reinterpret_cast<const f32x4 *>(src + (int64_t)(16 * wave + lm) * ld + dv + 16 * kb + 4 * lj);
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rS0[r][i] = src[(int64_t)(16 * r + 4 * lj + i) * ld + col];
+        for (int i = 0; i < 4; ++i) o.s0[i] = src[(int64_t)(16 * wave + 4 * lj + i) * ld + col];
     };
-    if (ns > 1) fetch(seg_of(0));
-    for (int it = 0; it < ns; ++it) {
-        const int gs = seg_of(it);
-        float *dst = seg_init + ((int64_t)gs * H + h) * DK * dv;
+    // step it: write S_in of segment it; unless it is the last, S <- M S + S^0
+    // from cur, and load step it + 3 into cur's registers afterwards
+    auto step = [&](int it, CmbOps &cur) -> bool {
+        float *dst = seg_init + ((int64_t)seg_of(it) * H + h) * DK * dv;
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
+        for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * wave + 4 * lj + i) * dv + col] = own[i];
+        if (it >= ns - 1) return false;
+        f32x4 a = cur.s0, b = zero4();                      // two accumulation chains
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i];
-        if (it == ns - 1) break;
-        __syncthreads();                                   // the previous step's reads of sM are done
-#pragma unroll
-        for (int k = 0; k < MIT; ++k)
-            *reinterpret_cast<f32x4 *>(sM + (tid / 32 + 8 * k) * CMB_LDM + 4 * (tid % 32)) = rM[k];
-        f32x4 Sn[DK / 16];
-#pragma unroll
-        for (int r = 0; r < DK / 16; ++r) Sn[r] = rS0[r];
-        __syncthreads();
-        fetch(seg_of(min(it + 1, ns - 2)));                // next step (the last step re-reads itself)
-#pragma unroll
-        for (int r = 0; r < DK / 16; ++r) {
-            const float *mrow = sM + (16 * r + lm) * CMB_LDM;
-#pragma unroll
-            for (int kb = 0; kb < DK / 16; ++kb)
-                Sn[r] = M::mma(*reinterpret_cast<const f32x4 *>(mrow + 16 * kb + 4 * lj), S[kb], Sn[r]);
+        for (int kb = 0; kb < DK / 16; kb += 2) {
+            a = M::mma(cur.m[kb], S[kb], a);
+            b = M::mma(cur.m[kb + 1], S[kb + 1], b);
         }
+        fetch(it + 3, cur);
+        __syncthreads();                                   // every wave's reads of the previous slice are done
+        own = a + b;
+        sS[wave][lane] = own;
+        __syncthreads();
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r) S[r] = Sn[r];
+        for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
+        return true;
+    };
+    CmbOps o0, o1, o2;
+    if (ns > 1) {
+        fetch(0, o0);
+        fetch(1, o1);
+        fetch(2, o2);
+    }
+    for (int it = 0;; it += 3) {
+        if (!step(it, o0) || !step(it + 1, o1) || !step(it + 2, o2)) break;
     }
 }
 
@@ -1640,17 +1645,10 @@ extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             int32_t reverse, hipStream_t stream)
 {
-    const int64_t grid = (int64_t)N * H * (dv / 64);
+    const int64_t grid = (int64_t)N * H * (dv / kda::CMB_COLS);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    static bool attr_set = false;   // idempotent; racing threads set the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kda::kda_cp_combine_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kda::CMB_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(256), kda::CMB_BYTES, stream, init, N,
-                       H, dv, seq_seg, seg_out, seg_init, reverse);
+    hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init,
+                       N, H, dv, seq_seg, seg_out, seg_init, reverse);
     return hipGetLastError();
 }
