@@ -1489,7 +1489,7 @@ struct CmbOps {
 __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
                                                                      int32_t H, int32_t dv,
                                                                      const int32_t *__restrict__ seq_seg,
-                                                                     const float *__restrict__ seg_out,
+                                                                     const float *seg_out,
                                                                      float *__restrict__ seg_init, int32_t reverse)
 {
     typedef Mma<float> M;
@@ -1536,6 +1536,7 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
             b = M::mma(cur.m[kb + 1], S[kb + 1], b);
         }
         fetch(it + 3, cur);
+        asm volatile("" ::: "memory");                     // keeps the loads here (not sunk into a later step)
         __syncthreads();                                   // every wave's reads of the previous slice are done
         own = a + b;
         sS[wave][lane] = own;
