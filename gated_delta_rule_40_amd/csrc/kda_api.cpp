@@ -18,6 +18,7 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
+                                         int32_t last_len, int32_t skip_last, int32_t *seq_order,
                                          hipStream_t stream);
 extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
                                             const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
@@ -27,7 +28,8 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, float *snap, hipStream_t stream);
+                                       const int32_t *sched, float *snap, const int32_t *init_seq_seg,
+                                       int32_t init_unit, int32_t init_units, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
                                                   const float *beta, const void *dout, const int32_t *plan,
@@ -50,7 +52,8 @@ extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const vo
                                                hipStream_t stream);
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
-                                            int32_t reverse, hipStream_t stream);
+                                            int32_t reverse, const int32_t *plan, const int32_t *seq_order,
+                                            hipStream_t stream);
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, float *state,
                                         int32_t N, int32_t H, void *out, hipStream_t stream);
@@ -174,33 +177,54 @@ constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the segme
 constexpr int32_t kCpSumBlock = 256; // value + transition columns per workgroup of the summary pass
 
 struct CpLayout {
-    size_t plan, sched, seq_seg, chunk_off, seg_out, seg_init, img, total;
-    int32_t max_segs, max_chunks;
+    size_t plan, sched, seq_seg, uplan, usched, useq_seg, seq_order, chunk_off, seg_out, seg_init, img, total;
+    int32_t max_segs, max_units, unit_len, max_chunks;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace sections: plan [max_segs][4] int32, dispatch order [max_segs]
-// int32, per-sequence first segment
-// [N + 1] int32, per-sequence first chunk [N + 1] int32, summaries
-// [max_segs][H][dk][dv + dk] fp32, entering states [max_segs][H][dk][dv]
-// fp32, chunk-operand images [max_chunks][H][image].  Every sequence of
-// length L takes max(1, ceil(L / seg_len)) segments and ceil(L / 32) chunks,
-// which max_segs and max_chunks bound.
+// Summary units: output segments (seg_len tokens) are cut into up to four
+// units for the summary pass and the combine, so that the summary pass, one
+// workgroup per (unit, head) at one per compute unit, is made of many short
+// pieces that pack the GPU evenly; the output pass still runs whole segments,
+// from the entering state of their first unit.  The unit length divides
+// seg_len and is a multiple of the chunk.
+int32_t cp_unit_len(int32_t seg_len)
+{
+    const int32_t m = seg_len / kCpChunk;
+    return m % 4 == 0 ? seg_len / 4 : (m % 2 == 0 ? seg_len / 2 : seg_len);
+}
+
+// Workspace sections: the output plan [max_segs][4] int32, its dispatch
+// order [max_segs] int32 and per-sequence first segment [N + 1] int32; the
+// same three for the summary units (max_units); the sequences by unit count
+// [N] int32; per-sequence first chunk
+// [N + 1] int32; summaries [max_units][H][dk][dv + dk] fp32; entering states
+// [max_units][H][dk][dv] fp32; chunk-operand images [max_chunks][H][image].
+// Every sequence of length L takes max(1, ceil(L / len)) segments (units) and
+// ceil(L / 32) chunks, which max_segs, max_units and max_chunks bound.
 bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16, int32_t seg_len, CpLayout *lay)
 {
+    const int32_t unit = cp_unit_len(seg_len);
     const int64_t segs = (int64_t)T / seg_len + 1 + N;
+    const int64_t units = (int64_t)T / unit + 1 + N;
     const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
-    if (segs > INT32_MAX / 4 || chunks > INT32_MAX / 4) return false;
+    if (units > INT32_MAX / 4 || chunks > INT32_MAX / 4) return false;
     lay->max_segs = (int32_t)segs;
+    lay->max_units = (int32_t)units;
+    lay->unit_len = unit;
     lay->max_chunks = (int32_t)chunks;
     lay->plan = 0;
     lay->sched = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
     lay->seq_seg = align256(lay->sched + sizeof(int32_t) * (size_t)segs);
-    lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->uplan = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->usched = align256(lay->uplan + sizeof(int32_t) * 4 * (size_t)units);
+    lay->useq_seg = align256(lay->usched + sizeof(int32_t) * (size_t)units);
+    lay->seq_order = align256(lay->useq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->chunk_off = align256(lay->seq_order + sizeof(int32_t) * ((size_t)N + 1));
     lay->seg_out = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
-    lay->seg_init = align256(lay->seg_out + sizeof(float) * (size_t)segs * H * dk * (dv + dk));
-    lay->img = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * dk * dv);
+    lay->seg_init = align256(lay->seg_out + sizeof(float) * (size_t)units * H * dk * (dv + dk));
+    lay->img = align256(lay->seg_init + sizeof(float) * (size_t)units * H * dk * dv);
     lay->total = align256(lay->img + kda_chunk_image_bytes(bf16) * (size_t)chunks * H);
     return true;
 }
@@ -246,31 +270,42 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
     CpLayout lay;
     if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, bf16, seg_len, &lay)) return KDA_ERR_INVALID_ARG;
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
-    if ((int64_t)lay.max_segs * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)lay.max_units * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
     if ((int64_t)lay.max_chunks * num_heads > INT32_MAX) return KDA_ERR_INVALID_ARG;
     if (num_seqs == 0) return KDA_OK;
     char *ws = static_cast<char *>(workspace);
     int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
     int32_t *sched = reinterpret_cast<int32_t *>(ws + lay.sched);
     int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
+    int32_t *uplan = reinterpret_cast<int32_t *>(ws + lay.uplan);
+    int32_t *usched = reinterpret_cast<int32_t *>(ws + lay.usched);
+    int32_t *useq_seg = reinterpret_cast<int32_t *>(ws + lay.useq_seg);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + lay.chunk_off);
     float *seg_out = reinterpret_cast<float *>(ws + lay.seg_out);
     float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
     void *img = ws + lay.img;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // output segments, then summary units (SEG_LAST: in a sequence's last segment)
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, sched, s);
+                                      kCpChunk, lay.max_chunks, chunk_off, sched, 0, 0, nullptr, s);
+    int32_t *seq_order = reinterpret_cast<int32_t *>(ws + lay.seq_order);
+    if (e == hipSuccess)
+        e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.unit_len, lay.max_units, uplan, useq_seg,
+                               kCpChunk, lay.max_chunks, nullptr, usched, seg_len, 1, seq_order, s);
     if (e == hipSuccess)   // chunk operands of every (chunk, head)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
-    if (e == hipSuccess)   // segment summaries (segments with a successor)
-        e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out, nullptr,
-                             plan, lay.max_segs, 1, nullptr, seg_out, chunk_off, img, sched, nullptr, s);
-    if (e == hipSuccess)   // entering state of every segment
-        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, seg_out, seg_init, 0, s);
-    if (e == hipSuccess)   // outputs and final states
+    if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
+        e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
+                             nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
+                             nullptr, 0, 0, s);
+    if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
+                                  seq_order, s);
+    if (e == hipSuccess)   // outputs and final states, each segment from the entering state of its first unit
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
-                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr, s);
+                             final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
+                             useq_seg, lay.unit_len, lay.max_units, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -438,30 +473,32 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     int32_t *fseq_seg = reinterpret_cast<int32_t *>(ws + lay.fseq_seg);
     void *img = ws + lay.img;
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, nullptr, s);
+                                      kCpChunk, lay.max_chunks, chunk_off, nullptr, 0, 0, nullptr, s);
     // forward: the state at every chunk start, by the context-parallel
     // pipeline (its own, longer segments) with state stores and no outputs
     if (e == hipSuccess)
         e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.fseg_len, lay.fmax_segs, fplan, fseq_seg,
-                               kCpChunk, lay.max_chunks, chunk_off, fsched, s);
+                               kCpChunk, lay.max_chunks, chunk_off, fsched, 0, 0, nullptr, s);
     if (e == hipSuccess)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
     if (e == hipSuccess)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, fplan, lay.fmax_segs, 1, nullptr, seg_sum, chunk_off, img, fsched,
-                             nullptr, s);
+                             nullptr, nullptr, 0, 0, s);
     if (e == hipSuccess)
-        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, fseq_seg, seg_sum, seg_dsend, 0, s);
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, fseq_seg, seg_sum, seg_dsend, 0, nullptr,
+                                  nullptr, s);
     if (e == hipSuccess)
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, fplan, lay.fmax_segs, 0, seg_dsend, nullptr, chunk_off, img, fsched,
-                             snaps, s);
+                             snaps, nullptr, 0, 0, s);
     if (e == hipSuccess)   // gradient summaries of every segment but a sequence's first
         e = kda_launch_backward_summary(bf16, q, k, g, beta, dout, plan, lay.max_segs, total_tokens, num_heads,
                                         seg_sum, s);
     if (e == hipSuccess)   // the gradient entering every segment at its end
-        e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, seg_sum, seg_dsend, 1, s);
+        e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, seg_sum, seg_dsend, 1, nullptr, nullptr,
+                                  s);
     if (e == hipSuccess)
         e = kda_launch_backward(bf16, q, k, v, g, beta, initial_state, cu_seqlens, chunk_off, snaps, dout, plan,
                                 lay.max_segs, seg_dsend, num_seqs, total_tokens, num_heads,

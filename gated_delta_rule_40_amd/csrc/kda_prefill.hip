@@ -153,7 +153,23 @@ struct SegArgs {
     int32_t snap_every;         // tokens between snapshots, a multiple of the chunk
     int32_t max_snaps;
     const int32_t *sched;       // [num_segs] plan index of each dispatch position, or nullptr (plan order)
+    // entering states indexed by summary unit instead of segment (SEG_OUTPUT):
+    // a segment starting t tokens into sequence n reads seg_init entry
+    // init_seq_seg[n] + t / init_unit (segments start on unit boundaries), or
+    // nullptr (entry = segment index)
+    const int32_t *init_seq_seg;
+    int32_t init_unit, init_units;
 };
+
+// seg_init entry of plan segment su (sequence n, first token t_start)
+__device__ __forceinline__ int64_t seg_init_entry(const SegArgs &seg, int su, int n, int t_start,
+                                                  const int32_t *cu_seqlens, int32_t total_tokens)
+{
+    if (!seg.init_seq_seg) return su;
+    const int seq_start = min(max(cu_seqlens[n], 0), total_tokens);
+    const int64_t e = (int64_t)seg.init_seq_seg[n] + max(t_start - seq_start, 0) / seg.init_unit;
+    return min(max(e, (int64_t)0), (int64_t)seg.init_units - 1);
+}
 
 enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2 };   // MODE_SNAP: fused + state snapshots
 constexpr int PREP_GROUP = 8;    // consecutive chunks per workgroup of the chunk-operand pass
@@ -665,7 +681,7 @@ void kda_prefill_kernel(
         // initial state was copied there before this pass, so a last segment
         // may overwrite it (final_state == initial_state) while others run
         S_in = seg.seg_init;
-        S_in_base = ((int64_t)su * num_heads + h) * DK * dv;
+        S_in_base = (seg_init_entry(seg, su, n, t_start, cu_seqlens, total_tokens) * num_heads + h) * DK * dv;
     } else if (initial_state) {
         S_in = initial_state;
         S_in_base = sbase;
@@ -1184,7 +1200,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         S_in = nullptr;
     } else if (segmented) {
         S_in = seg.seg_init;
-        S_in_base = ((int64_t)su * num_heads + h) * DK * dv;
+        S_in_base = (seg_init_entry(seg, su, n, t_start, cu_seqlens, total_tokens) * num_heads + h) * DK * dv;
     } else if (initial_state) {
         S_in = initial_state;
         S_in_base = sbase;
@@ -1385,7 +1401,8 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
                                                           int32_t *__restrict__ plan,
                                                           int32_t *__restrict__ seq_seg, int32_t chunk,
                                                           int32_t max_chunks, int32_t *__restrict__ chunk_off,
-                                                          int32_t *__restrict__ sched)
+                                                          int32_t *__restrict__ sched, int32_t last_len,
+                                                          int32_t skip_last, int32_t *__restrict__ seq_order)
 {
     __shared__ int64_t scan[256], cscan[256];
     __shared__ int32_t hist[256];
@@ -1416,12 +1433,16 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
             // With non-decreasing cu the host bound on max_segs always holds;
             // otherwise segments past it are dropped (memory-safe, result unspecified).
             seq_seg[n] = (int32_t)min(start, (int64_t)max_segs);
+            // SEG_LAST: the segment lies in the sequence's last stretch of
+            // last_len tokens (a multiple of seg_len), which no later segment follows
+            const int64_t nl = max((int64_t)1, ((int64_t)t1 - t0 + last_len - 1) / last_len);
             for (int s = 0; s < ns && start + s < max_segs; ++s) {
                 const int gs = (int)(start + s);
                 plan[4 * gs] = n;
                 plan[4 * gs + 1] = t0 + s * seg_len;
                 plan[4 * gs + 2] = min(t0 + (s + 1) * seg_len, t1);
-                plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) | (s == ns - 1 ? SEG_LAST : 0);
+                plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) |
+                                   ((int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
             }
         }
         carry += scan[255];
@@ -1430,6 +1451,30 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
     }
     const int32_t used = (int32_t)min(carry, (int64_t)max_segs);
     if (threadIdx.x == 0) seq_seg[N] = used;
+    if (seq_order) {
+        // sequences by segment count, most first (counting sort on 256
+        // buckets; 255 segments and more share the first): the combine walks
+        // the longest chains first
+        __syncthreads();   // every seq_seg entry written
+        hist[threadIdx.x] = 0;
+        __syncthreads();
+        auto seq_bucket = [&](int n) { return 255 - min(max(seq_seg[n + 1] - seq_seg[n], 0), 255); };
+        for (int n = (int)threadIdx.x; n < N; n += 256) atomicAdd(&hist[seq_bucket(n)], 1);
+        __syncthreads();
+        const int32_t c = hist[threadIdx.x];
+        scan[threadIdx.x] = c;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            scan[threadIdx.x] += x;
+            __syncthreads();
+        }
+        hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - c);
+        __syncthreads();
+        for (int n = (int)threadIdx.x; n < N; n += 256) seq_order[atomicAdd(&hist[seq_bucket(n)], 1)] = n;
+        __syncthreads();   // hist and scan are reused below
+    }
     if (chunk_off && threadIdx.x == 0) chunk_off[N] = (int32_t)min(ccarry, (int64_t)max_chunks);
     for (int gs = used + (int)threadIdx.x; gs < max_segs; gs += 256) {
         plan[4 * gs] = -1;
@@ -1443,13 +1488,16 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
     // so the short tail segments fill the gaps the full-length ones leave at
     // the end of a pass.  Counting sort on 256 length buckets (bucket 0 = full
     // length, 255 = empty); the order inside a bucket does not matter, since
-    // the segments of one pass are independent.
+    // the segments of one pass are independent.  skip_last: SEG_LAST segments
+    // count as empty (a summary pass skips them).
+    auto seg_bucket = [&](int gs) {
+        int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
+        if (skip_last && (plan[4 * gs + 3] & SEG_LAST)) len = 0;
+        return (int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len);
+    };
     hist[threadIdx.x] = 0;
     __syncthreads();   // also makes this workgroup's plan entries visible below
-    for (int gs = (int)threadIdx.x; gs < used; gs += 256) {
-        const int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
-        atomicAdd(&hist[(int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len)], 1);
-    }
+    for (int gs = (int)threadIdx.x; gs < used; gs += 256) atomicAdd(&hist[seg_bucket(gs)], 1);
     __syncthreads();
     const int32_t cnt = hist[threadIdx.x];
     scan[threadIdx.x] = cnt;
@@ -1462,10 +1510,7 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
     }
     hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - cnt);   // bucket start
     __syncthreads();
-    for (int gs = (int)threadIdx.x; gs < used; gs += 256) {
-        const int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
-        sched[atomicAdd(&hist[(int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len)], 1)] = gs;
-    }
+    for (int gs = (int)threadIdx.x; gs < used; gs += 256) sched[atomicAdd(&hist[seg_bucket(gs)], 1)] = gs;
 }
 
 // ------------------------------------------------------ segment combination
@@ -1477,9 +1522,13 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 // from its own rows of M and the whole current state slice, which every wave
 // holds in MFMA accumulator layout and which is exchanged through LDS after
 // each step.  A step's operands are loaded two steps ahead, into a ring of
-// three register sets.  reverse: the same combination walked from the last
-// segment to the first (gradients of the state, which enter a segment at its
-// end): G(last) = init, G(s-1) = R_s G(s) + G_s^0.
+// three register sets.  seq_order (may be nullptr): workgroups take the
+// sequences in this order, longest chains first.  plan (forward only, may be nullptr): the walk stops at
+// the sequence's first SEG_LAST segment, whose entering state is the last one
+// written (the segments after it have no summaries).  reverse: the same
+// combination walked from the last segment to the first (gradients of the
+// state, which enter a segment at its end): G(last) = init,
+// G(s-1) = R_s G(s) + G_s^0.
 constexpr int CMB_COLS = 16;
 constexpr int CMB_THREADS = 64 * (DK / 16);
 struct CmbOps {
@@ -1490,14 +1539,16 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
                                                                      int32_t H, int32_t dv,
                                                                      const int32_t *__restrict__ seq_seg,
                                                                      const float *seg_out,
-                                                                     float *__restrict__ seg_init, int32_t reverse)
+                                                                     float *__restrict__ seg_init, int32_t reverse,
+                                                                     const int32_t *__restrict__ plan,
+                                                                     const int32_t *__restrict__ seq_order)
 {
     typedef Mma<float> M;
     __shared__ __align__(16) f32x4 sS[DK / 16][64];         // the state slice, accumulator layout per row tile
     const int nblk = dv / CMB_COLS;
     const int64_t unit = blockIdx.x / nblk;
     if (unit >= (int64_t)N * H) return;
-    const int n = (int)(unit / H), h = (int)(unit % H);
+    const int n = seq_order ? min(max(seq_order[unit / H], 0), N - 1) : (int)(unit / H), h = (int)(unit % H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
     const int col = (blockIdx.x % nblk) * CMB_COLS + lm;
     const int ld = dv + DK;
@@ -1512,7 +1563,14 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
     own = sS[wave][lane];
-    const int s0 = seq_seg[n], s1 = seq_seg[n + 1], ns = s1 - s0;
+    const int s0 = seq_seg[n], s1 = seq_seg[n + 1];
+    int ns = s1 - s0;
+    if (plan && !reverse)
+        for (int it = 0; it < ns - 1; ++it)
+            if (plan[4 * (s0 + it) + 3] & SEG_LAST) {
+                ns = it + 1;
+                break;
+            }
     auto seg_of = [&](int it) { return reverse ? s1 - 1 - it : s0 + it; };
     auto fetch = [&](int it, CmbOps &o) {                  // step it's operands (clamped to the last step)
         const float *src = seg_out + ((int64_t)seg_of(min(it, ns - 2)) * H + h) * DK * ld;
@@ -1568,7 +1626,8 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
                                          int32_t max_snaps, const int32_t *snap_chunk_off, hipStream_t stream)
 {
     using namespace kda;
-    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, snap_chunk_off, nullptr, snap, snap_every, max_snaps, nullptr};
+    const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, snap_chunk_off, nullptr, snap, snap_every, max_snaps, nullptr,
+                         nullptr, 0, 0};
     if (snap) {   // snapshots: 32-token chunks, 64-column value blocks
         if (chunk != 32 || dv_block != 64) return hipErrorInvalidValue;
         if (bf16) return launch_prefill_t<bf16_t, 32, 4, MODE_SNAP>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
@@ -1588,13 +1647,20 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
     return hipErrorInvalidValue;
 }
 
+// last_len: SEG_LAST marks the segments in each sequence's last stretch of
+// last_len tokens (a multiple of seg_len; 0 = seg_len: the last segment);
+// skip_last: those segments go last in the dispatch order; seq_order
+// (optional, [N]): the sequences by segment count, most first.
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
+                                         int32_t last_len, int32_t skip_last, int32_t *seq_order,
                                          hipStream_t stream)
 {
+    if (last_len == 0) last_len = seg_len;
+    if (seg_len <= 0 || last_len % seg_len) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_tot, seg_len, max_segs,
-                       plan, seq_seg, chunk, max_chunks, chunk_off, sched);
+                       plan, seq_seg, chunk, max_chunks, chunk_off, sched, last_len, skip_last, seq_order);
     return hipGetLastError();
 }
 
@@ -1605,7 +1671,8 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
                                             hipStream_t stream)
 {
     using namespace kda;
-    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr};
+    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr,
+                   nullptr, 0, 0};
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
@@ -1617,12 +1684,14 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, float *snap, hipStream_t stream)
+                                       const int32_t *sched, float *snap, const int32_t *init_seq_seg,
+                                       int32_t init_unit, int32_t init_units, hipStream_t stream)
 {
     using namespace kda;
+    if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), mode == SEG_SUMMARY ? nullptr : snap, 0, 0,
-                   sched};
+                   sched, init_seq_seg, init_unit, init_units};
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
@@ -1644,12 +1713,13 @@ extern "C" size_t kda_chunk_image_bytes(int bf16)
 
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
-                                            int32_t reverse, hipStream_t stream)
+                                            int32_t reverse, const int32_t *plan, const int32_t *seq_order,
+                                            hipStream_t stream)
 {
     const int64_t grid = (int64_t)N * H * (dv / kda::CMB_COLS);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init,
-                       N, H, dv, seq_seg, seg_out, seg_init, reverse);
+                       N, H, dv, seq_seg, seg_out, seg_init, reverse, plan, seq_order);
     return hipGetLastError();
 }
