@@ -33,8 +33,8 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
                                                   const float *beta, const void *dout, const int32_t *plan,
-                                                  int32_t num_segs, int32_t T_tot, int32_t H, float *seg_out,
-                                                  hipStream_t stream);
+                                                  int32_t num_segs, int32_t T_tot, int32_t H, int32_t ncols,
+                                                  float *seg_out, hipStream_t stream);
 extern "C" size_t kda_backward_scratch_floats_per_wg();
 extern "C" int32_t kda_backward_max_wgs();
 extern "C" int32_t kda_backward_num_blocks();
@@ -53,7 +53,7 @@ extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const vo
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             int32_t reverse, const int32_t *plan, const int32_t *seq_order,
-                                            hipStream_t stream);
+                                            const float *m_src, int32_t m_trans, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, float *state,
                                         int32_t N, int32_t H, void *out, hipStream_t stream);
@@ -301,7 +301,7 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
                              nullptr, 0, 0, s);
     if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
-                                  seq_order, s);
+                                  seq_order, nullptr, 0, s);
     if (e == hipSuccess)   // outputs and final states, each segment from the entering state of its first unit
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
@@ -353,47 +353,35 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
 namespace {
 
 struct BwdLayout {
-    size_t plan, seq_seg, chunk_off, fplan, fsched, fseq_seg, img, snaps, seg_sum, seg_dsend, scratch, part_vec,
-        part_beta, total;
-    int32_t max_chunks, max_segs, seg_len, fmax_segs, fseg_len;
+    size_t plan, sched, seq_seg, chunk_off, img, snaps, fsum, bsum, seg_dsend, scratch, part_vec, part_beta, total;
+    int32_t max_chunks, max_segs, seg_len;
 };
 
-// Segment length of the backward passes: about 1,024 work items of (segment,
-// head, 32 columns) in total (two per workgroup of the main pass; shorter
-// segments lengthen the sequential combine), at least 64 tokens, a multiple
-// of the chunk.
+// Segment length of the backward, shared with the forward pipeline that
+// stores the chunk-start states (so that a segment's gradient transition is
+// the transpose of its forward transition): about 256 segments per head
+// count (about 1,024 work items of (segment, head, 32 columns), two per
+// workgroup of the main pass), at least 256 tokens, a multiple of the chunk.
 int32_t bwd_seg_len(int32_t T, int32_t H)
-{
-    int64_t len = (int64_t)T * H * kda_backward_num_blocks() / 1024;
-    len = len < 64 ? 64 : (len > 65536 ? 65536 : len);
-    return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
-}
-
-// Segment length of the forward pass that stores the chunk-start states (the
-// context-parallel pipeline with state stores): longer than the backward's.
-int32_t bwd_fwd_seg_len(int32_t T, int32_t H, int32_t bwd_len)
 {
     int64_t len = (int64_t)T * H / 256;
     len = len < 256 ? 256 : (len > 65536 ? 65536 : len);
-    len = (len + kCpChunk - 1) / kCpChunk * kCpChunk;
-    return (int32_t)(len < bwd_len ? bwd_len : len);
+    return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
 }
 
-// Workspace sections: the backward's plan [max_segs][4] int32 with the first
-// segment [N+1] and first chunk [N+1] of each sequence; the forward's plan
-// [fmax_segs][4], dispatch order and first segments; the forward's chunk
-// images; forward states at chunk starts [max_chunks][H][dk][dv]; summaries
-// [max_segs][H][dk][dv + dk] and entering states / gradients
-// [max_segs][H][dk][dv] (used by the forward pass, then by the backward);
-// the main pass's per-workgroup scratch; the partial row sums of dq, dk, dg
-// and dbeta.
+// Workspace sections: the plan [max_segs][4] int32 (no segment marked last:
+// the forward summaries cover every segment), its dispatch order [max_segs]
+// and the first segment [N+1] and first chunk [N+1] of each sequence; the
+// chunk images; forward states at chunk starts [max_chunks][H][dk][dv];
+// forward summaries [max_segs][H][dk][dv + dk]; gradient summaries
+// [max_segs][H][dk][dv]; entering states, then entering gradients
+// [max_segs][H][dk][dv]; the main pass's per-workgroup scratch; the partial
+// row sums of dq, dk, dg and dbeta.
 bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
 {
     const int32_t seg_len = bwd_seg_len(T, H);
-    const int32_t fseg_len = bwd_fwd_seg_len(T, H, seg_len);
     const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
     const int64_t segs = (int64_t)T / seg_len + 1 + N;
-    const int64_t fsegs = (int64_t)T / fseg_len + 1 + N;
     if (chunks > INT32_MAX / 4 || segs > INT32_MAX / 4) return false;
     const size_t S = (size_t)kHeadDim * kHeadDim;
     const size_t rows = (size_t)T * H;
@@ -401,20 +389,17 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     const int64_t items = segs * H * (int64_t)nblk;
     const size_t wgs = (size_t)(items < kda_backward_max_wgs() ? items : kda_backward_max_wgs());
     lay->seg_len = seg_len;
-    lay->fseg_len = fseg_len;
     lay->max_chunks = (int32_t)chunks;
     lay->max_segs = (int32_t)segs;
-    lay->fmax_segs = (int32_t)fsegs;
     lay->plan = 0;
-    lay->seq_seg = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
+    lay->sched = align256(lay->plan + sizeof(int32_t) * 4 * (size_t)segs);
+    lay->seq_seg = align256(lay->sched + sizeof(int32_t) * (size_t)segs);
     lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
-    lay->fplan = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
-    lay->fsched = align256(lay->fplan + sizeof(int32_t) * 4 * (size_t)fsegs);
-    lay->fseq_seg = align256(lay->fsched + sizeof(int32_t) * (size_t)fsegs);
-    lay->img = align256(lay->fseq_seg + sizeof(int32_t) * ((size_t)N + 1));
+    lay->img = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
     lay->snaps = align256(lay->img + kda_chunk_image_bytes(bf16) * (size_t)chunks * H);
-    lay->seg_sum = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
-    lay->seg_dsend = align256(lay->seg_sum + sizeof(float) * (size_t)segs * H * 2 * S);
+    lay->fsum = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
+    lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 2 * S);
+    lay->seg_dsend = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
     lay->scratch = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
     lay->part_vec = align256(lay->scratch + sizeof(float) * wgs * kda_backward_scratch_floats_per_wg());
     lay->part_beta = align256(lay->part_vec + sizeof(float) * nblk * 3 * rows * kHeadDim);
@@ -455,50 +440,47 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
     const int64_t units = (int64_t)num_seqs * num_heads;
     if (units == 0) return KDA_OK;
-    if ((int64_t)lay.max_segs * num_heads * 2 * kda_backward_num_blocks() > INT32_MAX ||
+    if ((int64_t)lay.max_segs * num_heads * ((dv + dk) / 16) > INT32_MAX ||
         (int64_t)lay.max_chunks * num_heads > INT32_MAX)
         return KDA_ERR_INVALID_ARG;
     const int bf16 = dtype == KDA_BF16 ? 1 : 0;
     char *ws = static_cast<char *>(workspace);
     int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
+    int32_t *sched = reinterpret_cast<int32_t *>(ws + lay.sched);
     int32_t *seq_seg = reinterpret_cast<int32_t *>(ws + lay.seq_seg);
     int32_t *chunk_off = reinterpret_cast<int32_t *>(ws + lay.chunk_off);
     float *snaps = reinterpret_cast<float *>(ws + lay.snaps);
-    float *seg_sum = reinterpret_cast<float *>(ws + lay.seg_sum);
+    float *fsum = reinterpret_cast<float *>(ws + lay.fsum);
+    float *bsum = reinterpret_cast<float *>(ws + lay.bsum);
     float *seg_dsend = reinterpret_cast<float *>(ws + lay.seg_dsend);
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // segments and chunk numbering
-    int32_t *fplan = reinterpret_cast<int32_t *>(ws + lay.fplan);
-    int32_t *fsched = reinterpret_cast<int32_t *>(ws + lay.fsched);
-    int32_t *fseq_seg = reinterpret_cast<int32_t *>(ws + lay.fseq_seg);
     void *img = ws + lay.img;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // segments and chunk numbering; no segment is marked last, so the forward
+    // summaries include every segment's transition
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, nullptr, 0, 0, nullptr, s);
+                                      kCpChunk, lay.max_chunks, chunk_off, sched, -1, 0, nullptr, s);
     // forward: the state at every chunk start, by the context-parallel
-    // pipeline (its own, longer segments) with state stores and no outputs
-    if (e == hipSuccess)
-        e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.fseg_len, lay.fmax_segs, fplan, fseq_seg,
-                               kCpChunk, lay.max_chunks, chunk_off, fsched, 0, 0, nullptr, s);
+    // pipeline with state stores and no outputs
     if (e == hipSuccess)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
     if (e == hipSuccess)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
-                             nullptr, nullptr, fplan, lay.fmax_segs, 1, nullptr, seg_sum, chunk_off, img, fsched,
+                             nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
                              nullptr, nullptr, 0, 0, s);
     if (e == hipSuccess)
-        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, fseq_seg, seg_sum, seg_dsend, 0, nullptr,
-                                  nullptr, s);
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_dsend, 0, nullptr,
+                                  nullptr, nullptr, 0, s);
     if (e == hipSuccess)
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
-                             nullptr, nullptr, fplan, lay.fmax_segs, 0, seg_dsend, nullptr, chunk_off, img, fsched,
+                             nullptr, nullptr, plan, lay.max_segs, 0, seg_dsend, nullptr, chunk_off, img, sched,
                              snaps, nullptr, 0, 0, s);
-    if (e == hipSuccess)   // gradient summaries of every segment but a sequence's first
+    if (e == hipSuccess)   // gradient summaries G^0 of every segment but a sequence's first
         e = kda_launch_backward_summary(bf16, q, k, g, beta, dout, plan, lay.max_segs, total_tokens, num_heads,
-                                        seg_sum, s);
-    if (e == hipSuccess)   // the gradient entering every segment at its end
-        e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, seg_sum, seg_dsend, 1, nullptr, nullptr,
-                                  s);
+                                        dk, bsum, s);
+    if (e == hipSuccess)   // the gradient entering every segment at its end, with R_s = M_s^T
+        e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
+                                  fsum, 1, s);
     if (e == hipSuccess)
         e = kda_launch_backward(bf16, q, k, v, g, beta, initial_state, cu_seqlens, chunk_off, snaps, dout, plan,
                                 lay.max_segs, seg_dsend, num_seqs, total_tokens, num_heads,

@@ -18,18 +18,23 @@
 // to per-block partial buffers that a second kernel adds in a fixed order
 // (deterministic).  The forward states are needed in reverse order: the
 // state at every 32-token chunk start comes from the forward prefill kernel
-// (snapshot mode), and inside a chunk the workgroup recomputes the 32 token
-// states into its own scratch area, then walks them backwards.
+// (context-parallel pipeline with state stores), and inside a chunk the
+// workgroup rebuilds the token states it needs in registers, then walks them
+// backwards.
 //
 // Segments.  The gradient recurrence is linear in dS, as the forward one is
 // in S (dS_{t-1} = Diag(alpha) (I - beta k k^T) (dS_t + q do^T)), so the
 // sequences are cut into chunk-aligned segments that run side by side, as in
 // the context-parallel forward: a summary pass takes each segment but a
-// sequence's first from a zero gradient at its end to its start over 128
-// value columns plus 128 transition columns (identity at the end, do = 0),
-// giving [G^0 | R]; a reverse combine then gives the gradient entering every
-// segment at its end, G(last) = d(final_state), G(s-1) = R_s G(s) + G^0_s; and
-// the main pass runs every segment from there.
+// sequence's first from a zero gradient at its end to its start over the 128
+// value columns, giving G^0; the segment's gradient transition R is the
+// transpose of its forward transition M, which the forward pipeline's
+// summaries already hold (the forward step is S_t = (I - beta k k^T) Diag(alpha)
+// S_{t-1}, the gradient step its transpose, and a product of transposes in
+// reverse order is the transpose of the product).  A reverse combine then
+// gives the gradient entering every segment at its end, G(last) =
+// d(final_state), G(s-1) = M_s^T G(s) + G^0_s, and the main pass runs every
+// segment from there.
 #include "kda_device.hpp"
 
 namespace kda {
@@ -69,19 +74,22 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
 __device__ __forceinline__ int chan_pos(int c) { return (c & 15) * 8 + (c >> 4); }
 
 // Segment summaries of the gradient recurrence: one workgroup per (segment,
-// head, block of 32 of the 128 + 128 columns), segments that are not a
-// sequence's first; each wave runs its 8 columns on its own (no barrier).
-// seg_out: [num_segs][H][BD][2 BD], [G^0 | R] per segment.
+// head, block of 32 of the ncols columns), segments that are not a sequence's
+// first; each wave runs its 8 columns on its own (no barrier).  seg_out:
+// [num_segs][H][BD][ncols]: [G^0 | R] per segment for ncols = 2 BD, G^0 alone
+// for ncols = BD (R is then the transpose of the forward transition M of the
+// same segment: dS_{t-1} = Diag(alpha)(I - beta k k^T) dS_t is the transpose of
+// the forward step's map, applied in the opposite order).
 template <typename T>
 __global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ plan,
-    int32_t num_segs, int32_t H, int32_t T_tot, float *__restrict__ seg_out)
+    int32_t num_segs, int32_t H, int32_t T_tot, int32_t ncols, float *__restrict__ seg_out)
 {
     __shared__ __align__(16) float sv[BWD_THREADS / 64][3][BD];   // per wave: k, alpha, q
-    constexpr int NB2 = 2 * BD / BWD_BV;
-    const int blk = blockIdx.x % NB2;
-    const int64_t unit = blockIdx.x / NB2;
+    const int ncb = ncols / BWD_BV;
+    const int blk = blockIdx.x % ncb;
+    const int64_t unit = blockIdx.x / ncb;
     if (unit >= (int64_t)num_segs * H) return;
     const int su = (int)(unit / H), h = (int)(unit % H);
     if (plan[4 * su] < 0 || (plan[4 * su + 3] & SEG_FIRST)) return;
@@ -147,10 +155,10 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
             G[i][1] = (G[i][1] - kr[i] * du1) * ar[i];
         }
     }
-    float *dst = seg_out + ((int64_t)su * H + h) * BD * (2 * BD);
+    float *dst = seg_out + ((int64_t)su * H + h) * BD * ncols;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<f32x2 *>(dst + (int64_t)(rg + 16 * i) * (2 * BD) + c0) = G[i];
+        *reinterpret_cast<f32x2 *>(dst + (int64_t)(rg + 16 * i) * ncols + c0) = G[i];
 }
 
 // Work items (segment su, head h, column block blk) in the order
@@ -484,21 +492,22 @@ extern "C" int32_t kda_backward_num_blocks() { return kda::BWD_NBLK; }
 
 extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
                                                   const float *beta, const void *dout, const int32_t *plan,
-                                                  int32_t num_segs, int32_t T_tot, int32_t H, float *seg_out,
-                                                  hipStream_t stream)
+                                                  int32_t num_segs, int32_t T_tot, int32_t H, int32_t ncols,
+                                                  float *seg_out, hipStream_t stream)
 {
     using namespace kda;
-    const int64_t grid = (int64_t)num_segs * H * (2 * BD / BWD_BV);
+    if (ncols != BD && ncols != 2 * BD) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)num_segs * H * (ncols / BWD_BV);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (bf16)
         hipLaunchKernelGGL(kda_backward_summary_kernel<bf16_t>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), g, beta,
-                           static_cast<const bf16_t *>(dout), plan, num_segs, H, T_tot, seg_out);
+                           static_cast<const bf16_t *>(dout), plan, num_segs, H, T_tot, ncols, seg_out);
     else
         hipLaunchKernelGGL(kda_backward_summary_kernel<float>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
                            static_cast<const float *>(q), static_cast<const float *>(k), g, beta,
-                           static_cast<const float *>(dout), plan, num_segs, H, T_tot, seg_out);
+                           static_cast<const float *>(dout), plan, num_segs, H, T_tot, ncols, seg_out);
     return hipGetLastError();
 }
 

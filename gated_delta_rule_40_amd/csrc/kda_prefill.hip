@@ -1435,14 +1435,14 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
             seq_seg[n] = (int32_t)min(start, (int64_t)max_segs);
             // SEG_LAST: the segment lies in the sequence's last stretch of
             // last_len tokens (a multiple of seg_len), which no later segment follows
-            const int64_t nl = max((int64_t)1, ((int64_t)t1 - t0 + last_len - 1) / last_len);
+            const int64_t nl = last_len > 0 ? max((int64_t)1, ((int64_t)t1 - t0 + last_len - 1) / last_len) : 1;
             for (int s = 0; s < ns && start + s < max_segs; ++s) {
                 const int gs = (int)(start + s);
                 plan[4 * gs] = n;
                 plan[4 * gs + 1] = t0 + s * seg_len;
                 plan[4 * gs + 2] = min(t0 + (s + 1) * seg_len, t1);
                 plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) |
-                                   ((int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
+                                   (last_len > 0 && (int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
             }
         }
         carry += scan[255];
@@ -1522,7 +1522,9 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 // from its own rows of M and the whole current state slice, which every wave
 // holds in MFMA accumulator layout and which is exchanged through LDS after
 // each step.  A step's operands are loaded two steps ahead, into a ring of
-// three register sets.  seq_order (may be nullptr): workgroups take the
+// three register sets.  m_src (may be nullptr): M from the forward summaries
+// instead of seg_out (which then holds S^0 only, rows of dv floats), as M^T
+// when m_trans.  seq_order (may be nullptr): workgroups take the
 // sequences in this order, longest chains first.  plan (forward only, may be nullptr): the walk stops at
 // the sequence's first SEG_LAST segment, whose entering state is the last one
 // written (the segments after it have no summaries).  reverse: the same
@@ -1541,7 +1543,8 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
                                                                      const float *seg_out,
                                                                      float *__restrict__ seg_init, int32_t reverse,
                                                                      const int32_t *__restrict__ plan,
-                                                                     const int32_t *__restrict__ seq_order)
+                                                                     const int32_t *__restrict__ seq_order,
+                                                                     const float *m_src, int32_t m_trans)
 {
     typedef Mma<float> M;
     __shared__ __align__(16) f32x4 sS[DK / 16][64];         // the state slice, accumulator layout per row tile
@@ -1551,7 +1554,11 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
     const int n = seq_order ? min(max(seq_order[unit / H], 0), N - 1) : (int)(unit / H), h = (int)(unit % H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
     const int col = (blockIdx.x % nblk) * CMB_COLS + lm;
-    const int ld = dv + DK;
+    // S^0 (and M, unless m_src) in seg_out rows of ld floats; M from m_src:
+    // forward summaries [.][H][DK][dv + DK], M at column dv, used transposed
+    // when m_trans (the gradient transition of a segment is the transpose of
+    // its forward transition)
+    const int ld = m_src ? dv : dv + DK, ldm = dv + DK;
     // the state slice: every wave holds all of it (rows 16 r + 4 lj + i, column
     // col) and its own row tile in own; both always come from LDS
     f32x4 own, S[DK / 16];
@@ -1573,10 +1580,20 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
             }
     auto seg_of = [&](int it) { return reverse ? s1 - 1 - it : s0 + it; };
     auto fetch = [&](int it, CmbOps &o) {                  // step it's operands (clamped to the last step)
-        const float *src = seg_out + ((int64_t)seg_of(min(it, ns - 2)) * H + h) * DK * ld;
+        const int64_t gs = seg_of(min(it, ns - 2));
+        const float *src = seg_out + (gs * H + h) * DK * ld;
+        const float *msrc = m_src ? m_src + (gs * H + h) * DK * ldm : src;
+        if (m_trans) {                                     // A[i][k] = M[k][i]
 #pragma unroll
-        for (int kb = 0; kb < DK / 16; ++kb)
-            o.m[kb] = *reinterpret_cast<const f32x4 *>(src + (int64_t)(16 * wave + lm) * ld + dv + 16 * kb + 4 * lj);
+            for (int kb = 0; kb < DK / 16; ++kb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    o.m[kb][e] = msrc[(int64_t)(16 * kb + 4 * lj + e) * ldm + dv + 16 * wave + lm];
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; ++kb)
+                o.m[kb] = *reinterpret_cast<const f32x4 *>(msrc + (int64_t)(16 * wave + lm) * ldm + dv + 16 * kb + 4 * lj);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) o.s0[i] = src[(int64_t)(16 * wave + 4 * lj + i) * ld + col];
     };
@@ -1648,7 +1665,8 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
 }
 
 // last_len: SEG_LAST marks the segments in each sequence's last stretch of
-// last_len tokens (a multiple of seg_len; 0 = seg_len: the last segment);
+// last_len tokens (a multiple of seg_len; 0 = seg_len: the last segment;
+// negative: no segment is marked, so a summary pass covers them all);
 // skip_last: those segments go last in the dispatch order; seq_order
 // (optional, [N]): the sequences by segment count, most first.
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
@@ -1658,7 +1676,7 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
                                          hipStream_t stream)
 {
     if (last_len == 0) last_len = seg_len;
-    if (seg_len <= 0 || last_len % seg_len) return hipErrorInvalidValue;
+    if (seg_len <= 0 || (last_len > 0 && last_len % seg_len)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_tot, seg_len, max_segs,
                        plan, seq_seg, chunk, max_chunks, chunk_off, sched, last_len, skip_last, seq_order);
     return hipGetLastError();
@@ -1714,12 +1732,12 @@ extern "C" size_t kda_chunk_image_bytes(int bf16)
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             int32_t reverse, const int32_t *plan, const int32_t *seq_order,
-                                            hipStream_t stream)
+                                            const float *m_src, int32_t m_trans, hipStream_t stream)
 {
     const int64_t grid = (int64_t)N * H * (dv / kda::CMB_COLS);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init,
-                       N, H, dv, seq_seg, seg_out, seg_init, reverse, plan, seq_order);
+                       N, H, dv, seq_seg, seg_out, seg_init, reverse, plan, seq_order, m_src, m_trans);
     return hipGetLastError();
 }
