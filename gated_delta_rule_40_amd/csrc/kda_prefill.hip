@@ -1548,12 +1548,15 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
 {
     typedef Mma<float> M;
     __shared__ __align__(16) f32x4 sS[DK / 16][64];         // the state slice, accumulator layout per row tile
+    // the column blocks of one (sequence, head) run on one XCD (workgroups are
+    // dealt to the XCDs in turn), so that they read M through one L2
     const int nblk = dv / CMB_COLS;
-    const int64_t unit = blockIdx.x / nblk;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
     if (unit >= (int64_t)N * H) return;
     const int n = seq_order ? min(max(seq_order[unit / H], 0), N - 1) : (int)(unit / H), h = (int)(unit % H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
-    const int col = (blockIdx.x % nblk) * CMB_COLS + lm;
+    const int col = (slot % nblk) * CMB_COLS + lm;
     // S^0 (and M, unless m_src) in seg_out rows of ld floats; M from m_src:
     // forward summaries [.][H][DK][dv + DK], M at column dv, used transposed
     // when m_trans (the gradient transition of a segment is the transpose of
@@ -1734,7 +1737,7 @@ extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_
                                             int32_t reverse, const int32_t *plan, const int32_t *seq_order,
                                             const float *m_src, int32_t m_trans, hipStream_t stream)
 {
-    const int64_t grid = (int64_t)N * H * (dv / kda::CMB_COLS);
+    const int64_t grid = ((int64_t)N * H + 7) / 8 * 8 * (dv / kda::CMB_COLS);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init,
