@@ -1524,7 +1524,7 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 // each step.  A step's operands are loaded two steps ahead, into a ring of
 // three register sets.  m_src (may be nullptr): M from the forward summaries
 // instead of seg_out (which then holds S^0 only, rows of dv floats), as M^T
-// when m_trans.  seq_order (may be nullptr): workgroups take the
+// when MT.  seq_order (may be nullptr): workgroups take the
 // sequences in this order, longest chains first.  plan (forward only, may be nullptr): the walk stops at
 // the sequence's first SEG_LAST segment, whose entering state is the last one
 // written (the segments after it have no summaries).  reverse: the same
@@ -1537,6 +1537,7 @@ struct CmbOps {
     f32x4 m[DK / 16];   // M rows 16 w + lm, columns 16 kb + 4 lj .. + 3 (the k order of Mma<float>)
     f32x4 s0;           // S^0 rows 16 w + 4 lj + i, this lane's column
 };
+template <bool MT>
 __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
                                                                      int32_t H, int32_t dv,
                                                                      const int32_t *__restrict__ seq_seg,
@@ -1544,7 +1545,7 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
                                                                      float *__restrict__ seg_init, int32_t reverse,
                                                                      const int32_t *__restrict__ plan,
                                                                      const int32_t *__restrict__ seq_order,
-                                                                     const float *m_src, int32_t m_trans)
+                                                                     const float *m_src)
 {
     typedef Mma<float> M;
     __shared__ __align__(16) f32x4 sS[DK / 16][64];         // the state slice, accumulator layout per row tile
@@ -1586,7 +1587,7 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
         const int64_t gs = seg_of(min(it, ns - 2));
         const float *src = seg_out + (gs * H + h) * DK * ld;
         const float *msrc = m_src ? m_src + (gs * H + h) * DK * ldm : src;
-        if (m_trans) {                                     // A[i][k] = M[k][i]
+        if constexpr (MT) {                                // A[i][k] = M[k][i]
 #pragma unroll
             for (int kb = 0; kb < DK / 16; ++kb)
 #pragma unroll
@@ -1600,13 +1601,15 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
 #pragma unroll
         for (int i = 0; i < 4; ++i) o.s0[i] = src[(int64_t)(16 * wave + 4 * lj + i) * ld + col];
     };
-    // step it: write S_in of segment it; unless it is the last, S <- M S + S^0
-    // from cur, and load step it + 3 into cur's registers afterwards
-    auto step = [&](int it, CmbOps &cur) -> bool {
+    // step it (it < ns - 1): write S_in of segment it, S <- M S + S^0 from
+    // cur, and load step it + 3 into cur's registers afterwards
+    auto write_own = [&](int it) {
         float *dst = seg_init + ((int64_t)seg_of(it) * H + h) * DK * dv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * wave + 4 * lj + i) * dv + col] = own[i];
-        if (it >= ns - 1) return false;
+    };
+    auto step = [&](int it, CmbOps &cur) {
+        write_own(it);
         f32x4 a = cur.s0, b = zero4();                      // two accumulation chains
 #pragma unroll
         for (int kb = 0; kb < DK / 16; kb += 2) {
@@ -1621,17 +1624,26 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
         __syncthreads();
 #pragma unroll
         for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
-        return true;
     };
+    // whole rounds of three steps with no exit inside (the wait for each
+    // step's operands then stays exact across the loop's back edge), then the
+    // remaining steps and the last segment's entering state
     CmbOps o0, o1, o2;
-    if (ns > 1) {
+    const int nst = ns - 1;
+    if (nst > 0) {
         fetch(0, o0);
         fetch(1, o1);
         fetch(2, o2);
     }
-    for (int it = 0;; it += 3) {
-        if (!step(it, o0) || !step(it + 1, o1) || !step(it + 2, o2)) break;
+    int it = 0;
+    for (; it + 3 <= nst; it += 3) {
+        step(it, o0);
+        step(it + 1, o1);
+        step(it + 2, o2);
     }
+    if (it < nst) step(it, o0);
+    if (it + 1 < nst) step(it + 1, o1);
+    if (ns > 0) write_own(ns - 1);
 }
 
 }  // namespace kda
@@ -1740,7 +1752,9 @@ extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_
     const int64_t grid = ((int64_t)N * H + 7) / 8 * 8 * (dv / kda::CMB_COLS);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kda::kda_cp_combine_kernel, dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init,
-                       N, H, dv, seq_seg, seg_out, seg_init, reverse, plan, seq_order, m_src, m_trans);
+    if (m_trans && !m_src) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(m_trans ? kda::kda_cp_combine_kernel<true> : kda::kda_cp_combine_kernel<false>,
+                       dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init, N, H, dv, seq_seg, seg_out,
+                       seg_init, reverse, plan, seq_order, m_src);
     return hipGetLastError();
 }
