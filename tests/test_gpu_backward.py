@@ -70,6 +70,14 @@ def test_backward_t512_h4():
     _check(_case([512], H=4, dtype=torch.bfloat16, seed=63), torch.bfloat16, "t512_h4")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_backward_several_segments_per_sequence(dtype):
+    # segments are at least 256 tokens: these sequences take 3, 2 and 5 of
+    # them, with ragged last segments (gradient summaries, the reverse combine
+    # through the transposed forward transitions, gradients entering mid-sequence)
+    _check(_case([700, 300, 1100], H=2, dtype=dtype, seed=65), dtype, "multi_segment")
+
+
 def test_backward_bitwise_deterministic():
     inp = _case([200, 77], H=2, dtype=torch.bfloat16, seed=64)
     a = K.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],

@@ -44,8 +44,10 @@ def _check_cp(inp, tol, label, seg_len, use_init=True):
 LENGTHS = [1, 17, 64, 0, 100, 63, 65, 130, 200, 333]
 
 
+# seg_len 64 and 128 cut every segment into 2 and 4 summary units; 96 (three
+# chunks) keeps one unit per segment
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("seg_len", [32, 64, 96])
+@pytest.mark.parametrize("seg_len", [32, 64, 96, 128])
 def test_cp_ragged_vs_oracle(dtype, seg_len):
     inp = to_dev(I.random_prefill(LENGTHS, H=3, dtype=dtype, seed=30))
     _check_cp(inp, TOL[dtype], "cp_ragged", seg_len)
@@ -128,6 +130,16 @@ def test_cp_empty_sequences_and_untouched_rows():
     ref_out, ref_fin = oracle_prefill(inp)
     assert_close(host(out)[:T], ref_out[:T], TOL[torch.bfloat16], "cp untouched out", torch.bfloat16)
     assert_close(host(fin), ref_fin, TOL[torch.bfloat16], "cp untouched final_state")
+
+
+def test_cp_many_sequences_vs_oracle():
+    # more than 256 sequences: the plan kernel walks them in several blocks of
+    # 256 (segment and chunk numbering, the order of sequences by unit count)
+    rng = np.random.default_rng(40)
+    lengths = [int(x) for x in rng.integers(0, 90, size=300)]
+    lengths[7], lengths[123], lengths[299] = 0, 257, 300
+    inp = to_dev(I.random_prefill(lengths, H=2, dtype=torch.float32, seed=40))
+    _check_cp(inp, TOL[torch.float32], "cp_many_seqs", 64)
 
 
 def test_cp_run_to_run_bitwise_determinism():
