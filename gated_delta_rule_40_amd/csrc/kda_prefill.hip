@@ -1138,7 +1138,7 @@ struct ChainCfg {
 // chunk's global index in seg.snap ([chunks][H][DK][dv]); out may be NULL.
 template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB>::WAVES_PER_EU)))
-void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
+void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
                       TIn *__restrict__ out, float *final_state, SegArgs seg)
 {
@@ -1234,8 +1234,8 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     // ---- chunk staging: image + value tile of chunk ci in registers
     constexpr int IIT = SUMMARY ? Q::IITEMS_SUM : Q::IITEMS;       // image vectors this pass reads
     constexpr int NV = SUMMARY ? Img::NVEC_SUM : Img::NVEC;
-    f32x4 ri[IIT], rv[Q::VITEMS];
-    auto load = [&](int ci) {
+    f32x4 ri[IIT], rv[Q::VITEMS], ri2[IIT], rv2[Q::VITEMS];
+    auto load_to = [&](int ci, f32x4 (&ri)[IIT], f32x4 (&rv)[Q::VITEMS]) {
         const f32x4 *src = seg.img + ((gc0 + ci) * H + h) * Img::NVEC;
 #pragma unroll
         for (int it = 0; it < IIT; ++it) ri[it] = src[min(tid + it * NT, NV - 1)];
@@ -1248,6 +1248,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
                                     : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
         }
     };
+    auto load = [&](int ci) { load_to(ci, ri, rv); };
     const typename Img::Offs offs = {Q::offNKp, Q::offQp, Q::offKhT, Q::offT, Q::offP, Q::offGam, Q::offBeta, Q::offTs};
     uint32_t stage_off[IIT];                              // LDS byte offsets of this thread's image vectors
 #pragma unroll
@@ -1256,7 +1257,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
     // the last vector, same value to the same place): a conditional consumer
     // would leave the loads pending at the loop head for the compiler, which
     // then waits there for all older memory operations, output stores included.
-    auto stage = [&](int ci, int b) {
+    auto stage_from = [&](int ci, int b, const f32x4 (&ri)[IIT], const f32x4 (&rv)[Q::VITEMS]) {
         unsigned char *base = smem + b * Q::BUF;
 #pragma unroll
         for (int it = 0; it < IIT; ++it) *reinterpret_cast<f32x4 *>(base + stage_off[it]) = ri[it];
@@ -1269,6 +1270,45 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
             *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < LL ? rv[it] : zero4();
         }
     };
+    auto stage = [&](int ci, int b) { stage_from(ci, b, ri, rv); };
+    if constexpr (SUMMARY && !SB) {
+        // summaries: the operands are loaded two chunks ahead, into register
+        // sets A (ri, rv) and B (ri2, rv2) in turn, so that a load has two
+        // chunks' work to arrive; the loop takes chunks in pairs to keep the
+        // sets apart, and a compiler barrier after each load keeps it from
+        // being moved next to its use
+        auto run = [&](int ci) {
+            const unsigned char *base = smem + (ci & 1) * Q::BUF;
+            chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT>(
+                S, sS, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
+                reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
+                reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
+                reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
+                reinterpret_cast<const TIn *>(base + Q::offV), 16 * NCT * wave + lm, nullptr, lm, lj, lm);
+        };
+        if (nch > 0) {
+            load_to(0, ri, rv);
+            stage_from(0, 0, ri, rv);
+            load_to(min(1, nch - 1), ri, rv);
+        }
+        int ci = 0;
+        for (; ci + 2 <= nch; ci += 2) {
+            __syncthreads();
+            load_to(min(ci + 2, nch - 1), ri2, rv2);
+            asm volatile("" ::: "memory");
+            run(ci);
+            stage_from(min(ci + 1, nch - 1), (ci + 1) & 1, ri, rv);
+            __syncthreads();
+            load_to(min(ci + 3, nch - 1), ri, rv);
+            asm volatile("" ::: "memory");
+            run(ci + 1);
+            stage_from(min(ci + 2, nch - 1), ci & 1, ri2, rv2);
+        }
+        if (ci < nch) {
+            __syncthreads();
+            run(ci);
+        }
+    } else {
     if (nch > 0) {
         load(0);
         stage(0, 0);
@@ -1318,6 +1358,7 @@ void kda_chain_kernel(const TIn *__restrict__ v, const float *initial_state, con
         }
         if constexpr (SB) __syncthreads();       // every wave is done with the buffer
         stage(min(ci + 1, nch - 1), SB ? 0 : (ci + 1) & 1);
+    }
     }
 
 #pragma unroll
