@@ -1563,15 +1563,18 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 // from its own rows of M and the whole current state slice, which every wave
 // holds in MFMA accumulator layout and which is exchanged through LDS after
 // each step.  A step's operands are loaded two steps ahead, into a ring of
-// three register sets.  m_src (may be nullptr): M from the forward summaries
-// instead of seg_out (which then holds S^0 only, rows of dv floats), as M^T
-// when MT.  seq_order (may be nullptr): workgroups take the
-// sequences in this order, longest chains first.  plan (forward only, may be nullptr): the walk stops at
-// the sequence's first SEG_LAST segment, whose entering state is the last one
-// written (the segments after it have no summaries).  reverse: the same
-// combination walked from the last segment to the first (gradients of the
-// state, which enter a segment at its end): G(last) = init,
-// G(s-1) = R_s G(s) + G_s^0.
+// three register sets.
+//   m_src (may be nullptr): M comes from the forward summaries
+//     [.][H][DK][dv + DK] (at column dv) instead of seg_out, which then holds
+//     S^0 alone in rows of dv floats; MT: M is used transposed.
+//   seq_order (may be nullptr): workgroups take the sequences in this order
+//     (longest chains first).
+//   plan (forward walks only, may be nullptr): the walk stops at the
+//     sequence's first SEG_LAST segment, whose entering state is the last one
+//     written (the segments after it have no summaries).
+//   reverse: the walk goes from the last segment to the first (gradients of
+//     the state, which enter a segment at its end): G(last) = init,
+//     G(s-1) = R_s G(s) + G_s^0, with R_s = M_s^T when MT.
 constexpr int CMB_COLS = 16;
 constexpr int CMB_THREADS = 64 * (DK / 16);
 struct CmbOps {
@@ -1599,10 +1602,7 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
     const int n = seq_order ? min(max(seq_order[unit / H], 0), N - 1) : (int)(unit / H), h = (int)(unit % H);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
     const int col = (slot % nblk) * CMB_COLS + lm;
-    // S^0 (and M, unless m_src) in seg_out rows of ld floats; M from m_src:
-    // forward summaries [.][H][DK][dv + DK], M at column dv, used transposed
-    // when m_trans (the gradient transition of a segment is the transpose of
-    // its forward transition)
+    // S^0 (and M, unless m_src) in seg_out rows of ld floats; M in rows of ldm
     const int ld = m_src ? dv : dv + DK, ldm = dv + DK;
     // the state slice: every wave holds all of it (rows 16 r + 4 lj + i, column
     // col) and its own row tile in own; both always come from LDS
