@@ -325,6 +325,42 @@ def main():
     bwd_tflops = Tb * Hb * BWD_FLOP_PER_HT / (bwd_ms * 1e-3) / 1e12
     bwd_bytes = Tb * Hb * BWD_BYTES_PER_HT + 3 * Hb * DK * DV * 4      # + initial state, dfinal, dinit
 
+    # the other prefill configurations (parity cases of their own), timed the
+    # same way for reference: context-parallel and plain entry points
+    def time_prefill_config(name):
+        wl = I.WORKLOADS[name]
+        inp = I.make_prefill(wl, device=dev)
+        Tc, Hc = inp["q"].shape[0], inp["q"].shape[1]
+        Nc = inp["cu_seqlens"].shape[0] - 1
+        o = torch.empty(Tc, Hc, DV, dtype=inp["q"].dtype, device=dev)
+        f = torch.empty(Nc, Hc, DK, DV, dtype=torch.float32, device=dev)
+        w = torch.empty(K.kda_prefill_cp_workspace_size(Nc, Tc, Hc, DK, DV, inp["q"].dtype, 0), dtype=torch.uint8,
+                        device=dev)
+        calls = {"kda_prefill_cp": lambda: K.kda_prefill_cp(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                                            inp["initial_state"], inp["cu_seqlens"], o, f,
+                                                            seg_len=0, workspace=w),
+                 "kda_prefill": lambda: K.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                                      inp["initial_state"], inp["cu_seqlens"], o, f)}
+        entry = {"total_tokens": Tc, "heads": Hc, "num_seqs": Nc}
+        nbytes = Tc * Hc * PREFILL_BYTES_PER_HT + 2 * Nc * Hc * DK * DV * 4   # + initial and final states
+        for key, fn in calls.items():
+            for _ in range(2):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(5):
+                fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            ms = ev[0].elapsed_time(ev[1]) / 5
+            entry[key] = {"ms": ms, "tokens_per_s": Tc / (ms * 1e-3), "head_tokens_per_s": Tc * Hc / (ms * 1e-3),
+                          "hbm_algorithmic_gbs": nbytes / (ms * 1e-3) / 1e9,
+                          "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del inp, o, f, w
+        return entry
+
+    other_prefill = {name: time_prefill_config(name) for name in ("prefill_t4096_h8", "prefill_4x16384_h32")}
+
     result = {
         "metric": METRIC,
         "value": T / (pre_avg * 1e-3),
@@ -369,9 +405,10 @@ def main():
                                   "flop_per_head_token": BWD_FLOP_PER_HT,
                                   "hbm_achieved_gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
                                   "algorithmic_bytes_per_launch": bwd_bytes},
-                     "kernels": "kda_cp_plan_kernel x2, chunk operands, kda_chain_kernel summary and output with "
+                     "kernels": "kda_cp_plan_kernel, chunk operands, kda_chain_kernel summary and output with "
                                 "state stores, kda_cp_combine_kernel x2, kda_backward_summary_kernel<bf16>, "
                                 "kda_backward_kernel<bf16>, kda_backward_reduce_kernel"},
+        "other_prefill_configs": other_prefill,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

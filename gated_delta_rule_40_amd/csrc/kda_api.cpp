@@ -183,15 +183,19 @@ struct CpLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Summary units: output segments (seg_len tokens) are cut into up to four
-// units for the summary pass and the combine, so that the summary pass, one
-// workgroup per (unit, head) at one per compute unit, is made of many short
-// pieces that pack the GPU evenly; the output pass still runs whole segments,
-// from the entering state of their first unit.  The unit length divides
-// seg_len and is a multiple of the chunk.
-int32_t cp_unit_len(int32_t seg_len)
+// Summary units: when there are at least as many (segment, head) pairs as
+// compute units (T / seg_len * H >= 256), output segments (seg_len tokens) are
+// cut into up to four units for the summary pass and the combine, so that the
+// summary pass, one workgroup per (unit, head) at one per compute unit, is
+// made of many short pieces that pack the GPU evenly; the output pass still
+// runs whole segments, from the entering state of their first unit.  Below
+// that the summary pass is a single round anyway, and more units would only
+// lengthen the combine's chain.  The unit length divides seg_len and is a
+// multiple of the chunk.
+int32_t cp_unit_len(int32_t seg_len, int32_t T, int32_t H)
 {
     const int32_t m = seg_len / kCpChunk;
+    if ((int64_t)T / seg_len * H < 256) return seg_len;
     return m % 4 == 0 ? seg_len / 4 : (m % 2 == 0 ? seg_len / 2 : seg_len);
 }
 
@@ -205,7 +209,7 @@ int32_t cp_unit_len(int32_t seg_len)
 // ceil(L / 32) chunks, which max_segs, max_units and max_chunks bound.
 bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16, int32_t seg_len, CpLayout *lay)
 {
-    const int32_t unit = cp_unit_len(seg_len);
+    const int32_t unit = cp_unit_len(seg_len, T, H);
     const int64_t segs = (int64_t)T / seg_len + 1 + N;
     const int64_t units = (int64_t)T / unit + 1 + N;
     const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
@@ -229,13 +233,14 @@ bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16
     return true;
 }
 
-// Default segment length: long enough that the extra segment-summary work
-// stays a fraction of the total, short enough that a long sequence splits
-// into several segments that run side by side.
+// Default segment length: about 512 (segment, head) pairs (two output-pass
+// workgroups per compute unit), at least 512 tokens (16 chunks: shorter
+// segments add more summary and combine steps than they take off a
+// workgroup's walk) and at most 65,536.
 int32_t cp_default_seg_len(int32_t T, int32_t H)
 {
     int64_t len = (int64_t)T * H / 512;
-    len = len < 4096 ? 4096 : (len > 65536 ? 65536 : len);
+    len = len < 512 ? 512 : (len > 65536 ? 65536 : len);
     return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
 }
 
