@@ -159,6 +159,7 @@ struct SegArgs {
     // nullptr (entry = segment index)
     const int32_t *init_seq_seg;
     int32_t init_unit, init_units;
+    int32_t prep_group;         // chunk-operand pass: consecutive chunks per workgroup (1 .. PREP_GROUP)
 };
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
@@ -172,7 +173,7 @@ __device__ __forceinline__ int64_t seg_init_entry(const SegArgs &seg, int su, in
 }
 
 enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2 };   // MODE_SNAP: fused + state snapshots
-constexpr int PREP_GROUP = 8;    // consecutive chunks per workgroup of the chunk-operand pass
+constexpr int PREP_GROUP = 8;    // most consecutive chunks per workgroup of the chunk-operand pass
 
 // Chunk-operand image: everything the state chain of one (chunk, head) reads
 // besides V, as computed by the chunk-operand pass -- -GS K+, GS K^
@@ -605,10 +606,11 @@ void kda_prefill_kernel(
     int gc_begin = 0, nch = 0;      // chunk-operand pass: first global chunk, chunk count
     if constexpr (kPrep) {
         h = wg % num_heads;
-        gc_begin = (wg / num_heads) * PREP_GROUP;
+        const int grp = min(max(seg.prep_group, 1), PREP_GROUP);
+        gc_begin = (wg / num_heads) * grp;
         const int total_chunks = seg.chunk_off[num_seqs];
         if (gc_begin >= total_chunks) return;
-        nch = min(PREP_GROUP, total_chunks - gc_begin);
+        nch = min(grp, total_chunks - gc_begin);
     } else {
         const int nblk = (summary ? dv + DK : dv) / BV;
         const int xcd = wg & 7, slot = wg >> 3;
@@ -1395,7 +1397,11 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t grid = (max_chunks + PREP_GROUP - 1) / PREP_GROUP * H;
+    // fewer chunks per workgroup when there are few: every compute unit
+    // gets work, and a workgroup's walk is short
+    const int64_t want = (max_chunks * H + 2047) / 2048;
+    seg.prep_group = (int32_t)(want < 1 ? 1 : (want > PREP_GROUP ? PREP_GROUP : want));
+    const int64_t grid = (max_chunks + seg.prep_group - 1) / seg.prep_group * H;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(P::NT), P::bytes, stream,
@@ -1700,7 +1706,7 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
 {
     using namespace kda;
     const SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, snap_chunk_off, nullptr, snap, snap_every, max_snaps, nullptr,
-                         nullptr, 0, 0};
+                         nullptr, 0, 0, 0};
     if (snap) {   // snapshots: 32-token chunks, 64-column value blocks
         if (chunk != 32 || dv_block != 64) return hipErrorInvalidValue;
         if (bf16) return launch_prefill_t<bf16_t, 32, 4, MODE_SNAP>(q, k, v, g, beta, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
@@ -1746,7 +1752,7 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
 {
     using namespace kda;
     SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr,
-                   nullptr, 0, 0};
+                   nullptr, 0, 0, PREP_GROUP};
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
@@ -1765,7 +1771,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), mode == SEG_SUMMARY ? nullptr : snap, 0, 0,
-                   sched, init_seq_seg, init_unit, init_units};
+                   sched, init_seq_seg, init_unit, init_units, 0};
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
