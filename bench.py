@@ -46,7 +46,7 @@ BWD_BYTES_PER_HT = 4 * 2 * DK + 4 * DK + 4 + 4 * (3 * DK + DV) + 4
 # dS^T k 2, S do with the update 4, dk 4, dSbar 2, dg 2, decay 1) = 25
 BWD_FLOP_PER_HT = 25 * DK * DV
 PREFILL_KERNELS = {
-    "cp": "kda_prefill_cp call: kda_cp_plan_kernel x2, kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
+    "cp": "kda_prefill_cp call: kda_cp_plan_kernel (two plans), kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
           "kda_chain_kernel<bf16,32,8 waves,2 tiles,summary>, kda_cp_combine_kernel, "
           "kda_chain_kernel<bf16,32,4 waves,2 tiles,output,single buffer>",
     "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
@@ -100,14 +100,15 @@ def write_traffic(fetch_csv, write_csv):
                         "--copy-calibration" % c for c in ("FETCH_SIZE", "WRITE_SIZE")]
                        + ["python bench.py --traffic-from <fetch dir>/run_counter_collection.csv "
                           "<write dir>/run_counter_collection.csv"],
-           "unit": "bytes per kda_prefill_cp call (all six launches), counters scaled by the 1 GiB negation"}
+           "unit": "bytes per kda_prefill_cp call (all five launches), counters scaled by the 1 GiB negation"}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _pmc_rows(path)
         calib = max(v for n, v in rows.values() if "neg" in n.lower())
         factor = float(1 << 30) / (calib * 1024.0)
-        # one kda_prefill_cp call = two plan launches and one launch of each
-        # other kind below (each kind is averaged over its own launches)
+        # one kda_prefill_cp call = one launch of each kind below (each kind
+        # is averaged over its own launches: the plan and combine kernels also
+        # serve the backward)
         kinds = {"plan": lambda n: "kda_cp_plan_kernel" in n,
                  "chunk_operands": lambda n: "kda_prefill_kernel" in n and "Li1EEE" in n,
                  # kda_chain_kernel<TIn, C, NW, NCT, SUMMARY, SB, SNAP>: the 5th argument
@@ -119,8 +120,7 @@ def write_traffic(fetch_csv, write_csv):
             vals = [v for n, v in rows.values() if match(n)]
             per_kind[kind] = {"launches": len(vals), "kib_avg_raw": sum(vals) / max(len(vals), 1),
                               "bytes_avg": sum(vals) / max(len(vals), 1) * 1024.0 * factor}
-        # launches per call: the plan kernel runs twice (output segments, summary units)
-        per_call = sum(k["kib_avg_raw"] * (2 if kind == "plan" else 1) for kind, k in per_kind.items()) * 1024.0
+        per_call = sum(k["kib_avg_raw"] for k in per_kind.values()) * 1024.0
         out[counter] = {"calibration_kib": calib, "scale": factor, "per_kernel": per_kind,
                         "kib_per_call_raw": per_call / 1024.0, "bytes_per_call": per_call * factor}
         total += per_call * factor

@@ -19,7 +19,9 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
                                          int32_t last_len, int32_t skip_last, int32_t *seq_order,
-                                         hipStream_t stream);
+                                         int32_t seg_len2, int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
+                                         int32_t *sched2, int32_t last_len2, int32_t skip_last2,
+                                         int32_t *seq_order2, hipStream_t stream);
 extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
                                             const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
                                             int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
@@ -290,13 +292,11 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
     float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
     void *img = ws + lay.img;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // output segments, then summary units (SEG_LAST: in a sequence's last segment)
-    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, sched, 0, 0, nullptr, s);
+    // output segments and summary units (SEG_LAST: in a sequence's last segment), one launch
     int32_t *seq_order = reinterpret_cast<int32_t *>(ws + lay.seq_order);
-    if (e == hipSuccess)
-        e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.unit_len, lay.max_units, uplan, useq_seg,
-                               kCpChunk, lay.max_chunks, nullptr, usched, seg_len, 1, seq_order, s);
+    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
+                                      kCpChunk, lay.max_chunks, chunk_off, sched, 0, 0, nullptr, lay.unit_len,
+                                      lay.max_units, uplan, useq_seg, usched, seg_len, 1, seq_order, s);
     if (e == hipSuccess)   // chunk operands of every (chunk, head)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, s);
@@ -463,7 +463,8 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     // segments and chunk numbering; no segment is marked last, so the forward
     // summaries include every segment's transition
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, sched, -1, 0, nullptr, s);
+                                      kCpChunk, lay.max_chunks, chunk_off, sched, -1, 0, nullptr, 0, 0, nullptr,
+                                      nullptr, nullptr, 0, 0, nullptr, s);
     // forward: the state at every chunk start, by the context-parallel
     // pipeline with state stores and no outputs
     if (e == hipSuccess)

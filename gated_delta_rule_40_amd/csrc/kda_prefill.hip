@@ -1443,14 +1443,22 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
 // chunk_off is given, the first chunk of each sequence in chunks of `chunk`
 // tokens (chunk_off[N] = total chunks, at most max_chunks); and, if sched is
 // given, a dispatch order of the max_segs plan entries (a permutation).
+struct PlanArgs {
+    int32_t seg_len, max_segs;
+    int32_t *plan, *seq_seg, *chunk_off, *sched;   // chunk_off, sched may be nullptr
+    int32_t last_len, skip_last;
+    int32_t *seq_order;                            // may be nullptr
+};
+// One plan per workgroup: workgroup b builds plan b (a second plan of the
+// same sequences at another granularity costs no extra launch).
 __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restrict__ cu, int32_t N,
-                                                          int32_t T_tot, int32_t seg_len, int32_t max_segs,
-                                                          int32_t *__restrict__ plan,
-                                                          int32_t *__restrict__ seq_seg, int32_t chunk,
-                                                          int32_t max_chunks, int32_t *__restrict__ chunk_off,
-                                                          int32_t *__restrict__ sched, int32_t last_len,
-                                                          int32_t skip_last, int32_t *__restrict__ seq_order)
+                                                          int32_t T_tot, int32_t chunk, int32_t max_chunks,
+                                                          PlanArgs a0, PlanArgs a1)
 {
+    const PlanArgs &pa = blockIdx.x == 0 ? a0 : a1;
+    const int32_t seg_len = pa.seg_len, max_segs = pa.max_segs, last_len = pa.last_len, skip_last = pa.skip_last;
+    int32_t *const plan = pa.plan, *const seq_seg = pa.seq_seg, *const chunk_off = pa.chunk_off;
+    int32_t *const sched = pa.sched, *const seq_order = pa.seq_order;
     __shared__ int64_t scan[256], cscan[256];
     __shared__ int32_t hist[256];
     int64_t carry = 0, ccarry = 0;                     // 64-bit: cu is not trusted
@@ -1730,17 +1738,32 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
 // last_len tokens (a multiple of seg_len; 0 = seg_len: the last segment;
 // negative: no segment is marked, so a summary pass covers them all);
 // skip_last: those segments go last in the dispatch order; seq_order
-// (optional, [N]): the sequences by segment count, most first.
+// (optional, [N]): the sequences by segment count, most first.  A second plan
+// (plan2 != nullptr, with its own seg_len2 ... seq_order2) is built by a
+// second workgroup of the same launch.
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
                                          int32_t last_len, int32_t skip_last, int32_t *seq_order,
-                                         hipStream_t stream)
+                                         int32_t seg_len2, int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
+                                         int32_t *sched2, int32_t last_len2, int32_t skip_last2,
+                                         int32_t *seq_order2, hipStream_t stream)
 {
-    if (last_len == 0) last_len = seg_len;
-    if (seg_len <= 0 || (last_len > 0 && last_len % seg_len)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(1), dim3(256), 0, stream, cu, N, T_tot, seg_len, max_segs,
-                       plan, seq_seg, chunk, max_chunks, chunk_off, sched, last_len, skip_last, seq_order);
+    auto args = [](int32_t sl, int32_t ms, int32_t *p, int32_t *ss, int32_t *co, int32_t *sc, int32_t ll,
+                   int32_t sk, int32_t *so, kda::PlanArgs *a) {
+        if (ll == 0) ll = sl;
+        if (sl <= 0 || (ll > 0 && ll % sl)) return false;
+        *a = {sl, ms, p, ss, co, sc, ll, sk, so};
+        return true;
+    };
+    kda::PlanArgs a0, a1;
+    if (!args(seg_len, max_segs, plan, seq_seg, chunk_off, sched, last_len, skip_last, seq_order, &a0))
+        return hipErrorInvalidValue;
+    a1 = a0;
+    if (plan2 && !args(seg_len2, max_segs2, plan2, seq_seg2, nullptr, sched2, last_len2, skip_last2, seq_order2, &a1))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(plan2 ? 2 : 1), dim3(256), 0, stream, cu, N, T_tot, chunk,
+                       max_chunks, a0, a1);
     return hipGetLastError();
 }
 
