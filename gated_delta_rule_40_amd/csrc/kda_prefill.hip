@@ -1075,13 +1075,8 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 {
     typedef PrefillCfg<TIn, C, NW> P;
     auto kern = kda_prefill_kernel<TIn, C, NW, MODE>;
-    static bool attr_set = false;   // idempotent; racing threads set the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)P::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)P::bytes, lds_set)) return e;
     const int64_t units = (int64_t)N * H;
     const int nblk = dv / P::BV;
     const int64_t groups = (units + 7) / 8;
@@ -1390,13 +1385,8 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
 {
     typedef PrefillCfg<TIn, C, 4> P;
     auto kern = kda_prefill_kernel<TIn, C, 4, MODE_PREP>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)P::bytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)P::bytes, lds_set)) return e;
     // fewer chunks per workgroup when there are few: every compute unit
     // gets work, and a workgroup's walk is short
     const int64_t want = (max_chunks * H + 2047) / 2048;
@@ -1420,13 +1410,8 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
     auto kern = kind == 1 ? kda_chain_kernel<TIn, C, NW, NCT, true, SB>
                           : (kind == 2 ? kda_chain_kernel<TIn, C, NW, NCT, false, SB, true>
                                        : kda_chain_kernel<TIn, C, NW, NCT, false, SB>);
-    static bool attr_set[3] = {false, false, false};   // idempotent; racing threads set the same value
-    if (!attr_set[kind]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q::bytes);
-        if (e != hipSuccess) return e;
-        attr_set[kind] = true;
-    }
+    static std::atomic<uint64_t> lds_set[3];
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)Q::bytes, lds_set[kind])) return e;
     const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
     const int nblk = (summary ? dv + DK : dv) / Q::BV;
     const int64_t grid = (units + 7) / 8 * 8 * nblk;

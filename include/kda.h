@@ -19,7 +19,9 @@
  * Conventions for every call:
  *   - Device pointers are on the current HIP device, dense and row-major as
  *     documented; the caller owns every buffer.  The library allocates no
- *     device memory and keeps no mutable global state (thread-safe).
+ *     device memory.  Its only global state is a per-device record (atomic
+ *     bits) that each kernel's LDS limit has been raised; calls are
+ *     thread-safe.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never
  *     synchronise.  Argument errors are returned before any HIP call; a
  *     launch failure returns KDA_ERR_LAUNCH; device faults surface at the
