@@ -139,9 +139,13 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  * fixed-size-state-fragment scheme of page ailearn.mscapital.top/kimi-k3.html,
  * card "传固定状态片段" (local cumulative transform and zero-state fragment,
  * then a prefix combination), applied across the compute units of one GPU.
- * Results equal kda_prefill up to fp32 rounding order.
+ * Results equal kda_prefill up to fp32 rounding order.  When there are many
+ * (segment, head) pairs, the zero-state runs and the chaining use summary
+ * units of a quarter (or half) segment instead of whole segments, so that
+ * they pack the compute units evenly; the outputs still run whole segments.
  *
  *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
+ *              (total_tokens * num_heads / 512, clamped to [512, 65536])
  *   workspace  device memory of at least kda_prefill_cp_workspace_size(...)
  *              bytes, 256-byte aligned, owned by the caller, contents
  *              ignored on entry; calls that share one workspace must not
@@ -222,7 +226,9 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  * Sequences are cut into segments that run side by side, as in
  * kda_prefill_cp (card "传固定状态片段"): the gradient recurrence is linear in
  * the state's gradient, so each segment's gradient summary combines, in reverse
- * segment order, into the gradient entering every segment.
+ * segment order, into the gradient entering every segment.  A segment's
+ * gradient transition is the transpose of its forward transition, which the
+ * forward pass that stores the chunk-start states computes anyway.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, dtype: as kda_prefill
  *   dout          [total_tokens, num_heads, dv]   dtype
