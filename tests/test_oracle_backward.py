@@ -9,7 +9,9 @@ the initial state.
 * central finite differences of the C forward oracle, on inputs and steps
   exactly representable in fp32 (so the fp64 forward sees exact perturbations);
 * the closed form at beta = 0 (pure decay);
-* a planted sign error is caught by the finite-difference check.
+* a planted sign error is caught by the finite-difference check;
+* the gradient transition of a stretch of tokens is the transpose of its
+  forward transition (which the GPU backward takes from the forward pass).
 """
 import numpy as np
 import pytest
@@ -131,3 +133,30 @@ def test_backward_beta_zero_closed_form():
         dS0 += np.exp(Gam[t])[:, None] * np.outer(inp["q"][t, 0], inp["dout"][t, 0])
     assert np.allclose(got["dinit"][0, 0], dS0, atol=1e-12)
     assert np.abs(got["dv"]).max() == 0 and np.abs(got["dk"]).max() == 0
+
+
+def test_gradient_transition_is_transpose_of_forward_transition():
+    """With v = 0 and dout = 0 the forward map init -> final_state is the
+    segment transition M (per value column) and the backward map
+    dfinal -> dinit is the gradient transition R.  R = M^T: the gradient step
+    Diag(alpha)(I - beta k k^T) is the transpose of the forward step
+    (I - beta k k^T) Diag(alpha), and the steps run in the opposite order.
+    M is built column by column from unit initial states and compared with
+    the R the backward oracle applies to unit dfinal matrices."""
+    inp = _inputs([37], H=1, dk=6, dv=6, seed=91)
+    inp["g"] = (inp["g"] * np.float32(0.05)).astype(np.float32)   # weak decay: M stays well above rounding
+    zero_v = np.zeros_like(inp["v"])
+    dk = 6
+    M = np.zeros((dk, dk))
+    R = np.zeros((dk, dk))
+    for j in range(dk):
+        e = np.zeros((1, 1, dk, 6))
+        e[0, 0, j, 0] = 1.0                               # value column 0 carries unit vector e_j
+        _, fin = O.prefill(inp["q"], inp["k"], zero_v, inp["g"], inp["beta"], e, inp["cu"])
+        M[:, j] = fin[0, 0, :, 0]
+        gr = O.backward(inp["q"], inp["k"], zero_v, inp["g"], inp["beta"], e * 0.0, inp["cu"],
+                        np.zeros_like(inp["dout"][:, :, :6]), e)
+        R[:, j] = gr["dinit"][0, 0, :, 0]
+    assert np.abs(M).max() > 1e-2                          # a nontrivial transition
+    assert np.abs(M - M.T).max() > 1e-3                    # and not symmetric: the transpose matters
+    np.testing.assert_allclose(R, M.T, rtol=1e-12, atol=1e-14)
