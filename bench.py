@@ -73,6 +73,67 @@ def pmc_traffic():
         return None
 
 
+# the launches of one kda_prefill_cp call, by kernel name
+CP_KINDS = {"plan": lambda n: "kda_cp_plan_kernel" in n,
+            "chunk_operands": lambda n: "kda_prefill_kernel" in n and "Li1EEE" in n,
+            # kda_chain_kernel<TIn, C, NW, NCT, SUMMARY, SB, SNAP>: the 5th argument
+            "summaries": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "1",
+            "combine": lambda n: "kda_cp_combine_kernel" in n,
+            "outputs": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "0"}
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_mfma.json")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+
+
+def write_mfma(path):
+    """Executed MFMA work per kda_prefill_cp call from one rocprofv3 --pmc run of
+    the four MFMA_COUNTERS (timed steps only): fp16 and fp32 MFMA flops (each
+    MOPS unit is 512 flops) per kernel kind and per call, and the share of
+    cycles the MFMA units were busy."""
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            name, vals = rows.setdefault(d, (r["Kernel_Name"], {}))
+            vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    first_extra = min((d for d, (n, _) in rows.items() if "kda_decode_tokens_kernel" in n), default=None)
+    rows = {d: v for d, v in rows.items() if first_extra is None or d < first_extra}
+    out = {"kernel_source_sha256_16": source_hash(PREFILL_SRC),
+           "commands": ["cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <dir> -o run "
+                        "-- python <repo>/bench.py --steps 1 --warmup 1 --decode-steps 2 --no-cpu-baseline"
+                        % " ".join(MFMA_COUNTERS),
+                        "python bench.py --mfma-from <dir>/run_counter_collection.csv"],
+           "unit": "flops executed by MFMA instructions per kda_prefill_cp call (MOPS x 512); 'raw' holds "
+                   "each counter's average per launch as rocprofv3 reports it"}
+    per_kind, f16, f32 = {}, 0.0, 0.0
+    for kind, match in CP_KINDS.items():
+        ks = [v for n, v in rows.values() if match(n)]
+        avg = lambda c: sum(k.get(c, 0.0) for k in ks) / max(len(ks), 1)
+        per_kind[kind] = {"launches": len(ks), "f16_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_F16") * 512,
+                          "f32_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_F32") * 512,
+                          "raw": {c: avg(c) for c in MFMA_COUNTERS}}
+        f16 += per_kind[kind]["f16_flops"]
+        f32 += per_kind[kind]["f32_flops"]
+    out.update(per_kernel=per_kind, f16_flops_per_call=f16, f32_flops_per_call=f32)
+    with open(MFMA_SUMMARY, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def pmc_mfma():
+    """(fp16, fp32) MFMA flops per prefill call from the committed counter
+    summary, if it was taken on the current kernel source (else None)."""
+    try:
+        with open(MFMA_SUMMARY) as f:
+            d = json.load(f)
+        if d.get("kernel_source_sha256_16") != source_hash(PREFILL_SRC):
+            return None
+        return float(d["f16_flops_per_call"]), float(d["f32_flops_per_call"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def _pmc_rows(path):
     """{dispatch id: (kernel name, counter value in KiB)} from a rocprofv3 counter
     CSV, for the timed steps only: the dispatches before the first replay
@@ -106,17 +167,11 @@ def write_traffic(fetch_csv, write_csv):
         rows = _pmc_rows(path)
         calib = max(v for n, v in rows.values() if "neg" in n.lower())
         factor = float(1 << 30) / (calib * 1024.0)
-        # one kda_prefill_cp call = one launch of each kind below (each kind
-        # is averaged over its own launches: the plan and combine kernels also
+        # one kda_prefill_cp call = one launch of each kind (each kind is
+        # averaged over its own launches: the plan and combine kernels also
         # serve the backward)
-        kinds = {"plan": lambda n: "kda_cp_plan_kernel" in n,
-                 "chunk_operands": lambda n: "kda_prefill_kernel" in n and "Li1EEE" in n,
-                 # kda_chain_kernel<TIn, C, NW, NCT, SUMMARY, SB, SNAP>: the 5th argument
-                 "summaries": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "1",
-                 "combine": lambda n: "kda_cp_combine_kernel" in n,
-                 "outputs": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "0"}
         per_kind = {}
-        for kind, match in kinds.items():
+        for kind, match in CP_KINDS.items():
             vals = [v for n, v in rows.values() if match(n)]
             per_kind[kind] = {"launches": len(vals), "kib_avg_raw": sum(vals) / max(len(vals), 1),
                               "bytes_avg": sum(vals) / max(len(vals), 1) * 1024.0 * factor}
@@ -186,9 +241,14 @@ def main():
     ap.add_argument("--seg-len", type=int, default=0, help="kda_prefill_cp segment length (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--mfma-from", metavar="PMC_CSV",
+                    help="write the executed-MFMA summary from a rocprofv3 --pmc run of the MFMA counters and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit (no GPU)")
     args = ap.parse_args()
+    if args.mfma_from:
+        write_mfma(args.mfma_from)
+        return
     if args.traffic_from:
         write_traffic(*args.traffic_from)
         return
@@ -274,6 +334,7 @@ def main():
     dec_bytes = Nd * Hd * DECODE_BYTES_PER_UNIT
     dec_gbs = dec_bytes / (dec_step_ms * 1e-3) / 1e9
     traffic = pmc_traffic()
+    mfma = pmc_mfma()
 
     # speculative-decoding replay: 4 draft tokens per (sequence, head) of the
     # decode batch, outputs for all of them and the state committed, one call
@@ -382,6 +443,11 @@ def main():
                         "dk": DK, "dv": DV, "io": "bf16 q/k/v/out, fp32 g/beta/state",
                         "initial_state": "zero", "ms": pre_avg, "head_tokens_per_s": head_tokens / (pre_avg * 1e-3),
                         "fref_tflops": pre_tflops, "mfma_frac_fref": pre_tflops / BF16_PEAK_TFLOPS,
+                        "mfma_executed": None if mfma is None else {
+                            "f16_tflops": mfma[0] / (pre_avg * 1e-3) / 1e12,
+                            "f32_tflops": mfma[1] / (pre_avg * 1e-3) / 1e12,
+                            "f16_frac_of_peak": mfma[0] / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "source": "rocprofv3 MFMA counters (profiles/kda_prefill_varlen_1m_h16_mfma.json)"},
                         "compute": "fp16 MFMA operands (exact power-of-two column scaling), fp32 accumulate and state"},
             "decode": {"num_seqs": Nd, "heads": Hd, "steps": args.decode_steps, "state_bytes": Nd * Hd * DK * DV * 4},
         },
