@@ -896,6 +896,7 @@ void kda_prefill_kernel(
         if constexpr (kPrep) {
             int n0, n1;
             chunk_range(min(ci + 1, nch - 1), n0, n1);
+            if (ci + 1 >= nch) n1 = n0 + 1;     // nothing left: every lane reads one (cached) row
             load_chunk(n0, n1);
         }
         __syncthreads();
