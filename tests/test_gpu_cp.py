@@ -44,8 +44,6 @@ def _check_cp(inp, tol, label, seg_len, use_init=True):
 LENGTHS = [1, 17, 64, 0, 100, 63, 65, 130, 200, 333]
 
 
-# seg_len 64 and 128 cut every segment into 2 and 4 summary units; 96 (three
-# chunks) keeps one unit per segment
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("seg_len", [32, 64, 96, 128])
 def test_cp_ragged_vs_oracle(dtype, seg_len):
@@ -130,6 +128,17 @@ def test_cp_empty_sequences_and_untouched_rows():
     ref_out, ref_fin = oracle_prefill(inp)
     assert_close(host(out)[:T], ref_out[:T], TOL[torch.bfloat16], "cp untouched out", torch.bfloat16)
     assert_close(host(fin), ref_fin, TOL[torch.bfloat16], "cp untouched final_state")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("seg_len", [128, 192])
+def test_cp_summary_units_vs_oracle(dtype, seg_len):
+    # (total_tokens / seg_len) x heads >= 256: the summaries and the combine
+    # run on units, four (seg_len 128) or two (192: six chunks) per segment,
+    # and every segment's output run starts from its first unit's state
+    inp = to_dev(I.random_prefill([400, 0, 333, 380, 1], H=64, dtype=dtype, seed=41))
+    assert (inp["q"].shape[0] // seg_len) * 64 >= 256
+    _check_cp(inp, TOL[dtype], "cp_units", seg_len)
 
 
 def test_cp_many_sequences_vs_oracle():
