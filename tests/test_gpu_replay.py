@@ -118,3 +118,42 @@ def test_replay_512x32_four_tokens():
     _, ref_out, ref_fin = _oracle(inp, [draft] * N)
     assert_close(host(out), ref_out, TOL[torch.bfloat16], "512x32 out", torch.bfloat16)
     assert_close(host(state), ref_fin, TOL[torch.bfloat16], "512x32 state")
+
+
+def test_odd_pair_count_and_runs_past_the_staged_tokens():
+    """An odd number of (sequence, head) pairs (a workgroup takes two: the last
+    one has a single pair) and sequences longer than the tokens whose vectors
+    are read up front (four), against the oracle."""
+    lengths = [9, 1, 0, 13, 5]                                 # 3 heads: 15 pairs
+    inp = _draft(lengths, H=3, dtype=torch.bfloat16, seed=46)
+    T, H = inp["q"].shape[:2]
+    out = torch.full((T, H, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    state_out = torch.empty_like(inp["initial_state"])
+    K.kda_decode_tokens(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"],
+                        inp["initial_state"], state_out=state_out, out=out)
+    torch.cuda.synchronize()
+    rows, ref_out, ref_fin = _oracle(inp, lengths)
+    assert_close(host(out)[rows], ref_out, TOL[torch.bfloat16], "odd pairs out", torch.bfloat16)
+    assert_close(host(state_out), ref_fin, TOL[torch.bfloat16], "odd pairs state")
+
+
+def test_no_tokens_commits_the_state_unchanged():
+    """total_tokens = 0: no token is processed; state_out receives state_in
+    bit for bit (and in place it stays as it is)."""
+    N, H = 3, 2
+    lib = K.load()
+    dummy = torch.zeros(4, 128, dtype=torch.bfloat16, device="cuda")   # never read
+    gdummy = torch.zeros(4, 128, dtype=torch.float32, device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    state_in = torch.randn(N, H, 128, 128, dtype=torch.float32, device="cuda")
+    keep = state_in.clone()
+    state_out = torch.full_like(state_in, float("nan"))
+    p = dummy.data_ptr()
+    for so in (state_out, state_in):
+        st = lib.kda_decode_tokens(p, p, p, gdummy.data_ptr(), gdummy.data_ptr(), cu.data_ptr(), None,
+                                   state_in.data_ptr(), so.data_ptr(), N, 0, H, 128, 128, K.KDA_BF16, p,
+                                   K._stream(None))
+        assert st == K.KDA_OK, K.status_string(st)
+    torch.cuda.synchronize()
+    assert torch.equal(state_out, keep)
+    assert torch.equal(state_in, keep)
