@@ -634,20 +634,34 @@ void kda_prefill_kernel(
         t_end = min(max(t_end, t_start), total_tokens);
         nch = (t_end - t_start + C - 1) / C;
     }
-    // chunk ci of this workgroup: tokens [c0, min(c0 + C, cend))
-    auto chunk_range = [&](int ci, int &c0, int &cend) {
-        if constexpr (kPrep) {
-            const int gc = gc_begin + ci;
+    // chunk-operand pass: the token range of each of the workgroup's chunks,
+    // found once (thread ci searches chunk_off for chunk gc_begin + ci) and
+    // kept in LDS.  Searching inside the chunk loop would put a chain of
+    // dependent loads there, and waiting for each of them waits for every
+    // memory operation in flight (they complete in order): the prefetched
+    // next chunk and the image stores of the previous one.
+    __shared__ int32_t prep_rng[2 * PREP_GROUP];
+    if constexpr (kPrep) {
+        if (threadIdx.x < (unsigned)nch) {
+            const int gc = gc_begin + (int)threadIdx.x;
             int lo = 0, hi = num_seqs;                 // chunk_off[lo] <= gc < chunk_off[hi]
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
                 if (seg.chunk_off[mid] <= gc) lo = mid; else hi = mid;
             }
             const int s0 = min(max(cu_seqlens[lo], 0), total_tokens);
-            cend = min(max(cu_seqlens[lo + 1], s0), total_tokens);
+            prep_rng[2 * threadIdx.x + 1] = min(max(cu_seqlens[lo + 1], s0), total_tokens);
             // in range for any valid cu_seqlens; the clamp keeps every load in
             // bounds for any other contents
-            c0 = min(s0 + (gc - seg.chunk_off[lo]) * C, total_tokens - 1);
+            prep_rng[2 * threadIdx.x] = min(s0 + (gc - seg.chunk_off[lo]) * C, total_tokens - 1);
+        }
+        __syncthreads();
+    }
+    // chunk ci of this workgroup: tokens [c0, min(c0 + C, cend))
+    auto chunk_range = [&](int ci, int &c0, int &cend) {
+        if constexpr (kPrep) {
+            c0 = prep_rng[2 * ci];
+            cend = prep_rng[2 * ci + 1];
         } else {
             c0 = t_start + ci * C;
             cend = t_end;
@@ -746,9 +760,9 @@ void kda_prefill_kernel(
                                     : *reinterpret_cast<const f32x4 *>(v + (int64_t)(cc0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
             }
         }
-        if (tid < C) rb = beta[(int64_t)(cc0 + min(tid, LL - 1)) * H + h];
+        rb = beta[(int64_t)(cc0 + min(tid, LL - 1)) * H + h];   // used by tid < C; unconditional, as above
     };
-    if (nch > 0) {
+    if (kPrep || nch > 0) {   // (the chunk-operand pass has nch >= 1: no branch around its loads)
         int a0, a1;
         chunk_range(0, a0, a1);
         load_chunk(a0, a1);
@@ -772,6 +786,22 @@ void kda_prefill_kernel(
                                       (uint32_t)P::offBeta, (uint32_t)P::offTs};
 #pragma unroll
         for (int it = 0; it < SITEMS; ++it) img_off[it] = Img::lds_off(min(tid + it * NT, Img::NVEC - 1), o);
+        // One placeholder store per image item after the first chunk's loads,
+        // so that the loop is entered as it is re-entered from its end (the
+        // chunk's loads followed by SITEMS stores): the compiler merges the two
+        // paths at the loop head and, were they to differ, would count as if
+        // there were no stores after the loads, and wait for the previous
+        // chunk's image stores before each use of the prefetched data.  Each
+        // placeholder goes to an address of chunk gc_begin's image that only
+        // this thread writes, and this thread's real store there follows it.
+        // (nch >= 1 here: a workgroup without chunks has returned)
+        static_assert(Img::NVEC >= NT, "every thread owns an image item");
+        f32x4 *dst0 = seg.img + ((int64_t)gc_begin * num_heads + h) * Img::NVEC;
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            const int idx = tid + it * NT;                      // past the end: this thread's previous item
+            dst0[idx < Img::NVEC ? idx : idx - NT] = zero4();
+        }
     }
     for (int ci = 0; ci < nch; ++ci) {
         int c0, cend;
