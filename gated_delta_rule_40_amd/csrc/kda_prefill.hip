@@ -1272,8 +1272,12 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         for (int it = 0; it < Q::VITEMS; ++it) {
             const int e = min(tid + it * NT, C * VPR - 1);
             const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
-            rv[it] = dv0 + cv >= dv ? zero4()      // transition columns: V = 0
-                                    : *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv + dv0 + cv);
+            // transition columns (V = 0) read the row's last value vector,
+            // zeroed when staged: with no branch around the load the compiler
+            // counts the loads in flight exactly, and does not wait for newer
+            // ones (a zero chosen here would become such a branch)
+            rv[it] = *reinterpret_cast<const f32x4 *>(v + (int64_t)(c0 + rc) * rowV + (int64_t)h * dv +
+                                                      min(dv0 + cv, dv - VEC));
         }
     };
     auto load = [&](int ci) { load_to(ci, ri, rv); };
@@ -1295,7 +1299,7 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         for (int it = 0; it < Q::VITEMS; ++it) {
             const int e = min(tid + it * NT, C * VPR - 1);
             const int r = e / VPR, cv = (e % VPR) * VEC;
-            *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < LL ? rv[it] : zero4();
+            *reinterpret_cast<f32x4 *>(sV + r * LDV + cv) = r < LL && dv0 + cv < dv ? rv[it] : zero4();
         }
     };
     auto stage = [&](int ci, int b) { stage_from(ci, b, ri, rv); };
