@@ -160,6 +160,7 @@ struct SegArgs {
     const int32_t *init_seq_seg;
     int32_t init_unit, init_units;
     int32_t prep_group;         // chunk-operand pass: consecutive chunks per workgroup (1 .. PREP_GROUP)
+    int32_t img_slots;          // chunk-operand pass: image slots per head (> chunks of valid input)
 };
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
@@ -791,17 +792,14 @@ void kda_prefill_kernel(
         // chunk's loads followed by SITEMS stores): the compiler merges the two
         // paths at the loop head and, were they to differ, would count as if
         // there were no stores after the loads, and wait for the previous
-        // chunk's image stores before each use of the prefetched data.  Each
-        // placeholder goes to an address of chunk gc_begin's image that only
-        // this thread writes, and this thread's real store there follows it.
-        // (nch >= 1 here: a workgroup without chunks has returned)
-        static_assert(Img::NVEC >= NT, "every thread owns an image item");
-        f32x4 *dst0 = seg.img + ((int64_t)gc_begin * num_heads + h) * Img::NVEC;
+        // chunk's image stores before each use of the prefetched data.  The
+        // placeholders go to the last image slot of this head, which valid
+        // input never uses (there are more slots than chunks); every
+        // workgroup of the head writes the same zeros there, so the lines
+        // stay in L2.  (nch >= 1 here: a workgroup without chunks has returned)
+        f32x4 *junk = seg.img + ((int64_t)(seg.img_slots - 1) * num_heads + h) * Img::NVEC;
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int idx = tid + it * NT;                      // past the end: this thread's previous item
-            dst0[idx < Img::NVEC ? idx : idx - NT] = zero4();
-        }
+        for (int it = 0; it < SITEMS; ++it) junk[min(tid + it * NT, Img::NVEC - 1)] = zero4();
     }
     for (int ci = 0; ci < nch; ++ci) {
         int c0, cend;
@@ -1794,8 +1792,9 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
                                             hipStream_t stream)
 {
     using namespace kda;
+    if (max_chunks < 1 || max_chunks > 0x7fffffff) return hipErrorInvalidValue;
     SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr,
-                   nullptr, 0, 0, PREP_GROUP};
+                   nullptr, 0, 0, PREP_GROUP, (int32_t)max_chunks};
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
