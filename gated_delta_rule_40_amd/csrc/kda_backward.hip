@@ -166,7 +166,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
 // area belongs to the workgroup, not the item).  seg_dsend: [num_segs][H][BD][BD],
 // the gradient entering each segment at its end.  part_vec: [NBLK][3][T_tot * H][BD]
 // partial row sums (dq, dk, dg); part_beta: [NBLK][T_tot * H]; scratch:
-// [gridDim.x][BWD_C / BWD_G][BD][BWD_BV] floats; snaps: [chunks][H][BD][BD], the
+// [gridDim.x][BWD_C / BWD_G + 1][BD][BWD_BV] floats; snaps: [chunks][H][BD][BD], the
 // state at the start of global chunk chunk_off[n] + c for c >= 1 (c = 0 is the
 // initial state).
 //
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
     const int rg = lane & 15, cg = lane >> 4;
     const int64_t rows_all = (int64_t)T_tot * H;
     // scratch: [checkpoint][wave][4][lane] f32x4, rows rg + 16 i of the lane's two columns
-    f32x4 *scr = reinterpret_cast<f32x4 *>(scratch + (int64_t)blockIdx.x * (BWD_C / BWD_G) * BD * BWD_BV) +
+    f32x4 *scr = reinterpret_cast<f32x4 *>(scratch + (int64_t)blockIdx.x * (BWD_C / BWD_G + 1) * BD * BWD_BV) +
                  wave * 4 * 64 + lane;
     constexpr int CK = NWV * 4 * 64;                             // f32x4 per checkpoint
     const int64_t items = (int64_t)num_segs * H * BWD_NBLK;
@@ -259,53 +259,78 @@ __global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
         for (int i = 0; i < 8; ++i)
             S[i] = src ? *reinterpret_cast<const f32x2 *>(src + (int64_t)(rg + 16 * i) * BD + cb) : f32x2{0.f, 0.f};
 
-        // ---- forward over the chunk: u of every token; the state before every 4th
-        // token to the scratch area.  Token vectors one step ahead (clamped rows).
-        Raw2 fk, fv;
-        f32x2 fg;
-        float fb;
-        auto fetch1 = [&](int j) {
-            const int64_t row = (int64_t)(c0 + j) * H + h;
-            fk = *reinterpret_cast<const Raw2 *>(k + row * BD + 2 * lane);
-            fg = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
-            fv = *reinterpret_cast<const Raw2 *>(v + row * BD + cb);
-            fb = beta[row];
+        // ---- forward over the chunk in groups of BWD_G tokens: u of every
+        // token; the state before every group to the scratch area.  A group's
+        // token vectors are loaded while the group before it runs, ahead of
+        // that group's state store: vector memory operations complete in
+        // order, so a load issued after a store could not be waited for
+        // without waiting for the store.  Every step is branch-free (tokens
+        // past the chunk's end are neutral: decay 1, write strength 0), so the
+        // compiler counts the operations in flight exactly.
+        // Two register sets in turn (groups taken in pairs, the group count
+        // padded to even with neutral groups): a set loaded during one group
+        // and read in the next would otherwise be copied at the loop's end,
+        // and the copy waits for the load.
+        struct FwdSet { Raw2 k[BWD_G], v[BWD_G]; f32x2 g[BWD_G]; float b[BWD_G]; };
+        FwdSet fa, fb_;
+        auto fetch_fwd = [&](int m, FwdSet &f) {
+#pragma unroll
+            for (int jj = 0; jj < BWD_G; ++jj) {
+                const int64_t row = (int64_t)(c0 + min(m * BWD_G + jj, Lc - 1)) * H + h;
+                f.k[jj] = *reinterpret_cast<const Raw2 *>(k + row * BD + 2 * lane);
+                f.g[jj] = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
+                f.v[jj] = *reinterpret_cast<const Raw2 *>(v + row * BD + cb);
+                f.b[jj] = beta[row];
+            }
+            asm volatile("" ::: "memory");   // keep the loads here
         };
-        fetch1(0);
-        for (int j = 0; j < Lc; ++j) {
-            if ((j & (BWD_G - 1)) == 0) {
-                f32x4 *sj = scr + (j / BWD_G) * CK;
+        auto store_state = [&](int m) {   // the state before token m * BWD_G (slot m; slot BWD_C / BWD_G is spare)
+            f32x4 *sj = scr + m * CK;
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    sj[p * 64] = f32x4{S[2 * p][0], S[2 * p][1], S[2 * p + 1][0], S[2 * p + 1][1]};
-            }
-            const Raw2 kk = fk, vv = fv;
-            const f32x2 gg = fg;
-            const float bt = fb;
-            fetch1(min(j + 1, Lc - 1));
-            float *w = tv[wave][0][0];
-            put(w, to_f(kk[0]), to_f(kk[1]));
-            put(w + BD, __expf(gg[0]), __expf(gg[1]));
-            __builtin_amdgcn_wave_barrier();
-            float kr[8], ar[8];
-            get(w, kr);
-            get(w + BD, ar);
-            __builtin_amdgcn_wave_barrier();
-            float pa0 = 0.f, pa1 = 0.f;
+            for (int p = 0; p < 4; ++p)
+                sj[p * 64] = f32x4{S[2 * p][0], S[2 * p][1], S[2 * p + 1][0], S[2 * p + 1][1]};
+        };
+        auto fwd_group = [&](int m, const FwdSet &f) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                S[i] *= ar[i];
-                pa0 += S[i][0] * kr[i];
-                pa1 += S[i][1] * kr[i];
-            }
-            const float u0 = to_f(vv[0]) - sum16(pa0), u1 = to_f(vv[1]) - sum16(pa1);
-            if (rg == 0) *reinterpret_cast<f32x2 *>(&su[wave][j][2 * cg]) = f32x2{u0, u1};
+            for (int jj = 0; jj < BWD_G; ++jj) {
+                const int j = m * BWD_G + jj;
+                const bool ok = j < Lc;
+                float *w = tv[wave][0][0];
+                put(w, to_f(f.k[jj][0]), to_f(f.k[jj][1]));
+                put(w + BD, ok ? __expf(f.g[jj][0]) : 1.f, ok ? __expf(f.g[jj][1]) : 1.f);
+                __builtin_amdgcn_wave_barrier();
+                float kr[8], ar[8];
+                get(w, kr);
+                get(w + BD, ar);
+                __builtin_amdgcn_wave_barrier();
+                float pa0 = 0.f, pa1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float bk = bt * kr[i];
-                S[i][0] += bk * u0;
-                S[i][1] += bk * u1;
+                for (int i = 0; i < 8; ++i) {
+                    S[i] *= ar[i];
+                    pa0 += S[i][0] * kr[i];
+                    pa1 += S[i][1] * kr[i];
+                }
+                const float u0 = to_f(f.v[jj][0]) - sum16(pa0), u1 = to_f(f.v[jj][1]) - sum16(pa1);
+                if (rg == 0) *reinterpret_cast<f32x2 *>(&su[wave][j][2 * cg]) = f32x2{u0, u1};
+                const float bt = ok ? f.b[jj] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float bk = bt * kr[i];
+                    S[i][0] += bk * u0;
+                    S[i][1] += bk * u1;
+                }
             }
+        };
+        const int ngf = (Lc + 2 * BWD_G - 1) / (2 * BWD_G) * 2;     // groups, padded to even (<= BWD_C / BWD_G)
+        fetch_fwd(0, fa);
+        store_state(0);
+        for (int m = 0; m < ngf; m += 2) {
+            fetch_fwd(m + 1, fb_);
+            fwd_group(m, fa);
+            store_state(m + 1);
+            fetch_fwd(min(m + 2, ngf - 1), fa);
+            fwd_group(m + 1, fb_);
+            store_state(m + 2);
         }
         __builtin_amdgcn_wave_barrier();
 
@@ -485,8 +510,8 @@ __global__ __launch_bounds__(256) void kda_backward_reduce_kernel(
 }  // namespace kda
 
 // Scratch floats per workgroup of the main pass, and the most workgroups it
-// launches (the item loop covers the rest): 512 x 128 KB of scratch at most.
-extern "C" size_t kda_backward_scratch_floats_per_wg() { return (size_t)(kda::BWD_C / kda::BWD_G) * kda::BD * kda::BWD_BV; }
+// launches (the item loop covers the rest): 512 x 144 KB of scratch at most.
+extern "C" size_t kda_backward_scratch_floats_per_wg() { return (size_t)(kda::BWD_C / kda::BWD_G + 1) * kda::BD * kda::BWD_BV; }
 extern "C" int32_t kda_backward_max_wgs() { return 512; }
 extern "C" int32_t kda_backward_num_blocks() { return kda::BWD_NBLK; }
 
