@@ -156,3 +156,17 @@ def test_cp_run_to_run_bitwise_determinism():
     o1, f1 = run_prefill_cp(inp, seg_len=64)
     o2, f2 = run_prefill_cp(inp, seg_len=64)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_cp_every_image_slot_but_the_spare_one_used(dtype):
+    # every length is 1 mod 32, so the chunk count reaches its bound less one:
+    # the chunk-operand pass's placeholder stores go to the one image slot
+    # past the last chunk, next to images the passes after it read
+    lengths = [33, 1, 97, 65, 129]
+    total = sum(lengths)
+    chunks = sum((n + 31) // 32 for n in lengths)
+    assert chunks == total // 32 + len(lengths)                # = the slots the workspace holds, less one
+    inp = to_dev(I.random_prefill(lengths, H=3, dtype=dtype, seed=42))
+    for seg_len in (32, 64):
+        _check_cp(inp, TOL[dtype], "cp_tight_slots", seg_len)
