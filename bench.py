@@ -223,10 +223,12 @@ def cpu_baseline(pre, H, target_s=20.0):
             lo = mid + 1
     Ls = lo
     t, tok = run(Ls)
+    what = ("all tokens of the %d sequences" % N if Ls >= max(lens)
+            else "the first %d tokens of each of the %d sequences" % (Ls, N))
     return {"value": tok / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "first %d tokens of each of the %d sequences x %d heads of the same prefill inputs "
+            "sample": "%s x %d heads of the same prefill inputs "
                       "(%d tokens, %d head-tokens, %.1f s, fp64 token loop, OpenMP over (sequence, head))"
-                      % (Ls, N, H, tok, tok * H, t)}
+                      % (what, H, tok, tok * H, t)}
 
 
 def main():
