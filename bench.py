@@ -16,6 +16,13 @@ HIP events recorded on the stream the kernels run on, inside the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--prefill cp|plain] [--seg-len L]
+
+Counter runs (rocprofv3 --pmc around one workload at a time) and the summaries
+under profiles/ that the JSON line reads while their kernel-source hash matches:
+
+    python bench.py --pmc-workload NAME           # 2 kda_prefill_cp calls + a 1 GiB negation
+    python bench.py --traffic-from FETCH.csv WRITE.csv --workload NAME
+    python bench.py --mfma-from MFMA.csv --workload NAME
 """
 import argparse
 import hashlib
@@ -35,6 +42,8 @@ DK = DV = 128
 PREFILL_BYTES_PER_HT = 3 * 2 * DK + 4 * DK + 4 + 2 * DV
 # reference chunk-form flops per head-token (three dk x dv contractions + chunk terms at C = 64)
 PREFILL_FREF_PER_HT = 6 * DK * DV + 2 * 64 * (DK + DV)
+# minimal flops per head-token: the three dk x dv contractions alone
+PREFILL_FALG_PER_HT = 6 * DK * DV
 # decode bytes per (sequence, head): state read + write, q/k/v/out bf16, g fp32, beta fp32
 DECODE_BYTES_PER_UNIT = 2 * DK * DV * 4 + 3 * 2 * DK + 4 * DK + 4 + 2 * DV
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
@@ -51,8 +60,14 @@ PREFILL_KERNELS = {
           "kda_chain_kernel<bf16,32,4 waves,2 tiles,output,single buffer>",
     "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
 }
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_traffic.json")
 PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_prefill.hip")
+PREFILL_WORKLOADS = ("prefill_t4096_h8", "prefill_4x16384_h32", "prefill_varlen_1m_h16")
+
+
+def profile_path(workload, kind):
+    """profiles/kda_prefill_<workload without its prefill_ prefix>_<kind>.json"""
+    short = workload[len("prefill_"):] if workload.startswith("prefill_") else workload
+    return os.path.join(ROOT, "profiles", "kda_prefill_%s_%s.json" % (short, kind))
 
 
 def source_hash(path):
@@ -60,11 +75,11 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def pmc_traffic():
-    """HBM bytes per prefill launch from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
+def pmc_traffic(workload):
+    """HBM bytes per kda_prefill_cp call on `workload` from the committed counter
+    summary, if it was taken on the current kernel source (else None)."""
     try:
-        with open(PMC_SUMMARY) as f:
+        with open(profile_path(workload, "traffic")) as f:
             d = json.load(f)
         if d.get("kernel_source_sha256_16") != source_hash(PREFILL_SRC):
             return None
@@ -80,16 +95,15 @@ CP_KINDS = {"plan": lambda n: "kda_cp_plan_kernel" in n,
             "summaries": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "1",
             "combine": lambda n: "kda_cp_combine_kernel" in n,
             "outputs": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "0"}
-MFMA_SUMMARY = os.path.join(ROOT, "profiles", "kda_prefill_varlen_1m_h16_mfma.json")
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
                  "GRBM_GUI_ACTIVE")
 
 
-def write_mfma(path):
-    """Executed MFMA work per kda_prefill_cp call from one rocprofv3 --pmc run of
-    the four MFMA_COUNTERS (timed steps only): fp16 and fp32 MFMA flops (each
-    MOPS unit is 512 flops) per kernel kind and per call, and the share of
-    cycles the MFMA units were busy."""
+def write_mfma(path, workload):
+    """Executed MFMA work per kda_prefill_cp call on `workload` from one
+    rocprofv3 --pmc run of the four MFMA_COUNTERS over ``--pmc-workload``:
+    fp16 and fp32 MFMA flops (each MOPS unit is 512 flops) per kernel kind and
+    per call, and the share of cycles the MFMA units were busy."""
     import csv
     rows = {}
     with open(path, newline="") as f:
@@ -99,11 +113,10 @@ def write_mfma(path):
             vals[r["Counter_Name"]] = vals.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     first_extra = min((d for d, (n, _) in rows.items() if "kda_decode_tokens_kernel" in n), default=None)
     rows = {d: v for d, v in rows.items() if first_extra is None or d < first_extra}
-    out = {"kernel_source_sha256_16": source_hash(PREFILL_SRC),
+    out = {"kernel_source_sha256_16": source_hash(PREFILL_SRC), "workload": workload,
            "commands": ["cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <dir> -o run "
-                        "-- python <repo>/bench.py --steps 1 --warmup 1 --decode-steps 2 --no-cpu-baseline"
-                        % " ".join(MFMA_COUNTERS),
-                        "python bench.py --mfma-from <dir>/run_counter_collection.csv"],
+                        "-- python <repo>/bench.py --pmc-workload %s" % (" ".join(MFMA_COUNTERS), workload),
+                        "python bench.py --mfma-from <dir>/run_counter_collection.csv --workload %s" % workload],
            "unit": "flops executed by MFMA instructions per kda_prefill_cp call (MOPS x 512); 'raw' holds "
                    "each counter's average per launch as rocprofv3 reports it"}
     per_kind, f16, f32 = {}, 0.0, 0.0
@@ -116,16 +129,17 @@ def write_mfma(path):
         f16 += per_kind[kind]["f16_flops"]
         f32 += per_kind[kind]["f32_flops"]
     out.update(per_kernel=per_kind, f16_flops_per_call=f16, f32_flops_per_call=f32)
-    with open(MFMA_SUMMARY, "w") as f:
+    with open(profile_path(workload, "mfma"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def pmc_mfma():
-    """(fp16, fp32) MFMA flops per prefill call from the committed counter
-    summary, if it was taken on the current kernel source (else None)."""
+def pmc_mfma(workload):
+    """(fp16, fp32) MFMA flops per kda_prefill_cp call on `workload` from the
+    committed counter summary, if it was taken on the current kernel source
+    (else None)."""
     try:
-        with open(MFMA_SUMMARY) as f:
+        with open(profile_path(workload, "mfma")) as f:
             d = json.load(f)
         if d.get("kernel_source_sha256_16") != source_hash(PREFILL_SRC):
             return None
@@ -151,16 +165,17 @@ def _pmc_rows(path):
             if first_extra is None or d < first_extra or "kda" not in v[0]}
 
 
-def write_traffic(fetch_csv, write_csv):
-    """HBM bytes per kda_prefill_cp call from two rocprofv3 --pmc runs of
-    ``bench.py --copy-calibration`` (FETCH_SIZE, then WRITE_SIZE), each scaled
-    by what the same counter reads for the 1 GiB-in / 1 GiB-out negation."""
-    out = {"kernel_source_sha256_16": source_hash(PREFILL_SRC),
+def write_traffic(fetch_csv, write_csv, workload):
+    """HBM bytes per kda_prefill_cp call on `workload` from two rocprofv3 --pmc
+    runs of ``bench.py --pmc-workload`` (FETCH_SIZE, then WRITE_SIZE), each
+    scaled by what the same counter reads for the 1 GiB-in / 1 GiB-out
+    negation in the same run."""
+    out = {"kernel_source_sha256_16": source_hash(PREFILL_SRC), "workload": workload,
            "commands": ["cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc %s --output-format csv -d <dir> -o run "
-                        "-- python <repo>/bench.py --steps 1 --warmup 1 --decode-steps 2 --no-cpu-baseline "
-                        "--copy-calibration" % c for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                        "-- python <repo>/bench.py --pmc-workload %s" % (c, workload)
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")]
                        + ["python bench.py --traffic-from <fetch dir>/run_counter_collection.csv "
-                          "<write dir>/run_counter_collection.csv"],
+                          "<write dir>/run_counter_collection.csv --workload %s" % workload],
            "unit": "bytes per kda_prefill_cp call (all five launches), counters scaled by the 1 GiB negation"}
     total = 0.0
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -180,20 +195,41 @@ def write_traffic(fetch_csv, write_csv):
                         "kib_per_call_raw": per_call / 1024.0, "bytes_per_call": per_call * factor}
         total += per_call * factor
     out["hbm_bytes_per_launch"] = total
-    with open(PMC_SUMMARY, "w") as f:
+    with open(profile_path(workload, "traffic"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
-def cpu_baseline(pre, H, target_s=20.0):
+def host_cores():
+    """(cores used, cores available): the cores this process may run on
+    (sched_getaffinity), at most OMP_NUM_THREADS when the environment sets it."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    used = min(avail, int(env)) if env.isdigit() and int(env) > 0 else avail
+    return max(1, used), avail
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(pre, H, small, target_s=20.0):
     """Time the fp64 oracle (as it stands) on host cores on a bounded sample:
-    the first Ls tokens of every sequence of the same prefill inputs, all heads."""
+    the first Ls tokens of every sequence of the same prefill inputs, all
+    heads; plus single-thread runs of the oracle on the small workloads
+    (`small`: {name: host input dict}) for a per-core rate."""
     import numpy as np
     import torch
     from oracle import kda_oracle as O
 
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    cores = max(1, min(cores, 16))
+    cores, avail = host_cores()
     cu = pre["cu_seqlens"].cpu().tolist()
     N = len(cu) - 1
 
@@ -225,10 +261,55 @@ def cpu_baseline(pre, H, target_s=20.0):
     t, tok = run(Ls)
     what = ("all tokens of the %d sequences" % N if Ls >= max(lens)
             else "the first %d tokens of each of the %d sequences" % (Ls, N))
-    return {"value": tok / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    single = {}
+    for name, inp in small.items():
+        T1, H1 = inp["q"].shape[0], inp["q"].shape[1]
+        init = inp["initial_state"]
+        t0 = time.perf_counter()
+        O.prefill(inp["q"].float().numpy(), inp["k"].float().numpy(), inp["v"].float().numpy(), inp["g"].numpy(),
+                  inp["beta"].numpy(), None if init is None else init.double().numpy(), inp["cu_seqlens"].numpy(),
+                  num_threads=1)
+        dt = time.perf_counter() - t0
+        single[name] = {"tokens_per_s": T1 / dt, "head_tokens_per_s": T1 * H1 / dt, "s": dt,
+                        "fp64_gflops": T1 * H1 * 7 * DK * DV / dt / 1e9}
+    return {"value": tok / t, "unit": "tokens/s", "cores": cores, "cores_available": avail, "cpu_model": cpu_model(),
+            "kind": "oracle", "head_tokens_per_s": tok * H / t, "fp64_gflops": tok * H * 7 * DK * DV / t / 1e9,
             "sample": "%s x %d heads of the same prefill inputs "
                       "(%d tokens, %d head-tokens, %.1f s, fp64 token loop, OpenMP over (sequence, head))"
-                      % (what, H, tok, tok * H, t)}
+                      % (what, H, tok, tok * H, t),
+            "single_thread": single}
+
+
+def pmc_workload_run(name):
+    """One workload under a counter run: a 1 GiB negation (the reference for
+    the HBM counters: torch's elementwise negation reads 1 GiB and writes
+    1 GiB, its kernel name holds "neg"), then two kda_prefill_cp calls."""
+    import torch
+    from gated_delta_rule_40_amd import inputs as I
+    from gated_delta_rule_40_amd import libkda as K
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    K.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    inp = I.make_prefill(I.WORKLOADS[name], device=dev)
+    T, H = inp["q"].shape[0], inp["q"].shape[1]
+    N = inp["cu_seqlens"].shape[0] - 1
+    out = torch.empty(T, H, DV, dtype=inp["q"].dtype, device=dev)
+    fin = torch.empty(N, H, DK, DV, dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kda_prefill_cp_workspace_size(N, T, H, DK, DV, inp["q"].dtype, 0), dtype=torch.uint8,
+                     device=dev)
+    for i in range(2):
+        K.kda_prefill_cp(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                         inp["cu_seqlens"], out, fin, seg_len=0, workspace=ws)
+        torch.cuda.synchronize()
+        print("pmc workload %s: kda_prefill_cp call %d done" % (name, i + 1), flush=True)
 
 
 def main():
@@ -241,18 +322,23 @@ def main():
     ap.add_argument("--prefill", choices=("cp", "plain"), default="cp",
                     help="cp: kda_prefill_cp (segments side by side); plain: kda_prefill")
     ap.add_argument("--seg-len", type=int, default=0, help="kda_prefill_cp segment length (0 = automatic)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--pmc-workload", choices=PREFILL_WORKLOADS,
+                    help="counter run: a 1 GiB negation then two kda_prefill_cp calls on this workload, and exit")
+    ap.add_argument("--workload", choices=PREFILL_WORKLOADS, default="prefill_varlen_1m_h16",
+                    help="workload of --mfma-from / --traffic-from")
     ap.add_argument("--mfma-from", metavar="PMC_CSV",
                     help="write the executed-MFMA summary from a rocprofv3 --pmc run of the MFMA counters and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit (no GPU)")
     args = ap.parse_args()
     if args.mfma_from:
-        write_mfma(args.mfma_from)
+        write_mfma(args.mfma_from, args.workload)
         return
     if args.traffic_from:
-        write_traffic(*args.traffic_from)
+        write_traffic(*args.traffic_from, args.workload)
+        return
+    if args.pmc_workload:
+        pmc_workload_run(args.pmc_workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: libkda runs the KDA path on a single MI355X "
@@ -280,15 +366,6 @@ def main():
     Nd, Hd = wl_d.num_seqs, wl_d.heads
     state = dec["state"]
     dout = torch.empty(args.decode_steps, Nd, Hd, DV, dtype=torch.bfloat16, device=dev)
-    if args.copy_calibration:
-        # a plain streaming kernel of known size for the HBM counters: torch's
-        # elementwise negation reads 1 GiB and writes 1 GiB (kernel name holds "neg")
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
     stream = torch.cuda.current_stream()
     ws = None
     if args.prefill == "cp":
@@ -335,8 +412,8 @@ def main():
     dec_step_ms = dec_avg / args.decode_steps
     dec_bytes = Nd * Hd * DECODE_BYTES_PER_UNIT
     dec_gbs = dec_bytes / (dec_step_ms * 1e-3) / 1e9
-    traffic = pmc_traffic()
-    mfma = pmc_mfma()
+    traffic = pmc_traffic("prefill_varlen_1m_h16")
+    mfma = pmc_mfma("prefill_varlen_1m_h16")
 
     # speculative-decoding replay: 4 draft tokens per (sequence, head) of the
     # decode batch, outputs for all of them and the state committed, one call
@@ -388,41 +465,103 @@ def main():
     bwd_tflops = Tb * Hb * BWD_FLOP_PER_HT / (bwd_ms * 1e-3) / 1e12
     bwd_bytes = Tb * Hb * BWD_BYTES_PER_HT + 3 * Hb * DK * DV * 4      # + initial state, dfinal, dinit
 
+    def flop_fields(head_tokens_c, ms):
+        fref = head_tokens_c * PREFILL_FREF_PER_HT / (ms * 1e-3) / 1e12
+        falg = head_tokens_c * PREFILL_FALG_PER_HT / (ms * 1e-3) / 1e12
+        return {"fref_tflops": fref, "mfma_frac_fref": fref / BF16_PEAK_TFLOPS,
+                "falg_tflops": falg, "mfma_frac_falg": falg / BF16_PEAK_TFLOPS}
+
+    def counter_fields(name, ms):
+        """HBM bytes and executed MFMA flops of one kda_prefill_cp call, from the
+        committed counter summaries while they match the kernel source."""
+        tr, mf = pmc_traffic(name), pmc_mfma(name)
+        return {"counter_hbm_bytes": tr,
+                "counter_hbm_gbs": None if tr is None else tr / (ms * 1e-3) / 1e9,
+                "mfma_executed": None if mf is None else {
+                    "f16_tflops": mf[0] / (ms * 1e-3) / 1e12, "f32_tflops": mf[1] / (ms * 1e-3) / 1e12,
+                    "f16_frac_of_peak": mf[0] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                "counter_source": "rocprofv3 counters: %s, %s" % (
+                    os.path.relpath(profile_path(name, "traffic"), ROOT),
+                    os.path.relpath(profile_path(name, "mfma"), ROOT))}
+
+    def time_calls(calls, reps=5):
+        res = {}
+        for key, fn in calls.items():
+            for _ in range(2):
+                fn()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                fn()
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            res[key] = ev[0].elapsed_time(ev[1]) / reps
+        return res
+
     # the other prefill configurations (parity cases of their own), timed the
     # same way for reference: context-parallel and plain entry points
-    def time_prefill_config(name):
+    def time_prefill_config(name, inp=None, entries=("kda_prefill_cp", "kda_prefill")):
         wl = I.WORKLOADS[name]
-        inp = I.make_prefill(wl, device=dev)
+        own = inp is None
+        if own:
+            inp = I.make_prefill(wl, device=dev)
         Tc, Hc = inp["q"].shape[0], inp["q"].shape[1]
         Nc = inp["cu_seqlens"].shape[0] - 1
         o = torch.empty(Tc, Hc, DV, dtype=inp["q"].dtype, device=dev)
         f = torch.empty(Nc, Hc, DK, DV, dtype=torch.float32, device=dev)
-        w = torch.empty(K.kda_prefill_cp_workspace_size(Nc, Tc, Hc, DK, DV, inp["q"].dtype, 0), dtype=torch.uint8,
-                        device=dev)
+        w = None
+        if "kda_prefill_cp" in entries:
+            w = torch.empty(K.kda_prefill_cp_workspace_size(Nc, Tc, Hc, DK, DV, inp["q"].dtype, 0),
+                            dtype=torch.uint8, device=dev)
         calls = {"kda_prefill_cp": lambda: K.kda_prefill_cp(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                                             inp["initial_state"], inp["cu_seqlens"], o, f,
                                                             seg_len=0, workspace=w),
                  "kda_prefill": lambda: K.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
                                                       inp["initial_state"], inp["cu_seqlens"], o, f)}
         entry = {"total_tokens": Tc, "heads": Hc, "num_seqs": Nc}
-        nbytes = Tc * Hc * PREFILL_BYTES_PER_HT + 2 * Nc * Hc * DK * DV * 4   # + initial and final states
-        for key, fn in calls.items():
-            for _ in range(2):
-                fn()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record(stream)
-            for _ in range(5):
-                fn()
-            ev[1].record(stream)
-            torch.cuda.synchronize()
-            ms = ev[0].elapsed_time(ev[1]) / 5
+        init_bytes = 0 if inp["initial_state"] is None else Nc * Hc * DK * DV * 4
+        nbytes = Tc * Hc * PREFILL_BYTES_PER_HT + Nc * Hc * DK * DV * 4 + init_bytes   # + final (initial) state
+        for key, ms in time_calls({k_: calls[k_] for k_ in entries}).items():
             entry[key] = {"ms": ms, "tokens_per_s": Tc / (ms * 1e-3), "head_tokens_per_s": Tc * Hc / (ms * 1e-3),
                           "hbm_algorithmic_gbs": nbytes / (ms * 1e-3) / 1e9,
-                          "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-        del inp, o, f, w
-        return entry
+                          "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "algorithmic_bytes_per_call": nbytes}
+            entry[key].update(flop_fields(Tc * Hc, ms))
+            if key == "kda_prefill_cp":
+                entry[key].update(counter_fields(name, ms))
+        if name == "prefill_t4096_h8":
+            # state snapshots every 512 tokens (kda_prefill_snapshots, 32-token
+            # chunks, 64-column blocks) against kda_prefill at the same tiling
+            every = 512
+            snaps = torch.empty(Nc, Tc // every, Hc, DK, DV, dtype=torch.float32, device=dev)
+            ms_s = time_calls({
+                "snapshots": lambda: K.kda_prefill_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                                             inp["initial_state"], inp["cu_seqlens"], o, f,
+                                                             snaps, every),
+                "same_tiling": lambda: K.kda_prefill_ex(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                                        inp["initial_state"], inp["cu_seqlens"], o, f,
+                                                        chunk=32, dv_block=64)})
+            entry["kda_prefill_snapshots"] = {"snap_every": every, "snapshots_per_seq": Tc // every,
+                                              "ms": ms_s["snapshots"], "kda_prefill_same_tiling_ms": ms_s["same_tiling"],
+                                              "overhead": ms_s["snapshots"] / ms_s["same_tiling"] - 1.0}
+            del snaps
+        small_host = {k_: (v_.cpu() if torch.is_tensor(v_) else v_) for k_, v_ in inp.items()} \
+            if name == "prefill_t4096_h8" else None
+        del o, f, w
+        if own:
+            del inp
+        return entry, small_host
 
-    other_prefill = {name: time_prefill_config(name) for name in ("prefill_t4096_h8", "prefill_4x16384_h32")}
+    other_prefill, small_inputs = {}, {}
+    for name in ("prefill_t4096_h8", "prefill_4x16384_h32"):
+        other_prefill[name], host_inp = time_prefill_config(name)
+        if host_inp is not None:
+            small_inputs[name] = host_inp
+    # plain kda_prefill on the bench's own 1M-token input (the longest
+    # sequence then runs as one chain)
+    other_prefill["prefill_varlen_1m_h16"], _ = time_prefill_config("prefill_varlen_1m_h16", inp=pre,
+                                                                    entries=("kda_prefill",))
+    small_inputs = dict({"parity_t128_fp32": I.make_prefill(I.WORKLOADS["parity_t128_fp32"])}, **small_inputs)
 
     result = {
         "metric": METRIC,
@@ -445,6 +584,11 @@ def main():
                         "dk": DK, "dv": DV, "io": "bf16 q/k/v/out, fp32 g/beta/state",
                         "initial_state": "zero", "ms": pre_avg, "head_tokens_per_s": head_tokens / (pre_avg * 1e-3),
                         "fref_tflops": pre_tflops, "mfma_frac_fref": pre_tflops / BF16_PEAK_TFLOPS,
+                        "falg_tflops": head_tokens * PREFILL_FALG_PER_HT / (pre_avg * 1e-3) / 1e12,
+                        "mfma_frac_falg": head_tokens * PREFILL_FALG_PER_HT / (pre_avg * 1e-3) / 1e12
+                        / BF16_PEAK_TFLOPS,
+                        "counter_hbm_bytes": traffic,
+                        "counter_hbm_gbs": None if traffic is None else traffic / (pre_avg * 1e-3) / 1e9,
                         "mfma_executed": None if mfma is None else {
                             "f16_tflops": mfma[0] / (pre_avg * 1e-3) / 1e12,
                             "f32_tflops": mfma[1] / (pre_avg * 1e-3) / 1e12,
@@ -480,7 +624,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(pre, H)
+        result["cpu_baseline"] = cpu_baseline(pre, H, small_inputs)
     print(json.dumps(result), flush=True)
 
 

@@ -5,7 +5,11 @@
 // is synchronised and no mutable state is shared between calls.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
 
 #include "kda.h"
 
@@ -81,6 +85,35 @@ kda_status check_common(const void *q, const void *k, const void *v, const float
     return KDA_OK;
 }
 
+// KDA_VALIDATE=1 in the environment (read once): the entry points that take
+// cu_seqlens copy it to the host, synchronising `stream`, and check it before
+// launching anything.  Off by default, since it costs a synchronisation.
+bool validate_enabled()
+{
+    static std::atomic<int> state{-1};
+    int v = state.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char *e = std::getenv("KDA_VALIDATE");
+        v = (e && std::strcmp(e, "1") == 0) ? 1 : 0;
+        state.store(v, std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+
+// cu[0] = 0, non-decreasing, cu[N] <= T.  Returns KDA_ERR_INVALID_ARG for
+// contents that break this, KDA_ERR_LAUNCH if the copy itself fails.
+kda_status validate_cu(const int32_t *cu, int32_t N, int32_t T, hipStream_t stream)
+{
+    std::vector<int32_t> h((size_t)N + 1);
+    if (hipMemcpyAsync(h.data(), cu, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return KDA_ERR_LAUNCH;
+    if (h[0] != 0 || h[N] > T) return KDA_ERR_INVALID_ARG;
+    for (int32_t n = 0; n < N; ++n)
+        if (h[n + 1] < h[n]) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
 // Value-column block per workgroup: the largest block that still gives at
 // least one workgroup per compute unit, but not below 64 columns (more
 // blocks = more parallel state chains, at the cost of repeating the
@@ -132,6 +165,9 @@ static kda_status prefill_impl(const void *q, const void *k, const void *v, cons
     const int64_t units = (int64_t)num_seqs * num_heads;
     if (units == 0) return KDA_OK;
     if (units * (dv / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;   // grid size
+    if (validate_enabled())
+        if (kda_status v = validate_cu(cu_seqlens, num_seqs, total_tokens, reinterpret_cast<hipStream_t>(stream)))
+            return v;
     if (dv_block == 0) {
         dv_block = auto_dv_block(units, dv);
         if (dv_block < min_block) dv_block = min_block;
@@ -264,26 +300,36 @@ size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int
     return lay.total;
 }
 
-kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const float *g,
-                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
-                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
-                          int32_t dv, kda_dtype dtype, void *out, float *final_state, int32_t seg_len,
-                          void *workspace, size_t workspace_bytes, kda_stream_t stream)
+namespace {
+
+// Argument checks of kda_prefill_cp (no HIP call):
+// resolves the automatic segment length and the workspace layout.
+kda_status cp_check(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                    int32_t dk, int32_t dv, kda_dtype dtype, void *out, int32_t *seg_len, CpLayout *lay)
 {
     kda_status st = check_common(q, k, v, g, beta, out, dk, dv, dtype);
     if (st == KDA_ERR_INVALID_ARG) return st;
-    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || seg_len < 0)
+    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || *seg_len < 0)
         return KDA_ERR_INVALID_ARG;
     if (st != KDA_OK) return st;
-    if (seg_len == 0) seg_len = cp_default_seg_len(total_tokens, num_heads);
-    if (seg_len < kCpChunk || seg_len % kCpChunk) return KDA_ERR_UNSUPPORTED;
-    const int bf16 = dtype == KDA_BF16 ? 1 : 0;
-    CpLayout lay;
-    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, bf16, seg_len, &lay)) return KDA_ERR_INVALID_ARG;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
-    if ((int64_t)lay.max_units * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
-    if ((int64_t)lay.max_chunks * num_heads > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (*seg_len == 0) *seg_len = cp_default_seg_len(total_tokens, num_heads);
+    if (*seg_len < kCpChunk || *seg_len % kCpChunk) return KDA_ERR_UNSUPPORTED;
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_BF16, *seg_len, lay))
+        return KDA_ERR_INVALID_ARG;
+    if ((int64_t)lay->max_units * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if ((int64_t)lay->max_chunks * num_heads > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    return KDA_OK;
+}
+
+// The five launches of a context-parallel prefill in workspace `ws` (layout `lay`).
+kda_status cp_launch(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                     const float *initial_state, const int32_t *cu_seqlens, int32_t num_seqs,
+                     int32_t total_tokens, int32_t num_heads, int32_t dv, kda_dtype dtype, void *out,
+                     float *final_state, int32_t seg_len, const CpLayout &lay, void *workspace, hipStream_t s)
+{
     if (num_seqs == 0) return KDA_OK;
+    const int bf16 = dtype == KDA_BF16 ? 1 : 0;
     char *ws = static_cast<char *>(workspace);
     int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);
     int32_t *sched = reinterpret_cast<int32_t *>(ws + lay.sched);
@@ -295,7 +341,6 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
     float *seg_out = reinterpret_cast<float *>(ws + lay.seg_out);
     float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
     void *img = ws + lay.img;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // output segments and summary units (SEG_LAST: in a sequence's last segment), one launch
     int32_t *seq_order = reinterpret_cast<int32_t *>(ws + lay.seq_order);
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
@@ -316,6 +361,26 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
                              useq_seg, lay.unit_len, lay.max_units, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                          int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                          int32_t dv, kda_dtype dtype, void *out, float *final_state, int32_t seg_len,
+                          void *workspace, size_t workspace_bytes, kda_stream_t stream)
+{
+    CpLayout lay;
+    kda_status st = cp_check(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv, dtype, out,
+                             &seg_len, &lay);
+    if (st != KDA_OK) return st;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < lay.total) return KDA_ERR_INVALID_ARG;
+    if (validate_enabled() && num_seqs > 0)
+        if (kda_status v = validate_cu(cu_seqlens, num_seqs, total_tokens, reinterpret_cast<hipStream_t>(stream)))
+            return v;
+    return cp_launch(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, dtype, out,
+                     final_state, seg_len, lay, workspace, reinterpret_cast<hipStream_t>(stream));
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g,
@@ -352,6 +417,9 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
     const int64_t units = (int64_t)num_seqs * num_heads;
     if (units == 0) return KDA_OK;
     if (units > INT32_MAX) return KDA_ERR_INVALID_ARG;
+    if (validate_enabled())
+        if (kda_status v = validate_cu(cu_seqlens, num_seqs, total_tokens, reinterpret_cast<hipStream_t>(stream)))
+            return v;
     hipError_t e = kda_launch_decode_tokens(dtype == KDA_BF16 ? 1 : 0, q, k, v, g, beta, cu_seqlens, num_tokens,
                                            state_in, state_out, num_seqs, total_tokens, num_heads, out,
                                            reinterpret_cast<hipStream_t>(stream));
@@ -452,6 +520,9 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if ((int64_t)lay.max_segs * num_heads * ((dv + dk) / 16) > INT32_MAX ||
         (int64_t)lay.max_chunks * num_heads > INT32_MAX)
         return KDA_ERR_INVALID_ARG;
+    if (validate_enabled())
+        if (kda_status v = validate_cu(cu_seqlens, num_seqs, total_tokens, reinterpret_cast<hipStream_t>(stream)))
+            return v;
     const int bf16 = dtype == KDA_BF16 ? 1 : 0;
     char *ws = static_cast<char *>(workspace);
     int32_t *plan = reinterpret_cast<int32_t *>(ws + lay.plan);

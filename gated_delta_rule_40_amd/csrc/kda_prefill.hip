@@ -86,6 +86,10 @@ struct PrefillCfg {
     static constexpr float SPAN_CHUNK = kIn16 ? 11.f : 60.f;
     // exact power-of-two rebalance of fp16 operands: row operands x GS, column /GS
     static constexpr float GS = kIn16 ? 32.f : 1.f;
+    // ... and, for fp16 operands, only when every column operand k e^-Gamma / GS
+    // of the chunk stays below this (a quarter of the fp16 range); a chunk with
+    // a larger key channel uses the sub-tile references, whose factors are <= 1
+    static constexpr float COL_MAX = 16384.f;
 
     // row strides (elements), rows padded by 16 bytes against bank conflicts
     static constexpr int LDK = DK + 16 / (int)sizeof(OpT);     // [C][DK] operand tiles
@@ -118,6 +122,10 @@ struct PrefillCfg {
     static constexpr size_t offT = offN + sizeof(OpT) * C * LDC;            // OpT [C][LDC]
     static constexpr size_t offP = offT + sizeof(OpT) * C * LDC;            // OpT [C][LDC]
     static constexpr size_t end1 = (offP + sizeof(OpT) * C * LDC + 15) / 16 * 16;
+    // phase 1 only: max |k| per (prep segment, channel), fp32 [NSEG][DK]; it
+    // overlays region 1, which the Gram tiles first write in phase 2
+    static constexpr size_t offKmax = offAd;
+    static_assert(sizeof(float) * NSEG * DK <= end1 - offAd, "key maxima fit region 1");
     // small fp32 tables
     static constexpr size_t offF = end1;                                    // [NGRP][DK]
     static constexpr size_t offH = offF + sizeof(float) * NGRP * DK;        // [NPAIR][DK]
@@ -594,6 +602,7 @@ void kda_prefill_kernel(
     float *sPre = reinterpret_cast<float *>(smem + P::offPre);   // prefix products of group decays
     float *sBeta = reinterpret_cast<float *>(smem + P::offBeta);
     float *sTs = reinterpret_cast<float *>(smem + P::offTs);
+    float *sKmax = reinterpret_cast<float *>(smem + P::offKmax);
 
     // ---- workgroup -> (work unit, value block); blocks of one unit share an XCD.
     //      A work unit is a (sequence, head) pair, or a (segment, head) pair when
@@ -827,6 +836,17 @@ void kda_prefill_kernel(
                     for (int x = 0; x < CPI; ++x) f[x] = __expf(sum[x]);
                     *reinterpret_cast<f32x4 *>(sF + G * DK + c) = f;
                 }
+                if constexpr (kIn16) {
+                    // largest |k| of channels c .. c + 3 over this segment's tokens
+                    f32x4 km = zero4();
+#pragma unroll
+                    for (int rr = 0; rr < SEG; ++rr) {
+                        const bool ok = sg * SEG + rr < L;
+#pragma unroll
+                        for (int x = 0; x < CPI; ++x) km[x] = fmaxf(km[x], ok ? fabsf(to_f(rk[it][rr][x])) : 0.f);
+                    }
+                    *reinterpret_cast<f32x4 *>(sKmax + sg * DK + c) = km;
+                }
             }
         }
         if (tid < C) sBeta[tid] = tid < L ? rb : 0.f;
@@ -844,6 +864,12 @@ void kda_prefill_kernel(
             }
             sGam[c] = gm;
             strong |= gm < __expf(-P::SPAN_CHUNK);
+            if constexpr (kIn16) {
+                // fp16 column operand of channel c: at most max_r |k_rc| / gamma_c / GS
+                float km = 0.f;
+                for (int sg = 0; sg < NSEG; ++sg) km = fmaxf(km, sKmax[sg * DK + c]);
+                strong |= !(km <= P::COL_MAX * P::GS * gm);
+            }
         }
         const bool slow = __syncthreads_or(strong);
         if (slow) {

@@ -115,13 +115,30 @@ def _require(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+def _on_device(ref: torch.Tensor, **tensors) -> None:
+    """Every given tensor (None entries skipped) must be a device tensor on
+    ref's device: the library dereferences the pointers on the GPU, so a host
+    pointer or another device's memory would fault there."""
+    _require(torch.is_tensor(ref) and ref.is_cuda, "q must be a device tensor")
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _require(torch.is_tensor(t) and t.is_cuda and t.device == ref.device,
+                 "%s must be a tensor on %s" % (name, ref.device))
+
+
 def _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state):
+    _on_device(q, k=k, v=v, g=g, beta=beta, initial_state=initial_state, cu_seqlens=cu_seqlens, out=out,
+               final_state=final_state)
+    _require(q.dim() == 3 and v.dim() == 3 and cu_seqlens.dim() == 1 and cu_seqlens.shape[0] >= 1,
+             "q, k, g, v, out must be [T, H, d] and cu_seqlens [N + 1]")
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.shape[0] - 1
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out),
+                    ("cu_seqlens", cu_seqlens)):
         _require(t.is_contiguous(), "%s must be contiguous" % name)
-    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens must be int32 on the device")
+    _require(cu_seqlens.dtype == torch.int32, "cu_seqlens must be int32")
     _require(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be float32")
     _require(k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (T, H) and out.shape == v.shape,
              "shape mismatch")
@@ -151,6 +168,7 @@ def kda_prefill_snapshots(q, k, v, g, beta, initial_state, cu_seqlens, out, fina
     """kda_prefill plus the state after every snap_every tokens of each
     sequence: snapshots [N, max_snaps, H, dk, dv] fp32 (max_snaps from its shape)."""
     N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    _on_device(q, snapshots=snapshots)
     _require(snapshots.dtype == torch.float32 and snapshots.is_contiguous() and snapshots.dim() == 5 and
              snapshots.shape[0] == N and tuple(snapshots.shape[2:]) == (H, dk, dv),
              "snapshots must be contiguous float32 [N, max_snaps, H, dk, dv]")
@@ -165,7 +183,9 @@ def kda_prefill_cp_workspace_size(num_seqs: int, total_tokens: int, num_heads: i
                                   dtype=torch.bfloat16, seg_len: int = 0) -> int:
     """Bytes of device workspace kda_prefill_cp needs (0 = unsupported sizes);
     dtype is that of q/k/v (torch.bfloat16 or torch.float32)."""
-    code = KDA_BF16 if dtype == torch.bfloat16 else KDA_F32
+    code = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32}.get(dtype)
+    if code is None:
+        raise TypeError("dtype must be torch.bfloat16 or torch.float32, got %s" % dtype)
     return int(load().kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, code, seg_len))
 
 
@@ -179,7 +199,8 @@ def kda_prefill_cp(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state
     need = kda_prefill_cp_workspace_size(N, T, H, dk, dv, q.dtype, seg_len)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _require(workspace.is_cuda and workspace.is_contiguous(), "workspace must be a contiguous device tensor")
+    _on_device(q, workspace=workspace)
+    _require(workspace.is_contiguous(), "workspace must be contiguous")
     nbytes = workspace.numel() * workspace.element_size()
     lib = load()
     _check(lib.kda_prefill_cp(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
@@ -195,11 +216,14 @@ def kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, s
 def kda_decode_step(q, k, v, g, beta, state_inout, out, stream=None) -> None:
     """One decode step, state updated in place.  q, k, g: [N, H, dk];
     v, out: [N, H, dv]; beta: [N, H]; state_inout: [N, H, dk, dv] fp32."""
+    _on_device(q, k=k, v=v, g=g, beta=beta, state_inout=state_inout, out=out)
+    _require(q.dim() == 3 and v.dim() == 3, "q, k, g, v, out must be [N, H, d]")
     N, H, dk = q.shape
     dv = v.shape[-1]
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state", state_inout),
                     ("out", out)):
         _require(t.is_contiguous(), "%s must be contiguous" % name)
+    _require(k.dtype == q.dtype and v.dtype == q.dtype and out.dtype == q.dtype, "q/k/v/out dtypes differ")
     _require(k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (N, H) and out.shape == v.shape,
              "shape mismatch")
     _require(tuple(beta.shape) == (N, H) and tuple(state_inout.shape) == (N, H, dk, dv), "shape mismatch")
@@ -216,12 +240,18 @@ def kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, ou
     q, k, g: [T, H, dk]; v, out: [T, H, dv]; beta: [T, H]; cu_seqlens: [N+1]
     int32 on the device; num_tokens: [N] int32 on the device or None;
     state_in / state_out: [N, H, dk, dv] fp32 (state_out None: not written)."""
+    _on_device(q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, state_out=state_out,
+               out=out, num_tokens=num_tokens)
+    _require(q.dim() == 3 and v.dim() == 3 and cu_seqlens.dim() == 1 and cu_seqlens.shape[0] >= 1,
+             "q, k, g, v, out must be [T, H, d] and cu_seqlens [N + 1]")
     T, H, dk = q.shape
     dv = v.shape[-1]
     N = cu_seqlens.shape[0] - 1
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_in", state_in)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("state_in", state_in),
+                    ("cu_seqlens", cu_seqlens)):
         _require(t.is_contiguous(), "%s must be contiguous" % name)
-    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.is_cuda, "cu_seqlens must be int32 on the device")
+    _require(cu_seqlens.dtype == torch.int32, "cu_seqlens must be int32")
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q/k/v dtypes differ")
     _require(k.shape == q.shape and g.shape == q.shape and v.shape[:2] == (T, H) and tuple(beta.shape) == (T, H),
              "shape mismatch")
     _require(g.dtype == torch.float32 and beta.dtype == torch.float32, "g and beta must be float32")
@@ -232,7 +262,7 @@ def kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, ou
     if out is not None:
         _require(out.is_contiguous() and out.shape == v.shape and out.dtype == q.dtype, "out must match v")
     if num_tokens is not None:
-        _require(num_tokens.dtype == torch.int32 and num_tokens.is_cuda and tuple(num_tokens.shape) == (N,),
+        _require(num_tokens.dtype == torch.int32 and num_tokens.is_contiguous() and tuple(num_tokens.shape) == (N,),
                  "num_tokens must be int32 [N] on the device")
     lib = load()
     _check(lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
@@ -255,17 +285,29 @@ def kda_backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None,
     of fp32 tensors dq, dk, dv, dg [T, H, *], dbeta [T, H] and dinit
     [N, H, dk, dv] (None unless want_dinit); ``grads`` may supply them."""
     N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, dout, None)
+    _on_device(q, dfinal=dfinal, workspace=workspace)
     if dfinal is not None:
         _require(dfinal.dtype == torch.float32 and dfinal.is_contiguous() and tuple(dfinal.shape) == (N, H, dk, dv),
                  "dfinal must be contiguous float32 [N, H, dk, dv]")
     dev = q.device
+    shapes = {"dq": (T, H, dk), "dk": (T, H, dk), "dv": (T, H, dv), "dg": (T, H, dk), "dbeta": (T, H),
+              "dinit": (N, H, dk, dv)}
     if grads is None:
         f = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)
-        grads = {"dq": f(T, H, dk), "dk": f(T, H, dk), "dv": f(T, H, dv), "dg": f(T, H, dk), "dbeta": f(T, H),
-                 "dinit": f(N, H, dk, dv) if want_dinit else None}
+        grads = {key: f(*shape) for key, shape in shapes.items() if key != "dinit"}
+        grads["dinit"] = f(*shapes["dinit"]) if want_dinit else None
+    for key, shape in shapes.items():
+        t = grads.get(key)
+        if t is None and key == "dinit":
+            continue
+        _require(t is not None, "grads[%r] is missing" % key)
+        _on_device(q, **{key: t})
+        _require(t.dtype == torch.float32 and t.is_contiguous() and tuple(t.shape) == shape,
+                 "grads[%r] must be contiguous float32 %s" % (key, list(shape)))
     need = kda_backward_workspace_size(N, T, H, dk, dv, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _require(workspace.is_contiguous(), "workspace must be contiguous")
     nbytes = workspace.numel() * workspace.element_size()
     lib = load()
     _check(lib.kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu_seqlens),

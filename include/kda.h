@@ -12,9 +12,22 @@
  * column = value channel), fixed in size whatever the sequence length (same
  * page, section "百万上下文的关键，不是让所有层都保存百万份 KV").  Nothing else
  * is applied: no query scaling, key normalisation, output gate or short
- * convolution.  Results are guaranteed for g in [-5, 0] (card "g ∈ (-5, 0)"):
- * outside that range the intermediate decay factors may overflow and the
- * result is unspecified.  beta may be any finite value.
+ * convolution.
+ *
+ * Input range (results are computed without overflow of any intermediate):
+ *   - g in [-5, 0] (card "g ∈ (-5, 0)"); outside it intermediate decay factors
+ *     may overflow and the result is unspecified.
+ *   - fp32 q/k/v: any finite q, k, v and beta whose state stays in fp32 range.
+ *   - bf16 q/k/v (the contractions run on fp16 MFMA operands with exact
+ *     power-of-two scales): in addition |q_c|, |k_c| <= 1024 per channel, and
+ *     for tokens r, i of one 32-token chunk ||q_r|| ||k_i|| <= 32768 and
+ *     |beta_r| ||k_r|| ||k_i|| <= 32768.  Chunks whose decay-scaled key
+ *     columns would leave fp16 range (large keys under strong decay) are
+ *     detected per chunk and evaluated with 16-token references whose factors
+ *     are all <= 1, so no key magnitude within these bounds overflows.
+ *   - beta has no range of its own.  Each step is non-expansive when
+ *     beta ||k||^2 lies in [0, 2]; outside that interval the recurrence itself
+ *     amplifies rounding (and, over long runs, the state can leave fp32 range).
  *
  * Conventions for every call:
  *   - Device pointers are on the current HIP device, dense and row-major as
@@ -23,9 +36,10 @@
  *     bits) that each kernel's LDS limit has been raised; calls are
  *     thread-safe.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never
- *     synchronise.  Argument errors are returned before any HIP call; a
- *     launch failure returns KDA_ERR_LAUNCH; device faults surface at the
- *     caller's next synchronisation of `stream`.
+ *     synchronise (except the opt-in KDA_VALIDATE=1 check of cu_seqlens,
+ *     below).  Argument errors are returned before any HIP call; a launch
+ *     failure returns KDA_ERR_LAUNCH; device faults surface at the caller's
+ *     next synchronisation of `stream`.
  *   - v1 supports dk = dv = 128 only (other sizes: KDA_ERR_UNSUPPORTED).
  *   - Arithmetic: q/k/v/out in `dtype`; g, beta and states fp32; all
  *     accumulation and the carried state are fp32.
@@ -67,6 +81,11 @@ typedef enum {
  *                 Sequence n owns tokens [cu[n], cu[n+1]).  It is not read on
  *                 the host; entries outside [0, total_tokens] are clamped on
  *                 the device (memory-safe, result for that sequence unspecified).
+ *                 With KDA_VALIDATE=1 in the environment (read at the first
+ *                 call), every entry point that takes cu_seqlens copies it to
+ *                 the host first, synchronising `stream` (so not under graph
+ *                 capture), and returns
+ *                 KDA_ERR_INVALID_ARG when these rules do not hold.
  *   out           [total_tokens, num_heads, dv]   dtype; rows of tokens owned
  *                 by a sequence are written, other rows are left untouched.
  *   final_state   [num_seqs, num_heads, dk, dv]   fp32, or NULL (not written).

@@ -102,6 +102,52 @@ def assert_close(got, ref, tol, what, dtype=torch.float32, ulps=0.5):
     """`dtype`: the dtype `got` was stored in (its rounding is allowed on top);
     ulps = 1 when both sides are device results stored in that dtype."""
     rel, err, rms = max_rel_err(got, ref, dtype, ulps)
-    log("  %-30s max|d|=%.3e rms=%.3e (|d|-ulp/2)/rms=%.3e (tol %.0e)" % (what, err, rms, rel, tol))
+    log("  %-30s max|d|=%.3e rms=%.3e raw max|d|/rms=%.3e (|d|-ulp/2)/rms=%.3e (tol %.0e)"
+        % (what, err, rms, err / rms if rms > 0 else err, rel, tol))
     assert np.all(np.isfinite(np.asarray(got))), "%s has non-finite values" % what
     assert rel <= tol, "%s: (|d| - ulp/2) / rms = %.3e > %.0e" % (what, rel, tol)
+
+
+class StreamingCompare:
+    """The rule of assert_close over a tensor too large to hold twice in fp64:
+    blocks of (got, ref) are added one by one, keeping max|d|, the largest
+    excess |d| - ulps * ulp(x) / 2 and the sum of ref^2; check() then applies
+    tol * RMS with the RMS over every element added (the whole tensor)."""
+
+    def __init__(self, what, tol, dtype=torch.float32, ulps=0.5):
+        self.what, self.tol, self.dtype, self.ulps = what, tol, dtype, ulps
+        self.sq, self.n, self.maxd, self.maxex, self.finite = 0.0, 0, 0.0, -np.inf, True
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, (got.shape, ref.shape)
+        if not ref.size:
+            return
+        self.finite &= bool(np.all(np.isfinite(got)))
+        d = np.abs(got - ref)
+        ex = d - 2 * self.ulps * half_ulp(np.maximum(np.abs(got), np.abs(ref)), self.dtype)
+        self.sq += float(np.sum(ref * ref))
+        self.n += ref.size
+        self.maxd = max(self.maxd, float(d.max()))
+        self.maxex = max(self.maxex, float(ex.max()))
+
+    def check(self):
+        rms = float(np.sqrt(self.sq / max(self.n, 1)))
+        rel = max(self.maxex, 0.0) / rms if rms > 0 else max(self.maxex, 0.0)
+        log("  %-30s %d elements max|d|=%.3e rms=%.3e raw max|d|/rms=%.3e (|d|-ulp/2)/rms=%.3e (tol %.0e)"
+            % (self.what, self.n, self.maxd, rms, self.maxd / rms if rms > 0 else self.maxd, rel, self.tol))
+        assert self.finite, "%s has non-finite values" % self.what
+        assert rel <= self.tol, "%s: (|d| - ulp/2) / rms = %.3e > %.0e" % (self.what, rel, self.tol)
+        return rel
+
+
+def oracle_threads():
+    """Host threads for the oracle: the cores this process may use, at most
+    OMP_NUM_THREADS when that is set."""
+    import os
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)

@@ -68,10 +68,12 @@ def test_cp_page_gate_range(dtype):
         _check_cp(inp2, TOL[dtype], "cp_g=%g" % gval, 64)
 
 
-def test_cp_t4096_h8_vs_oracle():
-    """B=1, H=8, T=4096, bf16, N(0, 0.1) initial state: 8 segments of 512 tokens, every output."""
+@pytest.mark.parametrize("seg_len", [0, 512])
+def test_cp_t4096_h8_vs_oracle(seg_len):
+    """B=1, H=8, T=4096, bf16, N(0, 0.1) initial state, every output: the
+    automatic segment length (the one bench.py times) and 8 segments of 512."""
     inp = to_dev(I.make_prefill(I.WORKLOADS["prefill_t4096_h8"]))
-    _check_cp(inp, TOL[torch.bfloat16], "cp_t4096_h8", 512)
+    _check_cp(inp, TOL[torch.bfloat16], "cp_t4096_h8", seg_len)
 
 
 def test_cp_single_segment_equals_plain_prefill_bitwise():

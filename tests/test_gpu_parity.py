@@ -14,7 +14,7 @@ import torch
 
 from gated_delta_rule_40_amd import inputs as I
 from gated_delta_rule_40_amd import libkda as K
-from kda_parity import TOL, assert_close, host, log, oracle_prefill, run_prefill, run_prefill_cp, to_dev
+from kda_parity import TOL, assert_close, host, log, oracle_prefill, run_prefill, to_dev
 from oracle import kda_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -198,47 +198,6 @@ def test_nonzero_stream():
     assert torch.equal(out, ref)
 
 
-# ------------------------------------------------------------ full sizes, sampled
-def _sampled_units_check(inp, units, tol, label, runners=(("prefill", run_prefill),)):
-    """Oracle on selected (sequence, head) units, packed into one H=1 problem;
-    every runner's outputs on those units are checked against it."""
-    cu = inp["cu_seqlens"].cpu().tolist()
-    sl = lambda key, n, h: inp[key][cu[n]:cu[n + 1], h:h + 1]
-    sub = {key: torch.cat([sl(key, n, h) for n, h in units]).cpu() for key in ("q", "k", "v", "g", "beta")}
-    lens = [cu[n + 1] - cu[n] for n, _ in units]
-    sub["cu_seqlens"] = I.cu_from_lengths(lens)
-    init = inp["initial_state"]
-    sub["initial_state"] = None if init is None else torch.stack([init[n, h:h + 1] for n, h in units])
-    log("[oracle] %s: %d units, %d tokens" % (label, len(units), sum(lens)))
-    ref_out, ref_fin = oracle_prefill(sub)
-    for name, run in runners:
-        log("[%s] %s" % (name, label))
-        out, fin = run(inp)
-        got_out = torch.cat([out[cu[n]:cu[n + 1], h] for n, h in units]).float().cpu().numpy()
-        got_fin = torch.stack([fin[n, h] for n, h in units]).cpu().numpy()
-        del out, fin
-        assert_close(got_out, ref_out[:, 0], tol, "%s %s out (sampled)" % (name, label), torch.bfloat16)
-        assert_close(got_fin, ref_fin[:, 0], tol, "%s %s final (sampled)" % (name, label))
-
-
-@pytest.mark.slow
-def test_parity_4x16384_h32_sampled():
-    wl = I.WORKLOADS["prefill_4x16384_h32"]
-    inp = I.make_prefill(wl, device="cuda")
-    units = [(n, h) for n in range(4) for h in (n, 31 - n)]
-    _sampled_units_check(inp, units, TOL[torch.bfloat16], "4x16384_h32")
-
-
-@pytest.mark.slow
-def test_parity_varlen_1m_h16_sampled():
-    wl = I.WORKLOADS["prefill_varlen_1m_h16"]
-    inp = I.make_prefill(wl, device="cuda")
-    log("[varlen_1m] lengths %s" % inp["lengths"])
-    units = [(n, (5 * n) % 16) for n in range(8)]
-    _sampled_units_check(inp, units, TOL[torch.bfloat16], "varlen_1m_h16",
-                         runners=(("prefill", run_prefill), ("prefill_cp", run_prefill_cp)))
-
-
 # ------------------------------------------------------------ decode
 def _decode_inputs(N, H, steps, dtype, seed, g_lo=-5 / 16):
     wl = I.Workload("dec", "decode", heads=H, dtype=dtype, num_seqs=N, steps=steps, seed=seed, g_lo=g_lo)
@@ -290,30 +249,3 @@ def test_64_decode_steps_equal_64_token_prefill():
     assert_close(host(dec.transpose(0, 1).reshape(N * steps, H, 128)), host(po), 2 * TOL[torch.bfloat16],
                  "64 decode vs prefill out", torch.bfloat16, ulps=1.0)
     assert_close(host(S), host(pf), 2 * TOL[torch.bfloat16], "64 decode vs prefill state")
-
-
-@pytest.mark.slow
-def test_decode_512x32_64_steps_sampled():
-    """512 sequences x 32 heads, 1 GiB fp32 state, 64 in-place steps; oracle on sampled units."""
-    wl = I.WORKLOADS["decode_512x32"]
-    d = I.make_decode(wl, device="cuda")
-    N, H, steps = wl.num_seqs, wl.heads, wl.steps
-    rng = np.random.default_rng(0)
-    units = sorted(set((int(n), int(h)) for n, h in zip(rng.integers(0, N, 48), rng.integers(0, H, 48))))
-    S_ref = np.stack([d["state"][n, h].double().cpu().numpy() for n, h in units])[:, None]
-    S = d["state"]
-    out = torch.empty(steps, N, H, 128, dtype=torch.bfloat16, device="cuda")
-    log("[decode_512x32] 64 steps on GPU")
-    for s in range(steps):
-        K.kda_decode_step(d["q"][s], d["k"][s], d["v"][s], d["g"][s], d["beta"][s], S, out[s])
-    torch.cuda.synchronize()
-    pick = lambda x, s: np.stack([host(x[s, n, h:h + 1]) for n, h in units])
-    ref_outs = []
-    for s in range(steps):
-        o, S_ref = O.decode_step(pick(d["q"], s), pick(d["k"], s), pick(d["v"], s), pick(d["g"], s),
-                                 np.stack([host(d["beta"][s, n, h:h + 1]) for n, h in units]), S_ref)
-        ref_outs.append(o[:, 0])
-    got = np.stack([[host(out[s, n, h]) for n, h in units] for s in range(steps)])
-    assert_close(got, np.stack(ref_outs), TOL[torch.bfloat16], "decode_512x32 out (sampled)", torch.bfloat16)
-    got_S = np.stack([host(S[n, h]) for n, h in units])
-    assert_close(got_S, S_ref[:, 0], TOL[torch.bfloat16], "decode_512x32 state (sampled)")

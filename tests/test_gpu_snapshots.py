@@ -68,3 +68,40 @@ def test_snapshot_equals_prefill_of_prefix_bitwise():
     # outputs equal the plain kda_prefill at the same tiling
     o_ref, _ = run_prefill(inp, chunk=32, dv_block=64)
     assert torch.equal(o_ref, out)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_restore_snapshot_then_continue_to_any_token_boundary(dtype):
+    """A prefix cache restores the state at any token boundary (page
+    ailearn.mscapital.top/kimi-k3.html, section "目标模型太大，缓存和草稿都必须理解
+    KDA"): take the last snapshot at or before the boundary and continue from it
+    over the remaining tokens -- with kda_prefill for a long tail and with
+    kda_decode_tokens for a short one.  The restored state, and the outputs of
+    the continuation, match the oracle run straight over the whole prefix."""
+    L, H, every = 300, 2, 64
+    inp = I.random_prefill([L], H=H, dtype=dtype, seed=52, device="cuda")
+    snaps = torch.empty(1, L // every, H, 128, 128, device="cuda")
+    out = torch.empty(L, H, 128, dtype=dtype, device="cuda")
+    K.kda_prefill_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                            inp["cu_seqlens"], out, None, snaps, every)
+    torch.cuda.synchronize()
+    for boundary in (100, 197, 258, 293, 300):
+        j = boundary // every - 1                      # last snapshot at or before the boundary
+        start = (j + 1) * every if j >= 0 else 0
+        state = snaps[0, j:j + 1].clone() if j >= 0 else inp["initial_state"].clone()
+        tail = {key: inp[key][start:boundary].contiguous() for key in ("q", "k", "v", "g", "beta")}
+        n_tail = boundary - start
+        tail_out = torch.empty(n_tail, H, 128, dtype=dtype, device="cuda")
+        cu = torch.tensor([0, n_tail], dtype=torch.int32, device="cuda")
+        if n_tail <= 8:
+            K.kda_decode_tokens(tail["q"], tail["k"], tail["v"], tail["g"], tail["beta"], cu, state,
+                                state_out=state, out=tail_out)
+            how = "kda_decode_tokens"
+        else:
+            K.kda_prefill(tail["q"], tail["k"], tail["v"], tail["g"], tail["beta"], state, cu, tail_out, state)
+            how = "kda_prefill"
+        torch.cuda.synchronize()
+        log("[restore] boundary %d: snapshot at %d, %d tokens by %s" % (boundary, start, n_tail, how))
+        ref_out, ref_fin = oracle_prefill(_prefix(inp, 0, boundary))
+        assert_close(host(tail_out), ref_out[start:boundary], TOL[dtype], "restored tail out @%d" % boundary, dtype)
+        assert_close(host(state), ref_fin, TOL[dtype], "restored state @%d" % boundary)
