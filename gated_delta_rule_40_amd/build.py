@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "lib", "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_backward.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_backward.hip", "kda_scratch.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -63,6 +63,7 @@ extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, float *state,
                                         int32_t N, int32_t H, void *out, hipStream_t stream);
+extern "C" hipError_t kda_static_scratch(void **ptr, size_t *bytes);
 
 namespace {
 
@@ -302,7 +303,7 @@ size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int
 
 namespace {
 
-// Argument checks of kda_prefill_cp (no HIP call):
+// Argument checks of kda_prefill_cp and kda_prefill_cp_noalloc (no HIP call):
 // resolves the automatic segment length and the workspace layout.
 kda_status cp_check(const void *q, const void *k, const void *v, const float *g, const float *beta,
                     const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
@@ -381,6 +382,24 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v, const flo
             return v;
     return cp_launch(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, dtype, out,
                      final_state, seg_len, lay, workspace, reinterpret_cast<hipStream_t>(stream));
+}
+
+kda_status kda_prefill_cp_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *initial_state, const int32_t *cu_seqlens,
+                                  int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dk,
+                                  int32_t dv, kda_dtype dtype, void *out, float *final_state, int32_t seg_len,
+                                  kda_stream_t stream)
+{
+    CpLayout lay;
+    kda_status st = cp_check(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, dk, dv, dtype, out,
+                             &seg_len, &lay);
+    if (st != KDA_OK) return st;
+    if (lay.total > (size_t)KDA_STATIC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+    void *ws = nullptr;
+    size_t bytes = 0;
+    if (kda_static_scratch(&ws, &bytes) != hipSuccess || !ws || bytes < lay.total) return KDA_ERR_LAUNCH;
+    return cp_launch(q, k, v, g, beta, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, dtype, out,
+                     final_state, seg_len, lay, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *g,
@@ -579,6 +598,9 @@ const char *kda_status_string(kda_status status)
     case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG: invalid argument (null, negative, misaligned or bad dtype)";
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid but unsupported configuration (v1: dk = dv = 128)";
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: HIP kernel launch failed";
+    case KDA_ERR_SCRATCH:
+        return "KDA_ERR_SCRATCH: the problem needs more workspace than the library's static device scratch "
+               "(KDA_STATIC_SCRATCH_BYTES) holds; use kda_prefill_cp with a caller-owned workspace";
     }
     return "unknown kda_status";
 }

@@ -10,6 +10,7 @@ fallback: if the library is missing the calls raise.
     kda_prefill_snapshots(..., snapshots, snap_every)
     kda_prefill_cp(..., seg_len=0, workspace=None)
     kda_prefill_cp_workspace_size(num_seqs, total_tokens, num_heads, dk, dv, seg_len)
+    kda_prefill_cp_noalloc(..., seg_len=0)
     kda_decode_step(q, k, v, g, beta, state_inout, out)
     kda_decode_tokens(q, k, v, g, beta, cu_seqlens, state_in, state_out=None, out=None, num_tokens=None)
     kda_backward(q, k, v, g, beta, initial_state, cu_seqlens, dout, dfinal=None, ...) -> gradients
@@ -25,11 +26,12 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libkda.so")
 
-KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH = 0, 1, 2, 3
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_LAUNCH, KDA_ERR_SCRATCH = 0, 1, 2, 3, 4
+KDA_STATIC_SCRATCH_BYTES = 256 * 1024 * 1024      # include/kda.h
 KDA_F32, KDA_BF16 = 0, 1
 
 EXPORTS = ("kda_prefill", "kda_prefill_ex", "kda_prefill_snapshots", "kda_prefill_cp",
-           "kda_prefill_cp_workspace_size", "kda_decode_step", "kda_decode_tokens", "kda_backward",
+           "kda_prefill_cp_workspace_size", "kda_prefill_cp_noalloc", "kda_decode_step", "kda_decode_tokens", "kda_backward",
            "kda_backward_workspace_size", "kda_status_string", "kda_version")
 
 _lib = None
@@ -62,6 +64,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_prefill_cp.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp, fp,
                                    i32, vp, ctypes.c_size_t, vp]
     lib.kda_prefill_cp.restype = ctypes.c_int
+    lib.kda_prefill_cp_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, ip, i32, i32, i32, i32, i32, ctypes.c_int, vp,
+                                           fp, i32, vp]
+    lib.kda_prefill_cp_noalloc.restype = ctypes.c_int
     lib.kda_prefill_cp_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.kda_prefill_cp_workspace_size.restype = ctypes.c_size_t
     lib.kda_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i32, i32, i32, i32, ctypes.c_int, vp, vp]
@@ -206,6 +211,19 @@ def kda_prefill_cp(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state
     _check(lib.kda_prefill_cp(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
                               _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
                               _ptr(final_state), int(seg_len), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def kda_prefill_cp_noalloc(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                           seg_len: int = 0, stream=None) -> None:
+    """kda_prefill_cp in the library's static device scratch: no workspace
+    argument and no allocation.  Raises KdaError(KDA_ERR_SCRATCH) when the
+    problem needs more than KDA_STATIC_SCRATCH_BYTES; calls overlapping in
+    time on one GPU race on the shared scratch."""
+    N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
+    lib = load()
+    _check(lib.kda_prefill_cp_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                                      _ptr(cu_seqlens), N, T, H, dk, dv, _dtype_code(q), _ptr(out),
+                                      _ptr(final_state), int(seg_len), _stream(stream)))
 
 
 def kda_prefill(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, stream=None) -> None:

@@ -31,10 +31,13 @@
  *
  * Conventions for every call:
  *   - Device pointers are on the current HIP device, dense and row-major as
- *     documented; the caller owns every buffer.  The library allocates no
- *     device memory.  Its only global state is a per-device record (atomic
- *     bits) that each kernel's LDS limit has been raised; calls are
- *     thread-safe.
+ *     documented; the caller owns every buffer.  No call allocates device
+ *     memory.  The library's global state is a per-device record (atomic
+ *     bits) that each kernel's LDS limit has been raised and, for
+ *     kda_prefill_cp_noalloc only, one static device array per GPU
+ *     (KDA_STATIC_SCRATCH_BYTES) with its cached address; calls are
+ *     thread-safe, except that kda_prefill_cp_noalloc calls overlapping on
+ *     one GPU share that array.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never
  *     synchronise (except the opt-in KDA_VALIDATE=1 check of cu_seqlens,
  *     below).  Argument errors are returned before any HIP call; a launch
@@ -60,8 +63,15 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad dtype, overflowing sizes */
     KDA_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. dk != 128) */
-    KDA_ERR_LAUNCH = 3       /* the HIP launch itself failed */
+    KDA_ERR_LAUNCH = 3,      /* the HIP launch itself failed */
+    KDA_ERR_SCRATCH = 4      /* kda_prefill_cp_noalloc: the problem needs more
+                                workspace than KDA_STATIC_SCRATCH_BYTES */
 } kda_status;
+
+/* Size of the static device scratch behind kda_prefill_cp_noalloc: 256 MiB,
+ * held on every GPU the library runs on from the first load of its code object
+ * on that GPU until the process ends. */
+#define KDA_STATIC_SCRATCH_BYTES (256u * 1024u * 1024u)
 
 typedef enum {
     KDA_F32 = 0,  /* q, k, v, out are fp32 */
@@ -84,7 +94,7 @@ typedef enum {
  *                 With KDA_VALIDATE=1 in the environment (read at the first
  *                 call), every entry point that takes cu_seqlens copies it to
  *                 the host first, synchronising `stream` (so not under graph
- *                 capture), and returns
+ *                 capture; kda_prefill_cp_noalloc skips it), and returns
  *                 KDA_ERR_INVALID_ARG when these rules do not hold.
  *   out           [total_tokens, num_heads, dv]   dtype; rows of tokens owned
  *                 by a sequence are written, other rows are left untouched.
@@ -183,6 +193,32 @@ kda_status kda_prefill_cp(const void *q, const void *k, const void *v,
                           int32_t dk, int32_t dv, kda_dtype dtype,
                           void *out, float *final_state, int32_t seg_len,
                           void *workspace, size_t workspace_bytes, kda_stream_t stream);
+
+/*
+ * kda_prefill_cp_noalloc -- kda_prefill_cp for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the workspace is the library's static device array
+ * of KDA_STATIC_SCRATCH_BYTES instead of a caller-owned buffer, and the call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ * The caller still owns every input and output.
+ *   - Limit: the workspace kda_prefill_cp_workspace_size(...) reports for the
+ *     same arguments must not exceed KDA_STATIC_SCRATCH_BYTES (for example
+ *     4,096 tokens x 8 heads in bf16 need 56 MiB); larger problems return
+ *     KDA_ERR_SCRATCH before any HIP call.
+ *   - The array is per GPU and shared by every call on that GPU: calls that
+ *     overlap in time on one GPU (other streams, other threads) race on it and
+ *     give undefined results.  Serialise them, or use kda_prefill_cp.
+ *   - The array keeps the last call's contents; the call needs none of them
+ *     (every part of the workspace it reads is written earlier in the call).
+ * Arguments, results and other errors as kda_prefill_cp.
+ */
+kda_status kda_prefill_cp_noalloc(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  const float *initial_state, const int32_t *cu_seqlens,
+                                  int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                                  int32_t dk, int32_t dv, kda_dtype dtype,
+                                  void *out, float *final_state, int32_t seg_len,
+                                  kda_stream_t stream);
 
 /*
  * kda_decode_step -- one new token per (sequence, head), state updated in place

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.kda_version() >= 100
-    for code in range(4):
+    for code in range(5):
         s = lib.kda_status_string(code)
         assert s and s.decode().startswith(("KDA_OK", "KDA_ERR"))
     assert lib.kda_status_string(99) is not None

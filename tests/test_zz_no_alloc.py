@@ -1,0 +1,67 @@
+"""kda_prefill_cp_noalloc: the context-parallel prefill in the library's static
+device scratch, for callers that cannot allocate.  Its output must equal that
+of kda_prefill_cp with a caller-owned workspace (same kernels, same
+arithmetic: bit for bit), and both match the fp64 oracle to the bf16 / fp32
+tolerance rule of tests/kda_parity.py.  Two calls in a row, the second on a
+smaller input, check that the scratch's leftover contents do not matter."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from gated_delta_rule_40_amd import inputs as I
+from gated_delta_rule_40_amd import libkda as K
+from kda_parity import TOL, assert_close, host, log, oracle_prefill, run_prefill_cp, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    K.load()
+
+
+def _noalloc(inp, seg_len=0):
+    q = inp["q"]
+    T, H, _ = q.shape
+    N = inp["cu_seqlens"].shape[0] - 1
+    out = torch.full((T, H, 128), float("nan"), dtype=q.dtype, device=q.device)
+    fin = torch.full((N, H, 128, 128), float("nan"), dtype=torch.float32, device=q.device)
+    K.kda_prefill_cp_noalloc(q, inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                             inp["cu_seqlens"], out, fin, seg_len=seg_len)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_noalloc_equals_workspace_entry_two_calls(dtype):
+    big = to_dev(I.random_prefill([1500, 37, 700, 0, 1100], H=4, dtype=dtype, seed=60))
+    small = to_dev(I.random_prefill([90, 300], H=2, dtype=dtype, seed=61))
+    for label, inp, seg_len in (("first (larger)", big, 0), ("second (smaller)", small, 64)):
+        log("[noalloc] %s call, T=%d H=%d seg_len=%d dtype=%s" % (label, inp["q"].shape[0], inp["q"].shape[1],
+                                                                  seg_len, dtype))
+        need = K.kda_prefill_cp_workspace_size(inp["cu_seqlens"].shape[0] - 1, inp["q"].shape[0],
+                                               inp["q"].shape[1], 128, 128, dtype, seg_len)
+        assert 0 < need <= K.KDA_STATIC_SCRATCH_BYTES
+        out_n, fin_n = _noalloc(inp, seg_len)
+        out_w, fin_w = run_prefill_cp(inp, seg_len=seg_len)
+        assert torch.equal(out_n, out_w) and torch.equal(fin_n, fin_w), label
+        ref_out, ref_fin = oracle_prefill(inp)
+        cu = inp["cu_seqlens"].cpu().numpy()
+        rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in range(len(cu) - 1)])
+        assert_close(host(out_n)[rows], ref_out[rows], TOL[dtype], "noalloc %s out" % label, dtype)
+        assert_close(host(fin_n), ref_fin, TOL[dtype], "noalloc %s final" % label)
+
+
+def test_noalloc_rejects_a_problem_larger_than_the_scratch():
+    # 4 x 65,536 tokens x 32 heads need about 2.2 GiB of workspace: the call
+    # returns KDA_ERR_SCRATCH before any HIP call (the pointers are not read)
+    lib = K.load()
+    assert K.kda_prefill_cp_workspace_size(4, 1 << 18, 32, 128, 128, torch.bfloat16, 0) > K.KDA_STATIC_SCRATCH_BYTES
+    P = ctypes.c_void_p(0x10000)
+    st = lib.kda_prefill_cp_noalloc(P, P, P, P, P, None, P, 4, 1 << 18, 32, 128, 128, K.KDA_BF16, P, None, 0, None)
+    assert st == K.KDA_ERR_SCRATCH
+    assert "KDA_STATIC_SCRATCH_BYTES" in K.status_string(st)
