@@ -23,6 +23,7 @@ under profiles/ that the JSON line reads while their kernel-source hash matches:
     python bench.py --pmc-workload NAME           # 2 kda_prefill_cp calls + a 1 GiB negation
     python bench.py --traffic-from FETCH.csv WRITE.csv --workload NAME
     python bench.py --mfma-from MFMA.csv --workload NAME
+    python bench.py --stats-from TRACE_DIR --workload NAME
 """
 import argparse
 import hashlib
@@ -200,6 +201,53 @@ def write_traffic(fetch_csv, write_csv, workload):
     print(json.dumps(out))
 
 
+def kernel_label(name):
+    """Short label of a libkda kernel from its (possibly mangled) name."""
+    for key, label in (("kda_cp_plan_kernel", "kda_cp_plan_kernel"), ("kda_cp_combine_kernel", "kda_cp_combine_kernel"),
+                       ("kda_decode_tokens_kernel", "kda_decode_tokens_kernel"), ("kda_decode_kernel", "kda_decode_kernel")):
+        if key in name:
+            return label
+    if "kda_prefill_kernel" in name:
+        return "kda_prefill_kernel<%s> (%s)" % ("bf16" if "DF16b" in name else "fp32",
+                                               "chunk operands" if "Li1EEE" in name else "fused")
+    if "kda_chain_kernel" in name:
+        kind = "segment summaries" if CP_KINDS["summaries"](name) else "segment outputs"
+        return "kda_chain_kernel<%s> (%s)" % ("bf16" if "DF16b" in name else "fp32", kind)
+    return name.split("(")[0][:60]
+
+
+def write_stats(trace_dir, workload):
+    """Per-kernel durations of the kda_prefill_cp calls of a rocprofv3
+    --kernel-trace run of ``bench.py --pmc-workload`` (the last call: the
+    first one pays first-use costs), written as a text summary."""
+    import csv
+    rows = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+            if "kda" in r["Kernel_Name"]]
+    ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
+    calls = len([k for k in ks if "kda_cp_plan_kernel" in k[2]])
+    last = ks[len(ks) - len(ks) // max(calls, 1):]
+    short = workload[len("prefill_"):] if workload.startswith("prefill_") else workload
+    path = os.path.join(ROOT, "profiles", "kda_prefill_cp_%s_kernel_stats.txt" % short)
+    lines = ["# rocprofv3 kernel trace: one kda_prefill_cp call on %s (automatic seg_len), MI355X (gfx950)" % workload,
+             "# kernel source sha256/16: %s" % source_hash(PREFILL_SRC),
+             "#",
+             "# command (repo at <repo>):",
+             "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run \\",
+             "#       -- python <repo>/bench.py --pmc-workload %s" % workload,
+             "#   python bench.py --stats-from <dir> --workload %s" % workload,
+             "# source: <dir>/run_kernel_trace.csv, the last of the run's %d calls" % calls,
+             "#",
+             "%-52s %12s" % ("kernel", "duration_us")]
+    for s0, e0, name in last:
+        lines.append("%-52s %12.1f" % (kernel_label(name), (e0 - s0) / 1e3))
+    lines.append("")
+    lines.append("# kernel time per call: %.1f us; first launch start to last launch end: %.1f us"
+                 % (sum(e0 - s0 for s0, e0, _ in last) / 1e3, (last[-1][1] - last[0][0]) / 1e3))
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def host_cores():
     """(cores used, cores available): the cores this process may run on
     (sched_getaffinity), at most OMP_NUM_THREADS when the environment sets it."""
@@ -330,7 +378,12 @@ def main():
                     help="write the executed-MFMA summary from a rocprofv3 --pmc run of the MFMA counters and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit (no GPU)")
+    ap.add_argument("--stats-from", metavar="TRACE_DIR",
+                    help="write the per-kernel duration summary of a rocprofv3 --kernel-trace run and exit")
     args = ap.parse_args()
+    if args.stats_from:
+        write_stats(args.stats_from, args.workload)
+        return
     if args.mfma_from:
         write_mfma(args.mfma_from, args.workload)
         return
