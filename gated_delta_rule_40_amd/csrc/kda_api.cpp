@@ -275,15 +275,20 @@ bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16
     return true;
 }
 
-// Default segment length: about 512 (segment, head) pairs (two output-pass
-// workgroups per compute unit), at least 256 tokens (8 chunks: shorter
-// segments add more combine steps than they take off a workgroup's walk;
-// 4,096 tokens x 8 heads: 0.132 ms at 256, 0.145 ms at 512, 0.41 ms at 128)
-// and at most 65,536.
+// Default segment length: about 256 (segment, head) pairs (one output-pass
+// workgroup per compute unit: fewer, longer segments than two per unit, so
+// fewer summary units and a shorter combine chain), at least 256 tokens (8
+// chunks: shorter segments add more combine steps than they take off a
+// workgroup's walk) and at most 32,768 (1,024 chunks: a longer segment's walk
+// becomes the critical path).  Measured: 4,096 tokens x 8 heads take 0.133 ms
+// at 256, 0.146 ms at 512 and 0.40 ms at 128; 4 x 16,384 tokens x 32 heads
+// 1.9-2.0 ms at 8,192 against 2.13 ms at 4,096 and 16,384; the 1M-token
+// varlen batch x 16 heads 17.0 ms at 32,768 against 17.3 ms at 16,384 and
+// 18.0-18.1 ms at 49,152 and 65,536.
 int32_t cp_default_seg_len(int32_t T, int32_t H)
 {
-    int64_t len = (int64_t)T * H / 512;
-    len = len < 256 ? 256 : (len > 65536 ? 65536 : len);
+    int64_t len = (int64_t)T * H / 256;
+    len = len < 256 ? 256 : (len > 32768 ? 32768 : len);
     return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
 }
 

@@ -378,8 +378,11 @@ constexpr float kScaleCap = 18446744073709551616.f;
 // W is rounded as W sS / GS, so (GS K^)^T (W sS / GS) = K^T W sS lands in the
 // same scaled units.  sS changes (by exact powers of two) only when a column
 // leaves [2^-8, 2^15), or when W sS / GS would leave the fp16 range.
-template <typename TIn, int C, int ldv, int ldo, bool SUMMARY, int NCT = 1>
-__device__ __forceinline__ void chain_chunk(
+// Tile ct reads value column vc + CTS ct and writes output column oc + CTS ct.
+// Returns (16-bit operands only; wave-uniform) a mask with bit ct set when
+// every column of tile ct is exactly zero after the update.
+template <typename TIn, int C, int ldv, int ldo, bool SUMMARY, int NCT = 1, int CTS = 16>
+__device__ __forceinline__ uint32_t chain_chunk(
     f32x4 (&S)[NCT][DK / 16], float (&sS)[NCT], const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
     const typename PrefillCfg<TIn, C, 4>::OpT *sQp, const typename PrefillCfg<TIn, C, 4>::OpT *sKhT,
     const typename PrefillCfg<TIn, C, 4>::OpT *sT, const typename PrefillCfg<TIn, C, 4>::OpT *sP,
@@ -427,7 +430,7 @@ __device__ __forceinline__ void chain_chunk(
             const float br = sBeta[r];
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
-                X[ct][mt][i] = br * (to_f(sV[r * ldv + vc + 16 * ct]) + t[ct][i] * isS[ct]);
+                X[ct][mt][i] = br * (to_f(sV[r * ldv + vc + CTS * ct]) + t[ct][i] * isS[ct]);
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) xmax[ct] = absmax_acc(xmax[ct], X[ct][mt]);
@@ -513,7 +516,7 @@ __device__ __forceinline__ void chain_chunk(
         for (int ct = 0; ct < NCT; ++ct) {
             const f32x4 o = o1[ct] * isS[ct] + o2[ct] * isWt[ct];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc + 16 * ct] = from_f<TIn>(o[i]);
+            for (int i = 0; i < 4; ++i) sO[(mt * SUB + 4 * lj + i) * ldo + oc + CTS * ct] = from_f<TIn>(o[i]);
         }
     }
     // S~ = Diag(gamma) S~ + (GS K^)^T Wf, the decayed state as the accumulator
@@ -543,10 +546,12 @@ __device__ __forceinline__ void chain_chunk(
     // the scale never grows past 2^64: a column decaying towards zero (the
     // transition columns of a strongly decaying segment) is then left to
     // shrink, its values being negligible at that point
+    uint32_t zero = 0;
     if (kIn16) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const float m = colmax(smax[ct]);
+            zero |= __ballot(m != 0.f) == 0 ? 1u << ct : 0u;
             float q = 1.f;
             if (m >= 32768.f) q = pow2_scale(m);
             else if (m > 0.f && m < 0.00390625f) q = fmaxf(1.f, fminf(pow2_scale(m), kScaleCap * pow2_inv(sS[ct])));
@@ -557,6 +562,7 @@ __device__ __forceinline__ void chain_chunk(
             }
         }
     }
+    return zero;
 }
 
 // MODE_FUSED: the whole chunk loop per (sequence, head, value block), as
@@ -1240,11 +1246,12 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
     const int64_t rowV = (int64_t)H * dv;
 
     // ---- entering state: tile ct of this wave is column dv0 + 16 (NCT wave + ct) + lm
+    const int vcol = 16 * NCT * wave + lm;           // tile 0's column in the block
     f32x4 S[NCT][DK / 16];
     float sS[NCT];
     int colc[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) colc[ct] = dv0 + 16 * (NCT * wave + ct) + lm;
+    for (int ct = 0; ct < NCT; ++ct) colc[ct] = dv0 + vcol + 16 * ct;
     const int64_t sbase = ((int64_t)n * num_heads + h) * DK * dv;
     const float *S_in = nullptr;
     int64_t S_in_base = 0;
@@ -1332,15 +1339,31 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         // sets A (ri, rv) and B (ri2, rv2) in turn, so that a load has two
         // chunks' work to arrive; the loop takes chunks in pairs to keep the
         // sets apart, and a compiler barrier after each load keeps it from
-        // being moved next to its use
+        // being moved next to its use.
+        // A wave whose columns are all transition columns (V = 0) stops
+        // computing once its whole slice is exactly zero: then X = 0, W = 0 and
+        // the state stays zero at every later chunk, so skipping the chain is
+        // exact.  Under decay this happens after about a thousand tokens, and
+        // the value columns' waves then have their SIMDs to themselves.  (Pairing
+        // a value and a transition tile in every wave, so that all waves keep a
+        // tile once the transition tiles die, measured no faster.)
+        const bool trans_wave = dv0 + 16 * NCT * wave >= dv;
+        bool dead = false;
         auto run = [&](int ci) {
+            if (dead) return;
             const unsigned char *base = smem + (ci & 1) * Q::BUF;
-            chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT>(
-                S, sS, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
-                reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
-                reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
-                reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
-                reinterpret_cast<const TIn *>(base + Q::offV), 16 * NCT * wave + lm, nullptr, lm, lj, lm);
+            const OpT *nkp = reinterpret_cast<const OpT *>(base + Q::offNKp);
+            const OpT *qp = reinterpret_cast<const OpT *>(base + Q::offQp);
+            const OpT *kht = reinterpret_cast<const OpT *>(base + Q::offKhT);
+            const OpT *tt = reinterpret_cast<const OpT *>(base + Q::offT);
+            const OpT *pp = reinterpret_cast<const OpT *>(base + Q::offP);
+            const float *ts = reinterpret_cast<const float *>(base + Q::offTs);
+            const float *gam = reinterpret_cast<const float *>(base + Q::offGam);
+            const float *bet = reinterpret_cast<const float *>(base + Q::offBeta);
+            const TIn *sv = reinterpret_cast<const TIn *>(base + Q::offV);
+            const uint32_t zero = chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT>(
+                S, sS, nkp, qp, kht, tt, pp, ts, gam, bet, sv, vcol, nullptr, lm, lj, lm);
+            dead = trans_wave && zero == (1u << NCT) - 1u;
         };
         if (nch > 0) {
             load_to(0, ri, rv);
@@ -1379,7 +1402,7 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
             reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
             reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
-            reinterpret_cast<const TIn *>(base + Q::offV), 16 * NCT * wave + lm, sOw, lm, lj, lm);
+            reinterpret_cast<const TIn *>(base + Q::offV), vcol, sOw, lm, lj, lm);
         if (!SUMMARY && (!SNAP || out)) {
             // this wave's 16 output columns: rows of 16 * sizeof(TIn) bytes, one
             // 16-byte vector per lane and step (LDS is in order within a wave).
@@ -1662,25 +1685,35 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
     const int col = (slot % nblk) * CMB_COLS + lm;
     // S^0 (and M, unless m_src) in seg_out rows of ld floats; M in rows of ldm
     const int ld = m_src ? dv : dv + DK, ldm = dv + DK;
+    // the walk's units first: their loads then overlap those of the state
+    const int s0 = seq_seg[n], s1 = seq_seg[n + 1];
+    int ns = s1 - s0;
     // the state slice: every wave holds all of it (rows 16 r + 4 lj + i, column
     // col) and its own row tile in own; both always come from LDS
     f32x4 own, S[DK / 16];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         own[i] = init ? init[((int64_t)n * H + h) * DK * dv + (int64_t)(16 * wave + 4 * lj + i) * dv + col] : 0.f;
+    if (plan && !reverse) {
+        // the sequence's first SEG_LAST unit, 64 units per step: lane i tests
+        // unit base + i and a ballot finds the first hit (wave-uniform), so
+        // the plan entries are read side by side rather than one dependent
+        // load after another
+        for (int base = 0; base < ns - 1; base += 64) {
+            const int it = base + lane;
+            const bool hit = it < ns - 1 && (plan[4 * (s0 + it) + 3] & SEG_LAST);
+            const uint64_t m = __ballot(hit);
+            if (m) {
+                ns = base + __builtin_ctzll(m) + 1;
+                break;
+            }
+        }
+    }
     sS[wave][lane] = own;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
     own = sS[wave][lane];
-    const int s0 = seq_seg[n], s1 = seq_seg[n + 1];
-    int ns = s1 - s0;
-    if (plan && !reverse)
-        for (int it = 0; it < ns - 1; ++it)
-            if (plan[4 * (s0 + it) + 3] & SEG_LAST) {
-                ns = it + 1;
-                break;
-            }
     auto seg_of = [&](int it) { return reverse ? s1 - 1 - it : s0 + it; };
     auto fetch = [&](int it, CmbOps &o) {                  // step it's operands (clamped to the last step)
         const int64_t gs = seg_of(min(it, ns - 2));

@@ -174,7 +174,7 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  * they pack the compute units evenly; the outputs still run whole segments.
  *
  *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
- *              (total_tokens * num_heads / 512, clamped to [256, 65536])
+ *              (total_tokens * num_heads / 256, clamped to [256, 32768])
  *   workspace  device memory of at least kda_prefill_cp_workspace_size(...)
  *              bytes, 256-byte aligned, owned by the caller, contents
  *              ignored on entry; calls that share one workspace must not
