@@ -248,6 +248,39 @@ def write_stats(trace_dir, workload):
     print("\n".join(lines))
 
 
+def write_kernel_summary(trace_dir, name):
+    """Average duration of every libkda kernel in a rocprofv3 --kernel-trace
+    run of the default bench step (``bench.py --steps 2 --warmup 1
+    --no-cpu-baseline``), written as a text summary: the decode, replay and
+    backward kernels that the JSON line times with HIP events."""
+    import csv
+    rows = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+            if "kda" in r["Kernel_Name"]]
+    agg = {}
+    for r in rows:
+        lab = kernel_label(r["Kernel_Name"]) if "backward" not in r["Kernel_Name"] else \
+            r["Kernel_Name"].split("(")[0].replace("void ", "")[:60]
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        agg.setdefault(lab, []).append(d)
+    path = os.path.join(ROOT, "profiles", "%s_kernel_stats.txt" % name)
+    lines = ["# rocprofv3 kernel trace of the default bench step, MI355X (gfx950)",
+             "# kernel source sha256/16 (kda_prefill.hip): %s" % source_hash(PREFILL_SRC),
+             "#",
+             "# command (repo at <repo>):",
+             "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run \\",
+             "#       -- python <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+             "#   python bench.py --kernel-summary-from <dir> --summary-name %s" % name,
+             "# every libkda kernel of the run (prefill calls of all workloads, 64 decode steps per",
+             "# bench step, the replay and backward measurements), averaged over its launches",
+             "#",
+             "%-60s %7s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+    for lab, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%-60s %7d %12.1f %12.1f %12.1f" % (lab, len(ds), sum(ds) / len(ds), min(ds), max(ds)))
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def host_cores():
     """(cores used, cores available): the cores this process may run on
     (sched_getaffinity), at most OMP_NUM_THREADS when the environment sets it."""
@@ -380,7 +413,14 @@ def main():
                     help="write the HBM-traffic summary from two rocprofv3 counter CSVs and exit (no GPU)")
     ap.add_argument("--stats-from", metavar="TRACE_DIR",
                     help="write the per-kernel duration summary of a rocprofv3 --kernel-trace run and exit")
+    ap.add_argument("--kernel-summary-from", metavar="TRACE_DIR",
+                    help="write the average duration of every libkda kernel of a bench trace and exit")
+    ap.add_argument("--summary-name", default="kda_bench_step",
+                    help="file name stem under profiles/ for --kernel-summary-from")
     args = ap.parse_args()
+    if args.kernel_summary_from:
+        write_kernel_summary(args.kernel_summary_from, args.summary_name)
+        return
     if args.stats_from:
         write_stats(args.stats_from, args.workload)
         return
