@@ -29,7 +29,7 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
 extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
                                             const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
                                             int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
-                                            hipStream_t stream);
+                                            void *gimg, hipStream_t stream);
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
@@ -37,20 +37,16 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, float *snap, const int32_t *init_seq_seg,
                                        int32_t init_unit, int32_t init_units, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
-extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
-                                                  const float *beta, const void *dout, const int32_t *plan,
-                                                  int32_t num_segs, int32_t T_tot, int32_t H, int32_t ncols,
-                                                  float *seg_out, hipStream_t stream);
-extern "C" size_t kda_backward_scratch_floats_per_wg();
-extern "C" int32_t kda_backward_max_wgs();
-extern "C" int32_t kda_backward_num_blocks();
-extern "C" hipError_t kda_launch_backward(int bf16, const void *q, const void *k, const void *v, const float *g,
-                                          const float *beta, const float *init, const int32_t *cu,
-                                          const int32_t *chunk_off, const float *snaps, const void *dout,
-                                          const int32_t *plan, int32_t num_segs, const float *seg_dsend,
-                                          int32_t N, int32_t T_tot, int32_t H, float *scratch,
-                                          float *part_vec, float *part_beta, float *dq, float *dk, float *dv,
-                                          float *dg, float *dbeta, float *dinit, hipStream_t stream);
+extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
+                                            int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
+                                            const int32_t *sched, const int32_t *chunk_off, const void *gimg,
+                                            const float *g_end, float *g_chunk, float *dinit, float *g0_out,
+                                            hipStream_t stream);
+extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const void *v, const float *g,
+                                           const float *beta, const void *dout, const float *init, const int32_t *cu,
+                                           const int32_t *chunk_off, int64_t max_chunks, const float *snaps,
+                                           const float *gchunk, int32_t N, int32_t T_tot, int32_t H, float *dq,
+                                           float *dk, float *dv, float *dg, float *dbeta, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const void *k, const void *v,
                                                const float *g, const float *beta, const int32_t *cu,
                                                const int32_t *num_tokens, const float *state_in,
@@ -354,7 +350,7 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
                                       lay.max_units, uplan, useq_seg, usched, seg_len, 1, seq_order, s);
     if (e == hipSuccess)   // chunk operands of every (chunk, head)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
-                                  lay.max_chunks, img, s);
+                                  lay.max_chunks, img, nullptr, s);
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
@@ -454,15 +450,14 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
 namespace {
 
 struct BwdLayout {
-    size_t plan, sched, seq_seg, chunk_off, img, snaps, fsum, bsum, seg_dsend, scratch, part_vec, part_beta, total;
+    size_t plan, sched, seq_seg, chunk_off, img, gimg, snaps, gchunk, fsum, bsum, seg_dsend, total;
     int32_t max_chunks, max_segs, seg_len;
 };
 
 // Segment length of the backward, shared with the forward pipeline that
 // stores the chunk-start states (so that a segment's gradient transition is
 // the transpose of its forward transition): about 256 segments per head
-// count (about 1,024 work items of (segment, head, 32 columns), two per
-// workgroup of the main pass), at least 256 tokens, a multiple of the chunk.
+// count, at least 256 tokens, a multiple of the chunk.
 int32_t bwd_seg_len(int32_t T, int32_t H)
 {
     int64_t len = (int64_t)T * H / 256;
@@ -473,11 +468,10 @@ int32_t bwd_seg_len(int32_t T, int32_t H)
 // Workspace sections: the plan [max_segs][4] int32 (no segment marked last:
 // the forward summaries cover every segment), its dispatch order [max_segs]
 // and the first segment [N+1] and first chunk [N+1] of each sequence; the
-// chunk images; forward states at chunk starts [max_chunks][H][dk][dv];
-// forward summaries [max_segs][H][dk][dv + dk]; gradient summaries
-// [max_segs][H][dk][dv]; entering states, then entering gradients
-// [max_segs][H][dk][dv]; the main pass's per-workgroup scratch; the partial
-// row sums of dq, dk, dg and dbeta.
+// chunk images and the gradient images (same slots); forward states at chunk
+// starts and state gradients at chunk ends [max_chunks][H][dk][dv]; forward
+// summaries [max_segs][H][dk][dv + dk]; gradient summaries [max_segs][H][dk][dv];
+// entering states, then entering gradients [max_segs][H][dk][dv].
 bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
 {
     const int32_t seg_len = bwd_seg_len(T, H);
@@ -485,10 +479,7 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     const int64_t segs = (int64_t)T / seg_len + 1 + N;
     if (chunks > INT32_MAX / 4 || segs > INT32_MAX / 4) return false;
     const size_t S = (size_t)kHeadDim * kHeadDim;
-    const size_t rows = (size_t)T * H;
-    const size_t nblk = (size_t)kda_backward_num_blocks();
-    const int64_t items = segs * H * (int64_t)nblk;
-    const size_t wgs = (size_t)(items < kda_backward_max_wgs() ? items : kda_backward_max_wgs());
+    const size_t img = kda_chunk_image_bytes(bf16) * (size_t)chunks * H;
     lay->seg_len = seg_len;
     lay->max_chunks = (int32_t)chunks;
     lay->max_segs = (int32_t)segs;
@@ -497,14 +488,13 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     lay->seq_seg = align256(lay->sched + sizeof(int32_t) * (size_t)segs);
     lay->chunk_off = align256(lay->seq_seg + sizeof(int32_t) * ((size_t)N + 1));
     lay->img = align256(lay->chunk_off + sizeof(int32_t) * ((size_t)N + 1));
-    lay->snaps = align256(lay->img + kda_chunk_image_bytes(bf16) * (size_t)chunks * H);
-    lay->fsum = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
+    lay->gimg = align256(lay->img + img);
+    lay->snaps = align256(lay->gimg + img);
+    lay->gchunk = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
+    lay->fsum = align256(lay->gchunk + sizeof(float) * (size_t)chunks * H * S);
     lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 2 * S);
     lay->seg_dsend = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
-    lay->scratch = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
-    lay->part_vec = align256(lay->scratch + sizeof(float) * wgs * kda_backward_scratch_floats_per_wg());
-    lay->part_beta = align256(lay->part_vec + sizeof(float) * nblk * 3 * rows * kHeadDim);
-    lay->total = align256(lay->part_beta + sizeof(float) * nblk * rows);
+    lay->total = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
     return true;
 }
 
@@ -558,17 +548,21 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     float *bsum = reinterpret_cast<float *>(ws + lay.bsum);
     float *seg_dsend = reinterpret_cast<float *>(ws + lay.seg_dsend);
     void *img = ws + lay.img;
+    void *gimg = ws + lay.gimg;
+    float *gchunk = reinterpret_cast<float *>(ws + lay.gchunk);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // segments and chunk numbering; no segment is marked last, so the forward
     // summaries include every segment's transition
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
                                       kCpChunk, lay.max_chunks, chunk_off, sched, -1, 0, nullptr, 0, 0, nullptr,
                                       nullptr, nullptr, 0, 0, nullptr, s);
-    // forward: the state at every chunk start, by the context-parallel
-    // pipeline with state stores and no outputs
+    // chunk operands of every (chunk, head): the forward image and the
+    // transposed one of the gradient chain
     if (e == hipSuccess)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
-                                  lay.max_chunks, img, s);
+                                  lay.max_chunks, img, gimg, s);
+    // forward: the state at every chunk start, by the context-parallel
+    // pipeline with state stores and no outputs
     if (e == hipSuccess)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
@@ -581,18 +575,17 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_dsend, nullptr, chunk_off, img, sched,
                              snaps, nullptr, 0, 0, s);
     if (e == hipSuccess)   // gradient summaries G^0 of every segment but a sequence's first
-        e = kda_launch_backward_summary(bf16, q, k, g, beta, dout, plan, lay.max_segs, total_tokens, num_heads,
-                                        dk, bsum, s);
+        e = kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
+                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, bsum, s);
     if (e == hipSuccess)   // the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
                                   fsum, 1, s);
-    if (e == hipSuccess)
-        e = kda_launch_backward(bf16, q, k, v, g, beta, initial_state, cu_seqlens, chunk_off, snaps, dout, plan,
-                                lay.max_segs, seg_dsend, num_seqs, total_tokens, num_heads,
-                                reinterpret_cast<float *>(ws + lay.scratch),
-                                reinterpret_cast<float *>(ws + lay.part_vec),
-                                reinterpret_cast<float *>(ws + lay.part_beta), dq, dk_out, dv_out, dg, dbeta, dinit,
-                                s);
+    if (e == hipSuccess)   // the gradient at every chunk end, and d(initial state)
+        e = kda_launch_grad_chain(bf16, 0, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
+                                  sched, chunk_off, gimg, seg_dsend, gchunk, dinit, nullptr, s);
+    if (e == hipSuccess)   // every chunk's gradients of q, k, v, g and beta
+        e = kda_launch_bwd_chunk(bf16, q, k, v, g, beta, dout, initial_state, cu_seqlens, chunk_off, lay.max_chunks,
+                                 snaps, gchunk, num_seqs, total_tokens, num_heads, dq, dk_out, dv_out, dg, dbeta, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -1,64 +1,32 @@
-// kda_backward.hip -- gradients of the KDA recurrence (training).
+// kda_backward.hip -- gradients of the KDA recurrence (training), chunk form.
 //
 // The recurrence (page ailearn.mscapital.top/kimi-k3.html, card "KDA 单头递归"),
-// token form with Sp = S_{t-1}, alpha = exp(g):
-//     Sbar = Diag(alpha) Sp,  u = v - Sbar^T k,  S = Sbar + beta k u^T,  o = S^T q.
-// Its reverse, for dS = dL/dS_t (from later tokens, or d(final_state)):
-//     dS  += q do^T;            dq = S do
-//     x    = dS^T k;            du = dv = beta x;       dbeta = x . u
-//     dk   = beta dS u - Sbar du
-//     dSbar = dS - k du^T;      dg = alpha (.) rowsum(dSbar (.) Sp)
-//     dS_{t-1} = Diag(alpha) dSbar
-// and d(initial_state) is dS after the first token.
-//
-// Work decomposition.  The state and its gradient evolve column by column:
-// column c of S and dS needs only column c of v, do and du.  Only dq, dk, dg
-// and dbeta sum over columns.  So one work item is a (segment, head) and a
-// block of BV = 32 value columns, with S and dS in registers; its row sums go
-// to per-block partial buffers that a second kernel adds in a fixed order
-// (deterministic).  The forward states are needed in reverse order: the
-// state at every 32-token chunk start comes from the forward prefill kernel
-// (context-parallel pipeline with state stores), and inside a chunk the
-// workgroup rebuilds the token states it needs in registers, then walks them
-// backwards.
-//
-// Segments.  The gradient recurrence is linear in dS, as the forward one is
-// in S (dS_{t-1} = Diag(alpha) (I - beta k k^T) (dS_t + q do^T)), so the
-// sequences are cut into chunk-aligned segments that run side by side, as in
-// the context-parallel forward: a summary pass takes each segment but a
-// sequence's first from a zero gradient at its end to its start over the 128
-// value columns, giving G^0; the segment's gradient transition R is the
-// transpose of its forward transition M, which the forward pipeline's
-// summaries already hold (the forward step is S_t = (I - beta k k^T) Diag(alpha)
-// S_{t-1}, the gradient step its transpose, and a product of transposes in
-// reverse order is the transpose of the product).  A reverse combine then
-// gives the gradient entering every segment at its end, G(last) =
-// d(final_state), G(s-1) = M_s^T G(s) + G^0_s, and the main pass runs every
-// segment from there.
+// S_t = (I - b_t k_t k_t^T) Diag(e^g_t) S_{t-1} + b_t k_t v_t^T, o_t = S_t^T q_t,
+// runs forward in the chunk form of kda_prefill.hip.  Its gradients come in
+// three steps, all chunk-parallel or segment-parallel:
+//   1. the forward pipeline stores the state at every chunk start (and the
+//      chunk-operand pass writes, next to each chunk image, the transposed
+//      "gradient image");
+//   2. the state gradient G_t = dL/dS_t runs backwards through the chunks in
+//      chunk form (kda_grad_chain_kernel, kda_prefill.hip): per segment from a
+//      zero gradient (summaries), a reverse combine through the transposed
+//      forward transitions, then every segment from its entering gradient,
+//      storing G at every chunk end;
+//   3. kda_bwd_chunk_kernel (below) turns each chunk's S (start), G (end) and
+//      inputs into its gradients of q, k, v, g and beta -- no recurrence left,
+//      one workgroup per (chunk, head).
 #include "kda_device.hpp"
 
 namespace kda {
 
 constexpr int BD = 128;              // dk = dv
-constexpr int BWD_THREADS = 256;
-constexpr int BWD_C = 32;            // tokens per checkpoint interval (the forward chunk)
-constexpr int BWD_BV = 32;           // value columns per workgroup
-constexpr int BWD_CPR = BWD_BV / 4;  // threads per row group (4 columns each)
-constexpr int BWD_RG = BWD_THREADS / BWD_CPR;   // row groups
-constexpr int BWD_RPT = BD / BWD_RG;            // rows per thread
-constexpr int BWD_NBLK = BD / BWD_BV;
-static_assert(BWD_CPR == 8, "row sums use sum8");
 
 __device__ __forceinline__ float dot4(const f32x4 &a, const f32x4 &b) {
     return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-// ---- wave-level layout.  A wave owns 8 columns: lane = rg + 16 cg holds rows
-// rg + 16 i (i = 0..7) of columns 2 cg, 2 cg + 1.  A sum over the 128 rows
-// is a sum over the 16 lanes of a DPP row (symmetric exchanges, so every lane
-// ends with the same value); a sum over the wave's columns is a sum over its
-// four DPP rows.  Token vectors go through a wave-private LDS area with
-// channel c at (c mod 16) 8 + c / 16, so that a lane's 8 rows are contiguous.
+// Sums across lanes: over the 16 lanes of a DPP row (a row of an MFMA tile's
+// columns), and over the four DPP rows (the lane groups that share a column).
 __device__ __forceinline__ float sum16(float x) {       // over the 16 lanes of each DPP row
     x += dpp_mov<0xB1>(x);                             // quad_perm(1,0,3,2): lane ^ 1
     x += dpp_mov<0x4E>(x);                             // quad_perm(2,3,0,1): lane ^ 2
@@ -71,502 +39,554 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
     const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-__device__ __forceinline__ int chan_pos(int c) { return (c & 15) * 8 + (c >> 4); }
 
-// Segment summaries of the gradient recurrence: one workgroup per (segment,
-// head, block of 32 of the ncols columns), segments that are not a sequence's
-// first; each wave runs its 8 columns on its own (no barrier).  seg_out:
-// [num_segs][H][BD][ncols]: [G^0 | R] per segment for ncols = 2 BD, G^0 alone
-// for ncols = BD (R is then the transpose of the forward transition M of the
-// same segment: dS_{t-1} = Diag(alpha)(I - beta k k^T) dS_t is the transpose of
-// the forward step's map, applied in the opposite order).
+// ============================================================ chunk form
+// Per (chunk, head) gradients from the state S at the chunk start and the
+// state gradient G at its end (fp32, [DK][DK] row-major; S from the forward
+// pipeline's chunk-start states, G from the state-gradient chain).  With the
+// chunk form of the forward (kda_prefill.hip; chunk of C tokens, Gamma the
+// cumulative gate, K+ = K (.) e^Gamma, Q+ = Q (.) e^Gamma, K^ = K (.)
+// e^(Gamma_L - Gamma), A, P the decayed Gram tiles, N = Diag(b) A,
+// T = (I + N)^-1, E_ric = e^(Gamma_rc - Gamma_ic)), the chain rule gives
+//     U = V - K+ S,   X = Diag(b) U,   W = T X
+//     dW = K^ G + P^T dO,   dX = T^T dW,   dv = Diag(b) dX
+//     dQ+ = dO S^T,   dK+ = -Diag(b) dX S^T,   dK^ = W G^T
+//     dP = tril(dO W^T),   dN = -stril(dX W^T),   dA = Diag(b) dN
+//     dbeta_r = sum_i dN_ri A_ri + sum_c U_rc dX_rc
+//     dq = dQ+ (.) e^Gamma + sum_i dP_ri k_i (.) E_ri
+//     dk = dK+ (.) e^Gamma + sum_i dA_ri k_i (.) E_ri                      (row part)
+//        + dK^ (.) e^(Gamma_L - Gamma) + sum_r (dA_ri k_r + dP_ri q_r) (.) E_ri   (column part)
+//     dGamma = q (.) dq + k (.) (row part) - k (.) (column part), and at the
+//              last token also sum_r k (.) dK^ (.) e^(Gamma_L - Gamma) + (G (.) S) 1 (.) e^Gamma_L
+//     dg = reverse cumulative sum of dGamma over the chunk.
+// Everything runs on fp32 (MFMA 16x16x4 and VALU), for both input types.
+// Gamma is kept in fp64: every decay factor is e^x of a difference of two of
+// its entries, rounded to fp32 only then, so a factor carries the rounding of
+// its own exponent, not that of the (up to 160 in magnitude) cumulative sums.
+// E is factored per 16-token block pair with a reference inside the pair --
+// the middle token of a diagonal block, the block boundary for the
+// off-diagonal one -- so every factor lies in [e^-80, e^40] for g in [-5, 0]:
+// the Gram tiles and the E-weighted token sums are then plain MFMA products of
+// factored operands, and a factor applied after a product is at most e^40.
+namespace bc {
+constexpr int C = 32, NT = 256;
+constexpr int LDG = BD + 2;          // fp64 Gamma rows
+constexpr int LDF = BD + 4;          // fp32 [C][BD] rows
+constexpr int LDX = C + 4;           // fp32 [C][C] rows
 template <typename T>
-__global__ __launch_bounds__(BWD_THREADS) void kda_backward_summary_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ plan,
-    int32_t num_segs, int32_t H, int32_t T_tot, int32_t ncols, float *__restrict__ seg_out)
-{
-    __shared__ __align__(16) float sv[BWD_THREADS / 64][3][BD];   // per wave: k, alpha, q
-    const int ncb = ncols / BWD_BV;
-    const int blk = blockIdx.x % ncb;
-    const int64_t unit = blockIdx.x / ncb;
-    if (unit >= (int64_t)num_segs * H) return;
-    const int su = (int)(unit / H), h = (int)(unit % H);
-    if (plan[4 * su] < 0 || (plan[4 * su + 3] & SEG_FIRST)) return;
-    const int ts = min(max(plan[4 * su + 1], 0), T_tot);
-    const int te = min(max(plan[4 * su + 2], ts), T_tot);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int rg = lane & 15, cg = lane >> 4;
-    const int c0 = blk * BWD_BV + 8 * wave + 2 * cg;   // this lane's columns c0, c0 + 1 in [0, 2 BD)
-    const bool trans = blk * BWD_BV >= BD;            // transition columns: identity at the end, do = 0
-    float (*w)[BD] = sv[wave];
-    f32x2 G[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = rg + 16 * i;
-        G[i][0] = (trans && r == c0 - BD) ? 1.f : 0.f;
-        G[i][1] = (trans && r == c0 + 1 - BD) ? 1.f : 0.f;
-    }
-    // the next token's vectors, one step ahead: channels 2 lane, 2 lane + 1 of
-    // k, g, q, and this lane's two columns of dout (clamped rows: loads on every path)
-    f32x2 nk, ng, nq, ndo;
-    float nb;
-    auto fetch = [&](int tt) {
-        const int64_t row = (int64_t)tt * H + h;
-        nk = load_pair(k + row * BD + 2 * lane);
-        ng = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
-        nq = load_pair(q + row * BD + 2 * lane);
-        ndo = load_pair(dout + row * BD + (c0 & (BD - 1)));
-        nb = beta[row];
-    };
-    if (te > ts) fetch(te - 1);
-    for (int tt = te - 1; tt >= ts; --tt) {
-        const f32x2 kk = nk, gg = ng, qq = nq, dd = trans ? f32x2{0.f, 0.f} : ndo;
-        const float bt = nb;
-        fetch(max(tt - 1, ts));
-        // wave-private LDS: written and read by this wave only, in order
-        w[0][chan_pos(2 * lane)] = kk[0];
-        w[0][chan_pos(2 * lane + 1)] = kk[1];
-        w[1][chan_pos(2 * lane)] = __expf(gg[0]);
-        w[1][chan_pos(2 * lane + 1)] = __expf(gg[1]);
-        w[2][chan_pos(2 * lane)] = qq[0];
-        w[2][chan_pos(2 * lane + 1)] = qq[1];
-        __builtin_amdgcn_wave_barrier();
-        float kr[8], ar[8], qr[8];
-        *reinterpret_cast<f32x4 *>(kr) = *reinterpret_cast<const f32x4 *>(&w[0][8 * rg]);
-        *reinterpret_cast<f32x4 *>(kr + 4) = *reinterpret_cast<const f32x4 *>(&w[0][8 * rg + 4]);
-        *reinterpret_cast<f32x4 *>(ar) = *reinterpret_cast<const f32x4 *>(&w[1][8 * rg]);
-        *reinterpret_cast<f32x4 *>(ar + 4) = *reinterpret_cast<const f32x4 *>(&w[1][8 * rg + 4]);
-        *reinterpret_cast<f32x4 *>(qr) = *reinterpret_cast<const f32x4 *>(&w[2][8 * rg]);
-        *reinterpret_cast<f32x4 *>(qr + 4) = *reinterpret_cast<const f32x4 *>(&w[2][8 * rg + 4]);
-        __builtin_amdgcn_wave_barrier();
-        float px0 = 0.f, px1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            G[i][0] += qr[i] * dd[0];                   // o = S^T q
-            G[i][1] += qr[i] * dd[1];
-            px0 += G[i][0] * kr[i];                      // dS^T k
-            px1 += G[i][1] * kr[i];
-        }
-        const float du0 = sum16(px0) * bt, du1 = sum16(px1) * bt;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            G[i][0] = (G[i][0] - kr[i] * du0) * ar[i];
-            G[i][1] = (G[i][1] - kr[i] * du1) * ar[i];
-        }
-    }
-    float *dst = seg_out + ((int64_t)su * H + h) * BD * ncols;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<f32x2 *>(dst + (int64_t)(rg + 16 * i) * ncols + c0) = G[i];
+struct Cfg {
+    static constexpr int LDI = BD + 16 / (int)sizeof(T);   // q, k rows (input type)
+    static constexpr uint32_t offK = 0;
+    static constexpr uint32_t offQ = offK + sizeof(T) * C * LDI;
+    static constexpr uint32_t offGm = (offQ + sizeof(T) * C * LDI + 15) / 16 * 16;
+    static constexpr uint32_t offDO = offGm + sizeof(double) * C * LDG;
+    static constexpr uint32_t offW = offDO + sizeof(float) * C * LDF;     // W, later dGamma
+    static constexpr uint32_t offDX = offW + sizeof(float) * C * LDF;
+    static constexpr uint32_t offA = offDX + sizeof(float) * C * LDF;
+    static constexpr uint32_t offP = offA + sizeof(float) * C * LDX;      // P, later dP
+    static constexpr uint32_t offPT = offP + sizeof(float) * C * LDX;     // P^T, later dP^T
+    static constexpr uint32_t offT = offPT + sizeof(float) * C * LDX;     // T, later dA
+    static constexpr uint32_t offTT = offT + sizeof(float) * C * LDX;     // T^T, later dA^T
+    static constexpr uint32_t offBeta = offTT + sizeof(float) * C * LDX;
+    static constexpr uint32_t offDb = offBeta + sizeof(float) * C;        // [8][C] partial dbeta
+    static constexpr uint32_t bytes = offDb + sizeof(float) * 8 * C;
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+};
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ f32x4 ld4(const T *p);
+template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+template <> __device__ __forceinline__ f32x4 ld4<bf16_t>(const bf16_t *p) {
+    const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])};
 }
-
-// Work items (segment su, head h, column block blk) in the order
-// item = (su H + h) NBLK + blk, walked with a stride of the grid (the scratch
-// area belongs to the workgroup, not the item).  seg_dsend: [num_segs][H][BD][BD],
-// the gradient entering each segment at its end.  part_vec: [NBLK][3][T_tot * H][BD]
-// partial row sums (dq, dk, dg); part_beta: [NBLK][T_tot * H]; scratch:
-// [gridDim.x][BWD_C / BWD_G + 1][BD][BWD_BV] floats; snaps: [chunks][H][BD][BD], the
-// state at the start of global chunk chunk_off[n] + c for c >= 1 (c = 0 is the
-// initial state).
-//
-// Each wave runs its 8 columns on its own, in the wave-level layout above.  Per
-// chunk: a forward walk from the chunk's start state keeps u of every token (in
-// LDS) and the state before every 4th token (in the scratch area, each lane's own
-// values); then the chunk is walked backwards in groups of 4 tokens, whose 4
-// states are rebuilt in registers from the group's stored state and the kept u
-// (S = Diag(alpha) S + beta k u^T, no reduction).  A token's row sums (dq, dk, dg
-// over the wave's columns) are reduced across the wave's four DPP rows so that
-// each lane keeps 6 of the 3 x 128; after each group the four waves' sums meet in
-// LDS and the workgroup adds them in wave order and writes its partials.
-constexpr int BWD_G = 4;                  // tokens per reverse group (and per partial-sum batch)
-constexpr int BWD_RED = 3 * BD;           // row sums per token and wave
-
-__device__ __forceinline__ float perm32_sum(float a, float b) {   // lanes 0-31: a over lanes L, L+32; 32-63: b
-    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+// e^(a_e - b_e) for four consecutive fp64 entries, the differences in fp64
+__device__ __forceinline__ f32x4 exp_diff4(const double *a, const double *b) {
+    const f64x2 a0 = *reinterpret_cast<const f64x2 *>(a), a1 = *reinterpret_cast<const f64x2 *>(a + 2);
+    const f64x2 b0 = *reinterpret_cast<const f64x2 *>(b), b1 = *reinterpret_cast<const f64x2 *>(b + 2);
+    return f32x4{__expf((float)(a0[0] - b0[0])), __expf((float)(a0[1] - b0[1])), __expf((float)(a1[0] - b1[0])),
+                 __expf((float)(a1[1] - b1[1]))};
 }
-__device__ __forceinline__ float perm16_sum(float a, float b) {   // even DPP rows: a over rows 2m, 2m+1; odd: b
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+__device__ __forceinline__ f32x4 exp4(const double *a) {
+    const f64x2 a0 = *reinterpret_cast<const f64x2 *>(a), a1 = *reinterpret_cast<const f64x2 *>(a + 2);
+    return f32x4{__expf((float)a0[0]), __expf((float)a0[1]), __expf((float)a1[0]), __expf((float)a1[1])};
 }
+}  // namespace bc
 
 template <typename T>
-__global__ __launch_bounds__(BWD_THREADS) void kda_backward_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, const float *initial_state,
+__global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, const T *__restrict__ dout, const float *initial_state,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, const float *__restrict__ snaps,
-    const T *__restrict__ dout, const int32_t *__restrict__ plan, int32_t num_segs,
-    const float *__restrict__ seg_dsend, int32_t H, int32_t T_tot,
-    float *__restrict__ scratch, float *__restrict__ part_vec, float *__restrict__ part_beta,
-    float *__restrict__ dv_out, float *dinit)
+    const float *__restrict__ gchunk, int32_t N, int32_t T_tot, int32_t H, float *__restrict__ dq,
+    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta)
 {
-    typedef typename Pair<T>::type Raw2;
-    constexpr int NWV = BWD_THREADS / 64;
-    __shared__ __align__(16) float tv[NWV][BWD_G][3][BD];       // per wave: k, alpha, q of a group's tokens
-    __shared__ __align__(16) float su[NWV][BWD_C][8];            // per wave: u of the chunk's tokens
-    __shared__ __align__(16) float red[NWV][BWD_G * BWD_RED];   // per wave: row sums of a group
-    __shared__ float redb[NWV][BWD_G];                           // per wave: dbeta of a group
+    using namespace bc;
+    typedef Cfg<T> Q;
+    typedef Mma<float> Mf;
+    constexpr int LDI = Q::LDI;
+    extern __shared__ __align__(16) unsigned char smem[];
+    T *sK = reinterpret_cast<T *>(smem + Q::offK);
+    T *sQ = reinterpret_cast<T *>(smem + Q::offQ);
+    double *sGm = reinterpret_cast<double *>(smem + Q::offGm);
+    float *sDO = reinterpret_cast<float *>(smem + Q::offDO);
+    float *sW = reinterpret_cast<float *>(smem + Q::offW);
+    float *sDX = reinterpret_cast<float *>(smem + Q::offDX);
+    float *sA = reinterpret_cast<float *>(smem + Q::offA);
+    float *sP = reinterpret_cast<float *>(smem + Q::offP);
+    float *sPT = reinterpret_cast<float *>(smem + Q::offPT);
+    float *sT = reinterpret_cast<float *>(smem + Q::offT);
+    float *sTT = reinterpret_cast<float *>(smem + Q::offTT);
+    float *sBeta = reinterpret_cast<float *>(smem + Q::offBeta);
+    float *sDb = reinterpret_cast<float *>(smem + Q::offDb);
+    float *sdP = sP, *sdPT = sPT, *sdA = sT, *sdAT = sTT, *sDG = sW;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int rg = lane & 15, cg = lane >> 4;
-    const int64_t rows_all = (int64_t)T_tot * H;
-    // scratch: [checkpoint][wave][4][lane] f32x4, rows rg + 16 i of the lane's two columns
-    f32x4 *scr = reinterpret_cast<f32x4 *>(scratch + (int64_t)blockIdx.x * (BWD_C / BWD_G + 1) * BD * BWD_BV) +
-                 wave * 4 * 64 + lane;
-    constexpr int CK = NWV * 4 * 64;                             // f32x4 per checkpoint
-    const int64_t items = (int64_t)num_segs * H * BWD_NBLK;
-    float *rw = red[wave];
+    // ---- workgroup -> (chunk, head); the chunk's sequence by binary search
+    const int64_t gc = blockIdx.x / H;
+    const int h = (int)(blockIdx.x % H);
+    if (N <= 0 || gc >= chunk_off[N]) return;
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= gc) lo = mid;
+        else hi = mid - 1;
+    }
+    const int n = lo;
+    const int t0 = min(max(cu[n], 0), T_tot), t1 = min(max(cu[n + 1], t0), T_tot);
+    const int64_t cs = gc - chunk_off[n];                 // chunk index within the sequence
+    const int64_t c0l = t0 + cs * C;
+    if (c0l >= t1) return;                                // only when cu_seqlens is not non-decreasing
+    const int c0 = (int)c0l, L = min(C, t1 - c0);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
+    const int64_t rowQ = (int64_t)H * BD;
+    const int64_t hoff = (int64_t)h * BD;
+    const float *Sg = cs ? snaps + (gc * H + h) * BD * BD
+                         : (initial_state ? initial_state + ((int64_t)n * H + h) * BD * BD : nullptr);
+    const float *Gg = gchunk + (gc * H + h) * BD * BD;
 
-    // a token's channel vectors (channels 2 lane, 2 lane + 1) to the wave's LDS
-    // slot, read back as this lane's rows rg + 16 i (written and read by this
-    // wave only, in order)
-    auto put = [&](float *dst, float x0, float x1) {
-        dst[chan_pos(2 * lane)] = x0;
-        dst[chan_pos(2 * lane + 1)] = x1;
-    };
-    auto get = [&](const float *src, float r[8]) {
-        *reinterpret_cast<f32x4 *>(r) = *reinterpret_cast<const f32x4 *>(src + 8 * rg);
-        *reinterpret_cast<f32x4 *>(r + 4) = *reinterpret_cast<const f32x4 *>(src + 8 * rg + 4);
-    };
-
-  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-    const int blk = (int)(item % BWD_NBLK);
-    const int64_t unit = item / BWD_NBLK;                 // (segment, head)
-    const int sg = (int)(unit / H), h = (int)(unit % H);
-    const int n = plan[4 * sg];
-    if (n < 0) continue;                                  // unused plan entry (uniform per workgroup)
-    const int flags = plan[4 * sg + 3];
-    const int cb = blk * BWD_BV + 8 * wave + 2 * cg;      // this lane's value columns cb, cb + 1
-    const int t0 = min(max(cu[n], 0), T_tot);             // the sequence
-    const int ts = min(max(plan[4 * sg + 1], t0), T_tot); // the segment: [ts, te), chunk-aligned in the sequence
-    const int te = min(max(plan[4 * sg + 2], ts), T_tot);
-    const int nch = (te - ts + BWD_C - 1) / BWD_C;
-    const int64_t sbase = ((int64_t)n * H + h) * BD * BD;   // this (sequence, head) in [N, H, BD, BD]
-    const float *gin = seg_dsend + unit * BD * BD;
-
-    f32x2 dS[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dS[i] = *reinterpret_cast<const f32x2 *>(gin + (int64_t)(rg + 16 * i) * BD + cb);
-
-    for (int c = nch - 1; c >= 0; --c) {
-        const int c0 = ts + c * BWD_C, Lc = min(BWD_C, te - c0);
-        const int cs = (c0 - t0) / BWD_C;                 // chunk index within the sequence
-        const float *src = cs ? snaps + ((int64_t)(chunk_off[n] + cs) * H + h) * BD * BD
-                              : (initial_state ? initial_state + sbase : nullptr);
-        f32x2 S[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            S[i] = src ? *reinterpret_cast<const f32x2 *>(src + (int64_t)(rg + 16 * i) * BD + cb) : f32x2{0.f, 0.f};
-
-        // ---- forward over the chunk in groups of BWD_G tokens: u of every
-        // token; the state before every group to the scratch area.  A group's
-        // token vectors are loaded while the group before it runs, ahead of
-        // that group's state store: vector memory operations complete in
-        // order, so a load issued after a store could not be waited for
-        // without waiting for the store.  Every step is branch-free (tokens
-        // past the chunk's end are neutral: decay 1, write strength 0), so the
-        // compiler counts the operations in flight exactly.
-        // Two register sets in turn (groups taken in pairs, the group count
-        // padded to even with neutral groups): a set loaded during one group
-        // and read in the next would otherwise be copied at the loop's end,
-        // and the copy waits for the load.
-        struct FwdSet { Raw2 k[BWD_G], v[BWD_G]; f32x2 g[BWD_G]; float b[BWD_G]; };
-        FwdSet fa, fb_;
-        auto fetch_fwd = [&](int m, FwdSet &f) {
-#pragma unroll
-            for (int jj = 0; jj < BWD_G; ++jj) {
-                const int64_t row = (int64_t)(c0 + min(m * BWD_G + jj, Lc - 1)) * H + h;
-                f.k[jj] = *reinterpret_cast<const Raw2 *>(k + row * BD + 2 * lane);
-                f.g[jj] = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
-                f.v[jj] = *reinterpret_cast<const Raw2 *>(v + row * BD + cb);
-                f.b[jj] = beta[row];
-            }
-            asm volatile("" ::: "memory");   // keep the loads here
-        };
-        auto store_state = [&](int m) {   // the state before token m * BWD_G (slot m; slot BWD_C / BWD_G is spare)
-            f32x4 *sj = scr + m * CK;
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                sj[p * 64] = f32x4{S[2 * p][0], S[2 * p][1], S[2 * p + 1][0], S[2 * p + 1][1]};
-        };
-        auto fwd_group = [&](int m, const FwdSet &f) {
-#pragma unroll
-            for (int jj = 0; jj < BWD_G; ++jj) {
-                const int j = m * BWD_G + jj;
-                const bool ok = j < Lc;
-                float *w = tv[wave][0][0];
-                put(w, to_f(f.k[jj][0]), to_f(f.k[jj][1]));
-                put(w + BD, ok ? __expf(f.g[jj][0]) : 1.f, ok ? __expf(f.g[jj][1]) : 1.f);
-                __builtin_amdgcn_wave_barrier();
-                float kr[8], ar[8];
-                get(w, kr);
-                get(w + BD, ar);
-                __builtin_amdgcn_wave_barrier();
-                float pa0 = 0.f, pa1 = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    S[i] *= ar[i];
-                    pa0 += S[i][0] * kr[i];
-                    pa1 += S[i][1] * kr[i];
-                }
-                const float u0 = to_f(f.v[jj][0]) - sum16(pa0), u1 = to_f(f.v[jj][1]) - sum16(pa1);
-                if (rg == 0) *reinterpret_cast<f32x2 *>(&su[wave][j][2 * cg]) = f32x2{u0, u1};
-                const float bt = ok ? f.b[jj] : 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float bk = bt * kr[i];
-                    S[i][0] += bk * u0;
-                    S[i][1] += bk * u1;
-                }
-            }
-        };
-        const int ngf = (Lc + 2 * BWD_G - 1) / (2 * BWD_G) * 2;     // groups, padded to even (<= BWD_C / BWD_G)
-        fetch_fwd(0, fa);
-        store_state(0);
-        for (int m = 0; m < ngf; m += 2) {
-            fetch_fwd(m + 1, fb_);
-            fwd_group(m, fa);
-            store_state(m + 1);
-            fetch_fwd(min(m + 2, ngf - 1), fa);
-            fwd_group(m + 1, fb_);
-            store_state(m + 2);
+    // ---- 0. the chunk's q, k (input type), dO (fp32), beta and Gamma (fp64);
+    //         rows past the chunk's end are zero (Gamma stays constant)
+    {
+        constexpr int VE = 16 / (int)sizeof(T), VPR = BD / VE;
+        for (int e = tid; e < C * VPR; e += NT) {
+            const int r = e / VPR, cv = (e % VPR) * VE;
+            const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cv;
+            f32x4 kv = *reinterpret_cast<const f32x4 *>(k + off), qv = *reinterpret_cast<const f32x4 *>(q + off);
+            if (r >= L) kv = qv = zero4();
+            *reinterpret_cast<f32x4 *>(sK + r * LDI + cv) = kv;
+            *reinterpret_cast<f32x4 *>(sQ + r * LDI + cv) = qv;
         }
-        __builtin_amdgcn_wave_barrier();
-
-        // ---- backwards in groups of BWD_G tokens; a group's vectors and stored
-        // state are loaded while the group before it is processed
-        Raw2 gk[BWD_G], gq[BWD_G], gd[BWD_G];
-        f32x2 gg_[BWD_G];
-        float gb[BWD_G];
-        f32x4 ck[4];
-        auto fetch_group = [&](int m) {
+        for (int e = tid; e < C * (BD / 4); e += NT) {
+            const int r = e / (BD / 4), cv = (e % (BD / 4)) * 4;
+            f32x4 d = ld4(dout + (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cv);
+            if (r >= L) d = zero4();
+            *reinterpret_cast<f32x4 *>(sDO + r * LDF + cv) = d;
+        }
+        if (tid < C) sBeta[tid] = tid < L ? beta[(int64_t)(c0 + tid) * H + h] : 0.f;
+        if (tid < BD) {
+            float gv[C];
 #pragma unroll
-            for (int jj = 0; jj < BWD_G; ++jj) {
-                const int64_t row = (int64_t)(c0 + min(m * BWD_G + jj, Lc - 1)) * H + h;
-                gk[jj] = *reinterpret_cast<const Raw2 *>(k + row * BD + 2 * lane);
-                gg_[jj] = *reinterpret_cast<const f32x2 *>(g + row * BD + 2 * lane);
-                gq[jj] = *reinterpret_cast<const Raw2 *>(q + row * BD + 2 * lane);
-                gd[jj] = *reinterpret_cast<const Raw2 *>(dout + row * BD + cb);
-                gb[jj] = beta[row];
+            for (int r = 0; r < C; ++r) gv[r] = g[(int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + tid];
+            double s = 0.0;
+#pragma unroll
+            for (int r = 0; r < C; ++r) {
+                if (r < L) s += (double)gv[r];
+                sGm[r * LDG + tid] = s;
             }
-            const f32x4 *sj = scr + m * CK;                  // this lane's own stores: in order
-#pragma unroll
-            for (int p = 0; p < 4; ++p) ck[p] = sj[p * 64];
-        };
-        const int mtop = (Lc - 1) / BWD_G;
-        fetch_group(mtop);
-        for (int m = mtop; m >= 0; --m) {
-            const int jl = m * BWD_G, ng = min(BWD_G, Lc - jl);
-            f32x2 dd[BWD_G], Sp[BWD_G][8];
-            float bb[BWD_G];
-#pragma unroll
-            for (int jj = 0; jj < BWD_G; ++jj) {
-                float *w = tv[wave][jj][0];
-                put(w, to_f(gk[jj][0]), to_f(gk[jj][1]));
-                put(w + BD, __expf(gg_[jj][0]), __expf(gg_[jj][1]));
-                put(w + 2 * BD, to_f(gq[jj][0]), to_f(gq[jj][1]));
-                dd[jj] = f32x2{to_f(gd[jj][0]), to_f(gd[jj][1])};
-                bb[jj] = gb[jj];
-            }
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                Sp[0][2 * p] = f32x2{ck[p][0], ck[p][1]};
-                Sp[0][2 * p + 1] = f32x2{ck[p][2], ck[p][3]};
-            }
-            fetch_group(max(m - 1, 0));
-            __builtin_amdgcn_wave_barrier();
-            // the group's states before each token, from the stored one and the kept u
-#pragma unroll
-            for (int jj = 1; jj < BWD_G; ++jj) {
-                if (jj < ng) {
-                    float kr[8], ar[8];
-                    get(tv[wave][jj - 1][0], kr);
-                    get(tv[wave][jj - 1][1], ar);
-                    const f32x2 u2 = *reinterpret_cast<const f32x2 *>(&su[wave][jl + jj - 1][2 * cg]);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float bk = bb[jj - 1] * kr[i];
-                        Sp[jj][i][0] = Sp[jj - 1][i][0] * ar[i] + bk * u2[0];
-                        Sp[jj][i][1] = Sp[jj - 1][i][1] * ar[i] + bk * u2[1];
-                    }
-                }
-            }
-#pragma unroll
-            for (int jj = BWD_G - 1; jj >= 0; --jj) {
-                if (jj < ng) {
-                    const int j = jl + jj;
-                    const int64_t row = (int64_t)(c0 + j) * H + h;
-                    float kr[8], ar[8], qr[8];
-                    get(tv[wave][jj][0], kr);
-                    get(tv[wave][jj][1], ar);
-                    get(tv[wave][jj][2], qr);
-                    const f32x2 u2 = *reinterpret_cast<const f32x2 *>(&su[wave][j][2 * cg]);
-                    const f32x2 d2 = dd[jj];
-                    const float bt = bb[jj];
-                    float px0 = 0.f, px1 = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        dS[i][0] += qr[i] * d2[0];                   // o = S^T q
-                        dS[i][1] += qr[i] * d2[1];
-                        px0 += dS[i][0] * kr[i];                     // dS^T k
-                        px1 += dS[i][1] * kr[i];
-                    }
-                    const float x0 = sum16(px0), x1 = sum16(px1);
-                    const float du0 = bt * x0, du1 = bt * x1;
-                    if (rg == 0) *reinterpret_cast<f32x2 *>(dv_out + row * BD + cb) = f32x2{du0, du1};
-                    float V[24];                                      // [dq | dk | dg] rows rg + 16 i, this lane's columns
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float a = ar[i], kr_ = kr[i], bk = bt * kr_;
-                        const f32x2 sp = Sp[jj][i];
-                        const f32x2 sb = sp * a;
-                        const f32x2 sn = sb + bk * u2;
-                        V[i] = sn[0] * d2[0] + sn[1] * d2[1];
-                        V[8 + i] = bt * (dS[i][0] * u2[0] + dS[i][1] * u2[1]) - (sb[0] * du0 + sb[1] * du1);
-                        const f32x2 dsb = f32x2{dS[i][0] - kr_ * du0, dS[i][1] - kr_ * du1};
-                        V[16 + i] = a * (dsb[0] * sp[0] + dsb[1] * sp[1]);
-                        dS[i] = dsb * a;
-                    }
-                    // sums over the wave's four DPP rows, scattered: lane cg keeps V[6 cg + e]
-                    float W[12], X[6];
-#pragma unroll
-                    for (int e = 0; e < 12; ++e) W[e] = perm32_sum(V[e], V[e + 12]);
-#pragma unroll
-                    for (int e = 0; e < 6; ++e) X[e] = perm16_sum(W[e], W[e + 6]);
-#pragma unroll
-                    for (int e = 0; e < 6; ++e) {
-                        const int ee = 6 * cg + e;                    // quantity ee / 8, row rg + 16 (ee % 8)
-                        rw[jj * BWD_RED + (ee >> 3) * BD + rg + 16 * (ee & 7)] = X[e];
-                    }
-                    const float db = sum_rows4(x0 * u2[0] + x1 * u2[1]);
-                    if (lane == 0) redb[wave][jj] = db;
-                }
-            }
-            // the group's partial sums: the four waves added in order
-            __syncthreads();
-            for (int idx = threadIdx.x; idx < ng * BWD_RED; idx += BWD_THREADS) {
-                float s = red[0][idx];
-#pragma unroll
-                for (int wv = 1; wv < NWV; ++wv) s += red[wv][idx];
-                const int tok = idx / BWD_RED, rem = idx - tok * BWD_RED;
-                const int qn = rem / BD, r = rem - qn * BD;
-                const int64_t prow = (int64_t)(c0 + jl + tok) * H + h;
-                part_vec[(((int64_t)blk * 3 + qn) * rows_all + prow) * BD + r] = s;
-            }
-            if ((int)threadIdx.x < ng) {
-                float s = redb[0][threadIdx.x];
-#pragma unroll
-                for (int wv = 1; wv < NWV; ++wv) s += redb[wv][threadIdx.x];
-                part_beta[(int64_t)blk * rows_all + (int64_t)(c0 + jl + threadIdx.x) * H + h] = s;
-            }
-            __syncthreads();
         }
     }
+    __syncthreads();
 
-    if (dinit && (flags & SEG_FIRST)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<f32x2 *>(dinit + sbase + (int64_t)(rg + 16 * i) * BD + cb) = dS[i];
-    }
-  }
-}
-
-// Sum of the per-block partials in block order: dq, dk, dg [rows][BD], dbeta [rows].
-// Rows of tokens outside every sequence are written as zeros in the partials'
-// place only if a workgroup wrote them; the caller's rows are selected by row_ok.
-__global__ __launch_bounds__(256) void kda_backward_reduce_kernel(
-    const float *__restrict__ part_vec, const float *__restrict__ part_beta, const int32_t *__restrict__ cu,
-    int32_t N, int32_t H, int64_t rows_all, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dg, float *__restrict__ dbeta)
-{
-    const int64_t nvec = rows_all * (BD / 4);
-    const int32_t t_lo = min(max(cu[0], 0), (int32_t)(rows_all / H));
-    const int32_t t_hi = min(max(cu[N], t_lo), (int32_t)(rows_all / H));
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < nvec; e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = e / (BD / 4);
-        const int32_t tok = (int32_t)(row / H);
-        if (tok < t_lo || tok >= t_hi) continue;        // tokens outside the packed sequences
-        f32x4 a = zero4(), b = zero4(), c = zero4();
-#pragma unroll
-        for (int blk = 0; blk < BWD_NBLK; ++blk) {
-            const f32x4 *pv = reinterpret_cast<const f32x4 *>(part_vec + (int64_t)blk * 3 * rows_all * BD);
-            a += pv[e];
-            b += pv[nvec + e];
-            c += pv[2 * nvec + e];
+    // ---- 1. Gram tiles A (strictly lower), P (lower incl.): waves 0, 1 the
+    //         diagonal blocks (reference: the block's middle token), wave 2 the
+    //         off-diagonal block (reference: token 15); wave 3 zeroes the upper block
+    if (wave < 3) {
+        const int rb = wave == 0 ? 0 : 16, ib = wave == 1 ? 16 : 0, ref = wave == 0 ? 7 : (wave == 1 ? 23 : 15);
+        const int r = rb + lm, i = ib + lm;
+        f32x4 accA = zero4(), accP = zero4();
+#pragma unroll 2
+        for (int kb = 0; kb < BD / 16; ++kb) {
+            const int c = 16 * kb + 4 * lj;
+            const f32x4 rf = exp_diff4(sGm + r * LDG + c, sGm + ref * LDG + c);
+            const f32x4 cf = exp_diff4(sGm + ref * LDG + c, sGm + i * LDG + c);
+            const f32x4 b = ld4(sK + i * LDI + c) * cf;
+            accA = Mf::mma(ld4(sK + r * LDI + c) * rf, b, accA);
+            accP = Mf::mma(ld4(sQ + r * LDI + c) * rf, b, accP);
         }
-        reinterpret_cast<f32x4 *>(dq)[e] = a;
-        reinterpret_cast<f32x4 *>(dk)[e] = b;
-        reinterpret_cast<f32x4 *>(dg)[e] = c;
-        if ((e % (BD / 4)) == 0) {
+        const bool diag = wave < 2;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int rr = rb + 4 * lj + ii, cc = ib + lm;
+            // selects, not products: entries above the diagonal may be inf
+            const float a = (!diag || cc < rr) ? accA[ii] : 0.f;
+            const float p = (!diag || cc <= rr) ? accP[ii] : 0.f;
+            sA[rr * LDX + cc] = a;
+            sP[rr * LDX + cc] = p;
+            sPT[cc * LDX + rr] = p;
+        }
+    } else {
+        for (int e = lane; e < 256; e += 64) {
+            const int rr = e >> 4, cc = 16 + (e & 15);
+            sA[rr * LDX + cc] = 0.f;
+            sP[rr * LDX + cc] = 0.f;
+            sPT[cc * LDX + rr] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- 1b. T = (I + Diag(b) A)^-1: the diagonal 16x16 blocks by forward
+    //          substitution (waves 0, 1: lane lm computes column lm; the four
+    //          lane groups repeat it), then T10 = -T11 (Diag(b) A)_10 T00 (wave 0)
+    if (wave < 2) {
+        const int a0 = 16 * wave, j = lm;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
             float s = 0.f;
 #pragma unroll
-            for (int blk = 0; blk < BWD_NBLK; ++blk) s += part_beta[(int64_t)blk * rows_all + row];
-            dbeta[row] = s;
+            for (int i = 0; i < r; ++i) s += sA[(a0 + r) * LDX + a0 + i] * t[i];
+            t[r] = r == j ? 1.f : (r < j ? 0.f : -sBeta[a0 + r] * s);
+        }
+        if (lj == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                sT[(a0 + r) * LDX + a0 + j] = t[r];
+                sTT[(a0 + j) * LDX + a0 + r] = t[r];
+            }
+        }
+    } else {
+        for (int e = tid - 128; e < 256; e += 128) {
+            const int rr = e >> 4, cc = 16 + (e & 15);
+            sT[rr * LDX + cc] = 0.f;
+            sTT[cc * LDX + rr] = 0.f;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // X = (Diag(b) A)_10 T00: B[i][j] = T00[i][j] = TT[j][i]
+        const f32x4 an = ld4(sA + (16 + lm) * LDX + 4 * lj) * sBeta[16 + lm];
+        const f32x4 x = Mf::mma(an, ld4(sTT + lm * LDX + 4 * lj), zero4());
+        const f32x4 t10 = -Mf::mma(ld4(sT + (16 + lm) * LDX + 16 + 4 * lj), x, zero4());
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            sT[(16 + 4 * lj + ii) * LDX + lm] = t10[ii];
+            sTT[lm * LDX + 16 + 4 * lj + ii] = t10[ii];
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. value columns vc0, vc0 + 16 of this wave (tiles ct), token row tiles rt
+    const int vc0 = 32 * wave + lm;
+    f32x4 U[2][2], dW[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) U[rt][ct] = dW[rt][ct] = zero4();
+    const double *gmL = sGm + (L - 1) * LDG;
+#pragma unroll 2
+    for (int kb = 0; kb < BD / 16; ++kb) {
+        const int c = 16 * kb + 4 * lj;
+        f32x4 sb[2], gb[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sb[ct][e] = Sg ? Sg[(int64_t)(c + e) * BD + vc0 + 16 * ct] : 0.f;
+                gb[ct][e] = Gg[(int64_t)(c + e) * BD + vc0 + 16 * ct];
+            }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int r = 16 * rt + lm;
+            const f32x4 kr = ld4(sK + r * LDI + c);
+            const f32x4 kp = kr * exp4(sGm + r * LDG + c);                 // K+
+            const f32x4 kh = kr * exp_diff4(gmL + c, sGm + r * LDG + c);   // K^
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                U[rt][ct] = Mf::mma(kp, sb[ct], U[rt][ct]);
+                dW[rt][ct] = Mf::mma(kh, gb[ct], dW[rt][ct]);
+            }
+        }
+    }
+    f32x4 X[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rt + 4 * lj + i;
+                const float vv = to_f(v[(int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + vc0 + 16 * ct]);
+                U[rt][ct][i] = (r < L ? vv : 0.f) - U[rt][ct][i];
+                X[rt][ct][i] = sBeta[r] * U[rt][ct][i];
+            }
+    // W = T X;  dW += P^T dO;  dX = T^T dW   (T lower, P^T and T^T upper by blocks)
+    f32x4 W[2][2], dX[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) W[rt][ct] = zero4();
+#pragma unroll
+        for (int bt = 0; bt <= rt; ++bt) {
+            const f32x4 ta = ld4(sT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) W[rt][ct] = Mf::mma(ta, X[bt][ct], W[rt][ct]);
+        }
+#pragma unroll
+        for (int bt = rt; bt < 2; ++bt) {
+            const f32x4 pa = ld4(sPT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x4 db;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) db[e] = sDO[(16 * bt + 4 * lj + e) * LDF + vc0 + 16 * ct];
+                dW[rt][ct] = Mf::mma(pa, db, dW[rt][ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) dX[rt][ct] = zero4();
+#pragma unroll
+        for (int bt = rt; bt < 2; ++bt) {
+            const f32x4 ta = ld4(sTT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) dX[rt][ct] = Mf::mma(ta, dW[bt][ct], dX[rt][ct]);
+        }
+    }
+    // dv, the U.dX part of dbeta (this wave's columns), W and dX to LDS
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * rt + 4 * lj + i;
+            float pb = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                const int col = vc0 + 16 * ct;
+                if (r < L) dv[(int64_t)(c0 + r) * rowQ + hoff + col] = sBeta[r] * dX[rt][ct][i];
+                pb += U[rt][ct][i] * dX[rt][ct][i];
+                sW[r * LDF + col] = W[rt][ct][i];
+                sDX[r * LDF + col] = dX[rt][ct][i];
+            }
+            pb = sum16(pb);
+            if (lm == 0) sDb[wave * C + r] = pb;
+        }
+    __syncthreads();
+
+    // ---- 3. contractions over the value columns: key channels cc of this
+    //         wave (tiles ct), S and G rows read from global memory
+    f32x4 dQp[2][2], dXS[2][2], dKh[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) dQp[rt][ct] = dXS[rt][ct] = dKh[rt][ct] = zero4();
+    float dgm[2] = {0.f, 0.f};
+#pragma unroll 2
+    for (int kb = 0; kb < BD / 16; ++kb) {
+        const int j = 16 * kb + 4 * lj;
+        f32x4 st[2], gt[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            const int cc = 32 * wave + 16 * ct + lm;
+            st[ct] = Sg ? *reinterpret_cast<const f32x4 *>(Sg + (int64_t)cc * BD + j) : zero4();
+            gt[ct] = *reinterpret_cast<const f32x4 *>(Gg + (int64_t)cc * BD + j);
+            dgm[ct] += dot4(st[ct], gt[ct]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int r = 16 * rt + lm;
+            const f32x4 ado = ld4(sDO + r * LDF + j), adx = ld4(sDX + r * LDF + j), aw = ld4(sW + r * LDF + j);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                dQp[rt][ct] = Mf::mma(ado, st[ct], dQp[rt][ct]);
+                dXS[rt][ct] = Mf::mma(adx, st[ct], dXS[rt][ct]);
+                dKh[rt][ct] = Mf::mma(aw, gt[ct], dKh[rt][ct]);
+            }
+        }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) dgm[ct] = sum_rows4(dgm[ct]);   // (G (.) S) 1 of channel cc
+    // dP and dN: waves 0, 1 the diagonal blocks, wave 2 the off-diagonal one
+    // (they overwrite P, P^T, T, T^T, whose last reads were in part 2)
+    if (wave < 3) {
+        const int rb = wave == 0 ? 0 : 16, ib = wave == 1 ? 16 : 0;
+        const bool diag = wave < 2;
+        f32x4 accP = zero4(), accN = zero4();
+#pragma unroll 2
+        for (int kb = 0; kb < BD / 16; ++kb) {
+            const int j = 16 * kb + 4 * lj;
+            const f32x4 bw = ld4(sW + (ib + lm) * LDF + j);
+            accP = Mf::mma(ld4(sDO + (rb + lm) * LDF + j), bw, accP);
+            accN = Mf::mma(ld4(sDX + (rb + lm) * LDF + j), bw, accN);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int rr = rb + 4 * lj + ii, cc = ib + lm;
+            const float dp = (!diag || cc <= rr) ? accP[ii] : 0.f;
+            const float dn = (!diag || cc < rr) ? -accN[ii] : 0.f;
+            const float da = sBeta[rr] * dn;
+            sdP[rr * LDX + cc] = dp;
+            sdPT[cc * LDX + rr] = dp;
+            sdA[rr * LDX + cc] = da;
+            sdAT[cc * LDX + rr] = da;
+            const float pb = sum16(dn * sA[rr * LDX + cc]);
+            if (lm == 0) sDb[(4 + wave) * C + rr] = pb;
+        }
+    } else {
+        for (int e = lane; e < 256; e += 64) {
+            const int rr = e >> 4, cc = 16 + (e & 15);
+            sdP[rr * LDX + cc] = 0.f;
+            sdPT[cc * LDX + rr] = 0.f;
+            sdA[rr * LDX + cc] = 0.f;
+            sdAT[cc * LDX + rr] = 0.f;
+        }
+        if (lane < 16) {      // rows that a block's dbeta part does not cover
+            sDb[4 * C + 16 + lane] = 0.f;
+            sDb[5 * C + lane] = 0.f;
+            sDb[6 * C + lane] = 0.f;
+            sDb[7 * C + lane] = 0.f;
+            sDb[7 * C + 16 + lane] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- 4. token sums weighted by E, and the per-element results
+#pragma unroll 1
+    for (int ct = 0; ct < 2; ++ct) {
+        const int c = 32 * wave + 16 * ct + lm;
+        auto gm = [&](int t) { return sGm[t * LDG + c]; };
+        auto kv = [&](int t) { return to_f(sK[t * LDI + c]); };
+        auto qv = [&](int t) { return to_f(sQ[t * LDI + c]); };
+        // B operands over tokens: lane group lj takes tokens tb + 4 lj + e
+        f32x4 Kcd[2], Krd[2], Qrd[2], Kco, Kro, Qro;
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const double gmid = gm(16 * a + 7);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * a + 4 * lj + e;
+                const float d = (float)(gm(t) - gmid);
+                const float rf = __expf(d);
+                Kcd[a][e] = kv(t) * __expf(-d);
+                Krd[a][e] = kv(t) * rf;
+                Qrd[a][e] = qv(t) * rf;
+            }
+        }
+        const double g15 = gm(15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t0_ = 4 * lj + e, t1_ = 16 + 4 * lj + e;
+            Kco[e] = kv(t0_) * __expf((float)(g15 - gm(t0_)));
+            const float ro = __expf((float)(gm(t1_) - g15));
+            Kro[e] = kv(t1_) * ro;
+            Qro[e] = qv(t1_) * ro;
+        }
+        f32x4 q2d[2], kr2d[2], kc2d[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const int ro = (16 * a + lm) * LDX + 16 * a + 4 * lj;
+            q2d[a] = Mf::mma(ld4(sdP + ro), Kcd[a], zero4());
+            kr2d[a] = Mf::mma(ld4(sdA + ro), Kcd[a], zero4());
+            kc2d[a] = Mf::mma(ld4(sdAT + ro), Krd[a], Mf::mma(ld4(sdPT + ro), Qrd[a], zero4()));
+        }
+        const f32x4 q2o = Mf::mma(ld4(sdP + (16 + lm) * LDX + 4 * lj), Kco, zero4());
+        const f32x4 kr2o = Mf::mma(ld4(sdA + (16 + lm) * LDX + 4 * lj), Kco, zero4());
+        const f32x4 kc2o = Mf::mma(ld4(sdAT + lm * LDX + 16 + 4 * lj), Kro,
+                                   Mf::mma(ld4(sdPT + lm * LDX + 16 + 4 * lj), Qro, zero4()));
+        // the last token's extra terms: sum_r k dK^ e^(Gamma_L - Gamma) and (G (.) S) 1 e^Gamma_L
+        const double gl = gm(L - 1);
+        float extra = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * rt + 4 * lj + ii;
+                extra += kv(r) * dKh[rt][ct][ii] * __expf((float)(gl - gm(r)));
+            }
+        extra = sum_rows4(extra) + dgm[ct] * __expf((float)gl);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int r = 16 * rt + 4 * lj + ii;
+                const double gr = gm(r), gmid = gm(16 * rt + 7);
+                const float dmid = (float)(gr - gmid);
+                float dq2 = __expf(dmid) * q2d[rt][ii], dkr2 = __expf(dmid) * kr2d[rt][ii];
+                float dkc2 = __expf(-dmid) * kc2d[rt][ii];
+                if (rt == 1) {
+                    const float ro = __expf((float)(gr - g15));
+                    dq2 += ro * q2o[ii];
+                    dkr2 += ro * kr2o[ii];
+                } else {
+                    dkc2 += __expf((float)(g15 - gr)) * kc2o[ii];
+                }
+                const float eG = __expf((float)gr), eGn = __expf((float)(gl - gr));
+                const float dq_ = dQp[rt][ct][ii] * eG + dq2;
+                const float dkrow = -sBeta[r] * dXS[rt][ct][ii] * eG + dkr2;
+                const float dkcol = dKh[rt][ct][ii] * eGn + dkc2;
+                const float kr = kv(r);
+                float dG = qv(r) * dq_ + kr * dkrow - kr * dkcol;
+                if (r == L - 1) dG += extra;
+                if (r < L) {
+                    dq[(int64_t)(c0 + r) * rowQ + hoff + c] = dq_;
+                    dk[(int64_t)(c0 + r) * rowQ + hoff + c] = dkrow + dkcol;
+                }
+                sDG[r * LDF + c] = dG;
+            }
+    }
+    __syncthreads();
+
+    // ---- 5. dg = reverse cumulative sum of dGamma; dbeta from its parts
+    if (tid < BD) {
+        float acc = 0.f;
+        for (int r = L - 1; r >= 0; --r) {
+            acc += sDG[r * LDF + tid];
+            dg[(int64_t)(c0 + r) * rowQ + hoff + tid] = acc;
+        }
+    } else if (tid < BD + C) {
+        const int r = tid - BD;
+        if (r < L) {
+            float s = 0.f;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) s += sDb[w * C + r];
+            dbeta[(int64_t)(c0 + r) * H + h] = s;
         }
     }
 }
 
 }  // namespace kda
 
-// Scratch floats per workgroup of the main pass, and the most workgroups it
-// launches (the item loop covers the rest): 512 x 144 KB of scratch at most.
-extern "C" size_t kda_backward_scratch_floats_per_wg() { return (size_t)(kda::BWD_C / kda::BWD_G + 1) * kda::BD * kda::BWD_BV; }
-extern "C" int32_t kda_backward_max_wgs() { return 512; }
-extern "C" int32_t kda_backward_num_blocks() { return kda::BWD_NBLK; }
-
-extern "C" hipError_t kda_launch_backward_summary(int bf16, const void *q, const void *k, const float *g,
-                                                  const float *beta, const void *dout, const int32_t *plan,
-                                                  int32_t num_segs, int32_t T_tot, int32_t H, int32_t ncols,
-                                                  float *seg_out, hipStream_t stream)
+// Per (chunk, head) gradients of the chunk form (kda_bwd_chunk_kernel): S at
+// every chunk start in snaps (a sequence's first chunk: initial_state, or zero
+// if nullptr), the gradient at every chunk end in gchunk, both [chunks][H][BD][BD].
+extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const void *v, const float *g,
+                                           const float *beta, const void *dout, const float *init, const int32_t *cu,
+                                           const int32_t *chunk_off, int64_t max_chunks, const float *snaps,
+                                           const float *gchunk, int32_t N, int32_t T_tot, int32_t H, float *dq,
+                                           float *dk, float *dv, float *dg, float *dbeta, hipStream_t stream)
 {
     using namespace kda;
-    if (ncols != BD && ncols != 2 * BD) return hipErrorInvalidValue;
-    const int64_t grid = (int64_t)num_segs * H * (ncols / BWD_BV);
-    if (grid <= 0) return hipSuccess;
+    const int64_t grid = max_chunks * H;
+    if (grid <= 0 || N <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (bf16)
-        hipLaunchKernelGGL(kda_backward_summary_kernel<bf16_t>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), g, beta,
-                           static_cast<const bf16_t *>(dout), plan, num_segs, H, T_tot, ncols, seg_out);
-    else
-        hipLaunchKernelGGL(kda_backward_summary_kernel<float>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
-                           static_cast<const float *>(q), static_cast<const float *>(k), g, beta,
-                           static_cast<const float *>(dout), plan, num_segs, H, T_tot, ncols, seg_out);
-    return hipGetLastError();
-}
-
-extern "C" hipError_t kda_launch_backward(int bf16, const void *q, const void *k, const void *v, const float *g,
-                                          const float *beta, const float *init, const int32_t *cu,
-                                          const int32_t *chunk_off, const float *snaps, const void *dout,
-                                          const int32_t *plan, int32_t num_segs, const float *seg_dsend,
-                                          int32_t N, int32_t T_tot, int32_t H, float *scratch,
-                                          float *part_vec, float *part_beta, float *dq, float *dk, float *dv,
-                                          float *dg, float *dbeta, float *dinit, hipStream_t stream)
-{
-    using namespace kda;
-    const int64_t items = (int64_t)num_segs * H * BWD_NBLK;
-    if (items <= 0) return hipSuccess;
-    const int64_t grid = min(items, (int64_t)kda_backward_max_wgs());
-    if (bf16)
-        hipLaunchKernelGGL(kda_backward_kernel<bf16_t>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
+    if (bf16) {
+        auto kern = kda_bwd_chunk_kernel<bf16_t>;
+        static std::atomic<uint64_t> lds_set{0};
+        if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bc::Cfg<bf16_t>::bytes, lds_set))
+            return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(bc::NT), bc::Cfg<bf16_t>::bytes, stream,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
-                           static_cast<const bf16_t *>(v), g, beta, init, cu, chunk_off, snaps,
-                           static_cast<const bf16_t *>(dout), plan, num_segs, seg_dsend, H, T_tot, scratch,
-                           part_vec, part_beta, dv, dinit);
-    else
-        hipLaunchKernelGGL(kda_backward_kernel<float>, dim3((unsigned)grid), dim3(BWD_THREADS), 0, stream,
+                           static_cast<const bf16_t *>(v), g, beta, static_cast<const bf16_t *>(dout), init, cu,
+                           chunk_off, snaps, gchunk, N, T_tot, H, dq, dk, dv, dg, dbeta);
+    } else {
+        auto kern = kda_bwd_chunk_kernel<float>;
+        static std::atomic<uint64_t> lds_set{0};
+        if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bc::Cfg<float>::bytes, lds_set))
+            return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(bc::NT), bc::Cfg<float>::bytes, stream,
                            static_cast<const float *>(q), static_cast<const float *>(k),
-                           static_cast<const float *>(v), g, beta, init, cu, chunk_off, snaps,
-                           static_cast<const float *>(dout), plan, num_segs, seg_dsend, H, T_tot, scratch,
-                           part_vec, part_beta, dv, dinit);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t rows_all = (int64_t)T_tot * H;
-    const int64_t nvec = rows_all * (BD / 4);
-    if (nvec == 0) return hipSuccess;
-    const int64_t blocks = min((nvec + 255) / 256, (int64_t)65536);
-    hipLaunchKernelGGL(kda_backward_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part_vec, part_beta,
-                       cu, N, H, rows_all, dq, dk, dg, dbeta);
+                           static_cast<const float *>(v), g, beta, static_cast<const float *>(dout), init, cu,
+                           chunk_off, snaps, gchunk, N, T_tot, H, dq, dk, dv, dg, dbeta);
+    }
     return hipGetLastError();
 }

@@ -169,6 +169,7 @@ struct SegArgs {
     int32_t init_unit, init_units;
     int32_t prep_group;         // chunk-operand pass: consecutive chunks per workgroup (1 .. PREP_GROUP)
     int32_t img_slots;          // chunk-operand pass: image slots per head (> chunks of valid input)
+    f32x4 *gimg;                // MODE_PREPG: gradient images, slots as for img
 };
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
@@ -181,7 +182,9 @@ __device__ __forceinline__ int64_t seg_init_entry(const SegArgs &seg, int su, in
     return min(max(e, (int64_t)0), (int64_t)seg.init_units - 1);
 }
 
-enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2 };   // MODE_SNAP: fused + state snapshots
+enum { MODE_FUSED = 0, MODE_PREP = 1, MODE_SNAP = 2, MODE_PREPG = 3 };
+// MODE_SNAP: fused + state snapshots; MODE_PREPG: the chunk-operand pass that
+// also writes the gradient image of every (chunk, head)
 constexpr int PREP_GROUP = 8;    // most consecutive chunks per workgroup of the chunk-operand pass
 
 // Chunk-operand image: everything the state chain of one (chunk, head) reads
@@ -223,6 +226,106 @@ struct ChunkImage {
         v -= vTs;
         if (v < vQp) return o.qp + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
         return o.p + (((v - vQp) / RC) * P::LDC + ((v - vQp) % RC) * EPV) * E;
+    }
+};
+
+// Gradient image: the chunk operands of the state-gradient chain, which runs
+// the transposed map (see grad_chunk) -- every matrix of the chunk image in
+// the other orientation: GS K^ [C][DK], -GS K+^T [DK][C], GS Q+^T [DK][C],
+// P^T [C][C] and the (I + N)^-1 blocks transposed [C][C] with their scales
+// transposed, then the chunk decay and beta.  Written by the chunk-operand
+// pass (MODE_PREPG) from the same LDS tiles as the chunk image, so both hold
+// the same rounded values.  Same vector count as the chunk image.
+template <typename TIn, int C>
+struct GradImage {
+    typedef PrefillCfg<TIn, C, 4> P;
+    typedef typename P::OpT OpT;
+    static constexpr int EPV = 16 / (int)sizeof(OpT);
+    static constexpr int NSUB = C / SUB;
+    static constexpr int vKh = C * DK / EPV, vNKpT = DK * C / EPV, vQpT = DK * C / EPV;
+    static constexpr int vPT = C * C / EPV, vTT = C * C / EPV;
+    static constexpr int vGam = DK / 4, vBeta = C / 4, vTs = (NSUB * NSUB + 3) / 4;
+    static constexpr int NVEC = vKh + vNKpT + vQpT + vPT + vTT + vGam + vBeta + vTs;
+    static_assert(NVEC == ChunkImage<TIn, C>::NVEC, "one slot size for both images");
+    struct Offs { uint32_t kh, nkpt, qpt, pt, tt, gam, beta, ts; };
+    __device__ static __forceinline__ uint32_t lds_off(int v, const Offs &o) {
+        constexpr int RK = DK / EPV, RC = C / EPV;
+        constexpr uint32_t E = sizeof(OpT);
+        if (v < vKh) return o.kh + ((v / RK) * P::LDK + (v % RK) * EPV) * E;
+        v -= vKh;
+        if (v < vNKpT) return o.nkpt + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vNKpT;
+        if (v < vQpT) return o.qpt + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vQpT;
+        if (v < vPT) return o.pt + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vPT;
+        if (v < vTT) return o.tt + ((v / RC) * P::LDC + (v % RC) * EPV) * E;
+        v -= vTT;
+        if (v < vGam) return o.gam + 16 * v;
+        v -= vGam;
+        if (v < vBeta) return o.beta + 16 * v;
+        return o.ts + 16 * (v - vBeta);
+    }
+    // contraction index stored at position p of a row (inverse of kperm)
+    __device__ static __forceinline__ int kinv(int p) {
+        if (sizeof(OpT) == 4) return p;
+        return (p & ~31) | (((p >> 2) & 1) << 4) | (((p >> 3) & 3) << 2) | (p & 3);
+    }
+    // Vector v of the image, gathered from the chunk-operand tiles in LDS
+    // (sNKp = -GS K+ and sQp = GS Q+ [C][LDK], sKhT = GS K^T [DK][LDC], sT and
+    // sP [C][LDC], as the chunk-operand pass leaves them).
+    __device__ static __forceinline__ f32x4 gather(int v, const OpT *sNKp, const OpT *sQp, const OpT *sKhT,
+                                                   const OpT *sT, const OpT *sP, const float *sGam,
+                                                   const float *sBeta, const float *sTs) {
+        constexpr int RK = DK / EPV, RC = C / EPV;
+        union { f32x4 f; OpT h[EPV]; } u;
+        u.f = zero4();
+        if (v < vKh) {                                     // row r (token), channels along the row
+            const int r = v / RK, p0 = (v % RK) * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) u.h[e] = sKhT[kinv(p0 + e) * P::LDC + kperm<OpT>(r)];
+            return u.f;
+        }
+        v -= vKh;
+        if (v < vNKpT + vQpT) {                            // row c (channel), tokens along the row
+            const OpT *src = v < vNKpT ? sNKp : sQp;
+            if (v >= vNKpT) v -= vNKpT;
+            const int c = v / RC, p0 = (v % RC) * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) u.h[e] = src[kinv(p0 + e) * P::LDK + kperm<OpT>(c)];
+            return u.f;
+        }
+        v -= vNKpT + vQpT;
+        if (v < vPT) {                                     // P^T[i][r] = P[r][i], r >= i
+            const int i = v / RC, p0 = (v % RC) * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int r = kinv(p0 + e);
+                u.h[e] = r >= i ? sP[r * P::LDC + kperm<OpT>(i)] : from_f<OpT>(0.f);
+            }
+            return u.f;
+        }
+        v -= vPT;
+        if (v < vTT) {                                     // T^T[i][r] = T[r][i], r >= i (plain order)
+            const int i = v / RC, p0 = (v % RC) * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                const int r = p0 + e;
+                u.h[e] = r >= i ? sT[r * P::LDC + i] : from_f<OpT>(0.f);
+            }
+            return u.f;
+        }
+        v -= vTT;
+        if (v < vGam) return *reinterpret_cast<const f32x4 *>(sGam + 4 * v);
+        v -= vGam;
+        if (v < vBeta) return *reinterpret_cast<const f32x4 *>(sBeta + 4 * v);
+        v -= vBeta;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {                      // block scales, transposed
+            const int idx = 4 * v + e, a = idx / NSUB, b = idx % NSUB;
+            u.f[e] = idx < NSUB * NSUB ? sTs[b * NSUB + a] : 0.f;
+        }
+        return u.f;
     }
 };
 
@@ -613,7 +716,8 @@ void kda_prefill_kernel(
     // ---- workgroup -> (work unit, value block); blocks of one unit share an XCD.
     //      A work unit is a (sequence, head) pair, or a (segment, head) pair when
     //      a segment plan is given; summary mode adds DK transition columns.
-    constexpr bool kPrep = MODE == MODE_PREP;
+    constexpr bool kPrep = MODE == MODE_PREP || MODE == MODE_PREPG;
+    constexpr bool kPrepG = MODE == MODE_PREPG;
     // the fused kernel runs whole sequences; segments run in kda_chain_kernel
     constexpr bool segmented = false;
     constexpr bool summary = false;
@@ -815,6 +919,11 @@ void kda_prefill_kernel(
         f32x4 *junk = seg.img + ((int64_t)(seg.img_slots - 1) * num_heads + h) * Img::NVEC;
 #pragma unroll
         for (int it = 0; it < SITEMS; ++it) junk[min(tid + it * NT, Img::NVEC - 1)] = zero4();
+        if constexpr (kPrepG) {   // the gradient images' placeholders likewise
+            f32x4 *gjunk = seg.gimg + ((int64_t)(seg.img_slots - 1) * num_heads + h) * Img::NVEC;
+#pragma unroll
+            for (int it = 0; it < SITEMS; ++it) gjunk[min(tid + it * NT, Img::NVEC - 1)] = zero4();
+        }
     }
     for (int ci = 0; ci < nch; ++ci) {
         int c0, cend;
@@ -1078,6 +1187,15 @@ void kda_prefill_kernel(
             for (int it = 0; it < SITEMS; ++it) tv[it] = *reinterpret_cast<const f32x4 *>(smem + img_off[it]);
 #pragma unroll
             for (int it = 0; it < SITEMS; ++it) dst[min(tid + it * NT, Img::NVEC - 1)] = tv[it];
+            if constexpr (kPrepG) {
+                typedef GradImage<TIn, C> GImg;
+                f32x4 *gdst = seg.gimg + ((int64_t)(gc_begin + ci) * num_heads + h) * GImg::NVEC;
+#pragma unroll 1
+                for (int it = 0; it < SITEMS; ++it) {
+                    const int gv = min(tid + it * NT, GImg::NVEC - 1);
+                    gdst[gv] = GImg::gather(gv, sNKp, sQp, sKhT, sT, sP, sGam, sBeta, sTs);
+                }
+            }
             continue;
         }
         // ---- 4. state-dependent chain (this wave's 16 columns)
@@ -1460,15 +1578,402 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
     }
 }
 
+// ----------------------------------------------------- state-gradient chain
+// Training: the gradient of the state, G_t = dL/dS_t, runs backwards through
+// the sequence.  With the chunk form of the forward (top of this file), the
+// gradient entering a chunk at its end, G, gives the one at its start as
+//     Y  = K^ G + P^T dO,     Z = Diag(b) (I + N)^-T Y,
+//     G' = Diag(e^Gamma_C) G - K+^T Z + Q+^T dO,
+// the transpose of the chunk's state map plus the outputs' contribution (dO:
+// the gradient of the chunk's outputs).  Z is also the chunk's dv, and the
+// per-chunk gradients of q, k, g and beta need S at the chunk start and G at
+// its end only, so this chain stores G at every chunk end and a chunk-parallel
+// pass (kda_backward.hip) does the rest.
+//
+// grad_chunk: one chunk for the 16 NCT value columns of this wave, reading
+// the gradient image from LDS (sKh = GS K^, sNKpT = -GS K+^T, sQpT = GS Q+^T,
+// sPT = P^T, sTT = (I + N)^-T blocks with scales sTsT, the chunk decay sGam,
+// sBeta) and dO from sD[r * ldd + vc + 16 ct].  G (MFMA accumulator layout,
+// rows = key channels) is carried scaled per column by an exact power of two,
+// G~ = G sG, as chain_chunk carries the state: G~ feeds the fp16 operand
+// directly, and the update runs as the accumulator with Z and dO rounded in
+// G~'s units (sG / GS).  A column that is exactly zero takes the scale that
+// puts the incoming Z and dO in range.
+template <typename TIn, int C, int ldd, int NCT>
+__device__ __forceinline__ void grad_chunk(
+    f32x4 (&G)[NCT][DK / 16], float (&sG)[NCT], const typename PrefillCfg<TIn, C, 4>::OpT *sKh,
+    const typename PrefillCfg<TIn, C, 4>::OpT *sNKpT, const typename PrefillCfg<TIn, C, 4>::OpT *sQpT,
+    const typename PrefillCfg<TIn, C, 4>::OpT *sPT, const typename PrefillCfg<TIn, C, 4>::OpT *sTT,
+    const float *sTsT, const float *sGam, const float *sBeta, const TIn *sD, int vc, int lj, int lm)
+{
+    typedef PrefillCfg<TIn, C, 4> P;
+    typedef typename P::OpT OpT;
+    typedef Mma<OpT> M;
+    constexpr bool kIn16 = P::kIn16;
+    constexpr int NSUB = P::NSUB, KB = P::KB, LDK = P::LDK, LDC = P::LDC;
+    constexpr float GS = P::GS;
+
+    // dO of this wave's columns in accumulator layout (rows = tokens)
+    f32x4 D[NCT][NSUB];
+    float dmax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        dmax[ct] = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < NSUB; ++mt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) D[ct][mt][i] = to_f(sD[(mt * SUB + 4 * lj + i) * ldd + vc + 16 * ct]);
+            dmax[ct] = absmax_acc(dmax[ct], D[ct][mt]);
+        }
+        dmax[ct] = colmax(dmax[ct]);
+    }
+
+    // Y = K^ G + P^T dO      (rows of sKh hold GS K^; dO enters with its own column scale)
+    float isG[NCT], isD[NCT];
+    typename M::frag Gf[NCT][DK / KB], Df[NCT][C / KB];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        isG[ct] = pow2_inv(sG[ct]) * (1.f / GS);
+        const float sd = kIn16 ? pow2_scale(dmax[ct]) : 1.f;
+        isD[ct] = pow2_inv(sd);
+#pragma unroll
+        for (int kb = 0; kb < DK / KB; ++kb) Gf[ct][kb] = M::from_acc(&G[ct][kb * (KB / 16)]);
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb) Df[ct][kb] = M::from_acc(&D[ct][kb * (KB / 16)], sd);
+    }
+    f32x4 Y[NCT][NSUB];
+    float ymax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) ymax[ct] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NSUB; ++mt) {
+        f32x4 y1[NCT], y2[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) y1[ct] = y2[ct] = zero4();
+        const OpT *rowK = sKh + (mt * SUB + lm) * LDK;
+#pragma unroll
+        for (int kb = 0; kb < DK / KB; ++kb) {
+            const typename M::frag kf = M::load_p(rowK, kb * KB, lj);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) y1[ct] = M::mma(kf, Gf[ct][kb], y1[ct]);
+        }
+        const OpT *rowP = sPT + (mt * SUB + lm) * LDC;
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb)
+            if (kb * KB + KB - 1 >= mt * SUB) {           // P^T is upper triangular
+                const typename M::frag pf = M::load_p(rowP, kb * KB, lj);
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) y2[ct] = M::mma(pf, Df[ct][kb], y2[ct]);
+            }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            Y[ct][mt] = y1[ct] * isG[ct] + y2[ct] * isD[ct];
+            ymax[ct] = absmax_acc(ymax[ct], Y[ct][mt]);
+        }
+    }
+    // Z = Diag(b) (I + N)^-T Y, block upper triangular, per-block scales
+    typename M::frag16 Y16[NCT][NSUB];
+    float isY[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const float sy = kIn16 ? pow2_scale(colmax(ymax[ct])) : 1.f;
+        isY[ct] = pow2_inv(sy);
+#pragma unroll
+        for (int b = 0; b < NSUB; ++b) Y16[ct][b] = M::from_acc16(Y[ct][b], sy);
+    }
+    f32x4 Z[NCT][NSUB];
+    float zmax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) zmax[ct] = 0.f;
+#pragma unroll
+    for (int a = 0; a < NSUB; ++a) {
+        f32x4 z[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) z[ct] = zero4();
+        const OpT *rowT = sTT + (a * SUB + lm) * LDC;
+#pragma unroll
+        for (int b = a; b < NSUB; ++b) {
+            const typename M::frag16 tf = M::load16(rowT, b * SUB, lj);
+            const float ts = sTsT[a * NSUB + b];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) z[ct] += M::mma16(tf, Y16[ct][b], zero4()) * (ts * isY[ct]);
+        }
+        const f32x4 bt = *reinterpret_cast<const f32x4 *>(sBeta + a * SUB + 4 * lj);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            Z[ct][a] = z[ct] * bt;
+            zmax[ct] = absmax_acc(zmax[ct], Z[ct][a]);
+        }
+    }
+    // Z and dO enter the update in G~'s units; if they would not fit fp16 the
+    // scale of G~ comes down first (wave-uniform branch, rarely taken)
+    typename M::frag Zf[NCT][C / KB], Ef[NCT][C / KB];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        float sU = sG[ct] * (1.f / GS);
+        if (kIn16) {
+            const float um = fmaxf(colmax(zmax[ct]), dmax[ct]);
+            float gm = 0.f;
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) gm = absmax_acc(gm, G[ct][r]);
+            const bool fresh = colmax(gm) == 0.f && um > 0.f;     // G~ column exactly zero
+            const float p = (!fresh && um * sU >= 32768.f) ? pow2_scale(um * sU) : 1.f;
+            if (__ballot(p != 1.f)) {
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r) G[ct][r] *= p;
+                sG[ct] *= p;
+                sU *= p;
+            }
+            if (fresh) {
+                sG[ct] = fminf(GS * pow2_scale(um), kScaleCap);
+                sU = sG[ct] * (1.f / GS);
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb) {
+            Zf[ct][kb] = M::from_acc(&Z[ct][kb * (KB / 16)], sU);
+            Ef[ct][kb] = M::from_acc(&D[ct][kb * (KB / 16)], sU);
+        }
+    }
+    // G~ = Diag(gamma) G~ + (-GS K+^T)(Z sG / GS) + (GS Q+^T)(dO sG / GS)
+    float gmax[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) gmax[ct] = 0.f;
+#pragma unroll
+    for (int r = 0; r < DK / 16; ++r) {
+        const f32x4 gm = *reinterpret_cast<const f32x4 *>(sGam + 16 * r + 4 * lj);
+        f32x4 t[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) t[ct] = G[ct][r] * gm;
+        const OpT *rowN = sNKpT + (16 * r + lm) * LDC;
+        const OpT *rowQ = sQpT + (16 * r + lm) * LDC;
+#pragma unroll
+        for (int kb = 0; kb < C / KB; ++kb) {
+            const typename M::frag nf = M::load_p(rowN, kb * KB, lj);
+            const typename M::frag qf = M::load_p(rowQ, kb * KB, lj);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                t[ct] = M::mma(nf, Zf[ct][kb], t[ct]);
+                t[ct] = M::mma(qf, Ef[ct][kb], t[ct]);
+            }
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            G[ct][r] = t[ct];
+            if (kIn16) gmax[ct] = absmax_acc(gmax[ct], t[ct]);
+        }
+    }
+    // keep every column inside [2^-8, 2^15), as chain_chunk does
+    if (kIn16) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float m = colmax(gmax[ct]);
+            float q = 1.f;
+            if (m >= 32768.f) q = pow2_scale(m);
+            else if (m > 0.f && m < 0.00390625f) q = fmaxf(1.f, fminf(pow2_scale(m), kScaleCap * pow2_inv(sG[ct])));
+            if (__ballot(q != 1.f)) {
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r) G[ct][r] *= q;
+                sG[ct] *= q;
+            }
+        }
+    }
+}
+
+// LDS of the gradient chain: one or two chunk buffers, each the gradient image
+// (padded strides) and the chunk's dO tile.
+template <typename TIn, int C, int NW, int NCT, bool SB>
+struct GChainCfg {
+    typedef PrefillCfg<TIn, C, NW> P;
+    typedef typename P::OpT OpT;
+    typedef GradImage<TIn, C> Img;
+    static constexpr int NT = 64 * NW, BV = 16 * NW * NCT, NSUB = C / SUB;
+    static_assert(BV == DK, "one workgroup covers every value column");
+    static constexpr int LDK = P::LDK, LDC = P::LDC, LDV = BV + 16 / (int)sizeof(TIn);
+    static constexpr uint32_t offKh = 0;
+    static constexpr uint32_t offNKpT = offKh + sizeof(OpT) * C * LDK;
+    static constexpr uint32_t offQpT = offNKpT + sizeof(OpT) * DK * LDC;
+    static constexpr uint32_t offPT = offQpT + sizeof(OpT) * DK * LDC;
+    static constexpr uint32_t offTT = offPT + sizeof(OpT) * C * LDC;
+    static constexpr uint32_t offGam = offTT + sizeof(OpT) * C * LDC;
+    static constexpr uint32_t offBeta = offGam + sizeof(float) * DK;
+    static constexpr uint32_t offTs = offBeta + sizeof(float) * C;
+    static constexpr uint32_t offD = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
+    static constexpr uint32_t BUF = (offD + sizeof(TIn) * C * LDV + 15) / 16 * 16;
+    static constexpr uint32_t bytes = (SB ? 1 : 2) * BUF;
+    static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static constexpr int IITEMS = (Img::NVEC + NT - 1) / NT;
+    static constexpr int VEC = 16 / (int)sizeof(TIn);
+    static constexpr int VPR = BV / VEC;
+    static constexpr int VITEMS = (C * VPR + NT - 1) / NT;
+};
+
+// One workgroup per (segment, head), all value columns (NW waves x NCT tiles
+// of 16), walking the segment's chunks from its end.  SUMMARY: from a zero
+// gradient at the segment's end, writing the gradient at its start (G^0 of
+// the segment: with R = M^T, the transposed forward transition, the reverse
+// combine then gives every segment's entering gradient); segments that are a
+// sequence's first are skipped.  Otherwise from g_end (the gradient at the
+// segment's end), storing the gradient at the end of every chunk at that
+// chunk's global index in g_chunk ([chunks][H][DK][DV]) and, for a sequence's
+// first segment, the gradient at the sequence start in dinit (may be nullptr).
+// The stored values are G~ / sG, exact.
+template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB>
+__global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
+    const TIn *dout, const int32_t *__restrict__ cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+    int32_t num_heads, const int32_t *__restrict__ plan, int32_t num_segs, const int32_t *__restrict__ sched,
+    const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, float *g_chunk,
+    float *dinit, float *g0_out)
+{
+    typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
+    typedef typename Q::OpT OpT;
+    typedef typename Q::Img Img;
+    constexpr int NT = Q::NT, LDV = Q::LDV, VEC = Q::VEC, VPR = Q::VPR;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    // ---- workgroup -> (segment, head); consecutive segments share an XCD
+    const int wg = blockIdx.x;
+    const int xcd = wg & 7, slot = wg >> 3;
+    const int64_t unit = (int64_t)slot * 8 + xcd;
+    if (unit >= (int64_t)num_segs * num_heads) return;
+    int su = (int)(unit / num_heads);
+    const int h = (int)(unit % num_heads);
+    if (sched) su = min(max(sched[su], 0), num_segs - 1);
+    const int n = plan[4 * su];
+    const int sflags = plan[4 * su + 3];
+    if (n < 0 || (SUMMARY && (sflags & SEG_FIRST))) return;
+    const int seq_start = min(max(cu_seqlens[n], 0), total_tokens);
+    const int t_start = min(max(plan[4 * su + 1], 0), total_tokens);
+    const int t_end = min(max(plan[4 * su + 2], t_start), total_tokens);
+    const int64_t gc0 = chunk_off[n] + (t_start - seq_start) / C;
+    const int nch = (int)max((int64_t)0, min((int64_t)(t_end - t_start + C - 1) / C,
+                                             (int64_t)chunk_off[num_seqs] - gc0));
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lj = lane >> 4, lm = lane & 15;
+    const int H = num_heads;
+    const int64_t rowV = (int64_t)H * DK;
+
+    // ---- entering gradient: tile ct of this wave is column 16 (NCT wave + ct) + lm
+    const int vcol = 16 * NCT * wave + lm;
+    f32x4 G[NCT][DK / 16];
+    float sG[NCT];
+    const float *gin = SUMMARY ? nullptr : g_end + ((int64_t)su * H + h) * DK * DK;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = vcol + 16 * ct;
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[ct][r][i] = gin ? gin[(int64_t)(16 * r + 4 * lj + i) * DK + col] : 0.f;
+        sG[ct] = 1.f;
+        if (Q::P::kIn16) {
+            float m = 0.f;
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, G[ct][r]);
+            sG[ct] = fminf(pow2_scale(colmax(m)), kScaleCap);
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) G[ct][r] *= sG[ct];
+        }
+    }
+
+    // ---- chunk staging: gradient image + dO tile of chunk ci in registers
+    f32x4 ri[Q::IITEMS], rd[Q::VITEMS];
+    auto load = [&](int ci) {
+        const f32x4 *src = gimg + ((gc0 + ci) * H + h) * Img::NVEC;
+#pragma unroll
+        for (int it = 0; it < Q::IITEMS; ++it) ri[it] = src[min(tid + it * NT, Img::NVEC - 1)];
+        const int c0 = t_start + ci * C, LL = min(C, t_end - c0);
+#pragma unroll
+        for (int it = 0; it < Q::VITEMS; ++it) {
+            const int e = min(tid + it * NT, C * VPR - 1);
+            const int rc = min(e / VPR, LL - 1), cv = (e % VPR) * VEC;
+            rd[it] = *reinterpret_cast<const f32x4 *>(dout + (int64_t)(c0 + rc) * rowV + (int64_t)h * DK + cv);
+        }
+    };
+    const typename Img::Offs offs = {Q::offKh, Q::offNKpT, Q::offQpT, Q::offPT, Q::offTT, Q::offGam, Q::offBeta,
+                                     Q::offTs};
+    uint32_t stage_off[Q::IITEMS];
+#pragma unroll
+    for (int it = 0; it < Q::IITEMS; ++it) stage_off[it] = Img::lds_off(min(tid + it * NT, Img::NVEC - 1), offs);
+    auto stage = [&](int ci, int b) {
+        unsigned char *base = smem + b * Q::BUF;
+#pragma unroll
+        for (int it = 0; it < Q::IITEMS; ++it) *reinterpret_cast<f32x4 *>(base + stage_off[it]) = ri[it];
+        TIn *sD = reinterpret_cast<TIn *>(base + Q::offD);
+        const int LL = min(C, t_end - (t_start + ci * C));
+#pragma unroll
+        for (int it = 0; it < Q::VITEMS; ++it) {
+            const int e = min(tid + it * NT, C * VPR - 1);
+            const int r = e / VPR, cv = (e % VPR) * VEC;
+            *reinterpret_cast<f32x4 *>(sD + r * LDV + cv) = r < LL ? rd[it] : zero4();
+        }
+    };
+    auto store_g = [&](float *dst) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const float inv = pow2_inv(sG[ct]);
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * r + 4 * lj + i) * DK + vcol + 16 * ct] = G[ct][r][i] * inv;
+        }
+    };
+    if (nch > 0) {
+        load(nch - 1);
+        stage(nch - 1, 0);
+    }
+    for (int k = 0; k < nch; ++k) {
+        const int ci = nch - 1 - k;
+        __syncthreads();                          // chunk ci staged; (double buffer) the previous one done
+        load(max(ci - 1, 0));                     // unconditional, see the forward chain
+        if constexpr (!SUMMARY) store_g(g_chunk + ((gc0 + ci) * H + h) * DK * DK);   // G at the chunk's end
+        const unsigned char *base = smem + (SB ? 0 : (k & 1) * Q::BUF);
+        grad_chunk<TIn, C, LDV, NCT>(
+            G, sG, reinterpret_cast<const OpT *>(base + Q::offKh), reinterpret_cast<const OpT *>(base + Q::offNKpT),
+            reinterpret_cast<const OpT *>(base + Q::offQpT), reinterpret_cast<const OpT *>(base + Q::offPT),
+            reinterpret_cast<const OpT *>(base + Q::offTT), reinterpret_cast<const float *>(base + Q::offTs),
+            reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
+            reinterpret_cast<const TIn *>(base + Q::offD), vcol, lj, lm);
+        if constexpr (SB) __syncthreads();       // every wave is done with the buffer
+        stage(max(ci - 1, 0), SB ? 0 : (k + 1) & 1);
+    }
+    if constexpr (SUMMARY) store_g(g0_out + ((int64_t)su * H + h) * DK * DK);
+    else if (dinit && (sflags & SEG_FIRST)) store_g(dinit + ((int64_t)n * H + h) * DK * DK);
+}
+
+template <typename TIn, int C, int NW, int NCT, bool SB>
+static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int32_t *cu, int32_t N, int32_t T_tot,
+                                      int32_t H, const int32_t *plan, int32_t num_segs, const int32_t *sched,
+                                      const int32_t *chunk_off, const void *gimg, const float *g_end, float *g_chunk,
+                                      float *dinit, float *g0_out, hipStream_t stream)
+{
+    typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
+    auto kern = summary ? kda_grad_chain_kernel<TIn, C, NW, NCT, true, SB>
+                        : kda_grad_chain_kernel<TIn, C, NW, NCT, false, SB>;
+    static std::atomic<uint64_t> lds_set[2];
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)Q::bytes, lds_set[summary ? 1 : 0]))
+        return e;
+    const int64_t grid = ((int64_t)num_segs * H + 7) / 8 * 8;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(dout), cu,
+                       N, T_tot, H, plan, num_segs, sched, chunk_off, static_cast<const f32x4 *>(gimg), g_end,
+                       g_chunk, dinit, g0_out);
+    return hipGetLastError();
+}
+
 template <typename TIn, int C>
 static hipError_t launch_prep_t(const void *q, const void *k, const float *g, const float *beta,
                                 const int32_t *cu, int32_t N, int32_t T_tot, int32_t H, int64_t max_chunks,
                                 SegArgs seg, hipStream_t stream)
 {
     typedef PrefillCfg<TIn, C, 4> P;
-    auto kern = kda_prefill_kernel<TIn, C, 4, MODE_PREP>;
-    static std::atomic<uint64_t> lds_set{0};
-    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)P::bytes, lds_set)) return e;
+    const bool grad = seg.gimg != nullptr;
+    auto kern = grad ? kda_prefill_kernel<TIn, C, 4, MODE_PREPG> : kda_prefill_kernel<TIn, C, 4, MODE_PREP>;
+    static std::atomic<uint64_t> lds_set[2];
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)P::bytes, lds_set[grad ? 1 : 0]))
+        return e;
     // fewer chunks per workgroup when there are few: every compute unit
     // gets work, and a workgroup's walk is short
     const int64_t want = (max_chunks * H + 2047) / 2048;
@@ -1845,15 +2350,16 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
 }
 
 // Chunk-operand pass: images of every (chunk, head), 32-token chunks.
+// gimg (may be nullptr): also the gradient images, same slots.
 extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
                                             const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
                                             int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
-                                            hipStream_t stream)
+                                            void *gimg, hipStream_t stream)
 {
     using namespace kda;
     if (max_chunks < 1 || max_chunks > 0x7fffffff) return hipErrorInvalidValue;
     SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr,
-                   nullptr, 0, 0, PREP_GROUP, (int32_t)max_chunks};
+                   nullptr, 0, 0, PREP_GROUP, (int32_t)max_chunks, static_cast<f32x4 *>(gimg)};
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
@@ -1885,6 +2391,28 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     if (dv_block != 64 && dv_block != 128 && dv_block != 256) return hipErrorInvalidValue;
     if (bf16) return launch_chain_t<bf16_t, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     return launch_chain_t<float, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+}
+
+// State-gradient chain over the gradient images (see kda_grad_chain_kernel):
+// summary = 1 writes G^0 of every segment but a sequence's first to g0_out
+// [num_segs][H][DK][DK]; summary = 0 runs every segment from g_end (same
+// layout), storing the gradient at every chunk end in g_chunk and d(initial
+// state) in dinit.
+extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
+                                            int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
+                                            const int32_t *sched, const int32_t *chunk_off, const void *gimg,
+                                            const float *g_end, float *g_chunk, float *dinit, float *g0_out,
+                                            hipStream_t stream)
+{
+    using namespace kda;
+    if (summary ? !g0_out : (!g_end || !g_chunk)) return hipErrorInvalidValue;
+    // bf16: double buffered (about 87 KB); fp32 images are twice as large: one buffer
+    if (bf16)
+        return launch_grad_chain_t<bf16_t, 32, 4, 2, false>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs,
+                                                            sched, chunk_off, gimg, g_end, g_chunk, dinit, g0_out,
+                                                            stream);
+    return launch_grad_chain_t<float, 32, 4, 2, true>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs, sched,
+                                                      chunk_off, gimg, g_end, g_chunk, dinit, g0_out, stream);
 }
 
 extern "C" size_t kda_chunk_image_bytes(int bf16)
