@@ -15,6 +15,8 @@
 //   3. kda_bwd_chunk_kernel (below) turns each chunk's S (start), G (end) and
 //      inputs into its gradients of q, k, v, g and beta -- no recurrence left,
 //      one workgroup per (chunk, head).
+#include <type_traits>
+
 #include "kda_device.hpp"
 
 namespace kda {
@@ -59,7 +61,15 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
 //     dGamma = q (.) dq + k (.) (row part) - k (.) (column part), and at the
 //              last token also sum_r k (.) dK^ (.) e^(Gamma_L - Gamma) + (G (.) S) 1 (.) e^Gamma_L
 //     dg = reverse cumulative sum of dGamma over the chunk.
-// Everything runs on fp32 (MFMA 16x16x4 and VALU), for both input types.
+// Precision: the Gram tiles, (I + N)^-1 and every 32-wide contraction run on
+// fp32 (MFMA 16x16x4 and VALU).  The seven 128-wide contractions (U, K^ G,
+// dQ+, dX S^T, dK^, dP, dN) run on the MFMA type of the forward: fp32 for
+// fp32 inputs; fp16 for 16-bit inputs, with S and G read as the fp16 values
+// and exact power-of-two column scales that the chains carry, and every other
+// operand given an exact power-of-two scale per row (the row maximum lands in
+// [2^13, 2^14)) -- a scale along the contraction index is folded into the
+// other operand, so every product is exact up to the fp16 rounding of its
+// operands.
 // Gamma is kept in fp64: every decay factor is e^x of a difference of two of
 // its entries, rounded to fp32 only then, so a factor carries the rounding of
 // its own exponent, not that of the (up to 160 in magnitude) cumulative sums.
@@ -68,11 +78,16 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
 // off-diagonal one -- so every factor lies in [e^-80, e^40] for g in [-5, 0]:
 // the Gram tiles and the E-weighted token sums are then plain MFMA products of
 // factored operands, and a factor applied after a product is at most e^40.
+// Work split: eight waves; in the value-column parts wave w owns columns
+// 16 w .. 16 w + 15, in the key-channel parts channels 16 w .. 16 w + 15.
 namespace bc {
-constexpr int C = 32, NT = 256;
+constexpr int C = 32, NW = 8, NT = 64 * NW;
 constexpr int LDG = BD + 2;          // fp64 Gamma rows
 constexpr int LDF = BD + 4;          // fp32 [C][BD] rows
 constexpr int LDX = C + 4;           // fp32 [C][C] rows
+constexpr int NDB = 12;              // partial dbeta slots: 8 value-column waves, 3 dN blocks, 1 spare
+constexpr int NMX = 6;               // row maxima: |dO|, |dO|/sS, |dX|, |dX|/sS, |W|, |W|/sG
+enum { MX_DO = 0, MX_DOS = 1, MX_DX = 2, MX_DXS = 3, MX_W = 4, MX_WG = 5 };
 template <typename T>
 struct Cfg {
     static constexpr int LDI = BD + 16 / (int)sizeof(T);   // q, k rows (input type)
@@ -88,8 +103,12 @@ struct Cfg {
     static constexpr uint32_t offT = offPT + sizeof(float) * C * LDX;     // T, later dA
     static constexpr uint32_t offTT = offT + sizeof(float) * C * LDX;     // T^T, later dA^T
     static constexpr uint32_t offBeta = offTT + sizeof(float) * C * LDX;
-    static constexpr uint32_t offDb = offBeta + sizeof(float) * C;        // [8][C] partial dbeta
-    static constexpr uint32_t bytes = offDb + sizeof(float) * 8 * C;
+    static constexpr uint32_t offDb = offBeta + sizeof(float) * C;        // [NDB][C] partial dbeta
+    static constexpr uint32_t offIS = offDb + sizeof(float) * NDB * C;    // [BD] 1 / column scale of S
+    static constexpr uint32_t offIG = offIS + sizeof(float) * BD;         // [BD] 1 / column scale of G
+    static constexpr uint32_t offMx = offIG + sizeof(float) * BD;         // [NW][NMX][C] partial row maxima
+    static constexpr uint32_t offRS = offMx + sizeof(float) * NW * NMX * C;   // [NMX][C] row scales
+    static constexpr uint32_t bytes = offRS + sizeof(float) * NMX * C;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
 typedef double f64x2 __attribute__((ext_vector_type(2)));
@@ -110,19 +129,46 @@ __device__ __forceinline__ f32x4 exp4(const double *a) {
     const f64x2 a0 = *reinterpret_cast<const f64x2 *>(a), a1 = *reinterpret_cast<const f64x2 *>(a + 2);
     return f32x4{__expf((float)a0[0]), __expf((float)a0[1]), __expf((float)a1[0]), __expf((float)a1[1])};
 }
+// Contraction indices of element e of lane group j's K-block fragment, in
+// groups of four consecutive ones: group 0 at k0 + 4 j, and for 16-bit
+// operands group 1 at k0 + 16 + 4 j (the layout of kda_device.hpp).
+template <typename OpT> struct Frag {
+    typedef Mma<OpT> M;
+    static constexpr int NG = M::KB / 16;                 // groups of four per fragment
+    __device__ static __forceinline__ int base(int k0, int j, int gi) { return k0 + 16 * gi + 4 * j; }
+    // fragment from NG f32x4 groups, each element times `scale`
+    __device__ static __forceinline__ typename M::frag make(const f32x4 (&x)[NG], float scale) {
+        typename M::frag f;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[4 * gi + e] = from_f<OpT>(x[gi][e] * scale);
+        return f;
+    }
+};
 }  // namespace bc
 
+// S (start state) and G (end gradient) of every chunk: [chunks][H][BD][BD] as
+// the chains store them -- fp16 values with column scales [chunks][H][BD]
+// (OpT = fp16) or fp32 (scales unused).
 template <typename T>
 __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
-    const float *__restrict__ beta, const T *__restrict__ dout, const float *initial_state,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, const float *__restrict__ snaps,
-    const float *__restrict__ gchunk, int32_t N, int32_t T_tot, int32_t H, float *__restrict__ dq,
-    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta)
+    const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const void *__restrict__ snaps, const float *__restrict__ snap_scale,
+    const void *__restrict__ gchunk, const float *__restrict__ g_scale, int32_t N, int32_t T_tot, int32_t H,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
+    float *__restrict__ dbeta)
 {
     using namespace bc;
     typedef Cfg<T> Q;
     typedef Mma<float> Mf;
+    constexpr bool kIn16 = !std::is_same<T, float>::value;
+    typedef typename std::conditional<kIn16, f16_t, float>::type OpT;   // 128-wide contractions
+    typedef Mma<OpT> Mo;
+    typedef Frag<OpT> F;
+    constexpr int KB = Mo::KB, NG = F::NG;
+    constexpr float GS = kIn16 ? 32.f : 1.f;   // K+ and K^ enter 16-bit operands times GS (|k| <= 1024)
     constexpr int LDI = Q::LDI;
     extern __shared__ __align__(16) unsigned char smem[];
     T *sK = reinterpret_cast<T *>(smem + Q::offK);
@@ -138,6 +184,10 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     float *sTT = reinterpret_cast<float *>(smem + Q::offTT);
     float *sBeta = reinterpret_cast<float *>(smem + Q::offBeta);
     float *sDb = reinterpret_cast<float *>(smem + Q::offDb);
+    float *sIS = reinterpret_cast<float *>(smem + Q::offIS);
+    float *sIG = reinterpret_cast<float *>(smem + Q::offIG);
+    float *sMx = reinterpret_cast<float *>(smem + Q::offMx);
+    float *sRS = reinterpret_cast<float *>(smem + Q::offRS);
     float *sdP = sP, *sdPT = sPT, *sdA = sT, *sdAT = sTT, *sDG = sW;
 
     // ---- workgroup -> (chunk, head); the chunk's sequence by binary search
@@ -152,19 +202,19 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     }
     const int n = lo;
     const int t0 = min(max(cu[n], 0), T_tot), t1 = min(max(cu[n + 1], t0), T_tot);
-    const int64_t cs = gc - chunk_off[n];                 // chunk index within the sequence
-    const int64_t c0l = t0 + cs * C;
+    const int64_t c0l = t0 + (gc - chunk_off[n]) * C;
     if (c0l >= t1) return;                                // only when cu_seqlens is not non-decreasing
     const int c0 = (int)c0l, L = min(C, t1 - c0);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lj = lane >> 4, lm = lane & 15;
     const int64_t rowQ = (int64_t)H * BD;
     const int64_t hoff = (int64_t)h * BD;
-    const float *Sg = cs ? snaps + (gc * H + h) * BD * BD
-                         : (initial_state ? initial_state + ((int64_t)n * H + h) * BD * BD : nullptr);
-    const float *Gg = gchunk + (gc * H + h) * BD * BD;
+    const int64_t unit = gc * H + h;
+    const OpT *Sg = static_cast<const OpT *>(snaps) + unit * BD * BD;
+    const OpT *Gg = static_cast<const OpT *>(gchunk) + unit * BD * BD;
 
-    // ---- 0. the chunk's q, k (input type), dO (fp32), beta and Gamma (fp64);
-    //         rows past the chunk's end are zero (Gamma stays constant)
+    // ---- 0. the chunk's q, k (input type), dO (fp32), beta, Gamma (fp64) and
+    //         the inverse column scales of S and G; rows past the chunk's end
+    //         are zero (Gamma stays constant)
     {
         constexpr int VE = 16 / (int)sizeof(T), VPR = BD / VE;
         for (int e = tid; e < C * VPR; e += NT) {
@@ -192,39 +242,47 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                 if (r < L) s += (double)gv[r];
                 sGm[r * LDG + tid] = s;
             }
+        } else if (tid < 2 * BD) {
+            const int c = tid - BD;
+            sIS[c] = kIn16 ? pow2_inv(snap_scale[unit * BD + c]) : 1.f;
+            sIG[c] = kIn16 ? pow2_inv(g_scale[unit * BD + c]) : 1.f;
         }
     }
     __syncthreads();
 
-    // ---- 1. Gram tiles A (strictly lower), P (lower incl.): waves 0, 1 the
-    //         diagonal blocks (reference: the block's middle token), wave 2 the
-    //         off-diagonal block (reference: token 15); wave 3 zeroes the upper block
-    if (wave < 3) {
-        const int rb = wave == 0 ? 0 : 16, ib = wave == 1 ? 16 : 0, ref = wave == 0 ? 7 : (wave == 1 ? 23 : 15);
+    // ---- 1. Gram tiles A (strictly lower), P (lower incl.): block x = 0, 1
+    //         diagonal (reference: the block's middle token), x = 2 the
+    //         off-diagonal one (reference: token 15); waves 0-2 A, 3-5 P,
+    //         waves 6-7 zero the upper block
+    if (wave < 6) {
+        const int x = wave % 3;
+        const bool isP = wave >= 3;
+        const int rb = x == 0 ? 0 : 16, ib = x == 1 ? 16 : 0, ref = x == 0 ? 7 : (x == 1 ? 23 : 15);
         const int r = rb + lm, i = ib + lm;
-        f32x4 accA = zero4(), accP = zero4();
+        const T *rowR = (isP ? sQ : sK) + r * LDI;
+        f32x4 acc = zero4();
 #pragma unroll 2
         for (int kb = 0; kb < BD / 16; ++kb) {
             const int c = 16 * kb + 4 * lj;
             const f32x4 rf = exp_diff4(sGm + r * LDG + c, sGm + ref * LDG + c);
             const f32x4 cf = exp_diff4(sGm + ref * LDG + c, sGm + i * LDG + c);
-            const f32x4 b = ld4(sK + i * LDI + c) * cf;
-            accA = Mf::mma(ld4(sK + r * LDI + c) * rf, b, accA);
-            accP = Mf::mma(ld4(sQ + r * LDI + c) * rf, b, accP);
+            acc = Mf::mma(ld4(rowR + c) * rf, ld4(sK + i * LDI + c) * cf, acc);
         }
-        const bool diag = wave < 2;
+        const bool diag = x < 2;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const int rr = rb + 4 * lj + ii, cc = ib + lm;
             // selects, not products: entries above the diagonal may be inf
-            const float a = (!diag || cc < rr) ? accA[ii] : 0.f;
-            const float p = (!diag || cc <= rr) ? accP[ii] : 0.f;
-            sA[rr * LDX + cc] = a;
-            sP[rr * LDX + cc] = p;
-            sPT[cc * LDX + rr] = p;
+            if (isP) {
+                const float p = (!diag || cc <= rr) ? acc[ii] : 0.f;
+                sP[rr * LDX + cc] = p;
+                sPT[cc * LDX + rr] = p;
+            } else {
+                sA[rr * LDX + cc] = (!diag || cc < rr) ? acc[ii] : 0.f;
+            }
         }
     } else {
-        for (int e = lane; e < 256; e += 64) {
+        for (int e = tid - 384; e < 256; e += 128) {
             const int rr = e >> 4, cc = 16 + (e & 15);
             sA[rr * LDX + cc] = 0.f;
             sP[rr * LDX + cc] = 0.f;
@@ -253,7 +311,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                 sTT[(a0 + j) * LDX + a0 + r] = t[r];
             }
         }
-    } else {
+    } else if (wave < 4) {
         for (int e = tid - 128; e < 256; e += 128) {
             const int rr = e >> 4, cc = 16 + (e & 15);
             sT[rr * LDX + cc] = 0.f;
@@ -274,186 +332,232 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     }
     __syncthreads();
 
-    // ---- 2. value columns vc0, vc0 + 16 of this wave (tiles ct), token row tiles rt
-    const int vc0 = 32 * wave + lm;
-    f32x4 U[2][2], dW[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) U[rt][ct] = dW[rt][ct] = zero4();
+    // ---- 2. value column col of this lane (wave w: columns 16 w + lm),
+    //         token row tiles rt; U = V - K+ S and K^ G on the MFMA type of the forward
+    const int col = 16 * wave + lm;
+    f32x4 U[2], dW[2];
+    U[0] = U[1] = dW[0] = dW[1] = zero4();
     const double *gmL = sGm + (L - 1) * LDG;
 #pragma unroll 2
-    for (int kb = 0; kb < BD / 16; ++kb) {
-        const int c = 16 * kb + 4 * lj;
-        f32x4 sb[2], gb[2];
+    for (int kb = 0; kb < BD / KB; ++kb) {
+        // B operands: column col of S and G, rows = the fragment's contraction indices
+        typename Mo::frag bs, bg;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                sb[ct][e] = Sg ? Sg[(int64_t)(c + e) * BD + vc0 + 16 * ct] : 0.f;
-                gb[ct][e] = Gg[(int64_t)(c + e) * BD + vc0 + 16 * ct];
+                const int64_t o = (int64_t)(F::base(kb * KB, lj, gi) + e) * BD + col;
+                bs[4 * gi + e] = Sg[o];
+                bg[4 * gi + e] = Gg[o];
             }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int r = 16 * rt + lm;
-            const f32x4 kr = ld4(sK + r * LDI + c);
-            const f32x4 kp = kr * exp4(sGm + r * LDG + c);                 // K+
-            const f32x4 kh = kr * exp_diff4(gmL + c, sGm + r * LDG + c);   // K^
+            f32x4 kp[NG], kh[NG];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                U[rt][ct] = Mf::mma(kp, sb[ct], U[rt][ct]);
-                dW[rt][ct] = Mf::mma(kh, gb[ct], dW[rt][ct]);
+            for (int gi = 0; gi < NG; ++gi) {
+                const int c = F::base(kb * KB, lj, gi);
+                const f32x4 kr = ld4(sK + r * LDI + c);
+                kp[gi] = kr * exp4(sGm + r * LDG + c);                 // K+
+                kh[gi] = kr * exp_diff4(gmL + c, sGm + r * LDG + c);   // K^
             }
+            U[rt] = Mo::mma(F::make(kp, GS), bs, U[rt]);
+            dW[rt] = Mo::mma(F::make(kh, GS), bg, dW[rt]);
         }
     }
-    f32x4 X[2][2];
+    {
+        const float us = sIS[col] * (1.f / GS), gs = sIG[col] * (1.f / GS);
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rt + 4 * lj + i;
-                const float vv = to_f(v[(int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + vc0 + 16 * ct]);
-                U[rt][ct][i] = (r < L ? vv : 0.f) - U[rt][ct][i];
-                X[rt][ct][i] = sBeta[r] * U[rt][ct][i];
-            }
-    // W = T X;  dW += P^T dO;  dX = T^T dW   (T lower, P^T and T^T upper by blocks)
-    f32x4 W[2][2], dX[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) W[rt][ct] = zero4();
-#pragma unroll
-        for (int bt = 0; bt <= rt; ++bt) {
-            const f32x4 ta = ld4(sT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) W[rt][ct] = Mf::mma(ta, X[bt][ct], W[rt][ct]);
-        }
-#pragma unroll
-        for (int bt = rt; bt < 2; ++bt) {
-            const f32x4 pa = ld4(sPT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                f32x4 db;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) db[e] = sDO[(16 * bt + 4 * lj + e) * LDF + vc0 + 16 * ct];
-                dW[rt][ct] = Mf::mma(pa, db, dW[rt][ct]);
-            }
+        for (int rt = 0; rt < 2; ++rt) {
+            U[rt] *= us;
+            dW[rt] *= gs;
         }
     }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) dX[rt][ct] = zero4();
-#pragma unroll
-        for (int bt = rt; bt < 2; ++bt) {
-            const f32x4 ta = ld4(sTT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj);
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) dX[rt][ct] = Mf::mma(ta, dW[bt][ct], dX[rt][ct]);
-        }
-    }
-    // dv, the U.dX part of dbeta (this wave's columns), W and dX to LDS
+    f32x4 X[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * rt + 4 * lj + i;
-            float pb = 0.f;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = vc0 + 16 * ct;
-                if (r < L) dv[(int64_t)(c0 + r) * rowQ + hoff + col] = sBeta[r] * dX[rt][ct][i];
-                pb += U[rt][ct][i] * dX[rt][ct][i];
-                sW[r * LDF + col] = W[rt][ct][i];
-                sDX[r * LDF + col] = dX[rt][ct][i];
-            }
-            pb = sum16(pb);
-            if (lm == 0) sDb[wave * C + r] = pb;
+            const float vv = to_f(v[(int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + col]);
+            U[rt][i] = (r < L ? vv : 0.f) - U[rt][i];
+            X[rt][i] = sBeta[r] * U[rt][i];
         }
+    // W = T X;  dW += P^T dO;  dX = T^T dW   (fp32; T lower, P^T and T^T upper by blocks)
+    f32x4 W[2], dX[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        W[rt] = zero4();
+#pragma unroll
+        for (int bt = 0; bt <= rt; ++bt) W[rt] = Mf::mma(ld4(sT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj), X[bt], W[rt]);
+#pragma unroll
+        for (int bt = rt; bt < 2; ++bt) {
+            f32x4 db;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) db[e] = sDO[(16 * bt + 4 * lj + e) * LDF + col];
+            dW[rt] = Mf::mma(ld4(sPT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj), db, dW[rt]);
+        }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        dX[rt] = zero4();
+#pragma unroll
+        for (int bt = rt; bt < 2; ++bt) dX[rt] = Mf::mma(ld4(sTT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj), dW[bt], dX[rt]);
+    }
+    // dv, the U.dX part of dbeta (this wave's columns), W and dX to LDS, and
+    // this wave's part of the row maxima that set the 16-bit operand scales
+    {
+        const float is = sIS[col], ig = sIG[col];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * rt + 4 * lj + i;
+                if (r < L) dv[(int64_t)(c0 + r) * rowQ + hoff + col] = sBeta[r] * dX[rt][i];
+                const float pb = sum16(U[rt][i] * dX[rt][i]);
+                sW[r * LDF + col] = W[rt][i];
+                sDX[r * LDF + col] = dX[rt][i];
+                const float ado = fabsf(sDO[r * LDF + col]), adx = fabsf(dX[rt][i]), aw = fabsf(W[rt][i]);
+                float m[NMX];
+                m[MX_DO] = rowmax16(ado);
+                m[MX_DOS] = rowmax16(ado * is);
+                m[MX_DX] = rowmax16(adx);
+                m[MX_DXS] = rowmax16(adx * is);
+                m[MX_W] = rowmax16(aw);
+                m[MX_WG] = rowmax16(aw * ig);
+                if (lm == 0) {
+                    sDb[wave * C + r] = pb;
+#pragma unroll
+                    for (int a = 0; a < NMX; ++a) sMx[(wave * NMX + a) * C + r] = m[a];
+                }
+            }
+    }
+    __syncthreads();
+    if (tid < NMX * C) {       // row scales: the row maximum into [2^13, 2^14) (1 for fp32 operands)
+        float m = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) m = fmaxf(m, sMx[w * NMX * C + tid]);
+        sRS[tid] = kIn16 ? pow2_scale(m) : 1.f;
+    }
     __syncthreads();
 
-    // ---- 3. contractions over the value columns: key channels cc of this
-    //         wave (tiles ct), S and G rows read from global memory
-    f32x4 dQp[2][2], dXS[2][2], dKh[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) dQp[rt][ct] = dXS[rt][ct] = dKh[rt][ct] = zero4();
-    float dgm[2] = {0.f, 0.f};
+    // ---- 3. contractions over the value columns, on the MFMA type of the
+    //         forward: key channel cc of this lane (wave w: 16 w + lm); S and G
+    //         rows from global memory (the fragment's indices along the row)
+    const int cc = 16 * wave + lm;
+    f32x4 dQp[2], dXS[2], dKh[2];
+    dQp[0] = dQp[1] = dXS[0] = dXS[1] = dKh[0] = dKh[1] = zero4();
+    float dgm = 0.f;
+    const float *rsDOS = sRS + MX_DOS * C, *rsDXS = sRS + MX_DXS * C, *rsWG = sRS + MX_WG * C;
 #pragma unroll 2
-    for (int kb = 0; kb < BD / 16; ++kb) {
-        const int j = 16 * kb + 4 * lj;
-        f32x4 st[2], gt[2];
+    for (int kb = 0; kb < BD / KB; ++kb) {
+        typename Mo::frag st, gt;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int cc = 32 * wave + 16 * ct + lm;
-            st[ct] = Sg ? *reinterpret_cast<const f32x4 *>(Sg + (int64_t)cc * BD + j) : zero4();
-            gt[ct] = *reinterpret_cast<const f32x4 *>(Gg + (int64_t)cc * BD + j);
-            dgm[ct] += dot4(st[ct], gt[ct]);
+        for (int gi = 0; gi < NG; ++gi) {
+            const int j = F::base(kb * KB, lj, gi);
+            typedef typename std::conditional<kIn16, f16x4, f32x4>::type V4;
+            const V4 sv = *reinterpret_cast<const V4 *>(Sg + (int64_t)cc * BD + j);
+            const V4 gv = *reinterpret_cast<const V4 *>(Gg + (int64_t)cc * BD + j);
+            const f32x4 isv = ld4(sIS + j), igv = ld4(sIG + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                st[4 * gi + e] = sv[e];
+                gt[4 * gi + e] = gv[e];
+                dgm += (float)sv[e] * isv[e] * ((float)gv[e] * igv[e]);
+            }
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int r = 16 * rt + lm;
-            const f32x4 ado = ld4(sDO + r * LDF + j), adx = ld4(sDX + r * LDF + j), aw = ld4(sW + r * LDF + j);
+            f32x4 ado[NG], adx[NG], aw[NG];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                dQp[rt][ct] = Mf::mma(ado, st[ct], dQp[rt][ct]);
-                dXS[rt][ct] = Mf::mma(adx, st[ct], dXS[rt][ct]);
-                dKh[rt][ct] = Mf::mma(aw, gt[ct], dKh[rt][ct]);
+            for (int gi = 0; gi < NG; ++gi) {
+                const int j = F::base(kb * KB, lj, gi);
+                const f32x4 isv = ld4(sIS + j), igv = ld4(sIG + j);
+                ado[gi] = ld4(sDO + r * LDF + j) * isv;
+                adx[gi] = ld4(sDX + r * LDF + j) * isv;
+                aw[gi] = ld4(sW + r * LDF + j) * igv;
             }
+            dQp[rt] = Mo::mma(F::make(ado, rsDOS[r]), st, dQp[rt]);
+            dXS[rt] = Mo::mma(F::make(adx, rsDXS[r]), st, dXS[rt]);
+            dKh[rt] = Mo::mma(F::make(aw, rsWG[r]), gt, dKh[rt]);
         }
     }
+    dgm = sum_rows4(dgm);                                 // (G (.) S) 1 of channel cc
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) dgm[ct] = sum_rows4(dgm[ct]);   // (G (.) S) 1 of channel cc
-    // dP and dN: waves 0, 1 the diagonal blocks, wave 2 the off-diagonal one
-    // (they overwrite P, P^T, T, T^T, whose last reads were in part 2)
-    if (wave < 3) {
-        const int rb = wave == 0 ? 0 : 16, ib = wave == 1 ? 16 : 0;
-        const bool diag = wave < 2;
-        f32x4 accP = zero4(), accN = zero4();
-#pragma unroll 2
-        for (int kb = 0; kb < BD / 16; ++kb) {
-            const int j = 16 * kb + 4 * lj;
-            const f32x4 bw = ld4(sW + (ib + lm) * LDF + j);
-            accP = Mf::mma(ld4(sDO + (rb + lm) * LDF + j), bw, accP);
-            accN = Mf::mma(ld4(sDX + (rb + lm) * LDF + j), bw, accN);
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {                     // undo the row scales
+            const int r = 16 * rt + 4 * lj + i;
+            dQp[rt][i] *= pow2_inv(rsDOS[r]);
+            dXS[rt][i] *= pow2_inv(rsDXS[r]);
+            dKh[rt][i] *= pow2_inv(rsWG[r]);
         }
+    // dP (waves 0-2) and dN (waves 3-5) by block x, B = W rows with their own
+    // row scales; they overwrite P, P^T, T, T^T, whose last reads were in part 2
+    if (wave < 6) {
+        const int x = wave % 3;
+        const bool isN = wave >= 3, diag = x < 2;
+        const int rb = x == 0 ? 0 : 16, ib = x == 1 ? 16 : 0;
+        const float *rowA = (isN ? sDX : sDO) + (rb + lm) * LDF;
+        const float ra = sRS[(isN ? MX_DX : MX_DO) * C + rb + lm], rw = sRS[MX_W * C + ib + lm];
+        f32x4 acc = zero4();
+#pragma unroll 2
+        for (int kb = 0; kb < BD / KB; ++kb) {
+            f32x4 a[NG], b[NG];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int j = F::base(kb * KB, lj, gi);
+                a[gi] = ld4(rowA + j);
+                b[gi] = ld4(sW + (ib + lm) * LDF + j);
+            }
+            acc = Mo::mma(F::make(a, ra), F::make(b, rw), acc);
+        }
+        const float iw = pow2_inv(sRS[MX_W * C + ib + lm]);
+        float pb[4];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int rr = rb + 4 * lj + ii, cc = ib + lm;
-            const float dp = (!diag || cc <= rr) ? accP[ii] : 0.f;
-            const float dn = (!diag || cc < rr) ? -accN[ii] : 0.f;
-            const float da = sBeta[rr] * dn;
-            sdP[rr * LDX + cc] = dp;
-            sdPT[cc * LDX + rr] = dp;
-            sdA[rr * LDX + cc] = da;
-            sdAT[cc * LDX + rr] = da;
-            const float pb = sum16(dn * sA[rr * LDX + cc]);
-            if (lm == 0) sDb[(4 + wave) * C + rr] = pb;
+            const int rr = rb + 4 * lj + ii, c2 = ib + lm;
+            const float val = acc[ii] * pow2_inv(sRS[(isN ? MX_DX : MX_DO) * C + rr]) * iw;
+            if (!isN) {
+                const float dp = (!diag || c2 <= rr) ? val : 0.f;
+                sdP[rr * LDX + c2] = dp;
+                sdPT[c2 * LDX + rr] = dp;
+                pb[ii] = 0.f;
+            } else {
+                const float dn = (!diag || c2 < rr) ? -val : 0.f;
+                const float da = sBeta[rr] * dn;
+                sdA[rr * LDX + c2] = da;
+                sdAT[c2 * LDX + rr] = da;
+                pb[ii] = sum16(dn * sA[rr * LDX + c2]);
+            }
+        }
+        if (isN && lm == 0) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) sDb[(NW + x) * C + rb + 4 * lj + ii] = pb[ii];
         }
     } else {
-        for (int e = lane; e < 256; e += 64) {
-            const int rr = e >> 4, cc = 16 + (e & 15);
-            sdP[rr * LDX + cc] = 0.f;
-            sdPT[cc * LDX + rr] = 0.f;
-            sdA[rr * LDX + cc] = 0.f;
-            sdAT[cc * LDX + rr] = 0.f;
+        for (int e = tid - 384; e < 256; e += 128) {
+            const int rr = e >> 4, c2 = 16 + (e & 15);
+            sdP[rr * LDX + c2] = 0.f;
+            sdPT[c2 * LDX + rr] = 0.f;
+            sdA[rr * LDX + c2] = 0.f;
+            sdAT[c2 * LDX + rr] = 0.f;
         }
-        if (lane < 16) {      // rows that a block's dbeta part does not cover
-            sDb[4 * C + 16 + lane] = 0.f;
-            sDb[5 * C + lane] = 0.f;
-            sDb[6 * C + lane] = 0.f;
-            sDb[7 * C + lane] = 0.f;
-            sDb[7 * C + 16 + lane] = 0.f;
+        if (tid - 384 < 16) {     // rows that a block's dbeta part does not cover
+            const int e = tid - 384;
+            sDb[NW * C + 16 + e] = 0.f;
+            sDb[(NW + 1) * C + e] = 0.f;
+            sDb[(NW + 2) * C + e] = 0.f;
+            sDb[(NW + 3) * C + e] = 0.f;
+            sDb[(NW + 3) * C + 16 + e] = 0.f;
         }
     }
     __syncthreads();
 
-    // ---- 4. token sums weighted by E, and the per-element results
-#pragma unroll 1
-    for (int ct = 0; ct < 2; ++ct) {
-        const int c = 32 * wave + 16 * ct + lm;
+    // ---- 4. token sums weighted by E, and the per-element results (channel cc)
+    {
+        const int c = cc;
         auto gm = [&](int t) { return sGm[t * LDG + c]; };
         auto kv = [&](int t) { return to_f(sK[t * LDI + c]); };
         auto qv = [&](int t) { return to_f(sQ[t * LDI + c]); };
@@ -475,11 +579,11 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
         const double g15 = gm(15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t0_ = 4 * lj + e, t1_ = 16 + 4 * lj + e;
-            Kco[e] = kv(t0_) * __expf((float)(g15 - gm(t0_)));
-            const float ro = __expf((float)(gm(t1_) - g15));
-            Kro[e] = kv(t1_) * ro;
-            Qro[e] = qv(t1_) * ro;
+            const int ta = 4 * lj + e, tb = 16 + 4 * lj + e;
+            Kco[e] = kv(ta) * __expf((float)(g15 - gm(ta)));
+            const float ro = __expf((float)(gm(tb) - g15));
+            Kro[e] = kv(tb) * ro;
+            Qro[e] = qv(tb) * ro;
         }
         f32x4 q2d[2], kr2d[2], kc2d[2];
 #pragma unroll
@@ -501,9 +605,9 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * rt + 4 * lj + ii;
-                extra += kv(r) * dKh[rt][ct][ii] * __expf((float)(gl - gm(r)));
+                extra += kv(r) * dKh[rt][ii] * __expf((float)(gl - gm(r)));
             }
-        extra = sum_rows4(extra) + dgm[ct] * __expf((float)gl);
+        extra = sum_rows4(extra) + dgm * __expf((float)gl);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -521,9 +625,9 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                     dkc2 += __expf((float)(g15 - gr)) * kc2o[ii];
                 }
                 const float eG = __expf((float)gr), eGn = __expf((float)(gl - gr));
-                const float dq_ = dQp[rt][ct][ii] * eG + dq2;
-                const float dkrow = -sBeta[r] * dXS[rt][ct][ii] * eG + dkr2;
-                const float dkcol = dKh[rt][ct][ii] * eGn + dkc2;
+                const float dq_ = dQp[rt][ii] * eG + dq2;
+                const float dkrow = -sBeta[r] * dXS[rt][ii] * eG + dkr2;
+                const float dkcol = dKh[rt][ii] * eGn + dkc2;
                 const float kr = kv(r);
                 float dG = qv(r) * dq_ + kr * dkrow - kr * dkcol;
                 if (r == L - 1) dG += extra;
@@ -548,27 +652,29 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
         if (r < L) {
             float s = 0.f;
 #pragma unroll
-            for (int w = 0; w < 8; ++w) s += sDb[w * C + r];
+            for (int w = 0; w < NDB; ++w) s += sDb[w * C + r];
             dbeta[(int64_t)(c0 + r) * H + h] = s;
         }
     }
 }
-
 }  // namespace kda
 
 // Per (chunk, head) gradients of the chunk form (kda_bwd_chunk_kernel): S at
-// every chunk start in snaps (a sequence's first chunk: initial_state, or zero
-// if nullptr), the gradient at every chunk end in gchunk, both [chunks][H][BD][BD].
+// every chunk start in snaps and the gradient at every chunk end in gchunk,
+// both [chunks][H][BD][BD] as the chains store them (bf16: fp16 values with
+// column scales [chunks][H][BD] in snap_scale / g_scale; fp32: fp32).
 extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const void *v, const float *g,
-                                           const float *beta, const void *dout, const float *init, const int32_t *cu,
-                                           const int32_t *chunk_off, int64_t max_chunks, const float *snaps,
-                                           const float *gchunk, int32_t N, int32_t T_tot, int32_t H, float *dq,
-                                           float *dk, float *dv, float *dg, float *dbeta, hipStream_t stream)
+                                           const float *beta, const void *dout, const int32_t *cu,
+                                           const int32_t *chunk_off, int64_t max_chunks, const void *snaps,
+                                           const float *snap_scale, const void *gchunk, const float *g_scale,
+                                           int32_t N, int32_t T_tot, int32_t H, float *dq, float *dk, float *dv,
+                                           float *dg, float *dbeta, hipStream_t stream)
 {
     using namespace kda;
     const int64_t grid = max_chunks * H;
     if (grid <= 0 || N <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (bf16 && (!snap_scale || !g_scale)) return hipErrorInvalidValue;
     if (bf16) {
         auto kern = kda_bwd_chunk_kernel<bf16_t>;
         static std::atomic<uint64_t> lds_set{0};
@@ -576,8 +682,8 @@ extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *
             return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(bc::NT), bc::Cfg<bf16_t>::bytes, stream,
                            static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
-                           static_cast<const bf16_t *>(v), g, beta, static_cast<const bf16_t *>(dout), init, cu,
-                           chunk_off, snaps, gchunk, N, T_tot, H, dq, dk, dv, dg, dbeta);
+                           static_cast<const bf16_t *>(v), g, beta, static_cast<const bf16_t *>(dout), cu, chunk_off,
+                           snaps, snap_scale, gchunk, g_scale, N, T_tot, H, dq, dk, dv, dg, dbeta);
     } else {
         auto kern = kda_bwd_chunk_kernel<float>;
         static std::atomic<uint64_t> lds_set{0};
@@ -585,8 +691,8 @@ extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *
             return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(bc::NT), bc::Cfg<float>::bytes, stream,
                            static_cast<const float *>(q), static_cast<const float *>(k),
-                           static_cast<const float *>(v), g, beta, static_cast<const float *>(dout), init, cu,
-                           chunk_off, snaps, gchunk, N, T_tot, H, dq, dk, dv, dg, dbeta);
+                           static_cast<const float *>(v), g, beta, static_cast<const float *>(dout), cu, chunk_off,
+                           snaps, snap_scale, gchunk, g_scale, N, T_tot, H, dq, dk, dv, dg, dbeta);
     }
     return hipGetLastError();
 }

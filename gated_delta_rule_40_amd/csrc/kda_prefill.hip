@@ -170,6 +170,7 @@ struct SegArgs {
     int32_t prep_group;         // chunk-operand pass: consecutive chunks per workgroup (1 .. PREP_GROUP)
     int32_t img_slots;          // chunk-operand pass: image slots per head (> chunks of valid input)
     f32x4 *gimg;                // MODE_PREPG: gradient images, slots as for img
+    float *snap_scale;          // kda_chain_kernel state stores, 16-bit inputs: [chunks][H][dv] column scales
 };
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
@@ -1269,6 +1270,38 @@ static hipError_t launch_prefill_t(const void *q, const void *k, const void *v, 
 }
 
 
+// Chunk-boundary states for the backward (stores of kda_chain_kernel with
+// SNAP and of kda_grad_chain_kernel): this wave's NCT column tiles of a
+// state carried scaled per column (X~ = X s, MFMA accumulator layout) at dst
+// ([DK][dv] row-major).  fp32 inputs: X in fp32 (s = 1).  16-bit inputs: X~
+// itself in fp16 -- every column of X~ lies below 2^15 -- and s per column in
+// scale[col], so that the reader gets fp16 operands with exact power-of-two
+// column scales and half the bytes.
+template <bool F16, int NCT>
+__device__ __forceinline__ void store_scaled_state(void *dst, float *scale, const f32x4 (&X)[NCT][DK / 16],
+                                                   const float (&s)[NCT], int col0, int dv, int lj, int lm)
+{
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = col0 + 16 * ct;
+        if constexpr (F16) {
+            f16_t *d = static_cast<f16_t *>(dst);
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[(int64_t)(16 * r + 4 * lj + i) * dv + col] = from_f<f16_t>(X[ct][r][i]);
+            if (lj == 0) scale[col] = s[ct];
+        } else {
+            float *d = static_cast<float *>(dst);
+            const float inv = pow2_inv(s[ct]);
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[(int64_t)(16 * r + 4 * lj + i) * dv + col] = X[ct][r][i] * inv;
+        }
+    }
+}
+
 // ------------------------------------------------------------ state chain
 // The state-dependent pass over chunk-operand images: one workgroup per
 // (unit, block of BV value columns) as in the fused kernel, walking the unit's
@@ -1506,6 +1539,17 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
             run(ci);
         }
     } else {
+    // SNAP: the state at the start of a sequence's first chunk too (the
+    // initial state, scaled as carried), so every chunk's start state is stored
+    auto snap_at = [&](int64_t gc) -> void * {
+        return Q::P::kIn16 ? static_cast<void *>(reinterpret_cast<f16_t *>(seg.snap) + (gc * num_heads + h) * DK * dv)
+                           : static_cast<void *>(seg.snap + (gc * num_heads + h) * DK * dv);
+    };
+    if constexpr (SNAP) {
+        if ((sflags & SEG_FIRST) && nch > 0)
+            store_scaled_state<Q::P::kIn16, NCT>(snap_at(gc0), seg.snap_scale + (gc0 * num_heads + h) * dv, S, sS,
+                                                 dv0 + vcol, dv, lj, lm);
+    }
     if (nch > 0) {
         load(0);
         stage(0, 0);
@@ -1540,18 +1584,9 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         }
         if constexpr (SNAP) {
             const int64_t gc = gc0 + ci + 1;            // the sequence's next chunk
-            if (gc < (int64_t)seg.chunk_off[n + 1]) {
-                float *dst = seg.snap + (gc * num_heads + h) * DK * dv;
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const float inv = pow2_inv(sS[ct]);
-#pragma unroll
-                    for (int r = 0; r < DK / 16; ++r)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            dst[(int64_t)(16 * r + 4 * lj + i) * dv + colc[ct]] = S[ct][r][i] * inv;
-                }
-            }
+            if (gc < (int64_t)seg.chunk_off[n + 1])
+                store_scaled_state<Q::P::kIn16, NCT>(snap_at(gc), seg.snap_scale + (gc * num_heads + h) * dv, S, sS,
+                                                     dv0 + vcol, dv, lj, lm);
         }
         if constexpr (SB) __syncthreads();       // every wave is done with the buffer
         stage(min(ci + 1, nch - 1), SB ? 0 : (ci + 1) & 1);
@@ -1815,15 +1850,16 @@ struct GChainCfg {
 // combine then gives every segment's entering gradient); segments that are a
 // sequence's first are skipped.  Otherwise from g_end (the gradient at the
 // segment's end), storing the gradient at the end of every chunk at that
-// chunk's global index in g_chunk ([chunks][H][DK][DV]) and, for a sequence's
-// first segment, the gradient at the sequence start in dinit (may be nullptr).
-// The stored values are G~ / sG, exact.
+// chunk's global index in g_chunk ([chunks][H][DK][DV], as store_scaled_state
+// writes it, column scales in g_scale) and, for a sequence's first segment,
+// the gradient at the sequence start in dinit (may be nullptr).  dinit and the
+// summaries are fp32, G~ / sG (exact).
 template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB>
 __global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
     const TIn *dout, const int32_t *__restrict__ cu_seqlens, int32_t num_seqs, int32_t total_tokens,
     int32_t num_heads, const int32_t *__restrict__ plan, int32_t num_segs, const int32_t *__restrict__ sched,
-    const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, float *g_chunk,
-    float *dinit, float *g0_out)
+    const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, void *g_chunk,
+    float *g_scale, float *dinit, float *g0_out)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     typedef typename Q::OpT OpT;
@@ -1927,7 +1963,12 @@ __global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
         const int ci = nch - 1 - k;
         __syncthreads();                          // chunk ci staged; (double buffer) the previous one done
         load(max(ci - 1, 0));                     // unconditional, see the forward chain
-        if constexpr (!SUMMARY) store_g(g_chunk + ((gc0 + ci) * H + h) * DK * DK);   // G at the chunk's end
+        if constexpr (!SUMMARY) {                 // G at the chunk's end
+            const int64_t o = (gc0 + ci) * H + h;
+            void *dst = Q::P::kIn16 ? static_cast<void *>(static_cast<f16_t *>(g_chunk) + o * DK * DK)
+                                    : static_cast<void *>(static_cast<float *>(g_chunk) + o * DK * DK);
+            store_scaled_state<Q::P::kIn16, NCT>(dst, g_scale + o * DK, G, sG, vcol, DK, lj, lm);
+        }
         const unsigned char *base = smem + (SB ? 0 : (k & 1) * Q::BUF);
         grad_chunk<TIn, C, LDV, NCT>(
             G, sG, reinterpret_cast<const OpT *>(base + Q::offKh), reinterpret_cast<const OpT *>(base + Q::offNKpT),
@@ -1945,8 +1986,8 @@ __global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
 template <typename TIn, int C, int NW, int NCT, bool SB>
 static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int32_t *cu, int32_t N, int32_t T_tot,
                                       int32_t H, const int32_t *plan, int32_t num_segs, const int32_t *sched,
-                                      const int32_t *chunk_off, const void *gimg, const float *g_end, float *g_chunk,
-                                      float *dinit, float *g0_out, hipStream_t stream)
+                                      const int32_t *chunk_off, const void *gimg, const float *g_end, void *g_chunk,
+                                      float *g_scale, float *dinit, float *g0_out, hipStream_t stream)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     auto kern = summary ? kda_grad_chain_kernel<TIn, C, NW, NCT, true, SB>
@@ -1959,7 +2000,7 @@ static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int3
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(dout), cu,
                        N, T_tot, H, plan, num_segs, sched, chunk_off, static_cast<const f32x4 *>(gimg), g_end,
-                       g_chunk, dinit, g0_out);
+                       g_chunk, g_scale, dinit, g0_out);
     return hipGetLastError();
 }
 
@@ -2366,19 +2407,25 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
 
 // State-chain pass over the images, value blocks of dv_block columns (64,
 // 128, or 256 for a summary's value + transition columns in one block);
-// plan, mode, seg_init and seg_out as for kda_launch_prefill.
+// plan, mode, seg_init and seg_out as for kda_launch_prefill.  snap (may be
+// nullptr): the state at every chunk start, [chunks][H][DK][dv] as
+// store_scaled_state writes it (bf16: fp16 values, column scales in
+// snap_scale [chunks][H][dv]).
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, float *snap, const int32_t *init_seq_seg,
-                                       int32_t init_unit, int32_t init_units, hipStream_t stream)
+                                       const int32_t *sched, void *snap, float *snap_scale,
+                                       const int32_t *init_seq_seg, int32_t init_unit, int32_t init_units,
+                                       hipStream_t stream)
 {
     using namespace kda;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
+    if (snap && bf16 && !snap_scale) return hipErrorInvalidValue;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
-                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)), mode == SEG_SUMMARY ? nullptr : snap, 0, 0,
-                   sched, init_seq_seg, init_unit, init_units, 0};
+                   const_cast<f32x4 *>(static_cast<const f32x4 *>(img)),
+                   mode == SEG_SUMMARY ? nullptr : static_cast<float *>(snap), 0, 0, sched, init_seq_seg, init_unit,
+                   init_units, 0, 0, nullptr, snap_scale};
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
@@ -2396,23 +2443,25 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
 // State-gradient chain over the gradient images (see kda_grad_chain_kernel):
 // summary = 1 writes G^0 of every segment but a sequence's first to g0_out
 // [num_segs][H][DK][DK]; summary = 0 runs every segment from g_end (same
-// layout), storing the gradient at every chunk end in g_chunk and d(initial
-// state) in dinit.
+// layout), storing the gradient at every chunk end in g_chunk (bf16: fp16
+// values with column scales in g_scale [chunks][H][DK]; fp32: fp32) and
+// d(initial state) in dinit.
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
-                                            const float *g_end, float *g_chunk, float *dinit, float *g0_out,
-                                            hipStream_t stream)
+                                            const float *g_end, void *g_chunk, float *g_scale, float *dinit,
+                                            float *g0_out, hipStream_t stream)
 {
     using namespace kda;
-    if (summary ? !g0_out : (!g_end || !g_chunk)) return hipErrorInvalidValue;
+    if (summary ? !g0_out : (!g_end || !g_chunk || (bf16 && !g_scale))) return hipErrorInvalidValue;
     // bf16: double buffered (about 87 KB); fp32 images are twice as large: one buffer
     if (bf16)
         return launch_grad_chain_t<bf16_t, 32, 4, 2, false>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs,
-                                                            sched, chunk_off, gimg, g_end, g_chunk, dinit, g0_out,
-                                                            stream);
+                                                            sched, chunk_off, gimg, g_end, g_chunk, g_scale, dinit,
+                                                            g0_out, stream);
     return launch_grad_chain_t<float, 32, 4, 2, true>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs, sched,
-                                                      chunk_off, gimg, g_end, g_chunk, dinit, g0_out, stream);
+                                                      chunk_off, gimg, g_end, g_chunk, g_scale, dinit, g0_out,
+                                                      stream);
 }
 
 extern "C" size_t kda_chunk_image_bytes(int bf16)
