@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kda.h"
@@ -452,7 +453,8 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
 namespace {
 
 struct BwdLayout {
-    size_t plan, sched, seq_seg, chunk_off, img, gimg, snaps, gchunk, sscale, gscale, fsum, bsum, seg_dsend, total;
+    size_t plan, sched, seq_seg, chunk_off, img, gimg, snaps, gchunk, sscale, gscale, fsum, bsum, seg_init, seg_dsend,
+        total;
     int32_t max_chunks, max_segs, seg_len;
 };
 
@@ -474,7 +476,8 @@ int32_t bwd_seg_len(int32_t T, int32_t H)
 // starts and state gradients at chunk ends [max_chunks][H][dk][dv] (fp32, or
 // fp16 with column scales [max_chunks][H][dv] each for bf16 inputs); forward
 // summaries [max_segs][H][dk][dv + dk]; gradient summaries [max_segs][H][dk][dv];
-// entering states, then entering gradients [max_segs][H][dk][dv].
+// entering states and entering gradients [max_segs][H][dk][dv] (the two
+// strands of the pipeline run side by side, so each has its own).
 bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
 {
     const int32_t seg_len = bwd_seg_len(T, H);
@@ -498,9 +501,48 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     lay->gscale = align256(lay->sscale + sizeof(float) * (size_t)chunks * H * kHeadDim);
     lay->fsum = align256(lay->gscale + sizeof(float) * (size_t)chunks * H * kHeadDim);
     lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 2 * S);
-    lay->seg_dsend = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
+    lay->seg_init = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
+    lay->seg_dsend = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * S);
     lay->total = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
     return true;
+}
+
+// A second stream per device for the backward: its two strands (states of
+// the forward, gradients of the state) are chains of small launches that
+// leave most compute units idle, so they run side by side -- forked from and
+// joined back into the caller's stream with events, which also works under
+// stream capture.  Created on first use (default priority, non-blocking),
+// kept until the process ends; the enqueue sequence of one call holds the
+// device's mutex, so calls from several host threads do not interleave their
+// event records.  If creation fails, everything runs on the caller's stream.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+    bool ready = false;
+    std::mutex use;
+};
+SideStream g_side[64];
+std::mutex g_side_init;
+
+SideStream *side_stream()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    SideStream &ss = g_side[dev];
+    std::lock_guard<std::mutex> lk(g_side_init);
+    if (!ss.ready) {
+        bool ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; i < 3 && ok; ++i) ok = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming) == hipSuccess;
+        if (!ok) {
+            for (int i = 0; i < 3; ++i)
+                if (ss.ev[i]) (void)hipEventDestroy(ss.ev[i]), ss.ev[i] = nullptr;
+            if (ss.stream) (void)hipStreamDestroy(ss.stream), ss.stream = nullptr;
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ss.ready = true;
+    }
+    return &ss;
 }
 
 }  // namespace
@@ -551,6 +593,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     void *snaps = ws + lay.snaps;
     float *fsum = reinterpret_cast<float *>(ws + lay.fsum);
     float *bsum = reinterpret_cast<float *>(ws + lay.bsum);
+    float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
     float *seg_dsend = reinterpret_cast<float *>(ws + lay.seg_dsend);
     void *img = ws + lay.img;
     void *gimg = ws + lay.gimg;
@@ -558,6 +601,21 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     float *sscale = reinterpret_cast<float *>(ws + lay.sscale);
     float *gscale = reinterpret_cast<float *>(ws + lay.gscale);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // Two strands after the chunk operands, on the caller's stream s and the
+    // side stream s2 (s itself when there is none):
+    //   s:  forward summaries -> forward combine -> forward states at chunk starts
+    //   s2: gradient summaries -> (forward summaries done) reverse combine ->
+    //       state gradients at chunk ends
+    // then, on s once both are done, the per-chunk gradients.
+    SideStream *ss = side_stream();
+    std::unique_lock<std::mutex> lk;
+    if (ss) lk = std::unique_lock<std::mutex>(ss->use);
+    hipStream_t s2 = ss ? ss->stream : s;
+    auto fork = [&](int i, hipStream_t from, hipStream_t to) -> hipError_t {
+        if (!ss) return hipSuccess;
+        hipError_t r = hipEventRecord(ss->ev[i], from);
+        return r == hipSuccess ? hipStreamWaitEvent(to, ss->ev[i], 0) : r;
+    };
     // segments and chunk numbering; no segment is marked last, so the forward
     // summaries include every segment's transition
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
@@ -568,28 +626,36 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (e == hipSuccess)
         e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
                                   lay.max_chunks, img, gimg, s);
-    // forward: the state at every chunk start, by the context-parallel
-    // pipeline with state stores and no outputs
-    if (e == hipSuccess)
+    bool forked = false;
+    if (e == hipSuccess) {
+        e = fork(0, s, s2);
+        forked = e == hipSuccess;
+    }
+    if (e == hipSuccess)   // s2: gradient summaries G^0 of every segment but a sequence's first
+        e = kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
+                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, s2);
+    if (e == hipSuccess)   // s: forward summaries [S^0 | M] of every segment
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
                              nullptr, nullptr, nullptr, 0, 0, s);
-    if (e == hipSuccess)
-        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_dsend, 0, nullptr,
-                                  nullptr, nullptr, 0, s);
-    if (e == hipSuccess)
-        e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
-                             nullptr, nullptr, plan, lay.max_segs, 0, seg_dsend, nullptr, chunk_off, img, sched,
-                             snaps, sscale, nullptr, 0, 0, s);
-    if (e == hipSuccess)   // gradient summaries G^0 of every segment but a sequence's first
-        e = kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, s);
-    if (e == hipSuccess)   // the gradient entering every segment at its end, with R_s = M_s^T
+    if (e == hipSuccess) e = fork(1, s, s2);
+    if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
-                                  fsum, 1, s);
-    if (e == hipSuccess)   // the gradient at every chunk end, and d(initial state)
+                                  fsum, 1, s2);
+    if (e == hipSuccess)   // s2: the gradient at every chunk end, and d(initial state)
         e = kda_launch_grad_chain(bf16, 0, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, s);
+                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, s2);
+    if (e == hipSuccess)   // s: the state entering every segment
+        e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_init, 0, nullptr,
+                                  nullptr, nullptr, 0, s);
+    if (e == hipSuccess)   // s: the state at every chunk start
+        e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
+                             nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
+                             snaps, sscale, nullptr, 0, 0, s);
+    if (forked) {          // join: s waits for s2 (also after a failed launch)
+        const hipError_t j = fork(2, s2, s);
+        if (e == hipSuccess) e = j;
+    }
     if (e == hipSuccess)   // every chunk's gradients of q, k, v, g and beta
         e = kda_launch_bwd_chunk(bf16, q, k, v, g, beta, dout, cu_seqlens, chunk_off, lay.max_chunks, snaps, sscale,
                                  gchunk, gscale, num_seqs, total_tokens, num_heads, dq, dk_out, dv_out, dg, dbeta, s);
