@@ -35,21 +35,22 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, void *snap, float *snap_scale,
-                                       const int32_t *init_seq_seg, int32_t init_unit, int32_t init_units,
-                                       hipStream_t stream);
+                                       const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
+                                       float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
+                                       int32_t init_units, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
                                             const float *g_end, void *g_chunk, float *g_scale, float *dinit,
-                                            float *g0_out, hipStream_t stream);
-extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const void *v, const float *g,
+                                            float *g0_out, float *dx_chunk, hipStream_t stream);
+extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const float *g,
                                            const float *beta, const void *dout, const int32_t *cu,
                                            const int32_t *chunk_off, int64_t max_chunks, const void *snaps,
                                            const float *snap_scale, const void *gchunk, const float *g_scale,
-                                           int32_t N, int32_t T_tot, int32_t H, float *dq, float *dk, float *dv,
-                                           float *dg, float *dbeta, hipStream_t stream);
+                                           const float *uw_u, const float *uw_w, const float *dx_chunk, int32_t N,
+                                           int32_t T_tot, int32_t H, float *dq, float *dk, float *dv, float *dg,
+                                           float *dbeta, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const void *k, const void *v,
                                                const float *g, const float *beta, const int32_t *cu,
                                                const int32_t *num_tokens, const float *state_in,
@@ -357,14 +358,14 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
-                             nullptr, nullptr, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, 0, 0, s);
     if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
                                   seq_order, nullptr, 0, s);
     if (e == hipSuccess)   // outputs and final states, each segment from the entering state of its first unit
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
-                             nullptr, useq_seg, lay.unit_len, lay.max_units, s);
+                             nullptr, nullptr, nullptr, useq_seg, lay.unit_len, lay.max_units, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -453,8 +454,8 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
 namespace {
 
 struct BwdLayout {
-    size_t plan, sched, seq_seg, chunk_off, img, gimg, snaps, gchunk, sscale, gscale, fsum, bsum, seg_init, seg_dsend,
-        total;
+    size_t plan, sched, seq_seg, chunk_off, img, gimg, snaps, gchunk, sscale, gscale, uw_u, uw_w, dx, fsum, bsum,
+        seg_init, seg_dsend, total;
     int32_t max_chunks, max_segs, seg_len;
 };
 
@@ -474,7 +475,8 @@ int32_t bwd_seg_len(int32_t T, int32_t H)
 // and the first segment [N+1] and first chunk [N+1] of each sequence; the
 // chunk images and the gradient images (same slots); forward states at chunk
 // starts and state gradients at chunk ends [max_chunks][H][dk][dv] (fp32, or
-// fp16 with column scales [max_chunks][H][dv] each for bf16 inputs); forward
+// fp16 with column scales [max_chunks][H][dv] each for bf16 inputs); every
+// chunk's U, W (forward) and dX (state gradient) [max_chunks][H][32][dv]; forward
 // summaries [max_segs][H][dk][dv + dk]; gradient summaries [max_segs][H][dk][dv];
 // entering states and entering gradients [max_segs][H][dk][dv] (the two
 // strands of the pipeline run side by side, so each has its own).
@@ -499,7 +501,10 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     lay->gchunk = align256(lay->snaps + sizeof(float) * (size_t)chunks * H * S);
     lay->sscale = align256(lay->gchunk + sizeof(float) * (size_t)chunks * H * S);
     lay->gscale = align256(lay->sscale + sizeof(float) * (size_t)chunks * H * kHeadDim);
-    lay->fsum = align256(lay->gscale + sizeof(float) * (size_t)chunks * H * kHeadDim);
+    lay->uw_u = align256(lay->gscale + sizeof(float) * (size_t)chunks * H * kHeadDim);
+    lay->uw_w = align256(lay->uw_u + sizeof(float) * (size_t)chunks * H * kCpChunk * kHeadDim);
+    lay->dx = align256(lay->uw_w + sizeof(float) * (size_t)chunks * H * kCpChunk * kHeadDim);
+    lay->fsum = align256(lay->dx + sizeof(float) * (size_t)chunks * H * kCpChunk * kHeadDim);
     lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 2 * S);
     lay->seg_init = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
     lay->seg_dsend = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * S);
@@ -600,6 +605,9 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     void *gchunk = ws + lay.gchunk;
     float *sscale = reinterpret_cast<float *>(ws + lay.sscale);
     float *gscale = reinterpret_cast<float *>(ws + lay.gscale);
+    float *uw_u = reinterpret_cast<float *>(ws + lay.uw_u);
+    float *uw_w = reinterpret_cast<float *>(ws + lay.uw_w);
+    float *dxc = reinterpret_cast<float *>(ws + lay.dx);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     // Two strands after the chunk operands, on the caller's stream s and the
     // side stream s2 (s itself when there is none):
@@ -633,32 +641,33 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     }
     if (e == hipSuccess)   // s2: gradient summaries G^0 of every segment but a sequence's first
         e = kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, s2);
+                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, nullptr, s2);
     if (e == hipSuccess)   // s: forward summaries [S^0 | M] of every segment
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
-                             nullptr, nullptr, nullptr, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, s);
     if (e == hipSuccess) e = fork(1, s, s2);
     if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
                                   fsum, 1, s2);
-    if (e == hipSuccess)   // s2: the gradient at every chunk end, and d(initial state)
+    if (e == hipSuccess)   // s2: the gradient at every chunk end, every chunk's dX, and d(initial state)
         e = kda_launch_grad_chain(bf16, 0, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, s2);
+                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, dxc, s2);
     if (e == hipSuccess)   // s: the state entering every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_init, 0, nullptr,
                                   nullptr, nullptr, 0, s);
-    if (e == hipSuccess)   // s: the state at every chunk start
+    if (e == hipSuccess)   // s: the state at every chunk start, and every chunk's U and W
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
-                             snaps, sscale, nullptr, 0, 0, s);
+                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, s);
     if (forked) {          // join: s waits for s2 (also after a failed launch)
         const hipError_t j = fork(2, s2, s);
         if (e == hipSuccess) e = j;
     }
     if (e == hipSuccess)   // every chunk's gradients of q, k, v, g and beta
-        e = kda_launch_bwd_chunk(bf16, q, k, v, g, beta, dout, cu_seqlens, chunk_off, lay.max_chunks, snaps, sscale,
-                                 gchunk, gscale, num_seqs, total_tokens, num_heads, dq, dk_out, dv_out, dg, dbeta, s);
+        e = kda_launch_bwd_chunk(bf16, q, k, g, beta, dout, cu_seqlens, chunk_off, lay.max_chunks, snaps, sscale,
+                                 gchunk, gscale, uw_u, uw_w, dxc, num_seqs, total_tokens, num_heads, dq, dk_out,
+                                 dv_out, dg, dbeta, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

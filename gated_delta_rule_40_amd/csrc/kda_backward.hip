@@ -44,14 +44,12 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
 
 // ============================================================ chunk form
 // Per (chunk, head) gradients from the state S at the chunk start and the
-// state gradient G at its end (fp32, [DK][DK] row-major; S from the forward
-// pipeline's chunk-start states, G from the state-gradient chain).  With the
-// chunk form of the forward (kda_prefill.hip; chunk of C tokens, Gamma the
-// cumulative gate, K+ = K (.) e^Gamma, Q+ = Q (.) e^Gamma, K^ = K (.)
-// e^(Gamma_L - Gamma), A, P the decayed Gram tiles, N = Diag(b) A,
-// T = (I + N)^-1, E_ric = e^(Gamma_rc - Gamma_ic)), the chain rule gives
-//     U = V - K+ S,   X = Diag(b) U,   W = T X
-//     dW = K^ G + P^T dO,   dX = T^T dW,   dv = Diag(b) dX
+// state gradient G at its end, with the chunk form of the forward
+// (kda_prefill.hip; chunk of C tokens, Gamma the cumulative gate, K+ = K (.)
+// e^Gamma, Q+ = Q (.) e^Gamma, K^ = K (.) e^(Gamma_L - Gamma), A, P the decayed
+// Gram tiles, N = Diag(b) A, E_ric = e^(Gamma_rc - Gamma_ic)).  The chain rule
+// gives, with U = V - K+ S, W = (I + N)^-1 Diag(b) U (the forward's) and
+// dX = (I + N)^-T (K^ G + P^T dO) (the state-gradient chain's; dv = Diag(b) dX):
 //     dQ+ = dO S^T,   dK+ = -Diag(b) dX S^T,   dK^ = W G^T
 //     dP = tril(dO W^T),   dN = -stril(dX W^T),   dA = Diag(b) dN
 //     dbeta_r = sum_i dN_ri A_ri + sum_c U_rc dX_rc
@@ -61,32 +59,35 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
 //     dGamma = q (.) dq + k (.) (row part) - k (.) (column part), and at the
 //              last token also sum_r k (.) dK^ (.) e^(Gamma_L - Gamma) + (G (.) S) 1 (.) e^Gamma_L
 //     dg = reverse cumulative sum of dGamma over the chunk.
-// Precision: the Gram tiles, (I + N)^-1 and every 32-wide contraction run on
-// fp32 (MFMA 16x16x4 and VALU).  The seven 128-wide contractions (U, K^ G,
-// dQ+, dX S^T, dK^, dP, dN) run on the MFMA type of the forward: fp32 for
-// fp32 inputs; fp16 for 16-bit inputs, with S and G read as the fp16 values
-// and exact power-of-two column scales that the chains carry, and every other
-// operand given an exact power-of-two scale per row (the row maximum lands in
-// [2^13, 2^14)) -- a scale along the contraction index is folded into the
-// other operand, so every product is exact up to the fp16 rounding of its
-// operands.
+// U and W come from the forward pass that stores the chunk-start states, dX
+// from the state-gradient chain (which also writes dv), S and G as those
+// passes store them.  What is left here has no recurrence: one workgroup per
+// (chunk, head).
+// Precision: the Gram tile A and every 32-wide contraction run on fp32 (MFMA
+// 16x16x4 and VALU).  The five 128-wide contractions (dQ+, dX S^T, dK^, dP,
+// dN) run on the MFMA type of the forward: fp32 for fp32 inputs; fp16 for
+// 16-bit inputs, with S and G read as the fp16 values and exact power-of-two
+// column scales that the chains carry, and every other operand given an exact
+// power-of-two scale per row (the row maximum lands in [2^13, 2^14)) -- a
+// scale along the contraction index is folded into the other operand, so every
+// product is exact up to the fp16 rounding of its operands.
 // Gamma is kept in fp64: every decay factor is e^x of a difference of two of
 // its entries, rounded to fp32 only then, so a factor carries the rounding of
 // its own exponent, not that of the (up to 160 in magnitude) cumulative sums.
 // E is factored per 16-token block pair with a reference inside the pair --
 // the middle token of a diagonal block, the block boundary for the
 // off-diagonal one -- so every factor lies in [e^-80, e^40] for g in [-5, 0]:
-// the Gram tiles and the E-weighted token sums are then plain MFMA products of
+// the Gram tile and the E-weighted token sums are then plain MFMA products of
 // factored operands, and a factor applied after a product is at most e^40.
-// Work split: eight waves; in the value-column parts wave w owns columns
-// 16 w .. 16 w + 15, in the key-channel parts channels 16 w .. 16 w + 15.
+// Work split: eight waves; in the key-channel parts wave w owns channels
+// 16 w .. 16 w + 15; token rows are loaded by 16 lanes each (8 columns per lane).
 namespace bc {
 constexpr int C = 32, NW = 8, NT = 64 * NW;
 constexpr int LDG = BD + 2;          // fp64 Gamma rows
 constexpr int LDF = BD + 4;          // fp32 [C][BD] rows
 constexpr int LDX = C + 4;           // fp32 [C][C] rows
-constexpr int NDB = 12;              // partial dbeta slots: 8 value-column waves, 3 dN blocks, 1 spare
-constexpr int NMX = 6;               // row maxima: |dO|, |dO|/sS, |dX|, |dX|/sS, |W|, |W|/sG
+constexpr int NDB = 4;               // partial dbeta slots: U.dX, and the dN (.) A part of 3 blocks
+constexpr int NMX = 6;               // row scales from |dO|, |dO|/sS, |dX|, |dX|/sS, |W|, |W|/sG
 enum { MX_DO = 0, MX_DOS = 1, MX_DX = 2, MX_DXS = 3, MX_W = 4, MX_WG = 5 };
 template <typename T>
 struct Cfg {
@@ -98,16 +99,16 @@ struct Cfg {
     static constexpr uint32_t offW = offDO + sizeof(float) * C * LDF;     // W, later dGamma
     static constexpr uint32_t offDX = offW + sizeof(float) * C * LDF;
     static constexpr uint32_t offA = offDX + sizeof(float) * C * LDF;
-    static constexpr uint32_t offP = offA + sizeof(float) * C * LDX;      // P, later dP
-    static constexpr uint32_t offPT = offP + sizeof(float) * C * LDX;     // P^T, later dP^T
-    static constexpr uint32_t offT = offPT + sizeof(float) * C * LDX;     // T, later dA
-    static constexpr uint32_t offTT = offT + sizeof(float) * C * LDX;     // T^T, later dA^T
-    static constexpr uint32_t offBeta = offTT + sizeof(float) * C * LDX;
+    static constexpr uint32_t offdP = offA + sizeof(float) * C * LDX;
+    static constexpr uint32_t offdPT = offdP + sizeof(float) * C * LDX;
+    static constexpr uint32_t offdA = offdPT + sizeof(float) * C * LDX;
+    static constexpr uint32_t offdAT = offdA + sizeof(float) * C * LDX;
+    static constexpr uint32_t offGp = offdAT + sizeof(float) * C * LDX;   // [3][256] partial Gram tiles
+    static constexpr uint32_t offBeta = offGp + sizeof(float) * 3 * 256;
     static constexpr uint32_t offDb = offBeta + sizeof(float) * C;        // [NDB][C] partial dbeta
     static constexpr uint32_t offIS = offDb + sizeof(float) * NDB * C;    // [BD] 1 / column scale of S
     static constexpr uint32_t offIG = offIS + sizeof(float) * BD;         // [BD] 1 / column scale of G
-    static constexpr uint32_t offMx = offIG + sizeof(float) * BD;         // [NW][NMX][C] partial row maxima
-    static constexpr uint32_t offRS = offMx + sizeof(float) * NW * NMX * C;   // [NMX][C] row scales
+    static constexpr uint32_t offRS = offIG + sizeof(float) * BD;         // [NMX][C] row scales
     static constexpr uint32_t bytes = offRS + sizeof(float) * NMX * C;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
 };
@@ -125,10 +126,8 @@ __device__ __forceinline__ f32x4 exp_diff4(const double *a, const double *b) {
     return f32x4{__expf((float)(a0[0] - b0[0])), __expf((float)(a0[1] - b0[1])), __expf((float)(a1[0] - b1[0])),
                  __expf((float)(a1[1] - b1[1]))};
 }
-__device__ __forceinline__ f32x4 exp4(const double *a) {
-    const f64x2 a0 = *reinterpret_cast<const f64x2 *>(a), a1 = *reinterpret_cast<const f64x2 *>(a + 2);
-    return f32x4{__expf((float)a0[0]), __expf((float)a0[1]), __expf((float)a1[0]), __expf((float)a1[1])};
-}
+__device__ __forceinline__ float max4(const f32x4 &x) { return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])); }
+__device__ __forceinline__ f32x4 abs4(const f32x4 &x) { return f32x4{fabsf(x[0]), fabsf(x[1]), fabsf(x[2]), fabsf(x[3])}; }
 // Contraction indices of element e of lane group j's K-block fragment, in
 // groups of four consecutive ones: group 0 at k0 + 4 j, and for 16-bit
 // operands group 1 at k0 + 16 + 4 j (the layout of kda_device.hpp).
@@ -150,13 +149,14 @@ template <typename OpT> struct Frag {
 
 // S (start state) and G (end gradient) of every chunk: [chunks][H][BD][BD] as
 // the chains store them -- fp16 values with column scales [chunks][H][BD]
-// (OpT = fp16) or fp32 (scales unused).
+// (OpT = fp16) or fp32 (scales unused); U, W, dX: [chunks][H][C][BD] fp32.
 template <typename T>
 __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
+    const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const void *__restrict__ snaps, const float *__restrict__ snap_scale,
-    const void *__restrict__ gchunk, const float *__restrict__ g_scale, int32_t N, int32_t T_tot, int32_t H,
+    const void *__restrict__ gchunk, const float *__restrict__ g_scale, const float *__restrict__ uw_u,
+    const float *__restrict__ uw_w, const float *__restrict__ dx_chunk, int32_t N, int32_t T_tot, int32_t H,
     float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg,
     float *__restrict__ dbeta)
 {
@@ -168,7 +168,6 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     typedef Mma<OpT> Mo;
     typedef Frag<OpT> F;
     constexpr int KB = Mo::KB, NG = F::NG;
-    constexpr float GS = kIn16 ? 32.f : 1.f;   // K+ and K^ enter 16-bit operands times GS (|k| <= 1024)
     constexpr int LDI = Q::LDI;
     extern __shared__ __align__(16) unsigned char smem[];
     T *sK = reinterpret_cast<T *>(smem + Q::offK);
@@ -178,17 +177,17 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     float *sW = reinterpret_cast<float *>(smem + Q::offW);
     float *sDX = reinterpret_cast<float *>(smem + Q::offDX);
     float *sA = reinterpret_cast<float *>(smem + Q::offA);
-    float *sP = reinterpret_cast<float *>(smem + Q::offP);
-    float *sPT = reinterpret_cast<float *>(smem + Q::offPT);
-    float *sT = reinterpret_cast<float *>(smem + Q::offT);
-    float *sTT = reinterpret_cast<float *>(smem + Q::offTT);
+    float *sdP = reinterpret_cast<float *>(smem + Q::offdP);
+    float *sdPT = reinterpret_cast<float *>(smem + Q::offdPT);
+    float *sdA = reinterpret_cast<float *>(smem + Q::offdA);
+    float *sdAT = reinterpret_cast<float *>(smem + Q::offdAT);
+    float *sGp = reinterpret_cast<float *>(smem + Q::offGp);
     float *sBeta = reinterpret_cast<float *>(smem + Q::offBeta);
     float *sDb = reinterpret_cast<float *>(smem + Q::offDb);
     float *sIS = reinterpret_cast<float *>(smem + Q::offIS);
     float *sIG = reinterpret_cast<float *>(smem + Q::offIG);
-    float *sMx = reinterpret_cast<float *>(smem + Q::offMx);
     float *sRS = reinterpret_cast<float *>(smem + Q::offRS);
-    float *sdP = sP, *sdPT = sPT, *sdA = sT, *sdAT = sTT, *sDG = sW;
+    float *sDG = sW;
 
     // ---- workgroup -> (chunk, head); the chunk's sequence by binary search
     const int64_t gc = blockIdx.x / H;
@@ -211,259 +210,185 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     const int64_t unit = gc * H + h;
     const OpT *Sg = static_cast<const OpT *>(snaps) + unit * BD * BD;
     const OpT *Gg = static_cast<const OpT *>(gchunk) + unit * BD * BD;
+    // S and G rows of this lane's key channel for part 3, loaded now so that
+    // they arrive during parts 0-1 (fragment order: K-block, group)
+    typedef typename std::conditional<kIn16, f16x4, f32x4>::type V4;
+    const int cc = 16 * wave + lm;
+    V4 spre[BD / KB][NG], gpre[BD / KB][NG];
+#pragma unroll
+    for (int kb = 0; kb < BD / KB; ++kb)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int j = F::base(kb * KB, lj, gi);
+            spre[kb][gi] = *reinterpret_cast<const V4 *>(Sg + (int64_t)cc * BD + j);
+            gpre[kb][gi] = *reinterpret_cast<const V4 *>(Gg + (int64_t)cc * BD + j);
+        }
+    asm volatile("" ::: "memory");                        // keeps the loads here
 
-    // ---- 0. the chunk's q, k (input type), dO (fp32), beta, Gamma (fp64) and
-    //         the inverse column scales of S and G; rows past the chunk's end
-    //         are zero (Gamma stays constant)
+    // ---- 0. loads.  Thread (row r = tid / 16, part m = tid % 16) takes columns
+    //         8 m .. 8 m + 7 of row r of q, k, dO, W, dX (and U, for the U.dX
+    //         part of dbeta, and the column scales of S and G); a row's 16
+    //         parts are one DPP row, so its sums and maxima are taken across
+    //         those lanes.  Threads 0-127 also take channel tid of the gate for
+    //         the fp64 cumulative sum.  Every global load is issued first, so
+    //         that the part waits for memory once.
     {
-        constexpr int VE = 16 / (int)sizeof(T), VPR = BD / VE;
-        for (int e = tid; e < C * VPR; e += NT) {
-            const int r = e / VPR, cv = (e % VPR) * VE;
-            const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cv;
-            f32x4 kv = *reinterpret_cast<const f32x4 *>(k + off), qv = *reinterpret_cast<const f32x4 *>(q + off);
-            if (r >= L) kv = qv = zero4();
-            *reinterpret_cast<f32x4 *>(sK + r * LDI + cv) = kv;
-            *reinterpret_cast<f32x4 *>(sQ + r * LDI + cv) = qv;
-        }
-        for (int e = tid; e < C * (BD / 4); e += NT) {
-            const int r = e / (BD / 4), cv = (e % (BD / 4)) * 4;
-            f32x4 d = ld4(dout + (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cv);
-            if (r >= L) d = zero4();
-            *reinterpret_cast<f32x4 *>(sDO + r * LDF + cv) = d;
-        }
-        if (tid < C) sBeta[tid] = tid < L ? beta[(int64_t)(c0 + tid) * H + h] : 0.f;
-        if (tid < BD) {
-            float gv[C];
+        typedef typename std::conditional<kIn16, f32x4, f32x4[2]>::type Raw8;   // 8 input elements
+        const int r = tid >> 4, m = tid & 15, cb = 8 * m;
+        const bool ok = r < L;
+        const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cb;
+        const int64_t cho = unit * C * BD + (int64_t)r * BD + cb;   // (chunk, head) row r of U, W, dX
+        Raw8 kraw, qraw, draw;
+        if constexpr (kIn16) {
+            kraw = *reinterpret_cast<const f32x4 *>(k + off);
+            qraw = *reinterpret_cast<const f32x4 *>(q + off);
+            draw = *reinterpret_cast<const f32x4 *>(dout + off);
+        } else {
 #pragma unroll
-            for (int r = 0; r < C; ++r) gv[r] = g[(int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + tid];
-            double s = 0.0;
-#pragma unroll
-            for (int r = 0; r < C; ++r) {
-                if (r < L) s += (double)gv[r];
-                sGm[r * LDG + tid] = s;
+            for (int hf = 0; hf < 2; ++hf) {
+                kraw[hf] = *reinterpret_cast<const f32x4 *>(k + off + 4 * hf);
+                qraw[hf] = *reinterpret_cast<const f32x4 *>(q + off + 4 * hf);
+                draw[hf] = *reinterpret_cast<const f32x4 *>(dout + off + 4 * hf);
             }
-        } else if (tid < 2 * BD) {
-            const int c = tid - BD;
-            sIS[c] = kIn16 ? pow2_inv(snap_scale[unit * BD + c]) : 1.f;
-            sIG[c] = kIn16 ? pow2_inv(g_scale[unit * BD + c]) : 1.f;
+        }
+        f32x4 w[2], x[2], u[2], ss[2], sg[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {   // rows past the chunk read row r of the block (stored, not used)
+            w[hf] = *reinterpret_cast<const f32x4 *>(uw_w + cho + 4 * hf);
+            x[hf] = *reinterpret_cast<const f32x4 *>(dx_chunk + cho + 4 * hf);
+            u[hf] = *reinterpret_cast<const f32x4 *>(uw_u + cho + 4 * hf);
+            ss[hf] = kIn16 ? *reinterpret_cast<const f32x4 *>(snap_scale + unit * BD + cb + 4 * hf) : f32x4{1.f, 1.f, 1.f, 1.f};
+            sg[hf] = kIn16 ? *reinterpret_cast<const f32x4 *>(g_scale + unit * BD + cb + 4 * hf) : f32x4{1.f, 1.f, 1.f, 1.f};
+        }
+        const float br = beta[(int64_t)(c0 + min(r, L - 1)) * H + h];
+        float gv[C];
+        if (tid < BD) {
+#pragma unroll
+            for (int i = 0; i < C; ++i) gv[i] = g[(int64_t)(c0 + min(i, L - 1)) * rowQ + hoff + tid];
+        }
+        asm volatile("" ::: "memory");                    // keeps the loads together
+        // q, k as they are (zero past the chunk)
+        if constexpr (kIn16) {
+            *reinterpret_cast<f32x4 *>(sK + r * LDI + cb) = ok ? kraw : zero4();
+            *reinterpret_cast<f32x4 *>(sQ + r * LDI + cb) = ok ? qraw : zero4();
+        } else {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                *reinterpret_cast<f32x4 *>(sK + r * LDI + cb + 4 * hf) = ok ? kraw[hf] : zero4();
+                *reinterpret_cast<f32x4 *>(sQ + r * LDI + cb + 4 * hf) = ok ? qraw[hf] : zero4();
+            }
+        }
+        f32x4 d[2];
+        if constexpr (kIn16) {
+            const bf16_t *db = reinterpret_cast<const bf16_t *>(&draw);
+            d[0] = ld4(db);
+            d[1] = ld4(db + 4);
+        } else {
+            d[0] = draw[0];
+            d[1] = draw[1];
+        }
+        float ux = 0.f, mx[NMX] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            if (!ok) d[hf] = w[hf] = x[hf] = u[hf] = zero4();
+            *reinterpret_cast<f32x4 *>(sDO + r * LDF + cb + 4 * hf) = d[hf];
+            *reinterpret_cast<f32x4 *>(sW + r * LDF + cb + 4 * hf) = w[hf];
+            *reinterpret_cast<f32x4 *>(sDX + r * LDF + cb + 4 * hf) = x[hf];
+            f32x4 is, ig;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                is[e] = pow2_inv(ss[hf][e]);
+                ig[e] = pow2_inv(sg[hf][e]);
+            }
+            if (r == 0) {
+                *reinterpret_cast<f32x4 *>(sIS + cb + 4 * hf) = is;
+                *reinterpret_cast<f32x4 *>(sIG + cb + 4 * hf) = ig;
+            }
+            ux += dot4(u[hf], x[hf]);
+            mx[MX_DO] = fmaxf(mx[MX_DO], max4(abs4(d[hf])));
+            mx[MX_DOS] = fmaxf(mx[MX_DOS], max4(abs4(d[hf]) * is));
+            mx[MX_DX] = fmaxf(mx[MX_DX], max4(abs4(x[hf])));
+            mx[MX_DXS] = fmaxf(mx[MX_DXS], max4(abs4(x[hf]) * is));
+            mx[MX_W] = fmaxf(mx[MX_W], max4(abs4(w[hf])));
+            mx[MX_WG] = fmaxf(mx[MX_WG], max4(abs4(w[hf]) * ig));
+        }
+        if (ok) {                                         // dv = Diag(b) dX
+            *reinterpret_cast<f32x4 *>(dv + off) = x[0] * br;
+            *reinterpret_cast<f32x4 *>(dv + off + 4) = x[1] * br;
+        }
+        ux = sum16(ux);
+#pragma unroll
+        for (int a = 0; a < NMX; ++a) mx[a] = rowmax16(mx[a]);
+        if (m == 0) {
+            sDb[r] = ux;
+            sBeta[r] = ok ? br : 0.f;
+#pragma unroll
+            for (int a = 0; a < NMX; ++a) sRS[a * C + r] = kIn16 ? pow2_scale(mx[a]) : 1.f;
+        }
+        if (tid < BD) {
+            double sum = 0.0;
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                if (i < L) sum += (double)gv[i];
+                sGm[i * LDG + tid] = sum;
+            }
         }
     }
     __syncthreads();
 
-    // ---- 1. Gram tiles A (strictly lower), P (lower incl.): block x = 0, 1
-    //         diagonal (reference: the block's middle token), x = 2 the
-    //         off-diagonal one (reference: token 15); waves 0-2 A, 3-5 P,
-    //         waves 6-7 zero the upper block
+    // ---- 1. Gram tile A (strictly lower), block x = 0, 1 diagonal (reference:
+    //         the block's middle token), x = 2 the off-diagonal one (reference:
+    //         token 15); waves x and x + 3 take the two halves of the channels,
+    //         wave 6 zeroes the upper block
+    f32x4 gacc = zero4();
+    const int gx = wave % 3, ghalf = wave / 3;
+    const int grb = gx == 0 ? 0 : 16, gib = gx == 1 ? 16 : 0;
     if (wave < 6) {
-        const int x = wave % 3;
-        const bool isP = wave >= 3;
-        const int rb = x == 0 ? 0 : 16, ib = x == 1 ? 16 : 0, ref = x == 0 ? 7 : (x == 1 ? 23 : 15);
-        const int r = rb + lm, i = ib + lm;
-        const T *rowR = (isP ? sQ : sK) + r * LDI;
-        f32x4 acc = zero4();
-#pragma unroll 2
-        for (int kb = 0; kb < BD / 16; ++kb) {
+        const int ref = gx == 0 ? 7 : (gx == 1 ? 23 : 15);
+        const int r = grb + lm, i = gib + lm;
+#pragma unroll
+        for (int kb = 4 * ghalf; kb < 4 * ghalf + 4; ++kb) {
             const int c = 16 * kb + 4 * lj;
             const f32x4 rf = exp_diff4(sGm + r * LDG + c, sGm + ref * LDG + c);
             const f32x4 cf = exp_diff4(sGm + ref * LDG + c, sGm + i * LDG + c);
-            acc = Mf::mma(ld4(rowR + c) * rf, ld4(sK + i * LDI + c) * cf, acc);
+            gacc = Mf::mma(ld4(sK + r * LDI + c) * rf, ld4(sK + i * LDI + c) * cf, gacc);
         }
-        const bool diag = x < 2;
+        if (ghalf) *reinterpret_cast<f32x4 *>(sGp + gx * 256 + 4 * lane) = gacc;
+    } else if (wave == 6) {
+        for (int e = lane; e < 256; e += 64) sA[(e >> 4) * LDX + 16 + (e & 15)] = 0.f;
+    }
+    __syncthreads();
+    if (wave < 3) {
+        gacc += *reinterpret_cast<const f32x4 *>(sGp + gx * 256 + 4 * lane);
+        const bool diag = gx < 2;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int rr = rb + 4 * lj + ii, cc = ib + lm;
-            // selects, not products: entries above the diagonal may be inf
-            if (isP) {
-                const float p = (!diag || cc <= rr) ? acc[ii] : 0.f;
-                sP[rr * LDX + cc] = p;
-                sPT[cc * LDX + rr] = p;
-            } else {
-                sA[rr * LDX + cc] = (!diag || cc < rr) ? acc[ii] : 0.f;
-            }
+            const int rr = grb + 4 * lj + ii, cc = gib + lm;
+            sA[rr * LDX + cc] = (!diag || cc < rr) ? gacc[ii] : 0.f;   // a select: entries above may be inf
         }
-    } else {
-        for (int e = tid - 384; e < 256; e += 128) {
-            const int rr = e >> 4, cc = 16 + (e & 15);
-            sA[rr * LDX + cc] = 0.f;
-            sP[rr * LDX + cc] = 0.f;
-            sPT[cc * LDX + rr] = 0.f;
-        }
-    }
-    __syncthreads();
-
-    // ---- 1b. T = (I + Diag(b) A)^-1: the diagonal 16x16 blocks by forward
-    //          substitution (waves 0, 1: lane lm computes column lm; the four
-    //          lane groups repeat it), then T10 = -T11 (Diag(b) A)_10 T00 (wave 0)
-    if (wave < 2) {
-        const int a0 = 16 * wave, j = lm;
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < r; ++i) s += sA[(a0 + r) * LDX + a0 + i] * t[i];
-            t[r] = r == j ? 1.f : (r < j ? 0.f : -sBeta[a0 + r] * s);
-        }
-        if (lj == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                sT[(a0 + r) * LDX + a0 + j] = t[r];
-                sTT[(a0 + j) * LDX + a0 + r] = t[r];
-            }
-        }
-    } else if (wave < 4) {
-        for (int e = tid - 128; e < 256; e += 128) {
-            const int rr = e >> 4, cc = 16 + (e & 15);
-            sT[rr * LDX + cc] = 0.f;
-            sTT[cc * LDX + rr] = 0.f;
-        }
-    }
-    __syncthreads();
-    if (wave == 0) {
-        // X = (Diag(b) A)_10 T00: B[i][j] = T00[i][j] = TT[j][i]
-        const f32x4 an = ld4(sA + (16 + lm) * LDX + 4 * lj) * sBeta[16 + lm];
-        const f32x4 x = Mf::mma(an, ld4(sTT + lm * LDX + 4 * lj), zero4());
-        const f32x4 t10 = -Mf::mma(ld4(sT + (16 + lm) * LDX + 16 + 4 * lj), x, zero4());
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            sT[(16 + 4 * lj + ii) * LDX + lm] = t10[ii];
-            sTT[lm * LDX + 16 + 4 * lj + ii] = t10[ii];
-        }
-    }
-    __syncthreads();
-
-    // ---- 2. value column col of this lane (wave w: columns 16 w + lm),
-    //         token row tiles rt; U = V - K+ S and K^ G on the MFMA type of the forward
-    const int col = 16 * wave + lm;
-    f32x4 U[2], dW[2];
-    U[0] = U[1] = dW[0] = dW[1] = zero4();
-    const double *gmL = sGm + (L - 1) * LDG;
-#pragma unroll 2
-    for (int kb = 0; kb < BD / KB; ++kb) {
-        // B operands: column col of S and G, rows = the fragment's contraction indices
-        typename Mo::frag bs, bg;
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t o = (int64_t)(F::base(kb * KB, lj, gi) + e) * BD + col;
-                bs[4 * gi + e] = Sg[o];
-                bg[4 * gi + e] = Gg[o];
-            }
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int r = 16 * rt + lm;
-            f32x4 kp[NG], kh[NG];
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const int c = F::base(kb * KB, lj, gi);
-                const f32x4 kr = ld4(sK + r * LDI + c);
-                kp[gi] = kr * exp4(sGm + r * LDG + c);                 // K+
-                kh[gi] = kr * exp_diff4(gmL + c, sGm + r * LDG + c);   // K^
-            }
-            U[rt] = Mo::mma(F::make(kp, GS), bs, U[rt]);
-            dW[rt] = Mo::mma(F::make(kh, GS), bg, dW[rt]);
-        }
-    }
-    {
-        const float us = sIS[col] * (1.f / GS), gs = sIG[col] * (1.f / GS);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            U[rt] *= us;
-            dW[rt] *= gs;
-        }
-    }
-    f32x4 X[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * rt + 4 * lj + i;
-            const float vv = to_f(v[(int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + col]);
-            U[rt][i] = (r < L ? vv : 0.f) - U[rt][i];
-            X[rt][i] = sBeta[r] * U[rt][i];
-        }
-    // W = T X;  dW += P^T dO;  dX = T^T dW   (fp32; T lower, P^T and T^T upper by blocks)
-    f32x4 W[2], dX[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        W[rt] = zero4();
-#pragma unroll
-        for (int bt = 0; bt <= rt; ++bt) W[rt] = Mf::mma(ld4(sT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj), X[bt], W[rt]);
-#pragma unroll
-        for (int bt = rt; bt < 2; ++bt) {
-            f32x4 db;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) db[e] = sDO[(16 * bt + 4 * lj + e) * LDF + col];
-            dW[rt] = Mf::mma(ld4(sPT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj), db, dW[rt]);
-        }
-    }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-        dX[rt] = zero4();
-#pragma unroll
-        for (int bt = rt; bt < 2; ++bt) dX[rt] = Mf::mma(ld4(sTT + (16 * rt + lm) * LDX + 16 * bt + 4 * lj), dW[bt], dX[rt]);
-    }
-    // dv, the U.dX part of dbeta (this wave's columns), W and dX to LDS, and
-    // this wave's part of the row maxima that set the 16-bit operand scales
-    {
-        const float is = sIS[col], ig = sIG[col];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * rt + 4 * lj + i;
-                if (r < L) dv[(int64_t)(c0 + r) * rowQ + hoff + col] = sBeta[r] * dX[rt][i];
-                const float pb = sum16(U[rt][i] * dX[rt][i]);
-                sW[r * LDF + col] = W[rt][i];
-                sDX[r * LDF + col] = dX[rt][i];
-                const float ado = fabsf(sDO[r * LDF + col]), adx = fabsf(dX[rt][i]), aw = fabsf(W[rt][i]);
-                float m[NMX];
-                m[MX_DO] = rowmax16(ado);
-                m[MX_DOS] = rowmax16(ado * is);
-                m[MX_DX] = rowmax16(adx);
-                m[MX_DXS] = rowmax16(adx * is);
-                m[MX_W] = rowmax16(aw);
-                m[MX_WG] = rowmax16(aw * ig);
-                if (lm == 0) {
-                    sDb[wave * C + r] = pb;
-#pragma unroll
-                    for (int a = 0; a < NMX; ++a) sMx[(wave * NMX + a) * C + r] = m[a];
-                }
-            }
-    }
-    __syncthreads();
-    if (tid < NMX * C) {       // row scales: the row maximum into [2^13, 2^14) (1 for fp32 operands)
-        float m = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) m = fmaxf(m, sMx[w * NMX * C + tid]);
-        sRS[tid] = kIn16 ? pow2_scale(m) : 1.f;
     }
     __syncthreads();
 
     // ---- 3. contractions over the value columns, on the MFMA type of the
     //         forward: key channel cc of this lane (wave w: 16 w + lm); S and G
-    //         rows from global memory (the fragment's indices along the row)
-    const int cc = 16 * wave + lm;
+    //         rows as prefetched (the fragment's indices along the row)
     f32x4 dQp[2], dXS[2], dKh[2];
     dQp[0] = dQp[1] = dXS[0] = dXS[1] = dKh[0] = dKh[1] = zero4();
     float dgm = 0.f;
     const float *rsDOS = sRS + MX_DOS * C, *rsDXS = sRS + MX_DXS * C, *rsWG = sRS + MX_WG * C;
-#pragma unroll 2
+#pragma unroll
     for (int kb = 0; kb < BD / KB; ++kb) {
         typename Mo::frag st, gt;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const int j = F::base(kb * KB, lj, gi);
-            typedef typename std::conditional<kIn16, f16x4, f32x4>::type V4;
-            const V4 sv = *reinterpret_cast<const V4 *>(Sg + (int64_t)cc * BD + j);
-            const V4 gv = *reinterpret_cast<const V4 *>(Gg + (int64_t)cc * BD + j);
+            const V4 sv = spre[kb][gi], gvv = gpre[kb][gi];
             const f32x4 isv = ld4(sIS + j), igv = ld4(sIG + j);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 st[4 * gi + e] = sv[e];
-                gt[4 * gi + e] = gv[e];
-                dgm += (float)sv[e] * isv[e] * ((float)gv[e] * igv[e]);
+                gt[4 * gi + e] = gvv[e];
+                dgm += (float)sv[e] * isv[e] * ((float)gvv[e] * igv[e]);
             }
         }
 #pragma unroll
@@ -494,7 +419,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
             dKh[rt][i] *= pow2_inv(rsWG[r]);
         }
     // dP (waves 0-2) and dN (waves 3-5) by block x, B = W rows with their own
-    // row scales; they overwrite P, P^T, T, T^T, whose last reads were in part 2
+    // row scales; waves 6-7 zero the upper blocks
     if (wave < 6) {
         const int x = wave % 3;
         const bool isN = wave >= 3, diag = x < 2;
@@ -534,7 +459,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
         }
         if (isN && lm == 0) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) sDb[(NW + x) * C + rb + 4 * lj + ii] = pb[ii];
+            for (int ii = 0; ii < 4; ++ii) sDb[(1 + x) * C + rb + 4 * lj + ii] = pb[ii];
         }
     } else {
         for (int e = tid - 384; e < 256; e += 128) {
@@ -546,11 +471,9 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
         }
         if (tid - 384 < 16) {     // rows that a block's dbeta part does not cover
             const int e = tid - 384;
-            sDb[NW * C + 16 + e] = 0.f;
-            sDb[(NW + 1) * C + e] = 0.f;
-            sDb[(NW + 2) * C + e] = 0.f;
-            sDb[(NW + 3) * C + e] = 0.f;
-            sDb[(NW + 3) * C + 16 + e] = 0.f;
+            sDb[1 * C + 16 + e] = 0.f;
+            sDb[2 * C + e] = 0.f;
+            sDb[3 * C + e] = 0.f;
         }
     }
     __syncthreads();
@@ -635,7 +558,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                     dq[(int64_t)(c0 + r) * rowQ + hoff + c] = dq_;
                     dk[(int64_t)(c0 + r) * rowQ + hoff + c] = dkrow + dkcol;
                 }
-                sDG[r * LDF + c] = dG;
+                sDG[r * LDF + c] = dG;    // sW's last reads were in part 3
             }
     }
     __syncthreads();
@@ -649,12 +572,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
         }
     } else if (tid < BD + C) {
         const int r = tid - BD;
-        if (r < L) {
-            float s = 0.f;
-#pragma unroll
-            for (int w = 0; w < NDB; ++w) s += sDb[w * C + r];
-            dbeta[(int64_t)(c0 + r) * H + h] = s;
-        }
+        if (r < L) dbeta[(int64_t)(c0 + r) * H + h] = sDb[r] + sDb[C + r] + sDb[2 * C + r] + sDb[3 * C + r];
     }
 }
 }  // namespace kda
@@ -662,13 +580,16 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
 // Per (chunk, head) gradients of the chunk form (kda_bwd_chunk_kernel): S at
 // every chunk start in snaps and the gradient at every chunk end in gchunk,
 // both [chunks][H][BD][BD] as the chains store them (bf16: fp16 values with
-// column scales [chunks][H][BD] in snap_scale / g_scale; fp32: fp32).
-extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const void *v, const float *g,
+// column scales [chunks][H][BD] in snap_scale / g_scale; fp32: fp32); every
+// chunk's U, W (forward) and dX (state-gradient chain) [chunks][H][32][BD]
+// fp32.  Writes dq, dk, dv, dg and dbeta.
+extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const float *g,
                                            const float *beta, const void *dout, const int32_t *cu,
                                            const int32_t *chunk_off, int64_t max_chunks, const void *snaps,
                                            const float *snap_scale, const void *gchunk, const float *g_scale,
-                                           int32_t N, int32_t T_tot, int32_t H, float *dq, float *dk, float *dv,
-                                           float *dg, float *dbeta, hipStream_t stream)
+                                           const float *uw_u, const float *uw_w, const float *dx_chunk, int32_t N,
+                                           int32_t T_tot, int32_t H, float *dq, float *dk, float *dv, float *dg,
+                                           float *dbeta, hipStream_t stream)
 {
     using namespace kda;
     const int64_t grid = max_chunks * H;
@@ -681,18 +602,18 @@ extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *
         if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bc::Cfg<bf16_t>::bytes, lds_set))
             return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(bc::NT), bc::Cfg<bf16_t>::bytes, stream,
-                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k),
-                           static_cast<const bf16_t *>(v), g, beta, static_cast<const bf16_t *>(dout), cu, chunk_off,
-                           snaps, snap_scale, gchunk, g_scale, N, T_tot, H, dq, dk, dv, dg, dbeta);
+                           static_cast<const bf16_t *>(q), static_cast<const bf16_t *>(k), g, beta,
+                           static_cast<const bf16_t *>(dout), cu, chunk_off, snaps, snap_scale, gchunk, g_scale,
+                           uw_u, uw_w, dx_chunk, N, T_tot, H, dq, dk, dv, dg, dbeta);
     } else {
         auto kern = kda_bwd_chunk_kernel<float>;
         static std::atomic<uint64_t> lds_set{0};
         if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bc::Cfg<float>::bytes, lds_set))
             return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(bc::NT), bc::Cfg<float>::bytes, stream,
-                           static_cast<const float *>(q), static_cast<const float *>(k),
-                           static_cast<const float *>(v), g, beta, static_cast<const float *>(dout), cu, chunk_off,
-                           snaps, snap_scale, gchunk, g_scale, N, T_tot, H, dq, dk, dv, dg, dbeta);
+                           static_cast<const float *>(q), static_cast<const float *>(k), g, beta,
+                           static_cast<const float *>(dout), cu, chunk_off, snaps, snap_scale, gchunk, g_scale,
+                           uw_u, uw_w, dx_chunk, N, T_tot, H, dq, dk, dv, dg, dbeta);
     }
     return hipGetLastError();
 }

@@ -171,6 +171,7 @@ struct SegArgs {
     int32_t img_slots;          // chunk-operand pass: image slots per head (> chunks of valid input)
     f32x4 *gimg;                // MODE_PREPG: gradient images, slots as for img
     float *snap_scale;          // kda_chain_kernel state stores, 16-bit inputs: [chunks][H][dv] column scales
+    float *uw_u, *uw_w;         // kda_chain_kernel state stores: U and W of every chunk, [chunks][H][C][dv]
 };
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
@@ -483,15 +484,18 @@ constexpr float kScaleCap = 18446744073709551616.f;
 // same scaled units.  sS changes (by exact powers of two) only when a column
 // leaves [2^-8, 2^15), or when W sS / GS would leave the fp16 range.
 // Tile ct reads value column vc + CTS ct and writes output column oc + CTS ct.
+// UW (the backward's forward pass): U = V - K+ S0 and W also go to uw_u, uw_w
+// ([C][ldu] fp32, tile ct at column ucol + 16 ct; every row, padding rows
+// included: stores under no condition, which the compiler can count).
 // Returns (16-bit operands only; wave-uniform) a mask with bit ct set when
 // every column of tile ct is exactly zero after the update.
-template <typename TIn, int C, int ldv, int ldo, bool SUMMARY, int NCT = 1, int CTS = 16>
+template <typename TIn, int C, int ldv, int ldo, bool SUMMARY, int NCT = 1, int CTS = 16, bool UW = false>
 __device__ __forceinline__ uint32_t chain_chunk(
     f32x4 (&S)[NCT][DK / 16], float (&sS)[NCT], const typename PrefillCfg<TIn, C, 4>::OpT *sNKp,
     const typename PrefillCfg<TIn, C, 4>::OpT *sQp, const typename PrefillCfg<TIn, C, 4>::OpT *sKhT,
     const typename PrefillCfg<TIn, C, 4>::OpT *sT, const typename PrefillCfg<TIn, C, 4>::OpT *sP,
     const float *sTs, const float *sGam, const float *sBeta, const TIn *sV, int vc, TIn *sO, int oc,
-    int lj, int lm)
+    int lj, int lm, float *uw_u = nullptr, float *uw_w = nullptr, int ldu = 0, int ucol = 0)
 {
     // NCT column tiles of 16 per wave (tile ct: value column vc + 16 ct, output column oc + 16 ct):
     // every operand fragment read from LDS serves all of them
@@ -533,8 +537,11 @@ __device__ __forceinline__ uint32_t chain_chunk(
             const int r = mt * SUB + 4 * lj + i;
             const float br = sBeta[r];
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
-                X[ct][mt][i] = br * (to_f(sV[r * ldv + vc + CTS * ct]) + t[ct][i] * isS[ct]);
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float u = to_f(sV[r * ldv + vc + CTS * ct]) + t[ct][i] * isS[ct];
+                if constexpr (UW) uw_u[r * ldu + ucol + 16 * ct] = u;
+                X[ct][mt][i] = br * u;
+            }
         }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) xmax[ct] = absmax_acc(xmax[ct], X[ct][mt]);
@@ -571,6 +578,10 @@ __device__ __forceinline__ uint32_t chain_chunk(
         for (int ct = 0; ct < NCT; ++ct) {
             W[ct][a] = w[ct];
             wmax[ct] = absmax_acc(wmax[ct], w[ct]);
+            if constexpr (UW) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) uw_w[(a * SUB + 4 * lj + i) * ldu + ucol + 16 * ct] = w[ct][i];
+            }
         }
     }
     // W enters in the state's units; if W sS / GS would not fit fp16, the
@@ -1290,7 +1301,7 @@ __device__ __forceinline__ void store_scaled_state(void *dst, float *scale, cons
             for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) d[(int64_t)(16 * r + 4 * lj + i) * dv + col] = from_f<f16_t>(X[ct][r][i]);
-            if (lj == 0) scale[col] = s[ct];
+            scale[col] = s[ct];      // the column's lanes all store the same value
         } else {
             float *d = static_cast<float *>(dst);
             const float inv = pow2_inv(s[ct]);
@@ -1342,9 +1353,10 @@ struct ChainCfg {
     static constexpr int OVEC = C * 16 * NCT / VEC;                 // vectors of one wave's output tile
 };
 
-// SNAP (outputs only): also store the state after every chunk that is not its
-// sequence's last, as the state at the start of the next chunk, at that
-// chunk's global index in seg.snap ([chunks][H][DK][dv]); out may be NULL.
+// SNAP (outputs only; the backward's forward pass): also store the state at
+// the start of every chunk at its global index in seg.snap ([chunks][H][DK][dv],
+// see store_scaled_state), and every chunk's U = V - K+ S0 and W in seg.uw_u,
+// seg.uw_w ([chunks][H][C][dv] fp32, rows of valid tokens); out may be NULL.
 template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
@@ -1559,12 +1571,14 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         __syncthreads();                          // chunk ci staged; (double buffer) ci - 1 done with the other
         load(min(ci + 1, nch - 1));               // unconditional, see the fused kernel
         const unsigned char *base = smem + (SB ? 0 : (ci & 1) * Q::BUF);
-        chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT>(
+        const int64_t uwo = ((gc0 + ci) * num_heads + h) * C * dv;   // (chunk, head) block of U and W
+        chain_chunk<TIn, C, LDV, 16 * NCT, SUMMARY, NCT, 16, SNAP>(
             S, sS, reinterpret_cast<const OpT *>(base + Q::offNKp), reinterpret_cast<const OpT *>(base + Q::offQp),
             reinterpret_cast<const OpT *>(base + Q::offKhT), reinterpret_cast<const OpT *>(base + Q::offT),
             reinterpret_cast<const OpT *>(base + Q::offP), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
-            reinterpret_cast<const TIn *>(base + Q::offV), vcol, sOw, lm, lj, lm);
+            reinterpret_cast<const TIn *>(base + Q::offV), vcol, sOw, lm, lj, lm, SNAP ? seg.uw_u + uwo : nullptr,
+            SNAP ? seg.uw_w + uwo : nullptr, dv, dv0 + vcol);
         if (!SUMMARY && (!SNAP || out)) {
             // this wave's 16 output columns: rows of 16 * sizeof(TIn) bytes, one
             // 16-byte vector per lane and step (LDS is in order within a wave).
@@ -1634,12 +1648,15 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
 // directly, and the update runs as the accumulator with Z and dO rounded in
 // G~'s units (sG / GS).  A column that is exactly zero takes the scale that
 // puts the incoming Z and dO in range.
-template <typename TIn, int C, int ldd, int NCT>
+// DX: also dX = (I + N)^-T Y to dx_out ([C][DK] fp32, every row: stores under
+// no condition, which the compiler can count; padding rows are not read).
+template <typename TIn, int C, int ldd, int NCT, bool DX = false>
 __device__ __forceinline__ void grad_chunk(
     f32x4 (&G)[NCT][DK / 16], float (&sG)[NCT], const typename PrefillCfg<TIn, C, 4>::OpT *sKh,
     const typename PrefillCfg<TIn, C, 4>::OpT *sNKpT, const typename PrefillCfg<TIn, C, 4>::OpT *sQpT,
     const typename PrefillCfg<TIn, C, 4>::OpT *sPT, const typename PrefillCfg<TIn, C, 4>::OpT *sTT,
-    const float *sTsT, const float *sGam, const float *sBeta, const TIn *sD, int vc, int lj, int lm)
+    const float *sTsT, const float *sGam, const float *sBeta, const TIn *sD, int vc, int lj, int lm,
+    float *dx_out = nullptr)
 {
     typedef PrefillCfg<TIn, C, 4> P;
     typedef typename P::OpT OpT;
@@ -1738,6 +1755,10 @@ __device__ __forceinline__ void grad_chunk(
         for (int ct = 0; ct < NCT; ++ct) {
             Z[ct][a] = z[ct] * bt;
             zmax[ct] = absmax_acc(zmax[ct], Z[ct][a]);
+            if constexpr (DX) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dx_out[(a * SUB + 4 * lj + i) * DK + vc + 16 * ct] = z[ct][i];
+            }
         }
     }
     // Z and dO enter the update in G~'s units; if they would not fit fp16 the
@@ -1852,14 +1873,15 @@ struct GChainCfg {
 // segment's end), storing the gradient at the end of every chunk at that
 // chunk's global index in g_chunk ([chunks][H][DK][DV], as store_scaled_state
 // writes it, column scales in g_scale) and, for a sequence's first segment,
-// the gradient at the sequence start in dinit (may be nullptr).  dinit and the
-// summaries are fp32, G~ / sG (exact).
+// the gradient at the sequence start in dinit (may be nullptr), and every
+// chunk's dX in dx_chunk ([chunks][H][C][DK] fp32).
+// dinit and the summaries are fp32, G~ / sG (exact).
 template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB>
 __global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
     const TIn *dout, const int32_t *__restrict__ cu_seqlens, int32_t num_seqs, int32_t total_tokens,
     int32_t num_heads, const int32_t *__restrict__ plan, int32_t num_segs, const int32_t *__restrict__ sched,
     const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, void *g_chunk,
-    float *g_scale, float *dinit, float *g0_out)
+    float *g_scale, float *dinit, float *g0_out, float *dx_chunk)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     typedef typename Q::OpT OpT;
@@ -1970,12 +1992,13 @@ __global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
             store_scaled_state<Q::P::kIn16, NCT>(dst, g_scale + o * DK, G, sG, vcol, DK, lj, lm);
         }
         const unsigned char *base = smem + (SB ? 0 : (k & 1) * Q::BUF);
-        grad_chunk<TIn, C, LDV, NCT>(
+        grad_chunk<TIn, C, LDV, NCT, !SUMMARY>(
             G, sG, reinterpret_cast<const OpT *>(base + Q::offKh), reinterpret_cast<const OpT *>(base + Q::offNKpT),
             reinterpret_cast<const OpT *>(base + Q::offQpT), reinterpret_cast<const OpT *>(base + Q::offPT),
             reinterpret_cast<const OpT *>(base + Q::offTT), reinterpret_cast<const float *>(base + Q::offTs),
             reinterpret_cast<const float *>(base + Q::offGam), reinterpret_cast<const float *>(base + Q::offBeta),
-            reinterpret_cast<const TIn *>(base + Q::offD), vcol, lj, lm);
+            reinterpret_cast<const TIn *>(base + Q::offD), vcol, lj, lm,
+            SUMMARY ? nullptr : dx_chunk + ((gc0 + ci) * H + h) * C * DK);
         if constexpr (SB) __syncthreads();       // every wave is done with the buffer
         stage(max(ci - 1, 0), SB ? 0 : (k + 1) & 1);
     }
@@ -1987,7 +2010,8 @@ template <typename TIn, int C, int NW, int NCT, bool SB>
 static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int32_t *cu, int32_t N, int32_t T_tot,
                                       int32_t H, const int32_t *plan, int32_t num_segs, const int32_t *sched,
                                       const int32_t *chunk_off, const void *gimg, const float *g_end, void *g_chunk,
-                                      float *g_scale, float *dinit, float *g0_out, hipStream_t stream)
+                                      float *g_scale, float *dinit, float *g0_out, float *dx_chunk,
+                                      hipStream_t stream)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     auto kern = summary ? kda_grad_chain_kernel<TIn, C, NW, NCT, true, SB>
@@ -2000,7 +2024,7 @@ static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int3
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(dout), cu,
                        N, T_tot, H, plan, num_segs, sched, chunk_off, static_cast<const f32x4 *>(gimg), g_end,
-                       g_chunk, g_scale, dinit, g0_out);
+                       g_chunk, g_scale, dinit, g0_out, dx_chunk);
     return hipGetLastError();
 }
 
@@ -2410,22 +2434,23 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
 // plan, mode, seg_init and seg_out as for kda_launch_prefill.  snap (may be
 // nullptr): the state at every chunk start, [chunks][H][DK][dv] as
 // store_scaled_state writes it (bf16: fp16 values, column scales in
-// snap_scale [chunks][H][dv]).
+// snap_scale [chunks][H][dv]), and every chunk's U and W in uw_u, uw_w
+// ([chunks][H][32][dv] fp32).
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
-                                       const int32_t *sched, void *snap, float *snap_scale,
-                                       const int32_t *init_seq_seg, int32_t init_unit, int32_t init_units,
-                                       hipStream_t stream)
+                                       const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
+                                       float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
+                                       int32_t init_units, hipStream_t stream)
 {
     using namespace kda;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
-    if (snap && bf16 && !snap_scale) return hipErrorInvalidValue;
+    if (snap && ((bf16 && !snap_scale) || !uw_u || !uw_w)) return hipErrorInvalidValue;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img)),
                    mode == SEG_SUMMARY ? nullptr : static_cast<float *>(snap), 0, 0, sched, init_seq_seg, init_unit,
-                   init_units, 0, 0, nullptr, snap_scale};
+                   init_units, 0, 0, nullptr, snap_scale, uw_u, uw_w};
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
@@ -2444,24 +2469,24 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
 // summary = 1 writes G^0 of every segment but a sequence's first to g0_out
 // [num_segs][H][DK][DK]; summary = 0 runs every segment from g_end (same
 // layout), storing the gradient at every chunk end in g_chunk (bf16: fp16
-// values with column scales in g_scale [chunks][H][DK]; fp32: fp32) and
-// d(initial state) in dinit.
+// values with column scales in g_scale [chunks][H][DK]; fp32: fp32),
+// d(initial state) in dinit and every chunk's dX in dx_chunk [chunks][H][32][DK].
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
                                             const float *g_end, void *g_chunk, float *g_scale, float *dinit,
-                                            float *g0_out, hipStream_t stream)
+                                            float *g0_out, float *dx_chunk, hipStream_t stream)
 {
     using namespace kda;
-    if (summary ? !g0_out : (!g_end || !g_chunk || (bf16 && !g_scale))) return hipErrorInvalidValue;
+    if (summary ? !g0_out : (!g_end || !g_chunk || (bf16 && !g_scale) || !dx_chunk)) return hipErrorInvalidValue;
     // bf16: double buffered (about 87 KB); fp32 images are twice as large: one buffer
     if (bf16)
         return launch_grad_chain_t<bf16_t, 32, 4, 2, false>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs,
                                                             sched, chunk_off, gimg, g_end, g_chunk, g_scale, dinit,
-                                                            g0_out, stream);
+                                                            g0_out, dx_chunk, stream);
     return launch_grad_chain_t<float, 32, 4, 2, true>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs, sched,
                                                       chunk_off, gimg, g_end, g_chunk, g_scale, dinit, g0_out,
-                                                      stream);
+                                                      dx_chunk, stream);
 }
 
 extern "C" size_t kda_chunk_image_bytes(int bf16)
