@@ -51,10 +51,11 @@ FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, TFLOP/s
 # backward, per head-token: q, k, v, dout in bf16, g fp32, beta in; dq, dk, dg,
 # dv fp32 and dbeta out
 BWD_BYTES_PER_HT = 4 * 2 * DK + 4 * DK + 4 + 4 * (3 * DK + DV) + 4
-# backward token form, flops per state element and token: recompute
-# (decay 1, S^T k 2, rank-1 update 2) + reverse (decay 1, S^T k 2, q do^T 2,
-# dS^T k 2, S do with the update 4, dk 4, dSbar 2, dg 2, decay 1) = 25
-BWD_FLOP_PER_HT = 25 * DK * DV
+# backward, chunk form: the dk x dv contractions per head-token (2 flops per
+# multiply-add) -- states at chunk starts (U = V - K+ S, S' = gamma S + K^T W: 2),
+# the state-gradient chain (K^ G, K+^T Z, Q+^T dO: 3), the chunk gradients
+# (dO S^T, dX S^T, W G^T: 3); 8 contractions x 2 dk dv flops
+BWD_FLOP_PER_HT = 16 * DK * DV
 PREFILL_KERNELS = {
     "cp": "kda_prefill_cp call: kda_cp_plan_kernel (two plans), kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
           "kda_chain_kernel<bf16,32,8 waves,2 tiles,summary>, kda_cp_combine_kernel, "
@@ -532,31 +533,40 @@ def main():
     rep_bytes = Nd * Hd * (2 * DK * DV * 4 + RT * (DECODE_BYTES_PER_UNIT - 2 * DK * DV * 4))
     rep_gbs = rep_bytes / (rep_ms * 1e-3) / 1e9
 
-    # backward (training) on the 4,096-token, 8-head workload: its own
-    # measurement, outside the timed steps
-    wl_b = I.WORKLOADS["prefill_t4096_h8"]
-    bwd = I.make_prefill(wl_b, device=dev)
-    Tb, Hb = bwd["q"].shape[0], bwd["q"].shape[1]
-    gen = torch.Generator(device=dev).manual_seed(7)
-    b_dout = torch.randn(Tb, Hb, DV, generator=gen, device=dev).to(torch.bfloat16)
-    b_ws = torch.empty(K.kda_backward_workspace_size(1, Tb, Hb, DK, DV, torch.bfloat16), dtype=torch.uint8, device=dev)
-    b_grads = None
+    # backward (training): its own measurement, outside the timed steps, on
+    # the 4,096-token, 8-head workload and on 4 x 16,384 tokens x 32 heads
+    def time_backward(wl_name, calls):
+        b = I.make_prefill(I.WORKLOADS[wl_name], device=dev)
+        T_, H_ = b["q"].shape[0], b["q"].shape[1]
+        N_ = b["cu_seqlens"].shape[0] - 1
+        gen = torch.Generator(device=dev).manual_seed(7)
+        dout_ = torch.randn(T_, H_, DV, generator=gen, device=dev).to(torch.bfloat16)
+        ws_ = torch.empty(K.kda_backward_workspace_size(N_, T_, H_, DK, DV, torch.bfloat16), dtype=torch.uint8,
+                          device=dev)
+        grads = K.kda_backward(b["q"], b["k"], b["v"], b["g"], b["beta"], b["initial_state"], b["cu_seqlens"],
+                               dout_, None, workspace=ws_)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(calls):
+            K.kda_backward(b["q"], b["k"], b["v"], b["g"], b["beta"], b["initial_state"], b["cu_seqlens"], dout_,
+                           None, grads=grads, workspace=ws_)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / calls
+        del b, dout_, ws_, grads
+        tflops = T_ * H_ * BWD_FLOP_PER_HT / (ms * 1e-3) / 1e12
+        nbytes = T_ * H_ * BWD_BYTES_PER_HT + 3 * N_ * H_ * DK * DV * 4      # + initial state, dfinal, dinit
+        return {"workload": wl_name, "total_tokens": T_, "heads": H_, "num_seqs": N_, "ms_per_call": ms,
+                "tokens_per_s": T_ / (ms * 1e-3), "head_tokens_per_s": T_ * H_ / (ms * 1e-3),
+                "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": tflops / BF16_PEAK_TFLOPS, "flop_per_head_token": BWD_FLOP_PER_HT,
+                             "hbm_achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
+                             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes_per_launch": nbytes}}
 
-    def backward():
-        return K.kda_backward(bwd["q"], bwd["k"], bwd["v"], bwd["g"], bwd["beta"], bwd["initial_state"],
-                              bwd["cu_seqlens"], b_dout, None, grads=b_grads, workspace=b_ws)
-
-    b_grads = backward()
-    torch.cuda.synchronize()
-    b_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    b_ev[0].record(stream)
-    for _ in range(3):
-        backward()
-    b_ev[1].record(stream)
-    torch.cuda.synchronize()
-    bwd_ms = b_ev[0].elapsed_time(b_ev[1]) / 3
-    bwd_tflops = Tb * Hb * BWD_FLOP_PER_HT / (bwd_ms * 1e-3) / 1e12
-    bwd_bytes = Tb * Hb * BWD_BYTES_PER_HT + 3 * Hb * DK * DV * 4      # + initial state, dfinal, dinit
+    bwd_small = time_backward("prefill_t4096_h8", 5)
+    bwd_large = time_backward("prefill_4x16384_h32", 3)
 
     def flop_fields(head_tokens_c, ms):
         fref = head_tokens_c * PREFILL_FREF_PER_HT / (ms * 1e-3) / 1e12
@@ -703,16 +713,12 @@ def main():
                           "roofline": {"bound": "hbm", "achieved": rep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": rep_gbs / HBM_PEAK_GBS, "kernel": "kda_decode_tokens_kernel<bf16>",
                                        "algorithmic_bytes_per_launch": rep_bytes}},
-        "backward": {"workload": "prefill_t4096_h8", "ms_per_call": bwd_ms, "tokens_per_s": Tb / (bwd_ms * 1e-3),
-                     "head_tokens_per_s": Tb * Hb / (bwd_ms * 1e-3),
-                     "roofline": {"bound": "alu", "achieved": bwd_tflops, "peak": FP32_VALU_PEAK_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": bwd_tflops / FP32_VALU_PEAK_TFLOPS,
-                                  "flop_per_head_token": BWD_FLOP_PER_HT,
-                                  "hbm_achieved_gbs": bwd_bytes / (bwd_ms * 1e-3) / 1e9,
-                                  "algorithmic_bytes_per_launch": bwd_bytes},
-                     "kernels": "kda_cp_plan_kernel, chunk operands, kda_chain_kernel summary and output with "
-                                "state stores, kda_cp_combine_kernel x2, kda_backward_summary_kernel<bf16>, "
-                                "kda_backward_kernel<bf16>, kda_backward_reduce_kernel"},
+        "backward": dict(bwd_small, larger=bwd_large,
+                         kernels="kda_cp_plan_kernel; kda_prefill_kernel<bf16,32,4,MODE_PREPG> (chunk and "
+                                 "gradient images); then side by side: kda_chain_kernel summaries, "
+                                 "kda_cp_combine_kernel, kda_chain_kernel with state stores | "
+                                 "kda_grad_chain_kernel summaries, kda_cp_combine_kernel<transposed>, "
+                                 "kda_grad_chain_kernel; then kda_bwd_chunk_kernel<bf16>"),
         "other_prefill_configs": other_prefill,
         "cpu_baseline": None,
     }

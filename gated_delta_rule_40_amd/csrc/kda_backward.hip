@@ -60,30 +60,33 @@ __device__ __forceinline__ float sum_rows4(float x) {  // over the four DPP rows
 //              last token also sum_r k (.) dK^ (.) e^(Gamma_L - Gamma) + (G (.) S) 1 (.) e^Gamma_L
 //     dg = reverse cumulative sum of dGamma over the chunk.
 // U and W come from the forward pass that stores the chunk-start states, dX
-// from the state-gradient chain (which also writes dv), S and G as those
-// passes store them.  What is left here has no recurrence: one workgroup per
-// (chunk, head).
+// from the state-gradient chain, S and G as those passes store them.  What is
+// left here has no recurrence: one workgroup per (chunk, head).
 // Precision: the Gram tile A and every 32-wide contraction run on fp32 (MFMA
 // 16x16x4 and VALU).  The five 128-wide contractions (dQ+, dX S^T, dK^, dP,
 // dN) run on the MFMA type of the forward: fp32 for fp32 inputs; fp16 for
 // 16-bit inputs, with S and G read as the fp16 values and exact power-of-two
-// column scales that the chains carry, and every other operand given an exact
-// power-of-two scale per row (the row maximum lands in [2^13, 2^14)) -- a
-// scale along the contraction index is folded into the other operand, so every
-// product is exact up to the fp16 rounding of its operands.
-// Gamma is kept in fp64: every decay factor is e^x of a difference of two of
-// its entries, rounded to fp32 only then, so a factor carries the rounding of
-// its own exponent, not that of the (up to 160 in magnitude) cumulative sums.
+// column scales that the chains carry, and dO, W and dX held in fp16 with an
+// exact power-of-two scale per row (the row maximum lands in [2^13, 2^14)); a
+// product that needs another scale of a row, or a scale along the contraction
+// index, rescales the fp16 values by an exact power of two, so every product
+// is exact up to the fp16 rounding of its operands.
+// Gamma: every decay factor is e^x of a difference of two cumulative gate
+// entries.  For fp32 inputs Gamma is kept in fp64 and each difference rounded
+// to fp32 only then, so a factor carries the rounding of its own exponent, not
+// that of the (up to 160 in magnitude) cumulative sums; 16-bit inputs keep it
+// in fp32, whose rounding (about 1e-5 of a factor) is far below their own.
 // E is factored per 16-token block pair with a reference inside the pair --
 // the middle token of a diagonal block, the block boundary for the
 // off-diagonal one -- so every factor lies in [e^-80, e^40] for g in [-5, 0]:
 // the Gram tile and the E-weighted token sums are then plain MFMA products of
 // factored operands, and a factor applied after a product is at most e^40.
-// Work split: eight waves; in the key-channel parts wave w owns channels
-// 16 w .. 16 w + 15; token rows are loaded by 16 lanes each (8 columns per lane).
+// Work split: four waves; in the key-channel parts wave w owns channels
+// 32 w .. 32 w + 31 (two tiles); token rows are loaded by 16 lanes each (8
+// columns per lane, two passes).  The 16-bit workgroup fits 80 KB of LDS, so
+// two share a compute unit: one loads while the other computes.
 namespace bc {
-constexpr int C = 32, NW = 8, NT = 64 * NW;
-constexpr int LDG = BD + 2;          // fp64 Gamma rows
+constexpr int C = 32, NW = 4, NT = 64 * NW, NCT = BD / (16 * NW);
 constexpr int LDF = BD + 4;          // fp32 [C][BD] rows
 constexpr int LDX = C + 4;           // fp32 [C][C] rows
 constexpr int NDB = 4;               // partial dbeta slots: U.dX, and the dN (.) A part of 3 blocks
@@ -91,26 +94,33 @@ constexpr int NMX = 6;               // row scales from |dO|, |dO|/sS, |dX|, |dX
 enum { MX_DO = 0, MX_DOS = 1, MX_DX = 2, MX_DXS = 3, MX_W = 4, MX_WG = 5 };
 template <typename T>
 struct Cfg {
-    static constexpr int LDI = BD + 16 / (int)sizeof(T);   // q, k rows (input type)
+    static constexpr bool kIn16 = !std::is_same<T, float>::value;
+    typedef typename std::conditional<kIn16, float, double>::type GT;   // cumulative gate
+    typedef typename std::conditional<kIn16, f16_t, float>::type RT;    // dO, W, dX rows (row-scaled)
+    static constexpr int LDI = BD + 16 / (int)sizeof(T);    // q, k rows (input type)
+    static constexpr int LDG = BD + 16 / (int)sizeof(GT);   // Gamma rows
+    static constexpr int LDR = BD + 16 / (int)sizeof(RT);   // dO, W, dX rows
     static constexpr uint32_t offK = 0;
     static constexpr uint32_t offQ = offK + sizeof(T) * C * LDI;
-    static constexpr uint32_t offGm = (offQ + sizeof(T) * C * LDI + 15) / 16 * 16;
-    static constexpr uint32_t offDO = offGm + sizeof(double) * C * LDG;
-    static constexpr uint32_t offW = offDO + sizeof(float) * C * LDF;     // W, later dGamma
-    static constexpr uint32_t offDX = offW + sizeof(float) * C * LDF;
-    static constexpr uint32_t offA = offDX + sizeof(float) * C * LDF;
-    static constexpr uint32_t offdP = offA + sizeof(float) * C * LDX;
-    static constexpr uint32_t offdPT = offdP + sizeof(float) * C * LDX;
-    static constexpr uint32_t offdA = offdPT + sizeof(float) * C * LDX;
-    static constexpr uint32_t offdAT = offdA + sizeof(float) * C * LDX;
-    static constexpr uint32_t offGp = offdAT + sizeof(float) * C * LDX;   // [3][256] partial Gram tiles
-    static constexpr uint32_t offBeta = offGp + sizeof(float) * 3 * 256;
+    static constexpr uint32_t offGm = offQ + sizeof(T) * C * LDI;
+    static constexpr uint32_t offDO = offGm + sizeof(GT) * C * LDG;
+    static constexpr uint32_t offW = offDO + sizeof(RT) * C * LDR;
+    static constexpr uint32_t offDX = offW + sizeof(RT) * C * LDR;
+    static constexpr uint32_t offA = offDX + sizeof(RT) * C * LDR;
+    static constexpr uint32_t offdP = offA + sizeof(float) * C * LDX;     // first the Gram partials [3][256]
+    static constexpr uint32_t offdA = offdP + sizeof(float) * C * LDX;
+    static constexpr uint32_t offBeta = offdA + sizeof(float) * C * LDX;
     static constexpr uint32_t offDb = offBeta + sizeof(float) * C;        // [NDB][C] partial dbeta
     static constexpr uint32_t offIS = offDb + sizeof(float) * NDB * C;    // [BD] 1 / column scale of S
     static constexpr uint32_t offIG = offIS + sizeof(float) * BD;         // [BD] 1 / column scale of G
     static constexpr uint32_t offRS = offIG + sizeof(float) * BD;         // [NMX][C] row scales
     static constexpr uint32_t bytes = offRS + sizeof(float) * NMX * C;
+    // dGamma (fp32 [C][LDF]) reuses the dO and W rows, dead after part 3
+    static_assert(sizeof(float) * C * LDF <= offDX - offDO, "dGamma fits the dO and W rows");
+    static_assert(3 * 256 * sizeof(float) <= sizeof(float) * C * LDX, "Gram partials fit dP");
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+    static_assert(!kIn16 || bytes <= 80 * 1024, "two 16-bit workgroups per compute unit");
+    static constexpr int WAVES_PER_EU = kIn16 ? 2 : 1;      // the register budget that allows it
 };
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 template <typename T> __device__ __forceinline__ f32x4 ld4(const T *p);
@@ -119,12 +129,20 @@ template <> __device__ __forceinline__ f32x4 ld4<bf16_t>(const bf16_t *p) {
     const bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
     return f32x4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])};
 }
-// e^(a_e - b_e) for four consecutive fp64 entries, the differences in fp64
+template <> __device__ __forceinline__ f32x4 ld4<f16_t>(const f16_t *p) {
+    const f16x4 x = *reinterpret_cast<const f16x4 *>(p);
+    return f32x4{to_f(x[0]), to_f(x[1]), to_f(x[2]), to_f(x[3])};
+}
+// e^(a_e - b_e) for four consecutive Gamma entries, the differences in Gamma's type
 __device__ __forceinline__ f32x4 exp_diff4(const double *a, const double *b) {
     const f64x2 a0 = *reinterpret_cast<const f64x2 *>(a), a1 = *reinterpret_cast<const f64x2 *>(a + 2);
     const f64x2 b0 = *reinterpret_cast<const f64x2 *>(b), b1 = *reinterpret_cast<const f64x2 *>(b + 2);
     return f32x4{__expf((float)(a0[0] - b0[0])), __expf((float)(a0[1] - b0[1])), __expf((float)(a1[0] - b1[0])),
                  __expf((float)(a1[1] - b1[1]))};
+}
+__device__ __forceinline__ f32x4 exp_diff4(const float *a, const float *b) {
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(a) - *reinterpret_cast<const f32x4 *>(b);
+    return f32x4{__expf(x[0]), __expf(x[1]), __expf(x[2]), __expf(x[3])};
 }
 __device__ __forceinline__ float max4(const f32x4 &x) { return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])); }
 __device__ __forceinline__ f32x4 abs4(const f32x4 &x) { return f32x4{fabsf(x[0]), fabsf(x[1]), fabsf(x[2]), fabsf(x[3])}; }
@@ -144,6 +162,18 @@ template <typename OpT> struct Frag {
             for (int e = 0; e < 4; ++e) f[4 * gi + e] = from_f<OpT>(x[gi][e] * scale);
         return f;
     }
+    // fragment of row `row` (elements of type OpT) as stored, no conversion
+    __device__ static __forceinline__ typename M::frag raw(const OpT *row, int k0, int j) {
+        typename M::frag f;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            typedef typename std::conditional<sizeof(OpT) == 2, f16x4, f32x4>::type V;
+            const V x = *reinterpret_cast<const V *>(row + base(k0, j, gi));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[4 * gi + e] = x[e];
+        }
+        return f;
+    }
 };
 }  // namespace bc
 
@@ -151,7 +181,8 @@ template <typename OpT> struct Frag {
 // the chains store them -- fp16 values with column scales [chunks][H][BD]
 // (OpT = fp16) or fp32 (scales unused); U, W, dX: [chunks][H][C][BD] fp32.
 template <typename T>
-__global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
+__global__ __launch_bounds__(bc::NT) __attribute__((amdgpu_waves_per_eu(bc::Cfg<T>::WAVES_PER_EU)))
+void kda_bwd_chunk_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const T *__restrict__ dout, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const void *__restrict__ snaps, const float *__restrict__ snap_scale,
@@ -163,31 +194,32 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     using namespace bc;
     typedef Cfg<T> Q;
     typedef Mma<float> Mf;
-    constexpr bool kIn16 = !std::is_same<T, float>::value;
+    constexpr bool kIn16 = Q::kIn16;
+    typedef typename Q::GT GT;
+    typedef typename Q::RT RT;
     typedef typename std::conditional<kIn16, f16_t, float>::type OpT;   // 128-wide contractions
+    static_assert(std::is_same<OpT, RT>::value, "rows are stored in the operand type");
     typedef Mma<OpT> Mo;
     typedef Frag<OpT> F;
     constexpr int KB = Mo::KB, NG = F::NG;
-    constexpr int LDI = Q::LDI;
+    constexpr int LDI = Q::LDI, LDG = Q::LDG, LDR = Q::LDR;
     extern __shared__ __align__(16) unsigned char smem[];
     T *sK = reinterpret_cast<T *>(smem + Q::offK);
     T *sQ = reinterpret_cast<T *>(smem + Q::offQ);
-    double *sGm = reinterpret_cast<double *>(smem + Q::offGm);
-    float *sDO = reinterpret_cast<float *>(smem + Q::offDO);
-    float *sW = reinterpret_cast<float *>(smem + Q::offW);
-    float *sDX = reinterpret_cast<float *>(smem + Q::offDX);
+    GT *sGm = reinterpret_cast<GT *>(smem + Q::offGm);
+    RT *sDO = reinterpret_cast<RT *>(smem + Q::offDO);
+    RT *sW = reinterpret_cast<RT *>(smem + Q::offW);
+    RT *sDX = reinterpret_cast<RT *>(smem + Q::offDX);
     float *sA = reinterpret_cast<float *>(smem + Q::offA);
     float *sdP = reinterpret_cast<float *>(smem + Q::offdP);
-    float *sdPT = reinterpret_cast<float *>(smem + Q::offdPT);
     float *sdA = reinterpret_cast<float *>(smem + Q::offdA);
-    float *sdAT = reinterpret_cast<float *>(smem + Q::offdAT);
-    float *sGp = reinterpret_cast<float *>(smem + Q::offGp);
+    float *sGp = sdP;
     float *sBeta = reinterpret_cast<float *>(smem + Q::offBeta);
     float *sDb = reinterpret_cast<float *>(smem + Q::offDb);
     float *sIS = reinterpret_cast<float *>(smem + Q::offIS);
     float *sIG = reinterpret_cast<float *>(smem + Q::offIG);
     float *sRS = reinterpret_cast<float *>(smem + Q::offRS);
-    float *sDG = sW;
+    float *sDG = reinterpret_cast<float *>(smem + Q::offDO);
 
     // ---- workgroup -> (chunk, head); the chunk's sequence by binary search
     const int64_t gc = blockIdx.x / H;
@@ -210,234 +242,260 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
     const int64_t unit = gc * H + h;
     const OpT *Sg = static_cast<const OpT *>(snaps) + unit * BD * BD;
     const OpT *Gg = static_cast<const OpT *>(gchunk) + unit * BD * BD;
-    // S and G rows of this lane's key channel for part 3, loaded now so that
-    // they arrive during parts 0-1 (fragment order: K-block, group)
+    // S and G rows of this lane's key channels for part 3 (tile ct: channel
+    // 32 wave + 16 ct + lm), loaded first so that they arrive during parts 0-1
     typedef typename std::conditional<kIn16, f16x4, f32x4>::type V4;
-    const int cc = 16 * wave + lm;
-    V4 spre[BD / KB][NG], gpre[BD / KB][NG];
+    V4 spre[NCT][BD / KB][NG], gpre[NCT][BD / KB][NG];
 #pragma unroll
-    for (int kb = 0; kb < BD / KB; ++kb)
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int j = F::base(kb * KB, lj, gi);
-            spre[kb][gi] = *reinterpret_cast<const V4 *>(Sg + (int64_t)cc * BD + j);
-            gpre[kb][gi] = *reinterpret_cast<const V4 *>(Gg + (int64_t)cc * BD + j);
-        }
-    asm volatile("" ::: "memory");                        // keeps the loads here
+        for (int kb = 0; kb < BD / KB; ++kb)
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const int64_t o = (int64_t)(32 * wave + 16 * ct + lm) * BD + F::base(kb * KB, lj, gi);
+                spre[ct][kb][gi] = *reinterpret_cast<const V4 *>(Sg + o);
+                gpre[ct][kb][gi] = *reinterpret_cast<const V4 *>(Gg + o);
+            }
 
-    // ---- 0. loads.  Thread (row r = tid / 16, part m = tid % 16) takes columns
-    //         8 m .. 8 m + 7 of row r of q, k, dO, W, dX (and U, for the U.dX
-    //         part of dbeta, and the column scales of S and G); a row's 16
-    //         parts are one DPP row, so its sums and maxima are taken across
-    //         those lanes.  Threads 0-127 also take channel tid of the gate for
-    //         the fp64 cumulative sum.  Every global load is issued first, so
-    //         that the part waits for memory once.
+    // ---- 0. loads.  Thread (row r = tid / 16 + 16 pass, part m = tid % 16)
+    //         takes columns 8 m .. 8 m + 7 of row r of q, k, dO, W, dX (and U,
+    //         for the U.dX part of dbeta); a row's 16 parts are one DPP row,
+    //         so its sums and maxima are taken across those lanes, and dO, W
+    //         and dX are stored with their row scales.  Threads 0-127 also take
+    //         channel tid of the gate for the cumulative sum.  Every global load
+    //         is issued first, so that the part waits for memory once.
     {
         typedef typename std::conditional<kIn16, f32x4, f32x4[2]>::type Raw8;   // 8 input elements
-        const int r = tid >> 4, m = tid & 15, cb = 8 * m;
-        const bool ok = r < L;
-        const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cb;
-        const int64_t cho = unit * C * BD + (int64_t)r * BD + cb;   // (chunk, head) row r of U, W, dX
-        Raw8 kraw, qraw, draw;
-        if constexpr (kIn16) {
-            kraw = *reinterpret_cast<const f32x4 *>(k + off);
-            qraw = *reinterpret_cast<const f32x4 *>(q + off);
-            draw = *reinterpret_cast<const f32x4 *>(dout + off);
-        } else {
+        const int m = tid & 15, cb = 8 * m;
+        Raw8 kraw[2], qraw[2], draw[2];
+        f32x4 w[2][2], x[2][2], u[2][2], ss[2], sg[2];
+        float br[2];
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+            const int r = (tid >> 4) + 16 * ps;
+            const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cb;
+            const int64_t cho = unit * C * BD + (int64_t)r * BD + cb;   // rows past the chunk: stored, not used
+            if constexpr (kIn16) {
+                kraw[ps] = *reinterpret_cast<const f32x4 *>(k + off);
+                qraw[ps] = *reinterpret_cast<const f32x4 *>(q + off);
+                draw[ps] = *reinterpret_cast<const f32x4 *>(dout + off);
+            } else {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    kraw[ps][hf] = *reinterpret_cast<const f32x4 *>(k + off + 4 * hf);
+                    qraw[ps][hf] = *reinterpret_cast<const f32x4 *>(q + off + 4 * hf);
+                    draw[ps][hf] = *reinterpret_cast<const f32x4 *>(dout + off + 4 * hf);
+                }
+            }
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                kraw[hf] = *reinterpret_cast<const f32x4 *>(k + off + 4 * hf);
-                qraw[hf] = *reinterpret_cast<const f32x4 *>(q + off + 4 * hf);
-                draw[hf] = *reinterpret_cast<const f32x4 *>(dout + off + 4 * hf);
+                w[ps][hf] = *reinterpret_cast<const f32x4 *>(uw_w + cho + 4 * hf);
+                x[ps][hf] = *reinterpret_cast<const f32x4 *>(dx_chunk + cho + 4 * hf);
+                u[ps][hf] = *reinterpret_cast<const f32x4 *>(uw_u + cho + 4 * hf);
             }
+            br[ps] = beta[(int64_t)(c0 + min(r, L - 1)) * H + h];
         }
-        f32x4 w[2], x[2], u[2], ss[2], sg[2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {   // rows past the chunk read row r of the block (stored, not used)
-            w[hf] = *reinterpret_cast<const f32x4 *>(uw_w + cho + 4 * hf);
-            x[hf] = *reinterpret_cast<const f32x4 *>(dx_chunk + cho + 4 * hf);
-            u[hf] = *reinterpret_cast<const f32x4 *>(uw_u + cho + 4 * hf);
+        for (int hf = 0; hf < 2; ++hf) {
             ss[hf] = kIn16 ? *reinterpret_cast<const f32x4 *>(snap_scale + unit * BD + cb + 4 * hf) : f32x4{1.f, 1.f, 1.f, 1.f};
             sg[hf] = kIn16 ? *reinterpret_cast<const f32x4 *>(g_scale + unit * BD + cb + 4 * hf) : f32x4{1.f, 1.f, 1.f, 1.f};
         }
-        const float br = beta[(int64_t)(c0 + min(r, L - 1)) * H + h];
         float gv[C];
         if (tid < BD) {
 #pragma unroll
             for (int i = 0; i < C; ++i) gv[i] = g[(int64_t)(c0 + min(i, L - 1)) * rowQ + hoff + tid];
         }
         asm volatile("" ::: "memory");                    // keeps the loads together
-        // q, k as they are (zero past the chunk)
-        if constexpr (kIn16) {
-            *reinterpret_cast<f32x4 *>(sK + r * LDI + cb) = ok ? kraw : zero4();
-            *reinterpret_cast<f32x4 *>(sQ + r * LDI + cb) = ok ? qraw : zero4();
-        } else {
+        f32x4 is[2], ig[2];
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                *reinterpret_cast<f32x4 *>(sK + r * LDI + cb + 4 * hf) = ok ? kraw[hf] : zero4();
-                *reinterpret_cast<f32x4 *>(sQ + r * LDI + cb + 4 * hf) = ok ? qraw[hf] : zero4();
-            }
-        }
-        f32x4 d[2];
-        if constexpr (kIn16) {
-            const bf16_t *db = reinterpret_cast<const bf16_t *>(&draw);
-            d[0] = ld4(db);
-            d[1] = ld4(db + 4);
-        } else {
-            d[0] = draw[0];
-            d[1] = draw[1];
-        }
-        float ux = 0.f, mx[NMX] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            if (!ok) d[hf] = w[hf] = x[hf] = u[hf] = zero4();
-            *reinterpret_cast<f32x4 *>(sDO + r * LDF + cb + 4 * hf) = d[hf];
-            *reinterpret_cast<f32x4 *>(sW + r * LDF + cb + 4 * hf) = w[hf];
-            *reinterpret_cast<f32x4 *>(sDX + r * LDF + cb + 4 * hf) = x[hf];
-            f32x4 is, ig;
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                is[e] = pow2_inv(ss[hf][e]);
-                ig[e] = pow2_inv(sg[hf][e]);
+                is[hf][e] = pow2_inv(ss[hf][e]);
+                ig[hf][e] = pow2_inv(sg[hf][e]);
             }
-            if (r == 0) {
-                *reinterpret_cast<f32x4 *>(sIS + cb + 4 * hf) = is;
-                *reinterpret_cast<f32x4 *>(sIG + cb + 4 * hf) = ig;
+        if (tid < 16) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                *reinterpret_cast<f32x4 *>(sIS + cb + 4 * hf) = is[hf];
+                *reinterpret_cast<f32x4 *>(sIG + cb + 4 * hf) = ig[hf];
             }
-            ux += dot4(u[hf], x[hf]);
-            mx[MX_DO] = fmaxf(mx[MX_DO], max4(abs4(d[hf])));
-            mx[MX_DOS] = fmaxf(mx[MX_DOS], max4(abs4(d[hf]) * is));
-            mx[MX_DX] = fmaxf(mx[MX_DX], max4(abs4(x[hf])));
-            mx[MX_DXS] = fmaxf(mx[MX_DXS], max4(abs4(x[hf]) * is));
-            mx[MX_W] = fmaxf(mx[MX_W], max4(abs4(w[hf])));
-            mx[MX_WG] = fmaxf(mx[MX_WG], max4(abs4(w[hf]) * ig));
         }
-        if (ok) {                                         // dv = Diag(b) dX
-            *reinterpret_cast<f32x4 *>(dv + off) = x[0] * br;
-            *reinterpret_cast<f32x4 *>(dv + off + 4) = x[1] * br;
-        }
-        ux = sum16(ux);
 #pragma unroll
-        for (int a = 0; a < NMX; ++a) mx[a] = rowmax16(mx[a]);
-        if (m == 0) {
-            sDb[r] = ux;
-            sBeta[r] = ok ? br : 0.f;
+        for (int ps = 0; ps < 2; ++ps) {
+            const int r = (tid >> 4) + 16 * ps;
+            const bool ok = r < L;
+            const int64_t off = (int64_t)(c0 + min(r, L - 1)) * rowQ + hoff + cb;
+            if constexpr (kIn16) {
+                *reinterpret_cast<f32x4 *>(sK + r * LDI + cb) = ok ? kraw[ps] : zero4();
+                *reinterpret_cast<f32x4 *>(sQ + r * LDI + cb) = ok ? qraw[ps] : zero4();
+            } else {
 #pragma unroll
-            for (int a = 0; a < NMX; ++a) sRS[a * C + r] = kIn16 ? pow2_scale(mx[a]) : 1.f;
+                for (int hf = 0; hf < 2; ++hf) {
+                    *reinterpret_cast<f32x4 *>(sK + r * LDI + cb + 4 * hf) = ok ? kraw[ps][hf] : zero4();
+                    *reinterpret_cast<f32x4 *>(sQ + r * LDI + cb + 4 * hf) = ok ? qraw[ps][hf] : zero4();
+                }
+            }
+            f32x4 d[2];
+            if constexpr (kIn16) {
+                const bf16_t *db = reinterpret_cast<const bf16_t *>(&draw[ps]);
+                d[0] = ld4(db);
+                d[1] = ld4(db + 4);
+            } else {
+                d[0] = draw[ps][0];
+                d[1] = draw[ps][1];
+            }
+            float ux = 0.f, mx[NMX] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                if (!ok) d[hf] = w[ps][hf] = x[ps][hf] = u[ps][hf] = zero4();
+                ux += dot4(u[ps][hf], x[ps][hf]);
+                mx[MX_DO] = fmaxf(mx[MX_DO], max4(abs4(d[hf])));
+                mx[MX_DOS] = fmaxf(mx[MX_DOS], max4(abs4(d[hf]) * is[hf]));
+                mx[MX_DX] = fmaxf(mx[MX_DX], max4(abs4(x[ps][hf])));
+                mx[MX_DXS] = fmaxf(mx[MX_DXS], max4(abs4(x[ps][hf]) * is[hf]));
+                mx[MX_W] = fmaxf(mx[MX_W], max4(abs4(w[ps][hf])));
+                mx[MX_WG] = fmaxf(mx[MX_WG], max4(abs4(w[ps][hf]) * ig[hf]));
+            }
+            if (ok) {                                     // dv = Diag(b) dX
+                *reinterpret_cast<f32x4 *>(dv + off) = x[ps][0] * br[ps];
+                *reinterpret_cast<f32x4 *>(dv + off + 4) = x[ps][1] * br[ps];
+            }
+            ux = sum16(ux);
+            float rs[NMX];
+#pragma unroll
+            for (int a = 0; a < NMX; ++a) rs[a] = kIn16 ? pow2_scale(rowmax16(mx[a])) : 1.f;
+            // dO, W, dX rows in the operand type with their row scales
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sDO[r * LDR + cb + 4 * hf + e] = from_f<RT>(d[hf][e] * rs[MX_DO]);
+                    sW[r * LDR + cb + 4 * hf + e] = from_f<RT>(w[ps][hf][e] * rs[MX_W]);
+                    sDX[r * LDR + cb + 4 * hf + e] = from_f<RT>(x[ps][hf][e] * rs[MX_DX]);
+                }
+            if (m == 0) {
+                sDb[r] = ux;
+                sBeta[r] = ok ? br[ps] : 0.f;
+#pragma unroll
+                for (int a = 0; a < NMX; ++a) sRS[a * C + r] = rs[a];
+            }
         }
         if (tid < BD) {
-            double sum = 0.0;
+            GT sum = 0;
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                if (i < L) sum += (double)gv[i];
+                if (i < L) sum += (GT)gv[i];
                 sGm[i * LDG + tid] = sum;
             }
         }
     }
     __syncthreads();
 
-    // ---- 1. Gram tile A (strictly lower), block x = 0, 1 diagonal (reference:
-    //         the block's middle token), x = 2 the off-diagonal one (reference:
-    //         token 15); waves x and x + 3 take the two halves of the channels,
-    //         wave 6 zeroes the upper block
-    f32x4 gacc = zero4();
-    const int gx = wave % 3, ghalf = wave / 3;
-    const int grb = gx == 0 ? 0 : 16, gib = gx == 1 ? 16 : 0;
-    if (wave < 6) {
-        const int ref = gx == 0 ? 7 : (gx == 1 ? 23 : 15);
-        const int r = grb + lm, i = gib + lm;
-#pragma unroll
-        for (int kb = 4 * ghalf; kb < 4 * ghalf + 4; ++kb) {
+    // ---- 1. Gram tile A (strictly lower): block x = wave for waves 0-2, x = 0,
+    //         1 diagonal (reference: the block's middle token), x = 2 the
+    //         off-diagonal one (reference: token 15); wave 3 zeroes the upper block
+    if (wave < 3) {
+        const int x = wave;
+        const int rb = x == 0 ? 0 : 16, ib = x == 1 ? 16 : 0, ref = x == 0 ? 7 : (x == 1 ? 23 : 15);
+        const int r = rb + lm, i = ib + lm;
+        f32x4 acc = zero4();
+#pragma unroll 4
+        for (int kb = 0; kb < BD / 16; ++kb) {
             const int c = 16 * kb + 4 * lj;
             const f32x4 rf = exp_diff4(sGm + r * LDG + c, sGm + ref * LDG + c);
             const f32x4 cf = exp_diff4(sGm + ref * LDG + c, sGm + i * LDG + c);
-            gacc = Mf::mma(ld4(sK + r * LDI + c) * rf, ld4(sK + i * LDI + c) * cf, gacc);
+            acc = Mf::mma(ld4(sK + r * LDI + c) * rf, ld4(sK + i * LDI + c) * cf, acc);
         }
-        if (ghalf) *reinterpret_cast<f32x4 *>(sGp + gx * 256 + 4 * lane) = gacc;
-    } else if (wave == 6) {
-        for (int e = lane; e < 256; e += 64) sA[(e >> 4) * LDX + 16 + (e & 15)] = 0.f;
-    }
-    __syncthreads();
-    if (wave < 3) {
-        gacc += *reinterpret_cast<const f32x4 *>(sGp + gx * 256 + 4 * lane);
-        const bool diag = gx < 2;
+        const bool diag = x < 2;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const int rr = grb + 4 * lj + ii, cc = gib + lm;
-            sA[rr * LDX + cc] = (!diag || cc < rr) ? gacc[ii] : 0.f;   // a select: entries above may be inf
+            const int rr = rb + 4 * lj + ii, cc = ib + lm;
+            sA[rr * LDX + cc] = (!diag || cc < rr) ? acc[ii] : 0.f;   // a select: entries above may be inf
         }
+    } else {
+        for (int e = lane; e < 256; e += 64) sA[(e >> 4) * LDX + 16 + (e & 15)] = 0.f;
     }
     __syncthreads();
 
     // ---- 3. contractions over the value columns, on the MFMA type of the
-    //         forward: key channel cc of this lane (wave w: 16 w + lm); S and G
+    //         forward: key channels 32 wave + 16 ct + lm of this lane; S and G
     //         rows as prefetched (the fragment's indices along the row)
-    f32x4 dQp[2], dXS[2], dKh[2];
-    dQp[0] = dQp[1] = dXS[0] = dXS[1] = dKh[0] = dKh[1] = zero4();
-    float dgm = 0.f;
-    const float *rsDOS = sRS + MX_DOS * C, *rsDXS = sRS + MX_DXS * C, *rsWG = sRS + MX_WG * C;
+    f32x4 dQp[NCT][2], dXS[NCT][2], dKh[NCT][2];
+    float dgm[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        dgm[ct] = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) dQp[ct][rt] = dXS[ct][rt] = dKh[ct][rt] = zero4();
+    }
 #pragma unroll
     for (int kb = 0; kb < BD / KB; ++kb) {
-        typename Mo::frag st, gt;
+        typename Mo::frag st[NCT], gt[NCT];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const int j = F::base(kb * KB, lj, gi);
-            const V4 sv = spre[kb][gi], gvv = gpre[kb][gi];
             const f32x4 isv = ld4(sIS + j), igv = ld4(sIG + j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                st[4 * gi + e] = sv[e];
-                gt[4 * gi + e] = gvv[e];
-                dgm += (float)sv[e] * isv[e] * ((float)gvv[e] * igv[e]);
-            }
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    st[ct][4 * gi + e] = spre[ct][kb][gi][e];
+                    gt[ct][4 * gi + e] = gpre[ct][kb][gi][e];
+                    dgm[ct] += (float)spre[ct][kb][gi][e] * isv[e] * ((float)gpre[ct][kb][gi][e] * igv[e]);
+                }
         }
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             const int r = 16 * rt + lm;
+            // rows stored with the scales MX_DO, MX_DX, MX_W; here they enter
+            // with MX_DOS, MX_DXS, MX_WG and a column factor 1/sS or 1/sG
+            const float fdo = sRS[MX_DOS * C + r] * pow2_inv(sRS[MX_DO * C + r]);
+            const float fdx = sRS[MX_DXS * C + r] * pow2_inv(sRS[MX_DX * C + r]);
+            const float fw = sRS[MX_WG * C + r] * pow2_inv(sRS[MX_W * C + r]);
             f32x4 ado[NG], adx[NG], aw[NG];
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const int j = F::base(kb * KB, lj, gi);
                 const f32x4 isv = ld4(sIS + j), igv = ld4(sIG + j);
-                ado[gi] = ld4(sDO + r * LDF + j) * isv;
-                adx[gi] = ld4(sDX + r * LDF + j) * isv;
-                aw[gi] = ld4(sW + r * LDF + j) * igv;
+                ado[gi] = ld4(sDO + r * LDR + j) * isv;
+                adx[gi] = ld4(sDX + r * LDR + j) * isv;
+                aw[gi] = ld4(sW + r * LDR + j) * igv;
             }
-            dQp[rt] = Mo::mma(F::make(ado, rsDOS[r]), st, dQp[rt]);
-            dXS[rt] = Mo::mma(F::make(adx, rsDXS[r]), st, dXS[rt]);
-            dKh[rt] = Mo::mma(F::make(aw, rsWG[r]), gt, dKh[rt]);
+            const typename Mo::frag fo = F::make(ado, fdo), fx = F::make(adx, fdx), fwf = F::make(aw, fw);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                dQp[ct][rt] = Mo::mma(fo, st[ct], dQp[ct][rt]);
+                dXS[ct][rt] = Mo::mma(fx, st[ct], dXS[ct][rt]);
+                dKh[ct][rt] = Mo::mma(fwf, gt[ct], dKh[ct][rt]);
+            }
         }
     }
-    dgm = sum_rows4(dgm);                                 // (G (.) S) 1 of channel cc
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < NCT; ++ct) {
+        dgm[ct] = sum_rows4(dgm[ct]);                     // (G (.) S) 1 of the channel
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {                     // undo the row scales
-            const int r = 16 * rt + 4 * lj + i;
-            dQp[rt][i] *= pow2_inv(rsDOS[r]);
-            dXS[rt][i] *= pow2_inv(rsDXS[r]);
-            dKh[rt][i] *= pow2_inv(rsWG[r]);
-        }
-    // dP (waves 0-2) and dN (waves 3-5) by block x, B = W rows with their own
-    // row scales; waves 6-7 zero the upper blocks
-    if (wave < 6) {
-        const int x = wave % 3;
-        const bool isN = wave >= 3, diag = x < 2;
-        const int rb = x == 0 ? 0 : 16, ib = x == 1 ? 16 : 0;
-        const float *rowA = (isN ? sDX : sDO) + (rb + lm) * LDF;
-        const float ra = sRS[(isN ? MX_DX : MX_DO) * C + rb + lm], rw = sRS[MX_W * C + ib + lm];
-        f32x4 acc = zero4();
-#pragma unroll 2
-        for (int kb = 0; kb < BD / KB; ++kb) {
-            f32x4 a[NG], b[NG];
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-                const int j = F::base(kb * KB, lj, gi);
-                a[gi] = ld4(rowA + j);
-                b[gi] = ld4(sW + (ib + lm) * LDF + j);
+            for (int i = 0; i < 4; ++i) {                 // undo the row scales
+                const int r = 16 * rt + 4 * lj + i;
+                dQp[ct][rt][i] *= pow2_inv(sRS[MX_DOS * C + r]);
+                dXS[ct][rt][i] *= pow2_inv(sRS[MX_DXS * C + r]);
+                dKh[ct][rt][i] *= pow2_inv(sRS[MX_WG * C + r]);
             }
-            acc = Mo::mma(F::make(a, ra), F::make(b, rw), acc);
-        }
+    }
+    // dP and dN by block x (jobs 0-2: dP, 3-5: dN; wave w takes jobs w and w + 4),
+    // A = dO or dX rows and B = W rows as stored; wave 3 also zeroes the upper blocks
+#pragma unroll 1
+    for (int job = wave; job < 6; job += NW) {
+        const int x = job % 3;
+        const bool isN = job >= 3, diag = x < 2;
+        const int rb = x == 0 ? 0 : 16, ib = x == 1 ? 16 : 0;
+        const RT *rowA = (isN ? sDX : sDO) + (rb + lm) * LDR;
+        const RT *rowB = sW + (ib + lm) * LDR;
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < BD / KB; ++kb) acc = Mo::mma(F::raw(rowA, kb * KB, lj), F::raw(rowB, kb * KB, lj), acc);
         const float iw = pow2_inv(sRS[MX_W * C + ib + lm]);
         float pb[4];
 #pragma unroll
@@ -445,15 +503,11 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
             const int rr = rb + 4 * lj + ii, c2 = ib + lm;
             const float val = acc[ii] * pow2_inv(sRS[(isN ? MX_DX : MX_DO) * C + rr]) * iw;
             if (!isN) {
-                const float dp = (!diag || c2 <= rr) ? val : 0.f;
-                sdP[rr * LDX + c2] = dp;
-                sdPT[c2 * LDX + rr] = dp;
+                sdP[rr * LDX + c2] = (!diag || c2 <= rr) ? val : 0.f;
                 pb[ii] = 0.f;
             } else {
                 const float dn = (!diag || c2 < rr) ? -val : 0.f;
-                const float da = sBeta[rr] * dn;
-                sdA[rr * LDX + c2] = da;
-                sdAT[c2 * LDX + rr] = da;
+                sdA[rr * LDX + c2] = sBeta[rr] * dn;
                 pb[ii] = sum16(dn * sA[rr * LDX + c2]);
             }
         }
@@ -461,34 +515,39 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) sDb[(1 + x) * C + rb + 4 * lj + ii] = pb[ii];
         }
-    } else {
-        for (int e = tid - 384; e < 256; e += 128) {
+    }
+    if (wave == NW - 1) {
+        for (int e = lane; e < 256; e += 64) {
             const int rr = e >> 4, c2 = 16 + (e & 15);
             sdP[rr * LDX + c2] = 0.f;
-            sdPT[c2 * LDX + rr] = 0.f;
             sdA[rr * LDX + c2] = 0.f;
-            sdAT[c2 * LDX + rr] = 0.f;
         }
-        if (tid - 384 < 16) {     // rows that a block's dbeta part does not cover
-            const int e = tid - 384;
-            sDb[1 * C + 16 + e] = 0.f;
-            sDb[2 * C + e] = 0.f;
-            sDb[3 * C + e] = 0.f;
+        if (lane < 16) {          // rows that a block's dbeta part does not cover
+            sDb[1 * C + 16 + lane] = 0.f;
+            sDb[2 * C + lane] = 0.f;
+            sDb[3 * C + lane] = 0.f;
         }
     }
     __syncthreads();
 
-    // ---- 4. token sums weighted by E, and the per-element results (channel cc)
-    {
-        const int c = cc;
+    // ---- 4. token sums weighted by E, and the per-element results
+    //         (dGamma to LDS over the dO and W rows, dead since part 3)
+#pragma unroll 1
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int c = 32 * wave + 16 * ct + lm;
         auto gm = [&](int t) { return sGm[t * LDG + c]; };
         auto kv = [&](int t) { return to_f(sK[t * LDI + c]); };
         auto qv = [&](int t) { return to_f(sQ[t * LDI + c]); };
+        // transposed A operands: lane row m reads column m of dP / dA
+        auto colA = [&](const float *M, int col, int r0) {
+            return f32x4{M[(r0 + 0) * LDX + col], M[(r0 + 1) * LDX + col], M[(r0 + 2) * LDX + col],
+                         M[(r0 + 3) * LDX + col]};
+        };
         // B operands over tokens: lane group lj takes tokens tb + 4 lj + e
         f32x4 Kcd[2], Krd[2], Qrd[2], Kco, Kro, Qro;
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-            const double gmid = gm(16 * a + 7);
+            const GT gmid = gm(16 * a + 7);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * a + 4 * lj + e;
@@ -499,7 +558,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                 Qrd[a][e] = qv(t) * rf;
             }
         }
-        const double g15 = gm(15);
+        const GT g15 = gm(15);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int ta = 4 * lj + e, tb = 16 + 4 * lj + e;
@@ -514,29 +573,29 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
             const int ro = (16 * a + lm) * LDX + 16 * a + 4 * lj;
             q2d[a] = Mf::mma(ld4(sdP + ro), Kcd[a], zero4());
             kr2d[a] = Mf::mma(ld4(sdA + ro), Kcd[a], zero4());
-            kc2d[a] = Mf::mma(ld4(sdAT + ro), Krd[a], Mf::mma(ld4(sdPT + ro), Qrd[a], zero4()));
+            kc2d[a] = Mf::mma(colA(sdA, 16 * a + lm, 16 * a + 4 * lj), Krd[a],
+                              Mf::mma(colA(sdP, 16 * a + lm, 16 * a + 4 * lj), Qrd[a], zero4()));
         }
         const f32x4 q2o = Mf::mma(ld4(sdP + (16 + lm) * LDX + 4 * lj), Kco, zero4());
         const f32x4 kr2o = Mf::mma(ld4(sdA + (16 + lm) * LDX + 4 * lj), Kco, zero4());
-        const f32x4 kc2o = Mf::mma(ld4(sdAT + lm * LDX + 16 + 4 * lj), Kro,
-                                   Mf::mma(ld4(sdPT + lm * LDX + 16 + 4 * lj), Qro, zero4()));
+        const f32x4 kc2o = Mf::mma(colA(sdA, lm, 16 + 4 * lj), Kro, Mf::mma(colA(sdP, lm, 16 + 4 * lj), Qro, zero4()));
         // the last token's extra terms: sum_r k dK^ e^(Gamma_L - Gamma) and (G (.) S) 1 e^Gamma_L
-        const double gl = gm(L - 1);
+        const GT gl = gm(L - 1);
         float extra = 0.f;
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * rt + 4 * lj + ii;
-                extra += kv(r) * dKh[rt][ii] * __expf((float)(gl - gm(r)));
+                extra += kv(r) * dKh[ct][rt][ii] * __expf((float)(gl - gm(r)));
             }
-        extra = sum_rows4(extra) + dgm * __expf((float)gl);
+        extra = sum_rows4(extra) + dgm[ct] * __expf((float)gl);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * rt + 4 * lj + ii;
-                const double gr = gm(r), gmid = gm(16 * rt + 7);
+                const GT gr = gm(r), gmid = gm(16 * rt + 7);
                 const float dmid = (float)(gr - gmid);
                 float dq2 = __expf(dmid) * q2d[rt][ii], dkr2 = __expf(dmid) * kr2d[rt][ii];
                 float dkc2 = __expf(-dmid) * kc2d[rt][ii];
@@ -548,9 +607,9 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                     dkc2 += __expf((float)(g15 - gr)) * kc2o[ii];
                 }
                 const float eG = __expf((float)gr), eGn = __expf((float)(gl - gr));
-                const float dq_ = dQp[rt][ii] * eG + dq2;
-                const float dkrow = -sBeta[r] * dXS[rt][ii] * eG + dkr2;
-                const float dkcol = dKh[rt][ii] * eGn + dkc2;
+                const float dq_ = dQp[ct][rt][ii] * eG + dq2;
+                const float dkrow = -sBeta[r] * dXS[ct][rt][ii] * eG + dkr2;
+                const float dkcol = dKh[ct][rt][ii] * eGn + dkc2;
                 const float kr = kv(r);
                 float dG = qv(r) * dq_ + kr * dkrow - kr * dkcol;
                 if (r == L - 1) dG += extra;
@@ -558,7 +617,7 @@ __global__ __launch_bounds__(bc::NT) void kda_bwd_chunk_kernel(
                     dq[(int64_t)(c0 + r) * rowQ + hoff + c] = dq_;
                     dk[(int64_t)(c0 + r) * rowQ + hoff + c] = dkrow + dkcol;
                 }
-                sDG[r * LDF + c] = dG;    // sW's last reads were in part 3
+                sDG[r * LDF + c] = dG;
             }
     }
     __syncthreads();

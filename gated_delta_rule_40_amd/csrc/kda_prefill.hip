@@ -1877,7 +1877,7 @@ struct GChainCfg {
 // chunk's dX in dx_chunk ([chunks][H][C][DK] fp32).
 // dinit and the summaries are fp32, G~ / sG (exact).
 template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB>
-__global__ __launch_bounds__(64 * NW) void kda_grad_chain_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) void kda_grad_chain_kernel(
     const TIn *dout, const int32_t *__restrict__ cu_seqlens, int32_t num_seqs, int32_t total_tokens,
     int32_t num_heads, const int32_t *__restrict__ plan, int32_t num_segs, const int32_t *__restrict__ sched,
     const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, void *g_chunk,
