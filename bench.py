@@ -63,6 +63,7 @@ PREFILL_KERNELS = {
     "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
 }
 PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_prefill.hip")
+BACKWARD_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_backward.hip")
 PREFILL_WORKLOADS = ("prefill_t4096_h8", "prefill_4x16384_h32", "prefill_varlen_1m_h16")
 
 
@@ -208,12 +209,21 @@ def kernel_label(name):
                        ("kda_decode_tokens_kernel", "kda_decode_tokens_kernel"), ("kda_decode_kernel", "kda_decode_kernel")):
         if key in name:
             return label
+    dt = "bf16" if "DF16b" in name else "fp32"
     if "kda_prefill_kernel" in name:
-        return "kda_prefill_kernel<%s> (%s)" % ("bf16" if "DF16b" in name else "fp32",
-                                               "chunk operands" if "Li1EEE" in name else "fused")
+        kind = "chunk operands" if "Li1EEE" in name else ("chunk and gradient images" if "Li3EEE" in name else "fused")
+        return "kda_prefill_kernel<%s> (%s)" % (dt, kind)
     if "kda_chain_kernel" in name:
-        kind = "segment summaries" if CP_KINDS["summaries"](name) else "segment outputs"
-        return "kda_chain_kernel<%s> (%s)" % ("bf16" if "DF16b" in name else "fp32", kind)
+        # kda_chain_kernel<TIn, C, NW, NCT, SUMMARY, SB, SNAP>
+        flags = [f[:1] for f in name.split("ELb")[1:4]]
+        kind = "segment summaries" if flags[0] == "1" else (
+            "chunk-start states, U, W" if len(flags) > 2 and flags[2] == "1" else "segment outputs")
+        return "kda_chain_kernel<%s> (%s)" % (dt, kind)
+    if "kda_grad_chain_kernel" in name:
+        kind = "gradient summaries" if name.split("ELb", 1)[1][:1] == "1" else "state gradients at chunk ends, dX"
+        return "kda_grad_chain_kernel<%s> (%s)" % (dt, kind)
+    if "kda_bwd_chunk_kernel" in name:
+        return "kda_bwd_chunk_kernel<%s> (chunk gradients)" % dt
     return name.split("(")[0][:60]
 
 
@@ -249,6 +259,70 @@ def write_stats(trace_dir, workload):
     print("\n".join(lines))
 
 
+def backward_run(workload, calls=5):
+    """Profiling run: kda_backward on this workload `calls` times after one
+    warm-up call (nothing else), printing the time per call."""
+    import torch
+    from gated_delta_rule_40_amd import inputs as I
+    from gated_delta_rule_40_amd import libkda as K
+    K.load()
+    dev = torch.device("cuda:0")
+    b = I.make_prefill(I.WORKLOADS[workload], device=dev)
+    T_, H_ = b["q"].shape[0], b["q"].shape[1]
+    N_ = b["cu_seqlens"].shape[0] - 1
+    gen = torch.Generator(device=dev).manual_seed(7)
+    dout = torch.randn(T_, H_, DV, generator=gen, device=dev).to(torch.bfloat16)
+    ws = torch.empty(K.kda_backward_workspace_size(N_, T_, H_, DK, DV, torch.bfloat16), dtype=torch.uint8, device=dev)
+    grads = K.kda_backward(b["q"], b["k"], b["v"], b["g"], b["beta"], b["initial_state"], b["cu_seqlens"], dout,
+                           None, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(calls):
+        K.kda_backward(b["q"], b["k"], b["v"], b["g"], b["beta"], b["initial_state"], b["cu_seqlens"], dout, None,
+                       grads=grads, workspace=ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    print(json.dumps({"backward_workload": workload, "calls": calls,
+                      "ms_per_call": ev[0].elapsed_time(ev[1]) / calls}), flush=True)
+
+
+def write_backward_stats(trace_dir, workload):
+    """Kernel timeline of the last kda_backward call of a rocprofv3
+    --kernel-trace run of ``bench.py --backward-workload``: start and end of
+    every launch relative to the call's first, so that the two strands that
+    run side by side show as overlapping intervals."""
+    import csv
+    rows = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
+            if "kda" in r["Kernel_Name"]]
+    ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
+    starts = [i for i, k in enumerate(ks) if "kda_cp_plan_kernel" in k[2]]
+    last = ks[starts[-1]:]
+    t0 = last[0][0]
+    short = workload[len("prefill_"):] if workload.startswith("prefill_") else workload
+    path = os.path.join(ROOT, "profiles", "kda_backward_%s_kernel_stats.txt" % short)
+    lines = ["# rocprofv3 kernel trace: one kda_backward call on %s (bf16), MI355X (gfx950)" % workload,
+             "# kernel source sha256/16 (kda_prefill.hip): %s, (kda_backward.hip): %s"
+             % (source_hash(PREFILL_SRC), source_hash(BACKWARD_SRC)),
+             "#",
+             "# command (repo at <repo>):",
+             "#   cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run \\",
+             "#       -- python <repo>/bench.py --backward-workload %s" % workload,
+             "#   python bench.py --backward-stats-from <dir> --backward-workload %s" % workload,
+             "# source: <dir>/run_kernel_trace.csv, the last of the run's %d calls; times in us from the" % len(starts),
+             "# call's first launch (the two strands after the chunk images run on two streams)",
+             "#",
+             "%-64s %9s %9s %9s" % ("kernel", "start", "end", "duration")]
+    for s0, e0, name in last:
+        lines.append("%-64s %9.1f %9.1f %9.1f" % (kernel_label(name), (s0 - t0) / 1e3, (e0 - t0) / 1e3, (e0 - s0) / 1e3))
+    lines.append("")
+    lines.append("# first launch start to last launch end: %.1f us; sum of kernel durations: %.1f us"
+                 % ((last[-1][1] - t0) / 1e3, sum(e0 - s0 for s0, e0, _ in last) / 1e3))
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def write_kernel_summary(trace_dir, name):
     """Average duration of every libkda kernel in a rocprofv3 --kernel-trace
     run of the default bench step (``bench.py --steps 2 --warmup 1
@@ -259,8 +333,7 @@ def write_kernel_summary(trace_dir, name):
             if "kda" in r["Kernel_Name"]]
     agg = {}
     for r in rows:
-        lab = kernel_label(r["Kernel_Name"]) if "backward" not in r["Kernel_Name"] else \
-            r["Kernel_Name"].split("(")[0].replace("void ", "")[:60]
+        lab = kernel_label(r["Kernel_Name"])
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         agg.setdefault(lab, []).append(d)
     path = os.path.join(ROOT, "profiles", "%s_kernel_stats.txt" % name)
@@ -418,7 +491,17 @@ def main():
                     help="write the average duration of every libkda kernel of a bench trace and exit")
     ap.add_argument("--summary-name", default="kda_bench_step",
                     help="file name stem under profiles/ for --kernel-summary-from")
+    ap.add_argument("--backward-workload", choices=PREFILL_WORKLOADS,
+                    help="profiling run: kda_backward on this workload only, and exit")
+    ap.add_argument("--backward-stats-from", metavar="TRACE_DIR",
+                    help="write the kernel timeline of a --backward-workload trace and exit")
     args = ap.parse_args()
+    if args.backward_stats_from:
+        write_backward_stats(args.backward_stats_from, args.backward_workload or "prefill_t4096_h8")
+        return
+    if args.backward_workload:
+        backward_run(args.backward_workload)
+        return
     if args.kernel_summary_from:
         write_kernel_summary(args.kernel_summary_from, args.summary_name)
         return

@@ -33,11 +33,12 @@
  *   - Device pointers are on the current HIP device, dense and row-major as
  *     documented; the caller owns every buffer.  No call allocates device
  *     memory.  The library's global state is a per-device record (atomic
- *     bits) that each kernel's LDS limit has been raised and, for
+ *     bits) that each kernel's LDS limit has been raised; for
  *     kda_prefill_cp_noalloc only, one static device array per GPU
- *     (KDA_STATIC_SCRATCH_BYTES) with its cached address; calls are
- *     thread-safe, except that kda_prefill_cp_noalloc calls overlapping on
- *     one GPU share that array.
+ *     (KDA_STATIC_SCRATCH_BYTES) with its cached address; and, for
+ *     kda_backward only, one stream and three events per GPU (see there).
+ *     Calls are thread-safe, except that kda_prefill_cp_noalloc calls
+ *     overlapping on one GPU share that array.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never
  *     synchronise (except the opt-in KDA_VALIDATE=1 check of cu_seqlens,
  *     below).  Argument errors are returned before any HIP call; a launch
@@ -277,13 +278,20 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  * kda_backward -- gradients for training: given dL/d(out) and dL/d(final
  * state) of a scalar loss L, the gradients with respect to q, k, v, g, beta
  * and the initial state, by the chain rule through the recurrence of card
- * "KDA 单头递归" (page ailearn.mscapital.top/kimi-k3.html) in reverse token order.
- * Sequences are cut into segments that run side by side, as in
- * kda_prefill_cp (card "传固定状态片段"): the gradient recurrence is linear in
- * the state's gradient, so each segment's gradient summary combines, in reverse
- * segment order, into the gradient entering every segment.  A segment's
- * gradient transition is the transpose of its forward transition, which the
- * forward pass that stores the chunk-start states computes anyway.
+ * "KDA 单头递归" (page ailearn.mscapital.top/kimi-k3.html), in chunk form (32
+ * tokens).  Sequences are cut into segments that run side by side, as in
+ * kda_prefill_cp (card "传固定状态片段"): the gradient of the state is linear
+ * in itself, so each segment's gradient summary combines, in reverse segment
+ * order, into the gradient entering every segment; a segment's gradient
+ * transition is the transpose of its forward transition.  The forward states
+ * at chunk starts and the state gradients at chunk ends are computed by two
+ * strands of launches that run side by side: the second runs on a per-device
+ * stream of the library (created on first use, default priority, kept until
+ * the process ends), forked from `stream` and joined back into it with events,
+ * so the call stays ordered on `stream` (also under stream capture).  A final
+ * chunk-parallel pass turns each chunk's states and inputs into its gradients.
+ * Precision as kda_prefill: bf16 inputs run the contractions on fp16 MFMA
+ * operands with exact power-of-two scales, fp32 inputs on fp32 MFMA.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, dtype: as kda_prefill
  *   dout          [total_tokens, num_heads, dv]   dtype
@@ -294,13 +302,14 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  *   dinit         [num_seqs, num_heads, dk, dv]   fp32, or NULL (not written)
  *   workspace     device memory of at least kda_backward_workspace_size(...)
  *                 bytes (for the same sizes and dtype), 256-byte aligned, owned
- *                 by the caller (segment plans, chunk images and the forward
- *                 states at every 32-token chunk start, segment summaries,
- *                 per-workgroup scratch and partial sums); calls sharing it
- *                 must not overlap
+ *                 by the caller (segment plans, chunk and gradient images, the
+ *                 states at every chunk start and state gradients at every
+ *                 chunk end, each chunk's intermediate products, segment
+ *                 summaries and entering states); calls sharing it must not
+ *                 overlap
  * Rows of tokens owned by a sequence are written; others are left untouched.
- * Gradients are fp32 whatever the input dtype.  Deterministic (fixed
- * summation order).
+ * Gradients are fp32 whatever the input dtype.  Deterministic: no result is
+ * accumulated across workgroups, and every sum has a fixed order.
  */
 size_t kda_backward_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                                    int32_t dk, int32_t dv, kda_dtype dtype);
