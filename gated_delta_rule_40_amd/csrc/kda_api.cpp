@@ -37,7 +37,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        float *seg_out, const int32_t *chunk_off, const void *img,
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
-                                       int32_t init_units, hipStream_t stream);
+                                       int32_t init_units, int32_t cmb_fmt, int32_t narrow, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
@@ -59,7 +59,7 @@ extern "C" hipError_t kda_launch_decode_tokens(int bf16, const void *q, const vo
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             int32_t reverse, const int32_t *plan, const int32_t *seq_order,
-                                            const float *m_src, int32_t m_trans, hipStream_t stream);
+                                            const float *m_src, int32_t m_trans, int32_t fmt, hipStream_t stream);
 extern "C" hipError_t kda_launch_decode(int bf16, const void *q, const void *k, const void *v,
                                         const float *g, const float *beta, float *state,
                                         int32_t N, int32_t H, void *out, hipStream_t stream);
@@ -217,6 +217,7 @@ namespace {
 constexpr int32_t kCpChunk = 32;     // chunk size of the segmented runs
 constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the segment-output pass
 constexpr int32_t kCpSumBlock = 256; // value + transition columns per workgroup of the summary pass
+constexpr int64_t kNumCUs = 256;     // compute units of one MI355X
 
 struct CpLayout {
     size_t plan, sched, seq_seg, uplan, usched, useq_seg, seq_order, chunk_off, seg_out, seg_init, img, total;
@@ -226,7 +227,8 @@ struct CpLayout {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Summary units: when there are at least as many (segment, head) pairs as
-// compute units (T / seg_len * H >= 256), output segments (seg_len tokens) are
+// compute units (T / seg_len * H >= 256) and segments are long (at least
+// 1,024 tokens), output segments (seg_len tokens) are
 // cut into up to four units for the summary pass and the combine, so that the
 // summary pass, one workgroup per (unit, head) at one per compute unit, is
 // made of many short pieces that pack the GPU evenly; the output pass still
@@ -237,7 +239,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int32_t cp_unit_len(int32_t seg_len, int32_t T, int32_t H)
 {
     const int32_t m = seg_len / kCpChunk;
-    if ((int64_t)T / seg_len * H < 256) return seg_len;
+    if ((int64_t)T / seg_len * H < 256 || seg_len < 1024) return seg_len;
     return m % 4 == 0 ? seg_len / 4 : (m % 2 == 0 ? seg_len / 2 : seg_len);
 }
 
@@ -347,6 +349,13 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     float *seg_out = reinterpret_cast<float *>(ws + lay.seg_out);
     float *seg_init = reinterpret_cast<float *>(ws + lay.seg_init);
     void *img = ws + lay.img;
+    // summaries in the order the combine loads them (see kda_prefill.hip, CMB_ROWS)
+    const int32_t cmb_fmt = bf16 ? 2 : 1;
+    // eight-wave 128-column workgroups when a pass has fewer workgroups than
+    // the GPU has compute units (bf16)
+    const int64_t out_wgs = (int64_t)lay.max_segs * num_heads;
+    const int32_t narrow_out = bf16 && out_wgs <= kNumCUs ? 1 : 0;
+    const int32_t narrow_sum = bf16 && (int64_t)lay.max_units * num_heads <= kNumCUs ? 1 : 0;
     // output segments and summary units (SEG_LAST: in a sequence's last segment), one launch
     int32_t *seq_order = reinterpret_cast<int32_t *>(ws + lay.seq_order);
     hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
@@ -358,14 +367,14 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
-                             nullptr, nullptr, nullptr, nullptr, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, s);
     if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
-                                  seq_order, nullptr, 0, s);
+                                  seq_order, nullptr, 0, cmb_fmt, s);
     if (e == hipSuccess)   // outputs and final states, each segment from the entering state of its first unit
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
-                             nullptr, nullptr, nullptr, useq_seg, lay.unit_len, lay.max_units, s);
+                             nullptr, nullptr, nullptr, useq_seg, lay.unit_len, lay.max_units, 0, narrow_out, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -645,21 +654,21 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (e == hipSuccess)   // s: forward summaries [S^0 | M] of every segment
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, s);
     if (e == hipSuccess) e = fork(1, s, s2);
     if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
-                                  fsum, 1, s2);
+                                  fsum, 1, 0, s2);
     if (e == hipSuccess)   // s2: the gradient at every chunk end, every chunk's dX, and d(initial state)
         e = kda_launch_grad_chain(bf16, 0, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
                                   sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, dxc, s2);
     if (e == hipSuccess)   // s: the state entering every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_init, 0, nullptr,
-                                  nullptr, nullptr, 0, s);
+                                  nullptr, nullptr, 0, 0, s);
     if (e == hipSuccess)   // s: the state at every chunk start, and every chunk's U and W
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
-                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, s);
+                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, s);
     if (forked) {          // join: s waits for s2 (also after a failed launch)
         const hipError_t j = fork(2, s2, s);
         if (e == hipSuccess) e = j;

@@ -172,7 +172,22 @@ struct SegArgs {
     f32x4 *gimg;                // MODE_PREPG: gradient images, slots as for img
     float *snap_scale;          // kda_chain_kernel state stores, 16-bit inputs: [chunks][H][dv] column scales
     float *uw_u, *uw_w;         // kda_chain_kernel state stores: U and W of every chunk, [chunks][H][C][dv]
+    int32_t cmb_fmt;            // SEG_SUMMARY: layout of seg_out (CMB_ROWS, CMB_F32 or CMB_SPLIT)
 };
+
+// Layouts of a segment summary [S^0 | M] in seg_out, DK (dv + DK) floats per
+// (unit, head) in every layout:
+//   CMB_ROWS: row-major [DK][dv + DK] (S^0 in columns < dv, M after them).
+//   CMB_F32, CMB_SPLIT: in the order in which kda_cp_combine_kernel loads its
+//     MFMA operands, so that every load is one contiguous 1 KB per wave.
+//     First S^0 as accumulator tiles: 16-byte entry ((cb * 8 + r) * 64 + lane)
+//     holds rows 16 r + 4 j + i (i = 0..3) of column 16 cb + m (lane = 16 j + m).
+//     Then M as A-operand fragments, row tile r, lane (j, m) = row 16 r + m:
+//       CMB_F32:   entry (r * 8 + kb) * 64 + lane: M[.][16 kb + 4 j + e], e = 0..3;
+//       CMB_SPLIT: entries ((r * 4 + kb) * 2 + p) * 64 + lane, bf16 x 8: the
+//                  32-block kb (columns 32 kb + 4 j + e and 32 kb + 16 + 4 j + e),
+//                  p = 0 the rounded value hi = bf16(M), p = 1 lo = bf16(M - hi).
+enum { CMB_ROWS = 0, CMB_F32 = 1, CMB_SPLIT = 2 };
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
 __device__ __forceinline__ int64_t seg_init_entry(const SegArgs &seg, int su, int n, int t_start,
@@ -1329,6 +1344,7 @@ struct ChainCfg {
     typedef typename P::OpT OpT;
     typedef ChunkImage<TIn, C> Img;
     static constexpr int NT = 64 * NW, BV = 16 * NW * NCT, NSUB = C / SUB;   // NCT 16-column tiles per wave
+    static constexpr int NCT_ = NCT;
     static constexpr int LDK = P::LDK, LDC = P::LDC, LDV = BV + 16 / (int)sizeof(TIn);
     static constexpr uint32_t offNKp = 0;
     static constexpr uint32_t offQp = offNKp + sizeof(OpT) * C * LDK;
@@ -1342,6 +1358,8 @@ struct ChainCfg {
     static constexpr uint32_t BUF = (offV + sizeof(TIn) * C * LDV + 15) / 16 * 16;   // one chunk buffer
     static constexpr uint32_t offO = (SB ? 1 : 2) * BUF;                       // [NW][C][16 NCT] outputs
     static constexpr uint32_t bytes = offO + sizeof(TIn) * NW * C * 16 * NCT;
+    // the LDS transpose of a summary's M columns (write_summary_frags) fits
+    static constexpr bool kCmbFits = sizeof(float) * DK * ((BV < DK ? BV : DK) + 4) <= bytes;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
     static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
@@ -1352,6 +1370,75 @@ struct ChainCfg {
     static constexpr int VITEMS = (C * VPR + NT - 1) / NT;
     static constexpr int OVEC = C * 16 * NCT / VEC;                 // vectors of one wave's output tile
 };
+
+// A segment summary in the CMB_F32 / CMB_SPLIT layout (see CMB_ROWS): the
+// S^0 columns go out straight from the accumulator tiles; M's columns (the
+// transition columns, each held by one lane) are transposed through the LDS,
+// which the walk no longer uses, and written as row fragments.  Every thread
+// of the workgroup calls this (it holds barriers).
+template <typename Q>
+__device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const f32x4 (&S)[Q::NCT_][DK / 16],
+                                                    const float (&sS)[Q::NCT_], const int (&colc)[Q::NCT_], int dv,
+                                                    int dv0, unsigned char *smem, int wave, int lane, int lj, int lm)
+{
+    constexpr int NCT = Q::NCT_, BV = Q::BV, NW = Q::NT / 64;
+    constexpr int NCM = BV < DK ? BV : DK;           // most transition columns in one block
+    constexpr int LDM = NCM + 4;                     // padded LDS row (floats): conflict-free half-wave writes
+    static_assert(sizeof(float) * DK * LDM <= Q::bytes, "M transpose fits the chain kernel's LDS");
+    f32x4 *s0f = reinterpret_cast<f32x4 *>(blob);
+    f32x4 *mf = reinterpret_cast<f32x4 *>(blob + (int64_t)DK * dv);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = colc[ct];
+        if (dv0 + 16 * (NCT * wave + ct) < dv) {      // wave-uniform: a value tile
+            const float inv = pow2_inv(sS[ct]);
+            const int cb = col >> 4;
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) s0f[(cb * 8 + r) * 64 + lane] = S[ct][r] * inv;
+        }
+    }
+    const int c_lo = max(dv0, dv) - dv, nc = dv0 + BV - max(dv0, dv);   // this block's columns of M
+    if (nc <= 0) return;                             // block-uniform
+    float *sM = reinterpret_cast<float *>(smem);     // [DK][LDM]: M rows, this block's columns
+    __syncthreads();                                 // every wave is done with the chunk buffers
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int col = colc[ct];
+        if (dv0 + 16 * (NCT * wave + ct) >= dv) {
+            const float inv = pow2_inv(sS[ct]);
+            const int c = col - dv - c_lo;
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sM[(16 * r + 4 * lj + i) * LDM + c] = S[ct][r][i] * inv;
+        }
+    }
+    __syncthreads();
+    if (fmt == CMB_SPLIT) {
+        for (int r = wave; r < DK / 16; r += NW)
+            for (int kb = 0; kb < nc / 32; ++kb) {
+                const float *row = sM + (16 * r + lm) * LDM + 32 * kb + 4 * lj;
+                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
+                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 16);
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hi[e] = from_f<bf16_t>(x0[e]);
+                    hi[e + 4] = from_f<bf16_t>(x1[e]);
+                    lo[e] = from_f<bf16_t>(x0[e] - to_f(hi[e]));
+                    lo[e + 4] = from_f<bf16_t>(x1[e] - to_f(hi[e + 4]));
+                }
+                const int kg = c_lo / 32 + kb;
+                mf[((r * 4 + kg) * 2) * 64 + lane] = __builtin_bit_cast(f32x4, hi);
+                mf[((r * 4 + kg) * 2 + 1) * 64 + lane] = __builtin_bit_cast(f32x4, lo);
+            }
+    } else {
+        for (int r = wave; r < DK / 16; r += NW)
+            for (int kb = 0; kb < nc / 16; ++kb)
+                mf[(r * 8 + c_lo / 16 + kb) * 64 + lane] =
+                    *reinterpret_cast<const f32x4 *>(sM + (16 * r + lm) * LDM + 16 * kb + 4 * lj);
+    }
+}
 
 // SNAP (outputs only; the backward's forward pass): also store the state at
 // the start of every chunk at its global index in seg.snap ([chunks][H][DK][dv],
@@ -1607,6 +1694,13 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
     }
     }
 
+    if constexpr (SUMMARY && Q::kCmbFits) {   // (the host passes CMB_ROWS to the others)
+        if (seg.cmb_fmt != CMB_ROWS) {
+            write_summary_frags<Q>(seg.seg_out + ((int64_t)su * num_heads + h) * DK * (dv + DK), seg.cmb_fmt, S, sS,
+                                   colc, dv, dv0, smem, wave, lane, lj, lm);
+            return;
+        }
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const int col = colc[ct];
@@ -2226,13 +2320,24 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 //   reverse: the walk goes from the last segment to the first (gradients of
 //     the state, which enter a segment at its end): G(last) = init,
 //     G(s-1) = R_s G(s) + G_s^0, with R_s = M_s^T when MT.
+//   FMT: the layout of seg_out (CMB_ROWS, CMB_F32 or CMB_SPLIT; the last two
+//     for forward walks without m_src).  With the fragment layouts every
+//     operand load is a contiguous 1 KB per wave; row-major M costs a cache
+//     line per 16 bytes read, which bounded the step.  CMB_SPLIT runs the
+//     product on bf16 MFMA in three terms, M S ~ Mh Sh + Mh Sl + Ml Sh, with
+//     x = xh + xl split by rounding (relative error of a product about 2^-16,
+//     against fp32 MFMA at 32 cycles per 16x16x4 step); each wave splits its
+//     own tile of the state once and the halves are exchanged through LDS.
 constexpr int CMB_COLS = 16;
 constexpr int CMB_THREADS = 64 * (DK / 16);
 struct CmbOps {
-    f32x4 m[DK / 16];   // M rows 16 w + lm, columns 16 kb + 4 lj .. + 3 (the k order of Mma<float>)
+    // CMB_ROWS, CMB_F32: M rows 16 w + lm, columns 16 kb + 4 lj .. + 3 (the k
+    // order of Mma<float>); CMB_SPLIT: m[2 kb + p] holds the bf16 x 8 fragment
+    // of 32-block kb, p = 0 hi, 1 lo
+    f32x4 m[DK / 16];
     f32x4 s0;           // S^0 rows 16 w + 4 lj + i, this lane's column
 };
-template <bool MT>
+template <bool MT, int FMT>
 __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float *__restrict__ init, int32_t N,
                                                                      int32_t H, int32_t dv,
                                                                      const int32_t *__restrict__ seq_seg,
@@ -2279,15 +2384,45 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
             }
         }
     }
-    sS[wave][lane] = own;
-    __syncthreads();
+    // The state slice in LDS.  CMB_ROWS / CMB_F32: sS[w][lane] = tile w (fp32),
+    // and S[r] = tile r.  CMB_SPLIT: the 16-byte entry (2 kb + p) * 64 + lane
+    // holds the bf16 B fragment p (0 hi, 1 lo) of 32-block kb -- elements 0..3
+    // from tile 2 kb, 4..7 from tile 2 kb + 1 -- and S[2 kb + p] is that fragment.
+    auto publish = [&](const f32x4 &x) {
+        if constexpr (FMT == CMB_SPLIT) {
+            bf16x4 hi, lo;
 #pragma unroll
-    for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
-    own = sS[wave][lane];
+            for (int i = 0; i < 4; ++i) {
+                hi[i] = from_f<bf16_t>(x[i]);
+                lo[i] = from_f<bf16_t>(x[i] - to_f(hi[i]));
+            }
+            bf16x4 *dst = reinterpret_cast<bf16x4 *>(&sS[0][0]);
+            dst[(((wave >> 1) * 2) * 64 + lane) * 2 + (wave & 1)] = hi;
+            dst[(((wave >> 1) * 2 + 1) * 64 + lane) * 2 + (wave & 1)] = lo;
+        } else {
+            sS[wave][lane] = x;
+        }
+    };
+    auto gather = [&]() {
+        const f32x4 *src = &sS[0][0];
+#pragma unroll
+        for (int r = 0; r < DK / 16; ++r) S[r] = src[r * 64 + lane];
+    };
+    publish(own);
+    __syncthreads();
+    gather();
     auto seg_of = [&](int it) { return reverse ? s1 - 1 - it : s0 + it; };
     auto fetch = [&](int it, CmbOps &o) {                  // step it's operands (clamped to the last step)
         const int64_t gs = seg_of(min(it, ns - 2));
         const float *src = seg_out + (gs * H + h) * DK * ld;
+        if constexpr (FMT != CMB_ROWS) {
+            const f32x4 *s0f = reinterpret_cast<const f32x4 *>(src);
+            const f32x4 *mf = reinterpret_cast<const f32x4 *>(src + (int64_t)DK * dv);
+            o.s0 = s0f[((col >> 4) * 8 + wave) * 64 + lane];
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; ++kb) o.m[kb] = mf[(wave * 8 + kb) * 64 + lane];
+            return;
+        }
         const float *msrc = m_src ? m_src + (gs * H + h) * DK * ldm : src;
         if constexpr (MT) {                                // A[i][k] = M[k][i]
 #pragma unroll
@@ -2313,19 +2448,30 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
     auto step = [&](int it, CmbOps &cur) {
         write_own(it);
         f32x4 a = cur.s0, b = zero4();                      // two accumulation chains
+        if constexpr (FMT == CMB_SPLIT) {
 #pragma unroll
-        for (int kb = 0; kb < DK / 16; kb += 2) {
-            a = M::mma(cur.m[kb], S[kb], a);
-            b = M::mma(cur.m[kb + 1], S[kb + 1], b);
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                const bf16x8 mh = __builtin_bit_cast(bf16x8, cur.m[2 * kb]);
+                const bf16x8 ml = __builtin_bit_cast(bf16x8, cur.m[2 * kb + 1]);
+                const bf16x8 sh = __builtin_bit_cast(bf16x8, S[2 * kb]), sl = __builtin_bit_cast(bf16x8, S[2 * kb + 1]);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh, sh, a, 0, 0, 0);
+                b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mh, sl, b, 0, 0, 0);
+                b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ml, sh, b, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < DK / 16; kb += 2) {
+                a = M::mma(cur.m[kb], S[kb], a);
+                b = M::mma(cur.m[kb + 1], S[kb + 1], b);
+            }
         }
         fetch(it + 3, cur);
         asm volatile("" ::: "memory");                     // keeps the loads here (not sunk into a later step)
         __syncthreads();                                   // every wave's reads of the previous slice are done
         own = a + b;
-        sS[wave][lane] = own;
+        publish(own);
         __syncthreads();
-#pragma unroll
-        for (int r = 0; r < DK / 16; ++r) S[r] = sS[r][lane];
+        gather();
     };
     // whole rounds of three steps with no exit inside (the wait for each
     // step's operands then stays exact across the loop's back edge), then the
@@ -2435,22 +2581,30 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
 // nullptr): the state at every chunk start, [chunks][H][DK][dv] as
 // store_scaled_state writes it (bf16: fp16 values, column scales in
 // snap_scale [chunks][H][dv]), and every chunk's U and W in uw_u, uw_w
-// ([chunks][H][32][dv] fp32).
+// ([chunks][H][32][dv] fp32).  cmb_fmt (summaries only): the layout of
+// seg_out, CMB_ROWS, or CMB_SPLIT for bf16 / CMB_F32 for fp32 (dv = 128).
+// narrow (bf16; dv_block 256 or 128): 128-column workgroups of eight waves,
+// for calls with fewer workgroups than compute units.
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
-                                       int32_t init_units, hipStream_t stream)
+                                       int32_t init_units, int32_t cmb_fmt, int32_t narrow, hipStream_t stream)
 {
     using namespace kda;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
+    // the fragment layouts: bf16 summaries in 256-column blocks (128 when
+    // narrow), fp32 in 64-column blocks
+    if (cmb_fmt != CMB_ROWS && (mode != SEG_SUMMARY || dv != DK || snap ||
+                                (bf16 ? cmb_fmt != CMB_SPLIT || dv_block != 256 : cmb_fmt != CMB_F32)))
+        return hipErrorInvalidValue;
     if (snap && ((bf16 && !snap_scale) || !uw_u || !uw_w)) return hipErrorInvalidValue;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img)),
                    mode == SEG_SUMMARY ? nullptr : static_cast<float *>(snap), 0, 0, sched, init_seq_seg, init_unit,
-                   init_units, 0, 0, nullptr, snap_scale, uw_u, uw_w};
+                   init_units, 0, 0, nullptr, snap_scale, uw_u, uw_w, cmb_fmt};
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
@@ -2458,6 +2612,11 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     // images are twice as large and their buffers fit the LDS at 64 columns only
     // with state stores: 64 columns per workgroup (the two-tile form has no registers left for them)
     if (bf16 && seg.snap) return launch_chain_t<bf16_t, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    // narrow (bf16, few workgroups): 128 columns per workgroup as 8 waves of
+    // one tile each -- two waves per SIMD, each with half of a chunk's
+    // contractions, so that one wave's dependent steps overlap the other's
+    if (bf16 && narrow && (dv_block == 256 || dv_block == 128))
+        return launch_chain_t<bf16_t, 32, 8, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (bf16 && dv_block == 256) return launch_chain_t<bf16_t, 32, 8, 2>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (bf16 && dv_block == 128) return launch_chain_t<bf16_t, 32, 4, 2, true>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     if (dv_block != 64 && dv_block != 128 && dv_block != 256) return hipErrorInvalidValue;
@@ -2497,14 +2656,20 @@ extern "C" size_t kda_chunk_image_bytes(int bf16)
 extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_t H, int32_t dv,
                                             const int32_t *seq_seg, const float *seg_out, float *seg_init,
                                             int32_t reverse, const int32_t *plan, const int32_t *seq_order,
-                                            const float *m_src, int32_t m_trans, hipStream_t stream)
+                                            const float *m_src, int32_t m_trans, int32_t fmt, hipStream_t stream)
 {
-    const int64_t grid = ((int64_t)N * H + 7) / 8 * 8 * (dv / kda::CMB_COLS);
+    using namespace kda;
+    const int64_t grid = ((int64_t)N * H + 7) / 8 * 8 * (dv / CMB_COLS);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (m_trans && !m_src) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(m_trans ? kda::kda_cp_combine_kernel<true> : kda::kda_cp_combine_kernel<false>,
-                       dim3((unsigned)grid), dim3(kda::CMB_THREADS), 0, stream, init, N, H, dv, seq_seg, seg_out,
+    if (fmt != CMB_ROWS && ((fmt != CMB_F32 && fmt != CMB_SPLIT) || m_src || reverse || dv != DK))
+        return hipErrorInvalidValue;
+    auto kern = m_trans ? kda_cp_combine_kernel<true, CMB_ROWS>
+                        : fmt == CMB_F32   ? kda_cp_combine_kernel<false, CMB_F32>
+                          : fmt == CMB_SPLIT ? kda_cp_combine_kernel<false, CMB_SPLIT>
+                                             : kda_cp_combine_kernel<false, CMB_ROWS>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CMB_THREADS), 0, stream, init, N, H, dv, seq_seg, seg_out,
                        seg_init, reverse, plan, seq_order, m_src);
     return hipGetLastError();
 }
