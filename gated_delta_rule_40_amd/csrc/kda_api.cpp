@@ -20,17 +20,15 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block, cons
                                          int32_t N, int32_t T_tot, int32_t H, int32_t dv,
                                          void *out, float *fin, float *snap, int32_t snap_every,
                                          int32_t max_snaps, const int32_t *snap_chunk_off, hipStream_t stream);
-extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
-                                         int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
-                                         int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
-                                         int32_t last_len, int32_t skip_last, int32_t *seq_order,
-                                         int32_t seg_len2, int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
-                                         int32_t *sched2, int32_t last_len2, int32_t skip_last2,
-                                         int32_t *seq_order2, hipStream_t stream);
-extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
-                                            const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
-                                            int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
-                                            void *gimg, hipStream_t stream);
+extern "C" hipError_t kda_launch_cp_plan_prep(int bf16, const void *q, const void *k, const float *g,
+                                              const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
+                                              int32_t H, int64_t max_chunks, void *img, void *gimg,
+                                              int32_t seg_len, int32_t max_segs, int32_t *plan, int32_t *seq_seg,
+                                              int32_t *chunk_off, int32_t *sched, int32_t last_len,
+                                              int32_t skip_last, int32_t *seq_order, int32_t seg_len2,
+                                              int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
+                                              int32_t *sched2, int32_t last_len2, int32_t skip_last2,
+                                              int32_t *seq_order2, hipStream_t stream);
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
@@ -358,12 +356,11 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     const int32_t narrow_sum = bf16 && (int64_t)lay.max_units * num_heads <= kNumCUs ? 1 : 0;
     // output segments and summary units (SEG_LAST: in a sequence's last segment), one launch
     int32_t *seq_order = reinterpret_cast<int32_t *>(ws + lay.seq_order);
-    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, sched, 0, 0, nullptr, lay.unit_len,
-                                      lay.max_units, uplan, useq_seg, usched, seg_len, 1, seq_order, s);
-    if (e == hipSuccess)   // chunk operands of every (chunk, head)
-        e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
-                                  lay.max_chunks, img, nullptr, s);
+    // and the chunk operands of every (chunk, head); one launch for up to 256 sequences
+    hipError_t e = kda_launch_cp_plan_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                                           lay.max_chunks, img, nullptr, seg_len, lay.max_segs, plan, seq_seg,
+                                           chunk_off, sched, 0, 0, nullptr, lay.unit_len, lay.max_units, uplan,
+                                           useq_seg, usched, seg_len, 1, seq_order, s);
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
@@ -633,16 +630,14 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
         hipError_t r = hipEventRecord(ss->ev[i], from);
         return r == hipSuccess ? hipStreamWaitEvent(to, ss->ev[i], 0) : r;
     };
-    // segments and chunk numbering; no segment is marked last, so the forward
-    // summaries include every segment's transition
-    hipError_t e = kda_launch_cp_plan(cu_seqlens, num_seqs, total_tokens, lay.seg_len, lay.max_segs, plan, seq_seg,
-                                      kCpChunk, lay.max_chunks, chunk_off, sched, -1, 0, nullptr, 0, 0, nullptr,
-                                      nullptr, nullptr, 0, 0, nullptr, s);
-    // chunk operands of every (chunk, head): the forward image and the
-    // transposed one of the gradient chain
-    if (e == hipSuccess)
-        e = kda_launch_chunk_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads, chunk_off,
-                                  lay.max_chunks, img, gimg, s);
+    // segments and chunk numbering (no segment is marked last, so the forward
+    // summaries include every segment's transition), and the chunk operands of
+    // every (chunk, head): the forward image and the transposed one of the
+    // gradient chain; one launch for up to 256 sequences
+    hipError_t e = kda_launch_cp_plan_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                                           lay.max_chunks, img, gimg, lay.seg_len, lay.max_segs, plan, seq_seg,
+                                           chunk_off, sched, -1, 0, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0,
+                                           nullptr, s);
     bool forked = false;
     if (e == hipSuccess) {
         e = fork(0, s, s2);

@@ -149,6 +149,14 @@ struct PrefillCfg {
 // entering state (seg_init) and writes outputs and, for a last segment, the
 // final state.
 enum { SEG_OUTPUT = 0, SEG_SUMMARY = 1 };
+// Arguments of one segment plan (see cp_plan_body).
+struct PlanArgs {
+    int32_t seg_len, max_segs;
+    int32_t *plan, *seq_seg, *chunk_off, *sched;   // chunk_off, sched may be nullptr
+    int32_t last_len, skip_last;
+    int32_t *seq_order;                            // may be nullptr
+};
+
 struct SegArgs {
     const int32_t *plan;     // [num_segs][4] or nullptr (one unit per sequence)
     int32_t num_segs;
@@ -173,7 +181,128 @@ struct SegArgs {
     float *snap_scale;          // kda_chain_kernel state stores, 16-bit inputs: [chunks][H][dv] column scales
     float *uw_u, *uw_w;         // kda_chain_kernel state stores: U and W of every chunk, [chunks][H][C][dv]
     int32_t cmb_fmt;            // SEG_SUMMARY: layout of seg_out (CMB_ROWS, CMB_F32 or CMB_SPLIT)
+    // chunk-operand pass: the first plan_wgs (0, 1 or 2) workgroups build the
+    // segment plans pl[0], pl[1] instead (num_seqs <= 256; the others then
+    // find their chunks from cu_seqlens themselves)
+    int32_t plan_wgs;
+    PlanArgs pl[2];
 };
+
+// One plan per 256-thread workgroup, in LDS scan[256], cscan[256] (int64) and hist[256].
+__device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int32_t N, int32_t T_tot,
+                                             int32_t chunk, int32_t max_chunks, const PlanArgs pa, int64_t *scan,
+                                             int64_t *cscan, int32_t *hist)
+{
+    const int32_t seg_len = pa.seg_len, max_segs = pa.max_segs, last_len = pa.last_len, skip_last = pa.skip_last;
+    int32_t *const plan = pa.plan, *const seq_seg = pa.seq_seg, *const chunk_off = pa.chunk_off;
+    int32_t *const sched = pa.sched, *const seq_order = pa.seq_order;
+    int64_t carry = 0, ccarry = 0;                     // 64-bit: cu is not trusted
+    for (int base = 0; base < N; base += 256) {
+        const int n = base + (int)threadIdx.x;
+        int32_t t0 = 0, t1 = 0, ns = 0, nc = 0;
+        if (n < N) {
+            t0 = min(max(cu[n], 0), T_tot);
+            t1 = min(max(cu[n + 1], t0), T_tot);
+            ns = max(1, (int32_t)(((int64_t)t1 - t0 + seg_len - 1) / seg_len));
+            nc = (int32_t)(((int64_t)t1 - t0 + chunk - 1) / chunk);
+        }
+        scan[threadIdx.x] = ns;
+        cscan[threadIdx.x] = nc;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {       // inclusive scans
+            const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+            const int64_t y = threadIdx.x >= (unsigned)off ? cscan[threadIdx.x - off] : 0;
+            __syncthreads();
+            scan[threadIdx.x] += x;
+            cscan[threadIdx.x] += y;
+            __syncthreads();
+        }
+        if (chunk_off && n < N) chunk_off[n] = (int32_t)min(ccarry + cscan[threadIdx.x] - nc, (int64_t)max_chunks);
+        const int64_t start = carry + scan[threadIdx.x] - ns;
+        if (n < N) {
+            // With non-decreasing cu the host bound on max_segs always holds;
+            // otherwise segments past it are dropped (memory-safe, result unspecified).
+            seq_seg[n] = (int32_t)min(start, (int64_t)max_segs);
+            // SEG_LAST: the segment lies in the sequence's last stretch of
+            // last_len tokens (a multiple of seg_len), which no later segment follows
+            const int64_t nl = last_len > 0 ? max((int64_t)1, ((int64_t)t1 - t0 + last_len - 1) / last_len) : 1;
+            for (int s = 0; s < ns && start + s < max_segs; ++s) {
+                const int gs = (int)(start + s);
+                plan[4 * gs] = n;
+                plan[4 * gs + 1] = t0 + s * seg_len;
+                plan[4 * gs + 2] = min(t0 + (s + 1) * seg_len, t1);
+                plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) |
+                                   (last_len > 0 && (int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
+            }
+        }
+        carry += scan[255];
+        ccarry += cscan[255];
+        __syncthreads();
+    }
+    const int32_t used = (int32_t)min(carry, (int64_t)max_segs);
+    if (threadIdx.x == 0) seq_seg[N] = used;
+    if (seq_order) {
+        // sequences by segment count, most first (counting sort on 256
+        // buckets; 255 segments and more share the first): the combine walks
+        // the longest chains first
+        __syncthreads();   // every seq_seg entry written
+        hist[threadIdx.x] = 0;
+        __syncthreads();
+        auto seq_bucket = [&](int n) { return 255 - min(max(seq_seg[n + 1] - seq_seg[n], 0), 255); };
+        for (int n = (int)threadIdx.x; n < N; n += 256) atomicAdd(&hist[seq_bucket(n)], 1);
+        __syncthreads();
+        const int32_t c = hist[threadIdx.x];
+        scan[threadIdx.x] = c;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+            __syncthreads();
+            scan[threadIdx.x] += x;
+            __syncthreads();
+        }
+        hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - c);
+        __syncthreads();
+        for (int n = (int)threadIdx.x; n < N; n += 256) seq_order[atomicAdd(&hist[seq_bucket(n)], 1)] = n;
+        __syncthreads();   // hist and scan are reused below
+    }
+    if (chunk_off && threadIdx.x == 0) chunk_off[N] = (int32_t)min(ccarry, (int64_t)max_chunks);
+    for (int gs = used + (int)threadIdx.x; gs < max_segs; gs += 256) {
+        plan[4 * gs] = -1;
+        plan[4 * gs + 1] = 0;
+        plan[4 * gs + 2] = 0;
+        plan[4 * gs + 3] = 0;
+        if (sched) sched[gs] = gs;
+    }
+    if (!sched) return;
+    // Dispatch order, longest segment first: workgroups start in index order,
+    // so the short tail segments fill the gaps the full-length ones leave at
+    // the end of a pass.  Counting sort on 256 length buckets (bucket 0 = full
+    // length, 255 = empty); the order inside a bucket does not matter, since
+    // the segments of one pass are independent.  skip_last: SEG_LAST segments
+    // count as empty (a summary pass skips them).
+    auto seg_bucket = [&](int gs) {
+        int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
+        if (skip_last && (plan[4 * gs + 3] & SEG_LAST)) len = 0;
+        return (int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len);
+    };
+    hist[threadIdx.x] = 0;
+    __syncthreads();   // also makes this workgroup's plan entries visible below
+    for (int gs = (int)threadIdx.x; gs < used; gs += 256) atomicAdd(&hist[seg_bucket(gs)], 1);
+    __syncthreads();
+    const int32_t cnt = hist[threadIdx.x];
+    scan[threadIdx.x] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
+        __syncthreads();
+        scan[threadIdx.x] += x;
+        __syncthreads();
+    }
+    hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - cnt);   // bucket start
+    __syncthreads();
+    for (int gs = (int)threadIdx.x; gs < used; gs += 256) sched[atomicAdd(&hist[seg_bucket(gs)], 1)] = gs;
+}
+
 
 // Layouts of a segment summary [S^0 | M] in seg_out, DK (dv + DK) floats per
 // (unit, head) in every layout:
@@ -748,14 +877,50 @@ void kda_prefill_kernel(
     // the fused kernel runs whole sequences; segments run in kda_chain_kernel
     constexpr bool segmented = false;
     constexpr bool summary = false;
-    const int wg = blockIdx.x;
+    if constexpr (kPrep) {
+        static_assert(!kPrep || NT == 256, "the plan and the chunk scan take 256 threads");
+        if ((int)blockIdx.x < seg.plan_wgs) {      // this launch's plan workgroups
+            int64_t *scan = reinterpret_cast<int64_t *>(smem);
+            cp_plan_body(cu_seqlens, num_seqs, total_tokens, C, seg.img_slots, blockIdx.x == 0 ? seg.pl[0] : seg.pl[1],
+                         scan, scan + 256, reinterpret_cast<int32_t *>(scan + 512));
+            return;
+        }
+    }
+    const int wg = (int)blockIdx.x - (kPrep ? seg.plan_wgs : 0);
     int su = 0, h = 0, n = 0, vb = 0, t_start = 0, t_end = 0, sflags = SEG_FIRST | SEG_LAST;
     int gc_begin = 0, nch = 0;      // chunk-operand pass: first global chunk, chunk count
     if constexpr (kPrep) {
         h = wg % num_heads;
         const int grp = min(max(seg.prep_group, 1), PREP_GROUP);
         gc_begin = (wg / num_heads) * grp;
-        const int total_chunks = seg.chunk_off[num_seqs];
+        int total_chunks;
+        if (seg.plan_wgs > 0) {
+            // num_seqs <= 256 and the plan is built by this launch: the first
+            // chunk of each sequence (chunk_off as the plan writes it) from an
+            // inclusive scan of the chunk counts, in LDS that phase 1 rewrites
+            int64_t *sc = reinterpret_cast<int64_t *>(smem);
+            int32_t *st = reinterpret_cast<int32_t *>(sc + 256);   // clamped token ranges [2][256]
+            const int t = (int)threadIdx.x;
+            int64_t ncs = 0;
+            if (t < num_seqs) {
+                const int32_t t0 = min(max(cu_seqlens[t], 0), total_tokens);
+                const int32_t t1 = min(max(cu_seqlens[t + 1], t0), total_tokens);
+                ncs = ((int64_t)t1 - t0 + C - 1) / C;
+                st[t] = t0;
+                st[256 + t] = t1;
+            }
+            sc[t] = ncs;
+            __syncthreads();
+            for (int off = 1; off < 256; off <<= 1) {
+                const int64_t x = t >= off ? sc[t - off] : 0;
+                __syncthreads();
+                sc[t] += x;
+                __syncthreads();
+            }
+            total_chunks = (int)min(sc[255], (int64_t)seg.img_slots);
+        } else {
+            total_chunks = seg.chunk_off[num_seqs];
+        }
         if (gc_begin >= total_chunks) return;
         nch = min(grp, total_chunks - gc_begin);
     } else {
@@ -791,16 +956,30 @@ void kda_prefill_kernel(
     if constexpr (kPrep) {
         if (threadIdx.x < (unsigned)nch) {
             const int gc = gc_begin + (int)threadIdx.x;
-            int lo = 0, hi = num_seqs;                 // chunk_off[lo] <= gc < chunk_off[hi]
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (seg.chunk_off[mid] <= gc) lo = mid; else hi = mid;
+            if (seg.plan_wgs > 0) {                    // from the scan above
+                const int64_t *sc = reinterpret_cast<const int64_t *>(smem);
+                const int32_t *st = reinterpret_cast<const int32_t *>(sc + 256);
+                auto off = [&](int n) { return (int)min(n > 0 ? sc[n - 1] : (int64_t)0, (int64_t)seg.img_slots); };
+                int lo = 0, hi = num_seqs;             // off(lo) <= gc < off(hi)
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (off(mid) <= gc) lo = mid; else hi = mid;
+                }
+                const int s0 = st[lo];
+                prep_rng[2 * threadIdx.x + 1] = st[256 + lo];
+                prep_rng[2 * threadIdx.x] = min(s0 + (gc - off(lo)) * C, total_tokens - 1);
+            } else {
+                int lo = 0, hi = num_seqs;             // chunk_off[lo] <= gc < chunk_off[hi]
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (seg.chunk_off[mid] <= gc) lo = mid; else hi = mid;
+                }
+                const int s0 = min(max(cu_seqlens[lo], 0), total_tokens);
+                prep_rng[2 * threadIdx.x + 1] = min(max(cu_seqlens[lo + 1], s0), total_tokens);
+                // in range for any valid cu_seqlens; the clamp keeps every load in
+                // bounds for any other contents
+                prep_rng[2 * threadIdx.x] = min(s0 + (gc - seg.chunk_off[lo]) * C, total_tokens - 1);
             }
-            const int s0 = min(max(cu_seqlens[lo], 0), total_tokens);
-            prep_rng[2 * threadIdx.x + 1] = min(max(cu_seqlens[lo + 1], s0), total_tokens);
-            // in range for any valid cu_seqlens; the clamp keeps every load in
-            // bounds for any other contents
-            prep_rng[2 * threadIdx.x] = min(s0 + (gc - seg.chunk_off[lo]) * C, total_tokens - 1);
         }
         __syncthreads();
     }
@@ -2134,10 +2313,14 @@ static hipError_t launch_prep_t(const void *q, const void *k, const float *g, co
     if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)P::bytes, lds_set[grad ? 1 : 0]))
         return e;
     // fewer chunks per workgroup when there are few: every compute unit
-    // gets work, and a workgroup's walk is short
-    const int64_t want = (max_chunks * H + 2047) / 2048;
+    // gets work, and a workgroup's walk is short.  Below 2,048 (chunk, head)
+    // pairs, enough chunks per workgroup that all workgroups fit one round
+    // (two per compute unit): a second round costs a workgroup's whole
+    // latency, a second chunk in the same workgroup about half of it.
+    const int64_t pairs = (int64_t)T_tot / C * H;
+    const int64_t want = pairs < 2048 ? (pairs + 511) / 512 : (max_chunks * H + 2047) / 2048;
     seg.prep_group = (int32_t)(want < 1 ? 1 : (want > PREP_GROUP ? PREP_GROUP : want));
-    const int64_t grid = (max_chunks + seg.prep_group - 1) / seg.prep_group * H;
+    const int64_t grid = (max_chunks + seg.prep_group - 1) / seg.prep_group * H + seg.plan_wgs;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(P::NT), P::bytes, stream,
@@ -2174,129 +2357,15 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
 // chunk_off is given, the first chunk of each sequence in chunks of `chunk`
 // tokens (chunk_off[N] = total chunks, at most max_chunks); and, if sched is
 // given, a dispatch order of the max_segs plan entries (a permutation).
-struct PlanArgs {
-    int32_t seg_len, max_segs;
-    int32_t *plan, *seq_seg, *chunk_off, *sched;   // chunk_off, sched may be nullptr
-    int32_t last_len, skip_last;
-    int32_t *seq_order;                            // may be nullptr
-};
 // One plan per workgroup: workgroup b builds plan b (a second plan of the
 // same sequences at another granularity costs no extra launch).
 __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restrict__ cu, int32_t N,
                                                           int32_t T_tot, int32_t chunk, int32_t max_chunks,
                                                           PlanArgs a0, PlanArgs a1)
 {
-    const PlanArgs &pa = blockIdx.x == 0 ? a0 : a1;
-    const int32_t seg_len = pa.seg_len, max_segs = pa.max_segs, last_len = pa.last_len, skip_last = pa.skip_last;
-    int32_t *const plan = pa.plan, *const seq_seg = pa.seq_seg, *const chunk_off = pa.chunk_off;
-    int32_t *const sched = pa.sched, *const seq_order = pa.seq_order;
     __shared__ int64_t scan[256], cscan[256];
     __shared__ int32_t hist[256];
-    int64_t carry = 0, ccarry = 0;                     // 64-bit: cu is not trusted
-    for (int base = 0; base < N; base += 256) {
-        const int n = base + (int)threadIdx.x;
-        int32_t t0 = 0, t1 = 0, ns = 0, nc = 0;
-        if (n < N) {
-            t0 = min(max(cu[n], 0), T_tot);
-            t1 = min(max(cu[n + 1], t0), T_tot);
-            ns = max(1, (int32_t)(((int64_t)t1 - t0 + seg_len - 1) / seg_len));
-            nc = (int32_t)(((int64_t)t1 - t0 + chunk - 1) / chunk);
-        }
-        scan[threadIdx.x] = ns;
-        cscan[threadIdx.x] = nc;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {       // inclusive scans
-            const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
-            const int64_t y = threadIdx.x >= (unsigned)off ? cscan[threadIdx.x - off] : 0;
-            __syncthreads();
-            scan[threadIdx.x] += x;
-            cscan[threadIdx.x] += y;
-            __syncthreads();
-        }
-        if (chunk_off && n < N) chunk_off[n] = (int32_t)min(ccarry + cscan[threadIdx.x] - nc, (int64_t)max_chunks);
-        const int64_t start = carry + scan[threadIdx.x] - ns;
-        if (n < N) {
-            // With non-decreasing cu the host bound on max_segs always holds;
-            // otherwise segments past it are dropped (memory-safe, result unspecified).
-            seq_seg[n] = (int32_t)min(start, (int64_t)max_segs);
-            // SEG_LAST: the segment lies in the sequence's last stretch of
-            // last_len tokens (a multiple of seg_len), which no later segment follows
-            const int64_t nl = last_len > 0 ? max((int64_t)1, ((int64_t)t1 - t0 + last_len - 1) / last_len) : 1;
-            for (int s = 0; s < ns && start + s < max_segs; ++s) {
-                const int gs = (int)(start + s);
-                plan[4 * gs] = n;
-                plan[4 * gs + 1] = t0 + s * seg_len;
-                plan[4 * gs + 2] = min(t0 + (s + 1) * seg_len, t1);
-                plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) |
-                                   (last_len > 0 && (int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
-            }
-        }
-        carry += scan[255];
-        ccarry += cscan[255];
-        __syncthreads();
-    }
-    const int32_t used = (int32_t)min(carry, (int64_t)max_segs);
-    if (threadIdx.x == 0) seq_seg[N] = used;
-    if (seq_order) {
-        // sequences by segment count, most first (counting sort on 256
-        // buckets; 255 segments and more share the first): the combine walks
-        // the longest chains first
-        __syncthreads();   // every seq_seg entry written
-        hist[threadIdx.x] = 0;
-        __syncthreads();
-        auto seq_bucket = [&](int n) { return 255 - min(max(seq_seg[n + 1] - seq_seg[n], 0), 255); };
-        for (int n = (int)threadIdx.x; n < N; n += 256) atomicAdd(&hist[seq_bucket(n)], 1);
-        __syncthreads();
-        const int32_t c = hist[threadIdx.x];
-        scan[threadIdx.x] = c;
-        __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-            const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
-            __syncthreads();
-            scan[threadIdx.x] += x;
-            __syncthreads();
-        }
-        hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - c);
-        __syncthreads();
-        for (int n = (int)threadIdx.x; n < N; n += 256) seq_order[atomicAdd(&hist[seq_bucket(n)], 1)] = n;
-        __syncthreads();   // hist and scan are reused below
-    }
-    if (chunk_off && threadIdx.x == 0) chunk_off[N] = (int32_t)min(ccarry, (int64_t)max_chunks);
-    for (int gs = used + (int)threadIdx.x; gs < max_segs; gs += 256) {
-        plan[4 * gs] = -1;
-        plan[4 * gs + 1] = 0;
-        plan[4 * gs + 2] = 0;
-        plan[4 * gs + 3] = 0;
-        if (sched) sched[gs] = gs;
-    }
-    if (!sched) return;
-    // Dispatch order, longest segment first: workgroups start in index order,
-    // so the short tail segments fill the gaps the full-length ones leave at
-    // the end of a pass.  Counting sort on 256 length buckets (bucket 0 = full
-    // length, 255 = empty); the order inside a bucket does not matter, since
-    // the segments of one pass are independent.  skip_last: SEG_LAST segments
-    // count as empty (a summary pass skips them).
-    auto seg_bucket = [&](int gs) {
-        int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
-        if (skip_last && (plan[4 * gs + 3] & SEG_LAST)) len = 0;
-        return (int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len);
-    };
-    hist[threadIdx.x] = 0;
-    __syncthreads();   // also makes this workgroup's plan entries visible below
-    for (int gs = (int)threadIdx.x; gs < used; gs += 256) atomicAdd(&hist[seg_bucket(gs)], 1);
-    __syncthreads();
-    const int32_t cnt = hist[threadIdx.x];
-    scan[threadIdx.x] = cnt;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int64_t x = threadIdx.x >= (unsigned)off ? scan[threadIdx.x - off] : 0;
-        __syncthreads();
-        scan[threadIdx.x] += x;
-        __syncthreads();
-    }
-    hist[threadIdx.x] = (int32_t)(scan[threadIdx.x] - cnt);   // bucket start
-    __syncthreads();
-    for (int gs = (int)threadIdx.x; gs < used; gs += 256) sched[atomicAdd(&hist[seg_bucket(gs)], 1)] = gs;
+    cp_plan_body(cu, N, T_tot, chunk, max_chunks, blockIdx.x == 0 ? a0 : a1, scan, cscan, hist);
 }
 
 // ------------------------------------------------------ segment combination
@@ -2534,6 +2603,15 @@ extern "C" hipError_t kda_launch_prefill(int bf16, int chunk, int dv_block,
 // (optional, [N]): the sequences by segment count, most first.  A second plan
 // (plan2 != nullptr, with its own seg_len2 ... seq_order2) is built by a
 // second workgroup of the same launch.
+static bool plan_args(int32_t sl, int32_t ms, int32_t *p, int32_t *ss, int32_t *co, int32_t *sc, int32_t ll,
+                      int32_t sk, int32_t *so, kda::PlanArgs *a)
+{
+    if (ll == 0) ll = sl;
+    if (sl <= 0 || (ll > 0 && ll % sl)) return false;
+    *a = {sl, ms, p, ss, co, sc, ll, sk, so};
+    return true;
+}
+
 extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T_tot, int32_t seg_len,
                                          int32_t max_segs, int32_t *plan, int32_t *seq_seg, int32_t chunk,
                                          int32_t max_chunks, int32_t *chunk_off, int32_t *sched,
@@ -2542,22 +2620,58 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
                                          int32_t *sched2, int32_t last_len2, int32_t skip_last2,
                                          int32_t *seq_order2, hipStream_t stream)
 {
-    auto args = [](int32_t sl, int32_t ms, int32_t *p, int32_t *ss, int32_t *co, int32_t *sc, int32_t ll,
-                   int32_t sk, int32_t *so, kda::PlanArgs *a) {
-        if (ll == 0) ll = sl;
-        if (sl <= 0 || (ll > 0 && ll % sl)) return false;
-        *a = {sl, ms, p, ss, co, sc, ll, sk, so};
-        return true;
-    };
     kda::PlanArgs a0, a1;
-    if (!args(seg_len, max_segs, plan, seq_seg, chunk_off, sched, last_len, skip_last, seq_order, &a0))
+    if (!plan_args(seg_len, max_segs, plan, seq_seg, chunk_off, sched, last_len, skip_last, seq_order, &a0))
         return hipErrorInvalidValue;
     a1 = a0;
-    if (plan2 && !args(seg_len2, max_segs2, plan2, seq_seg2, nullptr, sched2, last_len2, skip_last2, seq_order2, &a1))
+    if (plan2 && !plan_args(seg_len2, max_segs2, plan2, seq_seg2, nullptr, sched2, last_len2, skip_last2, seq_order2, &a1))
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(plan2 ? 2 : 1), dim3(256), 0, stream, cu, N, T_tot, chunk,
                        max_chunks, a0, a1);
     return hipGetLastError();
+}
+
+extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void *k, const float *g,
+                                            const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
+                                            int32_t H, const int32_t *chunk_off, int64_t max_chunks, void *img,
+                                            void *gimg, hipStream_t stream);
+
+// The plans of kda_launch_cp_plan (32-token chunks, chunk_off required) and
+// the chunk-operand pass of kda_launch_chunk_prep, in one launch when N <= 256
+// (the plan workgroups run beside the chunk workgroups, which find their
+// chunks from cu_seqlens), else as those two launches.
+extern "C" hipError_t kda_launch_cp_plan_prep(int bf16, const void *q, const void *k, const float *g,
+                                              const float *beta, const int32_t *cu, int32_t N, int32_t T_tot,
+                                              int32_t H, int64_t max_chunks, void *img, void *gimg,
+                                              int32_t seg_len, int32_t max_segs, int32_t *plan, int32_t *seq_seg,
+                                              int32_t *chunk_off, int32_t *sched, int32_t last_len,
+                                              int32_t skip_last, int32_t *seq_order, int32_t seg_len2,
+                                              int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
+                                              int32_t *sched2, int32_t last_len2, int32_t skip_last2,
+                                              int32_t *seq_order2, hipStream_t stream)
+{
+    using namespace kda;
+    if (!chunk_off || max_chunks < 1 || max_chunks > 0x7fffffff) return hipErrorInvalidValue;
+    if (N < 1 || N > 256) {
+        hipError_t e = kda_launch_cp_plan(cu, N, T_tot, seg_len, max_segs, plan, seq_seg, 32, (int32_t)max_chunks,
+                                          chunk_off, sched, last_len, skip_last, seq_order, seg_len2, max_segs2,
+                                          plan2, seq_seg2, sched2, last_len2, skip_last2, seq_order2, stream);
+        if (e != hipSuccess) return e;
+        return kda_launch_chunk_prep(bf16, q, k, g, beta, cu, N, T_tot, H, chunk_off, max_chunks, img, gimg, stream);
+    }
+    SegArgs seg = {nullptr, 0, SEG_OUTPUT, nullptr, nullptr, chunk_off, static_cast<f32x4 *>(img), nullptr, 0, 0, nullptr,
+                   nullptr, 0, 0, PREP_GROUP, (int32_t)max_chunks, static_cast<f32x4 *>(gimg)};
+    if (!plan_args(seg_len, max_segs, plan, seq_seg, chunk_off, sched, last_len, skip_last, seq_order, &seg.pl[0]))
+        return hipErrorInvalidValue;
+    seg.plan_wgs = 1;
+    if (plan2) {
+        if (!plan_args(seg_len2, max_segs2, plan2, seq_seg2, nullptr, sched2, last_len2, skip_last2, seq_order2,
+                       &seg.pl[1]))
+            return hipErrorInvalidValue;
+        seg.plan_wgs = 2;
+    }
+    if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
+    return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
 }
 
 // Chunk-operand pass: images of every (chunk, head), 32-token chunks.

@@ -132,13 +132,13 @@ def test_cp_empty_sequences_and_untouched_rows():
     assert_close(host(fin), ref_fin, TOL[torch.bfloat16], "cp untouched final_state")
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("seg_len", [128, 192])
+@pytest.mark.parametrize("dtype,seg_len", [(torch.bfloat16, 1024), (torch.float32, 1088)])
 def test_cp_summary_units_vs_oracle(dtype, seg_len):
-    # (total_tokens / seg_len) x heads >= 256: the summaries and the combine
-    # run on units, four (seg_len 128) or two (192: six chunks) per segment,
-    # and every segment's output run starts from its first unit's state
-    inp = to_dev(I.random_prefill([400, 0, 333, 380, 1], H=64, dtype=dtype, seed=41))
+    # (total_tokens / seg_len) x heads >= 256 and segments of 1,024 tokens or
+    # more: the summaries and the combine run on units, four (1,024: 32
+    # chunks) or two (1,088: 34 chunks) per segment, and every segment's
+    # output run starts from its first unit's state
+    inp = to_dev(I.random_prefill([2200, 0, 1500, 700, 1], H=64, dtype=dtype, seed=41))
     assert (inp["q"].shape[0] // seg_len) * 64 >= 256
     _check_cp(inp, TOL[dtype], "cp_units", seg_len)
 
