@@ -186,6 +186,10 @@ struct SegArgs {
     // find their chunks from cu_seqlens themselves)
     int32_t plan_wgs;
     PlanArgs pl[2];
+    // SEG_OUTPUT: seg_init entries hold accumulator tiles (16-byte entry
+    // (cb * 8 + r) * 64 + lane: rows 16 r + 4 j + i of column 16 cb + m, as
+    // kda_cp_combine_kernel writes them with a fragment layout) instead of rows
+    int32_t init_tiles;
 };
 
 // One plan per 256-thread workgroup, in LDS scan[256], cscan[256] (int64) and hist[256].
@@ -1696,7 +1700,11 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const int col = colc[ct];
-        if (S_in) {
+        if (S_in && segmented && seg.init_tiles) {
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(S_in + S_in_base);
+#pragma unroll
+            for (int r = 0; r < DK / 16; ++r) S[ct][r] = src[((col >> 4) * 8 + r) * 64 + lane];
+        } else if (S_in) {
 #pragma unroll
             for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
@@ -2509,10 +2517,15 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
     };
     // step it (it < ns - 1): write S_in of segment it, S <- M S + S^0 from
     // cur, and load step it + 3 into cur's registers afterwards
+    // (fragment layouts: as accumulator tiles, see SegArgs::init_tiles)
     auto write_own = [&](int it) {
         float *dst = seg_init + ((int64_t)seg_of(it) * H + h) * DK * dv;
+        if constexpr (FMT != CMB_ROWS) {
+            reinterpret_cast<f32x4 *>(dst)[((col >> 4) * 8 + wave) * 64 + lane] = own;
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * wave + 4 * lj + i) * dv + col] = own[i];
+            for (int i = 0; i < 4; ++i) dst[(int64_t)(16 * wave + 4 * lj + i) * dv + col] = own[i];
+        }
     };
     auto step = [&](int it, CmbOps &cur) {
         write_own(it);
@@ -2698,14 +2711,17 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
 // ([chunks][H][32][dv] fp32).  cmb_fmt (summaries only): the layout of
 // seg_out, CMB_ROWS, or CMB_SPLIT for bf16 / CMB_F32 for fp32 (dv = 128).
 // narrow (bf16; dv_block 256 or 128): 128-column workgroups of eight waves,
-// for calls with fewer workgroups than compute units.
+// for calls with fewer workgroups than compute units.  init_tiles (outputs,
+// dv = 128): seg_init as kda_cp_combine_kernel writes it with a fragment
+// layout (accumulator tiles).
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
                                        float *seg_out, const int32_t *chunk_off, const void *img,
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
-                                       int32_t init_units, int32_t cmb_fmt, int32_t narrow, hipStream_t stream)
+                                       int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
+                                       hipStream_t stream)
 {
     using namespace kda;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
@@ -2719,6 +2735,8 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                    const_cast<f32x4 *>(static_cast<const f32x4 *>(img)),
                    mode == SEG_SUMMARY ? nullptr : static_cast<float *>(snap), 0, 0, sched, init_seq_seg, init_unit,
                    init_units, 0, 0, nullptr, snap_scale, uw_u, uw_w, cmb_fmt};
+    seg.init_tiles = init_tiles;
+    if (init_tiles && (mode != SEG_OUTPUT || dv != DK || !plan)) return hipErrorInvalidValue;
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
     // two workgroups per compute unit (two tiles per wave share every operand
