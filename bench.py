@@ -98,15 +98,16 @@ CP_KINDS = {"plan": lambda n: "kda_cp_plan_kernel" in n,
             "summaries": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "1",
             "combine": lambda n: "kda_cp_combine_kernel" in n,
             "outputs": lambda n: "kda_chain_kernel" in n and n.split("ELb", 1)[1][:1] == "0"}
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES",
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES",
                  "GRBM_GUI_ACTIVE")
 
 
 def write_mfma(path, workload):
     """Executed MFMA work per kda_prefill_cp call on `workload` from one
-    rocprofv3 --pmc run of the four MFMA_COUNTERS over ``--pmc-workload``:
-    fp16 and fp32 MFMA flops (each MOPS unit is 512 flops) per kernel kind and
-    per call, and the share of cycles the MFMA units were busy."""
+    rocprofv3 --pmc run of the MFMA_COUNTERS over ``--pmc-workload``:
+    fp16, bf16 and fp32 MFMA flops (each MOPS unit is 512 flops) per kernel
+    kind and per call, and the share of cycles the MFMA units were busy."""
     import csv
     rows = {}
     with open(path, newline="") as f:
@@ -122,31 +123,33 @@ def write_mfma(path, workload):
                         "python bench.py --mfma-from <dir>/run_counter_collection.csv --workload %s" % workload],
            "unit": "flops executed by MFMA instructions per kda_prefill_cp call (MOPS x 512); 'raw' holds "
                    "each counter's average per launch as rocprofv3 reports it"}
-    per_kind, f16, f32 = {}, 0.0, 0.0
+    per_kind, f16, bf16, f32 = {}, 0.0, 0.0, 0.0
     for kind, match in CP_KINDS.items():
         ks = [v for n, v in rows.values() if match(n)]
         avg = lambda c: sum(k.get(c, 0.0) for k in ks) / max(len(ks), 1)
         per_kind[kind] = {"launches": len(ks), "f16_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_F16") * 512,
+                          "bf16_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512,
                           "f32_flops": avg("SQ_INSTS_VALU_MFMA_MOPS_F32") * 512,
                           "raw": {c: avg(c) for c in MFMA_COUNTERS}}
         f16 += per_kind[kind]["f16_flops"]
+        bf16 += per_kind[kind]["bf16_flops"]
         f32 += per_kind[kind]["f32_flops"]
-    out.update(per_kernel=per_kind, f16_flops_per_call=f16, f32_flops_per_call=f32)
+    out.update(per_kernel=per_kind, f16_flops_per_call=f16, bf16_flops_per_call=bf16, f32_flops_per_call=f32)
     with open(profile_path(workload, "mfma"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))
 
 
 def pmc_mfma(workload):
-    """(fp16, fp32) MFMA flops per kda_prefill_cp call on `workload` from the
-    committed counter summary, if it was taken on the current kernel source
-    (else None)."""
+    """(fp16 + bf16, fp32) MFMA flops per kda_prefill_cp call on `workload`
+    from the committed counter summary, if it was taken on the current kernel
+    source (else None)."""
     try:
         with open(profile_path(workload, "mfma")) as f:
             d = json.load(f)
         if d.get("kernel_source_sha256_16") != source_hash(PREFILL_SRC):
             return None
-        return float(d["f16_flops_per_call"]), float(d["f32_flops_per_call"])
+        return float(d["f16_flops_per_call"]) + float(d.get("bf16_flops_per_call", 0.0)), float(d["f32_flops_per_call"])
     except (OSError, ValueError, KeyError):
         return None
 
@@ -211,6 +214,7 @@ def kernel_label(name):
             return label
     dt = "bf16" if "DF16b" in name else "fp32"
     if "kda_prefill_kernel" in name:
+        # (up to 256 sequences the same launch also builds the segment plans)
         kind = "chunk operands" if "Li1EEE" in name else ("chunk and gradient images" if "Li3EEE" in name else "fused")
         return "kda_prefill_kernel<%s> (%s)" % (dt, kind)
     if "kda_chain_kernel" in name:
@@ -227,6 +231,16 @@ def kernel_label(name):
     return name.split("(")[0][:60]
 
 
+def call_starts(ks):
+    """Indices of the first launch of each kda_prefill_cp / kda_backward call
+    in a time-sorted kernel list: the plan kernel, or (up to 256 sequences,
+    where the plans are built inside it) the chunk-operand launch."""
+    is_plan = lambda n: "kda_cp_plan_kernel" in n
+    is_prep = lambda n: "kda_prefill_kernel" in n and ("Li1EEE" in n or "Li3EEE" in n)
+    return [i for i, k in enumerate(ks)
+            if is_plan(k[2]) or (is_prep(k[2]) and (i == 0 or not is_plan(ks[i - 1][2])))]
+
+
 def write_stats(trace_dir, workload):
     """Per-kernel durations of the kda_prefill_cp calls of a rocprofv3
     --kernel-trace run of ``bench.py --pmc-workload`` (the last call: the
@@ -235,8 +249,9 @@ def write_stats(trace_dir, workload):
     rows = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
             if "kda" in r["Kernel_Name"]]
     ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
-    calls = len([k for k in ks if "kda_cp_plan_kernel" in k[2]])
-    last = ks[len(ks) - len(ks) // max(calls, 1):]
+    starts = call_starts(ks)
+    calls = len(starts)
+    last = ks[starts[-1]:]
     short = workload[len("prefill_"):] if workload.startswith("prefill_") else workload
     path = os.path.join(ROOT, "profiles", "kda_prefill_cp_%s_kernel_stats.txt" % short)
     lines = ["# rocprofv3 kernel trace: one kda_prefill_cp call on %s (automatic seg_len), MI355X (gfx950)" % workload,
@@ -296,7 +311,7 @@ def write_backward_stats(trace_dir, workload):
     rows = [r for r in csv.DictReader(open(os.path.join(trace_dir, "run_kernel_trace.csv")))
             if "kda" in r["Kernel_Name"]]
     ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
-    starts = [i for i, k in enumerate(ks) if "kda_cp_plan_kernel" in k[2]]
+    starts = call_starts(ks)
     last = ks[starts[-1]:]
     t0 = last[0][0]
     short = workload[len("prefill_"):] if workload.startswith("prefill_") else workload
@@ -664,8 +679,8 @@ def main():
         return {"counter_hbm_bytes": tr,
                 "counter_hbm_gbs": None if tr is None else tr / (ms * 1e-3) / 1e9,
                 "mfma_executed": None if mf is None else {
-                    "f16_tflops": mf[0] / (ms * 1e-3) / 1e12, "f32_tflops": mf[1] / (ms * 1e-3) / 1e12,
-                    "f16_frac_of_peak": mf[0] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                    "f16_bf16_tflops": mf[0] / (ms * 1e-3) / 1e12, "f32_tflops": mf[1] / (ms * 1e-3) / 1e12,
+                    "f16_bf16_frac_of_peak": mf[0] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
                 "counter_source": "rocprofv3 counters: %s, %s" % (
                     os.path.relpath(profile_path(name, "traffic"), ROOT),
                     os.path.relpath(profile_path(name, "mfma"), ROOT))}
@@ -776,9 +791,9 @@ def main():
                         "counter_hbm_bytes": traffic,
                         "counter_hbm_gbs": None if traffic is None else traffic / (pre_avg * 1e-3) / 1e9,
                         "mfma_executed": None if mfma is None else {
-                            "f16_tflops": mfma[0] / (pre_avg * 1e-3) / 1e12,
+                            "f16_bf16_tflops": mfma[0] / (pre_avg * 1e-3) / 1e12,
                             "f32_tflops": mfma[1] / (pre_avg * 1e-3) / 1e12,
-                            "f16_frac_of_peak": mfma[0] / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                            "f16_bf16_frac_of_peak": mfma[0] / (pre_avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                             "source": "rocprofv3 MFMA counters (profiles/kda_prefill_varlen_1m_h16_mfma.json)"},
                         "compute": "fp16 MFMA operands (exact power-of-two column scaling), fp32 accumulate and state"},
             "decode": {"num_seqs": Nd, "heads": Hd, "steps": args.decode_steps, "state_bytes": Nd * Hd * DK * DV * 4},
