@@ -181,7 +181,7 @@ struct SegArgs {
     float *snap_scale;          // kda_chain_kernel state stores, 16-bit inputs: [chunks][H][dv] column scales
     float *uw_u, *uw_w;         // kda_chain_kernel state stores: U and W of every chunk, [chunks][H][C][dv]
     int32_t cmb_fmt;            // SEG_SUMMARY: layout of seg_out (CMB_ROWS, CMB_F32 or CMB_SPLIT)
-    // chunk-operand pass: the first plan_wgs (0, 1 or 2) workgroups build the
+    // chunk-operand pass: the last plan_wgs (0, 1 or 2) workgroups build the
     // segment plans pl[0], pl[1] instead (num_seqs <= 256; the others then
     // find their chunks from cu_seqlens themselves)
     int32_t plan_wgs;
@@ -191,6 +191,138 @@ struct SegArgs {
     // kda_cp_combine_kernel writes them with a fragment layout) instead of rows
     int32_t init_tiles;
 };
+
+// Inclusive scans of a (and b) over the 256 threads of a workgroup: in-wave
+// shuffles, then the four wave totals through LDS (wtot[8]), one barrier.
+// The caller synchronises before it writes wtot again.
+__device__ __forceinline__ void block_scan2_256(int64_t &a, int64_t &b, int64_t *wtot)
+{
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t x = __shfl_up(a, o), y = __shfl_up(b, o);
+        if (lane >= o) {
+            a += x;
+            b += y;
+        }
+    }
+    if (lane == 63) {
+        wtot[wave] = a;
+        wtot[4 + wave] = b;
+    }
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) {
+        a += wtot[w];
+        b += wtot[4 + w];
+    }
+}
+
+// The plan of cp_plan_body for at most 256 sequences, with the same plan,
+// seq_seg and chunk_off and a dispatch order / sequence order that sorts the
+// same keys (the order inside a key may differ, which no reader depends on):
+// scans by in-wave shuffles, plan entries one segment per thread (found by a
+// binary search of the segment scan in LDS), and no global read-back; five
+// barriers instead of about fifty.  lds: 6,272 bytes.
+__device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, int32_t N, int32_t T_tot,
+                                              int32_t chunk, int32_t max_chunks, const PlanArgs pa,
+                                              unsigned char *lds)
+{
+    const int32_t seg_len = pa.seg_len, max_segs = pa.max_segs, last_len = pa.last_len, skip_last = pa.skip_last;
+    int32_t *const plan = pa.plan, *const seq_seg = pa.seq_seg, *const chunk_off = pa.chunk_off;
+    int32_t *const sched = pa.sched, *const seq_order = pa.seq_order;
+    int64_t *sinc = reinterpret_cast<int64_t *>(lds);             // inclusive scan of segment counts
+    int32_t *st0 = reinterpret_cast<int32_t *>(sinc + 256), *st1 = st0 + 256;
+    int32_t *hist = st1 + 256, *hist2 = hist + 256;                // sched and seq_order keys
+    int64_t *wtot = reinterpret_cast<int64_t *>(hist2 + 256);      // [16]
+    const int t = (int)threadIdx.x;
+    int32_t t0 = 0, t1 = 0;
+    int64_t ns = 0, nc = 0;
+    if (t < N) {
+        t0 = min(max(cu[t], 0), T_tot);
+        t1 = min(max(cu[t + 1], t0), T_tot);
+        ns = max((int64_t)1, ((int64_t)t1 - t0 + seg_len - 1) / seg_len);
+        nc = ((int64_t)t1 - t0 + chunk - 1) / chunk;
+    }
+    int64_t si = ns, ci = nc;
+    block_scan2_256(si, ci, wtot);
+    sinc[t] = si;
+    st0[t] = t0;
+    st1[t] = t1;
+    hist[t] = 0;
+    hist2[t] = 0;
+    if (t == 255) wtot[8] = ci;                                    // total chunks
+    __syncthreads();
+    const int64_t total_s = sinc[255];
+    const int32_t used = (int32_t)min(total_s, (int64_t)max_segs);
+    if (t < N) {
+        seq_seg[t] = (int32_t)min(si - ns, (int64_t)max_segs);
+        if (chunk_off) chunk_off[t] = (int32_t)min(ci - nc, (int64_t)max_chunks);
+        if (seq_order) {
+            const int64_t cnt = min(si, (int64_t)max_segs) - min(si - ns, (int64_t)max_segs);
+            atomicAdd(&hist2[255 - (int)min(max(cnt, (int64_t)0), (int64_t)255)], 1);
+        }
+    }
+    if (t == 0) {
+        seq_seg[N] = used;
+        if (chunk_off) chunk_off[N] = (int32_t)min(wtot[8], (int64_t)max_chunks);
+    }
+    // plan entry and dispatch key of segment gs < used
+    auto entry = [&](int gs, int32_t &n, int32_t &a, int32_t &b, int32_t &fl) {
+        int lo = 0, hi = N - 1;                                    // first n with sinc[n] > gs
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sinc[mid] > gs) hi = mid; else lo = mid + 1;
+        }
+        n = lo;
+        const int64_t start = n > 0 ? sinc[n - 1] : 0;
+        const int s = (int)(gs - start);
+        const int32_t u0 = st0[n], u1 = st1[n];
+        const int64_t nl = last_len > 0 ? max((int64_t)1, ((int64_t)u1 - u0 + last_len - 1) / last_len) : 1;
+        a = u0 + s * seg_len;
+        b = min(u0 + (s + 1) * seg_len, u1);
+        fl = (s == 0 ? SEG_FIRST : 0) | (last_len > 0 && (int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
+    };
+    auto key = [&](int32_t a, int32_t b, int32_t fl) {
+        int64_t len = (int64_t)b - a;
+        if (skip_last && (fl & SEG_LAST)) len = 0;
+        return (int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len);
+    };
+    for (int gs = t; gs < max_segs; gs += 256) {
+        if (gs < used) {
+            int32_t n, a, b, fl;
+            entry(gs, n, a, b, fl);
+            plan[4 * gs] = n;
+            plan[4 * gs + 1] = a;
+            plan[4 * gs + 2] = b;
+            plan[4 * gs + 3] = fl;
+            if (sched) atomicAdd(&hist[key(a, b, fl)], 1);
+        } else {
+            plan[4 * gs] = -1;
+            plan[4 * gs + 1] = 0;
+            plan[4 * gs + 2] = 0;
+            plan[4 * gs + 3] = 0;
+            if (sched) sched[gs] = gs;
+        }
+    }
+    if (!sched && !seq_order) return;                              // (uniform)
+    __syncthreads();                                               // every key counted
+    const int64_t c1 = hist[t], c2 = hist2[t];
+    int64_t e1 = c1, e2 = c2;
+    block_scan2_256(e1, e2, wtot);
+    hist[t] = (int32_t)(e1 - c1);                                  // bucket starts
+    hist2[t] = (int32_t)(e2 - c2);
+    __syncthreads();
+    if (seq_order && t < N) {
+        const int64_t cnt = min(si, (int64_t)max_segs) - min(si - ns, (int64_t)max_segs);
+        seq_order[atomicAdd(&hist2[255 - (int)min(max(cnt, (int64_t)0), (int64_t)255)], 1)] = t;
+    }
+    if (sched)
+        for (int gs = t; gs < used; gs += 256) {
+            int32_t n, a, b, fl;
+            entry(gs, n, a, b, fl);
+            sched[atomicAdd(&hist[key(a, b, fl)], 1)] = gs;
+        }
+}
 
 // One plan per 256-thread workgroup, in LDS scan[256], cscan[256] (int64) and hist[256].
 __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int32_t N, int32_t T_tot,
@@ -883,14 +1015,16 @@ void kda_prefill_kernel(
     constexpr bool summary = false;
     if constexpr (kPrep) {
         static_assert(!kPrep || NT == 256, "the plan and the chunk scan take 256 threads");
-        if ((int)blockIdx.x < seg.plan_wgs) {      // this launch's plan workgroups
-            int64_t *scan = reinterpret_cast<int64_t *>(smem);
-            cp_plan_body(cu_seqlens, num_seqs, total_tokens, C, seg.img_slots, blockIdx.x == 0 ? seg.pl[0] : seg.pl[1],
-                         scan, scan + 256, reinterpret_cast<int32_t *>(scan + 512));
+        // this launch's plan workgroups (num_seqs <= 256): the last ones, so
+        // that a round of chunk workgroups that fills the GPU is not pushed
+        // into a second one by them (the plans take about 4 us)
+        const int pw = (int)blockIdx.x - ((int)gridDim.x - seg.plan_wgs);
+        if (pw >= 0) {
+            cp_plan_small(cu_seqlens, num_seqs, total_tokens, C, seg.img_slots, pw == 0 ? seg.pl[0] : seg.pl[1], smem);
             return;
         }
     }
-    const int wg = (int)blockIdx.x - (kPrep ? seg.plan_wgs : 0);
+    const int wg = (int)blockIdx.x;
     int su = 0, h = 0, n = 0, vb = 0, t_start = 0, t_end = 0, sflags = SEG_FIRST | SEG_LAST;
     int gc_begin = 0, nch = 0;      // chunk-operand pass: first global chunk, chunk count
     if constexpr (kPrep) {
@@ -904,6 +1038,7 @@ void kda_prefill_kernel(
             // inclusive scan of the chunk counts, in LDS that phase 1 rewrites
             int64_t *sc = reinterpret_cast<int64_t *>(smem);
             int32_t *st = reinterpret_cast<int32_t *>(sc + 256);   // clamped token ranges [2][256]
+            int64_t *wtot = sc + 512;
             const int t = (int)threadIdx.x;
             int64_t ncs = 0;
             if (t < num_seqs) {
@@ -913,14 +1048,10 @@ void kda_prefill_kernel(
                 st[t] = t0;
                 st[256 + t] = t1;
             }
-            sc[t] = ncs;
+            int64_t inc = ncs, unused = 0;
+            block_scan2_256(inc, unused, wtot);
+            sc[t] = inc;
             __syncthreads();
-            for (int off = 1; off < 256; off <<= 1) {
-                const int64_t x = t >= off ? sc[t - off] : 0;
-                __syncthreads();
-                sc[t] += x;
-                __syncthreads();
-            }
             total_chunks = (int)min(sc[255], (int64_t)seg.img_slots);
         } else {
             total_chunks = seg.chunk_off[num_seqs];
