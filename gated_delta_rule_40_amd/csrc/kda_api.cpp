@@ -42,7 +42,8 @@ extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *d
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
                                             const float *g_end, void *g_chunk, float *g_scale, float *dinit,
-                                            float *g0_out, float *dx_chunk, hipStream_t stream);
+                                            float *g0_out, float *dx_chunk, int32_t tiles,
+                                            hipStream_t stream);
 extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const float *g,
                                            const float *beta, const void *dout, const int32_t *cu,
                                            const int32_t *chunk_off, int64_t max_chunks, const void *snaps,
@@ -484,9 +485,11 @@ int32_t bwd_seg_len(int32_t T, int32_t H)
 // starts and state gradients at chunk ends [max_chunks][H][dk][dv] (fp32, or
 // fp16 with column scales [max_chunks][H][dv] each for bf16 inputs); every
 // chunk's U, W (forward) and dX (state gradient) [max_chunks][H][32][dv]; forward
-// summaries [max_segs][H][dk][dv + dk]; gradient summaries [max_segs][H][dk][dv];
+// summaries [max_segs][H][dk (dv + 2 dk)] (S^0, M and M^T in the combine's
+// fragment layout); gradient summaries [max_segs][H][dk][dv];
 // entering states and entering gradients [max_segs][H][dk][dv] (the two
-// strands of the pipeline run side by side, so each has its own).
+// strands of the pipeline run side by side, so each has its own; these three
+// as accumulator tiles).
 bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
 {
     const int32_t seg_len = bwd_seg_len(T, H);
@@ -512,7 +515,7 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     lay->uw_w = align256(lay->uw_u + sizeof(float) * (size_t)chunks * H * kCpChunk * kHeadDim);
     lay->dx = align256(lay->uw_w + sizeof(float) * (size_t)chunks * H * kCpChunk * kHeadDim);
     lay->fsum = align256(lay->dx + sizeof(float) * (size_t)chunks * H * kCpChunk * kHeadDim);
-    lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 2 * S);
+    lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 3 * S);
     lay->seg_init = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
     lay->seg_dsend = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * S);
     lay->total = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
@@ -644,27 +647,31 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
         e = fork(0, s, s2);
         forked = e == hipSuccess;
     }
+    // summaries in the combine's operand order, with M^T for the reverse
+    // walk; summaries of gradients, entering states and entering gradients as
+    // accumulator tiles (see kda_prefill.hip, CMB_ROWS)
+    const int32_t cmb_fmt = (bf16 ? 2 : 1) | 4;
     if (e == hipSuccess)   // s2: gradient summaries G^0 of every segment but a sequence's first
         e = kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, nullptr, s2);
-    if (e == hipSuccess)   // s: forward summaries [S^0 | M] of every segment
+                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, nullptr, 1, s2);
+    if (e == hipSuccess)   // s: forward summaries [S^0 | M | M^T] of every segment
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 0, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, s);
     if (e == hipSuccess) e = fork(1, s, s2);
     if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
-                                  fsum, 1, 0, s2);
+                                  fsum, 1, cmb_fmt, s2);
     if (e == hipSuccess)   // s2: the gradient at every chunk end, every chunk's dX, and d(initial state)
         e = kda_launch_grad_chain(bf16, 0, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, dxc, s2);
+                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, dxc, 1, s2);
     if (e == hipSuccess)   // s: the state entering every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_init, 0, nullptr,
-                                  nullptr, nullptr, 0, 0, s);
+                                  nullptr, nullptr, 0, cmb_fmt, s);
     if (e == hipSuccess)   // s: the state at every chunk start, and every chunk's U and W
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
-                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 0, s);
+                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, s);
     if (forked) {          // join: s waits for s2 (also after a failed launch)
         const hipError_t j = fork(2, s2, s);
         if (e == hipSuccess) e = j;

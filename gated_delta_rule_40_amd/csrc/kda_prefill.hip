@@ -452,7 +452,15 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
 //       CMB_SPLIT: entries ((r * 4 + kb) * 2 + p) * 64 + lane, bf16 x 8: the
 //                  32-block kb (columns 32 kb + 4 j + e and 32 kb + 16 + 4 j + e),
 //                  p = 0 the rounded value hi = bf16(M), p = 1 lo = bf16(M - hi).
-enum { CMB_ROWS = 0, CMB_F32 = 1, CMB_SPLIT = 2 };
+//   CMB_MT (with CMB_F32 or CMB_SPLIT): M^T follows M in the same fragment
+//     layout, DK (dv + 2 DK) floats per (unit, head) (the backward's reverse
+//     walk multiplies by the transposed transition).
+enum { CMB_ROWS = 0, CMB_F32 = 1, CMB_SPLIT = 2, CMB_MT = 4 };
+// floats per (unit, head) of a summary in layout fmt
+__host__ __device__ __forceinline__ int64_t cmb_unit_floats(int fmt, int dv)
+{
+    return (int64_t)DK * (dv + ((fmt & CMB_MT) ? 2 * DK : DK));
+}
 
 // seg_init entry of plan segment su (sequence n, first token t_start)
 __device__ __forceinline__ int64_t seg_init_entry(const SegArgs &seg, int su, int n, int t_start,
@@ -1527,14 +1535,17 @@ void kda_prefill_kernel(
 #pragma unroll
             for (int it = 0; it < SITEMS; ++it) tv[it] = *reinterpret_cast<const f32x4 *>(smem + img_off[it]);
 #pragma unroll
-            for (int it = 0; it < SITEMS; ++it) dst[min(tid + it * NT, Img::NVEC - 1)] = tv[it];
+            // non-temporal: the images are read by later launches, on other
+            // XCDs, and the kernel's end then has less in L2 to write back
+            // (the next launch started 1.4 us sooner on 4,096 x 8)
+            for (int it = 0; it < SITEMS; ++it) __builtin_nontemporal_store(tv[it], &dst[min(tid + it * NT, Img::NVEC - 1)]);
             if constexpr (kPrepG) {
                 typedef GradImage<TIn, C> GImg;
                 f32x4 *gdst = seg.gimg + ((int64_t)(gc_begin + ci) * num_heads + h) * GImg::NVEC;
 #pragma unroll 1
                 for (int it = 0; it < SITEMS; ++it) {
                     const int gv = min(tid + it * NT, GImg::NVEC - 1);
-                    gdst[gv] = GImg::gather(gv, sNKp, sQp, sKhT, sT, sP, sGam, sBeta, sTs);
+                    __builtin_nontemporal_store(GImg::gather(gv, sNKp, sQp, sKhT, sT, sP, sGam, sBeta, sTs), &gdst[gv]);
                 }
             }
             continue;
@@ -1688,8 +1699,9 @@ struct ChainCfg {
 // A segment summary in the CMB_F32 / CMB_SPLIT layout (see CMB_ROWS): the
 // S^0 columns go out straight from the accumulator tiles; M's columns (the
 // transition columns, each held by one lane) are transposed through the LDS,
-// which the walk no longer uses, and written as row fragments.  Every thread
-// of the workgroup calls this (it holds barriers).
+// which the walk no longer uses, and written as row fragments (and, with
+// CMB_MT, as the row fragments of M^T, read down the LDS columns).  Every
+// thread of the workgroup calls this (it holds barriers).
 template <typename Q>
 __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const f32x4 (&S)[Q::NCT_][DK / 16],
                                                     const float (&sS)[Q::NCT_], const int (&colc)[Q::NCT_], int dv,
@@ -1728,7 +1740,7 @@ __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const 
         }
     }
     __syncthreads();
-    if (fmt == CMB_SPLIT) {
+    if ((fmt & 3) == CMB_SPLIT) {
         for (int r = wave; r < DK / 16; r += NW)
             for (int kb = 0; kb < nc / 32; ++kb) {
                 const float *row = sM + (16 * r + lm) * LDM + 32 * kb + 4 * lj;
@@ -1751,6 +1763,34 @@ __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const 
             for (int kb = 0; kb < nc / 16; ++kb)
                 mf[(r * 8 + c_lo / 16 + kb) * 64 + lane] =
                     *reinterpret_cast<const f32x4 *>(sM + (16 * r + lm) * LDM + 16 * kb + 4 * lj);
+    }
+    if (!(fmt & CMB_MT)) return;
+    // M^T: its row tiles are this block's columns of M, read down the LDS columns
+    f32x4 *mtf = mf + DK * DK / 4;
+    for (int r = c_lo / 16 + wave; r < (c_lo + nc) / 16; r += NW) {
+        const float *col = sM + (16 * r + lm - c_lo);
+        if ((fmt & 3) == CMB_SPLIT) {
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = col[(32 * kb + 4 * lj + e) * LDM], x1 = col[(32 * kb + 16 + 4 * lj + e) * LDM];
+                    hi[e] = from_f<bf16_t>(x0);
+                    hi[e + 4] = from_f<bf16_t>(x1);
+                    lo[e] = from_f<bf16_t>(x0 - to_f(hi[e]));
+                    lo[e + 4] = from_f<bf16_t>(x1 - to_f(hi[e + 4]));
+                }
+                mtf[((r * 4 + kb) * 2) * 64 + lane] = __builtin_bit_cast(f32x4, hi);
+                mtf[((r * 4 + kb) * 2 + 1) * 64 + lane] = __builtin_bit_cast(f32x4, lo);
+            }
+        } else {
+            for (int kb = 0; kb < DK / 16; ++kb) {
+                f32x4 x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = col[(16 * kb + 4 * lj + e) * LDM];
+                mtf[(r * 8 + kb) * 64 + lane] = x;
+            }
+        }
     }
 }
 
@@ -2014,7 +2054,7 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
 
     if constexpr (SUMMARY && Q::kCmbFits) {   // (the host passes CMB_ROWS to the others)
         if (seg.cmb_fmt != CMB_ROWS) {
-            write_summary_frags<Q>(seg.seg_out + ((int64_t)su * num_heads + h) * DK * (dv + DK), seg.cmb_fmt, S, sS,
+            write_summary_frags<Q>(seg.seg_out + ((int64_t)su * num_heads + h) * cmb_unit_floats(seg.cmb_fmt, dv), seg.cmb_fmt, S, sS,
                                    colc, dv, dv0, smem, wave, lane, lj, lm);
             return;
         }
@@ -2293,7 +2333,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const TIn *dout, const int32_t *__restrict__ cu_seqlens, int32_t num_seqs, int32_t total_tokens,
     int32_t num_heads, const int32_t *__restrict__ plan, int32_t num_segs, const int32_t *__restrict__ sched,
     const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, void *g_chunk,
-    float *g_scale, float *dinit, float *g0_out, float *dx_chunk)
+    float *g_scale, float *dinit, float *g0_out, float *dx_chunk, int32_t tiles)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     typedef typename Q::OpT OpT;
@@ -2332,10 +2372,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const int col = vcol + 16 * ct;
+        if (gin && tiles) {                        // accumulator tiles (fragment-layout combine)
 #pragma unroll
-        for (int r = 0; r < DK / 16; ++r)
+            for (int r = 0; r < DK / 16; ++r) G[ct][r] = reinterpret_cast<const f32x4 *>(gin)[((col >> 4) * 8 + r) * 64 + lane];
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) G[ct][r][i] = gin ? gin[(int64_t)(16 * r + 4 * lj + i) * DK + col] : 0.f;
+            for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) G[ct][r][i] = gin ? gin[(int64_t)(16 * r + 4 * lj + i) * DK + col] : 0.f;
+        }
         sG[ct] = 1.f;
         if (Q::P::kIn16) {
             float m = 0.f;
@@ -2414,8 +2459,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
         if constexpr (SB) __syncthreads();       // every wave is done with the buffer
         stage(max(ci - 1, 0), SB ? 0 : (k + 1) & 1);
     }
-    if constexpr (SUMMARY) store_g(g0_out + ((int64_t)su * H + h) * DK * DK);
-    else if (dinit && (sflags & SEG_FIRST)) store_g(dinit + ((int64_t)n * H + h) * DK * DK);
+    if constexpr (SUMMARY) {
+        float *dst = g0_out + ((int64_t)su * H + h) * DK * DK;
+        if (tiles) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float inv = pow2_inv(sG[ct]);
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r)
+                    reinterpret_cast<f32x4 *>(dst)[(((vcol + 16 * ct) >> 4) * 8 + r) * 64 + lane] = G[ct][r] * inv;
+            }
+        } else {
+            store_g(dst);
+        }
+    } else if (dinit && (sflags & SEG_FIRST)) {
+        store_g(dinit + ((int64_t)n * H + h) * DK * DK);
+    }
 }
 
 template <typename TIn, int C, int NW, int NCT, bool SB>
@@ -2423,7 +2482,7 @@ static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int3
                                       int32_t H, const int32_t *plan, int32_t num_segs, const int32_t *sched,
                                       const int32_t *chunk_off, const void *gimg, const float *g_end, void *g_chunk,
                                       float *g_scale, float *dinit, float *g0_out, float *dx_chunk,
-                                      hipStream_t stream)
+                                      int32_t tiles, hipStream_t stream)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     auto kern = summary ? kda_grad_chain_kernel<TIn, C, NW, NCT, true, SB>
@@ -2436,7 +2495,7 @@ static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int3
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(dout), cu,
                        N, T_tot, H, plan, num_segs, sched, chunk_off, static_cast<const f32x4 *>(gimg), g_end,
-                       g_chunk, g_scale, dinit, g0_out, dx_chunk);
+                       g_chunk, g_scale, dinit, g0_out, dx_chunk, tiles);
     return hipGetLastError();
 }
 
@@ -2528,8 +2587,10 @@ __global__ __launch_bounds__(256) void kda_cp_plan_kernel(const int32_t *__restr
 //   reverse: the walk goes from the last segment to the first (gradients of
 //     the state, which enter a segment at its end): G(last) = init,
 //     G(s-1) = R_s G(s) + G_s^0, with R_s = M_s^T when MT.
-//   FMT: the layout of seg_out (CMB_ROWS, CMB_F32 or CMB_SPLIT; the last two
-//     for forward walks without m_src).  With the fragment layouts every
+//   FMT: the layout of seg_out (CMB_ROWS, CMB_F32 or CMB_SPLIT); with a
+//     fragment layout, so_floats, m_floats and m_off give the block sizes and
+//     the place of the M (or, transposed walks, M^T) fragments, and the
+//     entering states are written as accumulator tiles.  With the fragment layouts every
 //     operand load is a contiguous 1 KB per wave; row-major M costs a cache
 //     line per 16 bytes read, which bounded the step.  CMB_SPLIT runs the
 //     product on bf16 MFMA in three terms, M S ~ Mh Sh + Mh Sl + Ml Sh, with
@@ -2553,7 +2614,8 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
                                                                      float *__restrict__ seg_init, int32_t reverse,
                                                                      const int32_t *__restrict__ plan,
                                                                      const int32_t *__restrict__ seq_order,
-                                                                     const float *m_src)
+                                                                     const float *m_src, int32_t so_floats,
+                                                                     int32_t m_floats, int32_t m_off)
 {
     typedef Mma<float> M;
     __shared__ __align__(16) f32x4 sS[DK / 16][64];         // the state slice, accumulator layout per row tile
@@ -2624,8 +2686,11 @@ __global__ __launch_bounds__(CMB_THREADS) void kda_cp_combine_kernel(const float
         const int64_t gs = seg_of(min(it, ns - 2));
         const float *src = seg_out + (gs * H + h) * DK * ld;
         if constexpr (FMT != CMB_ROWS) {
-            const f32x4 *s0f = reinterpret_cast<const f32x4 *>(src);
-            const f32x4 *mf = reinterpret_cast<const f32x4 *>(src + (int64_t)DK * dv);
+            // fragment layouts: S^0 tiles at the start of a (unit, head) block
+            // of so_floats, the M (or M^T) fragments at m_off in a block of
+            // m_floats of m_src (or of seg_out)
+            const f32x4 *s0f = reinterpret_cast<const f32x4 *>(seg_out + (gs * H + h) * so_floats);
+            const f32x4 *mf = reinterpret_cast<const f32x4 *>((m_src ? m_src : seg_out) + (gs * H + h) * m_floats + m_off);
             o.s0 = s0f[((col >> 4) * 8 + wave) * 64 + lane];
 #pragma unroll
             for (int kb = 0; kb < DK / 16; ++kb) o.m[kb] = mf[(wave * 8 + kb) * 64 + lane];
@@ -2858,8 +2923,9 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
     // the fragment layouts: bf16 summaries in 256-column blocks (128 when
     // narrow), fp32 in 64-column blocks
-    if (cmb_fmt != CMB_ROWS && (mode != SEG_SUMMARY || dv != DK || snap ||
-                                (bf16 ? cmb_fmt != CMB_SPLIT || dv_block != 256 : cmb_fmt != CMB_F32)))
+    const int cbase = cmb_fmt & ~CMB_MT;
+    if (cmb_fmt != CMB_ROWS && (mode != SEG_SUMMARY || dv != DK || snap || (cmb_fmt & ~(CMB_MT | 3)) ||
+                                (bf16 ? cbase != CMB_SPLIT || dv_block != 256 : cbase != CMB_F32)))
         return hipErrorInvalidValue;
     if (snap && ((bf16 && !snap_scale) || !uw_u || !uw_w)) return hipErrorInvalidValue;
     SegArgs seg = {plan, num_segs, mode, seg_init, seg_out, chunk_off,
@@ -2874,7 +2940,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     // fragment; the second workgroup covers the waits of the first); fp32
     // images are twice as large and their buffers fit the LDS at 64 columns only
     // with state stores: 64 columns per workgroup (the two-tile form has no registers left for them)
-    if (bf16 && seg.snap) return launch_chain_t<bf16_t, 32, 4, 1>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
+    if (bf16 && seg.snap) return launch_chain_t<bf16_t, 32, 4, 1, true>(v, init, cu, N, T_tot, H, dv, out, fin, seg, stream);
     // narrow (bf16, few workgroups): 128 columns per workgroup as 8 waves of
     // one tile each -- two waves per SIMD, each with half of a chunk's
     // contractions, so that one wave's dependent steps overlap the other's
@@ -2893,11 +2959,12 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
 // layout), storing the gradient at every chunk end in g_chunk (bf16: fp16
 // values with column scales in g_scale [chunks][H][DK]; fp32: fp32),
 // d(initial state) in dinit and every chunk's dX in dx_chunk [chunks][H][32][DK].
+// tiles: g0_out (summary) and g_end as accumulator tiles (see SegArgs::init_tiles).
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
                                             const float *g_end, void *g_chunk, float *g_scale, float *dinit,
-                                            float *g0_out, float *dx_chunk, hipStream_t stream)
+                                            float *g0_out, float *dx_chunk, int32_t tiles, hipStream_t stream)
 {
     using namespace kda;
     if (summary ? !g0_out : (!g_end || !g_chunk || (bf16 && !g_scale) || !dx_chunk)) return hipErrorInvalidValue;
@@ -2905,10 +2972,10 @@ extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *d
     if (bf16)
         return launch_grad_chain_t<bf16_t, 32, 4, 2, false>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs,
                                                             sched, chunk_off, gimg, g_end, g_chunk, g_scale, dinit,
-                                                            g0_out, dx_chunk, stream);
+                                                            g0_out, dx_chunk, tiles, stream);
     return launch_grad_chain_t<float, 32, 4, 2, true>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs, sched,
                                                       chunk_off, gimg, g_end, g_chunk, g_scale, dinit, g0_out,
-                                                      dx_chunk, stream);
+                                                      dx_chunk, tiles, stream);
 }
 
 extern "C" size_t kda_chunk_image_bytes(int bf16)
@@ -2926,13 +2993,23 @@ extern "C" hipError_t kda_launch_cp_combine(const float *init, int32_t N, int32_
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (m_trans && !m_src) return hipErrorInvalidValue;
-    if (fmt != CMB_ROWS && ((fmt != CMB_F32 && fmt != CMB_SPLIT) || m_src || reverse || dv != DK))
-        return hipErrorInvalidValue;
-    auto kern = m_trans ? kda_cp_combine_kernel<true, CMB_ROWS>
-                        : fmt == CMB_F32   ? kda_cp_combine_kernel<false, CMB_F32>
-                          : fmt == CMB_SPLIT ? kda_cp_combine_kernel<false, CMB_SPLIT>
-                                             : kda_cp_combine_kernel<false, CMB_ROWS>;
+    // fragment layouts (fmt & 3 = CMB_F32 or CMB_SPLIT, dv = 128): the forward
+    // walk reads [S^0 | M] (| M^T with CMB_MT) from seg_out; the transposed
+    // walk (m_trans) reads S^0 tiles in blocks of DK dv from seg_out and the
+    // M^T fragments of m_src (whose blocks carry CMB_MT)
+    const int base = fmt & 3;
+    int32_t so_floats = 0, m_floats = 0, m_off = 0;
+    if (fmt != CMB_ROWS) {
+        if ((base != CMB_F32 && base != CMB_SPLIT) || (fmt & ~(CMB_MT | 3)) || dv != DK) return hipErrorInvalidValue;
+        if (m_trans ? (!m_src || !(fmt & CMB_MT)) : m_src != nullptr) return hipErrorInvalidValue;
+        m_floats = (int32_t)cmb_unit_floats(fmt, dv);
+        so_floats = m_trans ? DK * dv : m_floats;
+        m_off = DK * dv + (m_trans ? DK * DK : 0);
+    }
+    auto kern = fmt == CMB_ROWS ? (m_trans ? kda_cp_combine_kernel<true, CMB_ROWS> : kda_cp_combine_kernel<false, CMB_ROWS>)
+                                : (base == CMB_F32 ? kda_cp_combine_kernel<false, CMB_F32>
+                                                   : kda_cp_combine_kernel<false, CMB_SPLIT>);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(CMB_THREADS), 0, stream, init, N, H, dv, seq_seg, seg_out,
-                       seg_init, reverse, plan, seq_order, m_src);
+                       seg_init, reverse, plan, seq_order, m_src, so_floats, m_floats, m_off);
     return hipGetLastError();
 }
