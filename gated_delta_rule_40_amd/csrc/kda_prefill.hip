@@ -1663,7 +1663,9 @@ __device__ __forceinline__ void store_scaled_state(void *dst, float *scale, cons
 // other buffer.  Single-buffered (SB = true): a second barrier before the
 // registers overwrite the one buffer; half the LDS, so that two workgroups
 // share a compute unit and one runs while the other waits.
-template <typename TIn, int C, int NW, int NCT, bool SB = false>
+// SUM (segment summaries): no LDS for GS Q+, P or an output tile, which a
+// summary never stages.
+template <typename TIn, int C, int NW, int NCT, bool SB = false, bool SUM = false>
 struct ChainCfg {
     typedef PrefillCfg<TIn, C, NW> P;
     typedef typename P::OpT OpT;
@@ -1672,19 +1674,19 @@ struct ChainCfg {
     static constexpr int NCT_ = NCT;
     static constexpr int LDK = P::LDK, LDC = P::LDC, LDV = BV + 16 / (int)sizeof(TIn);
     static constexpr uint32_t offNKp = 0;
-    static constexpr uint32_t offQp = offNKp + sizeof(OpT) * C * LDK;
-    static constexpr uint32_t offKhT = offQp + sizeof(OpT) * C * LDK;
+    static constexpr uint32_t offQp = SUM ? 0 : offNKp + sizeof(OpT) * C * LDK;      // (SUM: never read)
+    static constexpr uint32_t offKhT = offNKp + (SUM ? 1 : 2) * sizeof(OpT) * C * LDK;
     static constexpr uint32_t offT = offKhT + sizeof(OpT) * DK * LDC;
-    static constexpr uint32_t offP = offT + sizeof(OpT) * C * LDC;
-    static constexpr uint32_t offGam = offP + sizeof(OpT) * C * LDC;
+    static constexpr uint32_t offP = SUM ? 0 : offT + sizeof(OpT) * C * LDC;          // (SUM: never read)
+    static constexpr uint32_t offGam = offT + (SUM ? 1 : 2) * sizeof(OpT) * C * LDC;
     static constexpr uint32_t offBeta = offGam + sizeof(float) * DK;
     static constexpr uint32_t offTs = offBeta + sizeof(float) * C;
     static constexpr uint32_t offV = offTs + (sizeof(float) * NSUB * NSUB + 15) / 16 * 16;
     static constexpr uint32_t BUF = (offV + sizeof(TIn) * C * LDV + 15) / 16 * 16;   // one chunk buffer
     static constexpr uint32_t offO = (SB ? 1 : 2) * BUF;                       // [NW][C][16 NCT] outputs
-    static constexpr uint32_t bytes = offO + sizeof(TIn) * NW * C * 16 * NCT;
-    // the LDS transpose of a summary's M columns (write_summary_frags) fits
-    static constexpr bool kCmbFits = sizeof(float) * DK * ((BV < DK ? BV : DK) + 4) <= bytes;
+    static constexpr uint32_t bytes = offO + (SUM ? 0 : sizeof(TIn) * NW * C * 16 * NCT);
+    // the LDS transpose of a summary's M columns (write_summary_frags, 64 columns a pass) fits
+    static constexpr bool kCmbFits = sizeof(float) * DK * (64 + 4) <= bytes;
     static_assert(bytes <= 160 * 1024, "LDS budget of one gfx950 workgroup");
     static constexpr int WG_PER_CU = (2 * bytes <= 160 * 1024) ? 2 : 1;
     static constexpr int WAVES_PER_EU = (WG_PER_CU * NW) / 4 >= 2 ? 2 : 1;
@@ -1699,20 +1701,21 @@ struct ChainCfg {
 // A segment summary in the CMB_F32 / CMB_SPLIT layout (see CMB_ROWS): the
 // S^0 columns go out straight from the accumulator tiles; M's columns (the
 // transition columns, each held by one lane) are transposed through the LDS,
-// which the walk no longer uses, and written as row fragments (and, with
-// CMB_MT, as the row fragments of M^T, read down the LDS columns).  Every
-// thread of the workgroup calls this (it holds barriers).
+// which the walk no longer uses, 64 columns at a time, and written as row
+// fragments (and, with CMB_MT, as the row fragments of M^T, read down the
+// LDS columns).  Every thread of the workgroup calls this (it holds barriers).
 template <typename Q>
 __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const f32x4 (&S)[Q::NCT_][DK / 16],
                                                     const float (&sS)[Q::NCT_], const int (&colc)[Q::NCT_], int dv,
                                                     int dv0, unsigned char *smem, int wave, int lane, int lj, int lm)
 {
     constexpr int NCT = Q::NCT_, BV = Q::BV, NW = Q::NT / 64;
-    constexpr int NCM = BV < DK ? BV : DK;           // most transition columns in one block
-    constexpr int LDM = NCM + 4;                     // padded LDS row (floats): conflict-free half-wave writes
+    constexpr int NCP = 64;                          // transition columns per transpose pass
+    constexpr int LDM = NCP + 4;                     // padded LDS row (floats): conflict-free half-wave writes
     static_assert(sizeof(float) * DK * LDM <= Q::bytes, "M transpose fits the chain kernel's LDS");
     f32x4 *s0f = reinterpret_cast<f32x4 *>(blob);
     f32x4 *mf = reinterpret_cast<f32x4 *>(blob + (int64_t)DK * dv);
+    f32x4 *mtf = mf + DK * DK / 4;                   // (CMB_MT)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const int col = colc[ct];
@@ -1725,70 +1728,74 @@ __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const 
     }
     const int c_lo = max(dv0, dv) - dv, nc = dv0 + BV - max(dv0, dv);   // this block's columns of M
     if (nc <= 0) return;                             // block-uniform
-    float *sM = reinterpret_cast<float *>(smem);     // [DK][LDM]: M rows, this block's columns
-    __syncthreads();                                 // every wave is done with the chunk buffers
+    float *sM = reinterpret_cast<float *>(smem);     // [DK][LDM]: M rows, the pass's 64 columns
+    const bool split = (fmt & 3) == CMB_SPLIT;
+    for (int c0 = c_lo; c0 < c_lo + nc; c0 += NCP) {
+        __syncthreads();                             // the chunk buffers, or the previous pass, are done with
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        const int col = colc[ct];
-        if (dv0 + 16 * (NCT * wave + ct) >= dv) {
-            const float inv = pow2_inv(sS[ct]);
-            const int c = col - dv - c_lo;
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = colc[ct] - dv - c0;        // wave-uniform tile test: its 16 columns lie in the pass
+            if (dv0 + 16 * (NCT * wave + ct) >= dv && c - lm >= 0 && c - lm < NCP) {
+                const float inv = pow2_inv(sS[ct]);
 #pragma unroll
-            for (int r = 0; r < DK / 16; ++r)
+                for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sM[(16 * r + 4 * lj + i) * LDM + c] = S[ct][r][i] * inv;
+                    for (int i = 0; i < 4; ++i) sM[(16 * r + 4 * lj + i) * LDM + c] = S[ct][r][i] * inv;
+            }
         }
-    }
-    __syncthreads();
-    if ((fmt & 3) == CMB_SPLIT) {
-        for (int r = wave; r < DK / 16; r += NW)
-            for (int kb = 0; kb < nc / 32; ++kb) {
-                const float *row = sM + (16 * r + lm) * LDM + 32 * kb + 4 * lj;
-                const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
-                const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 16);
-                bf16x8 hi, lo;
+        __syncthreads();
+        // M: row fragments of the pass's K-blocks, every row tile
+        for (int r = wave; r < DK / 16; r += NW) {
+            if (split) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    hi[e] = from_f<bf16_t>(x0[e]);
-                    hi[e + 4] = from_f<bf16_t>(x1[e]);
-                    lo[e] = from_f<bf16_t>(x0[e] - to_f(hi[e]));
-                    lo[e + 4] = from_f<bf16_t>(x1[e] - to_f(hi[e + 4]));
+                for (int kb = 0; kb < NCP / 32; ++kb) {
+                    const float *row = sM + (16 * r + lm) * LDM + 32 * kb + 4 * lj;
+                    const f32x4 x0 = *reinterpret_cast<const f32x4 *>(row);
+                    const f32x4 x1 = *reinterpret_cast<const f32x4 *>(row + 16);
+                    bf16x8 hi, lo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        hi[e] = from_f<bf16_t>(x0[e]);
+                        hi[e + 4] = from_f<bf16_t>(x1[e]);
+                        lo[e] = from_f<bf16_t>(x0[e] - to_f(hi[e]));
+                        lo[e + 4] = from_f<bf16_t>(x1[e] - to_f(hi[e + 4]));
+                    }
+                    const int kg = c0 / 32 + kb;
+                    mf[((r * 4 + kg) * 2) * 64 + lane] = __builtin_bit_cast(f32x4, hi);
+                    mf[((r * 4 + kg) * 2 + 1) * 64 + lane] = __builtin_bit_cast(f32x4, lo);
                 }
-                const int kg = c_lo / 32 + kb;
-                mf[((r * 4 + kg) * 2) * 64 + lane] = __builtin_bit_cast(f32x4, hi);
-                mf[((r * 4 + kg) * 2 + 1) * 64 + lane] = __builtin_bit_cast(f32x4, lo);
-            }
-    } else {
-        for (int r = wave; r < DK / 16; r += NW)
-            for (int kb = 0; kb < nc / 16; ++kb)
-                mf[(r * 8 + c_lo / 16 + kb) * 64 + lane] =
-                    *reinterpret_cast<const f32x4 *>(sM + (16 * r + lm) * LDM + 16 * kb + 4 * lj);
-    }
-    if (!(fmt & CMB_MT)) return;
-    // M^T: its row tiles are this block's columns of M, read down the LDS columns
-    f32x4 *mtf = mf + DK * DK / 4;
-    for (int r = c_lo / 16 + wave; r < (c_lo + nc) / 16; r += NW) {
-        const float *col = sM + (16 * r + lm - c_lo);
-        if ((fmt & 3) == CMB_SPLIT) {
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                bf16x8 hi, lo;
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x0 = col[(32 * kb + 4 * lj + e) * LDM], x1 = col[(32 * kb + 16 + 4 * lj + e) * LDM];
-                    hi[e] = from_f<bf16_t>(x0);
-                    hi[e + 4] = from_f<bf16_t>(x1);
-                    lo[e] = from_f<bf16_t>(x0 - to_f(hi[e]));
-                    lo[e + 4] = from_f<bf16_t>(x1 - to_f(hi[e + 4]));
+                for (int kb = 0; kb < NCP / 16; ++kb)
+                    mf[(r * 8 + c0 / 16 + kb) * 64 + lane] =
+                        *reinterpret_cast<const f32x4 *>(sM + (16 * r + lm) * LDM + 16 * kb + 4 * lj);
+            }
+        }
+        if (!(fmt & CMB_MT)) continue;
+        // M^T: its row tiles are the pass's columns of M, read down the LDS columns
+        for (int r = c0 / 16 + wave; r < (c0 + NCP) / 16; r += NW) {
+            const float *col = sM + (16 * r + lm - c0);
+            if (split) {
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    bf16x8 hi, lo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x0 = col[(32 * kb + 4 * lj + e) * LDM], x1 = col[(32 * kb + 16 + 4 * lj + e) * LDM];
+                        hi[e] = from_f<bf16_t>(x0);
+                        hi[e + 4] = from_f<bf16_t>(x1);
+                        lo[e] = from_f<bf16_t>(x0 - to_f(hi[e]));
+                        lo[e + 4] = from_f<bf16_t>(x1 - to_f(hi[e + 4]));
+                    }
+                    mtf[((r * 4 + kb) * 2) * 64 + lane] = __builtin_bit_cast(f32x4, hi);
+                    mtf[((r * 4 + kb) * 2 + 1) * 64 + lane] = __builtin_bit_cast(f32x4, lo);
                 }
-                mtf[((r * 4 + kb) * 2) * 64 + lane] = __builtin_bit_cast(f32x4, hi);
-                mtf[((r * 4 + kb) * 2 + 1) * 64 + lane] = __builtin_bit_cast(f32x4, lo);
-            }
-        } else {
-            for (int kb = 0; kb < DK / 16; ++kb) {
-                f32x4 x;
+            } else {
+                for (int kb = 0; kb < DK / 16; ++kb) {
+                    f32x4 x;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = col[(16 * kb + 4 * lj + e) * LDM];
-                mtf[(r * 8 + kb) * 64 + lane] = x;
+                    for (int e = 0; e < 4; ++e) x[e] = col[(16 * kb + 4 * lj + e) * LDM];
+                    mtf[(r * 8 + kb) * 64 + lane] = x;
+                }
             }
         }
     }
@@ -1799,12 +1806,12 @@ __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const 
 // see store_scaled_state), and every chunk's U = V - K+ S0 and W in seg.uw_u,
 // seg.uw_w ([chunks][H][C][dv] fp32, rows of valid tokens); out may be NULL.
 template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB>::WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB, SUMMARY>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
                       TIn *__restrict__ out, float *final_state, SegArgs seg)
 {
-    typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
+    typedef ChainCfg<TIn, C, NW, NCT, SB, SUMMARY> Q;
     typedef typename Q::OpT OpT;
     typedef typename Q::Img Img;
     constexpr int NT = Q::NT, BV = Q::BV, LDV = Q::LDV, VEC = Q::VEC, VPR = Q::VPR;
@@ -2531,20 +2538,22 @@ template <typename TIn, int C, int NW, int NCT, bool SB = false>
 static hipError_t launch_chain_t(const void *v, const float *init, const int32_t *cu, int32_t N, int32_t T_tot,
                                  int32_t H, int32_t dv, void *out, float *fin, SegArgs seg, hipStream_t stream)
 {
-    typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
     const bool summary = seg.mode == SEG_SUMMARY;
+    typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
+    typedef ChainCfg<TIn, C, NW, NCT, SB, true> QS;
     const int kind = summary ? 1 : (seg.snap ? 2 : 0);
+    const uint32_t bytes = summary ? QS::bytes : Q::bytes;
     auto kern = kind == 1 ? kda_chain_kernel<TIn, C, NW, NCT, true, SB>
                           : (kind == 2 ? kda_chain_kernel<TIn, C, NW, NCT, false, SB, true>
                                        : kda_chain_kernel<TIn, C, NW, NCT, false, SB>);
     static std::atomic<uint64_t> lds_set[3];
-    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)Q::bytes, lds_set[kind])) return e;
+    if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bytes, lds_set[kind])) return e;
     const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
     const int nblk = (summary ? dv + DK : dv) / Q::BV;
     const int64_t grid = (units + 7) / 8 * 8 * nblk;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(v), init,
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), bytes, stream, static_cast<const TIn *>(v), init,
                        cu, N, T_tot, H, dv, static_cast<TIn *>(out), fin, seg);
     return hipGetLastError();
 }
