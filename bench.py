@@ -57,7 +57,7 @@ BWD_BYTES_PER_HT = 4 * 2 * DK + 4 * DK + 4 + 4 * (3 * DK + DV) + 4
 # (dO S^T, dX S^T, W G^T: 3); 8 contractions x 2 dk dv flops
 BWD_FLOP_PER_HT = 16 * DK * DV
 PREFILL_KERNELS = {
-    "cp": "kda_prefill_cp call: kda_cp_plan_kernel (two plans), kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands), "
+    "cp": "kda_prefill_cp call: kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands; with at most 256 sequences its last two workgroups build the two plans, else kda_cp_plan_kernel runs first), "
           "kda_chain_kernel<bf16,32,8 waves,2 tiles,summary>, kda_cp_combine_kernel, "
           "kda_chain_kernel<bf16,32,4 waves,2 tiles,output,single buffer>",
     "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
