@@ -1893,17 +1893,24 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[ct][r][i] = (summary && 16 * r + 4 * lj + i == col - dv) ? 1.f : 0.f;
         }
-        // the state is carried scaled per column by a power of two (see chain_chunk)
-        sS[ct] = 1.f;
-        if (Q::P::kIn16) {
-            float m = 0.f;
-#pragma unroll
-            for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, S[ct][r]);
-            sS[ct] = fminf(pow2_scale(colmax(m)), kScaleCap);
-#pragma unroll
-            for (int r = 0; r < DK / 16; ++r) S[ct][r] *= sS[ct];
-        }
     }
+    // the state is carried scaled per column by a power of two (see chain_chunk);
+    // the scales are taken after the first chunk's loads are issued (outputs),
+    // so that those loads and the state's are in flight together
+    auto scale_state = [&]() {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            sS[ct] = 1.f;
+            if (Q::P::kIn16) {
+                float m = 0.f;
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r) m = absmax_acc(m, S[ct][r]);
+                sS[ct] = fminf(pow2_scale(colmax(m)), kScaleCap);
+#pragma unroll
+                for (int r = 0; r < DK / 16; ++r) S[ct][r] *= sS[ct];
+            }
+        }
+    };
 
     // ---- chunk staging: image + value tile of chunk ci in registers
     constexpr int IIT = SUMMARY ? Q::IITEMS_SUM : Q::IITEMS;       // image vectors this pass reads
@@ -1950,6 +1957,7 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
     };
     auto stage = [&](int ci, int b) { stage_from(ci, b, ri, rv); };
     if constexpr (SUMMARY && !SB) {
+        scale_state();
         // summaries: the operands are loaded two chunks ahead, into register
         // sets A (ri, rv) and B (ri2, rv2) in turn, so that a load has two
         // chunks' work to arrive; the loop takes chunks in pairs to keep the
@@ -2009,15 +2017,14 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         return Q::P::kIn16 ? static_cast<void *>(reinterpret_cast<f16_t *>(seg.snap) + (gc * num_heads + h) * DK * dv)
                            : static_cast<void *>(seg.snap + (gc * num_heads + h) * DK * dv);
     };
+    if (nch > 0) load(0);
+    scale_state();
     if constexpr (SNAP) {
         if ((sflags & SEG_FIRST) && nch > 0)
             store_scaled_state<Q::P::kIn16, NCT>(snap_at(gc0), seg.snap_scale + (gc0 * num_heads + h) * dv, S, sS,
                                                  dv0 + vcol, dv, lj, lm);
     }
-    if (nch > 0) {
-        load(0);
-        stage(0, 0);
-    }
+    if (nch > 0) stage(0, 0);
     TIn *sOw = reinterpret_cast<TIn *>(smem + Q::offO) + wave * C * 16 * NCT;   // this wave's output tile
     for (int ci = 0; ci < nch; ++ci) {
         __syncthreads();                          // chunk ci staged; (double buffer) ci - 1 done with the other
