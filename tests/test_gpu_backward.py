@@ -78,6 +78,16 @@ def test_backward_several_segments_per_sequence(dtype):
     _check(_case([700, 300, 1100], H=2, dtype=dtype, seed=65), dtype, "multi_segment")
 
 
+@pytest.mark.parametrize("nseq", [256, 300])
+def test_backward_many_sequences(nseq):
+    # 256 sequences: the plan is built inside the chunk-operand launch; 300:
+    # by its own launch first (more than one block of 256 sequences)
+    rng = np.random.default_rng(66)
+    lengths = [int(x) for x in rng.integers(0, 40, size=nseq)]
+    lengths[5], lengths[200] = 0, 300
+    _check(_case(lengths, H=2, dtype=torch.bfloat16, seed=66), torch.bfloat16, "many_seqs_%d" % nseq)
+
+
 def test_backward_bitwise_deterministic():
     inp = _case([200, 77], H=2, dtype=torch.bfloat16, seed=64)
     a = K.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],

@@ -143,14 +143,17 @@ def test_cp_summary_units_vs_oracle(dtype, seg_len):
     _check_cp(inp, TOL[dtype], "cp_units", seg_len)
 
 
-def test_cp_many_sequences_vs_oracle():
+@pytest.mark.parametrize("dtype,nseq", [(torch.float32, 300), (torch.bfloat16, 300), (torch.bfloat16, 256),
+                                        (torch.bfloat16, 257)])
+def test_cp_many_sequences_vs_oracle(dtype, nseq):
     # more than 256 sequences: the plan kernel walks them in several blocks of
-    # 256 (segment and chunk numbering, the order of sequences by unit count)
+    # 256 (segment and chunk numbering, the order of sequences by unit count);
+    # up to 256 the plans are built inside the chunk-operand launch
     rng = np.random.default_rng(40)
-    lengths = [int(x) for x in rng.integers(0, 90, size=300)]
-    lengths[7], lengths[123], lengths[299] = 0, 257, 300
-    inp = to_dev(I.random_prefill(lengths, H=2, dtype=torch.float32, seed=40))
-    _check_cp(inp, TOL[torch.float32], "cp_many_seqs", 64)
+    lengths = [int(x) for x in rng.integers(0, 90, size=nseq)]
+    lengths[7], lengths[123], lengths[nseq - 1] = 0, 257, 300
+    inp = to_dev(I.random_prefill(lengths, H=2, dtype=dtype, seed=40))
+    _check_cp(inp, TOL[dtype], "cp_many_seqs_%d" % nseq, 64)
 
 
 def test_cp_run_to_run_bitwise_determinism():
