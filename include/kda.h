@@ -169,10 +169,13 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  * fixed-size-state-fragment scheme of page ailearn.mscapital.top/kimi-k3.html,
  * card "传固定状态片段" (local cumulative transform and zero-state fragment,
  * then a prefix combination), applied across the compute units of one GPU.
- * Results equal kda_prefill up to fp32 rounding order.  When there are many
- * (segment, head) pairs, the zero-state runs and the chaining use summary
- * units of a quarter (or half) segment instead of whole segments, so that
- * they pack the compute units evenly; the outputs still run whole segments.
+ * Results equal kda_prefill up to rounding order; for bf16 inputs the
+ * chaining's products M_s S_in run as three bf16 MFMA terms of the values
+ * split into high and low halves (about 2^-16 relative error per product).
+ * When there are many (segment, head) pairs and segments of at least 1,024
+ * tokens, the zero-state runs and the chaining use summary units of a quarter
+ * (or half) segment instead of whole segments, so that they pack the compute
+ * units evenly; the outputs still run whole segments.
  *
  *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
  *              (total_tokens * num_heads / 256, clamped to [256, 32768])
