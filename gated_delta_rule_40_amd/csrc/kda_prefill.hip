@@ -635,10 +635,14 @@ __device__ __forceinline__ void pair_of(int p, int &a, int &b) {
 }
 
 // Gram tiles A (strictly lower) and P (lower incl.), one job = one sub-tile
-// pair and one of the two products.  Operands of type GT with row stride ld;
-// if hs != nullptr the column operand of pair p is scaled per channel by
-// hs[p][.].  sign: +1 if the row operand of A is +K, -1 if it holds -K.
+// pair, both products: they share the column operand, whose fragments are
+// then read once, and the two accumulation chains interleave.  Operands of
+// type GT with row stride ld; if hs != nullptr the column operand of pair p
+// is scaled per channel by hs[p][.].  sign: +1 if the row operand of A is
+// +K, -1 if it holds -K.
 // Output: N = Diag(beta) A (diagonal blocks fp32 to sAd, others to sN) and P.
+// With NPAIR < NW (32-token chunks: three pairs, four waves) the last wave
+// has no job.
 template <typename GT, typename OpT, int C, int NW>
 __device__ __forceinline__ void gram_tiles(const GT *rowA_base, const GT *rowP_base, const GT *col_base,
                                            int ld, const float *hs, float signA,
@@ -648,39 +652,36 @@ __device__ __forceinline__ void gram_tiles(const GT *rowA_base, const GT *rowP_b
     typedef Mma<GT> G;
     constexpr int NSUB = C / SUB, NPAIR = NSUB * (NSUB + 1) / 2;
     constexpr int KBc = Mma<OpT>::KB;    // K-block of the P W contraction in the chain
-    for (int job = wave; job < 2 * NPAIR; job += NW) {
-        const int p = job >> 1;
-        const bool isP = job & 1;
+    for (int p = wave; p < NPAIR; p += NW) {
         int a, b;
         pair_of(p, a, b);
-        f32x4 acc = zero4();
-        const GT *rowR = (isP ? rowP_base : rowA_base) + (a * SUB + lm) * ld;
+        f32x4 accA = zero4(), accP = zero4();
+        const GT *rowA = rowA_base + (a * SUB + lm) * ld;
+        const GT *rowP = rowP_base + (a * SUB + lm) * ld;
         const GT *rowC = col_base + (b * SUB + lm) * ld;
 #pragma unroll
         for (int k0 = 0; k0 < DK; k0 += G::KB) {
             const typename G::frag bf = hs ? G::load_scaled(rowC, hs + p * DK, k0, lj) : G::load_p(rowC, k0, lj);
-            acc = G::mma(G::load_p(rowR, k0, lj), bf, acc);
+            accA = G::mma(G::load_p(rowA, k0, lj), bf, accA);
+            accP = G::mma(G::load_p(rowP, k0, lj), bf, accP);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rl = 4 * lj + i;                 // row within sub-tile a
             const int r = a * SUB + rl, cc = b * SUB + lm;
-            if (isP) {
-                const float pv = (a == b && lm > rl) ? 0.f : acc[i];
-                sP[r * ldc + kperm<OpT>(cc)] = from_f<OpT>(pv);
-                if (KBc == 32 && a == b && (a & 1) == 0 && a + 1 < NSUB)
-                    sP[r * ldc + kperm<OpT>(cc + SUB)] = from_f<OpT>(0.f);  // a K-block pairs sub-tiles a, a+1
-            } else if (a != b) {
-                sN[r * ldc + cc] = from_f<OpT>(sBeta[r] * signA * acc[i]);   // N = Diag(beta) A
-            }
+            const float pv = (a == b && lm > rl) ? 0.f : accP[i];
+            sP[r * ldc + kperm<OpT>(cc)] = from_f<OpT>(pv);
+            if (KBc == 32 && a == b && (a & 1) == 0 && a + 1 < NSUB)
+                sP[r * ldc + kperm<OpT>(cc + SUB)] = from_f<OpT>(0.f);  // a K-block pairs sub-tiles a, a+1
+            if (a != b) sN[r * ldc + cc] = from_f<OpT>(sBeta[r] * signA * accA[i]);   // N = Diag(beta) A
         }
-        if (!isP && a == b) {
+        if (a == b) {
             // diagonal block, strictly lower, stored transposed: sAd[a][col][row]
             f32x4 nt;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rl = 4 * lj + i;
-                nt[i] = (lm >= rl) ? 0.f : sBeta[a * SUB + rl] * signA * acc[i];
+                nt[i] = (lm >= rl) ? 0.f : sBeta[a * SUB + rl] * signA * accA[i];
             }
             *reinterpret_cast<f32x4 *>(sAd + (a * SUB + lm) * 20 + 4 * lj) = nt;
         }
@@ -1245,29 +1246,62 @@ void kda_prefill_kernel(
     };
     constexpr int GPS = SUB / GRP;                        // groups per sub-tile
 
-    // chunk-operand pass: LDS byte offsets of this thread's image vectors (fixed)
+    // chunk-operand pass: the image of a chunk goes out in three parts.  The
+    // vectors that phase 1 makes final (the decayed operands, gamma, beta;
+    // "early") leave while the Gram and the diagonal solve run on fewer waves
+    // than the workgroup has, P with the second part; the (I + N)^-1 blocks
+    // and their scales ("late") at the end.  A chunk on the sub-tile path
+    // rewrites its operands after its Gram and stores its whole image at the end.
     typedef ChunkImage<TIn, C> Img;
     constexpr int SITEMS = kPrep ? (Img::NVEC + NT - 1) / NT : 1;
-    uint32_t img_off[SITEMS];
-    if constexpr (kPrep) {
-        const typename Img::Offs o = {(uint32_t)P::offNKp, (uint32_t)P::offQp, (uint32_t)P::offKhT,
+    const typename Img::Offs img_o = {(uint32_t)P::offNKp, (uint32_t)P::offQp, (uint32_t)P::offKhT,
                                       (uint32_t)P::offT, (uint32_t)P::offP, (uint32_t)P::offGam,
                                       (uint32_t)P::offBeta, (uint32_t)P::offTs};
+    constexpr int kE0 = Img::vNKp + Img::vKhT, kE1 = kE0 + Img::vGam + Img::vBeta;
+    constexpr int NEARLY = Img::NVEC - Img::vT - Img::vTs;          // early vectors, P last
+    constexpr int NLATE = Img::vT + Img::vTs;
+    auto early_vec = [](int e) { return e < kE0 ? e : (e < kE1 ? e + Img::vT : e + Img::vT + Img::vTs); };
+    auto late_vec = [](int l) { return l < Img::vT ? kE0 + l : kE0 + Img::vT + Img::vGam + Img::vBeta; };
+    // first part: the last wave, while the others run the Gram (NPAIR < NW),
+    // ITS_1 vectors per lane, none of them P; second part: the rest of the
+    // early vectors from waves 1 .. NW-1 while wave 0 runs the solve
+    constexpr int ITS_1 = P::NPAIR < NW ? 8 : 0, NE1 = 64 * ITS_1;
+    constexpr int ITS_2 = NW > 1 ? (NEARLY - NE1 + 64 * (NW - 1) - 1) / (64 * (NW - 1)) : 0;
+    static_assert(!kPrep || (NE1 <= NEARLY - Img::vP && NW >= 2), "image parts");
+    // early vectors e0 + t + j * nth (j < its), clamped to the last one (the
+    // same value again to the same place); LDS reads in batches of four
+    // ahead of their stores
+    auto store_early = [&](f32x4 *dst, int e0, int t, int nth, auto its_tag) {
+        constexpr int ITS = decltype(its_tag)::value;
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) img_off[it] = Img::lds_off(min(tid + it * NT, Img::NVEC - 1), o);
-        // One placeholder store per image item after the first chunk's loads,
-        // so that the loop is entered as it is re-entered from its end (the
-        // chunk's loads followed by SITEMS stores): the compiler merges the two
-        // paths at the loop head and, were they to differ, would count as if
-        // there were no stores after the loads, and wait for the previous
-        // chunk's image stores before each use of the prefetched data.  The
-        // placeholders go to the last image slot of this head, which valid
-        // input never uses (there are more slots than chunks); every
-        // workgroup of the head writes the same zeros there, so the lines
-        // stay in L2.  (nch >= 1 here: a workgroup without chunks has returned)
+        for (int j0 = 0; j0 < ITS; j0 += 4) {
+            f32x4 tv[4];
+            int vv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j0 + j < ITS) {
+                    vv[j] = early_vec(min(e0 + t + (j0 + j) * nth, NEARLY - 1));
+                    tv[j] = *reinterpret_cast<const f32x4 *>(smem + Img::lds_off(vv[j], img_o));
+                }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (j0 + j < ITS) __builtin_nontemporal_store(tv[j], &dst[vv[j]]);
+        }
+    };
+    if constexpr (kPrep) {
+        // Placeholder stores after the first chunk's loads, as many as every
+        // path through the loop issues after its prefetch at the least (the
+        // late part of the image), so that the loop is entered as it is
+        // re-entered from its end: the compiler merges the two paths at the
+        // loop head and, were the entry to have fewer, would wait for the
+        // previous chunk's image stores before each use of the prefetched
+        // data.  The placeholders go to the last image slot of this head,
+        // which valid input never uses (there are more slots than chunks);
+        // every workgroup of the head writes the same zeros there, so the
+        // lines stay in L2.  (nch >= 1 here: a workgroup without chunks has returned)
         f32x4 *junk = seg.img + ((int64_t)(seg.img_slots - 1) * num_heads + h) * Img::NVEC;
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) junk[min(tid + it * NT, Img::NVEC - 1)] = zero4();
+        for (int l0 = 0; l0 < NLATE; l0 += NT) junk[late_vec(min(l0 + tid, NLATE - 1))] = zero4();
         if constexpr (kPrepG) {   // the gradient images' placeholders likewise
             f32x4 *gjunk = seg.gimg + ((int64_t)(seg.img_slots - 1) * num_heads + h) * Img::NVEC;
 #pragma unroll
@@ -1426,6 +1460,11 @@ void kda_prefill_kernel(
         else   // rows hold -GS K+ and GS Q+, columns K e^-Gamma / GS
             gram_tiles<OpT, OpT, C, NW>(sNKp, sQp, sKc, LDK, nullptr, -1.f, sBeta, sAd, sN, sP, LDC,
                                         wave, lj, lm);
+        if constexpr (kPrep && ITS_1 > 0) {    // image, first part (the wave without a Gram job)
+            if (!slow && wave == NW - 1)
+                store_early(seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC, 0, lane, 64,
+                            std::integral_constant<int, ITS_1>());
+        }
         __syncthreads();
 
         // ---- 3. chain operands after a slow Gram; value tile; next chunk's
@@ -1495,6 +1534,11 @@ void kda_prefill_kernel(
 #pragma unroll
             for (int r = 0; r < SUB; ++r) sT[(a * SUB + r) * LDC + a * SUB + nc] = from_f<OpT>(x[r] * sc);
         }
+        if constexpr (kPrep) {                 // image, second part (P included; wave 0 solves)
+            if (!slow && wave > 0)
+                store_early(seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC, NE1, tid - 64,
+                            64 * (NW - 1), std::integral_constant<int, ITS_2>());
+        }
         __syncthreads();
 
         // ---- 3b. off-diagonal blocks: T_ab = -T_aa sum_{b<=s<a} N_as T_sb, by distance a-b
@@ -1528,17 +1572,29 @@ void kda_prefill_kernel(
 
         if constexpr (kPrep) {
             // ---- chunk-operand image of (chunk, head) -> global
-            f32x4 *dst = seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC;
-            // all LDS reads first, then the stores; surplus items repeat the last
-            // vector (same value, same place) so that every store is issued
-            f32x4 tv[SITEMS];
-#pragma unroll
-            for (int it = 0; it < SITEMS; ++it) tv[it] = *reinterpret_cast<const f32x4 *>(smem + img_off[it]);
-#pragma unroll
             // non-temporal: the images are read by later launches, on other
             // XCDs, and the kernel's end then has less in L2 to write back
             // (the next launch started 1.4 us sooner on 4,096 x 8)
-            for (int it = 0; it < SITEMS; ++it) __builtin_nontemporal_store(tv[it], &dst[min(tid + it * NT, Img::NVEC - 1)]);
+            f32x4 *dst = seg.img + ((int64_t)(gc_begin + ci) * num_heads + h) * Img::NVEC;
+            if (slow) {
+                // the whole image; all LDS reads first, then the stores;
+                // surplus items repeat the last vector (same value, same place)
+                f32x4 tv[SITEMS];
+#pragma unroll
+                for (int it = 0; it < SITEMS; ++it)
+                    tv[it] = *reinterpret_cast<const f32x4 *>(smem + Img::lds_off(min(tid + it * NT, Img::NVEC - 1), img_o));
+#pragma unroll
+                for (int it = 0; it < SITEMS; ++it) __builtin_nontemporal_store(tv[it], &dst[min(tid + it * NT, Img::NVEC - 1)]);
+            } else {
+                // one store per lane and item with no condition, so that every
+                // path ends with the same stores after the prefetch (surplus
+                // lanes repeat the last vector: one write per wave)
+#pragma unroll
+                for (int l0 = 0; l0 < NLATE; l0 += NT) {
+                    const int v = late_vec(min(l0 + tid, NLATE - 1));
+                    __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(smem + Img::lds_off(v, img_o)), &dst[v]);
+                }
+            }
             if constexpr (kPrepG) {
                 typedef GradImage<TIn, C> GImg;
                 f32x4 *gdst = seg.gimg + ((int64_t)(gc_begin + ci) * num_heads + h) * GImg::NVEC;
