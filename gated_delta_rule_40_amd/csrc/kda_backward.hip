@@ -535,6 +535,28 @@ void kda_bwd_chunk_kernel(
 #pragma unroll 1
     for (int ct = 0; ct < NCT; ++ct) {
         const int c = 32 * wave + 16 * ct + lm;
+        // this tile's products by selects over the tiles (compile-time indices:
+        // indexed by the loop's ct they would go through scratch memory, whose
+        // loads wait for the previous tile's dq / dk stores)
+        f32x4 cQp[2], cXS[2], cKh[2];
+        float cgm = dgm[0];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            cQp[rt] = dQp[0][rt];
+            cXS[rt] = dXS[0][rt];
+            cKh[rt] = dKh[0][rt];
+        }
+#pragma unroll
+        for (int t = 1; t < NCT; ++t)
+            if (ct == t) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    cQp[rt] = dQp[t][rt];
+                    cXS[rt] = dXS[t][rt];
+                    cKh[rt] = dKh[t][rt];
+                }
+                cgm = dgm[t];
+            }
         auto gm = [&](int t) { return sGm[t * LDG + c]; };
         auto kv = [&](int t) { return to_f(sK[t * LDI + c]); };
         auto qv = [&](int t) { return to_f(sQ[t * LDI + c]); };
@@ -587,9 +609,9 @@ void kda_bwd_chunk_kernel(
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int r = 16 * rt + 4 * lj + ii;
-                extra += kv(r) * dKh[ct][rt][ii] * __expf((float)(gl - gm(r)));
+                extra += kv(r) * cKh[rt][ii] * __expf((float)(gl - gm(r)));
             }
-        extra = sum_rows4(extra) + dgm[ct] * __expf((float)gl);
+        extra = sum_rows4(extra) + cgm * __expf((float)gl);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -607,9 +629,9 @@ void kda_bwd_chunk_kernel(
                     dkc2 += __expf((float)(g15 - gr)) * kc2o[ii];
                 }
                 const float eG = __expf((float)gr), eGn = __expf((float)(gl - gr));
-                const float dq_ = dQp[ct][rt][ii] * eG + dq2;
-                const float dkrow = -sBeta[r] * dXS[ct][rt][ii] * eG + dkr2;
-                const float dkcol = dKh[ct][rt][ii] * eGn + dkc2;
+                const float dq_ = cQp[rt][ii] * eG + dq2;
+                const float dkrow = -sBeta[r] * cXS[rt][ii] * eG + dkr2;
+                const float dkcol = cKh[rt][ii] * eGn + dkc2;
                 const float kr = kv(r);
                 float dG = qv(r) * dq_ + kr * dkrow - kr * dkcol;
                 if (r == L - 1) dG += extra;
@@ -624,11 +646,18 @@ void kda_bwd_chunk_kernel(
 
     // ---- 5. dg = reverse cumulative sum of dGamma; dbeta from its parts
     if (tid < BD) {
+        // every row read first (one batch of LDS reads, not one round trip
+        // per row), then summed from the last valid row down, as before
+        float dgr[C];
+#pragma unroll
+        for (int r = 0; r < C; ++r) dgr[r] = sDG[r * LDF + tid];
         float acc = 0.f;
-        for (int r = L - 1; r >= 0; --r) {
-            acc += sDG[r * LDF + tid];
-            dg[(int64_t)(c0 + r) * rowQ + hoff + tid] = acc;
-        }
+#pragma unroll
+        for (int r = C - 1; r >= 0; --r)
+            if (r < L) {
+                acc += dgr[r];
+                dg[(int64_t)(c0 + r) * rowQ + hoff + tid] = acc;
+            }
     } else if (tid < BD + C) {
         const int r = tid - BD;
         if (r < L) dbeta[(int64_t)(c0 + r) * H + h] = sDb[r] + sDb[C + r] + sDb[2 * C + r] + sDb[3 * C + r];

@@ -568,54 +568,60 @@ struct GradImage {
                                                    const OpT *sT, const OpT *sP, const float *sGam,
                                                    const float *sBeta, const float *sTs) {
         constexpr int RK = DK / EPV, RC = C / EPV;
-        union { f32x4 f; OpT h[EPV]; } u;
-        u.f = zero4();
+        // each branch builds its vector in a register vector type (a union
+        // written element by element went through scratch memory)
+        typedef OpT VE __attribute__((ext_vector_type(EPV)));
         if (v < vKh) {                                     // row r (token), channels along the row
             const int r = v / RK, p0 = (v % RK) * EPV;
+            VE w;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) u.h[e] = sKhT[kinv(p0 + e) * P::LDC + kperm<OpT>(r)];
-            return u.f;
+            for (int e = 0; e < EPV; ++e) w[e] = sKhT[kinv(p0 + e) * P::LDC + kperm<OpT>(r)];
+            return __builtin_bit_cast(f32x4, w);
         }
         v -= vKh;
         if (v < vNKpT + vQpT) {                            // row c (channel), tokens along the row
             const OpT *src = v < vNKpT ? sNKp : sQp;
             if (v >= vNKpT) v -= vNKpT;
             const int c = v / RC, p0 = (v % RC) * EPV;
+            VE w;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) u.h[e] = src[kinv(p0 + e) * P::LDK + kperm<OpT>(c)];
-            return u.f;
+            for (int e = 0; e < EPV; ++e) w[e] = src[kinv(p0 + e) * P::LDK + kperm<OpT>(c)];
+            return __builtin_bit_cast(f32x4, w);
         }
         v -= vNKpT + vQpT;
         if (v < vPT) {                                     // P^T[i][r] = P[r][i], r >= i
             const int i = v / RC, p0 = (v % RC) * EPV;
+            VE w;
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
                 const int r = kinv(p0 + e);
-                u.h[e] = r >= i ? sP[r * P::LDC + kperm<OpT>(i)] : from_f<OpT>(0.f);
+                w[e] = r >= i ? sP[r * P::LDC + kperm<OpT>(i)] : from_f<OpT>(0.f);
             }
-            return u.f;
+            return __builtin_bit_cast(f32x4, w);
         }
         v -= vPT;
         if (v < vTT) {                                     // T^T[i][r] = T[r][i], r >= i (plain order)
             const int i = v / RC, p0 = (v % RC) * EPV;
+            VE w;
 #pragma unroll
             for (int e = 0; e < EPV; ++e) {
                 const int r = p0 + e;
-                u.h[e] = r >= i ? sT[r * P::LDC + i] : from_f<OpT>(0.f);
+                w[e] = r >= i ? sT[r * P::LDC + i] : from_f<OpT>(0.f);
             }
-            return u.f;
+            return __builtin_bit_cast(f32x4, w);
         }
         v -= vTT;
         if (v < vGam) return *reinterpret_cast<const f32x4 *>(sGam + 4 * v);
         v -= vGam;
         if (v < vBeta) return *reinterpret_cast<const f32x4 *>(sBeta + 4 * v);
         v -= vBeta;
+        f32x4 x;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {                      // block scales, transposed
             const int idx = 4 * v + e, a = idx / NSUB, b = idx % NSUB;
-            u.f[e] = idx < NSUB * NSUB ? sTs[b * NSUB + a] : 0.f;
+            x[e] = idx < NSUB * NSUB ? sTs[b * NSUB + a] : 0.f;
         }
-        return u.f;
+        return x;
     }
 };
 
