@@ -36,7 +36,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
                                        int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
-                                       hipStream_t stream);
+                                       int32_t sum_tail, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
@@ -217,6 +217,10 @@ namespace {
 constexpr int32_t kCpChunk = 32;     // chunk size of the segmented runs
 constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the segment-output pass
 constexpr int32_t kCpSumBlock = 256; // value + transition columns per workgroup of the summary pass
+// chunks a summary unit is first walked over from its end: on decaying gates
+// the transition over them is exactly zero in fp32, and the rest of the unit
+// then cannot reach its end state (see the summary loop in kda_prefill.hip)
+constexpr int32_t kCpSumTail = 32;
 constexpr int64_t kNumCUs = 256;     // compute units of one MI355X
 
 struct CpLayout {
@@ -366,14 +370,14 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
-                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, 0, kCpSumTail, s);
     if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
                                   seq_order, nullptr, 0, cmb_fmt, s);
     if (e == hipSuccess)   // outputs and final states, each segment from the entering state of its first unit
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
-                             nullptr, nullptr, nullptr, useq_seg, lay.unit_len, lay.max_units, 0, narrow_out, 1, s);
+                             nullptr, nullptr, nullptr, useq_seg, lay.unit_len, lay.max_units, 0, narrow_out, 1, 0, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -657,7 +661,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (e == hipSuccess)   // s: forward summaries [S^0 | M | M^T] of every segment
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, 0, s);
     if (e == hipSuccess) e = fork(1, s, s2);
     if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
@@ -671,7 +675,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (e == hipSuccess)   // s: the state at every chunk start, and every chunk's U and W
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
-                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, s);
+                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, 0, s);
     if (forked) {          // join: s waits for s2 (also after a failed launch)
         const hipError_t j = fork(2, s2, s);
         if (e == hipSuccess) e = j;

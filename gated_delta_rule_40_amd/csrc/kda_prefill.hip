@@ -190,6 +190,11 @@ struct SegArgs {
     // (cb * 8 + r) * 64 + lane: rows 16 r + 4 j + i of column 16 cb + m, as
     // kda_cp_combine_kernel writes them with a fragment layout) instead of rows
     int32_t init_tiles;
+    // SEG_SUMMARY, workgroups holding every transition column (256-column
+    // bf16 summaries): a unit of more than sum_tail chunks (even, 0 = off) is
+    // first summarised from its last sum_tail chunks alone, and in full only
+    // if its transition over them is not exactly zero (see the summary loop)
+    int32_t sum_tail;
 };
 
 // Inclusive scans of a (and b) over the 256 threads of a workgroup: in-wave
@@ -2034,6 +2039,25 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         // tile once the transition tiles die, measured no faster.)
         const bool trans_wave = dv0 + 16 * NCT * wave >= dv;
         bool dead = false;
+        // Tail walk.  The unit's state enters its end through the product of
+        // the chunk transitions, which the transition columns compute from the
+        // identity.  When those columns, started at chunk nch - K, are all
+        // exactly zero at the end, the fp32 transition over the last K chunks
+        // has underflowed: whatever state enters chunk nch - K reaches the end
+        // scaled by less than the smallest fp32 subnormal, so the end state
+        // from a zero state at chunk nch - K equals the full walk's up to fp32
+        // rounding, and the unit's transition M is exactly zero either way.
+        // The walk then covers the last K chunks only.  Otherwise the state is
+        // reset and the whole unit is walked, as without the tail (K chunks
+        // more work).  Virtual chunk v is chunk nch - K + v for v < K and
+        // chunk v - K after a reset; the loop has one exit, so the waits for
+        // the prefetched operands stay exact.
+        const int K = seg.sum_tail;
+        const bool tail = K > 0 && (K & 1) == 0 && nch > K && dv0 == 0 && BV >= dv + DK;   // block-uniform
+        const int nvmax = tail ? K + nch : nch;                // virtual chunks, at most
+        int nv = tail ? K : nch;                               // virtual chunks to walk
+        auto real = [&](int v) { return tail ? (v < K ? nch - K + v : v - K) : v; };
+        __shared__ int tail_dead[NW];
         auto run = [&](int ci) {
             if (dead) return;
             const unsigned char *base = smem + (ci & 1) * Q::BUF;
@@ -2051,24 +2075,42 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
             dead = trans_wave && zero == (1u << NCT) - 1u;
         };
         if (nch > 0) {
-            load_to(0, ri, rv);
-            stage_from(0, 0, ri, rv);
-            load_to(min(1, nch - 1), ri, rv);
+            load_to(real(0), ri, rv);
+            stage_from(real(0), 0, ri, rv);
+            load_to(real(min(1, nvmax - 1)), ri, rv);
         }
         int ci = 0;
-        for (; ci + 2 <= nch; ci += 2) {
+        for (; ci + 2 <= nv; ci += 2) {
             __syncthreads();
-            load_to(min(ci + 2, nch - 1), ri2, rv2);
+            load_to(real(min(ci + 2, nvmax - 1)), ri2, rv2);
             asm volatile("" ::: "memory");
             run(ci);
-            stage_from(min(ci + 1, nch - 1), (ci + 1) & 1, ri, rv);
+            stage_from(real(min(ci + 1, nvmax - 1)), (ci + 1) & 1, ri, rv);
             __syncthreads();
-            load_to(min(ci + 3, nch - 1), ri, rv);
+            load_to(real(min(ci + 3, nvmax - 1)), ri, rv);
             asm volatile("" ::: "memory");
             run(ci + 1);
-            stage_from(min(ci + 2, nch - 1), ci & 1, ri2, rv2);
+            stage_from(real(min(ci + 2, nvmax - 1)), ci & 1, ri2, rv2);
+            if (tail && ci + 2 == K && nv == K) {              // end of the tail walk (block-uniform)
+                if (lane == 0) tail_dead[wave] = !trans_wave || dead;
+                __syncthreads();
+                bool all_dead = true;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) all_dead = all_dead && tail_dead[w] != 0;
+                if (!all_dead) {                              // the whole unit, from the start
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                        for (int r = 0; r < DK / 16; ++r)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) S[ct][r][i] = 16 * r + 4 * lj + i == colc[ct] - dv ? 1.f : 0.f;
+                    scale_state();
+                    dead = false;
+                    nv = K + nch;
+                }
+            }
         }
-        if (ci < nch) {
+        if (ci < nv) {
             __syncthreads();
             run(ci);
         }
@@ -2987,7 +3029,9 @@ extern "C" hipError_t kda_launch_chunk_prep(int bf16, const void *q, const void 
 // narrow (bf16; dv_block 256 or 128): 128-column workgroups of eight waves,
 // for calls with fewer workgroups than compute units.  init_tiles (outputs,
 // dv = 128): seg_init as kda_cp_combine_kernel writes it with a fragment
-// layout (accumulator tiles).
+// layout (accumulator tiles).  sum_tail (summaries; even, 0 = off): units of
+// more than sum_tail chunks are summarised from their last sum_tail chunks
+// when the transition over those is exactly zero (256-column bf16 form only).
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
@@ -2995,10 +3039,11 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
                                        int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
-                                       hipStream_t stream)
+                                       int32_t sum_tail, hipStream_t stream)
 {
     using namespace kda;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
+    if (sum_tail < 0 || (sum_tail & 1) || (sum_tail && mode != SEG_SUMMARY)) return hipErrorInvalidValue;
     // the fragment layouts: bf16 summaries in 256-column blocks (128 when
     // narrow), fp32 in 64-column blocks
     const int cbase = cmb_fmt & ~CMB_MT;
@@ -3011,6 +3056,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                    mode == SEG_SUMMARY ? nullptr : static_cast<float *>(snap), 0, 0, sched, init_seq_seg, init_unit,
                    init_units, 0, 0, nullptr, snap_scale, uw_u, uw_w, cmb_fmt};
     seg.init_tiles = init_tiles;
+    seg.sum_tail = sum_tail;
     if (init_tiles && (mode != SEG_OUTPUT || dv != DK || !plan)) return hipErrorInvalidValue;
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,

@@ -143,6 +143,18 @@ def test_cp_summary_units_vs_oracle(dtype, seg_len):
     _check_cp(inp, TOL[dtype], "cp_units", seg_len)
 
 
+@pytest.mark.parametrize("g_lo", [-5.0 / 16.0, -0.002])
+def test_cp_summary_tail_vs_oracle(g_lo):
+    # units of 256 chunks (seg_len 8,192; H = 64 puts the summaries in the
+    # 256-column form that holds every transition column).  Under the
+    # workloads' decay (g in (-5/16, 0]) the transition over a unit's last 32
+    # chunks is exactly zero, and each unit is summarised from those chunks
+    # alone; with g in (-0.002, 0] it is not, and each unit is walked again
+    # in full.  Both against the oracle's straight token walk.
+    inp = to_dev(I.random_prefill([20000, 9000, 300], H=64, dtype=torch.bfloat16, seed=43, g_lo=g_lo))
+    _check_cp(inp, TOL[torch.bfloat16], "cp_tail_g_lo=%g" % g_lo, 8192)
+
+
 @pytest.mark.parametrize("dtype,nseq", [(torch.float32, 300), (torch.bfloat16, 300), (torch.bfloat16, 256),
                                         (torch.bfloat16, 257)])
 def test_cp_many_sequences_vs_oracle(dtype, nseq):
