@@ -219,8 +219,12 @@ constexpr int32_t kCpBlock = 128;    // value columns per workgroup of the segme
 constexpr int32_t kCpSumBlock = 256; // value + transition columns per workgroup of the summary pass
 // chunks a summary unit is first walked over from its end: on decaying gates
 // the transition over them is exactly zero in fp32, and the rest of the unit
-// then cannot reach its end state (see the summary loop in kda_prefill.hip)
-constexpr int32_t kCpSumTail = 32;
+// then cannot reach its end state (see the summary loop in kda_prefill.hip).
+// Under g ~ U(-5/16, 0] the transition of a 256-chunk unit dies between 24
+// and 36 chunks from its end: 16 and 24 sent most units back to a full walk
+// (1M tokens x 16 heads: 17.7 ms), 32 some (13.7 ms), 36 almost none (13.3
+// ms); longer tails only add work (44: 13.5 ms).
+constexpr int32_t kCpSumTail = 36;
 constexpr int64_t kNumCUs = 256;     // compute units of one MI355X
 
 struct CpLayout {

@@ -176,6 +176,14 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  * tokens, the zero-state runs and the chaining use summary units of a quarter
  * (or half) segment instead of whole segments, so that they pack the compute
  * units evenly; the outputs still run whole segments.
+ * For bf16 inputs, when there are more (unit, head) pairs than compute units,
+ * a zero-state run over a unit longer than 36 chunks of 32 tokens first
+ * covers the unit's last 36 chunks only.  When the transition
+ * over them comes out exactly zero in fp32 (gates that decay: the state
+ * entering those chunks cannot reach their end above the smallest fp32
+ * subnormal), that run is the unit's S^0, equal to the full run's up to fp32
+ * rounding, and M is zero; otherwise the whole unit is run.  This holds for
+ * any inputs: the test is made on the computed transition, not assumed.
  *
  *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
  *              (total_tokens * num_heads / 256, clamped to [256, 32768])

@@ -147,7 +147,7 @@ def test_cp_summary_units_vs_oracle(dtype, seg_len):
 def test_cp_summary_tail_vs_oracle(g_lo):
     # units of 256 chunks (seg_len 8,192; H = 64 puts the summaries in the
     # 256-column form that holds every transition column).  Under the
-    # workloads' decay (g in (-5/16, 0]) the transition over a unit's last 32
+    # workloads' decay (g in (-5/16, 0]) the transition over a unit's last 36
     # chunks is exactly zero, and each unit is summarised from those chunks
     # alone; with g in (-0.002, 0] it is not, and each unit is walked again
     # in full.  Both against the oracle's straight token walk.
