@@ -1872,7 +1872,7 @@ __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const 
 // the start of every chunk at its global index in seg.snap ([chunks][H][DK][dv],
 // see store_scaled_state), and every chunk's U = V - K+ S0 and W in seg.uw_u,
 // seg.uw_w ([chunks][H][C][dv] fp32, rows of valid tokens); out may be NULL.
-template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false>
+template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false, bool TAIL = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB, SUMMARY>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
@@ -2051,9 +2051,10 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         // reset and the whole unit is walked, as without the tail (K chunks
         // more work).  Virtual chunk v is chunk nch - K + v for v < K and
         // chunk v - K after a reset; the loop has one exit, so the waits for
-        // the prefetched operands stay exact.
-        const int K = seg.sum_tail;
-        const bool tail = K > 0 && (K & 1) == 0 && nch > K && dv0 == 0 && BV >= dv + DK;   // block-uniform
+        // the prefetched operands stay exact.  (TAIL instantiations only: the
+        // others compile without the tail's registers and branches.)
+        const int K = TAIL ? seg.sum_tail : 0;
+        const bool tail = TAIL && K > 0 && (K & 1) == 0 && nch > K && dv0 == 0 && BV >= dv + DK;   // block-uniform
         const int nvmax = tail ? K + nch : nch;                // virtual chunks, at most
         int nv = tail ? K : nch;                               // virtual chunks to walk
         auto real = [&](int v) { return tail ? (v < K ? nch - K + v : v - K) : v; };
@@ -2652,12 +2653,16 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
     const bool summary = seg.mode == SEG_SUMMARY;
     typedef ChainCfg<TIn, C, NW, NCT, SB> Q;
     typedef ChainCfg<TIn, C, NW, NCT, SB, true> QS;
-    const int kind = summary ? 1 : (seg.snap ? 2 : 0);
+    // the summaries' tail walk needs every transition column in one workgroup
+    constexpr bool kTail = QS::BV >= 2 * DK && !SB;
+    const int kind = summary ? (kTail && seg.sum_tail > 0 ? 3 : 1) : (seg.snap ? 2 : 0);
     const uint32_t bytes = summary ? QS::bytes : Q::bytes;
     auto kern = kind == 1 ? kda_chain_kernel<TIn, C, NW, NCT, true, SB>
                           : (kind == 2 ? kda_chain_kernel<TIn, C, NW, NCT, false, SB, true>
                                        : kda_chain_kernel<TIn, C, NW, NCT, false, SB>);
-    static std::atomic<uint64_t> lds_set[3];
+    if constexpr (kTail)
+        if (kind == 3) kern = kda_chain_kernel<TIn, C, NW, NCT, true, SB, false, true>;
+    static std::atomic<uint64_t> lds_set[4];
     if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bytes, lds_set[kind])) return e;
     const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
     const int nblk = (summary ? dv + DK : dv) / Q::BV;

@@ -172,17 +172,17 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  * Results equal kda_prefill up to rounding order; for bf16 inputs the
  * chaining's products M_s S_in run as three bf16 MFMA terms of the values
  * split into high and low halves (about 2^-16 relative error per product).
- * When there are many (segment, head) pairs and segments of at least 1,024
- * tokens, the zero-state runs and the chaining use summary units of a quarter
- * (or half) segment instead of whole segments, so that they pack the compute
- * units evenly; the outputs still run whole segments.
- * For bf16 inputs, when there are more (unit, head) pairs than compute units,
- * a zero-state run over a unit longer than 36 chunks of 32 tokens first
- * covers the unit's last 36 chunks only.  When the transition
+ * For fp32 inputs, when there are many (segment, head) pairs and segments of
+ * at least 1,024 tokens, the zero-state runs and the chaining use summary
+ * units of a quarter (or half) segment instead of whole segments, so that they
+ * pack the compute units evenly; the outputs still run whole segments.
+ * For bf16 inputs, when there are more (segment, head) pairs than compute
+ * units, a zero-state run over a segment longer than 36 chunks of 32 tokens
+ * first covers the segment's last 36 chunks only.  When the transition
  * over them comes out exactly zero in fp32 (gates that decay: the state
  * entering those chunks cannot reach their end above the smallest fp32
- * subnormal), that run is the unit's S^0, equal to the full run's up to fp32
- * rounding, and M is zero; otherwise the whole unit is run.  This holds for
+ * subnormal), that run is the segment's S^0, equal to the full run's up to
+ * fp32 rounding, and M is zero; otherwise the whole segment is run.  This holds for
  * any inputs: the test is made on the computed transition, not assumed.
  *
  *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
