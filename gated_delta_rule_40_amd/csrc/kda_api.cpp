@@ -28,7 +28,8 @@ extern "C" hipError_t kda_launch_cp_plan_prep(int bf16, const void *q, const voi
                                               int32_t skip_last, int32_t *seq_order, int32_t seg_len2,
                                               int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
                                               int32_t *sched2, int32_t last_len2, int32_t skip_last2,
-                                              int32_t *seq_order2, hipStream_t stream);
+                                              int32_t *seq_order2, int32_t pieces, int32_t piece_len,
+                                              hipStream_t stream);
 extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, const float *init, const int32_t *cu, int32_t N,
                                        int32_t T_tot, int32_t H, int32_t dv, void *out, float *fin,
                                        const int32_t *plan, int32_t num_segs, int32_t mode, const float *seg_init,
@@ -36,7 +37,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
                                        int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
-                                       int32_t sum_tail, hipStream_t stream);
+                                       int32_t sum_tail, int32_t pieces, hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
@@ -230,6 +231,10 @@ constexpr int64_t kNumCUs = 256;     // compute units of one MI355X
 struct CpLayout {
     size_t plan, sched, seq_seg, uplan, usched, useq_seg, seq_order, chunk_off, seg_out, seg_init, img, total;
     int32_t max_segs, max_units, unit_len, max_chunks;
+    // > 0: segments cut at the ends of pieces of the packed chunk order (at
+    // most `pieces` per head, piece_len chunks each, or 0: equal pieces), one
+    // output workgroup per (piece, head); units are then the segments
+    int32_t pieces, piece_len;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -265,13 +270,18 @@ int32_t cp_unit_len(int32_t seg_len, int32_t T, int32_t H, int bf16)
 // [max_units][H][dk][dv] fp32; chunk-operand images [max_chunks][H][image].
 // Every sequence of length L takes max(1, ceil(L / len)) segments (units) and
 // ceil(L / 32) chunks, which max_segs, max_units and max_chunks bound.
-bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16, int32_t seg_len, CpLayout *lay)
+// With pieces, a sequence takes one segment per piece its chunks reach (one
+// when empty), so there are at most pieces + N segments.
+bool cp_layout(int32_t N, int32_t T, int32_t H, int32_t dk, int32_t dv, int bf16, int32_t seg_len, int32_t pieces,
+               int32_t piece_len, CpLayout *lay)
 {
-    const int32_t unit = cp_unit_len(seg_len, T, H, bf16);
-    const int64_t segs = (int64_t)T / seg_len + 1 + N;
-    const int64_t units = (int64_t)T / unit + 1 + N;
+    const int32_t unit = pieces > 0 ? seg_len : cp_unit_len(seg_len, T, H, bf16);
+    const int64_t segs = pieces > 0 ? (int64_t)pieces + 1 + N : (int64_t)T / seg_len + 1 + N;
+    const int64_t units = pieces > 0 ? segs : (int64_t)T / unit + 1 + N;
     const int64_t chunks = (int64_t)T / kCpChunk + 1 + N;
     if (units > INT32_MAX / 4 || chunks > INT32_MAX / 4) return false;
+    lay->pieces = pieces;
+    lay->piece_len = piece_len;
     lay->max_segs = (int32_t)segs;
     lay->max_units = (int32_t)units;
     lay->unit_len = unit;
@@ -308,6 +318,38 @@ int32_t cp_default_seg_len(int32_t T, int32_t H)
     return (int32_t)((len + kCpChunk - 1) / kCpChunk * kCpChunk);
 }
 
+// The segment cut of a call: seg_len > 0 cuts every sequence into seg_len
+// tokens from its start; seg_len < 0 cuts the packed chunk order into pieces
+// of -seg_len tokens (at most 256 sequences); 0 chooses.  Pieces are the
+// automatic choice for 16-bit inputs and at most 256 sequences when the
+// segments would be capped (T H / 256 above 32,768 tokens): then the fewest
+// equal pieces that give every one of two workgroups per compute unit one
+// piece (512 / H per head), so that every output walk has the same length.
+// Cut per sequence, the 1M-token varlen batch (eight sequences, 16 heads)
+// has 592 output workgroups of up to 1,024 chunks for 512 places, and the
+// last ones start as the first finish.
+kda_status cp_cut(int32_t N, int32_t T, int32_t H, int bf16, int32_t *seg_len, int32_t *pieces, int32_t *piece_len)
+{
+    *pieces = 0;
+    *piece_len = 0;
+    if (*seg_len < 0) {
+        if (*seg_len < -(INT32_MAX / 2) || (-*seg_len) % kCpChunk || N > 256) return KDA_ERR_UNSUPPORTED;
+        *seg_len = -*seg_len;
+        *piece_len = *seg_len / kCpChunk;
+        const int64_t np = ((int64_t)T / kCpChunk + N + *piece_len - 1) / *piece_len;
+        if (np > INT32_MAX / 8) return KDA_ERR_UNSUPPORTED;
+        *pieces = (int32_t)(np > 0 ? np : 1);
+        return KDA_OK;
+    }
+    if (*seg_len > 0) return *seg_len % kCpChunk ? KDA_ERR_UNSUPPORTED : KDA_OK;
+    *seg_len = cp_default_seg_len(T, H);
+    if (bf16 && N >= 1 && N <= 256 && (int64_t)T * H / 256 > 32768) {
+        *pieces = (int32_t)(2 * kNumCUs / H > 1 ? 2 * kNumCUs / H : 1);
+        *piece_len = 0;
+    }
+    return KDA_OK;
+}
+
 }  // namespace
 
 size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
@@ -315,10 +357,12 @@ size_t kda_prefill_cp_workspace_size(int32_t num_seqs, int32_t total_tokens, int
 {
     if (num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || dk != kHeadDim || dv != kHeadDim) return 0;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
-    if (seg_len == 0) seg_len = cp_default_seg_len(total_tokens, num_heads);
+    int32_t pieces, piece_len;
+    if (cp_cut(num_seqs, total_tokens, num_heads, dtype == KDA_BF16, &seg_len, &pieces, &piece_len) != KDA_OK) return 0;
     if (seg_len < kCpChunk || seg_len % kCpChunk) return 0;
     CpLayout lay;
-    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_BF16, seg_len, &lay)) return 0;
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_BF16, seg_len, pieces, piece_len, &lay))
+        return 0;
     return lay.total;
 }
 
@@ -332,12 +376,13 @@ kda_status cp_check(const void *q, const void *k, const void *v, const float *g,
 {
     kda_status st = check_common(q, k, v, g, beta, out, dk, dv, dtype);
     if (st == KDA_ERR_INVALID_ARG) return st;
-    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0 || *seg_len < 0)
-        return KDA_ERR_INVALID_ARG;
+    if (!cu_seqlens || num_seqs < 0 || total_tokens < 0 || num_heads <= 0) return KDA_ERR_INVALID_ARG;
     if (st != KDA_OK) return st;
-    if (*seg_len == 0) *seg_len = cp_default_seg_len(total_tokens, num_heads);
+    int32_t pieces, piece_len;
+    if (kda_status c = cp_cut(num_seqs, total_tokens, num_heads, dtype == KDA_BF16, seg_len, &pieces, &piece_len))
+        return c;
     if (*seg_len < kCpChunk || *seg_len % kCpChunk) return KDA_ERR_UNSUPPORTED;
-    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_BF16, *seg_len, lay))
+    if (!cp_layout(num_seqs, total_tokens, num_heads, dk, dv, dtype == KDA_BF16, *seg_len, pieces, piece_len, lay))
         return KDA_ERR_INVALID_ARG;
     if ((int64_t)lay->max_units * num_heads * ((dv + dk) / 16) > INT32_MAX) return KDA_ERR_INVALID_ARG;
     if ((int64_t)lay->max_chunks * num_heads > INT32_MAX) return KDA_ERR_INVALID_ARG;
@@ -367,7 +412,7 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     const int32_t cmb_fmt = bf16 ? 2 : 1;
     // eight-wave 128-column workgroups when a pass has fewer workgroups than
     // the GPU has compute units (bf16)
-    const int64_t out_wgs = (int64_t)lay.max_segs * num_heads;
+    const int64_t out_wgs = (int64_t)(lay.pieces > 0 ? lay.pieces : lay.max_segs) * num_heads;
     const int32_t narrow_out = bf16 && out_wgs <= kNumCUs ? 1 : 0;
     const int32_t narrow_sum = bf16 && (int64_t)lay.max_units * num_heads <= kNumCUs ? 1 : 0;
     // output segments and summary units (SEG_LAST: in a sequence's last segment), one launch
@@ -376,18 +421,19 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     hipError_t e = kda_launch_cp_plan_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                                            lay.max_chunks, img, nullptr, seg_len, lay.max_segs, plan, seq_seg,
                                            chunk_off, sched, 0, 0, nullptr, lay.unit_len, lay.max_units, uplan,
-                                           useq_seg, usched, seg_len, 1, seq_order, s);
+                                           useq_seg, usched, seg_len, 1, seq_order, lay.pieces, lay.piece_len, s);
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
-                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, 0, kCpSumTail, s);
+                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, 0, kCpSumTail, 0, s);
     if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
                                   seq_order, nullptr, 0, cmb_fmt, s);
     if (e == hipSuccess)   // outputs and final states, each segment from the entering state of its first unit
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
-                             nullptr, nullptr, nullptr, useq_seg, lay.unit_len, lay.max_units, 0, narrow_out, 1, 0, s);
+                             nullptr, nullptr, nullptr, lay.pieces > 0 ? nullptr : useq_seg, lay.unit_len,
+                             lay.max_units, 0, narrow_out, 1, 0, lay.pieces, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -655,7 +701,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     hipError_t e = kda_launch_cp_plan_prep(bf16, q, k, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                                            lay.max_chunks, img, gimg, lay.seg_len, lay.max_segs, plan, seq_seg,
                                            chunk_off, sched, -1, 0, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0,
-                                           nullptr, s);
+                                           nullptr, 0, 0, s);
     bool forked = false;
     if (e == hipSuccess) {
         e = fork(0, s, s2);
@@ -671,7 +717,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (e == hipSuccess)   // s: forward summaries [S^0 | M | M^T] of every segment
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, 0, 0, s);
     if (e == hipSuccess) e = fork(1, s, s2);
     if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
@@ -685,7 +731,7 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     if (e == hipSuccess)   // s: the state at every chunk start, and every chunk's U and W
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
-                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, 0, s);
+                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, 0, 0, s);
     if (forked) {          // join: s waits for s2 (also after a failed launch)
         const hipError_t j = fork(2, s2, s);
         if (e == hipSuccess) e = j;

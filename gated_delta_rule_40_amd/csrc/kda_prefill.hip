@@ -155,6 +155,15 @@ struct PlanArgs {
     int32_t *plan, *seq_seg, *chunk_off, *sched;   // chunk_off, sched may be nullptr
     int32_t last_len, skip_last;
     int32_t *seq_order;                            // may be nullptr
+    // Pieces (pieces > 0; cp_plan_small only): the packed chunks, numbered
+    // across the sequences, are cut into pieces of piece_len chunks (0: the
+    // fewest pieces of equal length, at most `pieces`), and each sequence into
+    // its parts in those pieces, so that its segments end where pieces end
+    // (seg_len and last_len are then unused; SEG_LAST marks a sequence's last
+    // segment).  piece_first (may be nullptr): [pieces + 1], the first segment
+    // of each piece, in plan order; pieces past the last one in use are empty.
+    int32_t pieces, piece_len;
+    int32_t *piece_first;
 };
 
 struct SegArgs {
@@ -195,6 +204,10 @@ struct SegArgs {
     // first summarised from its last sum_tail chunks alone, and in full only
     // if its transition over them is not exactly zero (see the summary loop)
     int32_t sum_tail;
+    // SEG_OUTPUT: > 0 when the plan is cut into pieces (see PlanArgs): one
+    // workgroup per (piece, head) runs the piece's segments in turn, which
+    // sched [pieces + 1] (the plan's piece_first) lists
+    int32_t pieces;
 };
 
 // Inclusive scans of a (and b) over the 256 threads of a workgroup: in-wave
@@ -227,7 +240,7 @@ __device__ __forceinline__ void block_scan2_256(int64_t &a, int64_t &b, int64_t 
 // same keys (the order inside a key may differ, which no reader depends on):
 // scans by in-wave shuffles, plan entries one segment per thread (found by a
 // binary search of the segment scan in LDS), and no global read-back; five
-// barriers instead of about fifty.  lds: 6,272 bytes.
+// barriers instead of about fifty (six with pieces).  lds: 7,296 bytes.
 __device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, int32_t N, int32_t T_tot,
                                               int32_t chunk, int32_t max_chunks, const PlanArgs pa,
                                               unsigned char *lds)
@@ -239,6 +252,7 @@ __device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, in
     int32_t *st0 = reinterpret_cast<int32_t *>(sinc + 256), *st1 = st0 + 256;
     int32_t *hist = st1 + 256, *hist2 = hist + 256;                // sched and seq_order keys
     int64_t *wtot = reinterpret_cast<int64_t *>(hist2 + 256);      // [16]
+    int32_t *cst = reinterpret_cast<int32_t *>(wtot + 16);         // pieces: first chunk of each sequence
     const int t = (int)threadIdx.x;
     int32_t t0 = 0, t1 = 0;
     int64_t ns = 0, nc = 0;
@@ -248,6 +262,21 @@ __device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, in
         ns = max((int64_t)1, ((int64_t)t1 - t0 + seg_len - 1) / seg_len);
         nc = ((int64_t)t1 - t0 + chunk - 1) / chunk;
     }
+    // pieces: the piece length follows from the total chunk count, and a
+    // sequence's segment count from where its chunks fall among the pieces
+    int64_t P = 0, np_used = 1;
+    if (pa.pieces > 0) {
+        int64_t ce = nc, unused = 0;
+        block_scan2_256(ce, unused, wtot);
+        const int64_t tc = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+        P = pa.piece_len > 0 ? (int64_t)pa.piece_len : max((tc + pa.pieces - 1) / pa.pieces, (int64_t)1);
+        np_used = max((tc + P - 1) / P, (int64_t)1);
+        const int64_t c0 = ce - nc;
+        cst[t] = (int32_t)min(c0, (int64_t)INT32_MAX);
+        if (t < N) ns = nc > 0 ? (c0 + nc - 1) / P - c0 / P + 1 : 1;
+        __syncthreads();                                           // wtot is written again below
+    }
+    const int64_t slen = P > 0 ? P * chunk : (int64_t)seg_len;     // a full segment's tokens
     int64_t si = ns, ci = nc;
     block_scan2_256(si, ci, wtot);
     sinc[t] = si;
@@ -271,8 +300,8 @@ __device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, in
         seq_seg[N] = used;
         if (chunk_off) chunk_off[N] = (int32_t)min(wtot[8], (int64_t)max_chunks);
     }
-    // plan entry and dispatch key of segment gs < used
-    auto entry = [&](int gs, int32_t &n, int32_t &a, int32_t &b, int32_t &fl) {
+    // plan entry, dispatch key and piece (pieces) of segment gs < used
+    auto entry_p = [&](int gs, int32_t &n, int32_t &a, int32_t &b, int32_t &fl, int64_t &pc) {
         int lo = 0, hi = N - 1;                                    // first n with sinc[n] > gs
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
@@ -282,15 +311,30 @@ __device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, in
         const int64_t start = n > 0 ? sinc[n - 1] : 0;
         const int s = (int)(gs - start);
         const int32_t u0 = st0[n], u1 = st1[n];
+        if (P > 0) {
+            // the sequence's chunks [c0, c0 + ncn) within piece c0 / P + s
+            const int64_t c0 = cst[n], ncn = ((int64_t)u1 - u0 + chunk - 1) / chunk, p0 = c0 / P;
+            const int64_t ga = max(c0, (p0 + s) * P), gb = min(c0 + ncn, (p0 + s + 1) * P);
+            a = (int32_t)(u0 + (ga - c0) * chunk);
+            b = (int32_t)min(u0 + (gb - c0) * chunk, (int64_t)u1);
+            fl = (s == 0 ? SEG_FIRST : 0) | ((int64_t)s == sinc[n] - start - 1 ? SEG_LAST : 0);
+            pc = min(p0 + s, np_used - 1);
+            return;
+        }
         const int64_t nl = last_len > 0 ? max((int64_t)1, ((int64_t)u1 - u0 + last_len - 1) / last_len) : 1;
         a = u0 + s * seg_len;
         b = min(u0 + (s + 1) * seg_len, u1);
         fl = (s == 0 ? SEG_FIRST : 0) | (last_len > 0 && (int64_t)s * seg_len >= (nl - 1) * last_len ? SEG_LAST : 0);
+        pc = 0;
+    };
+    auto entry = [&](int gs, int32_t &n, int32_t &a, int32_t &b, int32_t &fl) {
+        int64_t pc;
+        entry_p(gs, n, a, b, fl, pc);
     };
     auto key = [&](int32_t a, int32_t b, int32_t fl) {
         int64_t len = (int64_t)b - a;
         if (skip_last && (fl & SEG_LAST)) len = 0;
-        return (int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len);
+        return (int)((slen - min(max(len, (int64_t)0), slen)) * 255 / slen);
     };
     for (int gs = t; gs < max_segs; gs += 256) {
         if (gs < used) {
@@ -307,6 +351,18 @@ __device__ __forceinline__ void cp_plan_small(const int32_t *__restrict__ cu, in
             plan[4 * gs + 2] = 0;
             plan[4 * gs + 3] = 0;
             if (sched) sched[gs] = gs;
+        }
+    }
+    if (P > 0 && pa.piece_first) {
+        // first segment of each piece: segment gs starts the pieces after its
+        // predecessor's up to its own; `used` starts those past the last one
+        const int64_t np = pa.pieces;
+        for (int gs = t; gs <= used; gs += 256) {
+            int32_t n, a, b, fl;
+            int64_t pc = np, pp = -1;
+            if (gs < used) entry_p(gs, n, a, b, fl, pc);
+            if (gs > 0) entry_p(gs - 1, n, a, b, fl, pp);
+            for (int64_t p = pp + 1; p <= min(pc, np); ++p) pa.piece_first[p] = gs;
         }
     }
     if (!sched && !seq_order) return;                              // (uniform)
@@ -1035,6 +1091,7 @@ void kda_prefill_kernel(
     constexpr bool summary = false;
     if constexpr (kPrep) {
         static_assert(!kPrep || NT == 256, "the plan and the chunk scan take 256 threads");
+        static_assert(!kPrep || P::bytes >= 7296, "cp_plan_small's LDS");
         // this launch's plan workgroups (num_seqs <= 256): the last ones, so
         // that a round of chunk workgroups that fills the GPU is not pushed
         // into a second one by them (the plans take about 4 us)
@@ -1872,7 +1929,11 @@ __device__ __forceinline__ void write_summary_frags(float *blob, int fmt, const 
 // the start of every chunk at its global index in seg.snap ([chunks][H][DK][dv],
 // see store_scaled_state), and every chunk's U = V - K+ S0 and W in seg.uw_u,
 // seg.uw_w ([chunks][H][C][dv] fp32, rows of valid tokens); out may be NULL.
-template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false, bool TAIL = false>
+// PIECES (outputs): the plan is cut into pieces, and a workgroup runs the
+// segments of its piece in turn (seg.pieces > 0); its own instantiation, so
+// that the others keep the register allocation of one segment per workgroup.
+template <typename TIn, int C, int NW, int NCT, bool SUMMARY, bool SB, bool SNAP = false, bool TAIL = false,
+          bool PIECES = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(ChainCfg<TIn, C, NW, NCT, SB, SUMMARY>::WAVES_PER_EU)))
 void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *__restrict__ cu_seqlens,
                       int32_t num_seqs, int32_t total_tokens, int32_t num_heads, int32_t dv,
@@ -1892,12 +1953,21 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
     const int xcd = wg & 7, slot = wg >> 3;
     const int vb = slot % nblk;
     const int64_t unit = (int64_t)(slot / nblk) * 8 + xcd;
-    if (unit >= (int64_t)(segmented ? seg.num_segs : num_seqs) * num_heads) return;
-    int su = (int)(unit / num_heads);
+    // pieces (outputs): this workgroup runs the segments of piece `unit / H` in turn
+    static_assert(!PIECES || (!SUMMARY && !SNAP), "pieces: outputs only");
+    constexpr bool pieces = PIECES;
+    if (unit >= (int64_t)(segmented ? (pieces ? seg.pieces : seg.num_segs) : num_seqs) * num_heads) return;
     const int h = (int)(unit % num_heads);
+    int s_first = (int)(unit / num_heads), s_end = s_first + 1;
+    if (pieces) {
+        s_end = min(max(seg.sched[s_first + 1], 0), seg.num_segs);
+        s_first = min(max(seg.sched[s_first], 0), s_end);
+    }
+    __shared__ int tail_dead[NW];                     // summaries' tail walk
+    auto run_segment = [&](int su) {
     int n = su, t_start, t_end, sflags = SEG_FIRST | SEG_LAST;
     if (segmented) {
-        if (seg.sched) su = min(max(seg.sched[su], 0), seg.num_segs - 1);
+        if (seg.sched && !pieces) su = min(max(seg.sched[su], 0), seg.num_segs - 1);
         n = seg.plan[4 * su];
         t_start = seg.plan[4 * su + 1];
         t_end = seg.plan[4 * su + 2];
@@ -1917,7 +1987,11 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
                                              (int64_t)seg.chunk_off[num_seqs] - gc0));
     const int dv0 = vb * BV;                 // summary blocks may span value and transition columns
 
-    const int tid = threadIdx.x;
+    // pieces: the thread index passes an empty asm per segment, so that nothing
+    // derived from it (state and store addresses) is hoisted out of the
+    // segment loop and held in registers through the chunk walks
+    int tid = threadIdx.x;
+    if constexpr (PIECES) __asm__ volatile("" : "+v"(tid));
     const int wave = tid >> 6, lane = tid & 63;
     const int lj = lane >> 4, lm = lane & 15;
     const int H = num_heads;
@@ -2058,7 +2132,6 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         const int nvmax = tail ? K + nch : nch;                // virtual chunks, at most
         int nv = tail ? K : nch;                               // virtual chunks to walk
         auto real = [&](int v) { return tail ? (v < K ? nch - K + v : v - K) : v; };
-        __shared__ int tail_dead[NW];
         auto run = [&](int ci) {
             if (dead) return;
             const unsigned char *base = smem + (ci & 1) * Q::BUF;
@@ -2195,6 +2268,15 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
                 for (int i = 0; i < 4; ++i)
                     final_state[sbase + (int64_t)(16 * r + 4 * lj + i) * dv + col] = S[ct][r][i] * inv;
         }
+    }
+    };
+    if constexpr (PIECES) {
+        for (int su = s_first; su < s_end; ++su) {
+            if (su > s_first) __syncthreads();        // the last segment's chunks are out of LDS
+            run_segment(su);
+        }
+    } else {
+        run_segment(s_first);
     }
 }
 
@@ -2655,16 +2737,17 @@ static hipError_t launch_chain_t(const void *v, const float *init, const int32_t
     typedef ChainCfg<TIn, C, NW, NCT, SB, true> QS;
     // the summaries' tail walk needs every transition column in one workgroup
     constexpr bool kTail = QS::BV >= 2 * DK && !SB;
-    const int kind = summary ? (kTail && seg.sum_tail > 0 ? 3 : 1) : (seg.snap ? 2 : 0);
+    const int kind = summary ? (kTail && seg.sum_tail > 0 ? 3 : 1) : (seg.snap ? 2 : (seg.pieces > 0 ? 4 : 0));
     const uint32_t bytes = summary ? QS::bytes : Q::bytes;
     auto kern = kind == 1 ? kda_chain_kernel<TIn, C, NW, NCT, true, SB>
                           : (kind == 2 ? kda_chain_kernel<TIn, C, NW, NCT, false, SB, true>
-                                       : kda_chain_kernel<TIn, C, NW, NCT, false, SB>);
+                                       : (kind == 4 ? kda_chain_kernel<TIn, C, NW, NCT, false, SB, false, false, true>
+                                                    : kda_chain_kernel<TIn, C, NW, NCT, false, SB>));
     if constexpr (kTail)
         if (kind == 3) kern = kda_chain_kernel<TIn, C, NW, NCT, true, SB, false, true>;
-    static std::atomic<uint64_t> lds_set[4];
+    static std::atomic<uint64_t> lds_set[5];
     if (hipError_t e = ensure_lds_limit(reinterpret_cast<const void *>(kern), (int)bytes, lds_set[kind])) return e;
-    const int64_t units = (int64_t)(seg.plan ? seg.num_segs : N) * H;
+    const int64_t units = (int64_t)(seg.plan ? (!summary && seg.pieces > 0 ? seg.pieces : seg.num_segs) : N) * H;
     const int nblk = (summary ? dv + DK : dv) / Q::BV;
     const int64_t grid = (units + 7) / 8 * 8 * nblk;
     if (grid <= 0) return hipSuccess;
@@ -2982,10 +3065,15 @@ extern "C" hipError_t kda_launch_cp_plan_prep(int bf16, const void *q, const voi
                                               int32_t skip_last, int32_t *seq_order, int32_t seg_len2,
                                               int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
                                               int32_t *sched2, int32_t last_len2, int32_t skip_last2,
-                                              int32_t *seq_order2, hipStream_t stream)
+                                              int32_t *seq_order2, int32_t pieces, int32_t piece_len,
+                                              hipStream_t stream)
 {
     using namespace kda;
     if (!chunk_off || max_chunks < 1 || max_chunks > 0x7fffffff) return hipErrorInvalidValue;
+    // pieces (both plans cut alike; the first plan's sched becomes its
+    // piece_first table of pieces + 1 entries): built by cp_plan_small only
+    if (pieces < 0 || piece_len < 0 || (pieces > 0 && (N < 1 || N > 256 || !sched || pieces >= max_segs)))
+        return hipErrorInvalidValue;
     if (N < 1 || N > 256) {
         hipError_t e = kda_launch_cp_plan(cu, N, T_tot, seg_len, max_segs, plan, seq_seg, 32, (int32_t)max_chunks,
                                           chunk_off, sched, last_len, skip_last, seq_order, seg_len2, max_segs2,
@@ -3003,6 +3091,14 @@ extern "C" hipError_t kda_launch_cp_plan_prep(int bf16, const void *q, const voi
                        &seg.pl[1]))
             return hipErrorInvalidValue;
         seg.plan_wgs = 2;
+    }
+    if (pieces > 0) {
+        for (int i = 0; i < 2; ++i) {
+            seg.pl[i].pieces = pieces;
+            seg.pl[i].piece_len = piece_len;
+        }
+        seg.pl[0].piece_first = sched;
+        seg.pl[0].sched = nullptr;
     }
     if (bf16) return launch_prep_t<bf16_t, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
     return launch_prep_t<float, 32>(q, k, g, beta, cu, N, T_tot, H, max_chunks, seg, stream);
@@ -3044,9 +3140,10 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
                                        int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
-                                       int32_t sum_tail, hipStream_t stream)
+                                       int32_t sum_tail, int32_t pieces, hipStream_t stream)
 {
     using namespace kda;
+    if (pieces < 0 || (pieces > 0 && (mode != SEG_OUTPUT || !plan || !sched || snap))) return hipErrorInvalidValue;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
     if (sum_tail < 0 || (sum_tail & 1) || (sum_tail && mode != SEG_SUMMARY)) return hipErrorInvalidValue;
     // the fragment layouts: bf16 summaries in 256-column blocks (128 when
@@ -3062,6 +3159,7 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                    init_units, 0, 0, nullptr, snap_scale, uw_u, uw_w, cmb_fmt};
     seg.init_tiles = init_tiles;
     seg.sum_tail = sum_tail;
+    seg.pieces = pieces;
     if (init_tiles && (mode != SEG_OUTPUT || dv != DK || !plan)) return hipErrorInvalidValue;
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,

@@ -185,8 +185,23 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  * fp32 rounding, and M is zero; otherwise the whole segment is run.  This holds for
  * any inputs: the test is made on the computed transition, not assumed.
  *
- *   seg_len    tokens per segment, a positive multiple of 32; 0 = automatic
- *              (total_tokens * num_heads / 256, clamped to [256, 32768])
+ *   seg_len    > 0: tokens per segment, a multiple of 32, counted from each
+ *              sequence's start.
+ *              < 0: pieces of -seg_len tokens (a multiple of 32; at most 256
+ *              sequences, else KDA_ERR_UNSUPPORTED).  The 32-token chunks of
+ *              all sequences, numbered in packed order, are cut into pieces
+ *              of -seg_len / 32 chunks, and every sequence into its parts in
+ *              those pieces: a segment ends where a piece or its sequence
+ *              ends.  One workgroup per (piece, head) runs its piece's
+ *              segments in turn, so every output walk covers the same number
+ *              of chunks however the sequence lengths fall.  Zero-state runs
+ *              and chaining then use these segments as their units.
+ *              0 = automatic: for bf16 inputs, at most 256 sequences and
+ *              total_tokens * num_heads / 256 above 32,768, equal pieces,
+ *              max(1, 512 / num_heads) per head (two workgroups per compute
+ *              unit), each of ceil(chunks / pieces) chunks; otherwise
+ *              segments of total_tokens * num_heads / 256 tokens, clamped to
+ *              [256, 32768] and rounded up to a multiple of 32.
  *   workspace  device memory of at least kda_prefill_cp_workspace_size(...)
  *              bytes, 256-byte aligned, owned by the caller, contents
  *              ignored on entry; calls that share one workspace must not

@@ -8,7 +8,8 @@ segments for the outputs.  The oracle knows nothing of segments: it runs the
 token recurrence straight through, so these tests check the whole scheme.
 Comparisons use the rule of tests/kda_parity.py (tol * RMS + half an ulp of
 the stored dtype).  Small seg_len values force many segments per sequence,
-one-chunk segments and ragged last segments.
+one-chunk segments and ragged last segments; negative seg_len values cut the
+packed chunk order into pieces that span sequence boundaries.
 """
 import numpy as np
 import pytest
@@ -52,6 +53,41 @@ def test_cp_ragged_vs_oracle(dtype, seg_len):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("seg_len", [-32, -64, -96, -160])
+def test_cp_pieces_ragged_vs_oracle(dtype, seg_len):
+    # pieces (negative seg_len): the packed chunk order is cut into pieces of
+    # -seg_len / 32 chunks and each sequence into its parts in them, so a
+    # workgroup's piece holds the end of one sequence, whole short ones,
+    # empty ones and the start of the next, and runs them in turn
+    inp = to_dev(I.random_prefill(LENGTHS, H=3, dtype=dtype, seed=30))
+    _check_cp(inp, TOL[dtype], "cp_pieces", seg_len)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_cp_pieces_null_initial_state(dtype):
+    inp = to_dev(I.random_prefill([250, 0, 77, 5], H=2, dtype=dtype, seed=31))
+    _check_cp(inp, TOL[dtype], "cp_pieces_null_init", -64, use_init=False)
+
+
+@pytest.mark.parametrize("g_lo", [-5.0 / 16.0, -0.002])
+def test_cp_pieces_tail_vs_oracle(g_lo):
+    # pieces of 48 chunks with 32 heads: more (segment, head) pairs than
+    # compute units, so the summaries run in the 256-column form and walk a
+    # segment's last 36 chunks first (in full again when the transition over
+    # them is not exactly zero, g in (-0.002, 0]), and the outputs run in
+    # two-tile workgroups, one per (piece, head)
+    inp = to_dev(I.random_prefill([4000, 100, 6000, 3333, 3067], H=32, dtype=torch.bfloat16, seed=44, g_lo=g_lo))
+    _check_cp(inp, TOL[torch.bfloat16], "cp_pieces_tail_g_lo=%g" % g_lo, -1536)
+
+
+def test_cp_pieces_run_to_run_bitwise_determinism():
+    inp = to_dev(I.random_prefill([333, 640, 17, 0, 2000], H=4, dtype=torch.bfloat16, seed=45))
+    o1, f1 = run_prefill_cp(inp, seg_len=-256)
+    o2, f2 = run_prefill_cp(inp, seg_len=-256)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_cp_null_initial_state(dtype):
     inp = to_dev(I.random_prefill([250, 0, 77], H=2, dtype=dtype, seed=31))
     _check_cp(inp, TOL[dtype], "cp_null_init", 64, use_init=False)
@@ -88,7 +124,7 @@ def test_cp_single_segment_equals_plain_prefill_bitwise():
 def test_cp_equals_plain_prefill_within_tolerance():
     inp = to_dev(I.random_prefill([1000, 517, 3], H=4, dtype=torch.bfloat16, seed=34))
     o_ref, f_ref = run_prefill(inp)
-    for seg_len in (32, 128, 0):
+    for seg_len in (32, 128, 0, -64, -1024):
         o, f = run_prefill_cp(inp, seg_len=seg_len)
         assert_close(host(o), host(o_ref), 2 * TOL[torch.bfloat16], "cp(%d) vs plain out" % seg_len,
                      torch.bfloat16, ulps=1.0)
