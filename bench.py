@@ -59,7 +59,7 @@ BWD_FLOP_PER_HT = 16 * DK * DV
 PREFILL_KERNELS = {
     "cp": "kda_prefill_cp call: kda_prefill_kernel<bf16,32,4,MODE_PREP> (chunk operands; with at most 256 sequences its last two workgroups build the two plans, else kda_cp_plan_kernel runs first), "
           "kda_chain_kernel<bf16,32,8 waves,2 tiles,summary> (a segment's last 36 chunks when its transition over them is zero), kda_cp_combine_kernel, "
-          "kda_chain_kernel<bf16,32,4 waves,2 tiles,output,single buffer>",
+          "kda_chain_kernel<bf16,32,4 waves,2 tiles,output,single buffer,pieces> (one workgroup per (piece, head))",
     "plain": "kda_prefill call: kda_prefill_kernel<bf16,32,4,MODE_FUSED>",
 }
 PREFILL_SRC = os.path.join(ROOT, "gated_delta_rule_40_amd", "csrc", "kda_prefill.hip")
