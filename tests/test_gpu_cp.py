@@ -80,6 +80,17 @@ def test_cp_pieces_tail_vs_oracle(g_lo):
     _check_cp(inp, TOL[torch.bfloat16], "cp_pieces_tail_g_lo=%g" % g_lo, -1536)
 
 
+@pytest.mark.parametrize("lengths,seg_len", [
+    ([64, 64, 0, 128, 0], -64),         # piece ends on sequence ends; empty sequences between and last
+    ([64, 64, 0, 128, 0], -99968),      # one piece holds every sequence: one workgroup per head walks them all
+    ([0, 0, 31, 0], -32),               # a single ragged chunk among empty sequences
+    ([700, 1, 1, 1, 900], -96),         # one-token sequences sharing a piece with the ends of long ones
+])
+def test_cp_pieces_edges_vs_oracle(lengths, seg_len):
+    inp = to_dev(I.random_prefill(lengths, H=2, dtype=torch.bfloat16, seed=46))
+    _check_cp(inp, TOL[torch.bfloat16], "cp_pieces_edges", seg_len)
+
+
 def test_cp_pieces_run_to_run_bitwise_determinism():
     inp = to_dev(I.random_prefill([333, 640, 17, 0, 2000], H=4, dtype=torch.bfloat16, seed=45))
     o1, f1 = run_prefill_cp(inp, seg_len=-256)
