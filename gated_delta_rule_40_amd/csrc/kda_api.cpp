@@ -37,14 +37,15 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
                                        int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
-                                       int32_t sum_tail, int32_t pieces, hipStream_t stream);
+                                       int32_t sum_tail, int32_t pieces, int32_t *head_dead, int32_t sum_head,
+                                       hipStream_t stream);
 extern "C" size_t kda_chunk_image_bytes(int bf16);
 extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *dout, const int32_t *cu, int32_t N,
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
                                             const float *g_end, void *g_chunk, float *g_scale, float *dinit,
                                             float *g0_out, float *dx_chunk, int32_t tiles,
-                                            hipStream_t stream);
+                                            const int32_t *head_dead, int32_t sum_head, hipStream_t stream);
 extern "C" hipError_t kda_launch_bwd_chunk(int bf16, const void *q, const void *k, const float *g,
                                            const float *beta, const void *dout, const int32_t *cu,
                                            const int32_t *chunk_off, int64_t max_chunks, const void *snaps,
@@ -425,7 +426,8 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
     if (e == hipSuccess)   // unit summaries (units before a sequence's last segment)
         e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              nullptr, uplan, lay.max_units, 1, nullptr, seg_out, chunk_off, img, usched, nullptr,
-                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, 0, kCpSumTail, 0, s);
+                             nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, narrow_sum, 0, kCpSumTail, 0, nullptr,
+                             0, s);
     if (e == hipSuccess)   // entering state of every unit up to the start of a sequence's last segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, useq_seg, seg_out, seg_init, 0, uplan,
                                   seq_order, nullptr, 0, cmb_fmt, s);
@@ -433,7 +435,7 @@ kda_status cp_launch(const void *q, const void *k, const void *v, const float *g
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv, out,
                              final_state, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched, nullptr,
                              nullptr, nullptr, nullptr, lay.pieces > 0 ? nullptr : useq_seg, lay.unit_len,
-                             lay.max_units, 0, narrow_out, 1, 0, lay.pieces, s);
+                             lay.max_units, 0, narrow_out, 1, 0, lay.pieces, nullptr, 0, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
@@ -523,7 +525,7 @@ namespace {
 
 struct BwdLayout {
     size_t plan, sched, seq_seg, chunk_off, img, gimg, snaps, gchunk, sscale, gscale, uw_u, uw_w, dx, fsum, bsum,
-        seg_init, seg_dsend, total;
+        seg_init, seg_dsend, hflag, total;
     int32_t max_chunks, max_segs, seg_len;
 };
 
@@ -578,7 +580,8 @@ bool bwd_layout(int32_t N, int32_t T, int32_t H, int bf16, BwdLayout *lay)
     lay->bsum = align256(lay->fsum + sizeof(float) * (size_t)segs * H * 3 * S);
     lay->seg_init = align256(lay->bsum + sizeof(float) * (size_t)segs * H * S);
     lay->seg_dsend = align256(lay->seg_init + sizeof(float) * (size_t)segs * H * S);
-    lay->total = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
+    lay->hflag = align256(lay->seg_dsend + sizeof(float) * (size_t)segs * H * S);
+    lay->total = align256(lay->hflag + sizeof(int32_t) * (size_t)segs * H);
     return true;
 }
 
@@ -684,7 +687,9 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
     //   s:  forward summaries -> forward combine -> forward states at chunk starts
     //   s2: gradient summaries -> (forward summaries done) reverse combine ->
     //       state gradients at chunk ends
-    // then, on s once both are done, the per-chunk gradients.
+    // (with the head walk below, both summary passes run on s first and s2
+    // starts at the reverse combine); then, on s once both strands are done,
+    // the per-chunk gradients.
     SideStream *ss = side_stream();
     std::unique_lock<std::mutex> lk;
     if (ss) lk = std::unique_lock<std::mutex>(ss->use);
@@ -702,36 +707,62 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const float
                                            lay.max_chunks, img, gimg, lay.seg_len, lay.max_segs, plan, seq_seg,
                                            chunk_off, sched, -1, 0, nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0,
                                            nullptr, 0, 0, s);
-    bool forked = false;
-    if (e == hipSuccess) {
-        e = fork(0, s, s2);
-        forked = e == hipSuccess;
-    }
     // summaries in the combine's operand order, with M^T for the reverse
     // walk; summaries of gradients, entering states and entering gradients as
     // accumulator tiles (see kda_prefill.hip, CMB_ROWS)
     const int32_t cmb_fmt = (bf16 ? 2 : 1) | 4;
-    if (e == hipSuccess)   // s2: gradient summaries G^0 of every segment but a sequence's first
-        e = kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum, nullptr, 1, s2);
-    if (e == hipSuccess)   // s: forward summaries [S^0 | M | M^T] of every segment
-        e = kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
-                             nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, 0, 0, s);
-    if (e == hipSuccess) e = fork(1, s, s2);
+    // Head walk (16-bit inputs, segments of more than kCpSumTail chunks): the
+    // forward summaries flag every segment whose transition over its first
+    // kCpSumTail chunks is exactly zero, and the gradient summaries of those
+    // segments walk only those chunks.  The gradient summaries then follow the
+    // forward summaries on the caller's stream, ahead of the state pass, which
+    // would otherwise hold the compute units they wait for; without the head
+    // walk the two summary passes run side by side.
+    const bool head = bf16 && lay.seg_len / kCpChunk > kCpSumTail;
+    int32_t *hflag = head ? reinterpret_cast<int32_t *>(ws + lay.hflag) : nullptr;
+    const int32_t sum_head = head ? kCpSumTail : 0;
+    auto fwd_summaries = [&](hipStream_t st) {   // forward summaries [S^0 | M | M^T] of every segment
+        return kda_launch_chain(bf16, kCpSumBlock, v, nullptr, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
+                                nullptr, nullptr, plan, lay.max_segs, 1, nullptr, fsum, chunk_off, img, sched,
+                                nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, cmb_fmt, 0, 0, 0, 0, hflag,
+                                sum_head, st);
+    };
+    auto grad_summaries = [&](hipStream_t st) {  // gradient summaries G^0 of every segment but a sequence's first
+        return kda_launch_grad_chain(bf16, 1, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan,
+                                     lay.max_segs, sched, chunk_off, gimg, nullptr, nullptr, nullptr, nullptr, bsum,
+                                     nullptr, 1, hflag, sum_head, st);
+    };
+    bool forked = false;
+    if (head) {
+        if (e == hipSuccess) e = fwd_summaries(s);
+        if (e == hipSuccess) e = grad_summaries(s);
+        if (e == hipSuccess) {
+            e = fork(0, s, s2);
+            forked = e == hipSuccess;
+        }
+    } else {
+        if (e == hipSuccess) {
+            e = fork(0, s, s2);
+            forked = e == hipSuccess;
+        }
+        if (e == hipSuccess) e = grad_summaries(s2);
+        if (e == hipSuccess) e = fwd_summaries(s);
+        if (e == hipSuccess) e = fork(1, s, s2);
+    }
     if (e == hipSuccess)   // s2: the gradient entering every segment at its end, with R_s = M_s^T
         e = kda_launch_cp_combine(dfinal, num_seqs, num_heads, dv, seq_seg, bsum, seg_dsend, 1, nullptr, nullptr,
                                   fsum, 1, cmb_fmt, s2);
     if (e == hipSuccess)   // s2: the gradient at every chunk end, every chunk's dX, and d(initial state)
         e = kda_launch_grad_chain(bf16, 0, dout, cu_seqlens, num_seqs, total_tokens, num_heads, plan, lay.max_segs,
-                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, dxc, 1, s2);
+                                  sched, chunk_off, gimg, seg_dsend, gchunk, gscale, dinit, nullptr, dxc, 1, nullptr,
+                                  0, s2);
     if (e == hipSuccess)   // s: the state entering every segment
         e = kda_launch_cp_combine(initial_state, num_seqs, num_heads, dv, seq_seg, fsum, seg_init, 0, nullptr,
                                   nullptr, nullptr, 0, cmb_fmt, s);
     if (e == hipSuccess)   // s: the state at every chunk start, and every chunk's U and W
         e = kda_launch_chain(bf16, kCpBlock, v, initial_state, cu_seqlens, num_seqs, total_tokens, num_heads, dv,
                              nullptr, nullptr, plan, lay.max_segs, 0, seg_init, nullptr, chunk_off, img, sched,
-                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, 0, 0, s);
+                             snaps, sscale, uw_u, uw_w, nullptr, 0, 0, 0, 0, 1, 0, 0, nullptr, 0, s);
     if (forked) {          // join: s waits for s2 (also after a failed launch)
         const hipError_t j = fork(2, s2, s);
         if (e == hipSuccess) e = j;

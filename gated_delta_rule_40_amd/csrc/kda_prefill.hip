@@ -208,6 +208,12 @@ struct SegArgs {
     // workgroup per (piece, head) runs the piece's segments in turn, which
     // sched [pieces + 1] (the plan's piece_first) lists
     int32_t pieces;
+    // SEG_SUMMARY without the tail walk (may be nullptr): head_dead[unit * H
+    // + h] = 1 when the unit has more than sum_head chunks (even, > 0) and its
+    // transition over its first sum_head chunks is exactly zero, else 0;
+    // written by the workgroup that holds every transition column
+    int32_t *head_dead;
+    int32_t sum_head;
 };
 
 // Inclusive scans of a (and b) over the 256 threads of a workgroup: in-wave
@@ -2127,6 +2133,12 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
         // chunk v - K after a reset; the loop has one exit, so the waits for
         // the prefetched operands stay exact.  (TAIL instantiations only: the
         // others compile without the tail's registers and branches.)
+        // Head flag: whether the transition over the unit's first KH chunks
+        // is exactly zero (the state-gradient chain then needs only those
+        // chunks of the unit for its own summary, see kda_grad_chain_kernel)
+        const int KH = !TAIL && seg.head_dead ? seg.sum_head : 0;
+        const bool head_wg = KH > 0 && dv0 <= dv && dv0 + BV >= dv + DK;   // holds every transition column
+        if (head_wg && tid == 0) seg.head_dead[(int64_t)su * num_heads + h] = 0;
         const int K = TAIL ? seg.sum_tail : 0;
         const bool tail = TAIL && K > 0 && (K & 1) == 0 && nch > K && dv0 == 0 && BV >= dv + DK;   // block-uniform
         const int nvmax = tail ? K + nch : nch;                // virtual chunks, at most
@@ -2165,6 +2177,14 @@ void kda_chain_kernel(const TIn *v, const float *initial_state, const int32_t *_
             asm volatile("" ::: "memory");
             run(ci + 1);
             stage_from(real(min(ci + 2, nvmax - 1)), ci & 1, ri2, rv2);
+            if (head_wg && ci + 2 == KH && nch > KH) {         // after the first KH chunks (block-uniform)
+                if (lane == 0) tail_dead[wave] = !trans_wave || dead;
+                __syncthreads();
+                bool all_dead = true;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) all_dead = all_dead && tail_dead[w] != 0;
+                if (all_dead && tid == 0) seg.head_dead[(int64_t)su * num_heads + h] = 1;
+            }
             if (tail && ci + 2 == K && nv == K) {              // end of the tail walk (block-uniform)
                 if (lane == 0) tail_dead[wave] = !trans_wave || dead;
                 __syncthreads();
@@ -2534,7 +2554,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const TIn *dout, const int32_t *__restrict__ cu_seqlens, int32_t num_seqs, int32_t total_tokens,
     int32_t num_heads, const int32_t *__restrict__ plan, int32_t num_segs, const int32_t *__restrict__ sched,
     const int32_t *__restrict__ chunk_off, const f32x4 *gimg, const float *g_end, void *g_chunk,
-    float *g_scale, float *dinit, float *g0_out, float *dx_chunk, int32_t tiles)
+    float *g_scale, float *dinit, float *g0_out, float *dx_chunk, int32_t tiles,
+    const int32_t *__restrict__ head_dead, int32_t sum_head)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     typedef typename Q::OpT OpT;
@@ -2557,8 +2578,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int t_start = min(max(plan[4 * su + 1], 0), total_tokens);
     const int t_end = min(max(plan[4 * su + 2], t_start), total_tokens);
     const int64_t gc0 = chunk_off[n] + (t_start - seq_start) / C;
-    const int nch = (int)max((int64_t)0, min((int64_t)(t_end - t_start + C - 1) / C,
-                                             (int64_t)chunk_off[num_seqs] - gc0));
+    int nch = (int)max((int64_t)0, min((int64_t)(t_end - t_start + C - 1) / C,
+                                       (int64_t)chunk_off[num_seqs] - gc0));
+    // Summaries, head walk: G^0 sums every chunk's contribution carried to the
+    // segment's start through the transposed transitions of the chunks before
+    // it.  When the forward transition over the first sum_head chunks is
+    // exactly zero (head_dead, from the forward summaries), nothing from a
+    // later chunk reaches the start above the smallest fp32 subnormal, and the
+    // walk from a zero gradient at chunk sum_head gives G^0 up to fp32 rounding.
+    if (SUMMARY && head_dead && sum_head > 0 && nch > sum_head && head_dead[(int64_t)su * num_heads + h] != 0)
+        nch = sum_head;
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int lj = lane >> 4, lm = lane & 15;
@@ -2683,7 +2712,8 @@ static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int3
                                       int32_t H, const int32_t *plan, int32_t num_segs, const int32_t *sched,
                                       const int32_t *chunk_off, const void *gimg, const float *g_end, void *g_chunk,
                                       float *g_scale, float *dinit, float *g0_out, float *dx_chunk,
-                                      int32_t tiles, hipStream_t stream)
+                                      int32_t tiles, const int32_t *head_dead, int32_t sum_head,
+                                      hipStream_t stream)
 {
     typedef GChainCfg<TIn, C, NW, NCT, SB> Q;
     auto kern = summary ? kda_grad_chain_kernel<TIn, C, NW, NCT, true, SB>
@@ -2696,7 +2726,7 @@ static hipError_t launch_grad_chain_t(bool summary, const void *dout, const int3
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Q::NT), Q::bytes, stream, static_cast<const TIn *>(dout), cu,
                        N, T_tot, H, plan, num_segs, sched, chunk_off, static_cast<const f32x4 *>(gimg), g_end,
-                       g_chunk, g_scale, dinit, g0_out, dx_chunk, tiles);
+                       g_chunk, g_scale, dinit, g0_out, dx_chunk, tiles, head_dead, sum_head);
     return hipGetLastError();
 }
 
@@ -3140,9 +3170,11 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
                                        const int32_t *sched, void *snap, float *snap_scale, float *uw_u,
                                        float *uw_w, const int32_t *init_seq_seg, int32_t init_unit,
                                        int32_t init_units, int32_t cmb_fmt, int32_t narrow, int32_t init_tiles,
-                                       int32_t sum_tail, int32_t pieces, hipStream_t stream)
+                                       int32_t sum_tail, int32_t pieces, int32_t *head_dead, int32_t sum_head,
+                                       hipStream_t stream)
 {
     using namespace kda;
+    if (head_dead && (mode != SEG_SUMMARY || sum_tail || sum_head <= 0 || (sum_head & 1))) return hipErrorInvalidValue;
     if (pieces < 0 || (pieces > 0 && (mode != SEG_OUTPUT || !plan || !sched || snap))) return hipErrorInvalidValue;
     if (init_seq_seg && (init_unit <= 0 || init_units <= 0)) return hipErrorInvalidValue;
     if (sum_tail < 0 || (sum_tail & 1) || (sum_tail && mode != SEG_SUMMARY)) return hipErrorInvalidValue;
@@ -3160,6 +3192,8 @@ extern "C" hipError_t kda_launch_chain(int bf16, int dv_block, const void *v, co
     seg.init_tiles = init_tiles;
     seg.sum_tail = sum_tail;
     seg.pieces = pieces;
+    seg.head_dead = head_dead;
+    seg.sum_head = sum_head;
     if (init_tiles && (mode != SEG_OUTPUT || dv != DK || !plan)) return hipErrorInvalidValue;
     // bf16: 256 columns (segment summaries) as 8 waves x 2 tiles, double
     // buffered; 128 columns (outputs) as 4 waves x 2 tiles, single buffered,
@@ -3191,18 +3225,20 @@ extern "C" hipError_t kda_launch_grad_chain(int bf16, int summary, const void *d
                                             int32_t T_tot, int32_t H, const int32_t *plan, int32_t num_segs,
                                             const int32_t *sched, const int32_t *chunk_off, const void *gimg,
                                             const float *g_end, void *g_chunk, float *g_scale, float *dinit,
-                                            float *g0_out, float *dx_chunk, int32_t tiles, hipStream_t stream)
+                                            float *g0_out, float *dx_chunk, int32_t tiles,
+                                            const int32_t *head_dead, int32_t sum_head, hipStream_t stream)
 {
     using namespace kda;
     if (summary ? !g0_out : (!g_end || !g_chunk || (bf16 && !g_scale) || !dx_chunk)) return hipErrorInvalidValue;
+    if (sum_head < 0 || (sum_head & 1) || (head_dead && !summary)) return hipErrorInvalidValue;
     // bf16: double buffered (about 87 KB); fp32 images are twice as large: one buffer
     if (bf16)
         return launch_grad_chain_t<bf16_t, 32, 4, 2, false>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs,
                                                             sched, chunk_off, gimg, g_end, g_chunk, g_scale, dinit,
-                                                            g0_out, dx_chunk, tiles, stream);
+                                                            g0_out, dx_chunk, tiles, head_dead, sum_head, stream);
     return launch_grad_chain_t<float, 32, 4, 2, true>(summary != 0, dout, cu, N, T_tot, H, plan, num_segs, sched,
                                                       chunk_off, gimg, g_end, g_chunk, g_scale, dinit, g0_out,
-                                                      dx_chunk, tiles, stream);
+                                                      dx_chunk, tiles, head_dead, sum_head, stream);
 }
 
 extern "C" size_t kda_chunk_image_bytes(int bf16)

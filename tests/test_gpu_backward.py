@@ -78,6 +78,18 @@ def test_backward_several_segments_per_sequence(dtype):
     _check(_case([700, 300, 1100], H=2, dtype=dtype, seed=65), dtype, "multi_segment")
 
 
+@pytest.mark.parametrize("g_lo", [-5.0 / 16.0, -0.002])
+def test_backward_head_walk_vs_oracle(g_lo):
+    # 8,500 tokens x 64 heads make the segments 2,144 tokens long (67 chunks,
+    # more than the 36 of the head walk), and the 6,000-token sequence has two
+    # segments after its first (67 and 54 chunks): under the workloads' decay
+    # the forward transition over a segment's first 36 chunks is exactly zero
+    # and its gradient summary walks only those; with g in (-0.002, 0] it is
+    # not, and the gradient summaries walk every chunk
+    _check(_case([6000, 2500], H=64, dtype=torch.bfloat16, seed=67, g_lo=g_lo), torch.bfloat16,
+           "head_walk_g_lo=%g" % g_lo)
+
+
 @pytest.mark.parametrize("nseq", [256, 300])
 def test_backward_many_sequences(nseq):
     # 256 sequences: the plan is built inside the chunk-operand launch; 300:

@@ -40,7 +40,9 @@ def _noalloc(inp, seg_len=0):
 def test_noalloc_equals_workspace_entry_two_calls(dtype):
     big = to_dev(I.random_prefill([1500, 37, 700, 0, 1100], H=4, dtype=dtype, seed=60))
     small = to_dev(I.random_prefill([90, 300], H=2, dtype=dtype, seed=61))
-    for label, inp, seg_len in (("first (larger)", big, 0), ("second (smaller)", small, 64)):
+    pieces = to_dev(I.random_prefill([50, 400, 3, 0], H=2, dtype=dtype, seed=62))
+    for label, inp, seg_len in (("first (larger)", big, 0), ("second (smaller)", small, 64),
+                                ("third (pieces of 96 tokens)", pieces, -96)):
         log("[noalloc] %s call, T=%d H=%d seg_len=%d dtype=%s" % (label, inp["q"].shape[0], inp["q"].shape[1],
                                                                   seg_len, dtype))
         need = K.kda_prefill_cp_workspace_size(inp["cu_seqlens"].shape[0] - 1, inp["q"].shape[0],
