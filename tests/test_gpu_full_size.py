@@ -1,8 +1,9 @@
 """Parity at full size on every output: the 4 x 16,384-token x 32-head and the
 1,048,576-token x 16-head prefill workloads (every (sequence, head) unit, for
 kda_prefill and for kda_prefill_cp at its automatic segment length, which is
-what bench.py times), and the 512 x 32 decode workload (every unit, all 64
-in-place steps).
+what bench.py times), the 512 x 32 decode workload (every unit, all 64
+in-place steps), and the backward on the two workloads bench.py times it on
+(every unit of both).
 
 The result being checked is the recurrence of card "KDA 单头递归" (page
 ailearn.mscapital.top/kimi-k3.html), computed by the fp64 oracle on host
@@ -109,3 +110,53 @@ def test_decode_512x32_64_steps_every_unit():
         cmp_S.add(host(S[n0:n1]), S_ref)
     cmp_out.check()
     cmp_S.check()
+
+
+def _backward_vs_oracle(wl_name, head_group, threads):
+    """kda_backward on the whole workload, as bench.py times it (dout ~ N(0, 1)
+    in bf16 from a generator seeded with 7 on the device, no final-state
+    gradient), against the fp64 oracle backward on every unit, head_group
+    heads at a time (the oracle keeps every state of a unit in host memory,
+    so each group runs with few threads)."""
+    wl = I.WORKLOADS[wl_name]
+    inp = I.make_prefill(wl, device="cuda")
+    T, H = inp["q"].shape[0], inp["q"].shape[1]
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn(T, H, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    log("[%s backward] T=%d H=%d lengths=%s, oracle %d heads at a time with %d threads" %
+        (wl_name, T, H, inp["lengths"], head_group, threads))
+    gr = K.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                        inp["cu_seqlens"], dout, None)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    keys = ("dq", "dk", "dv", "dg", "dbeta", "dinit")
+    cmp = {key: StreamingCompare("%s backward %s" % (wl_name, key), tol) for key in keys}
+    init = inp["initial_state"]
+    for h0 in range(0, H, head_group):
+        h1 = min(H, h0 + head_group)
+        sel = lambda x: x[:, h0:h1].contiguous()
+        ref = O.backward(host(sel(inp["q"])), host(sel(inp["k"])), host(sel(inp["v"])), host(sel(inp["g"])),
+                         host(sel(inp["beta"])), None if init is None else sel(init).double().cpu().numpy(),
+                         inp["cu_seqlens"].cpu().numpy(), sel(dout).double().cpu().numpy(), None,
+                         num_threads=threads)
+        for key in keys:
+            got = sel(gr[key]).cpu().numpy()
+            for t0 in range(0, got.shape[0], TOK_BLOCK):
+                cmp[key].add(got[t0:t0 + TOK_BLOCK], ref[key][t0:t0 + TOK_BLOCK])
+        del ref
+    for key in keys:
+        cmp[key].check()
+
+
+@pytest.mark.timeout(600)
+def test_backward_t4096_h8_every_unit():
+    """kda_backward on the 4,096-token x 8-head workload: every gradient of every unit."""
+    _backward_vs_oracle("prefill_t4096_h8", 8, min(oracle_threads(), 8))
+
+
+@pytest.mark.timeout(900)
+def test_backward_4x16384_h32_every_unit():
+    """kda_backward on 4 x 16,384 tokens x 32 heads (segments of 256 chunks, the
+    gradient summaries' head walk): every gradient of all 128 units, four
+    heads at a time."""
+    _backward_vs_oracle("prefill_4x16384_h32", 4, min(oracle_threads(), 4))
