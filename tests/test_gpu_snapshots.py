@@ -105,3 +105,25 @@ def test_restore_snapshot_then_continue_to_any_token_boundary(dtype):
         ref_out, ref_fin = oracle_prefill(_prefix(inp, 0, boundary))
         assert_close(host(tail_out), ref_out[start:boundary], TOL[dtype], "restored tail out @%d" % boundary, dtype)
         assert_close(host(state), ref_fin, TOL[dtype], "restored state @%d" % boundary)
+
+
+def test_snapshots_t4096_h8_every_512_vs_oracle():
+    """The configuration bench.py times: the 4,096-token x 8-head workload with
+    a snapshot every 512 tokens (8 per head), every output, the final state
+    and every snapshot against the oracle on the same prefix."""
+    inp = I.make_prefill(I.WORKLOADS["prefill_t4096_h8"], device="cuda")
+    T, H = inp["q"].shape[0], inp["q"].shape[1]
+    every = 512
+    out = torch.empty(T, H, 128, dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty(1, H, 128, 128, device="cuda")
+    snaps = torch.full((1, T // every, H, 128, 128), float("nan"), device="cuda")
+    K.kda_prefill_snapshots(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"],
+                            inp["cu_seqlens"], out, fin, snaps, every)
+    torch.cuda.synchronize()
+    tol = TOL[torch.bfloat16]
+    ref_out, ref_fin = oracle_prefill(inp)
+    assert_close(host(out), ref_out, tol, "t4096_h8 snapshots out", torch.bfloat16)
+    assert_close(host(fin), ref_fin, tol, "t4096_h8 snapshots final_state")
+    for j in range(T // every):
+        _, ref = oracle_prefill(_prefix(inp, 0, (j + 1) * every))
+        assert_close(host(snaps[0, j]), ref[0], tol, "t4096_h8 snapshot after %d tokens" % ((j + 1) * every))
