@@ -1702,11 +1702,17 @@ void kda_prefill_kernel(
             if (seg.chunk_off || j < seg.max_snaps) {
                 float *dst = seg.snap + ((seg.chunk_off ? (int64_t)j : (int64_t)n * seg.max_snaps + j) * num_heads + h) *
                                             DK * dv;
+                // this lane's first element, through an empty asm: its
+                // per-lane offsets are then formed here, not hoisted out of
+                // the chunk loop and held in registers through it
+                int lane_off = 4 * lj * dv + col;
+                __asm__ volatile("" : "+v"(lane_off));
+                float *dl = dst + lane_off;
+                const float inv = pow2_inv(sS);
 #pragma unroll
                 for (int r = 0; r < DK / 16; ++r)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        dst[(int64_t)(16 * r + 4 * lj + i) * dv + col] = S[r][i] * pow2_inv(sS);
+                    for (int i = 0; i < 4; ++i) dl[(int64_t)(16 * r + i) * dv] = S[r][i] * inv;
             }
         }
     }
