@@ -148,6 +148,25 @@ def test_cp_workspace_size(lib):
     assert ws(3, 4096, 1, 128, 128, B, -1024) > 0              # pieces of 1,024 tokens
     assert ws(3, 4096, 1, 128, 128, B, -48) == 0
     assert ws(257, 4096, 1, 128, 128, B, -1024) == 0           # pieces: at most 256 sequences
+
+
+def test_cp_automatic_cut(lib):
+    # The automatic cut of a long bf16 batch (T H / 256 above 32,768 tokens,
+    # at most 256 sequences) is 512 / H pieces per head: for 2^20 tokens in 8
+    # sequences, 32 pieces at 16 heads and 8 at 64 heads (segments at most
+    # pieces + 8), the layouts of explicit pieces of 1,025 and 4,097 chunks;
+    # at 64 heads the per-sequence cut would take 32 + 8 segments.  fp32
+    # inputs, more than 256 sequences and short batches keep the per-sequence
+    # cut (segments of T H / 256 tokens, at most 32,768).
+    ws = lib.kda_prefill_cp_workspace_size
+    B, F = K.KDA_BF16, K.KDA_F32
+    T = 1 << 20
+    assert ws(8, T, 16, 128, 128, B, 0) == ws(8, T, 16, 128, 128, B, -1025 * 32)
+    assert ws(8, T, 64, 128, 128, B, 0) == ws(8, T, 64, 128, 128, B, -4097 * 32)
+    assert ws(8, T, 64, 128, 128, B, 0) < ws(8, T, 64, 128, 128, B, 32768)
+    assert ws(8, T, 64, 128, 128, F, 0) == ws(8, T, 64, 128, 128, F, 32768)
+    assert ws(257, T, 16, 128, 128, B, 0) == ws(257, T, 16, 128, 128, B, 32768)
+    assert ws(4, 65536, 32, 128, 128, B, 0) == ws(4, 65536, 32, 128, 128, B, 8192)
     assert ws(1, 4096, 1, 128, 128, 7, 1024) == 0              # bad dtype
     assert ws(-1, 4096, 1, 128, 128, B, 1024) == 0
 
