@@ -316,8 +316,13 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
  * the process ends), forked from `stream` and joined back into it with events,
  * so the call stays ordered on `stream` (also under stream capture).  A final
  * chunk-parallel pass turns each chunk's states and inputs into its gradients.
- * Precision as kda_prefill: bf16 inputs run the contractions on fp16 MFMA
- * operands with exact power-of-two scales, fp32 inputs on fp32 MFMA.
+ * For bf16 inputs with segments of more than 36 chunks, a segment whose
+ * forward transition over its first 36 chunks comes out exactly zero in fp32
+ * has its gradient summary formed from those chunks alone (nothing later in
+ * the segment reaches its start above the smallest fp32 subnormal); the test
+ * is made on the computed transition, so inputs that do not decay take the
+ * full walk.  Precision as kda_prefill: bf16 inputs run the contractions on
+ * fp16 MFMA operands with exact power-of-two scales, fp32 inputs on fp32 MFMA.
  *
  *   q, k, v, g, beta, initial_state, cu_seqlens, dtype: as kda_prefill
  *   dout          [total_tokens, num_heads, dv]   dtype
