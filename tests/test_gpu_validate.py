@@ -25,6 +25,7 @@ fin = torch.empty(2, 2, 128, 128, device="cuda")
 args = lambda cu: (inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["initial_state"], cu, out, fin)
 calls = {"kda_prefill": lambda cu: K.kda_prefill(*args(cu)),
          "kda_prefill_cp": lambda cu: K.kda_prefill_cp(*args(cu)),
+         "kda_prefill_cp pieces": lambda cu: K.kda_prefill_cp(*args(cu), seg_len=-64),
          "kda_decode_tokens": lambda cu: K.kda_decode_tokens(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cu,
                                                              inp["initial_state"], state_out=fin, out=out),
          "kda_backward": lambda cu: K.kda_backward(*args(cu)[:7], out)}
@@ -62,6 +63,6 @@ def _run(validate):
 
 def test_validate_rejects_bad_cu_seqlens():
     lines = _run(True)
-    assert len(lines) == 12
+    assert len(lines) == 15
     assert all(line.endswith(": 1") for line in lines), lines
 
