@@ -197,7 +197,9 @@ def kda_prefill_cp_workspace_size(num_seqs: int, total_tokens: int, num_heads: i
 def kda_prefill_cp(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                    seg_len: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Context-parallel prefill (same arguments and result as kda_prefill):
-    sequences are split into seg_len-token segments that run side by side.
+    sequences are split into seg_len-token segments that run side by side
+    (seg_len < 0: pieces of -seg_len tokens over the packed chunk order;
+    0: automatic, see include/kda.h).
     ``workspace`` is a uint8 device tensor of at least
     kda_prefill_cp_workspace_size(...) bytes; if None, one is allocated."""
     N, T, H, dk, dv = _check_prefill_args(q, k, v, g, beta, initial_state, cu_seqlens, out, final_state)
