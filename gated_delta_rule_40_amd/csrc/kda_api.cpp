@@ -321,7 +321,7 @@ int32_t cp_default_seg_len(int32_t T, int32_t H)
 
 // The segment cut of a call: seg_len > 0 cuts every sequence into seg_len
 // tokens from its start; seg_len < 0 cuts the packed chunk order into pieces
-// of -seg_len tokens (at most 256 sequences); 0 chooses.  Pieces are the
+// of -seg_len tokens; 0 chooses.  Pieces are the
 // automatic choice for 16-bit inputs and at most 256 sequences when the
 // segments would be capped (T H / 256 above 32,768 tokens): then the fewest
 // equal pieces that give every one of two workgroups per compute unit one
@@ -334,7 +334,7 @@ kda_status cp_cut(int32_t N, int32_t T, int32_t H, int bf16, int32_t *seg_len, i
     *pieces = 0;
     *piece_len = 0;
     if (*seg_len < 0) {
-        if (*seg_len < -(INT32_MAX / 2) || (-*seg_len) % kCpChunk || N > 256) return KDA_ERR_UNSUPPORTED;
+        if (*seg_len < -(INT32_MAX / 2) || (-*seg_len) % kCpChunk) return KDA_ERR_UNSUPPORTED;
         *seg_len = -*seg_len;
         *piece_len = *seg_len / kCpChunk;
         const int64_t np = ((int64_t)T / kCpChunk + N + *piece_len - 1) / *piece_len;

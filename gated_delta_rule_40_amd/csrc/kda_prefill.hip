@@ -155,7 +155,7 @@ struct PlanArgs {
     int32_t *plan, *seq_seg, *chunk_off, *sched;   // chunk_off, sched may be nullptr
     int32_t last_len, skip_last;
     int32_t *seq_order;                            // may be nullptr
-    // Pieces (pieces > 0; cp_plan_small only): the packed chunks, numbered
+    // Pieces (pieces > 0): the packed chunks, numbered
     // across the sequences, are cut into pieces of piece_len chunks (0: the
     // fewest pieces of equal length, at most `pieces`), and each sequence into
     // its parts in those pieces, so that its segments end where pieces end
@@ -399,6 +399,30 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
     const int32_t seg_len = pa.seg_len, max_segs = pa.max_segs, last_len = pa.last_len, skip_last = pa.skip_last;
     int32_t *const plan = pa.plan, *const seq_seg = pa.seq_seg, *const chunk_off = pa.chunk_off;
     int32_t *const sched = pa.sched, *const seq_order = pa.seq_order;
+    // pieces: the total chunk count first (the piece length follows from it)
+    int64_t P = 0, np_used = 1;
+    if (pa.pieces > 0) {
+        int64_t tc = 0;
+        for (int base = 0; base < N; base += 256) {
+            const int n = base + (int)threadIdx.x;
+            int64_t nc = 0;
+            if (n < N) {
+                const int32_t t0 = min(max(cu[n], 0), T_tot), t1 = min(max(cu[n + 1], t0), T_tot);
+                nc = ((int64_t)t1 - t0 + chunk - 1) / chunk;
+            }
+            cscan[threadIdx.x] = nc;
+            __syncthreads();
+            for (int off = 128; off > 0; off >>= 1) {    // tree sum
+                if ((int)threadIdx.x < off) cscan[threadIdx.x] += cscan[threadIdx.x + off];
+                __syncthreads();
+            }
+            tc += cscan[0];
+            __syncthreads();
+        }
+        P = pa.piece_len > 0 ? (int64_t)pa.piece_len : max((tc + pa.pieces - 1) / pa.pieces, (int64_t)1);
+        np_used = max((tc + P - 1) / P, (int64_t)1);
+    }
+    int64_t lp_carry = -1;                              // pieces: piece of the previous block's last segment
     int64_t carry = 0, ccarry = 0;                     // 64-bit: cu is not trusted
     for (int base = 0; base < N; base += 256) {
         const int n = base + (int)threadIdx.x;
@@ -408,6 +432,25 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
             t1 = min(max(cu[n + 1], t0), T_tot);
             ns = max(1, (int32_t)(((int64_t)t1 - t0 + seg_len - 1) / seg_len));
             nc = (int32_t)(((int64_t)t1 - t0 + chunk - 1) / chunk);
+        }
+        int64_t c0 = 0, p0 = 0, lp = -1;                // pieces: first chunk, first and last piece
+        if (P > 0) {
+            // the chunk scan first, then the segment counts from it
+            cscan[threadIdx.x] = nc;
+            __syncthreads();
+            for (int off = 1; off < 256; off <<= 1) {
+                const int64_t y = threadIdx.x >= (unsigned)off ? cscan[threadIdx.x - off] : 0;
+                __syncthreads();
+                cscan[threadIdx.x] += y;
+                __syncthreads();
+            }
+            c0 = ccarry + cscan[threadIdx.x] - nc;
+            p0 = c0 / P;
+            if (n < N) {
+                ns = nc > 0 ? (int32_t)((c0 + nc - 1) / P - p0 + 1) : 1;
+                lp = min(nc > 0 ? (c0 + nc - 1) / P : p0, np_used - 1);
+            }
+            __syncthreads();                            // cscan is rescanned below
         }
         scan[threadIdx.x] = ns;
         cscan[threadIdx.x] = nc;
@@ -422,6 +465,17 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
         }
         if (chunk_off && n < N) chunk_off[n] = (int32_t)min(ccarry + cscan[threadIdx.x] - nc, (int64_t)max_chunks);
         const int64_t start = carry + scan[threadIdx.x] - ns;
+        // pieces: the piece of the previous sequence's last segment, through
+        // LDS (hist, as int32: pieces fit) within the block, lp_carry across
+        int64_t prev_lp = lp_carry;
+        if (P > 0) {
+            hist[threadIdx.x] = (int32_t)lp;
+            __syncthreads();
+            if (threadIdx.x > 0) prev_lp = hist[threadIdx.x - 1];
+            const int last = min(255, N - 1 - base);
+            lp_carry = hist[last];
+            __syncthreads();                            // hist is reused below
+        }
         if (n < N) {
             // With non-decreasing cu the host bound on max_segs always holds;
             // otherwise segments past it are dropped (memory-safe, result unspecified).
@@ -432,6 +486,18 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
             for (int s = 0; s < ns && start + s < max_segs; ++s) {
                 const int gs = (int)(start + s);
                 plan[4 * gs] = n;
+                if (P > 0) {
+                    // the sequence's chunks [c0, c0 + nc) within piece p0 + s
+                    const int64_t ga = max(c0, (p0 + s) * P), gb = min(c0 + nc, (p0 + s + 1) * P);
+                    plan[4 * gs + 1] = (int32_t)(t0 + (ga - c0) * chunk);
+                    plan[4 * gs + 2] = (int32_t)min(t0 + (gb - c0) * chunk, (int64_t)t1);
+                    plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) | (s == ns - 1 ? SEG_LAST : 0);
+                    if (pa.piece_first) {                // first segment of the pieces after its predecessor's
+                        const int64_t pc = min(p0 + s, np_used - 1), pp = s == 0 ? prev_lp : pc - 1;
+                        for (int64_t p = pp + 1; p <= min(pc, (int64_t)pa.pieces); ++p) pa.piece_first[p] = gs;
+                    }
+                    continue;
+                }
                 plan[4 * gs + 1] = t0 + s * seg_len;
                 plan[4 * gs + 2] = min(t0 + (s + 1) * seg_len, t1);
                 plan[4 * gs + 3] = (s == 0 ? SEG_FIRST : 0) |
@@ -444,6 +510,8 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
     }
     const int32_t used = (int32_t)min(carry, (int64_t)max_segs);
     if (threadIdx.x == 0) seq_seg[N] = used;
+    if (P > 0 && pa.piece_first && threadIdx.x == 0)   // pieces past the last segment's: empty
+        for (int64_t p = max(lp_carry + 1, (int64_t)0); p <= (int64_t)pa.pieces; ++p) pa.piece_first[p] = used;
     if (seq_order) {
         // sequences by segment count, most first (counting sort on 256
         // buckets; 255 segments and more share the first): the combine walks
@@ -483,10 +551,11 @@ __device__ __forceinline__ void cp_plan_body(const int32_t *__restrict__ cu, int
     // length, 255 = empty); the order inside a bucket does not matter, since
     // the segments of one pass are independent.  skip_last: SEG_LAST segments
     // count as empty (a summary pass skips them).
+    const int64_t slen = P > 0 ? P * chunk : (int64_t)seg_len;   // a full segment's tokens
     auto seg_bucket = [&](int gs) {
         int64_t len = (int64_t)plan[4 * gs + 2] - plan[4 * gs + 1];
         if (skip_last && (plan[4 * gs + 3] & SEG_LAST)) len = 0;
-        return (int)((seg_len - min(max(len, (int64_t)0), (int64_t)seg_len)) * 255 / seg_len);
+        return (int)((slen - min(max(len, (int64_t)0), slen)) * 255 / slen);
     };
     hist[threadIdx.x] = 0;
     __syncthreads();   // also makes this workgroup's plan entries visible below
@@ -3071,7 +3140,8 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
                                          int32_t last_len, int32_t skip_last, int32_t *seq_order,
                                          int32_t seg_len2, int32_t max_segs2, int32_t *plan2, int32_t *seq_seg2,
                                          int32_t *sched2, int32_t last_len2, int32_t skip_last2,
-                                         int32_t *seq_order2, hipStream_t stream)
+                                         int32_t *seq_order2, int32_t pieces, int32_t piece_len,
+                                         hipStream_t stream)
 {
     kda::PlanArgs a0, a1;
     if (!plan_args(seg_len, max_segs, plan, seq_seg, chunk_off, sched, last_len, skip_last, seq_order, &a0))
@@ -3079,6 +3149,12 @@ extern "C" hipError_t kda_launch_cp_plan(const int32_t *cu, int32_t N, int32_t T
     a1 = a0;
     if (plan2 && !plan_args(seg_len2, max_segs2, plan2, seq_seg2, nullptr, sched2, last_len2, skip_last2, seq_order2, &a1))
         return hipErrorInvalidValue;
+    if (pieces > 0) {      // both plans cut alike; the first plan's sched becomes its piece_first table
+        a0.pieces = a1.pieces = pieces;
+        a0.piece_len = a1.piece_len = piece_len;
+        a0.piece_first = sched;
+        a0.sched = nullptr;
+    }
     hipLaunchKernelGGL(kda::kda_cp_plan_kernel, dim3(plan2 ? 2 : 1), dim3(256), 0, stream, cu, N, T_tot, chunk,
                        max_chunks, a0, a1);
     return hipGetLastError();
@@ -3107,13 +3183,14 @@ extern "C" hipError_t kda_launch_cp_plan_prep(int bf16, const void *q, const voi
     using namespace kda;
     if (!chunk_off || max_chunks < 1 || max_chunks > 0x7fffffff) return hipErrorInvalidValue;
     // pieces (both plans cut alike; the first plan's sched becomes its
-    // piece_first table of pieces + 1 entries): built by cp_plan_small only
-    if (pieces < 0 || piece_len < 0 || (pieces > 0 && (N < 1 || N > 256 || !sched || pieces >= max_segs)))
+    // piece_first table of pieces + 1 entries)
+    if (pieces < 0 || piece_len < 0 || (pieces > 0 && (N < 1 || !sched || pieces >= max_segs)))
         return hipErrorInvalidValue;
     if (N < 1 || N > 256) {
         hipError_t e = kda_launch_cp_plan(cu, N, T_tot, seg_len, max_segs, plan, seq_seg, 32, (int32_t)max_chunks,
                                           chunk_off, sched, last_len, skip_last, seq_order, seg_len2, max_segs2,
-                                          plan2, seq_seg2, sched2, last_len2, skip_last2, seq_order2, stream);
+                                          plan2, seq_seg2, sched2, last_len2, skip_last2, seq_order2, pieces,
+                                          piece_len, stream);
         if (e != hipSuccess) return e;
         return kda_launch_chunk_prep(bf16, q, k, g, beta, cu, N, T_tot, H, chunk_off, max_chunks, img, gimg, stream);
     }

@@ -187,8 +187,7 @@ kda_status kda_prefill_snapshots(const void *q, const void *k, const void *v,
  *
  *   seg_len    > 0: tokens per segment, a multiple of 32, counted from each
  *              sequence's start.
- *              < 0: pieces of -seg_len tokens (a multiple of 32; at most 256
- *              sequences, else KDA_ERR_UNSUPPORTED).  The 32-token chunks of
+ *              < 0: pieces of -seg_len tokens (a multiple of 32).  The 32-token chunks of
  *              all sequences, numbered in packed order, are cut into pieces
  *              of -seg_len / 32 chunks, and every sequence into its parts in
  *              those pieces: a segment ends where a piece or its sequence

@@ -203,17 +203,21 @@ def test_cp_summary_tail_vs_oracle(g_lo):
     _check_cp(inp, TOL[torch.bfloat16], "cp_tail_g_lo=%g" % g_lo, 8192)
 
 
-@pytest.mark.parametrize("dtype,nseq", [(torch.float32, 300), (torch.bfloat16, 300), (torch.bfloat16, 256),
-                                        (torch.bfloat16, 257)])
-def test_cp_many_sequences_vs_oracle(dtype, nseq):
+@pytest.mark.parametrize("dtype,nseq,seg_len", [(torch.float32, 300, 64), (torch.bfloat16, 300, 64),
+                                                (torch.bfloat16, 256, 64), (torch.bfloat16, 257, 64),
+                                                (torch.bfloat16, 300, -64), (torch.float32, 300, -96),
+                                                (torch.bfloat16, 600, -160), (torch.bfloat16, 256, -64)])
+def test_cp_many_sequences_vs_oracle(dtype, nseq, seg_len):
     # more than 256 sequences: the plan kernel walks them in several blocks of
-    # 256 (segment and chunk numbering, the order of sequences by unit count);
-    # up to 256 the plans are built inside the chunk-operand launch
+    # 256 (segment and chunk numbering, the order of sequences by unit count;
+    # with pieces, the total chunk count first and each block's last piece
+    # passed on to the next); up to 256 the plans are built inside the
+    # chunk-operand launch
     rng = np.random.default_rng(40)
     lengths = [int(x) for x in rng.integers(0, 90, size=nseq)]
     lengths[7], lengths[123], lengths[nseq - 1] = 0, 257, 300
     inp = to_dev(I.random_prefill(lengths, H=2, dtype=dtype, seed=40))
-    _check_cp(inp, TOL[dtype], "cp_many_seqs_%d" % nseq, 64)
+    _check_cp(inp, TOL[dtype], "cp_many_seqs_%d" % nseq, seg_len)
 
 
 def test_cp_run_to_run_bitwise_determinism():
